@@ -1,0 +1,239 @@
+"""Plain float64 definition of the indexer top-k path (oracle; test infrastructure only).
+
+Notation: row b (a query token), its window length n_b (the number of visible
+keys), row-local key positions j = 0..n_b-1, physical KV-cache slots, page
+size P.
+
+Readings where the pages are silent are marked READING. The same readings are
+listed in the repository's design notes.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .fp8 import decode_e4m3fn
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Addressing
+# ---------------------------------------------------------------------------
+
+
+def token_slots(bt_row: np.ndarray, page_size: int, n: int) -> np.ndarray:
+    """Physical slot of each of the first n tokens of one row.
+
+    [ATOM-1473], decode-kernel diff in the review thread: the kernel walks the
+    row's blocks, reads ``page = bt_row[blk]`` (widened to int64) and
+    addresses tokens ``blk * BLOCK_SIZE_K + off`` inside that page. So token j
+    lives at slot ``bt_row[j // P] * P + j % P``.
+    """
+    P = int(page_size)
+    j = np.arange(int(n), dtype=np.int64)
+    return np.asarray(bt_row, dtype=np.int64)[j // P] * P + j % P
+
+
+def page_transform(positions: np.ndarray, pt_row: np.ndarray, page_size: int) -> np.ndarray:
+    """Map row-local positions to physical slots; -1 stays -1.
+
+    [SGL-37889], Motivation and Modifications: the top-k "transform" maps the
+    selected row-local index through the page table, and with page_size 1
+    the table is the wide per-token table. For a general page size the same
+    slot rule as ``token_slots`` applies.
+    """
+    P = int(page_size)
+    pos = np.asarray(positions, dtype=np.int64)
+    out = np.full(pos.shape, -1, dtype=np.int64)
+    ok = pos >= 0
+    p = pos[ok]
+    out[ok] = np.asarray(pt_row, dtype=np.int64)[p // P] * P + p % P
+    return out
+
+
+def row_window(scores: np.ndarray, i: int, seq_lens, row_starts=None) -> np.ndarray:
+    """fp32 window of row i, widened exactly to float64.
+
+    [SGL-37889], Modifications, addressing table: without row_starts row i
+    reads ``scores[i, :seq_lens[i]]``; with it, row i reads
+    ``scores[i, row_starts[i] : row_starts[i] + seq_lens[i]]``.
+    """
+    n = int(seq_lens[i])
+    rs = 0 if row_starts is None else int(row_starts[i])
+    return _f64(scores[i, rs:rs + n])
+
+
+def page_row(i: int, row_to_batch=None) -> int:
+    """[SGL-37889], Modifications: page-table row is ``row_to_batch[i]`` if given, else i."""
+    return int(i) if row_to_batch is None else int(row_to_batch[i])
+
+
+# ---------------------------------------------------------------------------
+# Selection
+# ---------------------------------------------------------------------------
+
+
+def topk_order(values: np.ndarray, k: int) -> np.ndarray:
+    """Positions of the k best values of one row, padded with -1.
+
+    Definition: sort the whole row by value, descending, with a STABLE sort,
+    so equal values keep ascending position; keep the first min(k, n); fill
+    the rest of the k outputs with -1. Values compare as IEEE numbers:
+    -0.0 == +0.0, +-inf allowed. NaN is outside the input domain and raises.
+
+    READING: the pages give no tie rule. Ties go to the lower position, and
+    rows shorter than k are padded with -1. [SGL-37889], Modifications: the
+    selected index stays row-local until the transform.
+    """
+    v = _f64(values).reshape(-1)
+    if np.isnan(v).any():
+        raise ValueError("NaN score in top-k input")
+    k = int(k)
+    out = np.full(k, -1, dtype=np.int64)
+    m = min(k, v.shape[0])
+    if m > 0:
+        order = np.argsort(-v, kind="stable")
+        out[:m] = order[:m]
+    return out
+
+
+def topk_rows(scores: np.ndarray, seq_lens, k: int, row_starts=None, row_to_batch=None,
+              page_table=None, page_size: int = 1, rows=None) -> np.ndarray:
+    """Top-k with page transform over an fp32 score buffer, row by row.
+
+    [SGL-37889], Modifications: each row's window comes from the addressing
+    table (``row_window``), the best k row-local positions are kept
+    (``topk_order``), and the page-table row ``page_row`` maps them to slots
+    (``page_transform``). With ``page_table=None`` the row-local positions
+    are returned. ``rows`` picks a subset of rows (default: all).
+    """
+    rows = range(int(np.asarray(seq_lens).shape[0])) if rows is None else list(rows)
+    out = []
+    for i in rows:
+        pos = topk_order(row_window(scores, i, seq_lens, row_starts), k)
+        if page_table is not None:
+            pos = page_transform(pos, page_table[page_row(i, row_to_batch)], page_size)
+        out.append(pos)
+    return np.stack(out) if out else np.zeros((0, int(k)), np.int64)
+
+
+# ---------------------------------------------------------------------------
+# Scoring
+# ---------------------------------------------------------------------------
+
+
+def index_scores(q_b, q_scale_b, w_b, kcache, k_scale, bt_row, page_size: int, n: int) -> np.ndarray:
+    """Indexer score of every visible key of one row, in float64.
+
+    S[j] = sum_h w[h] * max(0, dot[h, j] * s_q * s_k[slot_j]),
+    dot[h, j] = sum_d qhat[h, d] * khat[slot_j, d].
+
+    [ATOM-1473], Pull request overview and commit "fp8 index score calculate
+    in fp8": queries and index keys are fp8 and the dot product is taken on
+    fp8 operands. The key of token j is fetched through the block table
+    (``token_slots``).
+
+    READING: the pages name the index score without writing it out. This
+    library's score is the weighted-ReLU head sum above, with one fp32 scale
+    per query row, one per cached token, and one fp32 weight per (row, head).
+    The scales multiply the dot before the ReLU.
+
+    The dot is exact in float64: every product of two e4m3 values is an
+    integer multiple of 2^-18 below 448^2, so sums of 128 of them need at most
+    43 significant bits.
+    """
+    qd = decode_e4m3fn(q_b)  # [H, D]
+    slots = token_slots(bt_row, page_size, n)
+    kd = decode_e4m3fn(np.asarray(kcache)[slots])  # [n, D]
+    dot = kd @ qd.T  # [n, H]
+    sk = _f64(np.asarray(k_scale)[slots])
+    logits = dot * float(q_scale_b) * sk[:, None]
+    return (np.maximum(logits, 0.0) * _f64(w_b)[None, :]).sum(axis=1)
+
+
+def case_scores(case, b: int) -> np.ndarray:
+    """``index_scores`` of row b of a workloads.IndexerCase."""
+    return index_scores(case.q[b], case.q_scale[b], case.w[b], case.kcache, case.k_scale,
+                        case.block_table[b], case.page_size, int(case.seq_lens[b]))
+
+
+def fused_topk(case, rows=None, k=None):
+    """Score + top-k + page transform for decode rows of an indexer case.
+
+    [ATOM-1473], Pull request overview: the decode indexer scores the fp8
+    index cache and keeps a top-k of key positions (the fused kernel only
+    removes the intermediate score tensor, so it computes the same thing).
+    Returns (slots [R, k] int64, positions [R, k] int64, scores list of the
+    float64 score rows).
+    """
+    k = int(case.k if k is None else k)
+    rows = range(case.batch) if rows is None else list(rows)
+    slots, positions, scores = [], [], []
+    for b in rows:
+        S = case_scores(case, b)
+        pos = topk_order(S, k)
+        positions.append(pos)
+        slots.append(page_transform(pos, case.block_table[b], case.page_size))
+        scores.append(S)
+    return np.stack(slots), np.stack(positions), scores
+
+
+# ---------------------------------------------------------------------------
+# Block-sparse variant
+# ---------------------------------------------------------------------------
+
+
+def block_scores(S: np.ndarray, block_size: int) -> np.ndarray:
+    """Block score = max of the token scores of the block's visible tokens.
+
+    [ATOM-1282], title and launch script (--block-size 128): key positions are
+    grouped in 128-token blocks and blocks are selected. [ATOM-1473], Pull
+    request overview: an index block-score kernel produces the block scores.
+    READING: the block score is the max over the block's visible tokens;
+    block c covers tokens [c*bs, min((c+1)*bs, n)), for c < ceil(n / bs).
+    """
+    S = _f64(S)
+    n = S.shape[0]
+    bs = int(block_size)
+    nb = -(-n // bs)
+    return np.array([S[c * bs:min((c + 1) * bs, n)].max() for c in range(nb)], dtype=np.float64)
+
+
+def block_topk(case, rows=None, block_size=None, top_blocks=None):
+    """Top blocks per row, as physical block ids and expanded slot lists.
+
+    [ATOM-1282], title: the sparse block list is built inside the top-k
+    step. READING: keep the top_blocks best blocks (ties to the lower block
+    id, via ``topk_order``). With block_size == page_size, block c is page
+    ``bt[b, c]`` and its slots are ``page * bs + t`` for its visible tokens t.
+    Past n_b the slot list holds -1, and missing blocks give -1 block ids and
+    -1 slots.
+
+    Returns (blocks [R, top] int64, slots [R, top*bs] int64, logical block ids
+    [R, top] int64, block-score rows).
+    """
+    bs = int(case.block_size if block_size is None else block_size)
+    top = int(case.top_blocks if top_blocks is None else top_blocks)
+    rows = range(case.batch) if rows is None else list(rows)
+    blocks, slot_lists, logical, bscores = [], [], [], []
+    for b in rows:
+        n = int(case.seq_lens[b])
+        S = case_scores(case, b)
+        bsv = block_scores(S, bs) if n > 0 else np.zeros(0)
+        sel = topk_order(bsv, top)
+        tok_slots = token_slots(case.block_table[b], case.page_size, n)
+        phys = np.full(top, -1, np.int64)
+        sl = np.full(top * bs, -1, np.int64)
+        for i, c in enumerate(sel):
+            if c < 0:
+                continue
+            phys[i] = int(case.block_table[b][c * bs // case.page_size])
+            lo, hi = c * bs, min((c + 1) * bs, n)
+            sl[i * bs:i * bs + (hi - lo)] = tok_slots[lo:hi]
+        blocks.append(phys)
+        slot_lists.append(sl)
+        logical.append(sel)
+        bscores.append(bsv)
+    return np.stack(blocks), np.stack(slot_lists), np.stack(logical), bscores

@@ -1,0 +1,313 @@
+"""Seeded synthetic inputs for the sparse-attention indexer top-k path.
+
+This module only draws random inputs and lays them out in memory. It holds
+none of the method's arithmetic (no decoding, no dot products, no scoring, no
+selection), so the CPU oracle and the HIP path can both consume its output
+without sharing any computation.
+
+Every random draw comes from ``numpy.random.default_rng([seed, stream, row])``
+so any single row can be regenerated on its own. The e4m3 bytes of queries and
+index keys are produced by torch's ``float8_e4m3fn`` conversion (a library
+cast, after clamping to the format's finite range of +-448).
+
+Workload shapes follow the pages:
+  * ROCm/ATOM PR 1473 ("enable minimax m3 fp8 index cache and fuse
+    index_score_kernel with partial_topk kernel"), the decode kernel's paged
+    index-key cache walked through a block table, 64-token pages;
+  * sgl-project/sglang PR 37889 ("Enable GLM DSA prefill top-k to the v2
+    kernel"), section Modifications: one packed fp32 score buffer shared by all
+    requests of an extend batch, addressed through row_starts / row_to_batch,
+    ISL 70000 and 16384-row launches (section Speed Tests and Profiling);
+  * ROCm/ATOM PR 1282 ("merge build sparse block into topk"), 128-token
+    blocks.
+"""
+from __future__ import annotations
+
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+# Independent random streams (second element of the rng seed list).
+STREAM_LEN = 1
+STREAM_VAL = 2
+STREAM_SNAP = 3
+STREAM_PT = 4
+STREAM_Q = 5
+STREAM_W = 6
+STREAM_KEY = 7
+STREAM_PAGE = 8
+
+E4M3_MAX = 448.0
+# Values written into every cache slot and score cell that no row may read:
+# key byte 0x7E is +448, the largest finite e4m3 value, and a large scale makes
+# any such token score far above every real token.
+SENTINEL_KEY_BYTE = 0x7E
+SENTINEL_KEY_SCALE = 1.0e3
+SENTINEL_SCORE = np.float32(np.inf)
+
+_POOL_THREADS = 8
+
+
+def rng(seed: int, stream: int, row: int = 0) -> np.random.Generator:
+    return np.random.default_rng([int(seed), int(stream), int(row)])
+
+
+def _to_e4m3_bytes(x: np.ndarray) -> np.ndarray:
+    """Cast float32 values to OCP e4m3fn bytes with torch (clamped to +-448)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    t = t.clamp_(-E4M3_MAX, E4M3_MAX)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _snap(v: np.ndarray, frac: float, g: np.random.Generator) -> None:
+    """Snap a Bernoulli(frac) subset of v to the 1/16 grid (round half to even)."""
+    if frac <= 0.0:
+        return
+    m = g.random(v.shape[0]) < frac
+    v[m] = np.round(v[m] * np.float32(16.0)) / np.float32(16.0)
+
+
+# --------------------------------------------------------------------------
+# Top-k over a given fp32 score buffer (decode layout and packed extend layout)
+# --------------------------------------------------------------------------
+
+
+@dataclass
+class RowsCase:
+    """fp32 score rows plus the addressing of the top-k-with-transform op."""
+
+    name: str
+    scores: np.ndarray  # float32 [rows, stride]; cells outside windows are +inf
+    seq_lens: np.ndarray  # int32 [rows]
+    row_starts: Optional[np.ndarray]  # int32 [rows] or None (window starts at 0)
+    row_to_batch: Optional[np.ndarray]  # int32 [rows] or None (page row = row)
+    page_table: np.ndarray  # int32 [pt_rows, pt_width]
+    page_size: int
+    k: int
+
+    @property
+    def rows(self) -> int:
+        return int(self.scores.shape[0])
+
+    @property
+    def stride(self) -> int:
+        return int(self.scores.shape[1])
+
+
+def _fill_row(buf_row: np.ndarray, start: int, n: int, seed: int, row: int, tie_frac: float) -> None:
+    v = rng(seed, STREAM_VAL, row).standard_normal(n, dtype=np.float32)
+    _snap(v, tie_frac, rng(seed, STREAM_SNAP, row))
+    buf_row[:] = SENTINEL_SCORE
+    buf_row[start:start + n] = v
+
+
+def _fill_rows(scores, starts, lens, seed, tie_frac):
+    rows = scores.shape[0]
+
+    def work(r):
+        _fill_row(scores[r], int(starts[r]), int(lens[r]), seed, r, tie_frac)
+
+    if rows * scores.shape[1] < (1 << 22):
+        for r in range(rows):
+            work(r)
+    else:
+        with ThreadPoolExecutor(_POOL_THREADS) as ex:
+            list(ex.map(work, range(rows)))
+
+
+def decode_rows_case(seed: int = 101, rows: int = 8, stride: int = 4096, n_lo: int = 256,
+                     n_hi: int = 4096, k: int = 512, tie_frac: float = 0.05,
+                     pt_width: int = 65536, name: str = "decode-topk") -> RowsCase:
+    """Decode layout: row i owns scores[i, :n_i] and page-table row i.
+
+    Default sizes: 8 rows of a [8, 4096] buffer, n_i uniform on [256, 4096],
+    5% of values snapped to the 1/16 grid, k = 512, page_size 1 tables made of
+    independent permutations of [0, 65536).
+    """
+    lens = rng(seed, STREAM_LEN).integers(n_lo, n_hi + 1, size=rows).astype(np.int32)
+    scores = np.empty((rows, stride), dtype=np.float32)
+    _fill_rows(scores, np.zeros(rows, np.int64), lens, seed, tie_frac)
+    pt = np.stack([rng(seed, STREAM_PT, i).permutation(pt_width) for i in range(rows)]).astype(np.int32)
+    return RowsCase(name, scores, lens, None, None, pt, 1, k)
+
+
+def packed_prefill_case(seed: int = 103, prefix0: int = 61808, new_tokens: int = 8192,
+                        k: int = 512, tie_frac: float = 0.01,
+                        name: str = "packed-prefill-topk") -> RowsCase:
+    """Packed extend layout of two requests sharing one fp32 score buffer.
+
+    Request 0 has a prefix of ``prefix0`` cached tokens, request 1 has none;
+    each contributes ``new_tokens`` query rows and attention is causal, so row
+    r of a request sees prefix + r + 1 keys. The buffer has
+    ``prefix0 + new_tokens + 1`` columns (70001 at full size: not a multiple of
+    4). The two windows cannot sit end to end in that width, so request 0's
+    rows start at column 0 and request 1's rows start at
+    ``stride - new_tokens`` (61809 at full size, odd), where its longest window
+    ends on the last column. Each request owns one page-table row of width
+    ``prefix0 + new_tokens``; the two rows are one permutation of
+    [0, 2 * width) so slots never collide across requests.
+    """
+    stride = prefix0 + new_tokens + 1
+    width = prefix0 + new_tokens
+    rows = 2 * new_tokens
+    r = np.arange(new_tokens, dtype=np.int64)
+    lens = np.concatenate([prefix0 + r + 1, r + 1]).astype(np.int32)
+    starts = np.concatenate([np.zeros(new_tokens, np.int64),
+                             np.full(new_tokens, stride - new_tokens, np.int64)]).astype(np.int32)
+    r2b = np.concatenate([np.zeros(new_tokens, np.int32), np.ones(new_tokens, np.int32)])
+    scores = np.empty((rows, stride), dtype=np.float32)
+    _fill_rows(scores, starts, lens, seed, tie_frac)
+    pt = rng(seed, STREAM_PT).permutation(2 * width).astype(np.int32).reshape(2, width)
+    return RowsCase(name, scores, lens, starts, r2b, pt, 1, k)
+
+
+# --------------------------------------------------------------------------
+# Indexer inputs: fp8 queries, head weights, paged fp8 index-key cache
+# --------------------------------------------------------------------------
+
+
+@dataclass
+class IndexerCase:
+    name: str
+    q: np.ndarray  # uint8 (e4m3fn bytes) [B, H, D]
+    q_scale: np.ndarray  # float32 [B]
+    w: np.ndarray  # float32 [B, H]
+    kcache: np.ndarray  # uint8 (e4m3fn bytes) [num_slots, D]
+    k_scale: np.ndarray  # float32 [num_slots]
+    block_table: np.ndarray  # int32 [B, max_pages]; unused entries name the sentinel page
+    page_size: int
+    seq_lens: np.ndarray  # int32 [B]
+    k: int = 2048
+    block_size: int = 0  # block-sparse variant: tokens per block
+    top_blocks: int = 0  # block-sparse variant: blocks kept per row
+    max_seq_len: int = 0  # upper bound on seq_lens the caller promises
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def batch(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def heads(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def dim(self) -> int:
+        return int(self.q.shape[2])
+
+
+def indexer_case(seed: int, batch: int, n_lo: int, n_hi: int, page_size: int, k: int = 2048,
+                 heads: int = 64, dim: int = 128, block_size: int = 0, top_blocks: int = 0,
+                 fixed_lens: Optional[np.ndarray] = None, name: str = "indexer") -> IndexerCase:
+    """Paged fp8 indexer inputs.
+
+    q ~ 0.5 N(0,1) per element with one fp32 scale per row (max|q| / 448); head
+    weights ~ N(0,1) / 8; keys ~ N(0,1) per element with one fp32 scale per
+    token (max|k_t| / 448). Every row gets ceil(n_b / page_size) pages drawn
+    from one permutation of all pages; one extra page filled with sentinels
+    backs every unused block-table entry, and unused slots of partly filled
+    pages hold sentinels too.
+    """
+    if fixed_lens is not None:
+        lens = np.asarray(fixed_lens, dtype=np.int32)
+        assert lens.shape == (batch,)
+    else:
+        lens = rng(seed, STREAM_LEN).integers(n_lo, n_hi + 1, size=batch).astype(np.int32)
+    max_seq_len = int(max(n_hi, int(lens.max()) if batch else 0))
+    P = int(page_size)
+    npages = [(int(n) + P - 1) // P for n in lens]
+    total_pages = int(sum(npages))
+    perm = rng(seed, STREAM_PAGE).permutation(total_pages).astype(np.int64)
+    sentinel_page = total_pages
+    num_slots = (total_pages + 1) * P
+    max_pages = max(1, (max_seq_len + P - 1) // P)
+
+    q = np.empty((batch, heads, dim), np.uint8)
+    q_scale = np.empty(batch, np.float32)
+    w = np.empty((batch, heads), np.float32)
+    for b in range(batch):
+        qf = rng(seed, STREAM_Q, b).standard_normal((heads, dim), dtype=np.float32) * np.float32(0.5)
+        s = np.float32(np.abs(qf).max() / np.float32(E4M3_MAX))
+        q_scale[b] = s
+        q[b] = _to_e4m3_bytes(qf / s)
+        w[b] = rng(seed, STREAM_W, b).standard_normal(heads, dtype=np.float32) / np.float32(8.0)
+
+    kcache = np.full((num_slots, dim), SENTINEL_KEY_BYTE, np.uint8)
+    k_scale = np.full(num_slots, SENTINEL_KEY_SCALE, np.float32)
+    bt = np.full((batch, max_pages), sentinel_page, np.int32)
+    offs = np.concatenate([[0], np.cumsum(npages)]).astype(np.int64)
+
+    def work(b):
+        n = int(lens[b])
+        pages = perm[offs[b]:offs[b + 1]]
+        bt[b, :pages.shape[0]] = pages.astype(np.int32)
+        if n == 0:
+            return
+        kf = rng(seed, STREAM_KEY, b).standard_normal((n, dim), dtype=np.float32)
+        s = (np.abs(kf).max(axis=1) / np.float32(E4M3_MAX)).astype(np.float32)
+        s = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+        kb = _to_e4m3_bytes(kf / s[:, None])
+        slots = (pages[:, None] * P + np.arange(P, dtype=np.int64)[None, :]).reshape(-1)[:n]
+        kcache[slots] = kb
+        k_scale[slots] = s
+
+    if batch * max_seq_len * dim < (1 << 24):
+        for b in range(batch):
+            work(b)
+    else:
+        with ThreadPoolExecutor(_POOL_THREADS) as ex:
+            list(ex.map(work, range(batch)))
+
+    return IndexerCase(name, q, q_scale, w, kcache, k_scale, bt, P, lens, k=k,
+                       block_size=block_size, top_blocks=top_blocks, max_seq_len=max_seq_len,
+                       meta={"total_pages": total_pages, "sentinel_page": sentinel_page})
+
+
+# --------------------------------------------------------------------------
+# The five named workloads (full size) and reduced versions for quick tests
+# --------------------------------------------------------------------------
+
+SEEDS = {"c1": 101, "c2": 102, "c3": 103, "c4": 104, "c5": 105}
+
+
+def c1_decode_topk() -> RowsCase:
+    return decode_rows_case(seed=SEEDS["c1"], name="decode-topk-8x4096-k512")
+
+
+def c2_fused_decode() -> IndexerCase:
+    return indexer_case(SEEDS["c2"], batch=32, n_lo=8192, n_hi=16384, page_size=64, k=2048,
+                        name="fused-decode-B32-n8k-16k-k2048")
+
+
+def c3_packed_prefill() -> RowsCase:
+    return packed_prefill_case(seed=SEEDS["c3"], name="packed-prefill-16384x70001-k512")
+
+
+def c4_block_sparse() -> IndexerCase:
+    return indexer_case(SEEDS["c4"], batch=64, n_lo=32768, n_hi=32768, page_size=128,
+                        k=0, block_size=128, top_blocks=32,
+                        name="block-sparse-B64-n32768-top32x128")
+
+
+def c5_long_decode() -> IndexerCase:
+    return indexer_case(SEEDS["c5"], batch=64, n_lo=131072, n_hi=327680, page_size=64, k=2048,
+                        name="long-decode-B64-n128k-320k-k2048")
+
+
+def expected_tokens(case: IndexerCase) -> int:
+    return int(np.asarray(case.seq_lens, dtype=np.int64).sum())
+
+
+def ceil_div(a: int, b: int) -> int:
+    return -(-int(a) // int(b))
+
+
+__all__ = [
+    "RowsCase", "IndexerCase", "decode_rows_case", "packed_prefill_case", "indexer_case",
+    "c1_decode_topk", "c2_fused_decode", "c3_packed_prefill", "c4_block_sparse", "c5_long_decode",
+    "SEEDS", "SENTINEL_KEY_BYTE", "SENTINEL_KEY_SCALE", "rng", "expected_tokens", "ceil_div",
+]
