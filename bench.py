@@ -1,0 +1,345 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse-attention indexer top-k path on one MI355X.
+
+Headline step: one topk_rows call over the packed-prefill batch, 16384 score
+rows of a [16384, 70001] fp32 buffer from two requests (prefix 61808 and 0,
+8192 new tokens each), k = 512, page_size 1 transform through row_to_batch.
+That is the workload of the pages' kernel-level measurement: grid 16384, ISL
+70000 ("[AMD] Enable GLM DSA prefill top-k to the v2 kernel", section Speed
+Tests and Profiling).
+
+The same JSON line also carries the other workloads, each with its own HBM
+roofline figure:
+  * decode top-k:    8 rows of [8, 4096], k 512;
+  * fused decode:    B 32, n ~ U[8192, 16384], k 2048;
+  * block-sparse:    B 64, n 32768, top 32 blocks of 128;
+  * long decode:     B 64, n ~ U[131072, 327680], k 2048.
+It also carries the CPU oracle's throughput on a bounded sample of the
+headline workload, run on the host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only c3|all|...] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "top-k rows/s + µs/launch and achieved HBM GB/s (% roofline), 1 MI355X"
+HBM_PEAK_GBPS = 8000.0
+FLUSH_BYTES = 1 << 30
+COUNTERS_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "topk_rows": ["topk_rows.hip", "select.hpp", "common.hpp"],
+    "fused": ["indexer.hip", "score_mfma.hpp", "select.hpp", "common.hpp"],
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "sparse_attention_indexer_fp8_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(name: str, kind: str):
+    """HBM bytes per launch from committed rocprofv3 PMC runs, if the kernel is unchanged."""
+    path = os.path.join(COUNTERS_DIR, f"{name}.counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != source_hash(kind):
+        return None
+    return d.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes (what the method must move; see the design notes)
+# ---------------------------------------------------------------------------
+
+
+def rows_algorithmic_bytes(case) -> int:
+    n = case.seq_lens.astype(np.int64)
+    k = case.k
+    read = int((4 * n[n > k]).sum())
+    sel = np.minimum(n, k)
+    out = case.rows * k * 4
+    gathers = int((4 * sel).sum()) if case.page_table is not None else 0
+    meta = 4 * case.rows * (1 + (case.row_starts is not None) + (case.row_to_batch is not None))
+    return read + out + gathers + meta
+
+
+def indexer_algorithmic_bytes(case, out_entries: int) -> int:
+    n = case.seq_lens.astype(np.int64)
+    P = case.page_size
+    keys = int((n * (case.dim + 4)).sum())
+    table = int((4 * ((n + P - 1) // P)).sum())
+    query = case.batch * case.heads * (case.dim + 4) + 8 * case.batch
+    return keys + table + query + 4 * out_entries
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline (runs before the GPU is touched; forked workers)
+# ---------------------------------------------------------------------------
+
+_CPU_CASE = None
+
+
+def _oracle_rows(rows):
+    import oracle
+
+    c = _CPU_CASE
+    return oracle.topk_rows(c.scores, c.seq_lens, c.k, c.row_starts, c.row_to_batch, c.page_table,
+                            c.page_size, rows=rows).shape[0]
+
+
+def cpu_baseline(case, every: int = 4):
+    import multiprocessing as mp
+
+    global _CPU_CASE
+    _CPU_CASE = case
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    rows = list(range(0, case.rows, every))
+    chunks = [rows[i::cores * 4] for i in range(cores * 4)]
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(cores) as pool:
+        done = sum(pool.map(_oracle_rows, chunks))
+    wall = time.perf_counter() - t0
+    assert done == len(rows)
+    return {"value": round(len(rows) / wall, 1), "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(rows)} of {case.rows} rows (every {every}th) of the packed-prefill buffer, "
+                      f"oracle.topk_rows (float64 full stable sort per row + page transform), "
+                      f"{cores} forked worker processes, wall {wall:.2f} s"}
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+
+
+class Timer:
+    def __init__(self, torch):
+        self.torch = torch
+        self.flush_buf = None
+
+    def flush(self):
+        if self.flush_buf is None:
+            self.flush_buf = self.torch.empty(FLUSH_BYTES // 4, dtype=self.torch.float32, device="cuda")
+        self.flush_buf.fill_(1.0)
+
+    def run(self, fn, warmup, steps, flush=False):
+        torch = self.torch
+        for _ in range(warmup):
+            if flush:
+                self.flush()
+            fn()
+        torch.cuda.synchronize()
+        ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            if flush:
+                self.flush()
+            ev0[i].record()
+            fn()
+            ev1[i].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in zip(ev0, ev1)])
+        return wall, us
+
+
+def summary(us, nbytes, rows):
+    med = float(np.median(us))
+    mean = float(np.mean(us))
+    gbps = nbytes / (mean * 1e-6) / 1e9
+    return {"us_per_launch_mean": round(mean, 2), "us_per_launch_median": round(med, 2),
+            "us_p10": round(float(np.percentile(us, 10)), 2), "us_p90": round(float(np.percentile(us, 90)), 2),
+            "rows_per_s": round(rows / (mean * 1e-6), 1), "algorithmic_bytes": int(nbytes),
+            "achieved_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
+def dev(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def bench_rows(torch, ops, timer, case, warmup, steps, flush):
+    sc = dev(torch, case.scores)
+    sl = dev(torch, case.seq_lens)
+    rs = None if case.row_starts is None else dev(torch, case.row_starts)
+    rb = None if case.row_to_batch is None else dev(torch, case.row_to_batch)
+    pt = dev(torch, case.page_table)
+    out = torch.empty((case.rows, case.k), dtype=torch.int32, device="cuda")
+
+    def step():
+        ops.topk_rows(sc, sl, case.k, rs, rb, pt, case.page_size, out=out)
+
+    wall, us = timer.run(step, warmup, steps, flush)
+    res = summary(us, rows_algorithmic_bytes(case), case.rows)
+    del sc
+    torch.cuda.empty_cache()
+    return wall, us, res
+
+
+def bench_fused(torch, ops, timer, case, warmup, steps, flush):
+    args = [dev(torch, x) for x in (case.q, case.q_scale, case.w, case.kcache, case.k_scale,
+                                    case.block_table, case.seq_lens)]
+    out = torch.empty((case.batch, case.k), dtype=torch.int32, device="cuda")
+    ws = ops.Workspace()
+
+    def step():
+        ops.idx_score_topk_fused(*args, case.page_size, case.max_seq_len, case.k, workspace=ws, out=out)
+
+    wall, us = timer.run(step, warmup, steps, flush)
+    res = summary(us, indexer_algorithmic_bytes(case, case.batch * case.k), case.batch)
+    res["tokens"] = int(case.seq_lens.astype(np.int64).sum())
+    del args
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_block(torch, ops, timer, case, warmup, steps, flush):
+    args = [dev(torch, x) for x in (case.q, case.q_scale, case.w, case.kcache, case.k_scale,
+                                    case.block_table, case.seq_lens)]
+    ws = ops.Workspace()
+
+    def step():
+        ops.block_topk(*args, case.page_size, case.max_seq_len, case.block_size, case.top_blocks, workspace=ws)
+
+    wall, us = timer.run(step, warmup, steps, flush)
+    out_entries = case.batch * case.top_blocks * (1 + case.block_size)
+    res = summary(us, indexer_algorithmic_bytes(case, out_entries), case.batch)
+    res["tokens"] = int(case.seq_lens.astype(np.int64).sum())
+    del args
+    torch.cuda.empty_cache()
+    return res
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default="all", help="comma list of c1..c5, or all")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for PMC byte-counter calibration)")
+    a = ap.parse_args(argv)
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the indexer top-k path here runs on a single MI355X "
+              "(no sharding, no collectives); run with --gpus 1", file=sys.stderr)
+        return 2
+    only = {"c1", "c2", "c3", "c4", "c5"} if a.only == "all" else set(a.only.split(","))
+
+    case3 = None
+    cpu = None
+    if "c3" in only:
+        log("generating packed-prefill 16384x70001 ...")
+        case3 = workloads.c3_packed_prefill()
+        if not a.no_cpu:
+            log("cpu oracle baseline ...")
+            cpu = cpu_baseline(case3)
+            log(f"cpu baseline {cpu['value']} rows/s on {cpu['cores']} cores")
+
+    import torch
+    from sparse_attention_indexer_fp8_amd import ops
+
+    torch.cuda.set_device(0)
+    timer = Timer(torch)
+    also = {}
+    line = None
+
+    if a.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 copies of 1 GiB")
+        del src, dst
+
+    if case3 is not None:
+        log("timing packed-prefill top-k ...")
+        wall, us, res = bench_rows(torch, ops, timer, case3, a.warmup, a.steps, flush=False)
+        traffic = counter_traffic("topk_rows_packed_prefill_16384x70001", "topk_rows")
+        roof = {"bound": "hbm", "achieved": res["achieved_GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(res["achieved_GBps"] / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": "topk_rows_kernel<25>",
+                "per_launch": {"algorithmic_bytes": res["algorithmic_bytes"],
+                               "avg_kernel_us": res["us_per_launch_mean"]}}
+        line = {
+            "metric": METRIC,
+            "value": round(case3.rows * a.steps / wall, 1),
+            "unit": "rows/s",
+            "n_gpus": 1,
+            "steps": a.steps,
+            "warmup": a.warmup,
+            "ms_per_step": round(wall / a.steps * 1e3, 4),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "f32",
+            "data": "synthetic",
+            "config": {"workload": "packed-prefill-topk: 16384 rows x 70001 fp32 (2 requests, prefix 61808/0, "
+                                   "8192 new tokens each), k=512, page_size 1, row_starts/row_to_batch",
+                       "rows": case3.rows, "stride": case3.stride, "k": case3.k,
+                       "sum_seq_len": int(case3.seq_lens.astype(np.int64).sum())},
+            "roofline": roof,
+            "cpu_baseline": cpu,
+            "us_per_launch": res["us_per_launch_mean"],
+            "us_per_launch_median": res["us_per_launch_median"],
+            "achieved_GBps": res["achieved_GBps"],
+        }
+        del case3
+    if "c1" in only:
+        log("timing decode top-k ...")
+        c1 = workloads.c1_decode_topk()
+        _, _, also["decode_topk_8x4096_k512"] = bench_rows(torch, ops, timer, c1, a.warmup, max(a.steps, 50),
+                                                           flush=True)
+    if "c2" in only:
+        log("timing fused decode B32 ...")
+        c2 = workloads.c2_fused_decode()
+        also["fused_decode_B32_k2048"] = bench_fused(torch, ops, timer, c2, a.warmup, max(a.steps, 50), True)
+        del c2
+    if "c4" in only:
+        log("timing block-sparse B64 ...")
+        c4 = workloads.c4_block_sparse()
+        also["block_sparse_B64_n32768_top32"] = bench_block(torch, ops, timer, c4, a.warmup, max(a.steps, 50),
+                                                            True)
+        del c4
+    if "c5" in only:
+        log("generating long decode B64 ...")
+        c5 = workloads.c5_long_decode()
+        log("timing long decode B64 ...")
+        also["long_decode_B64_k2048"] = bench_fused(torch, ops, timer, c5, a.warmup, a.steps, False)
+        del c5
+    if line is None:
+        line = {"metric": METRIC, "value": None, "unit": "rows/s", "n_gpus": 1, "steps": a.steps,
+                "warmup": a.warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                "dtype": "f32", "data": "synthetic", "config": {"workload": "partial run: " + a.only}}
+    line["also"] = also
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,226 @@
+/*
+ * libidxtopk -- sparse-attention indexer top-k for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI. Plain pointers and sizes only; no framework types.
+ *
+ * Pages this interface follows:
+ *   [ATOM-1473] ROCm/ATOM pull request 1473, "enable minimax m3 fp8 index cache
+ *               and fuse index_score_kernel with partial_topk kernel";
+ *   [SGL-37889] sgl-project/sglang pull request 37889, "[AMD] Enable GLM DSA
+ *               prefill top-k to the v2 kernel";
+ *   [ATOM-1282] ROCm/ATOM pull request 1282, "merge build sparse block into topk".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument except `stream` is a DEVICE pointer to memory owned
+ *   by the caller. The library never allocates, frees or synchronises. Each
+ *   call enqueues at most two kernels on `stream` (a hipStream_t; NULL = the
+ *   null stream) and returns without waiting.
+ * - Strides are in elements (int64). Index, length and slot arrays are int32.
+ * - fp8 data are OCP e4m3fn bytes (gfx950's native fp8). The pages name the
+ *   format only as fp8 e4m3 ([SGL-37889] Reproduce: --kv-cache-dtype
+ *   fp8_e4m3; [ATOM-1473] Pull request overview: FP8 index cache).
+ * - Top-k semantics: for each row, the k largest values of the row's window.
+ *   Equal values go to the lower key position, so -0.0 ties with +0.0.
+ *   Positions are row-local until the page transform ([SGL-37889]
+ *   Modifications). A row with fewer than k visible keys yields all of them,
+ *   then -1 padding. The ORDER of the k entries within a row is unspecified;
+ *   the SET is exact.
+ * - Return value: IDXTOPK_OK, or a negative status. Every argument is checked
+ *   on the host before anything is enqueued, and on error nothing is
+ *   enqueued. Kernel-launch failures return IDXTOPK_ELAUNCH.
+ * - Caller-owned preconditions, not checked on the device:
+ *     * windows lie inside their buffers;
+ *     * row_to_batch entries and page ids are valid rows / pages;
+ *     * seq_lens[b] <= max_seq_len;
+ *     * scales are finite and > 0;
+ *     * scores are not NaN;
+ *     * slots fit in int32.
+ *   Out-of-range inputs are undefined behaviour.
+ */
+#ifndef IDXTOPK_H
+#define IDXTOPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define IDXTOPK_VERSION 100 /* 1.0.0 */
+
+/* Status codes. */
+#define IDXTOPK_OK 0
+#define IDXTOPK_EINVAL (-1)       /* null required pointer, negative size, bad stride */
+#define IDXTOPK_EUNSUPPORTED (-2) /* valid but not implemented: dim != 128, heads, k too large */
+#define IDXTOPK_EWORKSPACE (-3)   /* workspace missing or smaller than idxtopk_workspace_bytes() */
+#define IDXTOPK_ELAUNCH (-4)      /* the HIP runtime refused a kernel launch */
+
+/* Limits. */
+#define IDXTOPK_DIM 128           /* index-key / query head dimension */
+#define IDXTOPK_MAX_K_ROWS 8192   /* topk_rows */
+#define IDXTOPK_MAX_K_FUSED 8192  /* idx_score_topk_fused */
+#define IDXTOPK_MAX_TOP_BLOCKS 4096 /* block_topk */
+
+/* Operation ids for idxtopk_workspace_bytes(). */
+#define IDXTOPK_OP_TOPK_ROWS 1
+#define IDXTOPK_OP_SCORE 2
+#define IDXTOPK_OP_PAGE_TRANSFORM 3
+#define IDXTOPK_OP_SCORE_TOPK_FUSED 4
+#define IDXTOPK_OP_BLOCK_TOPK 5
+
+/*
+ * Indexer inputs shared by idx_score_fp8, idx_score_topk_fused and block_topk.
+ *
+ *   q           uint8 e4m3fn [batch, heads, dim]: one query token per row, one
+ *               vector per index head.
+ *   q_scale     float [batch]: dequantisation scale of each query row (> 0).
+ *   w           float [batch, heads]: per-row, per-head weights.
+ *   kcache      uint8 e4m3fn [num_slots, dim]: the paged index-key cache.
+ *   k_scale     float [num_slots]: dequantisation scale of each cached key (> 0).
+ *   block_table int32 [batch, bt_stride]: physical page of each logical page of
+ *               a row. Token j of row b is at slot
+ *               block_table[b, j / page_size] * page_size + j % page_size
+ *               ([ATOM-1473] decode-kernel diff: page = bt_row[blk], widened
+ *               to int64 before use; positions blk * BLOCK_SIZE_K + offset).
+ *   seq_lens    int32 [batch]: n_b, the number of visible keys of row b (the
+ *               causal length of the decode kernel's mask in [ATOM-1473]).
+ *   max_seq_len an upper bound on every seq_lens[b], used to size the grid.
+ *
+ * Index score of token j of row b (computed in fp32 with fp8 MFMA):
+ *   S[b, j] = sum_h w[b, h] * max(0, q_scale[b] * k_scale[slot_j]
+ *                                   * sum_d q[b, h, d] * kcache[slot_j, d]).
+ * The pages name the index score and its fp8 operands ([ATOM-1473] Pull
+ * request overview; commit "fp8 index score calculate in fp8") but do not
+ * write the formula out. The weighted-ReLU head sum above is this library's
+ * definition.
+ *
+ * Supported shapes: dim == 128; heads in {16, 32, 64, 128}; page_size >= 1.
+ */
+
+/*
+ * idx_score_fp8 -- write the index score of every visible key.
+ *
+ * Writes scores[b * score_stride + j] for 0 <= j < seq_lens[b]. Other cells
+ * are untouched. This is the unfused score kernel of [ATOM-1473] (Pull
+ * request overview: the index_score_kernel whose output tensor the fused
+ * kernel removes).
+ * Requires max_seq_len <= score_stride.
+ */
+int idx_score_fp8(const uint8_t* q, const float* q_scale, const float* w,
+                  const uint8_t* kcache, const float* k_scale,
+                  const int32_t* block_table, int64_t bt_stride, int32_t page_size,
+                  const int32_t* seq_lens, int32_t batch, int32_t heads, int32_t dim,
+                  int32_t max_seq_len, float* scores, int64_t score_stride, void* stream);
+
+/*
+ * topk_rows -- top-k over a given fp32 score buffer, with page transform.
+ *
+ * [SGL-37889] Modifications, addressing table:
+ *   window of row i = scores[i * score_stride + rs_i + t], 0 <= t < seq_lens[i]
+ *       with rs_i = row_starts ? row_starts[i] : 0;
+ *   page-table row  = row_to_batch ? row_to_batch[i] : i.
+ * Both indirections are optional (NULL gives the decode layout). With
+ * row_to_batch the caller owns the page-table bound. The window may start at
+ * any column, and score_stride need not be a multiple of 4.
+ *
+ * out int32 [rows, k]: for each row, the k best row-local positions, mapped to
+ * physical slots page_table[prow * pt_stride + p / page_size] * page_size +
+ * p % page_size, or the positions themselves when page_table is NULL; -1 pads
+ * rows with seq_lens[i] < k.
+ *
+ * 1 <= k <= IDXTOPK_MAX_K_ROWS. No workspace.
+ */
+int topk_rows(const float* scores, int64_t score_stride, int32_t rows,
+              const int32_t* seq_lens, const int32_t* row_starts, const int32_t* row_to_batch,
+              const int32_t* page_table, int64_t pt_stride, int32_t page_size,
+              int32_t k, int32_t* out, void* stream);
+
+/*
+ * topk_page_transform -- map row-local positions to physical slots.
+ *
+ * out[i, t] = idx[i, t] < 0 ? -1
+ *           : page_table[prow * pt_stride + idx / page_size] * page_size + idx % page_size,
+ * with prow = row_to_batch ? row_to_batch[i] : i ([SGL-37889] Modifications:
+ * the selected index stays row-local and the transform maps it through the
+ * page table). idx and out are int32 [rows, k] and may alias.
+ */
+int topk_page_transform(const int32_t* idx, int32_t rows, int32_t k,
+                        const int32_t* page_table, int64_t pt_stride, int32_t page_size,
+                        const int32_t* row_to_batch, int32_t* out, void* stream);
+
+/*
+ * idx_score_topk_fused -- fused decode indexer: score + top-k + page transform.
+ *
+ * For every row b: the top k tokens of S[b, 0:seq_lens[b]] (ties to the lower
+ * position), emitted as physical slots (the block_table mapping above). The
+ * score row is never written to HBM ([ATOM-1473] Pull request overview: the
+ * fused kernel removes the intermediate score tensor). Chunks of each row
+ * keep their candidates in a caller-provided workspace, in place of the
+ * partial score and index buffers of [ATOM-1473]'s kernel launch.
+ *
+ * out_slots  int32 [batch, k]; -1 pads rows with seq_lens[b] < k.
+ * out_scores optional float [batch, k]: the score of each emitted token
+ *            (-inf for padding).
+ * workspace  device memory of at least
+ *            idxtopk_workspace_bytes(IDXTOPK_OP_SCORE_TOPK_FUSED, batch, k, max_seq_len)
+ *            bytes. It MUST be zero-filled before its first use, and every
+ *            call leaves it zero-filled again. Concurrent calls must not
+ *            share one workspace.
+ * 1 <= k <= IDXTOPK_MAX_K_FUSED.
+ */
+int idx_score_topk_fused(const uint8_t* q, const float* q_scale, const float* w,
+                         const uint8_t* kcache, const float* k_scale,
+                         const int32_t* block_table, int64_t bt_stride, int32_t page_size,
+                         const int32_t* seq_lens, int32_t batch, int32_t heads, int32_t dim,
+                         int32_t max_seq_len, int32_t k, int32_t* out_slots, float* out_scores,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * block_topk -- block-sparse variant: block scores, top blocks, sparse list.
+ *
+ * Block c of row b covers tokens [c * block_size, min((c + 1) * block_size,
+ * n_b)). Its score is the max of S over those tokens (the pages' "index
+ * block-score kernel" in [ATOM-1473] Pull request overview, reduction read as
+ * max). Keep the top_blocks best blocks, ties to the lower block id, and build
+ * the sparse block list in the same call ([ATOM-1282], title: merge build
+ * sparse block into topk).
+ *
+ * Requires block_size == page_size, so block c is physical page
+ * block_table[b, c].
+ * out_blocks int32 [batch, top_blocks]: physical block (page) ids; -1 pads.
+ * out_slots  optional int32 [batch, top_blocks * block_size]: entry
+ *            i * block_size + t is the slot of token t of the i-th emitted
+ *            block, or -1 past n_b or for padded blocks.
+ * workspace  at least idxtopk_workspace_bytes(IDXTOPK_OP_BLOCK_TOPK, batch,
+ *            block_size, max_seq_len) bytes, zero-filled before first use; left
+ *            zero-filled by every call.
+ * 1 <= top_blocks <= IDXTOPK_MAX_TOP_BLOCKS.
+ */
+int block_topk(const uint8_t* q, const float* q_scale, const float* w,
+               const uint8_t* kcache, const float* k_scale,
+               const int32_t* block_table, int64_t bt_stride, int32_t page_size,
+               const int32_t* seq_lens, int32_t batch, int32_t heads, int32_t dim,
+               int32_t max_seq_len, int32_t block_size, int32_t top_blocks,
+               int32_t* out_blocks, int32_t* out_slots,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes an operation needs (0 when it needs none).
+ * For IDXTOPK_OP_BLOCK_TOPK, pass block_size as `k`. Returns 0 for invalid
+ * arguments as well.
+ */
+size_t idxtopk_workspace_bytes(int32_t op, int32_t rows, int32_t k, int32_t max_seq_len);
+
+/* Human-readable text of a status code (static storage). */
+const char* idxtopk_status_str(int32_t status);
+
+/* IDXTOPK_VERSION of the loaded library. */
+int32_t idxtopk_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IDXTOPK_H */

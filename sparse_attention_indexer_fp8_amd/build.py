@@ -1,0 +1,81 @@
+"""Build libidxtopk.so (HIP, gfx950) in-tree with hipcc.
+
+Usage: python -m sparse_attention_indexer_fp8_amd.build [--debug] [-j N]
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+SOURCES = ["api.hip", "topk_rows.hip", "page_transform.hip", "indexer.hip"]
+LIB_NAME = "libidxtopk.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+BUILD_DIR = os.path.join(ROOT, "_build")
+ARCH = "gfx950"
+
+# Packed fp32 instructions stay off: hipcc would otherwise form them from
+# plain float code.
+COMMON_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-std=c++17",
+    "-fPIC",
+    "-fvisibility=hidden",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the HIP library cannot be built")
+
+
+def _run(cmd):
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in p.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if p.returncode != 0:
+        raise RuntimeError(f"command failed ({p.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(debug: bool = False, jobs: int = 4, verbose: bool = False) -> str:
+    hipcc = _hipcc()
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    opt = ["-O1", "-g"] if debug else ["-O3"]
+    objs = []
+    cmds = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        cmds.append([hipcc, *COMMON_FLAGS, *opt, "-c", os.path.join(CSRC, src), "-o", obj])
+    with cf.ThreadPoolExecutor(max(1, jobs)) as ex:
+        for out in ex.map(_run, cmds):
+            if verbose and out.strip():
+                print(out)
+    tmp = LIB_PATH + ".tmp"
+    _run([hipcc, *COMMON_FLAGS, "-shared", *objs, "-o", tmp])
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--debug", action="store_true")
+    ap.add_argument("-j", "--jobs", type=int, default=4)
+    ap.add_argument("-v", "--verbose", action="store_true")
+    a = ap.parse_args(argv)
+    path = build(debug=a.debug, jobs=a.jobs, verbose=a.verbose)
+    print(path)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,163 @@
+// C ABI of libidxtopk: argument validation, then the launchers.
+// Declarations and the meaning of every argument: include/idxtopk.h.
+#include "../../include/idxtopk.h"
+#include "launch.hpp"
+
+namespace {
+
+using idxtopk::IndexerInputs;
+
+bool heads_ok(int32_t h) { return h == 16 || h == 32 || h == 64 || h == 128; }
+
+// Shared checks of the paged indexer inputs (no device access).
+int check_indexer(const uint8_t* q, const float* q_scale, const float* w, const uint8_t* kcache,
+                  const float* k_scale, const int32_t* block_table, int64_t bt_stride,
+                  int32_t page_size, const int32_t* seq_lens, int32_t batch, int32_t heads,
+                  int32_t dim, int32_t max_seq_len) {
+  if (batch < 0 || heads <= 0 || dim <= 0 || page_size <= 0 || bt_stride < 0 || max_seq_len < 0)
+    return IDXTOPK_EINVAL;
+  if (batch > 0 && (!q || !q_scale || !w || !kcache || !k_scale || !block_table || !seq_lens))
+    return IDXTOPK_EINVAL;
+  if (dim != IDXTOPK_DIM || !heads_ok(heads)) return IDXTOPK_EUNSUPPORTED;
+  // every visible token's logical page must exist in the block-table row
+  if (static_cast<int64_t>(max_seq_len) > bt_stride * static_cast<int64_t>(page_size))
+    return IDXTOPK_EINVAL;
+  return IDXTOPK_OK;
+}
+
+IndexerInputs pack(const uint8_t* q, const float* q_scale, const float* w, const uint8_t* kcache,
+                   const float* k_scale, const int32_t* block_table, int64_t bt_stride,
+                   int32_t page_size, const int32_t* seq_lens, int32_t batch, int32_t heads,
+                   int32_t max_seq_len) {
+  IndexerInputs in;
+  in.q = q;
+  in.q_scale = q_scale;
+  in.w = w;
+  in.kcache = kcache;
+  in.k_scale = k_scale;
+  in.block_table = block_table;
+  in.bt_stride = bt_stride;
+  in.page_size = page_size;
+  in.seq_lens = seq_lens;
+  in.batch = batch;
+  in.heads = heads;
+  in.max_seq_len = max_seq_len;
+  return in;
+}
+
+}  // namespace
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+int idx_score_fp8(const uint8_t* q, const float* q_scale, const float* w, const uint8_t* kcache,
+                  const float* k_scale, const int32_t* block_table, int64_t bt_stride,
+                  int32_t page_size, const int32_t* seq_lens, int32_t batch, int32_t heads,
+                  int32_t dim, int32_t max_seq_len, float* scores, int64_t score_stride,
+                  void* stream) {
+  const int st = check_indexer(q, q_scale, w, kcache, k_scale, block_table, bt_stride, page_size,
+                               seq_lens, batch, heads, dim, max_seq_len);
+  if (st != IDXTOPK_OK) return st;
+  if (score_stride < 0 || (batch > 0 && !scores)) return IDXTOPK_EINVAL;
+  if (static_cast<int64_t>(max_seq_len) > score_stride) return IDXTOPK_EINVAL;
+  if (batch == 0 || max_seq_len == 0) return IDXTOPK_OK;
+  return idxtopk::launch_idx_score(
+      pack(q, q_scale, w, kcache, k_scale, block_table, bt_stride, page_size, seq_lens, batch,
+           heads, max_seq_len),
+      scores, score_stride, static_cast<hipStream_t>(stream));
+}
+
+int topk_rows(const float* scores, int64_t score_stride, int32_t rows, const int32_t* seq_lens,
+              const int32_t* row_starts, const int32_t* row_to_batch, const int32_t* page_table,
+              int64_t pt_stride, int32_t page_size, int32_t k, int32_t* out, void* stream) {
+  if (rows < 0 || k <= 0 || score_stride < 0) return IDXTOPK_EINVAL;
+  if (rows > 0 && (!scores || !seq_lens || !out)) return IDXTOPK_EINVAL;
+  if (page_table && (pt_stride < 0 || page_size <= 0)) return IDXTOPK_EINVAL;
+  if (k > IDXTOPK_MAX_K_ROWS) return IDXTOPK_EUNSUPPORTED;
+  if (rows == 0) return IDXTOPK_OK;
+  return idxtopk::launch_topk_rows(scores, score_stride, rows, seq_lens, row_starts, row_to_batch,
+                                   page_table, pt_stride, page_table ? page_size : 1, k, out,
+                                   static_cast<hipStream_t>(stream));
+}
+
+int topk_page_transform(const int32_t* idx, int32_t rows, int32_t k, const int32_t* page_table,
+                        int64_t pt_stride, int32_t page_size, const int32_t* row_to_batch,
+                        int32_t* out, void* stream) {
+  if (rows < 0 || k <= 0 || pt_stride < 0 || page_size <= 0) return IDXTOPK_EINVAL;
+  if (rows > 0 && (!idx || !page_table || !out)) return IDXTOPK_EINVAL;
+  if (rows == 0) return IDXTOPK_OK;
+  return idxtopk::launch_page_transform(idx, rows, k, page_table, pt_stride, page_size,
+                                        row_to_batch, out, static_cast<hipStream_t>(stream));
+}
+
+int idx_score_topk_fused(const uint8_t* q, const float* q_scale, const float* w,
+                         const uint8_t* kcache, const float* k_scale, const int32_t* block_table,
+                         int64_t bt_stride, int32_t page_size, const int32_t* seq_lens,
+                         int32_t batch, int32_t heads, int32_t dim, int32_t max_seq_len, int32_t k,
+                         int32_t* out_slots, float* out_scores, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  const int st = check_indexer(q, q_scale, w, kcache, k_scale, block_table, bt_stride, page_size,
+                               seq_lens, batch, heads, dim, max_seq_len);
+  if (st != IDXTOPK_OK) return st;
+  if (k <= 0 || (batch > 0 && !out_slots)) return IDXTOPK_EINVAL;
+  if (k > IDXTOPK_MAX_K_FUSED) return IDXTOPK_EUNSUPPORTED;
+  if (batch == 0) return IDXTOPK_OK;
+  if (!workspace || workspace_bytes < idxtopk::fused_workspace_bytes(batch, k, max_seq_len))
+    return IDXTOPK_EWORKSPACE;
+  return idxtopk::launch_fused(pack(q, q_scale, w, kcache, k_scale, block_table, bt_stride,
+                                    page_size, seq_lens, batch, heads, max_seq_len),
+                               k, out_slots, out_scores, workspace,
+                               static_cast<hipStream_t>(stream));
+}
+
+int block_topk(const uint8_t* q, const float* q_scale, const float* w, const uint8_t* kcache,
+               const float* k_scale, const int32_t* block_table, int64_t bt_stride,
+               int32_t page_size, const int32_t* seq_lens, int32_t batch, int32_t heads,
+               int32_t dim, int32_t max_seq_len, int32_t block_size, int32_t top_blocks,
+               int32_t* out_blocks, int32_t* out_slots, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  const int st = check_indexer(q, q_scale, w, kcache, k_scale, block_table, bt_stride, page_size,
+                               seq_lens, batch, heads, dim, max_seq_len);
+  if (st != IDXTOPK_OK) return st;
+  if (block_size <= 0 || top_blocks <= 0 || (batch > 0 && !out_blocks)) return IDXTOPK_EINVAL;
+  if (block_size != page_size || top_blocks > IDXTOPK_MAX_TOP_BLOCKS || block_size % 16 != 0 ||
+      block_size > 8192)
+    return IDXTOPK_EUNSUPPORTED;
+  if (batch == 0) return IDXTOPK_OK;
+  if (!workspace ||
+      workspace_bytes < idxtopk::block_workspace_bytes(batch, block_size, max_seq_len))
+    return IDXTOPK_EWORKSPACE;
+  return idxtopk::launch_block_topk(pack(q, q_scale, w, kcache, k_scale, block_table, bt_stride,
+                                         page_size, seq_lens, batch, heads, max_seq_len),
+                                    block_size, top_blocks, out_blocks, out_slots, workspace,
+                                    static_cast<hipStream_t>(stream));
+}
+
+size_t idxtopk_workspace_bytes(int32_t op, int32_t rows, int32_t k, int32_t max_seq_len) {
+  if (rows < 0 || max_seq_len < 0) return 0;
+  switch (op) {
+    case IDXTOPK_OP_SCORE_TOPK_FUSED:
+      return rows > 0 ? idxtopk::fused_workspace_bytes(rows, k, max_seq_len) : 0;
+    case IDXTOPK_OP_BLOCK_TOPK:
+      if (k <= 0) return 0;
+      return rows > 0 ? idxtopk::block_workspace_bytes(rows, k, max_seq_len) : 0;
+    default:
+      return 0;
+  }
+}
+
+const char* idxtopk_status_str(int32_t status) {
+  switch (status) {
+    case IDXTOPK_OK: return "ok";
+    case IDXTOPK_EINVAL: return "invalid argument";
+    case IDXTOPK_EUNSUPPORTED: return "unsupported shape or size";
+    case IDXTOPK_EWORKSPACE: return "workspace missing or too small";
+    case IDXTOPK_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t idxtopk_version(void) { return IDXTOPK_VERSION; }
+
+}  // extern "C"
+#pragma GCC visibility pop

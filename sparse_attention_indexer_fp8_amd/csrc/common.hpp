@@ -1,0 +1,122 @@
+// Shared device helpers for libidxtopk (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace idxtopk {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Ordered keys
+// ---------------------------------------------------------------------------
+
+// Order-preserving map from an fp32 value to uint32: a larger float gives a
+// larger key, -0.0 and +0.0 give the same key (they tie), denormals keep their
+// order, and +-inf sit at the ends of the finite range.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t mag = u & 0x7fffffffu;
+  return (u >> 31) ? (0x80000000u - mag) : (0x80000000u + mag);
+}
+
+// Inverse of float_key (zero comes back as +0.0).
+__device__ __forceinline__ float key_float(uint32_t key) {
+  return (key >= 0x80000000u) ? __uint_as_float(key - 0x80000000u)
+                              : __uint_as_float((0x80000000u - key) | 0x80000000u);
+}
+
+// Total order used by every selection: value first, then the lower position
+// wins. The 64-bit key is unique per position, so "the k largest keys" is
+// exactly the top-k with ties resolved toward the lower position.
+__device__ __forceinline__ uint64_t rank_key(uint32_t vkey, uint32_t pos) {
+  return (static_cast<uint64_t>(vkey) << 32) | static_cast<uint32_t>(~pos);
+}
+__device__ __forceinline__ uint32_t rank_pos(uint64_t key) {
+  return ~static_cast<uint32_t>(key);
+}
+__device__ __forceinline__ uint32_t rank_vkey(uint64_t key) {
+  return static_cast<uint32_t>(key >> 32);
+}
+
+// ---------------------------------------------------------------------------
+// Division by a runtime-invariant divisor (numerators below 2^31)
+// Granlund & Montgomery, "Division by invariant integers using
+// multiplication" (PLDI 1994): q = (umulhi(n, m) + n) >> l with
+// l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1.
+// ---------------------------------------------------------------------------
+struct FastDiv {
+  uint32_t d;
+  uint32_t m;
+  uint32_t l;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  const uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1ull;
+  return FastDiv{d, static_cast<uint32_t>(m), l};
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  return (__umulhi(n, f.m) + n) >> f.l;
+}
+
+// ---------------------------------------------------------------------------
+// Wave helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Inclusive suffix sum across the wave: lane l gets sum of v over lanes >= l.
+__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint32_t o = __shfl_down(v, d, kWave);
+    if (l + d < kWave) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+  for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int d = kWave / 2; d > 0; d >>= 1) {
+    const uint32_t o = __shfl_xor(v, d, kWave);
+    v = o < v ? o : v;
+  }
+  return v;
+}
+
+// Device-scope relaxed atomics on workspace words.
+__device__ __forceinline__ uint32_t ld_acquire_dev(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_dev(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_dev_acq_rel(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace idxtopk

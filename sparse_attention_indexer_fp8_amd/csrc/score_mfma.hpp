@@ -1,0 +1,205 @@
+// fp8 indexer scoring on gfx950 matrix cores.
+//
+// For one query row b and 16 consecutive key tokens at a time, one wave
+// computes logits[h, j] = q[b, h, :] . key[slot_j, :] with
+// v_mfma_f32_16x16x128_f8f6f4. The 16 tokens are the N columns, 16 heads are
+// the M rows, and K = 128 = the whole head dimension in one instruction. It
+// then reduces the heads in registers:
+//   S[j] = k_scale[slot_j] * sum_h (w[b, h] * q_scale[b]) * max(0, logits[h, j]).
+// (The scales are > 0, so folding them outside the ReLU is exact algebra.)
+//
+// Operand layout (both operands, lane l, c = l & 15, g = l >> 4):
+//   A (query):  row c of the 16-head tile, bytes [32g, 32g + 32) of the head vector
+//   B (keys):   column c = token tok0 + c, bytes [32g, 32g + 32) of its key
+// A and B use the same K grouping, so the product sums the full 128-term dot
+// whatever order the hardware assigns to the K index inside a group.
+// Result: lane l holds D[4g + r][c], r = 0..3, i.e. heads 4g + r of the tile
+// for token c.
+#pragma once
+
+#include "common.hpp"
+
+namespace idxtopk {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kDim = 128;
+constexpr int kGroup = 16;  // tokens per MFMA column block
+
+struct IndexerArgs {
+  const uint8_t* q;
+  const float* q_scale;
+  const float* w;
+  const uint8_t* kcache;
+  const float* k_scale;
+  const int32_t* block_table;
+  int64_t bt_stride;
+  int32_t page_size;
+  FastDiv pdiv;
+  const int32_t* seq_lens;
+  int32_t batch;
+  int32_t heads;
+  int32_t chunk;       // tokens per workgroup
+  int32_t nchunk_max;  // chunks per row in the grid
+};
+
+template <int NT>
+struct QOperand {
+  v8i a[NT];
+  float wt[NT][4];
+};
+
+__device__ __forceinline__ v8i load_v8i(const uint8_t* p) {
+  const uint4* p4 = reinterpret_cast<const uint4*>(p);
+  const uint4 x = p4[0];
+  const uint4 y = p4[1];
+  v8i r;
+  r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
+  r[4] = y.x; r[5] = y.y; r[6] = y.z; r[7] = y.w;
+  return r;
+}
+
+// Key bytes are read once per call: load them without keeping them in cache.
+__device__ __forceinline__ v8i load_v8i_stream(const uint8_t* p) {
+  const v8i* pv = reinterpret_cast<const v8i*>(p);
+  return __builtin_nontemporal_load(pv);
+}
+
+template <int NT>
+__device__ __forceinline__ void load_query(QOperand<NT>& qo, const uint8_t* q_row,
+                                           const float* w_row, float s_q) {
+  const int l = lane_id();
+  const int c = l & 15, g = l >> 4;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    qo.a[t] = load_v8i(q_row + (16 * t + c) * kDim + 32 * g);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) qo.wt[t][r] = w_row[16 * t + 4 * g + r] * s_q;
+  }
+}
+
+// Score of token (tok0 + (lane & 15)), returned in every lane of the wave.
+template <int NT>
+__device__ __forceinline__ float score16(const QOperand<NT>& qo, const v8i kb, float ks) {
+  float part = 0.0f;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.a[t], kb, acc, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part = fmaf(qo.wt[t][r], fmaxf(acc[r], 0.0f), part);
+  }
+  // sum the four 16-lane groups (heads 4g..4g+3 of every tile)
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part),
+                                                    false, false);
+  part = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
+                                                    false, false);
+  part = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+  return part * ks;
+}
+
+// Max number of page ids a chunk stages in LDS.
+constexpr int kMaxChunkPages = 1024;
+
+// Score the tokens [tok_begin, tok_end) of row b with a WG-thread workgroup.
+// The chunk's block-table entries are staged in LDS once (`lds_pages`).
+// Waves take contiguous ranges of 16-token groups. Each wave keeps a ring of
+// RING groups of key loads in flight: a slot is consumed in place and refilled
+// with the group RING ahead right after, so no register copy ever forces the
+// wave to wait for loads it has only just issued.
+// emit(j, score) is called by every lane with (lane >> 4) == 0 for each valid
+// token j.
+template <int NT, int WG, int RING, class Emit>
+__device__ void score_chunk(const IndexerArgs& a, int b, int tok_begin, int tok_end,
+                            int32_t* lds_pages, Emit&& emit) {
+  constexpr int NW = WG / kWave;
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid / kWave);
+  const int l = lane_id();
+  const int c = l & 15, g = l >> 4;
+  const uint32_t P = static_cast<uint32_t>(a.page_size);
+
+  const uint32_t p0 = fdiv(static_cast<uint32_t>(tok_begin), a.pdiv);
+  const uint32_t p1 = fdiv(static_cast<uint32_t>(tok_end - 1), a.pdiv);
+  const int32_t* bt_row = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
+  for (int i = tid; i <= static_cast<int>(p1 - p0); i += WG) lds_pages[i] = bt_row[p0 + i];
+
+  QOperand<NT> qo;
+  load_query<NT>(qo, a.q + static_cast<int64_t>(b) * a.heads * kDim,
+                 a.w + static_cast<int64_t>(b) * a.heads, a.q_scale[b]);
+  __syncthreads();
+
+  const int ngroups = (tok_end - tok_begin + kGroup - 1) / kGroup;
+  const int per = (ngroups + NW - 1) / NW;
+  const int g_lo = wave * per;
+  const int g_hi = min(ngroups, g_lo + per);
+  const int last = tok_end - 1;
+
+  // group gi of this chunk -> this lane's 32 key bytes and the token's scale
+  auto fetch = [&](int gi, v8i& kb, float& ks) {
+    int j = tok_begin + gi * kGroup + c;
+    j = j < last ? j : last;
+    const uint32_t pg = fdiv(static_cast<uint32_t>(j), a.pdiv);
+    const uint32_t off = static_cast<uint32_t>(j) - pg * P;
+    const int64_t slot = static_cast<int64_t>(lds_pages[pg - p0]) * P + off;
+    kb = load_v8i_stream(a.kcache + slot * kDim + 32 * g);
+    ks = a.k_scale[slot];
+  };
+
+  if (g_lo >= g_hi) return;
+  const int gmax = g_hi - 1;
+  auto consume = [&](int gi, float s) {
+    const int j = tok_begin + gi * kGroup + c;
+    if (g == 0 && j < tok_end) emit(j, s);
+  };
+
+  typedef float vks __attribute__((ext_vector_type(RING)));
+  v8i ring[RING];
+  vks ksr;
+#pragma unroll
+  for (int u = 0; u < RING; ++u) {
+    float t;
+    fetch(min(g_lo + u, gmax), ring[u], t);
+    ksr[u] = t;
+  }
+
+  // steady state: every refill is in range, so control flow is uniform and
+  // each group only waits for its own loads
+  int gi0 = g_lo;
+  for (; gi0 + 2 * RING <= g_hi; gi0 += RING) {
+#pragma unroll
+    for (int u = 0; u < RING; ++u) {
+      const float s = score16<NT>(qo, ring[u], ksr[u]);
+      // slot u is fully consumed before its refill is issued, so the refill can
+      // reuse the slot's registers (no copies, no early waits)
+      __builtin_amdgcn_sched_barrier(0);
+      float t;
+      fetch(gi0 + u + RING, ring[u], t);
+      ksr[u] = t;
+      consume(gi0 + u, s);
+    }
+  }
+  // drain: fewer than 2 * RING groups remain; the ring holds gi0 .. gi0 + RING - 1
+#pragma unroll
+  for (int u = 0; u < RING; ++u) {
+    const int gi = gi0 + u;
+    if (gi < g_hi) {
+      const float s = score16<NT>(qo, ring[u], ksr[u]);
+      if (gi + RING < g_hi) {
+        float t;
+        fetch(gi + RING, ring[u], t);
+        ksr[u] = t;
+      }
+      consume(gi, s);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < RING; ++u) {
+    const int gi = gi0 + RING + u;
+    if (gi < g_hi) consume(gi, score16<NT>(qo, ring[u], ksr[u]));
+  }
+}
+
+}  // namespace idxtopk

@@ -1,0 +1,191 @@
+"""Torch-facing wrappers of the libidxtopk C ABI (marshalling only).
+
+Each function checks dtypes, devices and layouts, passes raw device pointers,
+sizes and torch's current HIP stream to the library, and returns the output
+tensors. None of them computes anything on the host. The meaning of every
+argument is documented in include/idxtopk.h.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_P = ctypes.c_void_p
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else _P(t.data_ptr())
+
+
+def _stream():
+    return _P(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtypes, ndim: Optional[int] = None, contiguous=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be one of {dtypes} (got {t.dtype})")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims (got {tuple(t.shape)})")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+_F8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _as_u8(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+
+
+def workspace_bytes(op: int, rows: int, k: int, max_seq_len: int) -> int:
+    return int(_lib.load().idxtopk_workspace_bytes(op, rows, k, max_seq_len))
+
+
+class Workspace:
+    """A zero-filled device buffer the library keeps zero-filled between calls.
+
+    One Workspace must not be shared by calls that may run concurrently (for
+    example on two streams).
+    """
+
+    def __init__(self, device=None):
+        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+        self.buf: Optional[torch.Tensor] = None
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+_default_ws = {}
+
+
+def _workspace(ws: Optional[Workspace]) -> Workspace:
+    if ws is not None:
+        return ws
+    dev = torch.cuda.current_device()
+    if dev not in _default_ws:
+        _default_ws[dev] = Workspace(torch.device("cuda", dev))
+    return _default_ws[dev]
+
+
+def topk_rows(scores: torch.Tensor, seq_lens: torch.Tensor, k: int,
+              row_starts: Optional[torch.Tensor] = None, row_to_batch: Optional[torch.Tensor] = None,
+              page_table: Optional[torch.Tensor] = None, page_size: int = 1,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Top-k of each row's fp32 window, mapped through the page table."""
+    _need(scores, "scores", (torch.float32,), 2, contiguous=False)
+    if scores.stride(1) != 1:
+        raise ValueError("scores rows must be contiguous")
+    rows = scores.shape[0]
+    _need(seq_lens, "seq_lens", (torch.int32,), 1)
+    for name, t in (("row_starts", row_starts), ("row_to_batch", row_to_batch)):
+        if t is not None:
+            _need(t, name, (torch.int32,), 1)
+    pt_stride = 0
+    if page_table is not None:
+        _need(page_table, "page_table", (torch.int32,), 2, contiguous=False)
+        if page_table.stride(1) != 1:
+            raise ValueError("page_table rows must be contiguous")
+        pt_stride = page_table.stride(0)
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
+    _need(out, "out", (torch.int32,), 2)
+    st = _lib.load().topk_rows(_ptr(scores), scores.stride(0), rows, _ptr(seq_lens), _ptr(row_starts),
+                               _ptr(row_to_batch), _ptr(page_table), pt_stride, int(page_size), int(k),
+                               _ptr(out), _stream())
+    _lib.check("topk_rows", st)
+    return out
+
+
+def topk_page_transform(idx: torch.Tensor, page_table: torch.Tensor, page_size: int = 1,
+                        row_to_batch: Optional[torch.Tensor] = None,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _need(idx, "idx", (torch.int32,), 2)
+    _need(page_table, "page_table", (torch.int32,), 2, contiguous=False)
+    if page_table.stride(1) != 1:
+        raise ValueError("page_table rows must be contiguous")
+    if row_to_batch is not None:
+        _need(row_to_batch, "row_to_batch", (torch.int32,), 1)
+    if out is None:
+        out = torch.empty_like(idx)
+    _need(out, "out", (torch.int32,), 2)
+    rows, k = idx.shape
+    st = _lib.load().topk_page_transform(_ptr(idx), rows, k, _ptr(page_table), page_table.stride(0),
+                                         int(page_size), _ptr(row_to_batch), _ptr(out), _stream())
+    _lib.check("topk_page_transform", st)
+    return out
+
+
+def _indexer_args(q, q_scale, w, kcache, k_scale, block_table, seq_lens):
+    _need(q, "q", _F8, 3)
+    _need(q_scale, "q_scale", (torch.float32,), 1)
+    _need(w, "w", (torch.float32,), 2)
+    _need(kcache, "kcache", _F8, 2)
+    _need(k_scale, "k_scale", (torch.float32,), 1)
+    _need(block_table, "block_table", (torch.int32,), 2, contiguous=False)
+    if block_table.stride(1) != 1:
+        raise ValueError("block_table rows must be contiguous")
+    _need(seq_lens, "seq_lens", (torch.int32,), 1)
+    B, H, D = q.shape
+    return [_ptr(_as_u8(q)), _ptr(q_scale), _ptr(w), _ptr(_as_u8(kcache)), _ptr(k_scale),
+            _ptr(block_table), block_table.stride(0)], B, H, D
+
+
+def idx_score_fp8(q, q_scale, w, kcache, k_scale, block_table, seq_lens, page_size: int,
+                  max_seq_len: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Index scores S[b, j] for j < seq_lens[b] (other cells of `out` untouched)."""
+    args, B, H, D = _indexer_args(q, q_scale, w, kcache, k_scale, block_table, seq_lens)
+    if out is None:
+        out = torch.full((B, max(1, max_seq_len)), float("nan"), dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,), 2, contiguous=False)
+    st = _lib.load().idx_score_fp8(*args, int(page_size), _ptr(seq_lens), B, H, D, int(max_seq_len),
+                                   _ptr(out), out.stride(0), _stream())
+    _lib.check("idx_score_fp8", st)
+    return out
+
+
+def idx_score_topk_fused(q, q_scale, w, kcache, k_scale, block_table, seq_lens, page_size: int,
+                         max_seq_len: int, k: int, return_scores: bool = False,
+                         workspace: Optional[Workspace] = None, out: Optional[torch.Tensor] = None,
+                         out_scores: Optional[torch.Tensor] = None):
+    """Fused decode indexer: top-k slots per row (and their scores if asked)."""
+    args, B, H, D = _indexer_args(q, q_scale, w, kcache, k_scale, block_table, seq_lens)
+    if out is None:
+        out = torch.empty((B, k), dtype=torch.int32, device=q.device)
+    if return_scores and out_scores is None:
+        out_scores = torch.empty((B, k), dtype=torch.float32, device=q.device)
+    nbytes = workspace_bytes(_lib.OP_SCORE_TOPK_FUSED, B, k, max_seq_len)
+    ws = _workspace(workspace).get(nbytes)
+    st = _lib.load().idx_score_topk_fused(*args, int(page_size), _ptr(seq_lens), B, H, D,
+                                          int(max_seq_len), int(k), _ptr(out), _ptr(out_scores),
+                                          _ptr(ws), ws.numel(), _stream())
+    _lib.check("idx_score_topk_fused", st)
+    return (out, out_scores) if return_scores else out
+
+
+def block_topk(q, q_scale, w, kcache, k_scale, block_table, seq_lens, page_size: int,
+               max_seq_len: int, block_size: int, top_blocks: int, return_slots: bool = True,
+               workspace: Optional[Workspace] = None):
+    """Top blocks per row as physical block ids (and expanded slot lists)."""
+    args, B, H, D = _indexer_args(q, q_scale, w, kcache, k_scale, block_table, seq_lens)
+    out_blocks = torch.empty((B, top_blocks), dtype=torch.int32, device=q.device)
+    out_slots = (torch.empty((B, top_blocks * block_size), dtype=torch.int32, device=q.device)
+                 if return_slots else None)
+    nbytes = workspace_bytes(_lib.OP_BLOCK_TOPK, B, block_size, max_seq_len)
+    ws = _workspace(workspace).get(nbytes)
+    st = _lib.load().block_topk(*args, int(page_size), _ptr(seq_lens), B, H, D, int(max_seq_len),
+                                int(block_size), int(top_blocks), _ptr(out_blocks), _ptr(out_slots),
+                                _ptr(ws), ws.numel(), _stream())
+    _lib.check("block_topk", st)
+    return (out_blocks, out_slots) if return_slots else out_blocks

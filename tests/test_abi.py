@@ -1,0 +1,161 @@
+"""The C-ABI library loads, exports what include/idxtopk.h declares, and rejects
+bad arguments on the host (every call here returns before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "idxtopk.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def _defines():
+    out = {}
+    for m in re.finditer(r"#define\s+(IDXTOPK_[A-Z0-9_]+)\s+\(?(-?\d+)\)?", open(HEADER).read()):
+        out[m.group(1)] = int(m.group(2))
+    return out
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from sparse_attention_indexer_fp8_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from sparse_attention_indexer_fp8_amd import build
+        build.build()
+    return _lib.load()
+
+
+def test_header_declares_the_five_ops():
+    names = _declared_functions()
+    for op in ("idx_score_fp8", "topk_rows", "idx_score_topk_fused", "topk_page_transform", "block_topk"):
+        assert op in names
+    assert {"idxtopk_workspace_bytes", "idxtopk_status_str", "idxtopk_version"} <= set(names)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from sparse_attention_indexer_fp8_amd import _lib
+    names = _declared_functions()
+    assert set(names) == set(_lib.SIGNATURES)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_codes_and_version(lib):
+    d = _defines()
+    from sparse_attention_indexer_fp8_amd import _lib
+    assert (d["IDXTOPK_OK"], d["IDXTOPK_EINVAL"], d["IDXTOPK_EUNSUPPORTED"], d["IDXTOPK_EWORKSPACE"],
+            d["IDXTOPK_ELAUNCH"]) == (_lib.IDXTOPK_OK, _lib.IDXTOPK_EINVAL, _lib.IDXTOPK_EUNSUPPORTED,
+                                      _lib.IDXTOPK_EWORKSPACE, _lib.IDXTOPK_ELAUNCH)
+    assert lib.idxtopk_version() == d["IDXTOPK_VERSION"]
+    texts = {lib.idxtopk_status_str(s).decode() for s in (0, -1, -2, -3, -4, 7)}
+    assert len(texts) == 6
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails host validation
+NULL = None
+
+
+def _topk_rows(lib, **kw):
+    a = dict(scores=FAKE, stride=4096, rows=8, seq_lens=FAKE, rs=NULL, r2b=NULL, pt=NULL, pts=0, P=1,
+             k=512, out=FAKE)
+    a.update(kw)
+    return lib.topk_rows(a["scores"], a["stride"], a["rows"], a["seq_lens"], a["rs"], a["r2b"], a["pt"],
+                         a["pts"], a["P"], a["k"], a["out"], NULL)
+
+
+def test_topk_rows_validation(lib):
+    assert _topk_rows(lib, rows=-1) == -1
+    assert _topk_rows(lib, k=0) == -1
+    assert _topk_rows(lib, stride=-5) == -1
+    assert _topk_rows(lib, scores=NULL) == -1
+    assert _topk_rows(lib, seq_lens=NULL) == -1
+    assert _topk_rows(lib, out=NULL) == -1
+    assert _topk_rows(lib, pt=FAKE, P=0) == -1
+    assert _topk_rows(lib, pt=FAKE, pts=-1) == -1
+    assert _topk_rows(lib, k=8193) == -2
+    assert _topk_rows(lib, rows=0) == 0  # nothing to do, nothing enqueued
+
+
+def test_page_transform_validation(lib):
+    f = lib.topk_page_transform
+    assert f(FAKE, -1, 4, FAKE, 10, 1, NULL, FAKE, NULL) == -1
+    assert f(FAKE, 2, 0, FAKE, 10, 1, NULL, FAKE, NULL) == -1
+    assert f(FAKE, 2, 4, FAKE, 10, 0, NULL, FAKE, NULL) == -1
+    assert f(NULL, 2, 4, FAKE, 10, 1, NULL, FAKE, NULL) == -1
+    assert f(FAKE, 2, 4, NULL, 10, 1, NULL, FAKE, NULL) == -1
+    assert f(FAKE, 0, 4, FAKE, 10, 1, NULL, FAKE, NULL) == 0
+
+
+def _indexer(**kw):
+    a = dict(q=FAKE, qs=FAKE, w=FAKE, kc=FAKE, ks=FAKE, bt=FAKE, bts=256, P=64, sl=FAKE, B=32, H=64, D=128,
+             msl=16384)
+    a.update(kw)
+    return [a["q"], a["qs"], a["w"], a["kc"], a["ks"], a["bt"], a["bts"], a["P"], a["sl"], a["B"], a["H"],
+            a["D"], a["msl"]]
+
+
+def test_score_validation(lib):
+    f = lambda out=FAKE, ss=16384, **kw: lib.idx_score_fp8(*_indexer(**kw), out, ss, NULL)
+    assert f(D=64) == -2
+    assert f(H=48) == -2
+    assert f(H=0) == -1
+    assert f(P=0) == -1
+    assert f(q=NULL) == -1
+    assert f(kc=NULL) == -1
+    assert f(out=NULL) == -1
+    assert f(ss=100) == -1          # max_seq_len beyond the score row
+    assert f(bts=10) == -1          # block table too narrow for max_seq_len
+    assert f(B=0) == 0
+
+
+def test_fused_validation_and_workspace(lib):
+    need = lib.idxtopk_workspace_bytes(4, 32, 2048, 16384)
+    assert need > 32 * 16384 * 8
+    f = lambda k=2048, out=FAKE, ws=FAKE, nb=need, **kw: lib.idx_score_topk_fused(
+        *_indexer(**kw), k, out, NULL, ws, nb, NULL)
+    assert f(k=0) == -1
+    assert f(k=8193) == -2
+    assert f(out=NULL) == -1
+    assert f(ws=NULL) == -3
+    assert f(nb=need - 1) == -3
+    assert f(D=256) == -2
+    assert f(B=0) == 0
+
+
+def test_block_validation(lib):
+    need = lib.idxtopk_workspace_bytes(5, 32, 128, 32768)
+    assert need >= 32 * 256 * 4
+    f = lambda bs=128, top=32, out=FAKE, ws=FAKE, nb=need, **kw: lib.block_topk(
+        *_indexer(**{"P": 128, "msl": 32768, "bts": 256, **kw}), bs, top, out, NULL, ws, nb, NULL)
+    assert f(bs=64) == -2          # block size must equal page size
+    assert f(top=0) == -1
+    assert f(top=5000) == -2
+    assert f(out=NULL) == -1
+    assert f(nb=need - 1) == -3
+    assert f(B=0) == 0
+
+
+def test_workspace_bytes_rules(lib):
+    wb = lib.idxtopk_workspace_bytes
+    assert wb(1, 8, 512, 4096) == 0          # topk_rows needs none
+    assert wb(3, 8, 512, 4096) == 0
+    assert wb(4, -1, 2048, 100) == 0
+    assert wb(4, 64, 2048, 327680) >= 64 * 327680 * 8
+    assert wb(4, 64, 2048, 327680) > wb(4, 32, 2048, 327680)
+    assert wb(5, 64, 0, 32768) == 0
+
+
+def test_binding_imports_without_gpu():
+    import sparse_attention_indexer_fp8_amd as pkg
+    from sparse_attention_indexer_fp8_amd import ops
+
+    assert pkg.topk_rows is ops.topk_rows and pkg.ops is ops

@@ -1,0 +1,244 @@
+"""GPU parity of idx_score_fp8, idx_score_topk_fused and block_topk against the oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from oracle.indexer import case_scores
+from tests._helpers import check_fused_row, check_scores, dev, log, rms
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops():
+    import torch
+    from sparse_attention_indexer_fp8_amd import ops as _ops
+
+    torch.cuda.set_device(0)
+    return _ops
+
+
+def _inputs(case):
+    return (dev(case.q), dev(case.q_scale), dev(case.w), dev(case.kcache), dev(case.k_scale),
+            dev(case.block_table), dev(case.seq_lens))
+
+
+def _fused(ops, case, k=None, ws=None):
+    import torch
+
+    slots, sc = ops.idx_score_topk_fused(*_inputs(case), case.page_size, case.max_seq_len,
+                                         case.k if k is None else k, return_scores=True, workspace=ws)
+    torch.cuda.synchronize()
+    return slots.cpu().numpy(), sc.cpu().numpy()
+
+
+def _lens(seed, batch, n_lo, n_hi, first=()):
+    lens = workloads.rng(seed, workloads.synth.STREAM_LEN).integers(n_lo, n_hi + 1, size=batch).astype(np.int32)
+    lens[:len(first)] = first
+    return lens
+
+
+def _exact_case(seed, batch, n_lo, n_hi, page_size, heads=16, k=64, first=(), **kw):
+    """Inputs whose fp32 scores are exact: codes of +-0.5, +-1, +-2 and 0, unit
+    scales, power-of-two weights. Every product and partial sum is a multiple of
+    1/4 below 2^10, so the GPU's fp32 scores equal the oracle's float64 ones
+    and the selected sets must agree exactly, ties included."""
+    case = workloads.indexer_case(seed, batch=batch, n_lo=n_lo, n_hi=n_hi, page_size=page_size, k=k,
+                                  heads=heads, fixed_lens=_lens(seed, batch, n_lo, n_hi, first), **kw)
+    g = np.random.default_rng(seed + 1000)
+    codes = np.array([0x00, 0x30, 0x38, 0x40, 0xB0, 0xB8, 0xC0], np.uint8)
+    case.q[:] = g.choice(codes, size=case.q.shape)
+    case.q_scale[:] = 1.0
+    case.w[:] = g.choice(np.array([0.5, 1.0, 2.0, -1.0], np.float32), size=case.w.shape)
+    real = case.k_scale < workloads.SENTINEL_KEY_SCALE
+    case.kcache[real] = g.choice(codes, size=(int(real.sum()), case.dim))
+    case.k_scale[real] = 1.0
+    return case
+
+
+@pytest.mark.parametrize("heads", [16, 32, 64, 128])
+@pytest.mark.parametrize("page_size", [1, 16, 48, 64])
+def test_score_tolerance(ops, heads, page_size):
+    import torch
+
+    seed = 200 + heads + page_size
+    case = workloads.indexer_case(seed, batch=3, n_lo=1, n_hi=3000, page_size=page_size, k=64, heads=heads,
+                                  fixed_lens=_lens(seed, 3, 1, 3000, first=(1,)))
+    out = ops.idx_score_fp8(*_inputs(case), case.page_size, case.max_seq_len)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    rows = [case_scores(case, b) for b in range(case.batch)]
+    bsig = rms(np.concatenate(rows))
+    for b in range(case.batch):
+        n = int(case.seq_lens[b])
+        check_scores(out[b, :n], rows[b], bsig)
+        assert np.isnan(out[b, n:]).all(), "cells past n_b must stay untouched"
+
+
+def test_score_exact_values(ops):
+    import torch
+
+    case = _exact_case(301, batch=2, n_lo=500, n_hi=2000, page_size=64)
+    out = ops.idx_score_fp8(*_inputs(case), case.page_size, case.max_seq_len)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    for b in range(case.batch):
+        n = int(case.seq_lens[b])
+        assert np.array_equal(out[b, :n].astype(np.float64), case_scores(case, b))
+
+
+@pytest.mark.parametrize("page_size,heads,k", [(64, 64, 64), (16, 16, 200), (1, 32, 300), (48, 64, 1000),
+                                               (128, 128, 100)])
+def test_fused_exact_sets(ops, page_size, heads, k):
+    """Exact arithmetic: the fused selection equals the oracle's set exactly
+    (heavy ties are resolved toward the lower position)."""
+    case = _exact_case(400 + page_size, batch=5, n_lo=1, n_hi=12000, page_size=page_size, heads=heads, k=k,
+                       first=(0, k - 1, k))
+    slots, sc = _fused(ops, case)
+    ref_slots, ref_pos, scores = oracle.fused_topk(case)
+    for b in range(case.batch):
+        assert np.array_equal(np.sort(slots[b]), np.sort(ref_slots[b])), b
+        m = min(int(case.seq_lens[b]), k)
+        got_s = np.sort(sc[b][:m].astype(np.float64))
+        exp_s = np.sort(scores[b][ref_pos[b][:m]]) if m else np.zeros(0)
+        assert np.array_equal(got_s, exp_s)
+
+
+@pytest.mark.parametrize("page_size,k,n_lo,n_hi", [(64, 2048, 1, 20000), (64, 256, 3000, 40000),
+                                                   (16, 512, 100, 9000), (100, 64, 1, 500)])
+def test_fused_tolerance_random(ops, page_size, k, n_lo, n_hi):
+    case = workloads.indexer_case(500 + k, batch=6, n_lo=n_lo, n_hi=n_hi, page_size=page_size, k=k)
+    slots, sc = _fused(ops, case)
+    rows = [case_scores(case, b) for b in range(case.batch)]
+    bsig = rms(np.concatenate(rows))
+    for b in range(case.batch):
+        n = int(case.seq_lens[b])
+        ts = oracle.token_slots(case.block_table[b], case.page_size, n)
+        ov = check_fused_row(slots[b], sc[b], rows[b], ts, k, batch_sigma=bsig)
+        log(f"row {b} n={n} overlap={ov:.4f}")
+
+
+def test_fused_workspace_reuse_smaller_second_call(ops):
+    """The workspace is left zeroed: a second call with a smaller input is exact."""
+    from sparse_attention_indexer_fp8_amd import ops as o
+
+    ws = o.Workspace()
+    big = _exact_case(601, batch=8, n_lo=5000, n_hi=30000, page_size=64, k=500)
+    small = _exact_case(602, batch=3, n_lo=100, n_hi=3000, page_size=64, k=500)
+    for case in (big, small, big):
+        slots, _ = _fused(ops, case, ws=ws)
+        ref, _, _ = oracle.fused_topk(case)
+        assert np.array_equal(np.sort(slots, axis=1), np.sort(ref, axis=1))
+
+
+def test_fused_never_reads_outside_windows(ops):
+    """Sentinel keys (+448, scale 1e3) fill every slot no row owns; selecting
+    one of them would map to no token of the row and fail the inverse map."""
+    case = workloads.indexer_case(701, batch=4, n_lo=1, n_hi=700, page_size=64, k=128)
+    slots, sc = _fused(ops, case)
+    rows = [case_scores(case, b) for b in range(case.batch)]
+    bsig = rms(np.concatenate(rows))
+    for b in range(case.batch):
+        n = int(case.seq_lens[b])
+        ts = oracle.token_slots(case.block_table[b], case.page_size, n)
+        check_fused_row(slots[b], sc[b], rows[b], ts, case.k, batch_sigma=bsig)
+
+
+@pytest.mark.parametrize("bs,top", [(128, 32), (64, 5), (16, 40)])
+def test_block_exact(ops, bs, top):
+    import torch
+
+    case = _exact_case(800 + bs, batch=5, n_lo=1, n_hi=9000, page_size=bs, k=0, block_size=bs, top_blocks=top,
+                       first=(0, bs * top - 5, bs * top + 1))
+    blocks, slots = ops.block_topk(*_inputs(case), case.page_size, case.max_seq_len, bs, top)
+    torch.cuda.synchronize()
+    blocks, slots = blocks.cpu().numpy(), slots.cpu().numpy()
+    rb, rs, rl, _ = oracle.block_topk(case)
+    for b in range(case.batch):
+        assert np.array_equal(np.sort(blocks[b]), np.sort(rb[b])), b
+        # slot lists: compare per selected block
+        got = {int(blocks[b, i]): slots[b, i * bs:(i + 1) * bs].tolist() for i in range(top) if blocks[b, i] >= 0}
+        exp = {int(rb[b, i]): rs[b, i * bs:(i + 1) * bs].tolist() for i in range(top) if rb[b, i] >= 0}
+        assert got == exp
+        assert (slots[b, len(got) * bs:] == -1).all()
+
+
+def test_block_random_tolerance(ops):
+    """Random fp8 inputs: every chosen block's oracle block score is within tol
+    of the oracle's top-th block score."""
+    import torch
+
+    bs, top = 128, 32
+    case = workloads.indexer_case(900, batch=6, n_lo=bs, n_hi=40000, page_size=bs, k=0, block_size=bs,
+                                  top_blocks=top)
+    blocks = ops.block_topk(*_inputs(case), case.page_size, case.max_seq_len, bs, top, return_slots=False)
+    torch.cuda.synchronize()
+    blocks = blocks.cpu().numpy()
+    for b in range(case.batch):
+        S = case_scores(case, b)
+        bsv = oracle.block_scores(S, bs)
+        nb = bsv.shape[0]
+        m = min(nb, top)
+        page_to_blk = {int(case.block_table[b, c]): c for c in range(nb)}
+        sel = [page_to_blk[int(p)] for p in blocks[b, :m]]
+        assert len(set(sel)) == m and (blocks[b, m:] == -1).all()
+        sigma = float(np.sqrt(np.mean(S * S)))
+        kth = np.sort(bsv)[::-1][m - 1]
+        assert (bsv[sel] >= kth - 1e-3 * max(abs(kth), sigma)).all()
+
+
+def _sampled_full(case, rows):
+    return {b: case_scores(case, b) for b in rows}
+
+
+def test_fused_decode_full_size(ops):
+    """Full-size fused decode (B=32, n in [8192, 16384], k=2048): every row."""
+    case = workloads.c2_fused_decode()
+    log(f"case {case.name}")
+    slots, sc = _fused(ops, case)
+    for b in range(case.batch):
+        n = int(case.seq_lens[b])
+        ts = oracle.token_slots(case.block_table[b], case.page_size, n)
+        check_fused_row(slots[b], sc[b], case_scores(case, b), ts, case.k)
+
+
+def test_long_decode_full_size_sampled(ops):
+    """Full-size long-context decode (B=64, n up to 327680): sampled rows."""
+    case = workloads.c5_long_decode()
+    log(f"case {case.name} tokens={workloads.expected_tokens(case)}")
+    slots, sc = _fused(ops, case)
+    longest = int(np.argmax(case.seq_lens))
+    shortest = int(np.argmin(case.seq_lens))
+    for b in sorted({0, 31, 63, longest, shortest}):
+        n = int(case.seq_lens[b])
+        ts = oracle.token_slots(case.block_table[b], case.page_size, n)
+        ov = check_fused_row(slots[b], sc[b], case_scores(case, b), ts, case.k)
+        log(f"row {b} n={n} overlap={ov:.4f}")
+    # every row: count / distinct / padding properties
+    for b in range(case.batch):
+        assert (slots[b] >= 0).all() and np.unique(slots[b]).shape[0] == case.k
+
+
+def test_block_sparse_full_size(ops):
+    import torch
+
+    case = workloads.c4_block_sparse()
+    log(f"case {case.name}")
+    blocks, slots = ops.block_topk(*_inputs(case), case.page_size, case.max_seq_len, case.block_size,
+                                   case.top_blocks)
+    torch.cuda.synchronize()
+    blocks, slots = blocks.cpu().numpy(), slots.cpu().numpy()
+    bs, top = case.block_size, case.top_blocks
+    for b in (0, 17, 63):
+        S = case_scores(case, b)
+        bsv = oracle.block_scores(S, bs)
+        page_to_blk = {int(case.block_table[b, c]): c for c in range(bsv.shape[0])}
+        sel = [page_to_blk[int(p)] for p in blocks[b]]
+        sigma = float(np.sqrt(np.mean(S * S)))
+        kth = np.sort(bsv)[::-1][top - 1]
+        assert len(set(sel)) == top
+        assert (bsv[sel] >= kth - 1e-3 * max(abs(kth), sigma)).all()
+        for i, c in enumerate(sel):
+            exp = int(case.block_table[b, c]) * bs + np.arange(bs)
+            assert np.array_equal(slots[b, i * bs:(i + 1) * bs], exp)

@@ -1,0 +1,217 @@
+"""GPU parity of topk_rows / topk_page_transform against the oracle (bit-exact sets)."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests._helpers import dev, expected_set_fast, log, sorted_rows
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def ops():
+    import torch
+    from sparse_attention_indexer_fp8_amd import ops as _ops
+
+    torch.cuda.set_device(0)
+    return _ops
+
+
+def _run_rows(ops, scores, seq_lens, k, row_starts=None, row_to_batch=None, page_table=None, page_size=1):
+    import torch
+
+    out = ops.topk_rows(dev(scores), dev(seq_lens), k,
+                        None if row_starts is None else dev(row_starts),
+                        None if row_to_batch is None else dev(row_to_batch),
+                        None if page_table is None else dev(page_table), page_size)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _hand_cases():
+    with open(os.path.join(GOLDEN, "topk_hand_cases.json")) as f:
+        return json.load(f)["cases"]
+
+
+def test_hand_built_cases(ops):
+    for c in _hand_cases():
+        vals = np.array([float(v) for v in c["values"]], dtype=np.float32)
+        n = vals.shape[0]
+        buf = np.full((1, max(n, 1) + 3), np.inf, np.float32)
+        buf[0, :n] = vals
+        got = _run_rows(ops, buf, np.array([n], np.int32), c["k"])
+        assert sorted(got[0].tolist()) == sorted(c["expected"]), c["name"]
+
+
+def test_decode_c1_full(ops):
+    case = workloads.c1_decode_topk()
+    log(f"case {case.name}")
+    got = _run_rows(ops, case.scores, case.seq_lens, case.k, page_table=case.page_table)
+    ref = oracle.topk_rows(case.scores, case.seq_lens, case.k, page_table=case.page_table)
+    assert np.array_equal(sorted_rows(got), sorted_rows(ref))
+    # row-local positions too (no page table)
+    got = _run_rows(ops, case.scores, case.seq_lens, case.k)
+    ref = oracle.topk_rows(case.scores, case.seq_lens, case.k)
+    assert np.array_equal(sorted_rows(got), sorted_rows(ref))
+
+
+@pytest.mark.parametrize("k", [1, 7, 64, 512, 2048])
+def test_decode_rows_many_tiles(ops, k):
+    """Rows spanning several 4096-float tiles, ragged tails, n around k."""
+    case = workloads.decode_rows_case(seed=31 + k, rows=24, stride=20011, n_lo=max(1, k - 3), n_hi=20011,
+                                      k=k, tie_frac=0.05, pt_width=20011)
+    case.seq_lens[:4] = [k - 1 if k > 1 else 1, k, k + 1, 20011]
+    log(f"decode rows k={k}")
+    got = _run_rows(ops, case.scores, case.seq_lens, k, page_table=case.page_table)
+    ref = oracle.topk_rows(case.scores, case.seq_lens, k, page_table=case.page_table)
+    assert np.array_equal(sorted_rows(got), sorted_rows(ref))
+
+
+def test_packed_prefill_reduced(ops):
+    """Packed extend layout with an odd stride and both indirections."""
+    case = workloads.packed_prefill_case(seed=41, prefix0=9000, new_tokens=256, k=512)
+    log(f"packed reduced stride={case.stride}")
+    got = _run_rows(ops, case.scores, case.seq_lens, case.k, case.row_starts, case.row_to_batch,
+                    case.page_table, 1)
+    ref = oracle.topk_rows(case.scores, case.seq_lens, case.k, case.row_starts, case.row_to_batch,
+                           case.page_table, 1)
+    assert np.array_equal(sorted_rows(got), sorted_rows(ref))
+
+
+def test_packed_equals_row_local_on_gpu(ops):
+    case = workloads.packed_prefill_case(seed=42, prefix0=5000, new_tokens=128, k=256)
+    packed = _run_rows(ops, case.scores, case.seq_lens, case.k, case.row_starts, case.row_to_batch,
+                       case.page_table, 1)
+    n_max = int(case.seq_lens.max())
+    local = np.full((case.rows, n_max), np.inf, np.float32)
+    pt_local = np.empty((case.rows, case.page_table.shape[1]), np.int32)
+    for i in range(case.rows):
+        rs, n = int(case.row_starts[i]), int(case.seq_lens[i])
+        local[i, :n] = case.scores[i, rs:rs + n]
+        pt_local[i] = case.page_table[case.row_to_batch[i]]
+    row_local = _run_rows(ops, local, case.seq_lens, case.k, page_table=pt_local)
+    assert np.array_equal(sorted_rows(packed), sorted_rows(row_local))
+
+
+def _adversarial_rows(n=30000):
+    rows = {}
+    g = np.random.default_rng(5)
+    rows["ascending"] = np.arange(n, dtype=np.float32)  # every tile beats the last: many compactions
+    rows["descending"] = np.arange(n, 0, -1, dtype=np.float32)
+    rows["all_equal"] = np.full(n, 3.25, np.float32)
+    v = np.full(n, -1.0, np.float32)
+    v[g.choice(n, 700, replace=False)] = (np.arange(1, 701) * 1.401298464324817e-45).astype(np.float32)
+    z = g.choice(n, 4000, replace=False)
+    v[z[:2000]] = 0.0
+    v[z[2000:]] = -0.0
+    rows["denormal_threshold"] = v
+    w = np.where(g.random(n) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+    rows["signed_zeros_only"] = w
+    x = g.standard_normal(n).astype(np.float32)
+    x[g.choice(n, 50, replace=False)] = np.inf
+    x[g.choice(n, 50, replace=False)] = -np.inf
+    rows["with_infinities"] = x
+    y = np.round(g.standard_normal(n) * 2).astype(np.float32)  # few distinct values, heavy ties
+    rows["coarse_ties"] = y
+    return rows
+
+
+@pytest.mark.parametrize("k", [512, 2048])
+def test_adversarial_rows(ops, k):
+    rows = _adversarial_rows()
+    names = list(rows)
+    n = 30000
+    buf = np.stack([rows[nm] for nm in names])
+    lens = np.full(len(names), n, np.int32)
+    got = _run_rows(ops, buf, lens, k)
+    ref = oracle.topk_rows(buf, lens, k)
+    for i, nm in enumerate(names):
+        assert np.array_equal(np.sort(got[i]), np.sort(ref[i])), nm
+
+
+def test_max_k(ops):
+    case = workloads.decode_rows_case(seed=77, rows=6, stride=40000, n_lo=8000, n_hi=40000, k=8192,
+                                      pt_width=40000)
+    got = _run_rows(ops, case.scores, case.seq_lens, 8192, page_table=case.page_table)
+    ref = oracle.topk_rows(case.scores, case.seq_lens, 8192, page_table=case.page_table)
+    assert np.array_equal(sorted_rows(got), sorted_rows(ref))
+
+
+def test_empty_and_tiny_rows(ops):
+    buf = np.full((5, 16), np.inf, np.float32)
+    buf[1, :1] = 5.0
+    buf[2, :3] = [1.0, -2.0, 3.0]
+    buf[3, :16] = np.arange(16)
+    buf[4, :5] = [2.0, 2.0, 2.0, 2.0, 2.0]
+    lens = np.array([0, 1, 3, 16, 5], np.int32)
+    got = _run_rows(ops, buf, lens, 4)
+    ref = oracle.topk_rows(buf, lens, 4)
+    assert np.array_equal(sorted_rows(got), sorted_rows(ref))
+
+
+def test_page_sizes_and_transform(ops):
+    """General page sizes (including non powers of two) in the fused epilogue
+    and in the standalone transform."""
+    import torch
+
+    g = np.random.default_rng(9)
+    for P in (1, 3, 16, 48, 64, 100):
+        rows, k, n_hi = 6, 300, 9000
+        case = workloads.decode_rows_case(seed=90 + P, rows=rows, stride=n_hi, n_lo=100, n_hi=n_hi, k=k,
+                                          pt_width=4)
+        npg = -(-n_hi // P)
+        pt = np.stack([g.permutation(npg * 3)[:npg] for _ in range(rows)]).astype(np.int32)
+        got = _run_rows(ops, case.scores, case.seq_lens, k, page_table=pt, page_size=P)
+        ref = oracle.topk_rows(case.scores, case.seq_lens, k, page_table=pt, page_size=P)
+        assert np.array_equal(sorted_rows(got), sorted_rows(ref)), P
+        # standalone transform of the oracle's row-local positions
+        pos = oracle.topk_rows(case.scores, case.seq_lens, k).astype(np.int32)
+        r2b = g.integers(0, rows, size=rows).astype(np.int32)
+        out = ops.topk_page_transform(dev(pos), dev(pt), P, dev(r2b))
+        torch.cuda.synchronize()
+        exp = np.stack([oracle.page_transform(pos[i], pt[r2b[i]], P) for i in range(rows)])
+        assert np.array_equal(out.cpu().numpy(), exp), P
+
+
+def test_deterministic_sets(ops):
+    case = workloads.packed_prefill_case(seed=43, prefix0=3000, new_tokens=64, k=128)
+    a = _run_rows(ops, case.scores, case.seq_lens, case.k, case.row_starts, case.row_to_batch)
+    b = _run_rows(ops, case.scores, case.seq_lens, case.k, case.row_starts, case.row_to_batch)
+    assert np.array_equal(sorted_rows(a), sorted_rows(b))
+
+
+def test_packed_prefill_full_size(ops):
+    """The full 16384 x 70001 packed buffer, in the launch configuration the
+    benchmark times. Every row is checked against an O(n) exact set
+    computation; a sample of rows also against the oracle's full sort."""
+    import torch
+
+    log("generating packed-prefill 16384x70001")
+    case = workloads.c3_packed_prefill()
+    sc = dev(case.scores)
+    out = ops.topk_rows(sc, dev(case.seq_lens), case.k, dev(case.row_starts), dev(case.row_to_batch),
+                        dev(case.page_table), 1)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.int64)
+    del sc
+    inv = []
+    for r in range(2):  # slot -> row-local position of each request's table
+        m = np.full(int(case.page_table.max()) + 1, -1, np.int64)
+        m[case.page_table[r]] = np.arange(case.page_table.shape[1])
+        inv.append(m)
+    log("checking all rows")
+    for i in range(case.rows):
+        rs, n, p = int(case.row_starts[i]), int(case.seq_lens[i]), int(case.row_to_batch[i])
+        row = got[i]
+        pos = np.sort(np.where(row >= 0, inv[p][np.maximum(row, 0)], -1))
+        assert np.array_equal(pos, expected_set_fast(case.scores[i, rs:rs + n], case.k)), i
+    sample = [0, 1, 2, 4095, 8190, 8191, 8192, 8193, 8700, 12000, 16383]
+    ref = oracle.topk_rows(case.scores, case.seq_lens, case.k, case.row_starts, case.row_to_batch,
+                           case.page_table, 1, rows=sample)
+    assert np.array_equal(sorted_rows(got[sample]), sorted_rows(ref))
