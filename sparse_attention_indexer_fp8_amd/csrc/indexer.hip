@@ -308,13 +308,15 @@ __global__ __launch_bounds__(MG_WG) void fused_merge_kernel(IndexerArgs a, Fused
           nvk = e + 1;
         }
       }
-      const uint64_t T = wg_radix_select<MG_WG>(
+      // (the select histogram overlays the buffer, now held in registers)
+      __syncthreads();
+      const uint64_t T = wg_select<MG_WG>(
           [&](auto&& f) {
 #pragma unroll
             for (int e = 0; e < MG_MAXE; ++e)
               if (e < nvk) f(keys[e]);
           },
-          need, s.sel);
+          need, reinterpret_cast<uint32_t*>(s.buf), s.sel);
 #pragma unroll
       for (int e = 0; e < MG_MAXE; ++e) emit_keys(e < nvk && keys[e] >= T, keys[e], a, b, o, &s.ocnt);
     } else {
@@ -326,7 +328,7 @@ __global__ __launch_bounds__(MG_WG) void fused_merge_kernel(IndexerArgs a, Fused
           if ((rank_vkey(key) >> HIST_SHIFT) == bstar) f(key);
         }
       };
-      const uint64_t T = wg_radix_select<MG_WG>(each_mid, need, s.sel);
+      const uint64_t T = wg_select<MG_WG>(each_mid, need, reinterpret_cast<uint32_t*>(s.buf), s.sel);
       for (uint32_t i0 = 0; i0 < ncand; i0 += MG_WG) {
         const uint32_t i = i0 + tid;
         uint64_t key = 0;
@@ -420,7 +422,9 @@ __global__ __launch_bounds__(MG_WG) void block_merge_kernel(IndexerArgs a, Block
     auto each = [&](auto&& f) {
       for (int cb = tid; cb < nblk; cb += MG_WG) f(rank_key(bsc[cb], static_cast<uint32_t>(cb)));
     };
-    const uint64_t T = wg_radix_select<MG_WG>(each, static_cast<uint32_t>(top), s.sel);
+    // (the select histogram overlays sel_blocks, written only afterwards)
+    const uint64_t T = wg_select<MG_WG>(each, static_cast<uint32_t>(top),
+                                        reinterpret_cast<uint32_t*>(s.sel_blocks), s.sel);
     for (int c0 = 0; c0 < nblk; c0 += MG_WG) {
       const int cb = c0 + tid;
       const bool keep = cb < nblk && rank_key(bsc[cb], static_cast<uint32_t>(cb)) >= T;

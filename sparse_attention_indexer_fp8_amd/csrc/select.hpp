@@ -1,68 +1,174 @@
-// Workgroup-level exact selection primitives (LDS radix select, threshold bins).
+// Workgroup-level exact selection primitives (adaptive-bin select, threshold bins).
 #pragma once
 
 #include "common.hpp"
 
 namespace idxtopk {
 
-// LDS scratch for wg_radix_select: 256 histogram bins + 4 broadcast words.
+// ---------------------------------------------------------------------------
+// Exact selection over distinct 64-bit keys
+// ---------------------------------------------------------------------------
+
+constexpr int kSelBins = 1024;    // histogram bins of one select iteration
+constexpr int kSelMembers = 64;   // threshold-bin size a single wave resolves
+
+// LDS scratch of wg_select. The histogram (kSelBins words) is passed apart.
 struct SelectLds {
-  uint32_t hist[256];
+  uint64_t red[2][16];
+  uint64_t members[kSelMembers];
+  uint64_t result;
+  uint32_t part[16];
   uint32_t bcast[4];
+  uint32_t mcnt;
 };
 
-// Exact k-th largest of a set of DISTINCT 64-bit keys spread over the
-// workgroup. `for_each(f)` must call f(key) once for every key this thread
-// owns, the same set on every call. Precondition: the set holds more than k
-// keys, and k >= 1.
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+  const uint32_t hi = static_cast<uint32_t>(v >> 32), lo = static_cast<uint32_t>(v);
+  const uint32_t mhi = __reduce_min_sync(~0ull, hi);
+  const uint32_t mlo = __reduce_min_sync(~0ull, hi == mhi ? lo : 0xffffffffu);
+  return (static_cast<uint64_t>(mhi) << 32) | mlo;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  const uint32_t hi = static_cast<uint32_t>(v >> 32), lo = static_cast<uint32_t>(v);
+  const uint32_t mhi = __reduce_max_sync(~0ull, hi);
+  const uint32_t mlo = __reduce_max_sync(~0ull, hi == mhi ? lo : 0u);
+  return (static_cast<uint64_t>(mhi) << 32) | mlo;
+}
+
+// Inclusive prefix sum across the wave with DPP row shifts and row
+// broadcasts (no LDS traffic).
+__device__ __forceinline__ uint32_t wave_prefix_incl(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+// k-th largest of a set of DISTINCT 64-bit keys spread over the workgroup.
+// `for_each(f)` must call f(key) once for every key this thread owns, the
+// same set on every call. Precondition: the set holds more than k keys, k >= 1.
+// `hist` is LDS of kSelBins words.
 //
-// Returns T such that exactly k keys are >= T (T is the shortest digit prefix
-// that separates them, so it need not be one of the keys). MSB-first radix
-// select over 8-bit digits: each pass histograms the keys that still match
-// the prefix, then finds the digit where the count from the top reaches the
-// remaining rank. Stops as soon as the keys matching the prefix are exactly
-// the ones still needed.
+// Returns T such that exactly k keys are >= T. With bound_only, it stops after
+// the first histogram and returns a lower bound: at least k keys are >= T.
+//
+// Method: the undecided keys lie in [lo, hi], at first the keys' min and max.
+// Each iteration histograms them into kSelBins equal bins covering exactly
+// that range, which spreads them over many bins whatever their magnitude.
+// The bin where the count from the top reaches the remaining rank becomes the
+// new range, and the keys above it are decided. The loop ends when the bin's
+// keys are exactly the ones still needed. When the bin holds at most 64 keys,
+// one wave finishes instead: it ranks them against each other by broadcast.
+// Every iteration shrinks the range by a factor of kSelBins, so at most 7 run.
 template <int WG, class ForEach>
-__device__ uint64_t wg_radix_select(ForEach&& for_each, uint32_t k, SelectLds& s) {
+__device__ uint64_t wg_select(ForEach&& for_each, uint32_t k, uint32_t* hist, SelectLds& s,
+                              bool bound_only = false) {
+  constexpr int NW = WG / kWave;
+  constexpr int PER = kSelBins / WG;
+  static_assert(kSelBins % WG == 0, "bins per thread");
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
-  uint64_t prefix = 0, mask = 0;
-  uint32_t kk = k;
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += WG) s.hist[i] = 0;
-    __syncthreads();
-    for_each([&](uint64_t key) {
-      if ((key & mask) == prefix) atomicAdd(&s.hist[(key >> shift) & 0xffu], 1u);
-    });
-    __syncthreads();
-    if (wave == 0) {
-      const uint32_t c0 = s.hist[4 * lane + 0], c1 = s.hist[4 * lane + 1];
-      const uint32_t c2 = s.hist[4 * lane + 2], c3 = s.hist[4 * lane + 3];
-      const uint32_t incl = wave_suffix_sum(c0 + c1 + c2 + c3);
-      const uint32_t above_lane = incl - (c0 + c1 + c2 + c3);  // keys in bins of higher lanes
-      if (above_lane < kk && incl >= kk) {
-        uint32_t above = above_lane;
-        uint32_t c[4] = {c0, c1, c2, c3};
-        int d = 3;
-        for (; d > 0; --d) {
-          if (above + c[d] >= kk) break;
-          above += c[d];
-        }
-        s.bcast[0] = 4 * lane + d;
-        s.bcast[1] = above;
-        s.bcast[2] = c[d];
-      }
-    }
-    __syncthreads();
-    const uint32_t d = s.bcast[0], above = s.bcast[1], cnt = s.bcast[2];
-    kk -= above;
-    prefix |= static_cast<uint64_t>(d) << shift;
-    mask |= 0xffull << shift;
-    if (cnt == kk) break;
+
+  for (int i = tid; i < kSelBins; i += WG) hist[i] = 0;
+  uint64_t mn = ~0ull, mx = 0;
+  for_each([&](uint64_t key) {
+    mn = key < mn ? key : mn;
+    mx = key > mx ? key : mx;
+  });
+  mn = wave_min_u64(mn);
+  mx = wave_max_u64(mx);
+  if (lane == 0) {
+    s.red[0][wave] = mn;
+    s.red[1][wave] = mx;
   }
   __syncthreads();
-  return prefix;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint64_t a = s.red[0][w], b = s.red[1][w];
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
+  uint64_t lo = mn, hi = mx;
+  uint32_t kk = k;
+  for (int it = 0; it < 8; ++it) {
+    const uint64_t span = hi - lo;
+    if (span == 0) break;  // one key left, and it is the k-th
+    const int bits = 64 - __clzll(span);
+    const int shift = bits > 10 ? bits - 10 : 0;
+    if (it > 0) {
+      for (int i = tid; i < kSelBins; i += WG) hist[i] = 0;
+      __syncthreads();
+    }
+    for_each([&](uint64_t key) {
+      if (key >= lo && key <= hi) atomicAdd(&hist[static_cast<uint32_t>((key - lo) >> shift)], 1u);
+    });
+    __syncthreads();
+    // suffix counts; thread t owns bins [t*PER, (t+1)*PER)
+    uint32_t c[PER];
+    uint32_t local = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      c[i] = hist[tid * PER + i];
+      local += c[i];
+    }
+    const uint32_t pre = wave_prefix_incl(local);
+    const uint32_t wtot = __builtin_amdgcn_readlane(pre, kWave - 1);
+    if (lane == 0) s.part[wave] = wtot;
+    if (tid == 0) s.mcnt = 0;
+    __syncthreads();
+    uint32_t higher = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      if (w > wave) higher += s.part[w];
+    const uint32_t incl = wtot - pre + local + higher;  // keys in bins of threads >= tid
+    const uint32_t above_t = incl - local;
+    if (above_t < kk && incl >= kk) {
+      uint32_t above = above_t;
+      int i = PER - 1;
+      for (; i > 0; --i) {
+        if (above + c[i] >= kk) break;
+        above += c[i];
+      }
+      s.bcast[0] = tid * PER + i;
+      s.bcast[1] = above;
+      s.bcast[2] = c[i];
+    }
+    __syncthreads();
+    const uint32_t bin = s.bcast[0], above = s.bcast[1], cnt = s.bcast[2];
+    kk -= above;
+    lo += static_cast<uint64_t>(bin) << shift;
+    const uint64_t top = lo + ((1ull << shift) - 1ull);
+    hi = top < hi ? top : hi;
+    if (bound_only || cnt == kk) break;
+    if (cnt <= static_cast<uint32_t>(kSelMembers)) {
+      // few keys left: gather them and let one wave rank them
+      const uint64_t blo = lo, bhi = hi;
+      for_each([&](uint64_t key) {
+        if (key >= blo && key <= bhi) s.members[atomicAdd(&s.mcnt, 1u)] = key;
+      });
+      __syncthreads();
+      if (wave == 0) {
+        const uint64_t m = lane < static_cast<int>(cnt) ? s.members[lane] : 0ull;
+        uint32_t rank = 0;  // members greater than m
+        for (uint32_t j = 0; j < cnt; ++j) {
+          const uint32_t olo = __builtin_amdgcn_readlane(static_cast<uint32_t>(m), j);
+          const uint32_t ohi = __builtin_amdgcn_readlane(static_cast<uint32_t>(m >> 32), j);
+          rank += ((static_cast<uint64_t>(ohi) << 32) | olo) > m;
+        }
+        if (lane < static_cast<int>(cnt) && rank == kk - 1) s.result = m;
+      }
+      __syncthreads();
+      lo = s.result;
+      break;
+    }
+  }
+  __syncthreads();
+  return lo;
 }
 
 // Threshold bin of a histogram for rank k: the highest bin b with
@@ -93,8 +199,10 @@ __device__ BinThreshold wg_threshold_bin(Load&& load, uint32_t k, uint32_t* scra
     c[i] = load(tid * PER + i);
     local += c[i];
   }
-  const uint32_t incl_w = wave_suffix_sum(local);  // within wave, lanes >= lane
-  if (lane == 0) scratch[wave] = incl_w;            // wave total
+  const uint32_t pre = wave_prefix_incl(local);
+  const uint32_t wtot = __builtin_amdgcn_readlane(pre, kWave - 1);
+  const uint32_t incl_w = wtot - pre + local;  // within wave, lanes >= lane
+  if (lane == 0) scratch[wave] = wtot;         // wave total
   __syncthreads();
   uint32_t higher_waves = 0, total = 0;
 #pragma unroll

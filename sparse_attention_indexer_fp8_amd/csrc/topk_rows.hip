@@ -7,23 +7,25 @@
 // until the page transform in the epilogue.
 //
 // Design (one workgroup per row, one pass over HBM):
-//  * The window is streamed in tiles of TILE floats with 16-byte loads. A
-//    scalar head (up to 3 elements) and tail (up to 3 elements) make the
-//    stride and the start column free: no alignment is required.
-//  * A running lower bound L on the row's k-th value filters each tile with a
-//    single float compare per element. Survivors are appended to an LDS
-//    candidate buffer as unique 64-bit keys (value key, inverted position),
-//    using a wave ballot plus prefix count and one LDS atomic per wave.
-//  * When the buffer would overflow (or right after the first tile, to get a
-//    bound early), an exact radix select keeps its k best keys, and L becomes
-//    the smallest kept value. L never exceeds the row's true k-th value, so
-//    no winner is ever dropped.
-//  * At the end one more exact select over the buffer gives the top k. The
-//    epilogue maps positions through the page table and writes them.
+//  * The window is streamed in tiles of TR_TILE floats with 16-byte loads, with
+//    TR_RING tiles in flight. A scalar head (up to 3 elements, up to the first
+//    16-byte boundary) and tail (up to 3 elements) make the stride and the
+//    start column free: no alignment is required.
+//  * A running lower bound L on the row's k-th value filters each element with
+//    one float compare. Survivors are appended to an LDS candidate buffer as
+//    unique 64-bit keys (value key, inverted position), using a wave ballot
+//    plus prefix count and one LDS atomic per wave.
+//  * The first tile sets L with one histogram pass over its elements in
+//    registers (the edge of the bin where the count from the top reaches k).
+//    When the buffer would overflow, an exact select keeps its k best keys,
+//    and L becomes the smallest kept value. L never exceeds the row's true
+//    k-th value, so no winner is dropped.
+//  * At the end an exact select over the buffer gives the top k. The epilogue
+//    maps positions through the page table and writes them.
 //  * Rows with n <= k need no scores: every position is selected.
 #include "common.hpp"
-#include "select.hpp"
 #include "launch.hpp"
+#include "select.hpp"
 
 namespace idxtopk {
 
@@ -31,7 +33,6 @@ constexpr int TR_WG = 256;
 constexpr int TR_VEC = 2;                    // float4 loads per thread per tile
 constexpr int TR_TILE = TR_WG * TR_VEC * 4;  // floats per tile (8 KB)
 constexpr int TR_RING = 4;                   // tiles in flight per workgroup
-constexpr int TR_EXTRA = 8;                  // head + tail elements (<= 6)
 
 struct RowsArgs {
   const float* scores;
@@ -65,17 +66,32 @@ struct TopkRowsLds {
   uint32_t minkey;
 };
 
-// Append, in wave-ballot order, every element of the thread's tile that is
-// >= lf. Vectors past the window (vi >= nv) were loaded from a clamped address
-// and are dropped here.
-__device__ __forceinline__ void append_tile(const f4 (&x)[TR_VEC], int vi0, int nv, int head, float lf,
-                                            uint64_t* cand, uint32_t* cnt) {
+// Valid elements of one tile of this thread: vector v holds positions
+// head + 4 * vi + c with vi = vi0 + v * TR_WG + tid; vectors past the window
+// (vi >= nv) were loaded from a clamped address and are ignored.
+struct TileView {
+  int vi0;
+  int nv;
+  int head;
+  __device__ __forceinline__ bool valid(int v) const {
+    return vi0 + v * TR_WG + static_cast<int>(threadIdx.x) < nv;
+  }
+  __device__ __forceinline__ uint32_t pos(int v, int c) const {
+    return static_cast<uint32_t>(head) +
+           4u * static_cast<uint32_t>(vi0 + v * TR_WG + static_cast<int>(threadIdx.x)) + c;
+  }
+};
+
+// Append, in wave-ballot order, every valid element of the thread's tile
+// that is >= lf, plus the optional extra (head / tail) element.
+__device__ __forceinline__ void append_tile(const f4 (&x)[TR_VEC], const TileView& tv, bool has_e, float xe,
+                                            uint32_t pe, float lf, uint64_t* cand, uint32_t* cnt) {
   bool keep[TR_VEC][4];
   uint64_t m[TR_VEC][4];
   uint32_t total = 0;
 #pragma unroll
   for (int v = 0; v < TR_VEC; ++v) {
-    const bool valid = vi0 + v * TR_WG + static_cast<int>(threadIdx.x) < nv;
+    const bool valid = tv.valid(v);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       keep[v][c] = valid && x[v][c] >= lf;
@@ -83,6 +99,9 @@ __device__ __forceinline__ void append_tile(const f4 (&x)[TR_VEC], int vi0, int 
       total += __popcll(m[v][c]);
     }
   }
+  const bool keep_e = has_e && xe >= lf;
+  const uint64_t me = ballot(keep_e);
+  total += __popcll(me);
   if (total == 0) return;
   uint32_t base = 0;
   if (lane_id() == 0) base = atomicAdd(cnt, total);
@@ -90,16 +109,13 @@ __device__ __forceinline__ void append_tile(const f4 (&x)[TR_VEC], int vi0, int 
   uint32_t run = 0;
 #pragma unroll
   for (int v = 0; v < TR_VEC; ++v) {
-    const uint32_t vi = static_cast<uint32_t>(vi0 + v * TR_WG + static_cast<int>(threadIdx.x));
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      if (keep[v][c]) {
-        const uint32_t pos = static_cast<uint32_t>(head) + 4u * vi + c;
-        cand[base + run + lanes_below(m[v][c])] = rank_key(float_key(x[v][c]), pos);
-      }
+      if (keep[v][c]) cand[base + run + lanes_below(m[v][c])] = rank_key(float_key(x[v][c]), tv.pos(v, c));
       run += __popcll(m[v][c]);
     }
   }
+  if (keep_e) cand[base + run + lanes_below(me)] = rank_key(float_key(xe), pe);
 }
 
 // Load this thread's share of cand[0, n) into registers (entries tid + e*WG).
@@ -118,9 +134,12 @@ __device__ __forceinline__ int gather_entries(const uint64_t* cand, uint32_t n, 
 }
 
 template <int MAXE>
-__global__ __launch_bounds__(TR_WG) void topk_rows_kernel(RowsArgs a) {
+__global__ __launch_bounds__(TR_WG, 3) void topk_rows_kernel(RowsArgs a) {
   extern __shared__ uint64_t cand[];
   __shared__ TopkRowsLds s;
+  // The select histogram overlays the candidate buffer: every select first
+  // copies the buffer's keys to registers.
+  uint32_t* hist = reinterpret_cast<uint32_t*>(cand);
 
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
@@ -148,17 +167,17 @@ __global__ __launch_bounds__(TR_WG) void topk_rows_kernel(RowsArgs a) {
   const f4* vbase = reinterpret_cast<const f4*>(base + head);
   const int ntiles = (nv + TR_WG * TR_VEC - 1) / (TR_WG * TR_VEC);
 
-  // scalar head and tail elements go straight into the buffer
-  if (tid < head) {
-    cand[tid] = rank_key(float_key(base[tid]), static_cast<uint32_t>(tid));
-  } else if (tid < head + ntail) {
-    const int p = tail0 + (tid - head);
-    cand[tid] = rank_key(float_key(base[p]), static_cast<uint32_t>(p));
+  // scalar head and tail elements ride along with the first tile
+  const bool has_e = tid < head + ntail;
+  uint32_t pe = 0;
+  float xe = 0.0f;
+  if (has_e) {
+    pe = static_cast<uint32_t>(tid < head ? tid : tail0 + (tid - head));
+    xe = base[pe];
   }
-  if (tid == 0) s.cnt = static_cast<uint32_t>(head + ntail);
 
   // tile t, vector v of this thread; loads past the window use a clamped
-  // (in-bounds) address and are masked out in append_tile
+  // (in-bounds) address and are masked out by TileView
   auto load_tile = [&](int t, f4 (&x)[TR_VEC]) {
 #pragma unroll
     for (int v = 0; v < TR_VEC; ++v) {
@@ -167,31 +186,32 @@ __global__ __launch_bounds__(TR_WG) void topk_rows_kernel(RowsArgs a) {
       x[v] = __builtin_nontemporal_load(vbase + vi);
     }
   };
+  auto view = [&](int t) { return TileView{t * TR_WG * TR_VEC, nv, head}; };
 
   // exact top-k of the buffer; returns the separating key T
   auto select_buffer = [&](uint32_t c, uint64_t (&keys)[MAXE], int& nvk) -> uint64_t {
     nvk = gather_entries<MAXE>(cand, c, keys);
-    return wg_radix_select<TR_WG>(
+    __syncthreads();  // every thread holds its keys before the histogram overlays them
+    return wg_select<TR_WG>(
         [&](auto&& f) {
 #pragma unroll
           for (int e = 0; e < MAXE; ++e)
             if (e < nvk) f(keys[e]);
         },
-        k, s.sel);
+        k, hist, s.sel);
   };
 
+  if (tid == 0) s.cnt = 0;
   float lf = -__builtin_inff();
 
-  // After tile t: when the buffer holds more than k keys and either no bound
-  // exists yet or the next tile might not fit, keep exactly the k best keys
-  // and raise the bound to the smallest kept value.
+  // After tile t: when the buffer would not take another tile, keep exactly
+  // the k best keys and raise the bound to the smallest kept value.
   auto after_tile = [&](int t) {
     __syncthreads();
     const uint32_t c = s.cnt;
     __syncthreads();
     const bool last = (t + 1 == ntiles);
-    const bool unbounded = (lf == -__builtin_inff());
-    if (!last && c > k && (unbounded || c + TR_TILE > static_cast<uint32_t>(a.cap))) {
+    if (!last && c > k && c + TR_TILE > static_cast<uint32_t>(a.cap)) {
       uint64_t keys[MAXE];
       int nvk;
       const uint64_t T = select_buffer(c, keys, nvk);
@@ -233,31 +253,62 @@ __global__ __launch_bounds__(TR_WG) void topk_rows_kernel(RowsArgs a) {
     for (int u = 0; u < TR_RING; ++u) load_tile(u < ntiles ? u : ntiles - 1, ring[u]);
   }
   __syncthreads();
-  int t0 = 0;
+
+  // First tile (plus the head / tail elements): when more data follows, one
+  // histogram pass over these elements bounds the k-th value; then append
+  // what passes the bound.
+  {
+    const TileView tv = view(0);
+    const bool has_tile = ntiles > 0;
+    const int n0 = 4 * min(nv, TR_WG * TR_VEC) + head + ntail;
+    if (ntiles > 1 && n0 > a.k) {
+      const uint64_t bound = wg_select<TR_WG>(
+          [&](auto&& f) {
+#pragma unroll
+            for (int v = 0; v < TR_VEC; ++v)
+              if (tv.valid(v)) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) f(rank_key(float_key(ring[0][v][c]), tv.pos(v, c)));
+              }
+            if (has_e) f(rank_key(float_key(xe), pe));
+          },
+          k, hist, s.sel, 1);
+      lf = key_float(rank_vkey(bound));
+    }
+    if (has_tile) {
+      append_tile(ring[0], tv, has_e, xe, pe, lf, cand, &s.cnt);
+      __builtin_amdgcn_sched_barrier(0);
+      if (TR_RING < ntiles) load_tile(TR_RING, ring[0]);
+      after_tile(0);
+    } else {
+      const f4 none[TR_VEC] = {};
+      append_tile(none, TileView{0, 0, head}, has_e, xe, pe, lf, cand, &s.cnt);
+      __syncthreads();
+    }
+  }
+
+  // steady state: tiles t0 .. t0 + TR_RING - 1 (slot t % TR_RING), every
+  // refill in range, so control flow is uniform
+  int t0 = 1;
   for (; t0 + 2 * TR_RING <= ntiles; t0 += TR_RING) {
 #pragma unroll
     for (int u = 0; u < TR_RING; ++u) {
-      append_tile(ring[u], (t0 + u) * TR_WG * TR_VEC, nv, head, lf, cand, &s.cnt);
+      const int t = t0 + u;
+      const int slot = (1 + u) % TR_RING;
+      append_tile(ring[slot], view(t), false, 0.0f, 0u, lf, cand, &s.cnt);
       __builtin_amdgcn_sched_barrier(0);
-      load_tile(t0 + u + TR_RING, ring[u]);
-      after_tile(t0 + u);
-    }
-  }
-  // drain: fewer than 2 * TR_RING tiles remain, the ring holds t0 .. t0 + TR_RING - 1
-#pragma unroll
-  for (int u = 0; u < TR_RING; ++u) {
-    const int t = t0 + u;
-    if (t < ntiles) {
-      append_tile(ring[u], t * TR_WG * TR_VEC, nv, head, lf, cand, &s.cnt);
-      if (t + TR_RING < ntiles) load_tile(t + TR_RING, ring[u]);
+      load_tile(t + TR_RING, ring[slot]);
       after_tile(t);
     }
   }
+  // drain: fewer than 2 * TR_RING tiles remain
 #pragma unroll
-  for (int u = 0; u < TR_RING; ++u) {
-    const int t = t0 + TR_RING + u;
+  for (int u = 0; u < 2 * TR_RING; ++u) {
+    const int t = t0 + u;
+    const int slot = (1 + u) % TR_RING;
     if (t < ntiles) {
-      append_tile(ring[u], t * TR_WG * TR_VEC, nv, head, lf, cand, &s.cnt);
+      append_tile(ring[slot], view(t), false, 0.0f, 0u, lf, cand, &s.cnt);
+      if (t + TR_RING < ntiles) load_tile(t + TR_RING, ring[slot]);
       after_tile(t);
     }
   }
@@ -288,9 +339,13 @@ __global__ __launch_bounds__(TR_WG) void topk_rows_kernel(RowsArgs a) {
   }
 }
 
-// Candidate buffer sizing: room for the k kept keys plus one whole tile plus
-// the scalar head and tail elements.
-static inline int rows_cap(int k) { return (k > TR_TILE ? k : TR_TILE) + 2 * TR_TILE + TR_EXTRA; }
+// Candidate buffer sizing: room for the k kept keys plus two whole tiles
+// (one tile of slack between compactions), and never less than the select
+// histogram that overlays it.
+static inline int rows_cap(int k) {
+  const int c = (k > TR_TILE ? k : TR_TILE) + 2 * TR_TILE + 8;
+  return c > kSelBins / 2 ? c : kSelBins / 2;
+}
 
 int launch_topk_rows(const float* scores, int64_t stride, int rows, const int32_t* seq_lens,
                      const int32_t* row_starts, const int32_t* row_to_batch,
