@@ -79,31 +79,33 @@ __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Inclusive suffix sum across the wave: lane l gets sum of v over lanes >= l.
-__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const uint32_t o = __shfl_down(v, d, kWave);
-    if (l + d < kWave) v += o;
-  }
-  return v;
+// Inclusive prefix sum across the wave with DPP row shifts and row
+// broadcasts (no LDS traffic).
+__device__ __forceinline__ uint32_t wave_prefix_incl(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
 }
 
-__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-  for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
-  return v;
+// Reserve `mine` consecutive output slots for this thread: one DPP prefix
+// and at most one atomic per wave on the LDS counter `ctr`. Returns the
+// thread's first slot. Every lane of the wave must call.
+__device__ __forceinline__ uint32_t wave_reserve(uint32_t mine, uint32_t* ctr) {
+  const uint32_t pre = wave_prefix_incl(mine);
+  const uint32_t tot = __builtin_amdgcn_readlane(pre, kWave - 1);
+  uint32_t base = 0;
+  if (lane_id() == kWave - 1 && tot) base = atomicAdd(ctr, tot);
+  base = __builtin_amdgcn_readlane(base, kWave - 1);
+  return base + pre - mine;
 }
 
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int d = kWave / 2; d > 0; d >>= 1) {
-    const uint32_t o = __shfl_xor(v, d, kWave);
-    v = o < v ? o : v;
-  }
-  return v;
-}
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) { return __reduce_add_sync(~0ull, v); }
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return __reduce_min_sync(~0ull, v); }
 
 // Device-scope relaxed atomics on workspace words.
 __device__ __forceinline__ uint32_t ld_acquire_dev(const uint32_t* p) {

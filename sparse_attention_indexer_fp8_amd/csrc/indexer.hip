@@ -189,32 +189,19 @@ __global__ __launch_bounds__(IX_WG) void fused_chunk_kernel(IndexerArgs a, Fused
       static_cast<uint32_t>(k), s.scratch);
   const uint32_t bin_g = bound.all ? 0u : bound.bin;
 
-  // Emit this chunk's candidates (bin >= bound) to the row's list.
+  // Emit this chunk's candidates (bin >= bound) to the row's list: each
+  // thread's offset comes from a wave prefix plus one LDS and one global
+  // reservation for the whole chunk.
   uint32_t mine = 0;
   for (int i = tid; i < cnt; i += IX_WG) mine += ((float_key(s.sc[i]) >> HIST_SHIFT) >= bin_g);
-  mine = wave_sum(mine);
-  if (lane_id() == 0 && mine) atomicAdd(&s.lcnt, mine);
+  const uint32_t my0 = wave_reserve(mine, &s.lcnt);
   __syncthreads();
-  if (tid == 0) {
-    s.gbase = s.lcnt ? add_dev(&ctr[0], s.lcnt) : 0u;
-    s.lcnt = 0;
-  }
+  if (tid == 0) s.gbase = s.lcnt ? add_dev(&ctr[0], s.lcnt) : 0u;
   __syncthreads();
-  const uint32_t gbase = s.gbase;
-  for (int i0 = 0; i0 < cnt; i0 += IX_WG) {
-    const int i = i0 + tid;
-    uint32_t key = 0;
-    bool keep = false;
-    if (i < cnt) {
-      key = float_key(s.sc[i]);
-      keep = (key >> HIST_SHIFT) >= bin_g;
-    }
-    const uint64_t mk = ballot(keep);
-    if (mk == 0) continue;
-    uint32_t wb = 0;
-    if (lane_id() == 0) wb = atomicAdd(&s.lcnt, static_cast<uint32_t>(__popcll(mk)));
-    wb = uniform(wb);
-    if (keep) cand[gbase + wb + lanes_below(mk)] = rank_key(key, static_cast<uint32_t>(tb + i));
+  uint32_t at = s.gbase + my0;
+  for (int i = tid; i < cnt; i += IX_WG) {
+    const uint32_t key = float_key(s.sc[i]);
+    if ((key >> HIST_SHIFT) >= bin_g) cand[at++] = rank_key(key, static_cast<uint32_t>(tb + i));
   }
 }
 
@@ -226,21 +213,35 @@ struct MergeLds {
   uint32_t bcnt;
 };
 
-// Emit the keys for which `keep` holds (all lanes of the wave must call).
-__device__ __forceinline__ void emit_keys(bool keep, uint64_t key, const IndexerArgs& a, int b,
-                                          const FusedOut& o, uint32_t* ocnt) {
-  const uint64_t mk = ballot(keep);
-  if (mk == 0) return;
-  uint32_t wb = 0;
-  if (lane_id() == 0) wb = atomicAdd(ocnt, static_cast<uint32_t>(__popcll(mk)));
-  wb = uniform(wb);
-  const uint32_t idx = wb + lanes_below(mk);
-  if (keep && idx < static_cast<uint32_t>(o.k)) {
-    const int64_t at = static_cast<int64_t>(b) * o.k + idx;
-    o.slots[at] = token_slot(a, b, rank_pos(key));
-    if (o.scores) o.scores[at] = key_float(rank_vkey(key));
+// Emit this thread's keys with keep[e] set: one slot reservation per wave,
+// then independent block-table gathers and stores. All lanes of the wave must
+// call.
+template <int N>
+__device__ __forceinline__ void emit_batch(const uint64_t (&keys)[N], const bool (&keep)[N],
+                                           const IndexerArgs& a, int b, const FusedOut& o,
+                                           uint32_t* ocnt) {
+  uint32_t mine = 0;
+#pragma unroll
+  for (int e = 0; e < N; ++e) mine += keep[e];
+  uint32_t at = wave_reserve(mine, ocnt);
+  int32_t sl[N];
+#pragma unroll
+  for (int e = 0; e < N; ++e)
+    if (keep[e]) sl[e] = token_slot(a, b, rank_pos(keys[e]));
+  const int64_t row = static_cast<int64_t>(b) * o.k;
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    if (keep[e]) {
+      if (at < static_cast<uint32_t>(o.k)) {
+        o.slots[row + at] = sl[e];
+        if (o.scores) o.scores[row + at] = key_float(rank_vkey(keys[e]));
+      }
+      ++at;
+    }
   }
 }
+
+constexpr int MG_BATCH = 8;  // candidates per thread per pass of the merge
 
 // One workgroup per row. The row's histogram is complete now (previous
 // kernel), so it names the exact threshold bin: candidates above it are
@@ -257,68 +258,77 @@ __global__ __launch_bounds__(MG_WG) void fused_merge_kernel(IndexerArgs a, Fused
   uint64_t* cand = ws.cand + static_cast<int64_t>(b) * ws.cap;
   const uint32_t ncand = n > 0 ? ctr[0] : 0u;
 
+  wg_select_init<MG_WG>(s.sel);
   if (tid == 0) {
     s.ocnt = 0;
     s.bcnt = 0;
   }
   const BinThreshold th = wg_threshold_bin<MG_WG, HIST_BINS>([&](int i) { return Hg[i]; }, k, s.scratch);
-  if (th.all) {
-    for (uint32_t i0 = 0; i0 < ncand; i0 += MG_WG) {
-      const uint32_t i = i0 + tid;
-      const bool keep = i < ncand;
-      emit_keys(keep, keep ? cand[i] : 0ull, a, b, o, &s.ocnt);
+  const uint32_t bstar = th.all ? 0u : th.bin;
+  const uint32_t need = th.all ? 0u : k - th.above;
+  // Pass over the candidates: keys above the threshold bin (or all keys when
+  // the row holds fewer than k) are emitted, keys inside it go to LDS.
+  for (uint32_t i0 = 0; i0 < ncand; i0 += MG_WG * MG_BATCH) {
+    uint64_t key[MG_BATCH];
+    bool keep[MG_BATCH], mid[MG_BATCH];
+    uint32_t nmid = 0;
+#pragma unroll
+    for (int j = 0; j < MG_BATCH; ++j) {
+      const uint32_t i = i0 + j * MG_WG + tid;
+      const bool valid = i < ncand;
+      key[j] = valid ? cand[i] : 0ull;
+      const uint32_t bin = rank_vkey(key[j]) >> HIST_SHIFT;
+      keep[j] = valid && (th.all || bin > bstar);
+      mid[j] = valid && !th.all && bin == bstar;
+      nmid += mid[j];
     }
-  } else {
-    const uint32_t bstar = th.bin;
-    const uint32_t need = k - th.above;
-    for (uint32_t i0 = 0; i0 < ncand; i0 += MG_WG) {
-      const uint32_t i = i0 + tid;
-      uint64_t key = 0;
-      uint32_t bin = 0;
-      if (i < ncand) {
-        key = cand[i];
-        bin = rank_vkey(key) >> HIST_SHIFT;
-      }
-      emit_keys(i < ncand && bin > bstar, key, a, b, o, &s.ocnt);
-      const bool mid = (i < ncand) && bin == bstar;
-      const uint64_t mm = ballot(mid);
-      if (mm) {
-        uint32_t wb = 0;
-        if (lane_id() == 0) wb = atomicAdd(&s.bcnt, static_cast<uint32_t>(__popcll(mm)));
-        wb = uniform(wb);
-        const uint32_t at = wb + lanes_below(mm);
-        if (mid && at < MG_BUF) s.buf[at] = key;
+    emit_batch<MG_BATCH>(key, keep, a, b, o, &s.ocnt);
+    uint32_t at = wave_reserve(nmid, &s.bcnt);
+#pragma unroll
+    for (int j = 0; j < MG_BATCH; ++j) {
+      if (mid[j]) {
+        if (at < static_cast<uint32_t>(MG_BUF)) s.buf[at] = key[j];
+        ++at;
       }
     }
-    __syncthreads();
-    const uint32_t nb = s.bcnt;
-    if (nb <= need) {
-      for (uint32_t i0 = 0; i0 < nb; i0 += MG_WG) {
-        const uint32_t i = i0 + tid;
-        emit_keys(i < nb, i < nb ? s.buf[i] : 0ull, a, b, o, &s.ocnt);
-      }
-    } else if (nb <= static_cast<uint32_t>(MG_BUF)) {
+  }
+  __syncthreads();
+  const uint32_t nb = s.bcnt;
+  if (!th.all && nb > 0) {
+    if (nb <= static_cast<uint32_t>(MG_BUF)) {
       uint64_t keys[MG_MAXE];
       int nvk = 0;
 #pragma unroll
       for (int e = 0; e < MG_MAXE; ++e) {
         const uint32_t i = tid + e * MG_WG;
+        keys[e] = 0;
         if (i < nb) {
           keys[e] = s.buf[i];
           nvk = e + 1;
         }
       }
-      // (the select histogram overlays the buffer, now held in registers)
-      __syncthreads();
-      const uint64_t T = wg_select<MG_WG>(
-          [&](auto&& f) {
+      uint64_t T = 0;  // keys >= T are selected
+      if (nb > need) {
+        uint64_t mn = ~0ull, mx = 0;
 #pragma unroll
-            for (int e = 0; e < MG_MAXE; ++e)
-              if (e < nvk) f(keys[e]);
-          },
-          need, reinterpret_cast<uint32_t*>(s.buf), s.sel);
+        for (int e = 0; e < MG_MAXE; ++e)
+          if (e < nvk) {
+            mn = keys[e] < mn ? keys[e] : mn;
+            mx = keys[e] > mx ? keys[e] : mx;
+          }
+        wg_range<MG_WG>(mn, mx, s.sel);
+        T = wg_select<MG_WG>(
+            [&](auto&& f) {
 #pragma unroll
-      for (int e = 0; e < MG_MAXE; ++e) emit_keys(e < nvk && keys[e] >= T, keys[e], a, b, o, &s.ocnt);
+              for (int e = 0; e < MG_MAXE; ++e)
+                if (e < nvk) f(keys[e]);
+            },
+            need, mn, mx, s.sel);
+      }
+      bool keep[MG_MAXE];
+#pragma unroll
+      for (int e = 0; e < MG_MAXE; ++e) keep[e] = e < nvk && keys[e] >= T;
+      emit_batch<MG_MAXE>(keys, keep, a, b, o, &s.ocnt);
     } else {
       // threshold bin larger than the LDS buffer: select straight from the
       // candidate list (several passes over it)
@@ -328,16 +338,23 @@ __global__ __launch_bounds__(MG_WG) void fused_merge_kernel(IndexerArgs a, Fused
           if ((rank_vkey(key) >> HIST_SHIFT) == bstar) f(key);
         }
       };
-      const uint64_t T = wg_select<MG_WG>(each_mid, need, reinterpret_cast<uint32_t*>(s.buf), s.sel);
-      for (uint32_t i0 = 0; i0 < ncand; i0 += MG_WG) {
-        const uint32_t i = i0 + tid;
-        uint64_t key = 0;
-        bool keep = false;
-        if (i < ncand) {
-          key = cand[i];
-          keep = (rank_vkey(key) >> HIST_SHIFT) == bstar && key >= T;
+      uint64_t mn = ~0ull, mx = 0;
+      each_mid([&](uint64_t key) {
+        mn = key < mn ? key : mn;
+        mx = key > mx ? key : mx;
+      });
+      wg_range<MG_WG>(mn, mx, s.sel);
+      const uint64_t T = wg_select<MG_WG>(each_mid, need, mn, mx, s.sel);
+      for (uint32_t i0 = 0; i0 < ncand; i0 += MG_WG * MG_BATCH) {
+        uint64_t key[MG_BATCH];
+        bool keep[MG_BATCH];
+#pragma unroll
+        for (int j = 0; j < MG_BATCH; ++j) {
+          const uint32_t i = i0 + j * MG_WG + tid;
+          key[j] = i < ncand ? cand[i] : 0ull;
+          keep[j] = i < ncand && (rank_vkey(key[j]) >> HIST_SHIFT) == bstar && key[j] >= T;
         }
-        emit_keys(keep, key, a, b, o, &s.ocnt);
+        emit_batch<MG_BATCH>(key, keep, a, b, o, &s.ocnt);
       }
     }
   }
@@ -413,6 +430,7 @@ __global__ __launch_bounds__(MG_WG) void block_merge_kernel(IndexerArgs a, Block
   const int nblk = (n + bs - 1) / bs;
   uint32_t* bsc = ws.bscore + static_cast<int64_t>(b) * ws.nblk_max;
 
+  wg_select_init<MG_WG>(s.sel);
   if (tid == 0) s.ocnt = 0;
   __syncthreads();
   if (nblk <= top) {
@@ -422,9 +440,13 @@ __global__ __launch_bounds__(MG_WG) void block_merge_kernel(IndexerArgs a, Block
     auto each = [&](auto&& f) {
       for (int cb = tid; cb < nblk; cb += MG_WG) f(rank_key(bsc[cb], static_cast<uint32_t>(cb)));
     };
-    // (the select histogram overlays sel_blocks, written only afterwards)
-    const uint64_t T = wg_select<MG_WG>(each, static_cast<uint32_t>(top),
-                                        reinterpret_cast<uint32_t*>(s.sel_blocks), s.sel);
+    uint64_t mn = ~0ull, mx = 0;
+    each([&](uint64_t key) {
+      mn = key < mn ? key : mn;
+      mx = key > mx ? key : mx;
+    });
+    wg_range<MG_WG>(mn, mx, s.sel);
+    const uint64_t T = wg_select<MG_WG>(each, static_cast<uint32_t>(top), mn, mx, s.sel);
     for (int c0 = 0; c0 < nblk; c0 += MG_WG) {
       const int cb = c0 + tid;
       const bool keep = cb < nblk && rank_key(bsc[cb], static_cast<uint32_t>(cb)) >= T;

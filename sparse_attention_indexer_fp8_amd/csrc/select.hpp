@@ -12,15 +12,22 @@ namespace idxtopk {
 constexpr int kSelBins = 1024;    // histogram bins of one select iteration
 constexpr int kSelMembers = 64;   // threshold-bin size a single wave resolves
 
-// LDS scratch of wg_select. The histogram (kSelBins words) is passed apart.
+// LDS state of wg_select. `hist` and `mcnt` must be zero when a select starts
+// (wg_select_init once per kernel) and every select leaves them zero again.
 struct SelectLds {
+  uint32_t hist[kSelBins];
   uint64_t red[2][16];
   uint64_t members[kSelMembers];
   uint64_t result;
-  uint32_t part[16];
   uint32_t bcast[4];
   uint32_t mcnt;
 };
+
+template <int WG>
+__device__ __forceinline__ void wg_select_init(SelectLds& s) {
+  for (int i = threadIdx.x; i < kSelBins; i += WG) s.hist[i] = 0;
+  if (threadIdx.x == 0) s.mcnt = 0;
+}
 
 __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
   const uint32_t hi = static_cast<uint32_t>(v >> 32), lo = static_cast<uint32_t>(v);
@@ -36,53 +43,15 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return (static_cast<uint64_t>(mhi) << 32) | mlo;
 }
 
-// Inclusive prefix sum across the wave with DPP row shifts and row
-// broadcasts (no LDS traffic).
-__device__ __forceinline__ uint32_t wave_prefix_incl(uint32_t x) {
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);  // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false);  // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, false);  // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, false);  // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  return x;
-}
-
-// k-th largest of a set of DISTINCT 64-bit keys spread over the workgroup.
-// `for_each(f)` must call f(key) once for every key this thread owns, the
-// same set on every call. Precondition: the set holds more than k keys, k >= 1.
-// `hist` is LDS of kSelBins words.
-//
-// Returns T such that exactly k keys are >= T. With bound_only, it stops after
-// the first histogram and returns a lower bound: at least k keys are >= T.
-//
-// Method: the undecided keys lie in [lo, hi], at first the keys' min and max.
-// Each iteration histograms them into kSelBins equal bins covering exactly
-// that range, which spreads them over many bins whatever their magnitude.
-// The bin where the count from the top reaches the remaining rank becomes the
-// new range, and the keys above it are decided. The loop ends when the bin's
-// keys are exactly the ones still needed. When the bin holds at most 64 keys,
-// one wave finishes instead: it ranks them against each other by broadcast.
-// Every iteration shrinks the range by a factor of kSelBins, so at most 7 run.
-template <int WG, class ForEach>
-__device__ uint64_t wg_select(ForEach&& for_each, uint32_t k, uint32_t* hist, SelectLds& s,
-                              bool bound_only = false) {
+// Workgroup min and max of per-thread values (one barrier). Every thread
+// gets the results.
+template <int WG>
+__device__ __forceinline__ void wg_range(uint64_t& mn, uint64_t& mx, SelectLds& s) {
   constexpr int NW = WG / kWave;
-  constexpr int PER = kSelBins / WG;
-  static_assert(kSelBins % WG == 0, "bins per thread");
-  const int tid = threadIdx.x;
-  const int wave = tid / kWave;
-  const int lane = tid % kWave;
-
-  for (int i = tid; i < kSelBins; i += WG) hist[i] = 0;
-  uint64_t mn = ~0ull, mx = 0;
-  for_each([&](uint64_t key) {
-    mn = key < mn ? key : mn;
-    mx = key > mx ? key : mx;
-  });
+  const int wave = threadIdx.x / kWave;
   mn = wave_min_u64(mn);
   mx = wave_max_u64(mx);
-  if (lane == 0) {
+  if (lane_id() == 0) {
     s.red[0][wave] = mn;
     s.red[1][wave] = mx;
   }
@@ -93,50 +62,66 @@ __device__ uint64_t wg_select(ForEach&& for_each, uint32_t k, uint32_t* hist, Se
     mn = a < mn ? a : mn;
     mx = b > mx ? b : mx;
   }
-  uint64_t lo = mn, hi = mx;
+}
+
+// k-th largest of a set of DISTINCT 64-bit keys spread over the workgroup,
+// all within [lo, hi] (wg_range gives these). `for_each(f)` must call f(key)
+// once for every key this thread owns, the same set on every call.
+// Precondition: the set holds more than k keys, k >= 1.
+//
+// Returns T such that exactly k keys are >= T. With bound_only it stops after
+// the first histogram and returns a lower bound: at least k keys are >= T.
+//
+// Method: each iteration histograms the undecided keys into kSelBins equal
+// bins covering exactly their range [lo, hi], so they spread over many bins
+// whatever their magnitude. Wave 0 alone reads (and re-zeroes) the bins and
+// finds the one where the count from the top reaches the remaining rank.
+// That bin becomes the new range, and the keys above it are decided. The loop
+// ends when the bin's keys are exactly the ones still needed. When the bin
+// holds at most 64 keys, wave 0 instead ranks them against each other by
+// broadcast. Each iteration shrinks the range by a factor of kSelBins, so at
+// most 7 run; one or two are typical.
+template <int WG, class ForEach>
+__device__ __forceinline__ uint64_t wg_select(ForEach&& for_each, uint32_t k, uint64_t lo, uint64_t hi, SelectLds& s,
+                              bool bound_only = false) {
+  constexpr int PL = kSelBins / kWave;  // bins per lane of wave 0
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
   uint32_t kk = k;
   for (int it = 0; it < 8; ++it) {
     const uint64_t span = hi - lo;
     if (span == 0) break;  // one key left, and it is the k-th
     const int bits = 64 - __clzll(span);
     const int shift = bits > 10 ? bits - 10 : 0;
-    if (it > 0) {
-      for (int i = tid; i < kSelBins; i += WG) hist[i] = 0;
-      __syncthreads();
-    }
     for_each([&](uint64_t key) {
-      if (key >= lo && key <= hi) atomicAdd(&hist[static_cast<uint32_t>((key - lo) >> shift)], 1u);
+      if (key >= lo && key <= hi) atomicAdd(&s.hist[static_cast<uint32_t>((key - lo) >> shift)], 1u);
     });
     __syncthreads();
-    // suffix counts; thread t owns bins [t*PER, (t+1)*PER)
-    uint32_t c[PER];
-    uint32_t local = 0;
+    if (wave == 0) {
+      uint32_t c[PL];
+      uint32_t local = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      c[i] = hist[tid * PER + i];
-      local += c[i];
-    }
-    const uint32_t pre = wave_prefix_incl(local);
-    const uint32_t wtot = __builtin_amdgcn_readlane(pre, kWave - 1);
-    if (lane == 0) s.part[wave] = wtot;
-    if (tid == 0) s.mcnt = 0;
-    __syncthreads();
-    uint32_t higher = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w)
-      if (w > wave) higher += s.part[w];
-    const uint32_t incl = wtot - pre + local + higher;  // keys in bins of threads >= tid
-    const uint32_t above_t = incl - local;
-    if (above_t < kk && incl >= kk) {
-      uint32_t above = above_t;
-      int i = PER - 1;
-      for (; i > 0; --i) {
-        if (above + c[i] >= kk) break;
-        above += c[i];
+      for (int i = 0; i < PL; ++i) {
+        c[i] = s.hist[lane * PL + i];
+        local += c[i];
       }
-      s.bcast[0] = tid * PER + i;
-      s.bcast[1] = above;
-      s.bcast[2] = c[i];
+#pragma unroll
+      for (int i = 0; i < PL; ++i) s.hist[lane * PL + i] = 0;
+      const uint32_t pre = wave_prefix_incl(local);
+      const uint32_t tot = __builtin_amdgcn_readlane(pre, kWave - 1);
+      const uint32_t incl = tot - pre + local;  // keys in bins of lanes >= lane
+      const uint32_t above_l = incl - local;
+      if (above_l < kk && incl >= kk) {
+        uint32_t above = above_l;
+        int i = PL - 1;
+        for (; i > 0; --i) {
+          if (above + c[i] >= kk) break;
+          above += c[i];
+        }
+        s.bcast[0] = lane * PL + i;
+        s.bcast[1] = above;
+        s.bcast[2] = c[i];
+      }
     }
     __syncthreads();
     const uint32_t bin = s.bcast[0], above = s.bcast[1], cnt = s.bcast[2];
@@ -161,13 +146,13 @@ __device__ uint64_t wg_select(ForEach&& for_each, uint32_t k, uint32_t* hist, Se
           rank += ((static_cast<uint64_t>(ohi) << 32) | olo) > m;
         }
         if (lane < static_cast<int>(cnt) && rank == kk - 1) s.result = m;
+        if (lane == 0) s.mcnt = 0;
       }
       __syncthreads();
       lo = s.result;
       break;
     }
   }
-  __syncthreads();
   return lo;
 }
 

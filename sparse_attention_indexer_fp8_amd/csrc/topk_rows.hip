@@ -6,26 +6,33 @@
 // page-table row row_to_batch[i] (or i). Selected positions stay row-local
 // until the page transform in the epilogue.
 //
-// Design (one workgroup per row, one pass over HBM):
-//  * The window is streamed in tiles of TR_TILE floats with 16-byte loads, with
-//    TR_RING tiles in flight. A scalar head (up to 3 elements, up to the first
-//    16-byte boundary) and tail (up to 3 elements) make the stride and the
-//    start column free: no alignment is required.
+// Design (persistent workgroups, one row at a time each, one pass over HBM):
+//  * Workgroup g handles rows g, g + G, g + 2G, ... for a grid of G.
+//  * A row's window is streamed in tiles of TR_TILE floats with 16-byte
+//    loads, TR_RING tiles in flight. A scalar head (up to 3 elements, up to
+//    the first 16-byte boundary) and tail (up to 3 elements) make the stride
+//    and the start column free: no alignment is required.
 //  * A running lower bound L on the row's k-th value filters each element with
 //    one float compare. Survivors are appended to an LDS candidate buffer as
-//    unique 64-bit keys (value key, inverted position), using a wave ballot
-//    plus prefix count and one LDS atomic per wave.
+//    unique 64-bit keys (value key, inverted position): a wave ballot plus
+//    prefix count and one LDS atomic per wave.
 //  * The first tile sets L with one histogram pass over its elements in
 //    registers (the edge of the bin where the count from the top reaches k).
 //    When the buffer would overflow, an exact select keeps its k best keys,
 //    and L becomes the smallest kept value. L never exceeds the row's true
 //    k-th value, so no winner is dropped.
-//  * At the end an exact select over the buffer gives the top k. The epilogue
-//    maps positions through the page table and writes them.
+//  * At the end an exact select over the buffer gives the top k, and the
+//    epilogue maps positions through the page table. Before that, the first
+//    tiles of the workgroup's next row are already requested, so the select
+//    overlaps memory traffic.
 //  * Rows with n <= k need no scores: every position is selected.
 #include "common.hpp"
 #include "launch.hpp"
 #include "select.hpp"
+
+#include <map>
+#include <mutex>
+#include <utility>
 
 namespace idxtopk {
 
@@ -37,6 +44,7 @@ constexpr int TR_RING = 4;                   // tiles in flight per workgroup
 struct RowsArgs {
   const float* scores;
   int64_t stride;
+  int32_t rows;
   const int32_t* seq_lens;
   const int32_t* row_starts;
   const int32_t* row_to_batch;
@@ -66,6 +74,43 @@ struct TopkRowsLds {
   uint32_t minkey;
 };
 
+// Geometry of one row (all values uniform across the workgroup).
+struct RowCtx {
+  int row;
+  int n;
+  int head;    // scalar elements before the first 16-byte boundary
+  int nv;      // full float4 vectors after the head
+  int tail0;   // first tail element
+  int ntail;
+  int ntiles;
+  const float* base;
+  const f4* vbase;
+  const int32_t* pt_row;
+  int32_t* out;
+  bool trivial;  // n <= k: every position is selected
+};
+
+__device__ __forceinline__ RowCtx row_setup(const RowsArgs& a, int row) {
+  RowCtx r;
+  r.row = row;
+  r.n = a.seq_lens[row];
+  const int64_t rs = a.row_starts ? a.row_starts[row] : 0;
+  const int prow = a.row_to_batch ? a.row_to_batch[row] : row;
+  r.pt_row = a.page_table ? a.page_table + static_cast<int64_t>(prow) * a.pt_stride : nullptr;
+  r.out = a.out + static_cast<int64_t>(row) * a.k;
+  r.trivial = r.n <= a.k;
+  r.base = a.scores + static_cast<int64_t>(row) * a.stride + rs;
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(r.base);
+  int head = static_cast<int>(((16u - (addr & 15u)) & 15u) >> 2);
+  r.head = head < r.n ? head : r.n;
+  r.nv = (r.n - r.head) >> 2;
+  r.tail0 = r.head + 4 * r.nv;
+  r.ntail = r.n - r.tail0;
+  r.vbase = reinterpret_cast<const f4*>(r.base + r.head);
+  r.ntiles = r.trivial ? 0 : (r.nv + TR_WG * TR_VEC - 1) / (TR_WG * TR_VEC);
+  return r;
+}
+
 // Valid elements of one tile of this thread: vector v holds positions
 // head + 4 * vi + c with vi = vi0 + v * TR_WG + tid; vectors past the window
 // (vi >= nv) were loaded from a clamped address and are ignored.
@@ -82,10 +127,45 @@ struct TileView {
   }
 };
 
+__device__ __forceinline__ TileView tile_view(const RowCtx& r, int t) {
+  return TileView{t * TR_WG * TR_VEC, r.nv, r.head};
+}
+
+// Tile t of row r, this thread's vectors; loads past the window use a clamped
+// (in-bounds) address and are masked out by TileView.
+__device__ __forceinline__ void load_tile(const RowCtx& r, int t, f4 (&x)[TR_VEC]) {
+#pragma unroll
+  for (int v = 0; v < TR_VEC; ++v) {
+    int vi = t * TR_WG * TR_VEC + v * TR_WG + static_cast<int>(threadIdx.x);
+    vi = vi < r.nv ? vi : r.nv - 1;
+    x[v] = __builtin_nontemporal_load(r.vbase + vi);
+  }
+}
+
+// The scalar head / tail element this thread carries (if any).
+struct Extra {
+  bool has;
+  uint32_t pos;
+  float x;
+};
+
+// Request everything a row starts with: the first TR_RING tiles and the
+// head / tail elements.
+__device__ __forceinline__ void prefetch_row(const RowCtx& r, f4 (&ring)[TR_RING][TR_VEC], Extra& e) {
+  const int tid = threadIdx.x;
+  e.has = tid < r.head + r.ntail;
+  e.pos = static_cast<uint32_t>(tid < r.head ? tid : r.tail0 + (tid - r.head));
+  e.x = e.has ? r.base[e.pos] : 0.0f;
+  if (r.ntiles > 0) {
+#pragma unroll
+    for (int u = 0; u < TR_RING; ++u) load_tile(r, u < r.ntiles ? u : r.ntiles - 1, ring[u]);
+  }
+}
+
 // Append, in wave-ballot order, every valid element of the thread's tile
 // that is >= lf, plus the optional extra (head / tail) element.
-__device__ __forceinline__ void append_tile(const f4 (&x)[TR_VEC], const TileView& tv, bool has_e, float xe,
-                                            uint32_t pe, float lf, uint64_t* cand, uint32_t* cnt) {
+__device__ __forceinline__ void append_tile(const f4 (&x)[TR_VEC], const TileView& tv, const Extra& e,
+                                            bool with_extra, float lf, uint64_t* cand, uint32_t* cnt) {
   bool keep[TR_VEC][4];
   uint64_t m[TR_VEC][4];
   uint32_t total = 0;
@@ -99,7 +179,7 @@ __device__ __forceinline__ void append_tile(const f4 (&x)[TR_VEC], const TileVie
       total += __popcll(m[v][c]);
     }
   }
-  const bool keep_e = has_e && xe >= lf;
+  const bool keep_e = with_extra && e.has && e.x >= lf;
   const uint64_t me = ballot(keep_e);
   total += __popcll(me);
   if (total == 0) return;
@@ -115,190 +195,133 @@ __device__ __forceinline__ void append_tile(const f4 (&x)[TR_VEC], const TileVie
       run += __popcll(m[v][c]);
     }
   }
-  if (keep_e) cand[base + run + lanes_below(me)] = rank_key(float_key(xe), pe);
+  if (keep_e) cand[base + run + lanes_below(me)] = rank_key(float_key(e.x), e.pos);
 }
 
-// Load this thread's share of cand[0, n) into registers (entries tid + e*WG).
-template <int MAXE>
-__device__ __forceinline__ int gather_entries(const uint64_t* cand, uint32_t n, uint64_t (&keys)[MAXE]) {
-  int nv = 0;
-#pragma unroll
-  for (int e = 0; e < MAXE; ++e) {
-    const uint32_t i = threadIdx.x + e * TR_WG;
-    if (i < n) {
-      keys[e] = cand[i];
-      nv = e + 1;
-    }
+// Entries of cand[] a thread handles per batch in compaction and emission.
+constexpr int TR_BATCH = 4;
+
+// Exact top-k of cand[0, c) (c > k): returns the separating key T (exactly k
+// keys >= T). The keys stay in LDS; every histogram pass re-reads them there.
+__device__ __forceinline__ uint64_t select_buffer(const uint64_t* cand, uint32_t c, uint32_t k,
+                                                  TopkRowsLds& s) {
+  const uint32_t tid = threadIdx.x;
+  uint64_t mn = ~0ull, mx = 0;
+  for (uint32_t i = tid; i < c; i += TR_WG) {
+    const uint64_t x = cand[i];
+    mn = x < mn ? x : mn;
+    mx = x > mx ? x : mx;
   }
-  return nv;
+  wg_range<TR_WG>(mn, mx, s.sel);
+  return wg_select<TR_WG>(
+      [&](auto&& f) {
+#pragma unroll 4
+        for (uint32_t i = tid; i < c; i += TR_WG) f(cand[i]);
+      },
+      k, mn, mx, s.sel);
 }
 
-template <int MAXE>
-__global__ __launch_bounds__(TR_WG, 3) void topk_rows_kernel(RowsArgs a) {
-  extern __shared__ uint64_t cand[];
-  __shared__ TopkRowsLds s;
-  // The select histogram overlays the candidate buffer: every select first
-  // copies the buffer's keys to registers.
-  uint32_t* hist = reinterpret_cast<uint32_t*>(cand);
-
-  const int row = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int n = a.seq_lens[row];
-  const int64_t rs = a.row_starts ? a.row_starts[row] : 0;
-  const int prow = a.row_to_batch ? a.row_to_batch[row] : row;
-  const uint32_t k = static_cast<uint32_t>(a.k);
-  const uint32_t P = static_cast<uint32_t>(a.page_size);
-  int32_t* out = a.out + static_cast<int64_t>(row) * a.k;
-  const int32_t* pt_row = a.page_table ? a.page_table + static_cast<int64_t>(prow) * a.pt_stride : nullptr;
-
-  if (n <= a.k) {  // every visible key is selected
-    for (int i = tid; i < a.k; i += TR_WG)
-      out[i] = (i < n) ? map_slot(pt_row, static_cast<uint32_t>(i), P, a.pdiv) : -1;
-    return;
-  }
-
-  const float* base = a.scores + static_cast<int64_t>(row) * a.stride + rs;
-  const uintptr_t addr = reinterpret_cast<uintptr_t>(base);
-  int head = static_cast<int>(((16u - (addr & 15u)) & 15u) >> 2);
-  head = head < n ? head : n;
-  const int nv = (n - head) >> 2;  // full float4 vectors
-  const int tail0 = head + 4 * nv;
-  const int ntail = n - tail0;
-  const f4* vbase = reinterpret_cast<const f4*>(base + head);
-  const int ntiles = (nv + TR_WG * TR_VEC - 1) / (TR_WG * TR_VEC);
-
-  // scalar head and tail elements ride along with the first tile
-  const bool has_e = tid < head + ntail;
-  uint32_t pe = 0;
-  float xe = 0.0f;
-  if (has_e) {
-    pe = static_cast<uint32_t>(tid < head ? tid : tail0 + (tid - head));
-    xe = base[pe];
-  }
-
-  // tile t, vector v of this thread; loads past the window use a clamped
-  // (in-bounds) address and are masked out by TileView
-  auto load_tile = [&](int t, f4 (&x)[TR_VEC]) {
-#pragma unroll
-    for (int v = 0; v < TR_VEC; ++v) {
-      int vi = t * TR_WG * TR_VEC + v * TR_WG + tid;
-      vi = vi < nv ? vi : nv - 1;
-      x[v] = __builtin_nontemporal_load(vbase + vi);
-    }
-  };
-  auto view = [&](int t) { return TileView{t * TR_WG * TR_VEC, nv, head}; };
-
-  // exact top-k of the buffer; returns the separating key T
-  auto select_buffer = [&](uint32_t c, uint64_t (&keys)[MAXE], int& nvk) -> uint64_t {
-    nvk = gather_entries<MAXE>(cand, c, keys);
-    __syncthreads();  // every thread holds its keys before the histogram overlays them
-    return wg_select<TR_WG>(
-        [&](auto&& f) {
-#pragma unroll
-          for (int e = 0; e < MAXE; ++e)
-            if (e < nvk) f(keys[e]);
-        },
-        k, hist, s.sel);
-  };
-
-  if (tid == 0) s.cnt = 0;
-  float lf = -__builtin_inff();
-
-  // After tile t: when the buffer would not take another tile, keep exactly
-  // the k best keys and raise the bound to the smallest kept value.
-  auto after_tile = [&](int t) {
-    __syncthreads();
-    const uint32_t c = s.cnt;
-    __syncthreads();
-    const bool last = (t + 1 == ntiles);
-    if (!last && c > k && c + TR_TILE > static_cast<uint32_t>(a.cap)) {
-      uint64_t keys[MAXE];
-      int nvk;
-      const uint64_t T = select_buffer(c, keys, nvk);
-      if (tid == 0) {
-        s.cnt = 0;
-        s.minkey = 0xffffffffu;
-      }
-      __syncthreads();
-      uint32_t mymin = 0xffffffffu;
-#pragma unroll
-      for (int e = 0; e < MAXE; ++e) {
-        const bool keep = (e < nvk) && keys[e] >= T;
-        const uint64_t mk = ballot(keep);
-        if (mk == 0) continue;
-        uint32_t wb = 0;
-        if (lane_id() == 0) wb = atomicAdd(&s.cnt, static_cast<uint32_t>(__popcll(mk)));
-        wb = uniform(wb);
-        const uint32_t at = wb + lanes_below(mk);
-        if (keep && at < static_cast<uint32_t>(a.cap)) {
-          cand[at] = keys[e];
-          const uint32_t vk = rank_vkey(keys[e]);
-          mymin = vk < mymin ? vk : mymin;
-        }
-      }
-      mymin = wave_min_u32(mymin);
-      if (lane_id() == 0) atomicMin(&s.minkey, mymin);
-      __syncthreads();
-      lf = key_float(s.minkey);
-      __syncthreads();
-    }
-  };
-
-  // Ring of TR_RING tiles in flight: tile t lives in slot t % TR_RING, is
-  // consumed in place, and its slot is refilled with tile t + TR_RING right
-  // after (no register copies, so a tile only waits for its own loads).
-  f4 ring[TR_RING][TR_VEC];
-  if (ntiles > 0) {
-#pragma unroll
-    for (int u = 0; u < TR_RING; ++u) load_tile(u < ntiles ? u : ntiles - 1, ring[u]);
+// After tile t of row r: when the buffer would not take another tile, keep
+// exactly the k best keys and raise the bound to the smallest kept value.
+// Compaction is in place, in batches of TR_BATCH * TR_WG entries: a batch is
+// read completely (barrier) before its kept keys are written, and they land
+// below the batch's end, where every entry has been read already.
+__device__ __forceinline__ void after_tile(const RowCtx& r, int t, uint32_t k, int cap, float& lf,
+                                           uint64_t* cand, TopkRowsLds& s) {
+  __syncthreads();
+  const uint32_t c = s.cnt;
+  __syncthreads();
+  if (t + 1 == r.ntiles || c <= k || c + TR_TILE <= static_cast<uint32_t>(cap)) return;
+  const uint32_t tid = threadIdx.x;
+  const uint64_t T = select_buffer(cand, c, k, s);
+  if (tid == 0) {
+    s.cnt = 0;
+    s.minkey = 0xffffffffu;
   }
   __syncthreads();
+  uint32_t mymin = 0xffffffffu;
+  for (uint32_t b0 = 0; b0 < c; b0 += TR_BATCH * TR_WG) {
+    uint64_t key[TR_BATCH];
+    bool keep[TR_BATCH];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < TR_BATCH; ++j) {
+      const uint32_t i = b0 + j * TR_WG + tid;
+      key[j] = i < c ? cand[i] : 0ull;
+      keep[j] = i < c && key[j] >= T;
+      mine += keep[j];
+    }
+    __syncthreads();
+    uint32_t at = wave_reserve(mine, &s.cnt);
+#pragma unroll
+    for (int j = 0; j < TR_BATCH; ++j) {
+      if (keep[j]) {
+        cand[at++] = key[j];
+        const uint32_t vk = rank_vkey(key[j]);
+        mymin = vk < mymin ? vk : mymin;
+      }
+    }
+  }
+  mymin = wave_min_u32(mymin);
+  if (lane_id() == 0) atomicMin(&s.minkey, mymin);
+  __syncthreads();
+  lf = key_float(s.minkey);
+}
 
+// Stream all tiles of row r (its first TR_RING tiles and the extra element are
+// already requested) into the candidate buffer.
+__device__ __forceinline__ void stream_row(const RowCtx& r, f4 (&ring)[TR_RING][TR_VEC], const Extra& ex,
+                                           uint32_t k, int cap, uint64_t* cand, TopkRowsLds& s) {
+  float lf = -__builtin_inff();
   // First tile (plus the head / tail elements): when more data follows, one
   // histogram pass over these elements bounds the k-th value; then append
   // what passes the bound.
   {
-    const TileView tv = view(0);
-    const bool has_tile = ntiles > 0;
-    const int n0 = 4 * min(nv, TR_WG * TR_VEC) + head + ntail;
-    if (ntiles > 1 && n0 > a.k) {
-      const uint64_t bound = wg_select<TR_WG>(
-          [&](auto&& f) {
+    const TileView tv = tile_view(r, 0);
+    const int n0 = 4 * min(r.nv, TR_WG * TR_VEC) + r.head + r.ntail;
+    if (r.ntiles > 1 && n0 > static_cast<int>(k)) {
+      auto each = [&](auto&& f) {
 #pragma unroll
-            for (int v = 0; v < TR_VEC; ++v)
-              if (tv.valid(v)) {
+        for (int v = 0; v < TR_VEC; ++v)
+          if (tv.valid(v)) {
 #pragma unroll
-                for (int c = 0; c < 4; ++c) f(rank_key(float_key(ring[0][v][c]), tv.pos(v, c)));
-              }
-            if (has_e) f(rank_key(float_key(xe), pe));
-          },
-          k, hist, s.sel, 1);
+            for (int c = 0; c < 4; ++c) f(rank_key(float_key(ring[0][v][c]), tv.pos(v, c)));
+          }
+        if (ex.has) f(rank_key(float_key(ex.x), ex.pos));
+      };
+      uint64_t mn = ~0ull, mx = 0;
+      each([&](uint64_t key) {
+        mn = key < mn ? key : mn;
+        mx = key > mx ? key : mx;
+      });
+      wg_range<TR_WG>(mn, mx, s.sel);
+      const uint64_t bound = wg_select<TR_WG>(each, k, mn, mx, s.sel, true);
       lf = key_float(rank_vkey(bound));
     }
-    if (has_tile) {
-      append_tile(ring[0], tv, has_e, xe, pe, lf, cand, &s.cnt);
+    if (r.ntiles > 0) {
+      append_tile(ring[0], tv, ex, true, lf, cand, &s.cnt);
       __builtin_amdgcn_sched_barrier(0);
-      if (TR_RING < ntiles) load_tile(TR_RING, ring[0]);
-      after_tile(0);
+      if (TR_RING < r.ntiles) load_tile(r, TR_RING, ring[0]);
+      after_tile(r, 0, k, cap, lf, cand, s);
     } else {
       const f4 none[TR_VEC] = {};
-      append_tile(none, TileView{0, 0, head}, has_e, xe, pe, lf, cand, &s.cnt);
+      append_tile(none, TileView{0, 0, r.head}, ex, true, lf, cand, &s.cnt);
       __syncthreads();
     }
   }
-
   // steady state: tiles t0 .. t0 + TR_RING - 1 (slot t % TR_RING), every
   // refill in range, so control flow is uniform
+  const Extra none_e{false, 0u, 0.0f};
   int t0 = 1;
-  for (; t0 + 2 * TR_RING <= ntiles; t0 += TR_RING) {
+  for (; t0 + 2 * TR_RING <= r.ntiles; t0 += TR_RING) {
 #pragma unroll
     for (int u = 0; u < TR_RING; ++u) {
       const int t = t0 + u;
       const int slot = (1 + u) % TR_RING;
-      append_tile(ring[slot], view(t), false, 0.0f, 0u, lf, cand, &s.cnt);
+      append_tile(ring[slot], tile_view(r, t), none_e, false, lf, cand, &s.cnt);
       __builtin_amdgcn_sched_barrier(0);
-      load_tile(t + TR_RING, ring[slot]);
-      after_tile(t);
+      load_tile(r, t + TR_RING, ring[slot]);
+      after_tile(r, t, k, cap, lf, cand, s);
     }
   }
   // drain: fewer than 2 * TR_RING tiles remain
@@ -306,45 +329,127 @@ __global__ __launch_bounds__(TR_WG, 3) void topk_rows_kernel(RowsArgs a) {
   for (int u = 0; u < 2 * TR_RING; ++u) {
     const int t = t0 + u;
     const int slot = (1 + u) % TR_RING;
-    if (t < ntiles) {
-      append_tile(ring[slot], view(t), false, 0.0f, 0u, lf, cand, &s.cnt);
-      if (t + TR_RING < ntiles) load_tile(t + TR_RING, ring[slot]);
-      after_tile(t);
+    if (t < r.ntiles) {
+      append_tile(ring[slot], tile_view(r, t), none_e, false, lf, cand, &s.cnt);
+      if (t + TR_RING < r.ntiles) load_tile(r, t + TR_RING, ring[slot]);
+      after_tile(r, t, k, cap, lf, cand, s);
     }
-  }
-
-  // final selection over the buffer
-  const uint32_t c = s.cnt;
-  if (tid == 0) s.ocnt = 0;
-  __syncthreads();
-  if (c <= k) {
-    // only reachable with NaN inputs (outside the domain): emit what is there
-    for (uint32_t i = tid; i < k; i += TR_WG)
-      out[i] = (i < c) ? map_slot(pt_row, rank_pos(cand[i]), P, a.pdiv) : -1;
-    return;
-  }
-  uint64_t keys[MAXE];
-  int nvk;
-  const uint64_t T = select_buffer(c, keys, nvk);
-#pragma unroll
-  for (int e = 0; e < MAXE; ++e) {
-    const bool keep = (e < nvk) && keys[e] >= T;
-    const uint64_t mk = ballot(keep);
-    if (mk == 0) continue;
-    uint32_t wb = 0;
-    if (lane_id() == 0) wb = atomicAdd(&s.ocnt, static_cast<uint32_t>(__popcll(mk)));
-    wb = uniform(wb);
-    const uint32_t at = wb + lanes_below(mk);
-    if (keep && at < k) out[at] = map_slot(pt_row, rank_pos(keys[e]), P, a.pdiv);
   }
 }
 
-// Candidate buffer sizing: room for the k kept keys plus two whole tiles
-// (one tile of slack between compactions), and never less than the select
-// histogram that overlays it.
-static inline int rows_cap(int k) {
-  const int c = (k > TR_TILE ? k : TR_TILE) + 2 * TR_TILE + 8;
-  return c > kSelBins / 2 ? c : kSelBins / 2;
+// Final exact select over the buffer and the page-transform epilogue, then
+// the buffer and counters are reset for the workgroup's next row.
+__device__ __forceinline__ void finish_row(const RowCtx& r, const RowsArgs& a, uint64_t* cand,
+                                           TopkRowsLds& s) {
+  const uint32_t tid = threadIdx.x;
+  const uint32_t k = static_cast<uint32_t>(a.k);
+  const uint32_t P = static_cast<uint32_t>(a.page_size);
+  const uint32_t c = s.cnt;  // stable: the last after_tile ended with a barrier
+  if (c <= k) {
+    // only reachable with NaN inputs (outside the domain): emit what is there
+    for (uint32_t i = tid; i < k; i += TR_WG)
+      r.out[i] = (i < c) ? map_slot(r.pt_row, rank_pos(cand[i]), P, a.pdiv) : -1;
+  } else {
+    const uint64_t T = select_buffer(cand, c, k, s);
+    // per batch: one reservation per wave, then independent page-table
+    // gathers and stores
+    for (uint32_t b0 = 0; b0 < c; b0 += TR_BATCH * TR_WG) {
+      uint32_t pos[TR_BATCH];
+      bool keep[TR_BATCH];
+      uint32_t mine = 0;
+#pragma unroll
+      for (int j = 0; j < TR_BATCH; ++j) {
+        const uint32_t i = b0 + j * TR_WG + tid;
+        const uint64_t key = i < c ? cand[i] : 0ull;
+        keep[j] = i < c && key >= T;
+        pos[j] = rank_pos(key);
+        mine += keep[j];
+      }
+      uint32_t at = wave_reserve(mine, &s.ocnt);
+      int32_t slot[TR_BATCH];
+#pragma unroll
+      for (int j = 0; j < TR_BATCH; ++j)
+        if (keep[j]) slot[j] = map_slot(r.pt_row, pos[j], P, a.pdiv);
+#pragma unroll
+      for (int j = 0; j < TR_BATCH; ++j)
+        if (keep[j]) r.out[at++] = slot[j];
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    s.cnt = 0;
+    s.ocnt = 0;
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(TR_WG, 3) void topk_rows_kernel(RowsArgs a) {
+  extern __shared__ uint64_t cand[];
+  __shared__ TopkRowsLds s;
+  const int tid = threadIdx.x;
+  const uint32_t k = static_cast<uint32_t>(a.k);
+  const uint32_t P = static_cast<uint32_t>(a.page_size);
+
+  wg_select_init<TR_WG>(s.sel);
+  if (tid == 0) {
+    s.cnt = 0;
+    s.ocnt = 0;
+  }
+  __syncthreads();
+
+  f4 ring[TR_RING][TR_VEC];
+  Extra ex;
+  RowCtx cur = row_setup(a, blockIdx.x);
+  if (!cur.trivial) prefetch_row(cur, ring, ex);
+  for (;;) {
+    const int nrow = cur.row + static_cast<int>(gridDim.x);
+    const bool has_next = nrow < a.rows;
+    if (cur.trivial) {
+      for (int i = tid; i < a.k; i += TR_WG)
+        cur.out[i] = (i < cur.n) ? map_slot(cur.pt_row, static_cast<uint32_t>(i), P, a.pdiv) : -1;
+      if (!has_next) break;
+      cur = row_setup(a, nrow);
+      if (!cur.trivial) prefetch_row(cur, ring, ex);
+      continue;
+    }
+    stream_row(cur, ring, ex, k, a.cap, cand, s);
+    // the ring is free: request the next row before finishing this one
+    RowCtx nxt;
+    if (has_next) {
+      nxt = row_setup(a, nrow);
+      if (!nxt.trivial) prefetch_row(nxt, ring, ex);
+    }
+    finish_row(cur, a, cand, s);
+    if (!has_next) break;
+    cur = nxt;
+  }
+}
+
+// Candidate buffer sizing: room for the k kept keys plus one and a half
+// tiles (half a tile of slack between compactions).
+static inline int rows_cap(int k) { return (k > TR_TILE ? k : TR_TILE) + TR_TILE + TR_TILE / 2 + 8; }
+
+// Workgroups of topk_rows_kernel resident at once on the current device for
+// `lds` bytes of dynamic LDS, as the runtime computes occupancy. Cached per
+// (device, size).
+static int resident_workgroups(const void* kernel, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::pair<int, size_t>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(dev, lds);
+  const auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, TR_WG, lds) != hipSuccess || per_cu <= 0)
+    per_cu = 1;
+  (void)hipGetLastError();
+  const int v = per_cu * cus;
+  cache.emplace(key, v);
+  return v;
 }
 
 int launch_topk_rows(const float* scores, int64_t stride, int rows, const int32_t* seq_lens,
@@ -354,6 +459,7 @@ int launch_topk_rows(const float* scores, int64_t stride, int rows, const int32_
   RowsArgs a;
   a.scores = scores;
   a.stride = stride;
+  a.rows = rows;
   a.seq_lens = seq_lens;
   a.row_starts = row_starts;
   a.row_to_batch = row_to_batch;
@@ -365,20 +471,13 @@ int launch_topk_rows(const float* scores, int64_t stride, int rows, const int32_
   a.out = out;
   a.cap = rows_cap(k);
   const size_t lds = static_cast<size_t>(a.cap) * sizeof(uint64_t);
-  const int maxe_needed = (a.cap + TR_WG - 1) / TR_WG;
-  if (maxe_needed <= 25) {  // k <= 2048
-    static std::atomic<size_t> granted25{0};
-    if (allow_dynamic_lds(reinterpret_cast<const void*>(&topk_rows_kernel<25>), lds, granted25) != hipSuccess)
-      return -4;
-    (void)hipGetLastError();
-    hipLaunchKernelGGL(topk_rows_kernel<25>, dim3(rows), dim3(TR_WG), lds, stream, a);
-  } else {  // k <= 8192
-    static std::atomic<size_t> granted49{0};
-    if (allow_dynamic_lds(reinterpret_cast<const void*>(&topk_rows_kernel<49>), lds, granted49) != hipSuccess)
-      return -4;
-    (void)hipGetLastError();
-    hipLaunchKernelGGL(topk_rows_kernel<49>, dim3(rows), dim3(TR_WG), lds, stream, a);
-  }
+  const void* kern = reinterpret_cast<const void*>(&topk_rows_kernel);
+  static std::atomic<size_t> granted{0};
+  if (allow_dynamic_lds(kern, lds, granted) != hipSuccess) return -4;
+  const int res = resident_workgroups(kern, lds);
+  const int grid = rows < res ? rows : res;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(topk_rows_kernel, dim3(grid), dim3(TR_WG), lds, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
