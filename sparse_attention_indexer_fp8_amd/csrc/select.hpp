@@ -69,8 +69,10 @@ __device__ __forceinline__ void wg_range(uint64_t& mn, uint64_t& mx, SelectLds& 
 // once for every key this thread owns, the same set on every call.
 // Precondition: the set holds more than k keys, k >= 1.
 //
-// Returns T such that exactly k keys are >= T. With bound_only it stops after
-// the first histogram and returns a lower bound: at least k keys are >= T.
+// Returns T such that exactly k keys are >= T. With slack > 0 it may stop
+// earlier, at a bound T with k <= (keys >= T) <= k + slack: it stops as soon
+// as the keys in and above the current range are few enough (slack = ~0u
+// stops after the first histogram).
 //
 // Method: each iteration histograms the undecided keys into kSelBins equal
 // bins covering exactly their range [lo, hi], so they spread over many bins
@@ -83,7 +85,7 @@ __device__ __forceinline__ void wg_range(uint64_t& mn, uint64_t& mx, SelectLds& 
 // most 7 run; one or two are typical.
 template <int WG, class ForEach>
 __device__ __forceinline__ uint64_t wg_select(ForEach&& for_each, uint32_t k, uint64_t lo, uint64_t hi, SelectLds& s,
-                              bool bound_only = false) {
+                              uint32_t slack = 0) {
   constexpr int PL = kSelBins / kWave;  // bins per lane of wave 0
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
@@ -129,7 +131,7 @@ __device__ __forceinline__ uint64_t wg_select(ForEach&& for_each, uint32_t k, ui
     lo += static_cast<uint64_t>(bin) << shift;
     const uint64_t top = lo + ((1ull << shift) - 1ull);
     hi = top < hi ? top : hi;
-    if (bound_only || cnt == kk) break;
+    if (cnt - kk <= slack) break;  // keys >= lo: (k - kk) + cnt
     if (cnt <= static_cast<uint32_t>(kSelMembers)) {
       // few keys left: gather them and let one wave rank them
       const uint64_t blo = lo, bhi = hi;

@@ -7,24 +7,31 @@
 // until the page transform in the epilogue.
 //
 // Design (persistent workgroups, one row at a time each, one pass over HBM):
-//  * Workgroup g handles rows g, g + G, g + 2G, ... for a grid of G.
+//  * Workgroup g handles rows g, g + G, g + 2G, ... for a grid of G (the
+//    number of workgroups resident at once).
 //  * A row's window is streamed in tiles of TR_TILE floats with 16-byte
 //    loads, TR_RING tiles in flight. A scalar head (up to 3 elements, up to
 //    the first 16-byte boundary) and tail (up to 3 elements) make the stride
 //    and the start column free: no alignment is required.
-//  * A running lower bound L on the row's k-th value filters each element with
-//    one float compare. Survivors are appended to an LDS candidate buffer as
-//    unique 64-bit keys (value key, inverted position): a wave ballot plus
-//    prefix count and one LDS atomic per wave.
-//  * The first tile sets L with one histogram pass over its elements in
-//    registers (the edge of the bin where the count from the top reaches k).
-//    When the buffer would overflow, an exact select keeps its k best keys,
-//    and L becomes the smallest kept value. L never exceeds the row's true
-//    k-th value, so no winner is dropped.
-//  * At the end an exact select over the buffer gives the top k, and the
-//    epilogue maps positions through the page table. Before that, the first
-//    tiles of the workgroup's next row are already requested, so the select
-//    overlaps memory traffic.
+//  * A running lower bound L filters each element with one float compare.
+//    Survivors are appended to an LDS candidate buffer as unique 64-bit keys
+//    (value key, inverted position): a wave ballot plus prefix count and one
+//    LDS atomic per wave.
+//  * The first tile sets L with one histogram pass over its n0 elements in
+//    registers: the edge of the bin where the count from the top reaches a
+//    rank r. With r = k, L is a proven lower bound on the row's k-th value.
+//    A long row first tries r ~ 2 k n0 / n + 16 (about 2k of the row's n
+//    values are expected above it). The buffer then holds every element
+//    >= L, so if it ends with at least k keys, L was below the k-th value and
+//    the result is exact; otherwise the row is streamed again with r = k.
+//  * When the buffer would overflow, a select finds a bound with between k
+//    and k + slack keys above it, the buffer keeps those, and L becomes the
+//    smallest kept value (never above the row's k-th value).
+//  * At the end an exact select packs the k best keys to the front of the
+//    buffer; positions go through the page table and are stored coalesced.
+//    The first tiles of the workgroup's next row are requested before the
+//    select, the rest after the page-table gathers, so the gathers never
+//    wait behind a whole ring of loads.
 //  * Rows with n <= k need no scores: every position is selected.
 #include "common.hpp"
 #include "launch.hpp"
@@ -40,6 +47,9 @@ constexpr int TR_WG = 256;
 constexpr int TR_VEC = 2;                    // float4 loads per thread per tile
 constexpr int TR_TILE = TR_WG * TR_VEC * 4;  // floats per tile (8 KB)
 constexpr int TR_RING = 4;                   // tiles in flight per workgroup
+constexpr int TR_HEAD = 2;                   // next-row tiles requested before the final select
+constexpr int TR_BATCH = 4;                  // buffer entries per thread per compaction batch
+constexpr int TR_EMIT = 4;                   // outputs per thread per emission round
 
 struct RowsArgs {
   const float* scores;
@@ -70,7 +80,6 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 struct TopkRowsLds {
   SelectLds sel;
   uint32_t cnt;
-  uint32_t ocnt;
   uint32_t minkey;
 };
 
@@ -149,16 +158,24 @@ struct Extra {
   float x;
 };
 
-// Request everything a row starts with: the first TR_RING tiles and the
-// head / tail elements.
-__device__ __forceinline__ void prefetch_row(const RowCtx& r, f4 (&ring)[TR_RING][TR_VEC], Extra& e) {
+// Request the start of a row: its head / tail elements and tiles
+// [0, TR_HEAD). prefetch_tail requests tiles [TR_HEAD, TR_RING). Tiles past
+// the row's last repeat the last one (the loads stay in bounds).
+__device__ __forceinline__ void prefetch_head(const RowCtx& r, f4 (&ring)[TR_RING][TR_VEC], Extra& e) {
   const int tid = threadIdx.x;
   e.has = tid < r.head + r.ntail;
   e.pos = static_cast<uint32_t>(tid < r.head ? tid : r.tail0 + (tid - r.head));
   e.x = e.has ? r.base[e.pos] : 0.0f;
   if (r.ntiles > 0) {
 #pragma unroll
-    for (int u = 0; u < TR_RING; ++u) load_tile(r, u < r.ntiles ? u : r.ntiles - 1, ring[u]);
+    for (int u = 0; u < TR_HEAD; ++u) load_tile(r, u < r.ntiles ? u : r.ntiles - 1, ring[u]);
+  }
+}
+
+__device__ __forceinline__ void prefetch_tail(const RowCtx& r, f4 (&ring)[TR_RING][TR_VEC]) {
+  if (r.ntiles > 0) {
+#pragma unroll
+    for (int u = TR_HEAD; u < TR_RING; ++u) load_tile(r, u < r.ntiles ? u : r.ntiles - 1, ring[u]);
   }
 }
 
@@ -198,13 +215,11 @@ __device__ __forceinline__ void append_tile(const f4 (&x)[TR_VEC], const TileVie
   if (keep_e) cand[base + run + lanes_below(me)] = rank_key(float_key(e.x), e.pos);
 }
 
-// Entries of cand[] a thread handles per batch in compaction and emission.
-constexpr int TR_BATCH = 4;
-
-// Exact top-k of cand[0, c) (c > k): returns the separating key T (exactly k
-// keys >= T). The keys stay in LDS; every histogram pass re-reads them there.
+// Select over cand[0, c) (c > k): a key T with k <= (keys >= T) <= k + slack
+// (exactly k for slack 0). The keys stay in LDS; every histogram pass
+// re-reads them there.
 __device__ __forceinline__ uint64_t select_buffer(const uint64_t* cand, uint32_t c, uint32_t k,
-                                                  TopkRowsLds& s) {
+                                                  uint32_t slack, TopkRowsLds& s) {
   const uint32_t tid = threadIdx.x;
   uint64_t mn = ~0ull, mx = 0;
   for (uint32_t i = tid; i < c; i += TR_WG) {
@@ -218,22 +233,17 @@ __device__ __forceinline__ uint64_t select_buffer(const uint64_t* cand, uint32_t
 #pragma unroll 4
         for (uint32_t i = tid; i < c; i += TR_WG) f(cand[i]);
       },
-      k, mn, mx, s.sel);
+      k, mn, mx, s.sel, slack);
 }
 
-// After tile t of row r: when the buffer would not take another tile, keep
-// exactly the k best keys and raise the bound to the smallest kept value.
-// Compaction is in place, in batches of TR_BATCH * TR_WG entries: a batch is
-// read completely (barrier) before its kept keys are written, and they land
-// below the batch's end, where every entry has been read already.
-__device__ __forceinline__ void after_tile(const RowCtx& r, int t, uint32_t k, int cap, float& lf,
-                                           uint64_t* cand, TopkRowsLds& s) {
-  __syncthreads();
-  const uint32_t c = s.cnt;
-  __syncthreads();
-  if (t + 1 == r.ntiles || c <= k || c + TR_TILE <= static_cast<uint32_t>(cap)) return;
+// Keep the keys >= T of cand[0, c), packed to the front of the buffer (in no
+// particular order); s.cnt becomes their count. Returns the smallest kept
+// value key. Every thread must have read c before the call.
+// In place, in batches of TR_BATCH * TR_WG entries: a batch is read
+// completely (barrier) before its kept keys are written, and they land below
+// the batch's end, where every entry has been read already.
+__device__ __forceinline__ uint32_t keep_compact(uint64_t* cand, uint32_t c, uint64_t T, TopkRowsLds& s) {
   const uint32_t tid = threadIdx.x;
-  const uint64_t T = select_buffer(cand, c, k, s);
   if (tid == 0) {
     s.cnt = 0;
     s.minkey = 0xffffffffu;
@@ -265,21 +275,48 @@ __device__ __forceinline__ void after_tile(const RowCtx& r, int t, uint32_t k, i
   mymin = wave_min_u32(mymin);
   if (lane_id() == 0) atomicMin(&s.minkey, mymin);
   __syncthreads();
-  lf = key_float(s.minkey);
+  return s.minkey;
+}
+
+// After tile t of row r: when the buffer would not take another tile, keep
+// between k and k + (cap - TR_TILE - k) / 2 of its best keys (so at least
+// half the spare room is freed) and raise the bound to the smallest kept
+// value.
+__device__ __forceinline__ void after_tile(const RowCtx& r, int t, uint32_t k, int cap, float& lf,
+                                           uint64_t* cand, TopkRowsLds& s) {
+  __syncthreads();
+  const uint32_t c = s.cnt;
+  __syncthreads();
+  if (t + 1 == r.ntiles || c <= k || c + TR_TILE <= static_cast<uint32_t>(cap)) return;
+  const uint32_t slack = (static_cast<uint32_t>(cap) - TR_TILE - k) / 2;
+  const uint64_t T = select_buffer(cand, c, k, slack, s);
+  lf = key_float(keep_compact(cand, c, T, s));
 }
 
 // Stream all tiles of row r (its first TR_RING tiles and the extra element are
-// already requested) into the candidate buffer.
-__device__ __forceinline__ void stream_row(const RowCtx& r, f4 (&ring)[TR_RING][TR_VEC], const Extra& ex,
-                                           uint32_t k, int cap, uint64_t* cand, TopkRowsLds& s) {
+// already requested) into the candidate buffer. With `estimate`, a long row's
+// first-tile bound uses the rank r ~ 2 k n0 / n + 16 instead of k; returns
+// whether it did (then the caller must check that at least k keys were kept).
+__device__ __forceinline__ bool stream_row(const RowCtx& r, f4 (&ring)[TR_RING][TR_VEC], const Extra& ex,
+                                           uint32_t k, int cap, bool estimate, uint64_t* cand,
+                                           TopkRowsLds& s) {
   float lf = -__builtin_inff();
+  bool estimated = false;
   // First tile (plus the head / tail elements): when more data follows, one
-  // histogram pass over these elements bounds the k-th value; then append
+  // histogram pass over these elements bounds the rank-r value; then append
   // what passes the bound.
   {
     const TileView tv = tile_view(r, 0);
     const int n0 = 4 * min(r.nv, TR_WG * TR_VEC) + r.head + r.ntail;
     if (r.ntiles > 1 && n0 > static_cast<int>(k)) {
+      uint32_t rank = k;
+      if (estimate) {
+        const uint64_t want = (2ull * k * static_cast<uint64_t>(n0) + r.n - 1) / static_cast<uint64_t>(r.n) + 16u;
+        if (want < k) {
+          rank = static_cast<uint32_t>(want);
+          estimated = true;
+        }
+      }
       auto each = [&](auto&& f) {
 #pragma unroll
         for (int v = 0; v < TR_VEC; ++v)
@@ -295,7 +332,7 @@ __device__ __forceinline__ void stream_row(const RowCtx& r, f4 (&ring)[TR_RING][
         mx = key > mx ? key : mx;
       });
       wg_range<TR_WG>(mn, mx, s.sel);
-      const uint64_t bound = wg_select<TR_WG>(each, k, mn, mx, s.sel, true);
+      const uint64_t bound = wg_select<TR_WG>(each, rank, mn, mx, s.sel, ~0u);
       lf = key_float(rank_vkey(bound));
     }
     if (r.ntiles > 0) {
@@ -335,99 +372,101 @@ __device__ __forceinline__ void stream_row(const RowCtx& r, f4 (&ring)[TR_RING][
       after_tile(r, t, k, cap, lf, cand, s);
     }
   }
+  return estimated;
 }
 
-// Final exact select over the buffer and the page-transform epilogue, then
-// the buffer and counters are reset for the workgroup's next row.
-__device__ __forceinline__ void finish_row(const RowCtx& r, const RowsArgs& a, uint64_t* cand,
-                                           TopkRowsLds& s) {
-  const uint32_t tid = threadIdx.x;
-  const uint32_t k = static_cast<uint32_t>(a.k);
+// Outputs of a row with n <= k: positions 0 .. n - 1 mapped, then -1.
+__device__ __forceinline__ void emit_all(const RowCtx& r, const RowsArgs& a) {
   const uint32_t P = static_cast<uint32_t>(a.page_size);
-  const uint32_t c = s.cnt;  // stable: the last after_tile ended with a barrier
-  if (c <= k) {
-    // only reachable with NaN inputs (outside the domain): emit what is there
-    for (uint32_t i = tid; i < k; i += TR_WG)
-      r.out[i] = (i < c) ? map_slot(r.pt_row, rank_pos(cand[i]), P, a.pdiv) : -1;
-  } else {
-    const uint64_t T = select_buffer(cand, c, k, s);
-    // per batch: one reservation per wave, then independent page-table
-    // gathers and stores
-    for (uint32_t b0 = 0; b0 < c; b0 += TR_BATCH * TR_WG) {
-      uint32_t pos[TR_BATCH];
-      bool keep[TR_BATCH];
-      uint32_t mine = 0;
-#pragma unroll
-      for (int j = 0; j < TR_BATCH; ++j) {
-        const uint32_t i = b0 + j * TR_WG + tid;
-        const uint64_t key = i < c ? cand[i] : 0ull;
-        keep[j] = i < c && key >= T;
-        pos[j] = rank_pos(key);
-        mine += keep[j];
-      }
-      uint32_t at = wave_reserve(mine, &s.ocnt);
-      int32_t slot[TR_BATCH];
-#pragma unroll
-      for (int j = 0; j < TR_BATCH; ++j)
-        if (keep[j]) slot[j] = map_slot(r.pt_row, pos[j], P, a.pdiv);
-#pragma unroll
-      for (int j = 0; j < TR_BATCH; ++j)
-        if (keep[j]) r.out[at++] = slot[j];
-    }
-  }
-  __syncthreads();
-  if (tid == 0) {
-    s.cnt = 0;
-    s.ocnt = 0;
-  }
-  __syncthreads();
+  for (int i = threadIdx.x; i < a.k; i += TR_WG)
+    r.out[i] = (i < r.n) ? map_slot(r.pt_row, static_cast<uint32_t>(i), P, a.pdiv) : -1;
 }
 
-__global__ __launch_bounds__(TR_WG, 3) void topk_rows_kernel(RowsArgs a) {
+__global__ __launch_bounds__(TR_WG, 4) void topk_rows_kernel(RowsArgs a) {
   extern __shared__ uint64_t cand[];
   __shared__ TopkRowsLds s;
-  const int tid = threadIdx.x;
+  const uint32_t tid = threadIdx.x;
   const uint32_t k = static_cast<uint32_t>(a.k);
   const uint32_t P = static_cast<uint32_t>(a.page_size);
 
   wg_select_init<TR_WG>(s.sel);
-  if (tid == 0) {
-    s.cnt = 0;
-    s.ocnt = 0;
-  }
+  if (tid == 0) s.cnt = 0;
   __syncthreads();
 
   f4 ring[TR_RING][TR_VEC];
   Extra ex;
   RowCtx cur = row_setup(a, blockIdx.x);
-  if (!cur.trivial) prefetch_row(cur, ring, ex);
+  if (!cur.trivial) {
+    prefetch_head(cur, ring, ex);
+    prefetch_tail(cur, ring);
+  }
   for (;;) {
     const int nrow = cur.row + static_cast<int>(gridDim.x);
     const bool has_next = nrow < a.rows;
     if (cur.trivial) {
-      for (int i = tid; i < a.k; i += TR_WG)
-        cur.out[i] = (i < cur.n) ? map_slot(cur.pt_row, static_cast<uint32_t>(i), P, a.pdiv) : -1;
+      emit_all(cur, a);
       if (!has_next) break;
       cur = row_setup(a, nrow);
-      if (!cur.trivial) prefetch_row(cur, ring, ex);
+      if (!cur.trivial) {
+        prefetch_head(cur, ring, ex);
+        prefetch_tail(cur, ring);
+      }
       continue;
     }
-    stream_row(cur, ring, ex, k, a.cap, cand, s);
-    // the ring is free: request the next row before finishing this one
-    RowCtx nxt;
+    const bool estimated = stream_row(cur, ring, ex, k, a.cap, true, cand, s);
+    uint32_t c = s.cnt;  // stable: the last after_tile ended with a barrier
+    if (estimated && c < k) {
+      // the estimated bound was above the row's k-th value: stream the row
+      // again with the proven first-tile bound
+      __syncthreads();
+      if (tid == 0) s.cnt = 0;
+      __syncthreads();
+      prefetch_head(cur, ring, ex);
+      prefetch_tail(cur, ring);
+      stream_row(cur, ring, ex, k, a.cap, false, cand, s);
+      c = s.cnt;
+    }
+    // the ring is free: request the start of the next row
+    RowCtx nxt = cur;
+    bool pre = false;
     if (has_next) {
       nxt = row_setup(a, nrow);
-      if (!nxt.trivial) prefetch_row(nxt, ring, ex);
+      pre = !nxt.trivial;
     }
-    finish_row(cur, a, cand, s);
+    if (pre) prefetch_head(nxt, ring, ex);
+    // exactly the k best keys to cand[0, k); c < k only with NaN inputs
+    // (outside the domain), then what is there is emitted and padded
+    if (c > k) keep_compact(cand, c, select_buffer(cand, c, k, 0, s), s);
+    const uint32_t m = c < k ? c : k;
+    for (uint32_t b0 = 0; b0 < k; b0 += TR_EMIT * TR_WG) {
+      int32_t slot[TR_EMIT];
+#pragma unroll
+      for (int j = 0; j < TR_EMIT; ++j) {
+        const uint32_t i = b0 + j * TR_WG + tid;
+        slot[j] = i < m ? map_slot(cur.pt_row, rank_pos(cand[i]), P, a.pdiv) : -1;
+      }
+      if (b0 == 0 && pre) prefetch_tail(nxt, ring);
+#pragma unroll
+      for (int j = 0; j < TR_EMIT; ++j) {
+        const uint32_t i = b0 + j * TR_WG + tid;
+        if (i < k) cur.out[i] = slot[j];
+      }
+    }
+    __syncthreads();
+    if (tid == 0) s.cnt = 0;
+    __syncthreads();
     if (!has_next) break;
     cur = nxt;
   }
 }
 
-// Candidate buffer sizing: room for the k kept keys plus one and a half
-// tiles (half a tile of slack between compactions).
-static inline int rows_cap(int k) { return (k > TR_TILE ? k : TR_TILE) + TR_TILE + TR_TILE / 2 + 8; }
+// Candidate buffer entries: at least two tiles (the first tile is appended
+// whole in the worst case), and k plus one and a half tiles so that a
+// compaction frees at least a quarter tile beyond the next tile.
+static inline int rows_cap(int k) {
+  const int a = k + TR_TILE + TR_TILE / 2, b = 2 * TR_TILE;
+  return (a > b ? a : b) + 8;
+}
 
 // Workgroups of topk_rows_kernel resident at once on the current device for
 // `lds` bytes of dynamic LDS, as the runtime computes occupancy. Cached per

@@ -135,6 +135,30 @@ def test_adversarial_rows(ops, k):
         assert np.array_equal(np.sort(got[i]), np.sort(ref[i])), nm
 
 
+def test_restream_inside_persistent_loop(ops):
+    """More rows than resident workgroups, so each workgroup takes several rows
+    in turn: descending rows defeat the estimated first-tile bound and are
+    streamed again, ascending rows force compactions, and trivial rows
+    (n <= k) sit in between, all next to ordinary random rows."""
+    k, rows, stride = 512, 3000, 6007
+    g = np.random.default_rng(11)
+    lens = g.integers(300, stride + 1, size=rows).astype(np.int32)
+    buf = np.full((rows, stride), np.inf, np.float32)
+    for i in range(rows):
+        n = int(lens[i])
+        kind = i % 4
+        if kind == 0:
+            buf[i, :n] = np.arange(n, 0, -1, dtype=np.float32) * 0.5
+        elif kind == 1:
+            buf[i, :n] = np.arange(n, dtype=np.float32)
+        else:
+            buf[i, :n] = g.standard_normal(n).astype(np.float32)
+    log(f"restream rows={rows} k={k}")
+    got = _run_rows(ops, buf, lens, k)
+    ref = oracle.topk_rows(buf, lens, k)
+    assert np.array_equal(sorted_rows(got), sorted_rows(ref))
+
+
 def test_max_k(ops):
     case = workloads.decode_rows_case(seed=77, rows=6, stride=40000, n_lo=8000, n_hi=40000, k=8192,
                                       pt_width=40000)
