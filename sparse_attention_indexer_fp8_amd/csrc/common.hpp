@@ -63,6 +63,13 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
   return (__umulhi(n, f.m) + n) >> f.l;
 }
 
+// Load of a uniform address through the scalar unit (constant address space).
+// Only for data no kernel of the launch writes (row metadata, tables).
+template <class T>
+__device__ __forceinline__ T load_uniform(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
+}
+
 // ---------------------------------------------------------------------------
 // Wave helpers
 // ---------------------------------------------------------------------------
@@ -103,9 +110,52 @@ __device__ __forceinline__ uint32_t wave_reserve(uint32_t mine, uint32_t* ctr) {
   return base + pre - mine;
 }
 
-__device__ __forceinline__ uint32_t wave_sum(uint32_t v) { return __reduce_add_sync(~0ull, v); }
+// DPP lane moves of 32- and 64-bit values (every lane valid for the
+// controls used here: quad permutes and row rotations).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t x) {
+  return __builtin_amdgcn_update_dpp(0u, x, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_move(uint64_t x) {
+  const uint32_t lo = dpp_move<CTRL>(static_cast<uint32_t>(x));
+  const uint32_t hi = dpp_move<CTRL>(static_cast<uint32_t>(x >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint32_t read_lane(uint32_t x, int lane) { return __builtin_amdgcn_readlane(x, lane); }
+__device__ __forceinline__ uint64_t read_lane(uint64_t x, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(x), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(x >> 32), lane);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
 
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return __reduce_min_sync(~0ull, v); }
+// Wave-wide reduction: two quad permutes and two row rotations reduce each
+// row of 16 lanes in place, then the four row results (lanes 0, 16, 32, 48)
+// are combined. The result is uniform.
+template <class T, class Op>
+__device__ __forceinline__ T wave_reduce(T x, Op op) {
+  x = op(x, dpp_move<0xb1>(x));   // quad_perm:[1,0,3,2]
+  x = op(x, dpp_move<0x4e>(x));   // quad_perm:[2,3,0,1]
+  x = op(x, dpp_move<0x124>(x));  // row_ror:4
+  x = op(x, dpp_move<0x128>(x));  // row_ror:8
+  return op(op(read_lane(x, 0), read_lane(x, 16)), op(read_lane(x, 32), read_lane(x, 48)));
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+  return wave_reduce(v, [](uint32_t a, uint32_t b) { return a + b; });
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return wave_reduce(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return wave_reduce(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+  return wave_reduce(v, [](uint64_t a, uint64_t b) { return a < b ? a : b; });
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  return wave_reduce(v, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
+}
 
 // Device-scope relaxed atomics on workspace words.
 __device__ __forceinline__ uint32_t ld_acquire_dev(const uint32_t* p) {

@@ -14,6 +14,9 @@ constexpr int kSelMembers = 64;   // threshold-bin size a single wave resolves
 
 // LDS state of wg_select. `hist` and `mcnt` must be zero when a select starts
 // (wg_select_init once per kernel) and every select leaves them zero again.
+// Bin b lives at word sel_slot(b): the 16 bins lane l of wave 0 scans
+// (16 l .. 16 l + 15) then sit in 16 rows of 64 consecutive words, one per
+// lane, so the scan reads and clears without bank conflicts.
 struct SelectLds {
   uint32_t hist[kSelBins];
   uint64_t red[2][16];
@@ -23,24 +26,31 @@ struct SelectLds {
   uint32_t mcnt;
 };
 
+static_assert(kSelBins == 16 * kWave, "sel_slot assumes 16 bins per lane of one wave");
+__device__ __forceinline__ uint32_t sel_slot(uint32_t bin) { return ((bin & 15u) << 6) | (bin >> 4); }
+
 template <int WG>
 __device__ __forceinline__ void wg_select_init(SelectLds& s) {
   for (int i = threadIdx.x; i < kSelBins; i += WG) s.hist[i] = 0;
   if (threadIdx.x == 0) s.mcnt = 0;
 }
 
-__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
-  const uint32_t hi = static_cast<uint32_t>(v >> 32), lo = static_cast<uint32_t>(v);
-  const uint32_t mhi = __reduce_min_sync(~0ull, hi);
-  const uint32_t mlo = __reduce_min_sync(~0ull, hi == mhi ? lo : 0xffffffffu);
-  return (static_cast<uint64_t>(mhi) << 32) | mlo;
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  const uint32_t hi = static_cast<uint32_t>(v >> 32), lo = static_cast<uint32_t>(v);
-  const uint32_t mhi = __reduce_max_sync(~0ull, hi);
-  const uint32_t mlo = __reduce_max_sync(~0ull, hi == mhi ? lo : 0u);
-  return (static_cast<uint64_t>(mhi) << 32) | mlo;
+// Calls f(buf[i]) for i = tid, tid + WG, ... below n, CH loads in flight per
+// thread: the loads of a chunk are issued together (an index past n re-reads
+// the chunk's first entry, which is in range) before any is used.
+template <int WG, int CH, class F>
+__device__ __forceinline__ void lds_for_each(const uint64_t* buf, uint32_t n, F&& f) {
+  for (uint32_t b = threadIdx.x; b < n; b += CH * WG) {
+    uint64_t x[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const uint32_t i = b + j * WG;
+      x[j] = buf[i < n ? i : b];
+    }
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+      if (b + j * WG < n) f(x[j]);
+  }
 }
 
 // Workgroup min and max of per-thread values (one barrier). Every thread
@@ -64,6 +74,53 @@ __device__ __forceinline__ void wg_range(uint64_t& mn, uint64_t& mx, SelectLds& 
   }
 }
 
+// Pick from the kSelBins histogram in s.hist (every thread has added its
+// counts; the call starts with the barrier that completes them): the highest
+// bin b whose count from the top reaches kk (which the total must). Returns
+// b, the count above it and its own count, and leaves the histogram zeroed.
+// Wave 0 alone reads (16 bins per lane, conflict-free through sel_slot),
+// clears and scans.
+struct HistPick {
+  uint32_t bin;
+  uint32_t above;
+  uint32_t cnt;
+};
+
+template <int WG>
+__device__ __forceinline__ HistPick wg_hist_pick(uint32_t kk, SelectLds& s) {
+  constexpr int PL = kSelBins / kWave;  // bins per lane of wave 0
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    const int lane = lane_id();
+    uint32_t c[PL];
+    uint32_t local = 0;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      c[i] = s.hist[i * kWave + lane];  // bin lane * PL + i
+      local += c[i];
+    }
+#pragma unroll
+    for (int i = 0; i < PL; ++i) s.hist[i * kWave + lane] = 0;
+    const uint32_t pre = wave_prefix_incl(local);
+    const uint32_t tot = __builtin_amdgcn_readlane(pre, kWave - 1);
+    const uint32_t incl = tot - pre + local;  // bins of lanes >= lane
+    const uint32_t above_l = incl - local;
+    if (above_l < kk && incl >= kk) {
+      uint32_t above = above_l;
+      int i = PL - 1;
+      for (; i > 0; --i) {
+        if (above + c[i] >= kk) break;
+        above += c[i];
+      }
+      s.bcast[0] = lane * PL + i;
+      s.bcast[1] = above;
+      s.bcast[2] = c[i];
+    }
+  }
+  __syncthreads();
+  return HistPick{s.bcast[0], s.bcast[1], s.bcast[2]};
+}
+
 // k-th largest of a set of DISTINCT 64-bit keys spread over the workgroup,
 // all within [lo, hi] (wg_range gives these). `for_each(f)` must call f(key)
 // once for every key this thread owns, the same set on every call.
@@ -76,17 +133,15 @@ __device__ __forceinline__ void wg_range(uint64_t& mn, uint64_t& mx, SelectLds& 
 //
 // Method: each iteration histograms the undecided keys into kSelBins equal
 // bins covering exactly their range [lo, hi], so they spread over many bins
-// whatever their magnitude. Wave 0 alone reads (and re-zeroes) the bins and
-// finds the one where the count from the top reaches the remaining rank.
-// That bin becomes the new range, and the keys above it are decided. The loop
-// ends when the bin's keys are exactly the ones still needed. When the bin
-// holds at most 64 keys, wave 0 instead ranks them against each other by
-// broadcast. Each iteration shrinks the range by a factor of kSelBins, so at
-// most 7 run; one or two are typical.
+// whatever their magnitude. The bin where the count from the top reaches the
+// remaining rank becomes the new range, and the keys above it are decided.
+// The loop ends when the bin's keys are exactly the ones still needed. When
+// the bin holds at most 64 keys, wave 0 instead ranks them against each other
+// by broadcast. Each iteration shrinks the range by a factor of kSelBins, so
+// at most 7 run; one or two are typical.
 template <int WG, class ForEach>
 __device__ __forceinline__ uint64_t wg_select(ForEach&& for_each, uint32_t k, uint64_t lo, uint64_t hi, SelectLds& s,
                               uint32_t slack = 0) {
-  constexpr int PL = kSelBins / kWave;  // bins per lane of wave 0
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
   uint32_t kk = k;
@@ -96,39 +151,12 @@ __device__ __forceinline__ uint64_t wg_select(ForEach&& for_each, uint32_t k, ui
     const int bits = 64 - __clzll(span);
     const int shift = bits > 10 ? bits - 10 : 0;
     for_each([&](uint64_t key) {
-      if (key >= lo && key <= hi) atomicAdd(&s.hist[static_cast<uint32_t>((key - lo) >> shift)], 1u);
+      if (key >= lo && key <= hi) atomicAdd(&s.hist[sel_slot(static_cast<uint32_t>((key - lo) >> shift))], 1u);
     });
-    __syncthreads();
-    if (wave == 0) {
-      uint32_t c[PL];
-      uint32_t local = 0;
-#pragma unroll
-      for (int i = 0; i < PL; ++i) {
-        c[i] = s.hist[lane * PL + i];
-        local += c[i];
-      }
-#pragma unroll
-      for (int i = 0; i < PL; ++i) s.hist[lane * PL + i] = 0;
-      const uint32_t pre = wave_prefix_incl(local);
-      const uint32_t tot = __builtin_amdgcn_readlane(pre, kWave - 1);
-      const uint32_t incl = tot - pre + local;  // keys in bins of lanes >= lane
-      const uint32_t above_l = incl - local;
-      if (above_l < kk && incl >= kk) {
-        uint32_t above = above_l;
-        int i = PL - 1;
-        for (; i > 0; --i) {
-          if (above + c[i] >= kk) break;
-          above += c[i];
-        }
-        s.bcast[0] = lane * PL + i;
-        s.bcast[1] = above;
-        s.bcast[2] = c[i];
-      }
-    }
-    __syncthreads();
-    const uint32_t bin = s.bcast[0], above = s.bcast[1], cnt = s.bcast[2];
-    kk -= above;
-    lo += static_cast<uint64_t>(bin) << shift;
+    const HistPick p = wg_hist_pick<WG>(kk, s);
+    const uint32_t cnt = p.cnt;
+    kk -= p.above;
+    lo += static_cast<uint64_t>(p.bin) << shift;
     const uint64_t top = lo + ((1ull << shift) - 1ull);
     hi = top < hi ? top : hi;
     if (cnt - kk <= slack) break;  // keys >= lo: (k - kk) + cnt

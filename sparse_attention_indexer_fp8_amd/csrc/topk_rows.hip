@@ -6,9 +6,9 @@
 // page-table row row_to_batch[i] (or i). Selected positions stay row-local
 // until the page transform in the epilogue.
 //
-// Design (persistent workgroups, one row at a time each, one pass over HBM):
-//  * Workgroup g handles rows g, g + G, g + 2G, ... for a grid of G (the
-//    number of workgroups resident at once).
+// Design (one workgroup per row, one pass over HBM):
+//  * Workgroups are dispatched in row order, several resident per compute
+//    unit, so while one runs its selects the others keep loads in flight.
 //  * A row's window is streamed in tiles of TR_TILE floats with 16-byte
 //    loads, TR_RING tiles in flight. A scalar head (up to 3 elements, up to
 //    the first 16-byte boundary) and tail (up to 3 elements) make the stride
@@ -20,26 +20,23 @@
 //  * The first tile sets L with one histogram pass over its n0 elements in
 //    registers: the edge of the bin where the count from the top reaches a
 //    rank r. With r = k, L is a proven lower bound on the row's k-th value.
-//    A long row first tries r ~ 2 k n0 / n + 16 (about 2k of the row's n
-//    values are expected above it). The buffer then holds every element
-//    >= L, so if it ends with at least k keys, L was below the k-th value and
-//    the result is exact; otherwise the row is streamed again with r = k.
+//    A long row first tries r ~ 1.5 k n0 / n + 8 (about 1.5 k of the row's
+//    n values are expected above it), binned by value (equal-width bins
+//    over the tile's range) rather than by key. The buffer then holds every
+//    element >= L, so if it ends with at least k keys, L was below the k-th
+//    value and the result is exact; otherwise the row is streamed again with
+//    r = k.
 //  * When the buffer would overflow, a select finds a bound with between k
 //    and k + slack keys above it, the buffer keeps those, and L becomes the
 //    smallest kept value (never above the row's k-th value).
-//  * At the end an exact select packs the k best keys to the front of the
-//    buffer; positions go through the page table and are stored coalesced.
-//    The first tiles of the workgroup's next row are requested before the
-//    select, the rest after the page-table gathers, so the gathers never
-//    wait behind a whole ring of loads.
+//  * At the end an exact select gives the key T of the k-th best; the keys
+//    >= T go through the page table to the output (slots reserved per wave,
+//    all page-table gathers of a round issued before any is used).
 //  * Rows with n <= k need no scores: every position is selected.
 #include "common.hpp"
 #include "launch.hpp"
 #include "select.hpp"
 
-#include <map>
-#include <mutex>
-#include <utility>
 
 namespace idxtopk {
 
@@ -47,14 +44,12 @@ constexpr int TR_WG = 256;
 constexpr int TR_VEC = 2;                    // float4 loads per thread per tile
 constexpr int TR_TILE = TR_WG * TR_VEC * 4;  // floats per tile (8 KB)
 constexpr int TR_RING = 4;                   // tiles in flight per workgroup
-constexpr int TR_HEAD = 2;                   // next-row tiles requested before the final select
 constexpr int TR_BATCH = 4;                  // buffer entries per thread per compaction batch
-constexpr int TR_EMIT = 4;                   // outputs per thread per emission round
+constexpr int TR_EMIT = 8;                   // outputs per thread per emission round
 
 struct RowsArgs {
   const float* scores;
   int64_t stride;
-  int32_t rows;
   const int32_t* seq_lens;
   const int32_t* row_starts;
   const int32_t* row_to_batch;
@@ -80,6 +75,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 struct TopkRowsLds {
   SelectLds sel;
   uint32_t cnt;
+  uint32_t ocnt;
   uint32_t minkey;
 };
 
@@ -102,9 +98,9 @@ struct RowCtx {
 __device__ __forceinline__ RowCtx row_setup(const RowsArgs& a, int row) {
   RowCtx r;
   r.row = row;
-  r.n = a.seq_lens[row];
-  const int64_t rs = a.row_starts ? a.row_starts[row] : 0;
-  const int prow = a.row_to_batch ? a.row_to_batch[row] : row;
+  r.n = load_uniform(a.seq_lens + row);
+  const int64_t rs = a.row_starts ? load_uniform(a.row_starts + row) : 0;
+  const int prow = a.row_to_batch ? load_uniform(a.row_to_batch + row) : row;
   r.pt_row = a.page_table ? a.page_table + static_cast<int64_t>(prow) * a.pt_stride : nullptr;
   r.out = a.out + static_cast<int64_t>(row) * a.k;
   r.trivial = r.n <= a.k;
@@ -158,24 +154,17 @@ struct Extra {
   float x;
 };
 
-// Request the start of a row: its head / tail elements and tiles
-// [0, TR_HEAD). prefetch_tail requests tiles [TR_HEAD, TR_RING). Tiles past
-// the row's last repeat the last one (the loads stay in bounds).
-__device__ __forceinline__ void prefetch_head(const RowCtx& r, f4 (&ring)[TR_RING][TR_VEC], Extra& e) {
+// Request the start of a row: its head / tail element (if this thread has
+// one) and tiles [0, TR_RING) (slots past the row's last tile repeat it; the
+// duplicates are never read).
+__device__ __forceinline__ void prefetch_row(const RowCtx& r, f4 (&ring)[TR_RING][TR_VEC], Extra& e) {
   const int tid = threadIdx.x;
   e.has = tid < r.head + r.ntail;
   e.pos = static_cast<uint32_t>(tid < r.head ? tid : r.tail0 + (tid - r.head));
   e.x = e.has ? r.base[e.pos] : 0.0f;
   if (r.ntiles > 0) {
 #pragma unroll
-    for (int u = 0; u < TR_HEAD; ++u) load_tile(r, u < r.ntiles ? u : r.ntiles - 1, ring[u]);
-  }
-}
-
-__device__ __forceinline__ void prefetch_tail(const RowCtx& r, f4 (&ring)[TR_RING][TR_VEC]) {
-  if (r.ntiles > 0) {
-#pragma unroll
-    for (int u = TR_HEAD; u < TR_RING; ++u) load_tile(r, u < r.ntiles ? u : r.ntiles - 1, ring[u]);
+    for (int u = 0; u < TR_RING; ++u) load_tile(r, u < r.ntiles ? u : r.ntiles - 1, ring[u]);
   }
 }
 
@@ -220,20 +209,13 @@ __device__ __forceinline__ void append_tile(const f4 (&x)[TR_VEC], const TileVie
 // re-reads them there.
 __device__ __forceinline__ uint64_t select_buffer(const uint64_t* cand, uint32_t c, uint32_t k,
                                                   uint32_t slack, TopkRowsLds& s) {
-  const uint32_t tid = threadIdx.x;
   uint64_t mn = ~0ull, mx = 0;
-  for (uint32_t i = tid; i < c; i += TR_WG) {
-    const uint64_t x = cand[i];
+  lds_for_each<TR_WG, 4>(cand, c, [&](uint64_t x) {
     mn = x < mn ? x : mn;
     mx = x > mx ? x : mx;
-  }
+  });
   wg_range<TR_WG>(mn, mx, s.sel);
-  return wg_select<TR_WG>(
-      [&](auto&& f) {
-#pragma unroll 4
-        for (uint32_t i = tid; i < c; i += TR_WG) f(cand[i]);
-      },
-      k, mn, mx, s.sel, slack);
+  return wg_select<TR_WG>([&](auto&& f) { lds_for_each<TR_WG, 4>(cand, c, f); }, k, mn, mx, s.sel, slack);
 }
 
 // Keep the keys >= T of cand[0, c), packed to the front of the buffer (in no
@@ -257,7 +239,7 @@ __device__ __forceinline__ uint32_t keep_compact(uint64_t* cand, uint32_t c, uin
 #pragma unroll
     for (int j = 0; j < TR_BATCH; ++j) {
       const uint32_t i = b0 + j * TR_WG + tid;
-      key[j] = i < c ? cand[i] : 0ull;
+      key[j] = cand[i < c ? i : 0];
       keep[j] = i < c && key[j] >= T;
       mine += keep[j];
     }
@@ -295,7 +277,7 @@ __device__ __forceinline__ void after_tile(const RowCtx& r, int t, uint32_t k, i
 
 // Stream all tiles of row r (its first TR_RING tiles and the extra element are
 // already requested) into the candidate buffer. With `estimate`, a long row's
-// first-tile bound uses the rank r ~ 2 k n0 / n + 16 instead of k; returns
+// first-tile bound uses the rank r ~ 1.5 k n0 / n + 8 instead of k; returns
 // whether it did (then the caller must check that at least k keys were kept).
 __device__ __forceinline__ bool stream_row(const RowCtx& r, f4 (&ring)[TR_RING][TR_VEC], const Extra& ex,
                                            uint32_t k, int cap, bool estimate, uint64_t* cand,
@@ -311,7 +293,8 @@ __device__ __forceinline__ bool stream_row(const RowCtx& r, f4 (&ring)[TR_RING][
     if (r.ntiles > 1 && n0 > static_cast<int>(k)) {
       uint32_t rank = k;
       if (estimate) {
-        const uint64_t want = (2ull * k * static_cast<uint64_t>(n0) + r.n - 1) / static_cast<uint64_t>(r.n) + 16u;
+        const uint64_t n = static_cast<uint64_t>(r.n);
+        const uint64_t want = (3ull * k * static_cast<uint64_t>(n0) + 2 * n - 1) / (2 * n) + 8u;
         if (want < k) {
           rank = static_cast<uint32_t>(want);
           estimated = true;
@@ -332,8 +315,33 @@ __device__ __forceinline__ bool stream_row(const RowCtx& r, f4 (&ring)[TR_RING][
         mx = key > mx ? key : mx;
       });
       wg_range<TR_WG>(mn, mx, s.sel);
-      const uint64_t bound = wg_select<TR_WG>(each, rank, mn, mx, s.sel, ~0u);
-      lf = key_float(rank_vkey(bound));
+      const float vmin = key_float(rank_vkey(mn)), vmax = key_float(rank_vkey(mx));
+      const float width = vmax - vmin;
+      if (estimated && width > 0.0f && width < __builtin_inff()) {
+        // estimate: kSelBins equal-width value bins over the tile's range;
+        // the bound is the lower edge of the bin where the count from the
+        // top reaches the rank
+        const float scale = static_cast<float>(kSelBins) / width;
+        auto add = [&](float x) {
+          float f = (x - vmin) * scale;
+          f = f < static_cast<float>(kSelBins - 1) ? f : static_cast<float>(kSelBins - 1);
+          f = f > 0.0f ? f : 0.0f;
+          atomicAdd(&s.sel.hist[sel_slot(static_cast<uint32_t>(f))], 1u);
+        };
+#pragma unroll
+        for (int v = 0; v < TR_VEC; ++v)
+          if (tv.valid(v)) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) add(ring[0][v][c]);
+          }
+        if (ex.has) add(ex.x);
+        const HistPick p = wg_hist_pick<TR_WG>(rank, s.sel);
+        lf = vmin + static_cast<float>(p.bin) / scale;
+      } else {
+        // proven: at least rank keys of the tile are >= the bound
+        const uint64_t bound = wg_select<TR_WG>(each, rank, mn, mx, s.sel, ~0u);
+        lf = key_float(rank_vkey(bound));
+      }
     }
     if (r.ntiles > 0) {
       append_tile(ring[0], tv, ex, true, lf, cand, &s.cnt);
@@ -388,76 +396,73 @@ __global__ __launch_bounds__(TR_WG, 4) void topk_rows_kernel(RowsArgs a) {
   const uint32_t tid = threadIdx.x;
   const uint32_t k = static_cast<uint32_t>(a.k);
   const uint32_t P = static_cast<uint32_t>(a.page_size);
-
-  wg_select_init<TR_WG>(s.sel);
-  if (tid == 0) s.cnt = 0;
-  __syncthreads();
-
+  const RowCtx cur = row_setup(a, blockIdx.x);
+  if (cur.trivial) {
+    emit_all(cur, a);
+    return;
+  }
   f4 ring[TR_RING][TR_VEC];
   Extra ex;
-  RowCtx cur = row_setup(a, blockIdx.x);
-  if (!cur.trivial) {
-    prefetch_head(cur, ring, ex);
-    prefetch_tail(cur, ring);
+  prefetch_row(cur, ring, ex);
+  wg_select_init<TR_WG>(s.sel);
+  if (tid == 0) {
+    s.cnt = 0;
+    s.ocnt = 0;
   }
-  for (;;) {
-    const int nrow = cur.row + static_cast<int>(gridDim.x);
-    const bool has_next = nrow < a.rows;
-    if (cur.trivial) {
-      emit_all(cur, a);
-      if (!has_next) break;
-      cur = row_setup(a, nrow);
-      if (!cur.trivial) {
-        prefetch_head(cur, ring, ex);
-        prefetch_tail(cur, ring);
-      }
-      continue;
-    }
-    const bool estimated = stream_row(cur, ring, ex, k, a.cap, true, cand, s);
-    uint32_t c = s.cnt;  // stable: the last after_tile ended with a barrier
-    if (estimated && c < k) {
-      // the estimated bound was above the row's k-th value: stream the row
-      // again with the proven first-tile bound
-      __syncthreads();
-      if (tid == 0) s.cnt = 0;
-      __syncthreads();
-      prefetch_head(cur, ring, ex);
-      prefetch_tail(cur, ring);
-      stream_row(cur, ring, ex, k, a.cap, false, cand, s);
-      c = s.cnt;
-    }
-    // the ring is free: request the start of the next row
-    RowCtx nxt = cur;
-    bool pre = false;
-    if (has_next) {
-      nxt = row_setup(a, nrow);
-      pre = !nxt.trivial;
-    }
-    if (pre) prefetch_head(nxt, ring, ex);
-    // exactly the k best keys to cand[0, k); c < k only with NaN inputs
-    // (outside the domain), then what is there is emitted and padded
-    if (c > k) keep_compact(cand, c, select_buffer(cand, c, k, 0, s), s);
-    const uint32_t m = c < k ? c : k;
-    for (uint32_t b0 = 0; b0 < k; b0 += TR_EMIT * TR_WG) {
-      int32_t slot[TR_EMIT];
-#pragma unroll
-      for (int j = 0; j < TR_EMIT; ++j) {
-        const uint32_t i = b0 + j * TR_WG + tid;
-        slot[j] = i < m ? map_slot(cur.pt_row, rank_pos(cand[i]), P, a.pdiv) : -1;
-      }
-      if (b0 == 0 && pre) prefetch_tail(nxt, ring);
-#pragma unroll
-      for (int j = 0; j < TR_EMIT; ++j) {
-        const uint32_t i = b0 + j * TR_WG + tid;
-        if (i < k) cur.out[i] = slot[j];
-      }
-    }
+  __syncthreads();
+
+  const bool estimated = stream_row(cur, ring, ex, k, a.cap, true, cand, s);
+  uint32_t c = s.cnt;  // stable: the last after_tile ended with a barrier
+  if (estimated && c < k) {
+    // the estimated bound was above the row's k-th value: stream the row
+    // again with the proven first-tile bound
     __syncthreads();
     if (tid == 0) s.cnt = 0;
     __syncthreads();
-    if (!has_next) break;
-    cur = nxt;
+    prefetch_row(cur, ring, ex);
+    stream_row(cur, ring, ex, k, a.cap, false, cand, s);
+    c = s.cnt;
   }
+  // the k best keys are those >= T (all of them when c <= k, which with
+  // c < k happens only for NaN inputs, outside the domain: the rest of the
+  // row is padded with -1). Each round reserves output slots per wave, then
+  // issues all its page-table gathers before using any.
+  const uint64_t T = c > k ? select_buffer(cand, c, k, 0, s) : 0ull;
+  for (uint32_t b0 = 0; b0 < c; b0 += TR_EMIT * TR_WG) {
+    bool keep[TR_EMIT];
+    uint32_t pos[TR_EMIT];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < TR_EMIT; ++j) {
+      const uint32_t i = b0 + j * TR_WG + tid;
+      const uint64_t key = cand[i < c ? i : 0];
+      keep[j] = i < c && key >= T;
+      pos[j] = rank_pos(key);
+      mine += keep[j];
+    }
+    uint32_t at = wave_reserve(mine, &s.ocnt);
+    // entries not kept read page 0 (in range)
+    uint32_t pg[TR_EMIT];
+    int32_t base[TR_EMIT];
+    const bool paged = cur.pt_row != nullptr;
+    if (paged) {
+#pragma unroll
+      for (int j = 0; j < TR_EMIT; ++j) {
+        pg[j] = keep[j] ? fdiv(pos[j], a.pdiv) : 0u;
+        base[j] = cur.pt_row[pg[j]];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TR_EMIT; ++j) {
+      if (keep[j]) {
+        const int32_t slot = paged ? static_cast<int32_t>(static_cast<int64_t>(base[j]) * P + (pos[j] - pg[j] * P))
+                                   : static_cast<int32_t>(pos[j]);
+        if (at < k) cur.out[at] = slot;
+        ++at;
+      }
+    }
+  }
+  for (uint32_t i = c + tid; i < k; i += TR_WG) cur.out[i] = -1;
 }
 
 // Candidate buffer entries: at least two tiles (the first tile is appended
@@ -468,29 +473,6 @@ static inline int rows_cap(int k) {
   return (a > b ? a : b) + 8;
 }
 
-// Workgroups of topk_rows_kernel resident at once on the current device for
-// `lds` bytes of dynamic LDS, as the runtime computes occupancy. Cached per
-// (device, size).
-static int resident_workgroups(const void* kernel, size_t lds) {
-  static std::mutex mu;
-  static std::map<std::pair<int, size_t>, int> cache;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
-  std::lock_guard<std::mutex> lock(mu);
-  const auto key = std::make_pair(dev, lds);
-  const auto it = cache.find(key);
-  if (it != cache.end()) return it->second;
-  int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, TR_WG, lds) != hipSuccess || per_cu <= 0)
-    per_cu = 1;
-  (void)hipGetLastError();
-  const int v = per_cu * cus;
-  cache.emplace(key, v);
-  return v;
-}
-
 int launch_topk_rows(const float* scores, int64_t stride, int rows, const int32_t* seq_lens,
                      const int32_t* row_starts, const int32_t* row_to_batch,
                      const int32_t* page_table, int64_t pt_stride, int page_size, int k,
@@ -498,7 +480,6 @@ int launch_topk_rows(const float* scores, int64_t stride, int rows, const int32_
   RowsArgs a;
   a.scores = scores;
   a.stride = stride;
-  a.rows = rows;
   a.seq_lens = seq_lens;
   a.row_starts = row_starts;
   a.row_to_batch = row_to_batch;
@@ -513,10 +494,8 @@ int launch_topk_rows(const float* scores, int64_t stride, int rows, const int32_
   const void* kern = reinterpret_cast<const void*>(&topk_rows_kernel);
   static std::atomic<size_t> granted{0};
   if (allow_dynamic_lds(kern, lds, granted) != hipSuccess) return -4;
-  const int res = resident_workgroups(kern, lds);
-  const int grid = rows < res ? rows : res;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(topk_rows_kernel, dim3(grid), dim3(TR_WG), lds, stream, a);
+  hipLaunchKernelGGL(topk_rows_kernel, dim3(rows), dim3(TR_WG), lds, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
