@@ -39,6 +39,7 @@ import workloads  # noqa: E402
 METRIC = "top-k rows/s + µs/launch and achieved HBM GB/s (% roofline), 1 MI355X"
 HBM_PEAK_GBPS = 8000.0
 FLUSH_BYTES = 1 << 30
+COPY_CALIBRATION_BYTES = 1 << 30
 COUNTERS_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "topk_rows": ["topk_rows.hip", "select.hpp", "common.hpp"],
@@ -56,6 +57,52 @@ def source_hash(kind: str) -> str:
         with open(os.path.join(ROOT, "sparse_attention_indexer_fp8_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+PMC_KERNELS = {
+    # counters file name -> (source kind, kernel name prefix, grid size of the workload's launch)
+    "topk_rows_packed_prefill_16384x70001": ("topk_rows", "idxtopk::topk_rows_kernel", 16384 * 256),
+    "fused_long_decode_B64_k2048": ("fused", "void idxtopk::fused_chunk_kernel", 2560 * 256),
+}
+
+
+def _pmc_rows(path):
+    import csv
+
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def write_counters_from_pmc(fetch_csv: str, write_csv: str, command: str) -> None:
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch) into profiles/<name>.counters.json. Each counter is scaled by
+    what it reads for the 1 GiB device copy of --copy-calibration (a plain
+    copy kernel that reads and writes exactly 1 GiB)."""
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in _pmc_rows(path) if r["Counter_Name"] == counter]
+        copies = [float(r["Counter_Value"]) for r in rows
+                  if "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) >= 65536]
+        if not copies:
+            raise SystemExit(f"{path}: no 1 GiB copy dispatch to calibrate {counter}")
+        factor = (COPY_CALIBRATION_BYTES / 1024) / (sum(copies) / len(copies))
+        for name, (kind, prefix, grid) in PMC_KERNELS.items():
+            vals = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"].startswith(prefix)
+                    and (grid is None or int(r["Grid_Size"]) == grid)]
+            if vals:
+                e = out.setdefault(name, {"kind": kind, "kernel": prefix})
+                e[counter] = {"kib_per_dispatch": sum(vals) / len(vals), "dispatches": len(vals),
+                              "copy_calibration_factor": factor,
+                              "bytes_per_dispatch": sum(vals) / len(vals) * 1024 * factor}
+    for name, e in out.items():
+        if "FETCH_SIZE" not in e or "WRITE_SIZE" not in e:
+            continue
+        e["bytes_per_launch"] = round(e["FETCH_SIZE"]["bytes_per_dispatch"] + e["WRITE_SIZE"]["bytes_per_dispatch"])
+        e["source_hash"] = source_hash(e["kind"])
+        e["command"] = command
+        with open(os.path.join(COUNTERS_DIR, f"{name}.counters.json"), "w") as f:
+            json.dump(e, f, indent=1)
+        log(f"wrote {name}: {e['bytes_per_launch']} bytes per launch")
 
 
 def counter_traffic(name: str, kind: str):
@@ -242,7 +289,14 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for PMC byte-counter calibration)")
+    ap.add_argument("--from-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/*.counters.json from two rocprofv3 --pmc counter_collection.csv "
+                         "files (FETCH_SIZE run, WRITE_SIZE run) and exit")
+    ap.add_argument("--pmc-command", default="", help="the command the --pmc runs used (recorded)")
     a = ap.parse_args(argv)
+    if a.from_pmc:
+        write_counters_from_pmc(a.from_pmc[0], a.from_pmc[1], a.pmc_command)
+        return 0
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the indexer top-k path here runs on a single MI355X "
               "(no sharding, no collectives); run with --gpus 1", file=sys.stderr)
@@ -268,7 +322,7 @@ def main(argv=None):
     line = None
 
     if a.copy_calibration:
-        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        src = torch.empty(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         src.fill_(1.0)
         for _ in range(3):
@@ -331,6 +385,8 @@ def main(argv=None):
         c5 = workloads.c5_long_decode()
         log("timing long decode B64 ...")
         also["long_decode_B64_k2048"] = bench_fused(torch, ops, timer, c5, a.warmup, a.steps, False)
+        also["long_decode_B64_k2048"]["chunk_kernel_traffic"] = counter_traffic("fused_long_decode_B64_k2048",
+                                                                                "fused")
         del c5
     if line is None:
         line = {"metric": METRIC, "value": None, "unit": "rows/s", "n_gpus": 1, "steps": a.steps,
