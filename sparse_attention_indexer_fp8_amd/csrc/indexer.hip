@@ -10,8 +10,9 @@
 //   128-token blocks; the sparse block list is built inside the top-k kernel.
 //
 // Grid: one workgroup per (row, chunk) pair, chunk-major (all rows' chunk 0
-// first). Chunks past a row's length exit at once. Every workgroup scores its
-// chunk with the fp8 MFMA core (score_mfma.hpp).
+// first), the row index rotated per chunk so each row's chunks spread over
+// all XCDs. Chunks past a row's length exit at once. Every workgroup scores
+// its chunk with the fp8 MFMA core (score_mfma.hpp).
 //
 // Fused decode (idx_score_topk_fused), per chunk:
 //  1. Scores stay in LDS. A 4096-bin LDS histogram of the value keys' top 12
@@ -23,12 +24,13 @@
 //  3. The chunk emits only tokens in bins >= that bound, as unique 64-bit
 //     keys (score key, inverted position), to the row's candidate list in
 //     the workspace.
-//  4. The last chunk of the row (acq_rel counter) merges. The complete
-//     histogram names the exact threshold bin. Candidates above it are
-//     emitted directly. Candidates in it go to LDS, and an exact radix select
-//     takes the remaining count. Output goes through the block table to
-//     slots. The merging workgroup then zeroes the row's histogram and
-//     counters, so the workspace is clean for the next call.
+//  4. A second kernel merges, one workgroup per row, once every chunk is
+//     done. The complete histogram names the exact threshold bin.
+//     Candidates above it are emitted directly. Candidates in it go to LDS,
+//     and an exact select takes the remaining count. Output goes through the
+//     block table to slots. The merging workgroup then zeroes the row's
+//     histogram, counters and candidates, so the workspace is clean for the
+//     next call.
 // The score row never exists in HBM.
 #include "common.hpp"
 #include "launch.hpp"
@@ -100,6 +102,33 @@ size_t block_workspace_bytes(int rows, int block_size, int max_seq_len) {
   return align256(static_cast<size_t>(rows) * nblk * 4) + align256(static_cast<size_t>(rows) * 16);
 }
 
+// Workgroup -> (row b, chunk c), chunk-major. Workgroups are dealt to the
+// XCDs round-robin by index; with a plain b = index % batch each XCD would
+// own a fixed subset of rows (every row whose index is congruent to it modulo
+// the XCD count) and the XCDs holding the longest rows would finish last. The
+// row index is therefore rotated by the chunk index: a row's chunks land on
+// every XCD in turn.
+__device__ __forceinline__ void chunk_of(const IndexerArgs& a, int& b, int& c) {
+  c = blockIdx.x / a.batch;
+  b = (blockIdx.x + c) % a.batch;
+}
+
+// First token and token count of chunk c under the guided schedule: the
+// grid is chunk-major, so the last workgroups dispatched are the short ones
+// and the tail of the launch stays short.
+__device__ __forceinline__ void chunk_span(const IndexerArgs& a, int c, int& tb, int& len) {
+  if (c < a.n_full) {
+    tb = c * a.chunk;
+    len = a.chunk;
+  } else if (c < a.n_full + a.n_half) {
+    len = a.chunk / 2;
+    tb = a.tok_half + (c - a.n_full) * len;
+  } else {
+    len = a.chunk / 4;
+    tb = a.tok_quarter + (c - a.n_full - a.n_half) * len;
+  }
+}
+
 __device__ __forceinline__ int32_t token_slot(const IndexerArgs& a, int b, uint32_t pos) {
   const uint32_t P = static_cast<uint32_t>(a.page_size);
   const uint32_t pg = fdiv(pos, a.pdiv);
@@ -115,12 +144,13 @@ __device__ __forceinline__ int32_t token_slot(const IndexerArgs& a, int b, uint3
 template <int NT>
 __global__ __launch_bounds__(IX_WG) void score_kernel(IndexerArgs a, float* scores, int64_t sstride) {
   __shared__ int32_t pages[IX_PAGES];
-  const int b = blockIdx.x % a.batch;
-  const int c = blockIdx.x / a.batch;
+  int b, c;
+  chunk_of(a, b, c);
   const int n = a.seq_lens[b];
-  const int tb = c * a.chunk;
+  int tb, clen;
+  chunk_span(a, c, tb, clen);
   if (tb >= n) return;
-  const int te = min(n, tb + a.chunk);
+  const int te = min(n, tb + clen);
   float* srow = scores + static_cast<int64_t>(b) * sstride;
   score_chunk<NT, IX_WG, IX_RING>(a, b, tb, te, pages, [&](int j, float s) { srow[j] = s; });
 }
@@ -133,12 +163,33 @@ constexpr int MG_WG = 512;                      // merge workgroup
 constexpr int MG_BUF = 6144;                    // threshold-bin entries held in LDS (48 KB)
 constexpr int MG_MAXE = MG_BUF / MG_WG;
 
+static_assert(HIST_BINS == 16 * IX_WG, "16 histogram bins per thread");
+
+// The 16 counts of bins [16 t, 16 t + 16) of an LDS histogram, for thread t
+// (four 16-byte reads).
+__device__ __forceinline__ void own_bins16(const uint32_t* hist, uint32_t (&c)[16]) {
+  const uint4* p = reinterpret_cast<const uint4*>(hist) + threadIdx.x * 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint4 v = p[j];
+    c[4 * j + 0] = v.x;
+    c[4 * j + 1] = v.y;
+    c[4 * j + 2] = v.z;
+    c[4 * j + 3] = v.w;
+  }
+}
+
+constexpr uint32_t FU_STAGE = HIST_BINS / 2;  // candidates staged in the histogram's LDS
+
 struct ChunkLds {
-  float sc[FU_CH_MAX];
-  uint32_t hist[HIST_BINS];
+  union {
+    alignas(16) uint32_t hist[HIST_BINS];  // the chunk's histogram, until its bound is known
+    uint64_t stage[FU_STAGE];              // then the chunk's candidates
+  };
   int32_t pages[IX_PAGES];
   uint32_t scratch[16];
   uint32_t lcnt;
+  uint32_t lcnt2;
   uint32_t gbase;
 };
 
@@ -148,60 +199,124 @@ struct FusedOut {
   int k;
 };
 
+// Dynamic LDS: the chunk's scores (a.chunk floats).
 template <int NT>
 __global__ __launch_bounds__(IX_WG) void fused_chunk_kernel(IndexerArgs a, FusedWs ws, int k) {
+  extern __shared__ float sc[];
   __shared__ ChunkLds s;
   const int tid = threadIdx.x;
-  const int b = blockIdx.x % a.batch;
-  const int c = blockIdx.x / a.batch;
+  int b, c;
+  chunk_of(a, b, c);
   const int n = a.seq_lens[b];
-  const int tb = c * a.chunk;
+  int tb, clen;
+  chunk_span(a, c, tb, clen);
   if (tb >= n) return;
-  const int te = min(n, tb + a.chunk);
+  const int te = min(n, tb + clen);
   const int cnt = te - tb;
   uint32_t* Hg = ws.hist + static_cast<int64_t>(b) * HIST_BINS;
   uint32_t* ctr = ws.ctr + static_cast<int64_t>(b) * 4;
   uint64_t* cand = ws.cand + static_cast<int64_t>(b) * ws.cap;
 
   for (int i = tid; i < HIST_BINS; i += IX_WG) s.hist[i] = 0;
-  if (tid == 0) s.lcnt = 0;
+  if (tid == 0) {
+    s.lcnt = 0;
+    s.lcnt2 = 0;
+  }
   // (score_chunk synchronises before its first emit)
   score_chunk<NT, IX_WG, IX_RING>(a, b, tb, te, s.pages, [&](int j, float v) {
-    s.sc[j - tb] = v;
+    sc[j - tb] = v;
     atomicAdd(&s.hist[float_key(v) >> HIST_SHIFT], 1u);
   });
   __syncthreads();
 
-  // Publish the chunk histogram, then bound the row's k-th score with what
-  // the row's histogram holds so far. Per bin, max(row count seen, own count)
-  // never exceeds the number of real tokens in that bin, so the threshold bin
-  // of these counts is a valid lower bound whatever has become visible.
-  for (int i = tid; i < HIST_BINS; i += IX_WG) {
-    const uint32_t h = s.hist[i];
-    if (h) add_dev(&Hg[i], h);
+  // 1. The chunk's own threshold bin: the row holds these tokens, so the
+  //    row's threshold bin is at least this one, and counts of lower bins
+  //    can never decide it.
+  uint32_t c16[16];
+  own_bins16(s.hist, c16);
+  const BinThreshold own = wg_threshold_counts<IX_WG, 16>(c16, static_cast<uint32_t>(k), s.scratch);
+  const uint32_t lo_bin = own.all ? 0u : own.bin;
+  // 2. Publish the counts of bins >= lo_bin to the row's histogram, then read
+  //    the row's counts back (coalesced: bin i * IX_WG + tid; all loads issued
+  //    before any is used; bins below lo_bin re-read lo_bin's counter).
+  uint32_t g16[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t bin = i * IX_WG + tid;
+    const uint32_t h = s.hist[bin];
+    if (h && bin >= lo_bin) add_dev(&Hg[bin], h);
   }
-  const BinThreshold bound = wg_threshold_bin<IX_WG, HIST_BINS>(
-      [&](int i) {
-        const uint32_t g = ld_acquire_dev(&Hg[i]);
-        const uint32_t l = s.hist[i];
-        return g > l ? g : l;
-      },
-      static_cast<uint32_t>(k), s.scratch);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t bin = i * IX_WG + tid;
+    g16[i] = ld_acquire_dev(&Hg[bin >= lo_bin ? bin : lo_bin]);
+  }
+  // 3. Bound the row's k-th score with what the row's histogram holds so far.
+  //    Per bin, max(row count seen, own count) never exceeds the number of
+  //    real tokens in that bin, so the threshold bin of these counts is a
+  //    valid lower bound whatever has become visible; bins below lo_bin
+  //    cannot hold it. (Each thread rewrites only the bins it read.)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t bin = i * IX_WG + tid;
+    const uint32_t l = s.hist[bin];
+    s.hist[bin] = bin >= lo_bin ? (g16[i] > l ? g16[i] : l) : 0u;
+  }
+  __syncthreads();
+  own_bins16(s.hist, c16);
+  const BinThreshold bound = wg_threshold_counts<IX_WG, 16>(c16, static_cast<uint32_t>(k), s.scratch);
   const uint32_t bin_g = bound.all ? 0u : bound.bin;
 
-  // Emit this chunk's candidates (bin >= bound) to the row's list: each
-  // thread's offset comes from a wave prefix plus one LDS and one global
-  // reservation for the whole chunk.
-  uint32_t mine = 0;
-  for (int i = tid; i < cnt; i += IX_WG) mine += ((float_key(s.sc[i]) >> HIST_SHIFT) >= bin_g);
-  const uint32_t my0 = wave_reserve(mine, &s.lcnt);
+  // 4. Emit this chunk's candidates (bin >= bound) to the row's list: staged
+  //    in LDS (over the histogram, which is no longer read) with one slot
+  //    reservation per wave per batch, then one global reservation and a
+  //    coalesced copy. If more than FU_STAGE pass, a second pass writes them
+  //    straight to the list instead.
+  constexpr int EB = 8;
+  for (int i0 = 0; i0 < cnt; i0 += EB * IX_WG) {
+    uint32_t key[EB];
+    bool keep[EB];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < EB; ++j) {
+      const int i = i0 + j * IX_WG + tid;
+      key[j] = float_key(sc[i < cnt ? i : 0]);
+      keep[j] = i < cnt && (key[j] >> HIST_SHIFT) >= bin_g;
+      mine += keep[j];
+    }
+    uint32_t at = wave_reserve(mine, &s.lcnt);
+#pragma unroll
+    for (int j = 0; j < EB; ++j) {
+      if (keep[j]) {
+        if (at < FU_STAGE) s.stage[at] = rank_key(key[j], static_cast<uint32_t>(tb + i0 + j * IX_WG + tid));
+        ++at;
+      }
+    }
+  }
   __syncthreads();
-  if (tid == 0) s.gbase = s.lcnt ? add_dev(&ctr[0], s.lcnt) : 0u;
+  const uint32_t m = s.lcnt;
+  if (tid == 0) s.gbase = m ? add_dev(&ctr[0], m) : 0u;
   __syncthreads();
-  uint32_t at = s.gbase + my0;
-  for (int i = tid; i < cnt; i += IX_WG) {
-    const uint32_t key = float_key(s.sc[i]);
-    if ((key >> HIST_SHIFT) >= bin_g) cand[at++] = rank_key(key, static_cast<uint32_t>(tb + i));
+  const uint32_t gbase = s.gbase;
+  if (m <= FU_STAGE) {
+    for (uint32_t i = tid; i < m; i += IX_WG) cand[gbase + i] = s.stage[i];
+  } else {
+    for (int i0 = 0; i0 < cnt; i0 += EB * IX_WG) {
+      uint32_t key[EB];
+      bool keep[EB];
+      uint32_t mine = 0;
+#pragma unroll
+      for (int j = 0; j < EB; ++j) {
+        const int i = i0 + j * IX_WG + tid;
+        key[j] = float_key(sc[i < cnt ? i : 0]);
+        keep[j] = i < cnt && (key[j] >> HIST_SHIFT) >= bin_g;
+        mine += keep[j];
+      }
+      uint32_t at = gbase + wave_reserve(mine, &s.lcnt2);
+#pragma unroll
+      for (int j = 0; j < EB; ++j)
+        if (keep[j]) cand[at++] = rank_key(key[j], static_cast<uint32_t>(tb + i0 + j * IX_WG + tid));
+    }
   }
 }
 
@@ -401,12 +516,13 @@ template <int NT>
 __global__ __launch_bounds__(IX_WG) void block_chunk_kernel(IndexerArgs a, BlockWs ws, int bs) {
   __shared__ BlockChunkLds s;
   const int tid = threadIdx.x;
-  const int b = blockIdx.x % a.batch;
-  const int c = blockIdx.x / a.batch;
+  int b, c;
+  chunk_of(a, b, c);
   const int n = a.seq_lens[b];
-  const int tb = c * a.chunk;
+  int tb, clen;
+  chunk_span(a, c, tb, clen);
   if (tb >= n) return;
-  const int te = min(n, tb + a.chunk);
+  const int te = min(n, tb + clen);
   const int nbc = (te - tb + bs - 1) / bs;
   uint32_t* bsc = ws.bscore + static_cast<int64_t>(b) * ws.nblk_max;
 
@@ -486,7 +602,7 @@ __global__ __launch_bounds__(MG_WG) void block_merge_kernel(IndexerArgs a, Block
 // Launchers
 // ---------------------------------------------------------------------------
 
-static IndexerArgs make_args(const IndexerInputs& in, int chunk) {
+static IndexerArgs make_args(const IndexerInputs& in, int chunk, bool guided = false, int guide_align = 16) {
   IndexerArgs a;
   a.q = in.q;
   a.q_scale = in.q_scale;
@@ -502,7 +618,22 @@ static IndexerArgs make_args(const IndexerInputs& in, int chunk) {
   a.heads = in.heads;
   a.chunk = chunk;
   const int msl = in.max_seq_len > 0 ? in.max_seq_len : 1;
-  a.nchunk_max = (msl + chunk - 1) / chunk;
+  // Guided schedule when quarter chunks stay large (and aligned): full-size
+  // chunks up to half the longest row, halves up to three quarters, then
+  // quarters.
+  const int quarter = chunk / 4;
+  if (guided && chunk % 4 == 0 && quarter >= 1024 && quarter % guide_align == 0 && msl > 2 * chunk) {
+    a.n_full = (msl / 2) / chunk;
+    a.tok_half = a.n_full * chunk;
+    a.n_half = ((msl - a.tok_half) / 2) / (chunk / 2);
+    a.tok_quarter = a.tok_half + a.n_half * (chunk / 2);
+    a.nchunk_max = a.n_full + a.n_half + (msl - a.tok_quarter + quarter - 1) / quarter;
+  } else {
+    a.n_full = (msl + chunk - 1) / chunk;
+    a.n_half = 0;
+    a.tok_half = a.tok_quarter = a.n_full * chunk;
+    a.nchunk_max = a.n_full;
+  }
   return a;
 }
 
@@ -520,21 +651,23 @@ static int choose_chunk(int batch, int max_seq_len, int page_size, int align, in
   return static_cast<int>(ch);
 }
 
-#define IDXTOPK_DISPATCH_NT(KERNEL, heads, grid, stream, ...)                                 \
-  do {                                                                                      \
-    switch (heads) {                                                                        \
-      case 16: hipLaunchKernelGGL(KERNEL<1>, grid, dim3(IX_WG), 0, stream, __VA_ARGS__); break; \
-      case 32: hipLaunchKernelGGL(KERNEL<2>, grid, dim3(IX_WG), 0, stream, __VA_ARGS__); break; \
-      case 64: hipLaunchKernelGGL(KERNEL<4>, grid, dim3(IX_WG), 0, stream, __VA_ARGS__); break; \
-      case 128: hipLaunchKernelGGL(KERNEL<8>, grid, dim3(IX_WG), 0, stream, __VA_ARGS__); break; \
-      default: return -2;                                                                   \
-    }                                                                                       \
+#define IDXTOPK_DISPATCH_NT_LDS(KERNEL, heads, grid, lds, stream, ...)                               \
+  do {                                                                                            \
+    switch (heads) {                                                                              \
+      case 16: hipLaunchKernelGGL(KERNEL<1>, grid, dim3(IX_WG), lds, stream, __VA_ARGS__); break;   \
+      case 32: hipLaunchKernelGGL(KERNEL<2>, grid, dim3(IX_WG), lds, stream, __VA_ARGS__); break;   \
+      case 64: hipLaunchKernelGGL(KERNEL<4>, grid, dim3(IX_WG), lds, stream, __VA_ARGS__); break;   \
+      case 128: hipLaunchKernelGGL(KERNEL<8>, grid, dim3(IX_WG), lds, stream, __VA_ARGS__); break;  \
+      default: return -2;                                                                         \
+    }                                                                                             \
   } while (0)
+#define IDXTOPK_DISPATCH_NT(KERNEL, heads, grid, stream, ...) \
+  IDXTOPK_DISPATCH_NT_LDS(KERNEL, heads, grid, 0, stream, __VA_ARGS__)
 
 int launch_idx_score(const IndexerInputs& in, float* scores, int64_t score_stride, hipStream_t stream) {
   if (in.batch == 0) return 0;
   const int chunk = choose_chunk(in.batch, in.max_seq_len, in.page_size, kGroup, 512, 8192);
-  const IndexerArgs a = make_args(in, chunk);
+  const IndexerArgs a = make_args(in, chunk, true);
   const dim3 grid(static_cast<unsigned>(a.nchunk_max * in.batch));
   (void)hipGetLastError();
   IDXTOPK_DISPATCH_NT(score_kernel, in.heads, grid, stream, a, scores, score_stride);
@@ -545,7 +678,7 @@ int launch_fused(const IndexerInputs& in, int k, int32_t* out_slots, float* out_
                  hipStream_t stream) {
   if (in.batch == 0) return 0;
   const int chunk = choose_chunk(in.batch, in.max_seq_len, in.page_size, kGroup, 512, FU_CH_MAX);
-  const IndexerArgs a = make_args(in, chunk);
+  const IndexerArgs a = make_args(in, chunk, true);
   const FusedWs w = fused_ws(ws, in.batch, in.max_seq_len);
   FusedOut o;
   o.slots = out_slots;
@@ -553,7 +686,10 @@ int launch_fused(const IndexerInputs& in, int k, int32_t* out_slots, float* out_
   o.k = k;
   const dim3 grid(static_cast<unsigned>(a.nchunk_max * in.batch));
   (void)hipGetLastError();
-  IDXTOPK_DISPATCH_NT(fused_chunk_kernel, in.heads, grid, stream, a, w, k);
+  // the scores' dynamic LDS plus the static part stay within 64 KB
+  static_assert(FU_CH_MAX * 4 + sizeof(ChunkLds) <= 64 * 1024, "fused chunk LDS");
+  const size_t lds = static_cast<size_t>(chunk) * sizeof(float);
+  IDXTOPK_DISPATCH_NT_LDS(fused_chunk_kernel, in.heads, grid, lds, stream, a, w, k);
   hipLaunchKernelGGL(fused_merge_kernel, dim3(in.batch), dim3(MG_WG), 0, stream, a, w, o);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
@@ -563,7 +699,7 @@ int launch_block_topk(const IndexerInputs& in, int block_size, int top_blocks, i
   if (in.batch == 0) return 0;
   int chunk = choose_chunk(in.batch, in.max_seq_len, in.page_size, block_size, 512, 8192);
   if (chunk / block_size > BK_MAX_BLOCKS_PER_CHUNK) chunk = BK_MAX_BLOCKS_PER_CHUNK * block_size;
-  const IndexerArgs a = make_args(in, chunk);
+  const IndexerArgs a = make_args(in, chunk, true, block_size);
   const BlockWs w = block_ws(ws, in.batch, block_size, in.max_seq_len);
   BlockOut o;
   o.blocks = out_blocks;

@@ -40,8 +40,16 @@ struct IndexerArgs {
   const int32_t* seq_lens;
   int32_t batch;
   int32_t heads;
-  int32_t chunk;       // tokens per workgroup
+  int32_t chunk;       // tokens per full-size chunk
   int32_t nchunk_max;  // chunks per row in the grid
+  // Guided chunk schedule: chunks [0, n_full) have `chunk` tokens, the next
+  // n_half have chunk / 2 from token tok_half, the rest chunk / 4 from token
+  // tok_quarter (n_half = 0 and tok_half = tok_quarter = n_full * chunk when
+  // every chunk is full size).
+  int32_t n_full;
+  int32_t n_half;
+  int32_t tok_half;
+  int32_t tok_quarter;
 };
 
 template <int NT>

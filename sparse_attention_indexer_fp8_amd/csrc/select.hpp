@@ -196,24 +196,18 @@ struct BinThreshold {
   bool all;
 };
 
-// `load(i)` returns the count of bin i (0 <= i < NBINS). Every thread of the
-// workgroup must call this. Uses `scratch` (LDS, >= WG/64 + 4 words).
-template <int WG, int NBINS, class Load>
-__device__ BinThreshold wg_threshold_bin(Load&& load, uint32_t k, uint32_t* scratch) {
-  static_assert(NBINS % WG == 0, "bins per thread");
-  constexpr int PER = NBINS / WG;
+// Threshold bin from counts already in registers: thread t holds the counts
+// of bins [t * PER, (t + 1) * PER) in c[]. Every thread of the workgroup must
+// call this. Uses `scratch` (LDS, >= WG/64 + 4 words).
+template <int WG, int PER>
+__device__ BinThreshold wg_threshold_counts(const uint32_t (&c)[PER], uint32_t k, uint32_t* scratch) {
   constexpr int NW = WG / kWave;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
-  // thread t owns bins [t*PER, (t+1)*PER)
-  uint32_t c[PER];
   uint32_t local = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    c[i] = load(tid * PER + i);
-    local += c[i];
-  }
+  for (int i = 0; i < PER; ++i) local += c[i];
   const uint32_t pre = wave_prefix_incl(local);
   const uint32_t wtot = __builtin_amdgcn_readlane(pre, kWave - 1);
   const uint32_t incl_w = wtot - pre + local;  // within wave, lanes >= lane
@@ -253,6 +247,20 @@ __device__ BinThreshold wg_threshold_bin(Load&& load, uint32_t k, uint32_t* scra
   }
   __syncthreads();
   return r;
+}
+
+// `load(i)` returns the count of bin i (0 <= i < NBINS); all of a thread's
+// loads are issued before any count is used. Every thread of the workgroup
+// must call this. Uses `scratch` (LDS, >= WG/64 + 4 words).
+template <int WG, int NBINS, class Load>
+__device__ BinThreshold wg_threshold_bin(Load&& load, uint32_t k, uint32_t* scratch) {
+  static_assert(NBINS % WG == 0, "bins per thread");
+  constexpr int PER = NBINS / WG;
+  // thread t owns bins [t*PER, (t+1)*PER)
+  uint32_t c[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) c[i] = load(static_cast<int>(threadIdx.x) * PER + i);
+  return wg_threshold_counts<WG, PER>(c, k, scratch);
 }
 
 }  // namespace idxtopk
