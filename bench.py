@@ -62,7 +62,7 @@ def source_hash(kind: str) -> str:
 PMC_KERNELS = {
     # counters file name -> (source kind, kernel name prefix, grid size of the workload's launch)
     "topk_rows_packed_prefill_16384x70001": ("topk_rows", "idxtopk::topk_rows_kernel", 16384 * 256),
-    "fused_long_decode_B64_k2048": ("fused", "void idxtopk::fused_chunk_kernel", 2560 * 256),
+    "fused_long_decode_B64_k2048": ("fused", "void idxtopk::fused_chunk_kernel", None),
 }
 
 

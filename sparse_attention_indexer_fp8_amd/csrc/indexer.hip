@@ -40,7 +40,7 @@
 namespace idxtopk {
 
 constexpr int IX_WG = 256;
-constexpr int IX_RING = 6;  // 16-token key groups in flight per wave
+constexpr int IX_RING = 4;  // 16-token key groups in flight per wave
 constexpr int HIST_BITS = 12;
 constexpr int HIST_BINS = 1 << HIST_BITS;
 constexpr int HIST_SHIFT = 32 - HIST_BITS;
