@@ -141,6 +141,16 @@ __device__ __forceinline__ T wave_reduce(T x, Op op) {
   return op(op(read_lane(x, 0), read_lane(x, 16)), op(read_lane(x, 32), read_lane(x, 48)));
 }
 
+// Maximum over each row of 16 lanes, in every lane of the row.
+__device__ __forceinline__ uint32_t row16_max(uint32_t x) {
+  auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  x = mx(x, dpp_move<0xb1>(x));   // quad_perm:[1,0,3,2]
+  x = mx(x, dpp_move<0x4e>(x));   // quad_perm:[2,3,0,1]
+  x = mx(x, dpp_move<0x124>(x));  // row_ror:4
+  x = mx(x, dpp_move<0x128>(x));  // row_ror:8
+  return x;
+}
+
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
   return wave_reduce(v, [](uint32_t a, uint32_t b) { return a + b; });
 }

@@ -152,7 +152,9 @@ __global__ __launch_bounds__(IX_WG) void score_kernel(IndexerArgs a, float* scor
   if (tb >= n) return;
   const int te = min(n, tb + clen);
   float* srow = scores + static_cast<int64_t>(b) * sstride;
-  score_chunk<NT, IX_WG, IX_RING>(a, b, tb, te, pages, [&](int j, float s) { srow[j] = s; });
+  score_chunk<NT, IX_WG, IX_RING>(a, b, tb, te, pages, [&](int j, float s, bool valid) {
+    if (valid) srow[j] = s;
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -223,9 +225,11 @@ __global__ __launch_bounds__(IX_WG) void fused_chunk_kernel(IndexerArgs a, Fused
     s.lcnt2 = 0;
   }
   // (score_chunk synchronises before its first emit)
-  score_chunk<NT, IX_WG, IX_RING>(a, b, tb, te, s.pages, [&](int j, float v) {
-    sc[j - tb] = v;
-    atomicAdd(&s.hist[float_key(v) >> HIST_SHIFT], 1u);
+  score_chunk<NT, IX_WG, IX_RING>(a, b, tb, te, s.pages, [&](int j, float v, bool valid) {
+    if (valid) {
+      sc[j - tb] = v;
+      atomicAdd(&s.hist[float_key(v) >> HIST_SHIFT], 1u);
+    }
   });
   __syncthreads();
 
@@ -528,8 +532,13 @@ __global__ __launch_bounds__(IX_WG) void block_chunk_kernel(IndexerArgs a, Block
 
   for (int i = tid; i < nbc; i += IX_WG) s.bmax[i] = 0;
   // block size equals page size, so the page division gives the block index
-  score_chunk<NT, IX_WG, IX_RING>(a, b, tb, te, s.pages, [&](int j, float v) {
-    atomicMax(&s.bmax[fdiv(static_cast<uint32_t>(j - tb), a.pdiv)], float_key(v));
+  // A 16-token group lies inside one block (block size and chunk starts are
+  // multiples of 16), so the group's maximum is taken in registers (DPP over
+  // the 16 lanes of each row) and one lane updates the block.
+  score_chunk<NT, IX_WG, IX_RING>(a, b, tb, te, s.pages, [&](int j, float v, bool valid) {
+    uint32_t key = valid ? float_key(v) : 0u;
+    key = row16_max(key);
+    if (lane_id() == 0 && key) atomicMax(&s.bmax[fdiv(static_cast<uint32_t>(j - tb), a.pdiv)], key);
   });
   __syncthreads();
   const int blk0 = tb / bs;

@@ -117,8 +117,10 @@ constexpr int kMaxChunkPages = 1024;
 // RING groups of key loads in flight: a slot is consumed in place and refilled
 // with the group RING ahead right after, so no register copy ever forces the
 // wave to wait for loads it has only just issued.
-// emit(j, score) is called by every lane with (lane >> 4) == 0 for each valid
-// token j.
+// emit(j, score, valid) is called by every lane of the wave for each 16-token
+// group: lane l carries token j = group start + (l & 15) and its score, and
+// valid is true for exactly one lane per token in the chunk ((l >> 4) == 0
+// and j < tok_end).
 template <int NT, int WG, int RING, class Emit>
 __device__ void score_chunk(const IndexerArgs& a, int b, int tok_begin, int tok_end,
                             int32_t* lds_pages, Emit&& emit) {
@@ -160,7 +162,7 @@ __device__ void score_chunk(const IndexerArgs& a, int b, int tok_begin, int tok_
   const int gmax = g_hi - 1;
   auto consume = [&](int gi, float s) {
     const int j = tok_begin + gi * kGroup + c;
-    if (g == 0 && j < tok_end) emit(j, s);
+    emit(j, s, g == 0 && j < tok_end);
   };
 
   typedef float vks __attribute__((ext_vector_type(RING)));
