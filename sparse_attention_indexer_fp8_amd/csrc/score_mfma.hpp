@@ -13,6 +13,9 @@
 //   B (keys):   column c = token tok0 + c, bytes [32g, 32g + 32) of its key
 // A and B use the same K grouping, so the product sums the full 128-term dot
 // whatever order the hardware assigns to the K index inside a group.
+// The key operand is not loaded in this layout (16 scattered half-lines per
+// instruction stream at ~80% of the rate of whole lines): keys_to_operand
+// builds it from whole-line loads.
 // Result: lane l holds D[4g + r][c], r = 0..3, i.e. heads 4g + r of the tile
 // for token c.
 #pragma once
@@ -22,6 +25,7 @@
 namespace idxtopk {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kDim = 128;
@@ -52,6 +56,10 @@ struct IndexerArgs {
   int32_t tok_quarter;
 };
 
+struct KeyPieces {
+  v4i x0, x1;
+};
+
 template <int NT>
 struct QOperand {
   v8i a[NT];
@@ -69,9 +77,38 @@ __device__ __forceinline__ v8i load_v8i(const uint8_t* p) {
 }
 
 // Key bytes are read once per call: load them without keeping them in cache.
-__device__ __forceinline__ v8i load_v8i_stream(const uint8_t* p) {
-  const v8i* pv = reinterpret_cast<const v8i*>(p);
-  return __builtin_nontemporal_load(pv);
+__device__ __forceinline__ v4i load_v4i_stream(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+}
+
+// Keys are fetched in whole lines: for a group of 16 tokens, lane l loads the
+// 16-byte piece (l & 7) of token (l >> 3) (x0) and of token 8 + (l >> 3) (x1),
+// so each load instruction covers eight complete 128-byte keys. The B operand
+// wants lane (c, g) to hold pieces 2g and 2g + 1 of token c; two rounds of
+// ds_bpermute move them. In round 0 a lane with c < 8 pulls piece 2g from x0
+// of lane 8c + 2g, and a lane with c >= 8 pulls piece 2g + 1 from x1 of lane
+// 8(c - 8) + 2g + 1; round 1 pulls the other piece from the other parity.
+// Even lanes offer x0 in round 0 and x1 in round 1, odd lanes the reverse, so
+// every piece is sent once. Lanes with c >= 8 receive their pieces in swapped
+// order and put them back.
+__device__ __forceinline__ v8i keys_to_operand(const v4i x0, const v4i x1) {
+  const int l = lane_id();
+  const int c = l & 15, g = l >> 4, hi = c >> 3;
+  const int a0 = 4 * (8 * (c & 7) + 2 * g + hi);
+  const int a1 = 4 * (8 * (c & 7) + 2 * g + 1 - hi);
+  const bool even = (l & 1) == 0;
+  const v4i r0 = even ? x0 : x1, r1 = even ? x1 : x0;
+  v4i t0, t1;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    t0[d] = __builtin_amdgcn_ds_bpermute(a0, r0[d]);
+    t1[d] = __builtin_amdgcn_ds_bpermute(a1, r1[d]);
+  }
+  const v4i lo = hi ? t1 : t0, up = hi ? t0 : t1;
+  v8i kb;
+  kb[0] = lo[0]; kb[1] = lo[1]; kb[2] = lo[2]; kb[3] = lo[3];
+  kb[4] = up[0]; kb[5] = up[1]; kb[6] = up[2]; kb[7] = up[3];
+  return kb;
 }
 
 template <int NT>
@@ -147,15 +184,30 @@ __device__ void score_chunk(const IndexerArgs& a, int b, int tok_begin, int tok_
   const int g_hi = min(ngroups, g_lo + per);
   const int last = tok_end - 1;
 
-  // group gi of this chunk -> this lane's 32 key bytes and the token's scale
-  auto fetch = [&](int gi, v8i& kb, float& ks) {
-    int j = tok_begin + gi * kGroup + c;
+  // token j (clamped into the chunk) -> its cache slot. Slot ids fit in 32
+  // bits (they are returned as int32), so only byte offsets are widened.
+  // slot = page * P + (j - pg * P) = (page - pg) * P + j. The empty asm keeps
+  // the multiply and the add apart: fused, they become a 64-bit mad whose
+  // unused high addend half may alias a register with a key load still in
+  // flight, and the wait for that load would stall the ring.
+  auto slot_of = [&](int j) {
     j = j < last ? j : last;
     const uint32_t pg = fdiv(static_cast<uint32_t>(j), a.pdiv);
-    const uint32_t off = static_cast<uint32_t>(j) - pg * P;
-    const int64_t slot = static_cast<int64_t>(lds_pages[pg - p0]) * P + off;
-    kb = load_v8i_stream(a.kcache + slot * kDim + 32 * g);
-    ks = a.k_scale[slot];
+    uint32_t m = (static_cast<uint32_t>(lds_pages[pg - p0]) - pg) * P;
+    asm volatile("" : "+v"(m));
+    return m + static_cast<uint32_t>(j);
+  };
+  auto key_piece = [&](uint32_t slot, int lp) {
+    return load_v4i_stream(a.kcache + (static_cast<uint64_t>(slot) << 7) + lp);
+  };
+  // group gi of this chunk -> this lane's two whole-line key pieces and the
+  // scale of token c
+  const int lt = l >> 3, lp = 16 * (l & 7);
+  auto fetch = [&](int gi, KeyPieces& kp, float& ks) {
+    const int j0 = tok_begin + gi * kGroup;
+    kp.x0 = key_piece(slot_of(j0 + lt), lp);
+    kp.x1 = key_piece(slot_of(j0 + 8 + lt), lp);
+    ks = a.k_scale[slot_of(j0 + c)];
   };
 
   if (g_lo >= g_hi) return;
@@ -166,7 +218,7 @@ __device__ void score_chunk(const IndexerArgs& a, int b, int tok_begin, int tok_
   };
 
   typedef float vks __attribute__((ext_vector_type(RING)));
-  v8i ring[RING];
+  KeyPieces ring[RING];
   vks ksr;
 #pragma unroll
   for (int u = 0; u < RING; ++u) {
@@ -181,9 +233,12 @@ __device__ void score_chunk(const IndexerArgs& a, int b, int tok_begin, int tok_
   for (; gi0 + 2 * RING <= g_hi; gi0 += RING) {
 #pragma unroll
     for (int u = 0; u < RING; ++u) {
-      const float s = score16<NT>(qo, ring[u], ksr[u]);
+      float s = score16<NT>(qo, keys_to_operand(ring[u].x0, ring[u].x1), ksr[u]);
       // slot u is fully consumed before its refill is issued, so the refill can
-      // reuse the slot's registers (no copies, no early waits)
+      // reuse the slot's registers (no copies, no early waits). The empty asm
+      // makes the score final here, so the scale multiply cannot sink past the
+      // refill and keep the old scale alive beside the new one.
+      asm volatile("" : "+v"(s));
       __builtin_amdgcn_sched_barrier(0);
       float t;
       fetch(gi0 + u + RING, ring[u], t);
@@ -196,7 +251,7 @@ __device__ void score_chunk(const IndexerArgs& a, int b, int tok_begin, int tok_
   for (int u = 0; u < RING; ++u) {
     const int gi = gi0 + u;
     if (gi < g_hi) {
-      const float s = score16<NT>(qo, ring[u], ksr[u]);
+      const float s = score16<NT>(qo, keys_to_operand(ring[u].x0, ring[u].x1), ksr[u]);
       if (gi + RING < g_hi) {
         float t;
         fetch(gi + RING, ring[u], t);
@@ -208,7 +263,7 @@ __device__ void score_chunk(const IndexerArgs& a, int b, int tok_begin, int tok_
 #pragma unroll
   for (int u = 0; u < RING; ++u) {
     const int gi = gi0 + RING + u;
-    if (gi < g_hi) consume(gi, score16<NT>(qo, ring[u], ksr[u]));
+    if (gi < g_hi) consume(gi, score16<NT>(qo, keys_to_operand(ring[u].x0, ring[u].x1), ksr[u]));
   }
 }
 
