@@ -28,6 +28,8 @@ COMMON_FLAGS = [
     "-fPIC",
     "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results go straight to VGPRs (no accumulator-register reads)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 

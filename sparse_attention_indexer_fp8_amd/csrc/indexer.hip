@@ -31,7 +31,9 @@
 //     block table to slots. The merging workgroup then zeroes the row's
 //     histogram, counters and candidates, so the workspace is clean for the
 //     next call.
-// The score row never exists in HBM.
+// The score row never exists in HBM on this path. Batches of at most
+// FS_MAX_TOKENS tokens take a variant whose chunks write their scores to the
+// workspace instead (see "Fused decode, small batches" below).
 #include "common.hpp"
 #include "launch.hpp"
 #include "score_mfma.hpp"
@@ -492,6 +494,293 @@ __global__ __launch_bounds__(MG_WG) void fused_merge_kernel(IndexerArgs a, Fused
 }
 
 // ---------------------------------------------------------------------------
+// Fused decode, small batches: score buffer instead of candidates
+// ---------------------------------------------------------------------------
+//
+// When the batch holds few tokens (batch * max_seq_len <= FS_MAX_TOKENS) the
+// chunks are sized so that every chunk workgroup is resident at once, and a
+// chunk ends without waiting on anything: it writes its scores to the
+// workspace (the candidate area, as fp32 [rows][cap]) and adds its histogram
+// to the row's with fire-and-forget atomics. The per-chunk bound, the
+// read-back and the candidate reservation of the path above each cost a
+// dependent round trip that a short chunk cannot hide. One workgroup per row
+// then issues the histogram, the block table and its first scores together,
+// takes the exact threshold bin, emits the scores above it and selects
+// inside it. The extra bytes (scores written, read back and zeroed: 12 B per
+// token against 132 B of key and scale) stay in the last-level cache at
+// these sizes.
+
+constexpr int64_t FS_MAX_TOKENS = int64_t{1} << 21;
+constexpr int FS_CH_MAX = 4096;  // chunk tokens (dynamic LDS for the scores)
+constexpr int FS_CH_MIN = 256;
+constexpr int FS_RING = 4;       // key groups in flight per wave
+constexpr int FS_WG = 1024;      // merge workgroup
+constexpr int FS_PER = 8;        // scores per thread per pass of the merge
+constexpr int FS_BUF = 4096;     // threshold-bin keys held in LDS (32 KB)
+constexpr int FS_MAXE = FS_BUF / FS_WG;
+constexpr int FS_PAGES = 4096;   // block-table entries staged in LDS
+constexpr int FS_PG_PER = FS_PAGES / FS_WG;
+
+__device__ __forceinline__ float* fused_scores_row(const FusedWs& w, int b) {
+  return reinterpret_cast<float*>(w.cand) + static_cast<int64_t>(b) * w.cap;
+}
+
+struct ScoresChunkLds {
+  alignas(16) uint32_t hist[HIST_BINS];
+  int32_t pages[IX_PAGES];
+};
+
+template <int NT>
+__global__ __launch_bounds__(IX_WG) void fused_scores_chunk_kernel(IndexerArgs a, FusedWs ws) {
+  extern __shared__ float4 sc4[];
+  float* sc = reinterpret_cast<float*>(sc4);
+  __shared__ ScoresChunkLds s;
+  const int tid = threadIdx.x;
+  int b, c;
+  chunk_of(a, b, c);
+  const int n = a.seq_lens[b];
+  int tb, clen;
+  chunk_span(a, c, tb, clen);
+  if (tb >= n) return;
+  const int te = min(n, tb + clen);
+  const int cnt = te - tb;
+
+  for (int i = tid; i < HIST_BINS; i += IX_WG) s.hist[i] = 0;
+  // (score_chunk synchronises before its first emit)
+  score_chunk<NT, IX_WG, FS_RING>(a, b, tb, te, s.pages, [&](int j, float v, bool valid) {
+    if (valid) {
+      sc[j - tb] = v;
+      atomicAdd(&s.hist[float_key(v) >> HIST_SHIFT], 1u);
+    }
+  });
+  __syncthreads();
+  // scores out, 16 bytes per lane where the row's base allows it
+  float* srow = fused_scores_row(ws, b) + tb;
+  if ((reinterpret_cast<uintptr_t>(srow) & 15u) == 0) {
+    for (int i = 4 * tid; i < cnt; i += 4 * IX_WG) {
+      if (i + 4 <= cnt) {
+        *reinterpret_cast<float4*>(srow + i) = sc4[i / 4];
+      } else {
+        for (int e = i; e < cnt; ++e) srow[e] = sc[e];
+      }
+    }
+  } else {
+    for (int i = tid; i < cnt; i += IX_WG) srow[i] = sc[i];
+  }
+  uint32_t* Hg = ws.hist + static_cast<int64_t>(b) * HIST_BINS;
+#pragma unroll
+  for (int i = 0; i < HIST_BINS / IX_WG; ++i) {
+    const int bin = i * IX_WG + tid;
+    const uint32_t h = s.hist[bin];
+    if (h) add_dev(&Hg[bin], h);
+  }
+}
+
+struct ScoresMergeLds {
+  uint64_t buf[FS_BUF];
+  int32_t pages[FS_PAGES];
+  SelectLds sel;
+  uint32_t scratch[24];
+  uint32_t ocnt;
+  uint32_t bcnt;
+};
+
+// One workgroup per row: exact top-k of the row's scores from its complete
+// histogram, then the row's scores and histogram are zeroed again.
+__global__ __launch_bounds__(FS_WG) void fused_scores_merge_kernel(IndexerArgs a, FusedWs ws, FusedOut o) {
+  __shared__ ScoresMergeLds s;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int n = a.seq_lens[b];
+  const uint32_t k = static_cast<uint32_t>(o.k);
+  const uint32_t P = static_cast<uint32_t>(a.page_size);
+  uint32_t* Hg = ws.hist + static_cast<int64_t>(b) * HIST_BINS;
+  float* srow = fused_scores_row(ws, b);
+  const int32_t* bt_row = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
+  const int npages = n > 0 ? static_cast<int>(fdiv(static_cast<uint32_t>(n - 1), a.pdiv)) + 1 : 0;
+  const bool staged = npages <= FS_PAGES;
+  const int64_t orow = static_cast<int64_t>(b) * o.k;
+
+  wg_select_init<FS_WG>(s.sel);
+  if (tid == 0) {
+    s.ocnt = 0;
+    s.bcnt = 0;
+  }
+  // In flight together: the first pass of scores, the block table, the
+  // histogram (indices past the row re-read entry 0, which exists).
+  float v0[FS_PER];
+#pragma unroll
+  for (int e = 0; e < FS_PER; ++e) {
+    const int i = e * FS_WG + tid;
+    v0[e] = srow[i < n ? i : 0];
+  }
+  if (staged && npages > 0) {
+    int32_t pg[FS_PG_PER];
+#pragma unroll
+    for (int r = 0; r < FS_PG_PER; ++r) {
+      const int i = r * FS_WG + tid;
+      pg[r] = bt_row[i < npages ? i : 0];
+    }
+#pragma unroll
+    for (int r = 0; r < FS_PG_PER; ++r)
+      if (r * FS_WG + tid < npages) s.pages[r * FS_WG + tid] = pg[r];
+  }
+  const BinThreshold th = wg_threshold_bin<FS_WG, HIST_BINS>([&](int i) { return Hg[i]; }, k, s.scratch);
+  const uint32_t bstar = th.all ? 0u : th.bin;
+  const uint32_t need = th.all ? 0u : k - th.above;
+
+  auto slot_of = [&](uint32_t pos) {
+    const uint32_t pg = fdiv(pos, a.pdiv);
+    const int32_t page = staged ? s.pages[pg] : bt_row[pg];
+    return static_cast<int32_t>(static_cast<uint32_t>(page) * P + (pos - pg * P));
+  };
+  // Emit the keys with keep[e] set: one reservation per wave, then slots.
+  // Every slot is looked up before any is stored, outside the branches, so
+  // the lookups overlap.
+  auto emit = [&](const uint64_t* key, const bool* keep, int m) {
+    uint32_t mine = 0;
+    for (int e = 0; e < m; ++e) mine += keep[e];
+    uint32_t at = wave_reserve(mine, &s.ocnt);
+    int32_t sl[FS_MAXE];
+    for (int e = 0; e < m; ++e) sl[e] = slot_of(keep[e] ? rank_pos(key[e]) : 0u);
+    for (int e = 0; e < m; ++e) {
+      if (keep[e]) {
+        if (at < k) {
+          o.slots[orow + at] = sl[e];
+          if (o.scores) o.scores[orow + at] = key_float(rank_vkey(key[e]));
+        }
+        ++at;
+      }
+    }
+  };
+  // One pass: scores above the threshold bin (all of them when the row holds
+  // at most k) are emitted, scores inside it go to LDS as unique keys.
+  auto pass = [&](const float (&v)[FS_PER], int base) {
+    static_assert(FS_PER <= 32, "bit masks");
+    uint32_t keepm = 0, midm = 0;
+#pragma unroll
+    for (int e = 0; e < FS_PER; ++e) {
+      const bool valid = base + e * FS_WG + tid < n;
+      const uint32_t bin = float_key(v[e]) >> HIST_SHIFT;
+      keepm |= static_cast<uint32_t>(valid && (th.all || bin > bstar)) << e;
+      midm |= static_cast<uint32_t>(valid && !th.all && bin == bstar) << e;
+    }
+    uint32_t at = wave_reserve(__builtin_popcount(keepm), &s.ocnt);
+    int32_t sl[FS_PER];
+#pragma unroll
+    for (int e = 0; e < FS_PER; ++e) {
+      const int i = base + e * FS_WG + tid;
+      sl[e] = slot_of(static_cast<uint32_t>(i < n ? i : 0));
+    }
+#pragma unroll
+    for (int e = 0; e < FS_PER; ++e) {
+      if ((keepm >> e) & 1u) {
+        if (at < k) {
+          o.slots[orow + at] = sl[e];
+          if (o.scores) o.scores[orow + at] = v[e];
+        }
+        ++at;
+      }
+    }
+    uint32_t bt = wave_reserve(__builtin_popcount(midm), &s.bcnt);
+#pragma unroll
+    for (int e = 0; e < FS_PER; ++e) {
+      if ((midm >> e) & 1u) {
+        if (bt < static_cast<uint32_t>(FS_BUF))
+          s.buf[bt] = rank_key(float_key(v[e]), static_cast<uint32_t>(base + e * FS_WG + tid));
+        ++bt;
+      }
+    }
+  };
+  // the next pass's scores are in flight while this pass is processed
+  for (int base = 0; base == 0 || base < n; base += FS_PER * FS_WG) {
+    float nx[FS_PER];
+    const int nb0 = base + FS_PER * FS_WG;
+    if (nb0 < n) {
+#pragma unroll
+      for (int e = 0; e < FS_PER; ++e) {
+        const int i = nb0 + e * FS_WG + tid;
+        nx[e] = srow[i < n ? i : 0];
+      }
+    }
+    pass(v0, base);
+    if (nb0 < n) {
+#pragma unroll
+      for (int e = 0; e < FS_PER; ++e) v0[e] = nx[e];
+    }
+  }
+  __syncthreads();
+  const uint32_t nb = s.bcnt;
+  if (!th.all && nb > 0) {
+    if (nb <= static_cast<uint32_t>(FS_BUF)) {
+      uint64_t keys[FS_MAXE];
+      bool keep[FS_MAXE];
+      uint64_t mn = ~0ull, mx = 0;
+#pragma unroll
+      for (int e = 0; e < FS_MAXE; ++e) {
+        const uint32_t i = tid + e * FS_WG;
+        keys[e] = i < nb ? s.buf[i] : 0ull;
+        if (i < nb) {
+          mn = keys[e] < mn ? keys[e] : mn;
+          mx = keys[e] > mx ? keys[e] : mx;
+        }
+      }
+      uint64_t T = 0;  // keys >= T are selected
+      if (nb > need) {
+        wg_range<FS_WG>(mn, mx, s.sel);
+        T = wg_select<FS_WG>(
+            [&](auto&& f) {
+#pragma unroll
+              for (int e = 0; e < FS_MAXE; ++e)
+                if (tid + e * FS_WG < nb) f(keys[e]);
+            },
+            need, mn, mx, s.sel);
+      }
+#pragma unroll
+      for (int e = 0; e < FS_MAXE; ++e) keep[e] = tid + e * FS_WG < nb && keys[e] >= T;
+      emit(keys, keep, FS_MAXE);
+    } else {
+      // threshold bin larger than the LDS buffer: select straight from the
+      // row's scores (several passes over them)
+      auto each_mid = [&](auto&& f) {
+        for (int i = tid; i < n; i += FS_WG) {
+          const uint32_t vk = float_key(srow[i]);
+          if ((vk >> HIST_SHIFT) == bstar) f(rank_key(vk, static_cast<uint32_t>(i)));
+        }
+      };
+      uint64_t mn = ~0ull, mx = 0;
+      each_mid([&](uint64_t key) {
+        mn = key < mn ? key : mn;
+        mx = key > mx ? key : mx;
+      });
+      wg_range<FS_WG>(mn, mx, s.sel);
+      const uint64_t T = wg_select<FS_WG>(each_mid, need, mn, mx, s.sel);
+      for (int i0 = 0; i0 < n; i0 += FS_WG) {
+        const int i = i0 + tid;
+        uint64_t key = 0;
+        bool keep = false;
+        if (i < n) {
+          const uint32_t vk = float_key(srow[i]);
+          key = rank_key(vk, static_cast<uint32_t>(i));
+          keep = (vk >> HIST_SHIFT) == bstar && key >= T;
+        }
+        emit(&key, &keep, 1);
+      }
+    }
+  }
+  __syncthreads();
+  // padding for rows shorter than k
+  for (uint32_t i = min(s.ocnt, k) + tid; i < k; i += FS_WG) {
+    o.slots[orow + i] = -1;
+    if (o.scores) o.scores[orow + i] = -__builtin_inff();
+  }
+  // leave the row's workspace bytes zero again
+  for (int i = tid; i < n; i += FS_WG) srow[i] = 0.0f;
+  if (n > 0)
+    for (int i = tid; i < HIST_BINS; i += FS_WG) Hg[i] = 0;
+}
+
+// ---------------------------------------------------------------------------
 // Block-sparse top-k: chunk kernel (block maxima), then per-row merge kernel
 // ---------------------------------------------------------------------------
 
@@ -683,9 +972,60 @@ int launch_idx_score(const IndexerInputs& in, float* scores, int64_t score_strid
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
+// Workgroups of fused_scores_chunk_kernel that the current device holds at
+// once (all compute units, launched with the largest score LDS). Cached per
+// device and head count.
+static int fs_resident_wgs(int heads) {
+  static int cache[4][64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  const int ti = heads == 16 ? 0 : heads == 32 ? 1 : heads == 64 ? 2 : 3;
+  if (cache[ti][dev] > 0) return cache[ti][dev];
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  const size_t lds = static_cast<size_t>(FS_CH_MAX) * sizeof(float);
+  hipError_t e = hipErrorInvalidValue;
+  switch (heads) {
+    case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_scores_chunk_kernel<1>, IX_WG, lds); break;
+    case 32: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_scores_chunk_kernel<2>, IX_WG, lds); break;
+    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_scores_chunk_kernel<4>, IX_WG, lds); break;
+    case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_scores_chunk_kernel<8>, IX_WG, lds); break;
+    default: break;
+  }
+  if (e != hipSuccess || per < 1) per = 1;
+  cache[ti][dev] = cus * per;
+  return cache[ti][dev];
+}
+
+// Score-buffer path: chunks sized so the whole grid is resident at once.
+static int launch_fused_scores(const IndexerInputs& in, const FusedWs& w, const FusedOut& o, hipStream_t stream) {
+  const int64_t tokens = static_cast<int64_t>(in.batch) * (in.max_seq_len > 0 ? in.max_seq_len : 1);
+  const int64_t nwg = fs_resident_wgs(in.heads);
+  int64_t ch = nwg > 0 ? (tokens + nwg - 1) / nwg : FS_CH_MAX;
+  ch = (ch + kGroup - 1) / kGroup * kGroup;
+  if (ch < FS_CH_MIN) ch = FS_CH_MIN;
+  if (ch > FS_CH_MAX) ch = FS_CH_MAX;
+  const int64_t page_cap = (static_cast<int64_t>(IX_PAGES - 2) * in.page_size) / kGroup * kGroup;
+  if (ch > page_cap) ch = page_cap > kGroup ? page_cap : kGroup;
+  const IndexerArgs a = make_args(in, static_cast<int>(ch), false);
+  const dim3 grid(static_cast<unsigned>(a.nchunk_max * in.batch));
+  const size_t lds = static_cast<size_t>(ch) * sizeof(float);
+  (void)hipGetLastError();
+  IDXTOPK_DISPATCH_NT_LDS(fused_scores_chunk_kernel, in.heads, grid, lds, stream, a, w);
+  hipLaunchKernelGGL(fused_scores_merge_kernel, dim3(in.batch), dim3(FS_WG), 0, stream, a, w, o);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
 int launch_fused(const IndexerInputs& in, int k, int32_t* out_slots, float* out_scores, void* ws,
                  hipStream_t stream) {
   if (in.batch == 0) return 0;
+  if (static_cast<int64_t>(in.batch) * in.max_seq_len <= FS_MAX_TOKENS) {
+    FusedOut o;
+    o.slots = out_slots;
+    o.scores = out_scores;
+    o.k = k;
+    return launch_fused_scores(in, fused_ws(ws, in.batch, in.max_seq_len), o, stream);
+  }
   const int chunk = choose_chunk(in.batch, in.max_seq_len, in.page_size, kGroup, 512, FU_CH_MAX);
   const IndexerArgs a = make_args(in, chunk, true);
   const FusedWs w = fused_ws(ws, in.batch, in.max_seq_len);

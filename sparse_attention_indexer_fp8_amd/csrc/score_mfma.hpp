@@ -124,16 +124,29 @@ __device__ __forceinline__ void load_query(QOperand<NT>& qo, const uint8_t* q_ro
   }
 }
 
+// max(x, 0) for a float that is not NaN, as one integer max on its bits:
+// positive floats are positive integers, negative ones (and -0) negative.
+__device__ __forceinline__ float relu_bits(float x) {
+  const int b = __float_as_int(x);
+  return __int_as_float(b > 0 ? b : 0);
+}
+
 // Score of token (tok0 + (lane & 15)), returned in every lane of the wave.
 template <int NT>
 __device__ __forceinline__ float score16(const QOperand<NT>& qo, const v8i kb, float ks) {
+  // all tiles' products first, so no result is waited on while another
+  // product could still be issued
+  v4f acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.a[t], kb, zero, 0, 0, 0, 0, 0, 0);
+  }
   float part = 0.0f;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.a[t], kb, acc, 0, 0, 0, 0, 0, 0);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) part = fmaf(qo.wt[t][r], fmaxf(acc[r], 0.0f), part);
+    for (int r = 0; r < 4; ++r) part = fmaf(qo.wt[t][r], relu_bits(acc[t][r]), part);
   }
   // sum the four 16-lane groups (heads 4g..4g+3 of every tile)
   const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part),
@@ -158,9 +171,9 @@ constexpr int kMaxChunkPages = 1024;
 // group: lane l carries token j = group start + (l & 15) and its score, and
 // valid is true for exactly one lane per token in the chunk ((l >> 4) == 0
 // and j < tok_end).
-template <int NT, int WG, int RING, class Emit>
-__device__ void score_chunk(const IndexerArgs& a, int b, int tok_begin, int tok_end,
-                            int32_t* lds_pages, Emit&& emit) {
+template <int NT, int WG, int RING, bool WHOLE, class Emit>
+__device__ __forceinline__ void score_chunk_impl(const IndexerArgs& a, int b, int tok_begin, int tok_end,
+                                                 int32_t* lds_pages, Emit&& emit) {
   constexpr int NW = WG / kWave;
   const int tid = threadIdx.x;
   const int wave = uniform(tid / kWave);
@@ -201,13 +214,26 @@ __device__ void score_chunk(const IndexerArgs& a, int b, int tok_begin, int tok_
     return load_v4i_stream(a.kcache + (static_cast<uint64_t>(slot) << 7) + lp);
   };
   // group gi of this chunk -> this lane's two whole-line key pieces and the
-  // scale of token c
+  // scale of token c. When pages hold whole groups and the chunk starts on a
+  // group boundary, a group never straddles a page: one lookup gives the
+  // group's first slot, and tokens past the chunk's end read bytes of that
+  // same page (never used), so nothing is clamped.
   const int lt = l >> 3, lp = 16 * (l & 7);
   auto fetch = [&](int gi, KeyPieces& kp, float& ks) {
     const int j0 = tok_begin + gi * kGroup;
-    kp.x0 = key_piece(slot_of(j0 + lt), lp);
-    kp.x1 = key_piece(slot_of(j0 + 8 + lt), lp);
-    ks = a.k_scale[slot_of(j0 + c)];
+    if (WHOLE) {
+      const uint32_t pg = fdiv(static_cast<uint32_t>(j0), a.pdiv);
+      uint32_t m = (static_cast<uint32_t>(uniform(lds_pages[pg - p0])) - pg) * P;
+      asm volatile("" : "+s"(m));
+      const uint32_t s0 = m + static_cast<uint32_t>(j0);
+      kp.x0 = key_piece(s0 + lt, lp);
+      kp.x1 = key_piece(s0 + 8 + lt, lp);
+      ks = a.k_scale[s0 + c];
+    } else {
+      kp.x0 = key_piece(slot_of(j0 + lt), lp);
+      kp.x1 = key_piece(slot_of(j0 + 8 + lt), lp);
+      ks = a.k_scale[slot_of(j0 + c)];
+    }
   };
 
   if (g_lo >= g_hi) return;
@@ -265,6 +291,18 @@ __device__ void score_chunk(const IndexerArgs& a, int b, int tok_begin, int tok_
     const int gi = gi0 + RING + u;
     if (gi < g_hi) consume(gi, score16<NT>(qo, keys_to_operand(ring[u].x0, ring[u].x1), ksr[u]));
   }
+}
+
+// Score the tokens [tok_begin, tok_end) of row b with a WG-thread workgroup
+// (see score_chunk_impl). Chunks whose pages hold whole 16-token groups, and
+// that start on a group boundary, take the one-lookup-per-group fetch.
+template <int NT, int WG, int RING, class Emit>
+__device__ void score_chunk(const IndexerArgs& a, int b, int tok_begin, int tok_end, int32_t* lds_pages,
+                            Emit&& emit) {
+  if (a.page_size % kGroup == 0 && tok_begin % kGroup == 0)
+    score_chunk_impl<NT, WG, RING, true>(a, b, tok_begin, tok_end, lds_pages, emit);
+  else
+    score_chunk_impl<NT, WG, RING, false>(a, b, tok_begin, tok_end, lds_pages, emit);
 }
 
 }  // namespace idxtopk

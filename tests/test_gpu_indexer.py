@@ -132,6 +132,73 @@ def test_fused_workspace_reuse_smaller_second_call(ops):
         assert np.array_equal(np.sort(slots, axis=1), np.sort(ref, axis=1))
 
 
+# Batches of at most this many tokens (batch * max_seq_len) take the
+# score-buffer variant of the fused path; larger ones the candidate variant.
+FUSED_SCORE_PATH_TOKENS = 1 << 21
+
+
+def _candidate_variant(case):
+    """The same case with a max_seq_len (an upper bound on every row length)
+    large enough to send it down the candidate variant. The block table gets
+    zero columns so it covers that bound, as the API requires; no row reads
+    them."""
+    import copy
+
+    big = copy.copy(case)
+    big.max_seq_len = FUSED_SCORE_PATH_TOKENS // case.batch + 1
+    cols = -(-big.max_seq_len // case.page_size)
+    bt = np.zeros((case.batch, cols), np.int32)
+    bt[:, :case.block_table.shape[1]] = case.block_table
+    big.block_table = bt
+    return big
+
+
+@pytest.mark.parametrize("page_size,heads,k", [(64, 64, 2048), (16, 32, 300), (1, 16, 100)])
+def test_fused_both_variants_exact(ops, page_size, heads, k):
+    """The score-buffer and candidate variants of the fused path select the
+    oracle's exact set on the same inputs."""
+    case = _exact_case(450 + page_size, batch=6, n_lo=1, n_hi=16000, page_size=page_size, heads=heads, k=k,
+                       first=(0, k - 1, k, 16000))
+    assert case.batch * case.max_seq_len <= FUSED_SCORE_PATH_TOKENS
+    ref_slots, _, _ = oracle.fused_topk(case)
+    big = _candidate_variant(case)
+    for c in (case, big):
+        log(f"fused variant check: batch={c.batch} max_seq_len={c.max_seq_len} k={k} page_size={page_size}")
+        slots, _ = _fused(ops, c)
+        for b in range(case.batch):
+            assert np.array_equal(np.sort(slots[b]), np.sort(ref_slots[b])), (c.max_seq_len, b)
+
+
+def test_fused_workspace_reuse_across_variants(ops):
+    """Each variant leaves the workspace zeroed for the other."""
+    from sparse_attention_indexer_fp8_amd import ops as o
+
+    ws = o.Workspace()
+    a = _exact_case(611, batch=4, n_lo=3000, n_hi=20000, page_size=64, k=700)
+    b = _exact_case(612, batch=3, n_lo=100, n_hi=5000, page_size=16, k=300)
+    a_big = _candidate_variant(a)
+    for case in (a, a_big, b, a_big, a):
+        slots, _ = _fused(ops, case, ws=ws)
+        ref, _, _ = oracle.fused_topk(case)
+        assert np.array_equal(np.sort(slots, axis=1), np.sort(ref, axis=1))
+
+
+def test_fused_all_scores_tied(ops):
+    """Every key of a row is the same vector, so all its scores tie and the
+    threshold bin holds the whole row (more keys than the merge buffers):
+    the k lowest positions are selected."""
+    case = _exact_case(620, batch=3, n_lo=9000, n_hi=12000, page_size=64, k=1500, first=(12000, 5000))
+    real = case.k_scale < workloads.SENTINEL_KEY_SCALE
+    case.kcache[real] = case.kcache[real][0]
+    ref_slots, ref_pos, _ = oracle.fused_topk(case)
+    for b in range(case.batch):
+        assert np.array_equal(np.sort(ref_pos[b]), np.arange(case.k)), b
+    for c in (case, _candidate_variant(case)):
+        slots, _ = _fused(ops, c)
+        for b in range(case.batch):
+            assert np.array_equal(np.sort(slots[b]), np.sort(ref_slots[b])), (c.max_seq_len, b)
+
+
 def test_fused_never_reads_outside_windows(ops):
     """Sentinel keys (+448, scale 1e3) fill every slot no row owns; selecting
     one of them would map to no token of the row and fail the inverse map."""
