@@ -518,6 +518,7 @@ constexpr int FS_WG = 1024;      // merge workgroup
 constexpr int FS_PER = 8;        // scores per thread per pass of the merge
 constexpr int FS_BUF = 4096;     // threshold-bin keys held in LDS (32 KB)
 constexpr int FS_MAXE = FS_BUF / FS_WG;
+static_assert(FS_MAXE <= FS_PER, "slot lookups of one emission");
 constexpr int FS_PAGES = 4096;   // block-table entries staged in LDS
 constexpr int FS_PG_PER = FS_PAGES / FS_WG;
 
@@ -586,19 +587,17 @@ struct ScoresMergeLds {
 };
 
 // One workgroup per row: exact top-k of the row's scores from its complete
-// histogram, then the row's scores and histogram are zeroed again.
-__global__ __launch_bounds__(FS_WG) void fused_scores_merge_kernel(IndexerArgs a, FusedWs ws, FusedOut o) {
-  __shared__ ScoresMergeLds s;
+// histogram, then the row's scores and histogram are zeroed again. STAGED:
+// the row's block table fits in LDS (else slots are looked up in HBM).
+template <bool STAGED>
+__device__ __forceinline__ void fused_scores_merge_row(const IndexerArgs& a, const FusedWs& ws, const FusedOut& o,
+                                                       ScoresMergeLds& s, int b, int n, int npages) {
   const int tid = threadIdx.x;
-  const int b = blockIdx.x;
-  const int n = a.seq_lens[b];
   const uint32_t k = static_cast<uint32_t>(o.k);
   const uint32_t P = static_cast<uint32_t>(a.page_size);
   uint32_t* Hg = ws.hist + static_cast<int64_t>(b) * HIST_BINS;
   float* srow = fused_scores_row(ws, b);
   const int32_t* bt_row = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
-  const int npages = n > 0 ? static_cast<int>(fdiv(static_cast<uint32_t>(n - 1), a.pdiv)) + 1 : 0;
-  const bool staged = npages <= FS_PAGES;
   const int64_t orow = static_cast<int64_t>(b) * o.k;
 
   wg_select_init<FS_WG>(s.sel);
@@ -614,7 +613,7 @@ __global__ __launch_bounds__(FS_WG) void fused_scores_merge_kernel(IndexerArgs a
     const int i = e * FS_WG + tid;
     v0[e] = srow[i < n ? i : 0];
   }
-  if (staged && npages > 0) {
+  if (STAGED && npages > 0) {
     int32_t pg[FS_PG_PER];
 #pragma unroll
     for (int r = 0; r < FS_PG_PER; ++r) {
@@ -629,10 +628,24 @@ __global__ __launch_bounds__(FS_WG) void fused_scores_merge_kernel(IndexerArgs a
   const uint32_t bstar = th.all ? 0u : th.bin;
   const uint32_t need = th.all ? 0u : k - th.above;
 
-  auto slot_of = [&](uint32_t pos) {
-    const uint32_t pg = fdiv(pos, a.pdiv);
-    const int32_t page = staged ? s.pages[pg] : bt_row[pg];
-    return static_cast<int32_t>(static_cast<uint32_t>(page) * P + (pos - pg * P));
+  // Slots of M positions: every page lookup is issued before any is used.
+  // slot = (page - pg) * P + pos, with the multiply and the add kept apart
+  // by an empty asm (fused, they become a 64-bit mad whose unused high
+  // addend half can alias a register with a load in flight, and the wait for
+  // it drains every load); the asm also fixes each slot before the branches
+  // that store it.
+  auto slots_of = [&](const uint32_t* pos, int32_t* sl, int m) {
+    uint32_t pg[FS_PER];
+    int32_t page[FS_PER];
+    for (int e = 0; e < m; ++e) {
+      pg[e] = fdiv(pos[e], a.pdiv);
+      page[e] = STAGED ? s.pages[pg[e]] : bt_row[pg[e]];
+    }
+    for (int e = 0; e < m; ++e) {
+      uint32_t x = (static_cast<uint32_t>(page[e]) - pg[e]) * P;
+      asm volatile("" : "+v"(x));
+      sl[e] = static_cast<int32_t>(x + pos[e]);
+    }
   };
   // Emit the keys with keep[e] set: one reservation per wave, then slots.
   // Every slot is looked up before any is stored, outside the branches, so
@@ -641,8 +654,10 @@ __global__ __launch_bounds__(FS_WG) void fused_scores_merge_kernel(IndexerArgs a
     uint32_t mine = 0;
     for (int e = 0; e < m; ++e) mine += keep[e];
     uint32_t at = wave_reserve(mine, &s.ocnt);
+    uint32_t pos[FS_MAXE];
     int32_t sl[FS_MAXE];
-    for (int e = 0; e < m; ++e) sl[e] = slot_of(keep[e] ? rank_pos(key[e]) : 0u);
+    for (int e = 0; e < m; ++e) pos[e] = keep[e] ? rank_pos(key[e]) : 0u;
+    slots_of(pos, sl, m);
     for (int e = 0; e < m; ++e) {
       if (keep[e]) {
         if (at < k) {
@@ -666,12 +681,14 @@ __global__ __launch_bounds__(FS_WG) void fused_scores_merge_kernel(IndexerArgs a
       midm |= static_cast<uint32_t>(valid && !th.all && bin == bstar) << e;
     }
     uint32_t at = wave_reserve(__builtin_popcount(keepm), &s.ocnt);
+    uint32_t pos[FS_PER];
     int32_t sl[FS_PER];
 #pragma unroll
     for (int e = 0; e < FS_PER; ++e) {
       const int i = base + e * FS_WG + tid;
-      sl[e] = slot_of(static_cast<uint32_t>(i < n ? i : 0));
+      pos[e] = static_cast<uint32_t>(i < n ? i : 0);
     }
+    slots_of(pos, sl, FS_PER);
 #pragma unroll
     for (int e = 0; e < FS_PER; ++e) {
       if ((keepm >> e) & 1u) {
@@ -778,6 +795,17 @@ __global__ __launch_bounds__(FS_WG) void fused_scores_merge_kernel(IndexerArgs a
   for (int i = tid; i < n; i += FS_WG) srow[i] = 0.0f;
   if (n > 0)
     for (int i = tid; i < HIST_BINS; i += FS_WG) Hg[i] = 0;
+}
+
+__global__ __launch_bounds__(FS_WG) void fused_scores_merge_kernel(IndexerArgs a, FusedWs ws, FusedOut o) {
+  __shared__ ScoresMergeLds s;
+  const int b = blockIdx.x;
+  const int n = a.seq_lens[b];
+  const int npages = n > 0 ? static_cast<int>(fdiv(static_cast<uint32_t>(n - 1), a.pdiv)) + 1 : 0;
+  if (npages <= FS_PAGES)
+    fused_scores_merge_row<true>(a, ws, o, s, b, n, npages);
+  else
+    fused_scores_merge_row<false>(a, ws, o, s, b, n, npages);
 }
 
 // ---------------------------------------------------------------------------
@@ -1043,10 +1071,44 @@ int launch_fused(const IndexerInputs& in, int k, int32_t* out_slots, float* out_
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
+// Workgroups of block_chunk_kernel that the current device holds at once.
+static int bk_resident_wgs(int heads) {
+  static int cache[4][64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  const int ti = heads == 16 ? 0 : heads == 32 ? 1 : heads == 64 ? 2 : 3;
+  if (cache[ti][dev] > 0) return cache[ti][dev];
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  hipError_t e = hipErrorInvalidValue;
+  switch (heads) {
+    case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, block_chunk_kernel<1>, IX_WG, 0); break;
+    case 32: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, block_chunk_kernel<2>, IX_WG, 0); break;
+    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, block_chunk_kernel<4>, IX_WG, 0); break;
+    case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, block_chunk_kernel<8>, IX_WG, 0); break;
+    default: break;
+  }
+  if (e != hipSuccess || per < 1) per = 1;
+  cache[ti][dev] = cus * per;
+  return cache[ti][dev];
+}
+
 int launch_block_topk(const IndexerInputs& in, int block_size, int top_blocks, int32_t* out_blocks,
                       int32_t* out_slots, void* ws, hipStream_t stream) {
   if (in.batch == 0) return 0;
   int chunk = choose_chunk(in.batch, in.max_seq_len, in.page_size, block_size, 512, 8192);
+  // When one resident wave of workgroups can hold the whole batch at chunks
+  // of at most 8192 tokens, size the chunks for exactly that: every chunk
+  // then runs at once, and each amortises its setup over more tokens.
+  const int64_t tokens = static_cast<int64_t>(in.batch) * (in.max_seq_len > 0 ? in.max_seq_len : 1);
+  const int64_t nwg = bk_resident_wgs(in.heads);
+  if (nwg > 0 && tokens <= nwg * 8192) {
+    int64_t ch = (tokens + nwg - 1) / nwg;
+    ch = (ch + block_size - 1) / block_size * block_size;
+    const int64_t page_cap = static_cast<int64_t>(IX_PAGES - 2) * in.page_size / block_size * block_size;
+    if (ch > page_cap) ch = page_cap;
+    if (ch > chunk) chunk = static_cast<int>(ch);
+  }
   if (chunk / block_size > BK_MAX_BLOCKS_PER_CHUNK) chunk = BK_MAX_BLOCKS_PER_CHUNK * block_size;
   const IndexerArgs a = make_args(in, chunk, true, block_size);
   const BlockWs w = block_ws(ws, in.batch, block_size, in.max_seq_len);
