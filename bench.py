@@ -299,6 +299,29 @@ def bench_fused(torch, ops, timer, case, warmup, steps, flush):
     return res
 
 
+def bench_unfused(torch, ops, timer, case, warmup, steps, flush):
+    """The unfused path on the same inputs: idx_score_fp8 writes the score
+    rows, then topk_rows selects and maps through the block table (the pages'
+    "before" of the fusion). Same algorithmic bytes as the fused call, so the
+    two figures compare directly."""
+    args = [dev(torch, x) for x in (case.q, case.q_scale, case.w, case.kcache, case.k_scale,
+                                    case.block_table, case.seq_lens)]
+    scores = torch.empty((case.batch, max(1, case.max_seq_len)), dtype=torch.float32, device="cuda")
+    out = torch.empty((case.batch, case.k), dtype=torch.int32, device="cuda")
+    bt, sl = args[5], args[6]
+
+    def step():
+        ops.idx_score_fp8(*args, case.page_size, case.max_seq_len, out=scores)
+        ops.topk_rows(scores, sl, case.k, page_table=bt, page_size=case.page_size, out=out)
+
+    wall, us, region = timer.run(step, warmup, steps, flush)
+    res = summary(us, indexer_algorithmic_bytes(case, case.batch * case.k), case.batch, region, timer.settled)
+    res["score_buffer_bytes"] = int(scores.numel() * 4)
+    del args, scores
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_block(torch, ops, timer, case, warmup, steps, flush):
     args = [dev(torch, x) for x in (case.q, case.q_scale, case.w, case.kcache, case.k_scale,
                                     case.block_table, case.seq_lens)]
@@ -410,6 +433,9 @@ def main(argv=None):
         log("timing fused decode B32 ...")
         c2 = workloads.c2_fused_decode()
         also["fused_decode_B32_k2048"] = bench_fused(torch, ops, timer, c2, a.warmup, max(a.steps, 50), True)
+        log("timing fused decode B32, unfused path ...")
+        also["fused_decode_B32_k2048_unfused"] = bench_unfused(torch, ops, timer, c2, a.warmup, max(a.steps, 50),
+                                                               True)
         del c2
     if "c4" in only:
         log("timing block-sparse B64 ...")
@@ -424,6 +450,8 @@ def main(argv=None):
         also["long_decode_B64_k2048"] = bench_fused(torch, ops, timer, c5, a.warmup, a.steps, False)
         also["long_decode_B64_k2048"]["chunk_kernel_traffic"] = counter_traffic("fused_long_decode_B64_k2048",
                                                                                 "fused")
+        log("timing long decode B64, unfused path ...")
+        also["long_decode_B64_k2048_unfused"] = bench_unfused(torch, ops, timer, c5, a.warmup, a.steps, False)
         del c5
     if line is None:
         line = {"metric": METRIC, "value": None, "unit": "rows/s", "n_gpus": 1, "steps": a.steps,

@@ -34,6 +34,7 @@
 // The score row never exists in HBM on this path. Batches of at most
 // FS_MAX_TOKENS tokens take a variant whose chunks write their scores to the
 // workspace instead (see "Fused decode, small batches" below).
+#include "../../include/idxtopk.h"
 #include "common.hpp"
 #include "launch.hpp"
 #include "score_mfma.hpp"
@@ -628,40 +629,17 @@ __device__ __forceinline__ void fused_scores_merge_row(const IndexerArgs& a, con
   const uint32_t bstar = th.all ? 0u : th.bin;
   const uint32_t need = th.all ? 0u : k - th.above;
 
-  // Slots of M positions: every page lookup is issued before any is used.
-  // slot = (page - pg) * P + pos, with the multiply and the add kept apart
-  // by an empty asm (fused, they become a 64-bit mad whose unused high
-  // addend half can alias a register with a load in flight, and the wait for
-  // it drains every load); the asm also fixes each slot before the branches
-  // that store it.
-  auto slots_of = [&](const uint32_t* pos, int32_t* sl, int m) {
-    uint32_t pg[FS_PER];
-    int32_t page[FS_PER];
-    for (int e = 0; e < m; ++e) {
-      pg[e] = fdiv(pos[e], a.pdiv);
-      page[e] = STAGED ? s.pages[pg[e]] : bt_row[pg[e]];
-    }
-    for (int e = 0; e < m; ++e) {
-      uint32_t x = (static_cast<uint32_t>(page[e]) - pg[e]) * P;
-      asm volatile("" : "+v"(x));
-      sl[e] = static_cast<int32_t>(x + pos[e]);
-    }
-  };
-  // Emit the keys with keep[e] set: one reservation per wave, then slots.
-  // Every slot is looked up before any is stored, outside the branches, so
-  // the lookups overlap.
+  // Selected tokens are first written to the output row as positions (and
+  // scores); one coalesced pass at the end turns positions into slots, so
+  // no block-table lookup sits on the selection passes.
   auto emit = [&](const uint64_t* key, const bool* keep, int m) {
     uint32_t mine = 0;
     for (int e = 0; e < m; ++e) mine += keep[e];
     uint32_t at = wave_reserve(mine, &s.ocnt);
-    uint32_t pos[FS_MAXE];
-    int32_t sl[FS_MAXE];
-    for (int e = 0; e < m; ++e) pos[e] = keep[e] ? rank_pos(key[e]) : 0u;
-    slots_of(pos, sl, m);
     for (int e = 0; e < m; ++e) {
       if (keep[e]) {
         if (at < k) {
-          o.slots[orow + at] = sl[e];
+          o.slots[orow + at] = static_cast<int32_t>(rank_pos(key[e]));
           if (o.scores) o.scores[orow + at] = key_float(rank_vkey(key[e]));
         }
         ++at;
@@ -681,19 +659,11 @@ __device__ __forceinline__ void fused_scores_merge_row(const IndexerArgs& a, con
       midm |= static_cast<uint32_t>(valid && !th.all && bin == bstar) << e;
     }
     uint32_t at = wave_reserve(__builtin_popcount(keepm), &s.ocnt);
-    uint32_t pos[FS_PER];
-    int32_t sl[FS_PER];
-#pragma unroll
-    for (int e = 0; e < FS_PER; ++e) {
-      const int i = base + e * FS_WG + tid;
-      pos[e] = static_cast<uint32_t>(i < n ? i : 0);
-    }
-    slots_of(pos, sl, FS_PER);
 #pragma unroll
     for (int e = 0; e < FS_PER; ++e) {
       if ((keepm >> e) & 1u) {
         if (at < k) {
-          o.slots[orow + at] = sl[e];
+          o.slots[orow + at] = base + e * FS_WG + tid;
           if (o.scores) o.scores[orow + at] = v[e];
         }
         ++at;
@@ -786,8 +756,37 @@ __device__ __forceinline__ void fused_scores_merge_row(const IndexerArgs& a, con
     }
   }
   __syncthreads();
+  const uint32_t nout = min(s.ocnt, k);
+  // positions -> slots (this workgroup wrote them; the barrier orders it).
+  // Each thread reads all its positions, issues every page lookup, then
+  // forms and stores the slots. slot = (page - pg) * P + pos, with the
+  // multiply and the add kept apart by an empty asm: fused, they become a
+  // 64-bit mad whose unused high addend half can alias a register with a
+  // load in flight, and the wait for it would drain every load.
+  static_assert(IDXTOPK_MAX_K_FUSED <= FS_PER * FS_WG, "output entries per thread");
+  {
+    uint32_t pos[FS_PER], pg[FS_PER];
+    int32_t page[FS_PER];
+#pragma unroll
+    for (int e = 0; e < FS_PER; ++e) {
+      const uint32_t i = e * FS_WG + tid;
+      pos[e] = i < nout ? static_cast<uint32_t>(o.slots[orow + i]) : 0u;
+    }
+#pragma unroll
+    for (int e = 0; e < FS_PER; ++e) {
+      pg[e] = fdiv(pos[e], a.pdiv);
+      page[e] = e * FS_WG + tid < static_cast<int>(nout) ? (STAGED ? s.pages[pg[e]] : bt_row[pg[e]]) : 0;
+    }
+#pragma unroll
+    for (int e = 0; e < FS_PER; ++e) {
+      uint32_t x = (static_cast<uint32_t>(page[e]) - pg[e]) * P;
+      asm volatile("" : "+v"(x));
+      const uint32_t i = e * FS_WG + tid;
+      if (i < nout) o.slots[orow + i] = static_cast<int32_t>(x + pos[e]);
+    }
+  }
   // padding for rows shorter than k
-  for (uint32_t i = min(s.ocnt, k) + tid; i < k; i += FS_WG) {
+  for (uint32_t i = nout + tid; i < k; i += FS_WG) {
     o.slots[orow + i] = -1;
     if (o.scores) o.scores[orow + i] = -__builtin_inff();
   }

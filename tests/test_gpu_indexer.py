@@ -199,6 +199,24 @@ def test_fused_all_scores_tied(ops):
             assert np.array_equal(np.sort(slots[b]), np.sort(ref_slots[b])), (c.max_seq_len, b)
 
 
+@pytest.mark.parametrize("page_size,k,n_lo,n_hi,batch", [(64, 2048, 1, 20000, 6), (16, 300, 100, 9000, 5),
+                                                         (1, 64, 1, 3000, 4)])
+def test_fused_equals_unfused(ops, page_size, k, n_lo, n_hi, batch):
+    """idx_score_fp8 then topk_rows through the block table (the unfused
+    path) computes the same fp32 score per token as the fused kernels, so
+    both fused variants select exactly its set, ties included."""
+    import torch
+
+    case = workloads.indexer_case(800 + k, batch=batch, n_lo=n_lo, n_hi=n_hi, page_size=page_size, k=k)
+    scores = ops.idx_score_fp8(*_inputs(case), case.page_size, case.max_seq_len)
+    ref = ops.topk_rows(scores, dev(case.seq_lens), k, page_table=dev(case.block_table), page_size=page_size)
+    torch.cuda.synchronize()
+    ref = np.sort(ref.cpu().numpy(), axis=1)
+    for c in (case, _candidate_variant(case)):
+        slots, _ = _fused(ops, c)
+        assert np.array_equal(np.sort(slots, axis=1), ref), c.max_seq_len
+
+
 def test_fused_never_reads_outside_windows(ops):
     """Sentinel keys (+448, scale 1e3) fill every slot no row owns; selecting
     one of them would map to no token of the row and fail the inverse map."""
