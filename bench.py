@@ -13,7 +13,8 @@ roofline figure:
   * decode top-k:    8 rows of [8, 4096], k 512;
   * fused decode:    B 32, n ~ U[8192, 16384], k 2048;
   * block-sparse:    B 64, n 32768, top 32 blocks of 128;
-  * long decode:     B 64, n ~ U[131072, 327680], k 2048.
+  * long decode:     B 64, n ~ U[131072, 327680], k 2048;
+  * multi-token decode: 16 requests x 4 query rows, n ~ U[16384, 65536], k 2048.
 It also carries the CPU oracle's throughput on a bounded sample of the
 headline workload, run on the host's cores.
 
@@ -143,7 +144,16 @@ def rows_algorithmic_bytes(case) -> int:
 
 
 def indexer_algorithmic_bytes(case, out_entries: int) -> int:
+    """Keys (128 B + 4 B scale per token), block-table entries, queries, head
+    weights and scales, outputs. Query rows that share a block-table row
+    (row_to_batch) read nested windows of the same keys: those count once per
+    block-table row, at the longest window."""
     n = case.seq_lens.astype(np.int64)
+    r2b = getattr(case, "row_to_batch", None)
+    if r2b is not None:
+        longest = np.zeros(case.block_table.shape[0], np.int64)
+        np.maximum.at(longest, np.asarray(r2b, np.int64), n)
+        n = longest
     P = case.page_size
     keys = int((n * (case.dim + 4)).sum())
     table = int((4 * ((n + P - 1) // P)).sum())
@@ -299,6 +309,28 @@ def bench_fused(torch, ops, timer, case, warmup, steps, flush):
     return res
 
 
+def bench_fused_mq(torch, ops, timer, case, warmup, steps, flush):
+    """Fused path on multi-token decode rows (row_to_batch shares block-table
+    rows between a request's query tokens)."""
+    args = [dev(torch, x) for x in (case.q, case.q_scale, case.w, case.kcache, case.k_scale,
+                                    case.block_table, case.seq_lens)]
+    r2b = dev(torch, case.row_to_batch)
+    out = torch.empty((case.batch, case.k), dtype=torch.int32, device="cuda")
+    ws = ops.Workspace()
+
+    def step():
+        ops.idx_score_topk_fused(*args, case.page_size, case.max_seq_len, case.k, workspace=ws, out=out,
+                                 row_to_batch=r2b)
+
+    wall, us, region = timer.run(step, warmup, steps, flush)
+    res = summary(us, indexer_algorithmic_bytes(case, case.batch * case.k), case.batch, region, timer.settled)
+    res["rows"] = case.batch
+    res["row_tokens"] = int(case.seq_lens.astype(np.int64).sum())
+    del args
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_unfused(torch, ops, timer, case, warmup, steps, flush):
     """The unfused path on the same inputs: idx_score_fp8 writes the score
     rows, then topk_rows selects and maps through the block table (the pages'
@@ -344,7 +376,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="all", help="comma list of c1..c5, or all")
+    ap.add_argument("--only", default="all", help="comma list of c1..c5, mtp, or all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for PMC byte-counter calibration)")
@@ -360,7 +392,7 @@ def main(argv=None):
         print("bench.py measures one GPU only: the indexer top-k path here runs on a single MI355X "
               "(no sharding, no collectives); run with --gpus 1", file=sys.stderr)
         return 2
-    only = {"c1", "c2", "c3", "c4", "c5"} if a.only == "all" else set(a.only.split(","))
+    only = {"c1", "c2", "c3", "c4", "c5", "mtp"} if a.only == "all" else set(a.only.split(","))
 
     case3 = None
     cpu = None
@@ -437,6 +469,11 @@ def main(argv=None):
         also["fused_decode_B32_k2048_unfused"] = bench_unfused(torch, ops, timer, c2, a.warmup, max(a.steps, 50),
                                                                True)
         del c2
+    if "mtp" in only:
+        log("timing multi-token decode 16x4 ...")
+        mq = workloads.mtp_decode()
+        also["mtp_decode_16x4_k2048"] = bench_fused_mq(torch, ops, timer, mq, a.warmup, max(a.steps, 50), True)
+        del mq
     if "c4" in only:
         log("timing block-sparse B64 ...")
         c4 = workloads.c4_block_sparse()

@@ -79,11 +79,17 @@ extern "C" {
  *   w           float [batch, heads]: per-row, per-head weights.
  *   kcache      uint8 e4m3fn [num_slots, dim]: the paged index-key cache.
  *   k_scale     float [num_slots]: dequantisation scale of each cached key (> 0).
- *   block_table int32 [batch, bt_stride]: physical page of each logical page of
- *               a row. Token j of row b is at slot
- *               block_table[b, j / page_size] * page_size + j % page_size
+ *   block_table int32 [requests, bt_stride]: physical page of each logical
+ *               page of a request. Token j of row b is at slot
+ *               block_table[prow, j / page_size] * page_size + j % page_size
  *               ([ATOM-1473] decode-kernel diff: page = bt_row[blk], widened
  *               to int64 before use; positions blk * BLOCK_SIZE_K + offset).
+ *   row_to_batch optional int32 [batch]: prow = row_to_batch[b], the
+ *               block-table row of query row b; NULL gives prow = b. Several
+ *               rows may share one block-table row: multi-token decode puts
+ *               each of a request's query tokens in its own row, with its own
+ *               causal length in seq_lens. Same indirection as topk_rows
+ *               ([SGL-37889] Modifications); the caller owns its bound.
  *   seq_lens    int32 [batch]: n_b, the number of visible keys of row b (the
  *               causal length of the decode kernel's mask in [ATOM-1473]).
  *   max_seq_len an upper bound on every seq_lens[b], used to size the grid.
@@ -111,8 +117,9 @@ extern "C" {
 int idx_score_fp8(const uint8_t* q, const float* q_scale, const float* w,
                   const uint8_t* kcache, const float* k_scale,
                   const int32_t* block_table, int64_t bt_stride, int32_t page_size,
-                  const int32_t* seq_lens, int32_t batch, int32_t heads, int32_t dim,
-                  int32_t max_seq_len, float* scores, int64_t score_stride, void* stream);
+                  const int32_t* row_to_batch, const int32_t* seq_lens, int32_t batch,
+                  int32_t heads, int32_t dim, int32_t max_seq_len, float* scores,
+                  int64_t score_stride, void* stream);
 
 /*
  * topk_rows -- top-k over a given fp32 score buffer, with page transform.
@@ -173,9 +180,10 @@ int topk_page_transform(const int32_t* idx, int32_t rows, int32_t k,
 int idx_score_topk_fused(const uint8_t* q, const float* q_scale, const float* w,
                          const uint8_t* kcache, const float* k_scale,
                          const int32_t* block_table, int64_t bt_stride, int32_t page_size,
-                         const int32_t* seq_lens, int32_t batch, int32_t heads, int32_t dim,
-                         int32_t max_seq_len, int32_t k, int32_t* out_slots, float* out_scores,
-                         void* workspace, size_t workspace_bytes, void* stream);
+                         const int32_t* row_to_batch, const int32_t* seq_lens, int32_t batch,
+                         int32_t heads, int32_t dim, int32_t max_seq_len, int32_t k,
+                         int32_t* out_slots, float* out_scores, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /*
  * block_topk -- block-sparse variant: block scores, top blocks, sparse list.
@@ -201,8 +209,9 @@ int idx_score_topk_fused(const uint8_t* q, const float* q_scale, const float* w,
 int block_topk(const uint8_t* q, const float* q_scale, const float* w,
                const uint8_t* kcache, const float* k_scale,
                const int32_t* block_table, int64_t bt_stride, int32_t page_size,
-               const int32_t* seq_lens, int32_t batch, int32_t heads, int32_t dim,
-               int32_t max_seq_len, int32_t block_size, int32_t top_blocks,
+               const int32_t* row_to_batch, const int32_t* seq_lens, int32_t batch,
+               int32_t heads, int32_t dim, int32_t max_seq_len, int32_t block_size,
+               int32_t top_blocks,
                int32_t* out_blocks, int32_t* out_slots,
                void* workspace, size_t workspace_bytes, void* stream);
 

@@ -153,10 +153,19 @@ def index_scores(q_b, q_scale_b, w_b, kcache, k_scale, bt_row, page_size: int, n
     return (np.maximum(logits, 0.0) * _f64(w_b)[None, :]).sum(axis=1)
 
 
+def case_bt_row(case, b: int) -> np.ndarray:
+    """Block-table row of query row b: ``row_to_batch[b]`` if the case has one,
+    else b. Several query rows may share a block-table row (multi-token
+    decode: one row per query token of a request, each with its own causal
+    length in ``seq_lens``). Same addressing rule as ``page_row`` ([SGL-37889],
+    Modifications)."""
+    return case.block_table[page_row(b, getattr(case, "row_to_batch", None))]
+
+
 def case_scores(case, b: int) -> np.ndarray:
     """``index_scores`` of row b of a workloads.IndexerCase."""
     return index_scores(case.q[b], case.q_scale[b], case.w[b], case.kcache, case.k_scale,
-                        case.block_table[b], case.page_size, int(case.seq_lens[b]))
+                        case_bt_row(case, b), case.page_size, int(case.seq_lens[b]))
 
 
 def fused_topk(case, rows=None, k=None):
@@ -175,7 +184,7 @@ def fused_topk(case, rows=None, k=None):
         S = case_scores(case, b)
         pos = topk_order(S, k)
         positions.append(pos)
-        slots.append(page_transform(pos, case.block_table[b], case.page_size))
+        slots.append(page_transform(pos, case_bt_row(case, b), case.page_size))
         scores.append(S)
     return np.stack(slots), np.stack(positions), scores
 
@@ -223,13 +232,14 @@ def block_topk(case, rows=None, block_size=None, top_blocks=None):
         S = case_scores(case, b)
         bsv = block_scores(S, bs) if n > 0 else np.zeros(0)
         sel = topk_order(bsv, top)
-        tok_slots = token_slots(case.block_table[b], case.page_size, n)
+        bt_row = case_bt_row(case, b)
+        tok_slots = token_slots(bt_row, case.page_size, n)
         phys = np.full(top, -1, np.int64)
         sl = np.full(top * bs, -1, np.int64)
         for i, c in enumerate(sel):
             if c < 0:
                 continue
-            phys[i] = int(case.block_table[b][c * bs // case.page_size])
+            phys[i] = int(bt_row[c * bs // case.page_size])
             lo, hi = c * bs, min((c + 1) * bs, n)
             sl[i * bs:i * bs + (hi - lo)] = tok_slots[lo:hi]
         blocks.append(phys)

@@ -31,14 +31,14 @@ _sz = ctypes.c_size_t
 
 # name -> (restype, argtypes), in the order of include/idxtopk.h
 SIGNATURES = {
-    "idx_score_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _i32, _i32, _i32, _i32,
-                             _vp, _i64, _vp]),
+    "idx_score_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32, _i32,
+                             _i32, _vp, _i64, _vp]),
     "topk_rows": (_i32, [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp]),
     "topk_page_transform": (_i32, [_vp, _i32, _i32, _vp, _i64, _i32, _vp, _vp, _vp]),
-    "idx_score_topk_fused": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _i32, _i32, _i32,
-                                    _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
-    "block_topk": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
-                          _i32, _vp, _vp, _vp, _sz, _vp]),
+    "idx_score_topk_fused": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32,
+                                    _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "block_topk": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
+                          _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "idxtopk_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "idxtopk_status_str": (ctypes.c_char_p, [_i32]),
     "idxtopk_version": (_i32, []),

@@ -27,8 +27,8 @@ int check_indexer(const uint8_t* q, const float* q_scale, const float* w, const 
 
 IndexerInputs pack(const uint8_t* q, const float* q_scale, const float* w, const uint8_t* kcache,
                    const float* k_scale, const int32_t* block_table, int64_t bt_stride,
-                   int32_t page_size, const int32_t* seq_lens, int32_t batch, int32_t heads,
-                   int32_t max_seq_len) {
+                   int32_t page_size, const int32_t* row_to_batch, const int32_t* seq_lens,
+                   int32_t batch, int32_t heads, int32_t max_seq_len) {
   IndexerInputs in;
   in.q = q;
   in.q_scale = q_scale;
@@ -38,6 +38,7 @@ IndexerInputs pack(const uint8_t* q, const float* q_scale, const float* w, const
   in.block_table = block_table;
   in.bt_stride = bt_stride;
   in.page_size = page_size;
+  in.row_to_batch = row_to_batch;
   in.seq_lens = seq_lens;
   in.batch = batch;
   in.heads = heads;
@@ -52,7 +53,8 @@ extern "C" {
 
 int idx_score_fp8(const uint8_t* q, const float* q_scale, const float* w, const uint8_t* kcache,
                   const float* k_scale, const int32_t* block_table, int64_t bt_stride,
-                  int32_t page_size, const int32_t* seq_lens, int32_t batch, int32_t heads,
+                  int32_t page_size, const int32_t* row_to_batch, const int32_t* seq_lens,
+                  int32_t batch, int32_t heads,
                   int32_t dim, int32_t max_seq_len, float* scores, int64_t score_stride,
                   void* stream) {
   const int st = check_indexer(q, q_scale, w, kcache, k_scale, block_table, bt_stride, page_size,
@@ -62,8 +64,8 @@ int idx_score_fp8(const uint8_t* q, const float* q_scale, const float* w, const 
   if (static_cast<int64_t>(max_seq_len) > score_stride) return IDXTOPK_EINVAL;
   if (batch == 0 || max_seq_len == 0) return IDXTOPK_OK;
   return idxtopk::launch_idx_score(
-      pack(q, q_scale, w, kcache, k_scale, block_table, bt_stride, page_size, seq_lens, batch,
-           heads, max_seq_len),
+      pack(q, q_scale, w, kcache, k_scale, block_table, bt_stride, page_size, row_to_batch, seq_lens,
+           batch, heads, max_seq_len),
       scores, score_stride, static_cast<hipStream_t>(stream));
 }
 
@@ -92,8 +94,8 @@ int topk_page_transform(const int32_t* idx, int32_t rows, int32_t k, const int32
 
 int idx_score_topk_fused(const uint8_t* q, const float* q_scale, const float* w,
                          const uint8_t* kcache, const float* k_scale, const int32_t* block_table,
-                         int64_t bt_stride, int32_t page_size, const int32_t* seq_lens,
-                         int32_t batch, int32_t heads, int32_t dim, int32_t max_seq_len, int32_t k,
+                         int64_t bt_stride, int32_t page_size, const int32_t* row_to_batch,
+                         const int32_t* seq_lens, int32_t batch, int32_t heads, int32_t dim, int32_t max_seq_len, int32_t k,
                          int32_t* out_slots, float* out_scores, void* workspace,
                          size_t workspace_bytes, void* stream) {
   const int st = check_indexer(q, q_scale, w, kcache, k_scale, block_table, bt_stride, page_size,
@@ -105,14 +107,15 @@ int idx_score_topk_fused(const uint8_t* q, const float* q_scale, const float* w,
   if (!workspace || workspace_bytes < idxtopk::fused_workspace_bytes(batch, k, max_seq_len))
     return IDXTOPK_EWORKSPACE;
   return idxtopk::launch_fused(pack(q, q_scale, w, kcache, k_scale, block_table, bt_stride,
-                                    page_size, seq_lens, batch, heads, max_seq_len),
+                                    page_size, row_to_batch, seq_lens, batch, heads, max_seq_len),
                                k, out_slots, out_scores, workspace,
                                static_cast<hipStream_t>(stream));
 }
 
 int block_topk(const uint8_t* q, const float* q_scale, const float* w, const uint8_t* kcache,
                const float* k_scale, const int32_t* block_table, int64_t bt_stride,
-               int32_t page_size, const int32_t* seq_lens, int32_t batch, int32_t heads,
+               int32_t page_size, const int32_t* row_to_batch, const int32_t* seq_lens,
+               int32_t batch, int32_t heads,
                int32_t dim, int32_t max_seq_len, int32_t block_size, int32_t top_blocks,
                int32_t* out_blocks, int32_t* out_slots, void* workspace, size_t workspace_bytes,
                void* stream) {
@@ -128,7 +131,8 @@ int block_topk(const uint8_t* q, const float* q_scale, const float* w, const uin
       workspace_bytes < idxtopk::block_workspace_bytes(batch, block_size, max_seq_len))
     return IDXTOPK_EWORKSPACE;
   return idxtopk::launch_block_topk(pack(q, q_scale, w, kcache, k_scale, block_table, bt_stride,
-                                         page_size, seq_lens, batch, heads, max_seq_len),
+                                         page_size, row_to_batch, seq_lens, batch, heads,
+                                         max_seq_len),
                                     block_size, top_blocks, out_blocks, out_slots, workspace,
                                     static_cast<hipStream_t>(stream));
 }

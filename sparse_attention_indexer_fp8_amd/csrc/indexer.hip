@@ -132,14 +132,6 @@ __device__ __forceinline__ void chunk_span(const IndexerArgs& a, int c, int& tb,
   }
 }
 
-__device__ __forceinline__ int32_t token_slot(const IndexerArgs& a, int b, uint32_t pos) {
-  const uint32_t P = static_cast<uint32_t>(a.page_size);
-  const uint32_t pg = fdiv(pos, a.pdiv);
-  const uint32_t off = pos - pg * P;
-  const int32_t page = a.block_table[static_cast<int64_t>(b) * a.bt_stride + pg];
-  return static_cast<int32_t>(static_cast<int64_t>(page) * P + off);
-}
-
 // ---------------------------------------------------------------------------
 // Unfused scores
 // ---------------------------------------------------------------------------
@@ -335,30 +327,64 @@ struct MergeLds {
   uint32_t bcnt;
 };
 
-// Emit this thread's keys with keep[e] set: one slot reservation per wave,
-// then independent block-table gathers and stores. All lanes of the wave must
-// call.
+// Emit this thread's keys with keep[e] set: one output reservation per
+// wave, then each key's row-local position (and score) is stored. The merge
+// turns positions into slots in one pass at the end (positions_to_slots).
+// All lanes of the wave must call.
 template <int N>
-__device__ __forceinline__ void emit_batch(const uint64_t (&keys)[N], const bool (&keep)[N],
-                                           const IndexerArgs& a, int b, const FusedOut& o,
-                                           uint32_t* ocnt) {
+__device__ __forceinline__ void emit_batch(const uint64_t (&keys)[N], const bool (&keep)[N], int b,
+                                           const FusedOut& o, uint32_t* ocnt) {
   uint32_t mine = 0;
 #pragma unroll
   for (int e = 0; e < N; ++e) mine += keep[e];
   uint32_t at = wave_reserve(mine, ocnt);
-  int32_t sl[N];
-#pragma unroll
-  for (int e = 0; e < N; ++e)
-    if (keep[e]) sl[e] = token_slot(a, b, rank_pos(keys[e]));
   const int64_t row = static_cast<int64_t>(b) * o.k;
 #pragma unroll
   for (int e = 0; e < N; ++e) {
     if (keep[e]) {
       if (at < static_cast<uint32_t>(o.k)) {
-        o.slots[row + at] = sl[e];
+        o.slots[row + at] = static_cast<int32_t>(rank_pos(keys[e]));
         if (o.scores) o.scores[row + at] = key_float(rank_vkey(keys[e]));
       }
       ++at;
+    }
+  }
+}
+
+// Row b's first nout output entries hold row-local positions written by this
+// workgroup (a barrier must separate the writes from this call): map them to
+// slots through the block table (page_of(logical page) gives the physical
+// page). Each thread reads PER positions, issues all their block-table
+// lookups, then forms and stores the slots. slot =
+// (page - pg) * P + pos, with the multiply and the add kept apart by an empty
+// asm: fused, they become a 64-bit mad whose unused high addend half can
+// alias a register with a load in flight, and the wait for it would drain
+// every load.
+template <int WG, int PER, class PageOf>
+__device__ __forceinline__ void positions_to_slots(const IndexerArgs& a, int b, const FusedOut& o, uint32_t nout,
+                                                   PageOf&& page_of) {
+  const int tid = threadIdx.x;
+  const uint32_t P = static_cast<uint32_t>(a.page_size);
+  const int64_t row = static_cast<int64_t>(b) * o.k;
+  for (uint32_t i0 = 0; i0 < nout; i0 += PER * WG) {
+    uint32_t pos[PER], pg[PER];
+    int32_t page[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const uint32_t i = i0 + e * WG + tid;
+      pos[e] = i < nout ? static_cast<uint32_t>(o.slots[row + i]) : 0u;
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      pg[e] = fdiv(pos[e], a.pdiv);
+      page[e] = page_of(pg[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      uint32_t x = (static_cast<uint32_t>(page[e]) - pg[e]) * P;
+      asm volatile("" : "+v"(x));
+      const uint32_t i = i0 + e * WG + tid;
+      if (i < nout) o.slots[row + i] = static_cast<int32_t>(x + pos[e]);
     }
   }
 }
@@ -404,7 +430,7 @@ __global__ __launch_bounds__(MG_WG) void fused_merge_kernel(IndexerArgs a, Fused
       mid[j] = valid && !th.all && bin == bstar;
       nmid += mid[j];
     }
-    emit_batch<MG_BATCH>(key, keep, a, b, o, &s.ocnt);
+    emit_batch<MG_BATCH>(key, keep, b, o, &s.ocnt);
     uint32_t at = wave_reserve(nmid, &s.bcnt);
 #pragma unroll
     for (int j = 0; j < MG_BATCH; ++j) {
@@ -450,7 +476,7 @@ __global__ __launch_bounds__(MG_WG) void fused_merge_kernel(IndexerArgs a, Fused
       bool keep[MG_MAXE];
 #pragma unroll
       for (int e = 0; e < MG_MAXE; ++e) keep[e] = e < nvk && keys[e] >= T;
-      emit_batch<MG_MAXE>(keys, keep, a, b, o, &s.ocnt);
+      emit_batch<MG_MAXE>(keys, keep, b, o, &s.ocnt);
     } else {
       // threshold bin larger than the LDS buffer: select straight from the
       // candidate list (several passes over it)
@@ -476,11 +502,15 @@ __global__ __launch_bounds__(MG_WG) void fused_merge_kernel(IndexerArgs a, Fused
           key[j] = i < ncand ? cand[i] : 0ull;
           keep[j] = i < ncand && (rank_vkey(key[j]) >> HIST_SHIFT) == bstar && key[j] >= T;
         }
-        emit_batch<MG_BATCH>(key, keep, a, b, o, &s.ocnt);
+        emit_batch<MG_BATCH>(key, keep, b, o, &s.ocnt);
       }
     }
   }
   __syncthreads();
+  {
+    const int32_t* bt_row = bt_row_of(a, b);
+    positions_to_slots<MG_WG, 8>(a, b, o, min(s.ocnt, k), [&](uint32_t pg) { return bt_row[pg]; });
+  }
   // padding for rows shorter than k
   for (uint32_t i = min(s.ocnt, k) + tid; i < k; i += MG_WG) {
     o.slots[static_cast<int64_t>(b) * o.k + i] = -1;
@@ -598,7 +628,7 @@ __device__ __forceinline__ void fused_scores_merge_row(const IndexerArgs& a, con
   const uint32_t P = static_cast<uint32_t>(a.page_size);
   uint32_t* Hg = ws.hist + static_cast<int64_t>(b) * HIST_BINS;
   float* srow = fused_scores_row(ws, b);
-  const int32_t* bt_row = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
+  const int32_t* bt_row = bt_row_of(a, b);
   const int64_t orow = static_cast<int64_t>(b) * o.k;
 
   wg_select_init<FS_WG>(s.sel);
@@ -757,34 +787,10 @@ __device__ __forceinline__ void fused_scores_merge_row(const IndexerArgs& a, con
   }
   __syncthreads();
   const uint32_t nout = min(s.ocnt, k);
-  // positions -> slots (this workgroup wrote them; the barrier orders it).
-  // Each thread reads all its positions, issues every page lookup, then
-  // forms and stores the slots. slot = (page - pg) * P + pos, with the
-  // multiply and the add kept apart by an empty asm: fused, they become a
-  // 64-bit mad whose unused high addend half can alias a register with a
-  // load in flight, and the wait for it would drain every load.
-  static_assert(IDXTOPK_MAX_K_FUSED <= FS_PER * FS_WG, "output entries per thread");
-  {
-    uint32_t pos[FS_PER], pg[FS_PER];
-    int32_t page[FS_PER];
-#pragma unroll
-    for (int e = 0; e < FS_PER; ++e) {
-      const uint32_t i = e * FS_WG + tid;
-      pos[e] = i < nout ? static_cast<uint32_t>(o.slots[orow + i]) : 0u;
-    }
-#pragma unroll
-    for (int e = 0; e < FS_PER; ++e) {
-      pg[e] = fdiv(pos[e], a.pdiv);
-      page[e] = e * FS_WG + tid < static_cast<int>(nout) ? (STAGED ? s.pages[pg[e]] : bt_row[pg[e]]) : 0;
-    }
-#pragma unroll
-    for (int e = 0; e < FS_PER; ++e) {
-      uint32_t x = (static_cast<uint32_t>(page[e]) - pg[e]) * P;
-      asm volatile("" : "+v"(x));
-      const uint32_t i = e * FS_WG + tid;
-      if (i < nout) o.slots[orow + i] = static_cast<int32_t>(x + pos[e]);
-    }
-  }
+  // positions -> slots (this workgroup wrote them; the barrier orders it)
+  positions_to_slots<FS_WG, FS_PER>(a, b, o, nout, [&](uint32_t pg) {
+    return STAGED ? s.pages[pg] : bt_row[pg];
+  });
   // padding for rows shorter than k
   for (uint32_t i = nout + tid; i < k; i += FS_WG) {
     o.slots[orow + i] = -1;
@@ -902,7 +908,7 @@ __global__ __launch_bounds__(MG_WG) void block_merge_kernel(IndexerArgs a, Block
   }
   __syncthreads();
   const int nsel = min(static_cast<int>(s.ocnt), top);
-  const int32_t* bt_row = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
+  const int32_t* bt_row = bt_row_of(a, b);
   for (int i = tid; i < top; i += MG_WG)
     o.blocks[static_cast<int64_t>(b) * top + i] = i < nsel ? bt_row[s.sel_blocks[i]] : -1;
   if (o.slots) {
@@ -935,6 +941,7 @@ static IndexerArgs make_args(const IndexerInputs& in, int chunk, bool guided = f
   a.kcache = in.kcache;
   a.k_scale = in.k_scale;
   a.block_table = in.block_table;
+  a.row_to_batch = in.row_to_batch;
   a.bt_stride = in.bt_stride;
   a.page_size = in.page_size;
   a.pdiv = make_fastdiv(static_cast<uint32_t>(in.page_size));

@@ -41,6 +41,7 @@ struct IndexerInputs {
   const int32_t* block_table;
   int64_t bt_stride;
   int32_t page_size;
+  const int32_t* row_to_batch;  // block-table row of each query row, or null (row b -> b)
   const int32_t* seq_lens;
   int32_t batch;
   int32_t heads;

@@ -41,6 +41,7 @@ struct IndexerArgs {
   int64_t bt_stride;
   int32_t page_size;
   FastDiv pdiv;
+  const int32_t* row_to_batch;  // block-table row of each query row, or null (row b -> b)
   const int32_t* seq_lens;
   int32_t batch;
   int32_t heads;
@@ -59,6 +60,12 @@ struct IndexerArgs {
 struct KeyPieces {
   v4i x0, x1;
 };
+
+// Block-table row of query row b (several query rows may share one).
+__device__ __forceinline__ const int32_t* bt_row_of(const IndexerArgs& a, int b) {
+  const int prow = a.row_to_batch ? load_uniform(a.row_to_batch + b) : b;
+  return a.block_table + static_cast<int64_t>(prow) * a.bt_stride;
+}
 
 template <int NT>
 struct QOperand {
@@ -183,7 +190,7 @@ __device__ __forceinline__ void score_chunk_impl(const IndexerArgs& a, int b, in
 
   const uint32_t p0 = fdiv(static_cast<uint32_t>(tok_begin), a.pdiv);
   const uint32_t p1 = fdiv(static_cast<uint32_t>(tok_end - 1), a.pdiv);
-  const int32_t* bt_row = a.block_table + static_cast<int64_t>(b) * a.bt_stride;
+  const int32_t* bt_row = bt_row_of(a, b);
   for (int i = tid; i <= static_cast<int>(p1 - p0); i += WG) lds_pages[i] = bt_row[p0 + i];
 
   QOperand<NT> qo;

@@ -127,7 +127,7 @@ def topk_page_transform(idx: torch.Tensor, page_table: torch.Tensor, page_size: 
     return out
 
 
-def _indexer_args(q, q_scale, w, kcache, k_scale, block_table, seq_lens):
+def _indexer_args(q, q_scale, w, kcache, k_scale, block_table, seq_lens, row_to_batch=None):
     _need(q, "q", _F8, 3)
     _need(q_scale, "q_scale", (torch.float32,), 1)
     _need(w, "w", (torch.float32,), 2)
@@ -137,19 +137,24 @@ def _indexer_args(q, q_scale, w, kcache, k_scale, block_table, seq_lens):
     if block_table.stride(1) != 1:
         raise ValueError("block_table rows must be contiguous")
     _need(seq_lens, "seq_lens", (torch.int32,), 1)
+    if row_to_batch is not None:
+        _need(row_to_batch, "row_to_batch", (torch.int32,), 1)
     B, H, D = q.shape
     return [_ptr(_as_u8(q)), _ptr(q_scale), _ptr(w), _ptr(_as_u8(kcache)), _ptr(k_scale),
             _ptr(block_table), block_table.stride(0)], B, H, D
 
 
 def idx_score_fp8(q, q_scale, w, kcache, k_scale, block_table, seq_lens, page_size: int,
-                  max_seq_len: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Index scores S[b, j] for j < seq_lens[b] (other cells of `out` untouched)."""
-    args, B, H, D = _indexer_args(q, q_scale, w, kcache, k_scale, block_table, seq_lens)
+                  max_seq_len: int, out: Optional[torch.Tensor] = None,
+                  row_to_batch: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Index scores S[b, j] for j < seq_lens[b] (other cells of `out` untouched).
+    row_to_batch: block-table row of each query row (default: row b -> b)."""
+    args, B, H, D = _indexer_args(q, q_scale, w, kcache, k_scale, block_table, seq_lens, row_to_batch)
     if out is None:
         out = torch.full((B, max(1, max_seq_len)), float("nan"), dtype=torch.float32, device=q.device)
     _need(out, "out", (torch.float32,), 2, contiguous=False)
-    st = _lib.load().idx_score_fp8(*args, int(page_size), _ptr(seq_lens), B, H, D, int(max_seq_len),
+    st = _lib.load().idx_score_fp8(*args, int(page_size), _ptr(row_to_batch), _ptr(seq_lens), B, H, D,
+                                   int(max_seq_len),
                                    _ptr(out), out.stride(0), _stream())
     _lib.check("idx_score_fp8", st)
     return out
@@ -158,16 +163,17 @@ def idx_score_fp8(q, q_scale, w, kcache, k_scale, block_table, seq_lens, page_si
 def idx_score_topk_fused(q, q_scale, w, kcache, k_scale, block_table, seq_lens, page_size: int,
                          max_seq_len: int, k: int, return_scores: bool = False,
                          workspace: Optional[Workspace] = None, out: Optional[torch.Tensor] = None,
-                         out_scores: Optional[torch.Tensor] = None):
-    """Fused decode indexer: top-k slots per row (and their scores if asked)."""
-    args, B, H, D = _indexer_args(q, q_scale, w, kcache, k_scale, block_table, seq_lens)
+                         out_scores: Optional[torch.Tensor] = None, row_to_batch: Optional[torch.Tensor] = None):
+    """Fused decode indexer: top-k slots per row (and their scores if asked).
+    row_to_batch: block-table row of each query row (default: row b -> b)."""
+    args, B, H, D = _indexer_args(q, q_scale, w, kcache, k_scale, block_table, seq_lens, row_to_batch)
     if out is None:
         out = torch.empty((B, k), dtype=torch.int32, device=q.device)
     if return_scores and out_scores is None:
         out_scores = torch.empty((B, k), dtype=torch.float32, device=q.device)
     nbytes = workspace_bytes(_lib.OP_SCORE_TOPK_FUSED, B, k, max_seq_len)
     ws = _workspace(workspace).get(nbytes)
-    st = _lib.load().idx_score_topk_fused(*args, int(page_size), _ptr(seq_lens), B, H, D,
+    st = _lib.load().idx_score_topk_fused(*args, int(page_size), _ptr(row_to_batch), _ptr(seq_lens), B, H, D,
                                           int(max_seq_len), int(k), _ptr(out), _ptr(out_scores),
                                           _ptr(ws), ws.numel(), _stream())
     _lib.check("idx_score_topk_fused", st)
@@ -176,15 +182,17 @@ def idx_score_topk_fused(q, q_scale, w, kcache, k_scale, block_table, seq_lens, 
 
 def block_topk(q, q_scale, w, kcache, k_scale, block_table, seq_lens, page_size: int,
                max_seq_len: int, block_size: int, top_blocks: int, return_slots: bool = True,
-               workspace: Optional[Workspace] = None):
-    """Top blocks per row as physical block ids (and expanded slot lists)."""
-    args, B, H, D = _indexer_args(q, q_scale, w, kcache, k_scale, block_table, seq_lens)
+               workspace: Optional[Workspace] = None, row_to_batch: Optional[torch.Tensor] = None):
+    """Top blocks per row as physical block ids (and expanded slot lists).
+    row_to_batch: block-table row of each query row (default: row b -> b)."""
+    args, B, H, D = _indexer_args(q, q_scale, w, kcache, k_scale, block_table, seq_lens, row_to_batch)
     out_blocks = torch.empty((B, top_blocks), dtype=torch.int32, device=q.device)
     out_slots = (torch.empty((B, top_blocks * block_size), dtype=torch.int32, device=q.device)
                  if return_slots else None)
     nbytes = workspace_bytes(_lib.OP_BLOCK_TOPK, B, block_size, max_seq_len)
     ws = _workspace(workspace).get(nbytes)
-    st = _lib.load().block_topk(*args, int(page_size), _ptr(seq_lens), B, H, D, int(max_seq_len),
+    st = _lib.load().block_topk(*args, int(page_size), _ptr(row_to_batch), _ptr(seq_lens), B, H, D,
+                                int(max_seq_len),
                                 int(block_size), int(top_blocks), _ptr(out_blocks), _ptr(out_slots),
                                 _ptr(ws), ws.numel(), _stream())
     _lib.check("block_topk", st)

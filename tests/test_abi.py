@@ -96,11 +96,11 @@ def test_page_transform_validation(lib):
 
 
 def _indexer(**kw):
-    a = dict(q=FAKE, qs=FAKE, w=FAKE, kc=FAKE, ks=FAKE, bt=FAKE, bts=256, P=64, sl=FAKE, B=32, H=64, D=128,
-             msl=16384)
+    a = dict(q=FAKE, qs=FAKE, w=FAKE, kc=FAKE, ks=FAKE, bt=FAKE, bts=256, P=64, r2b=NULL, sl=FAKE, B=32, H=64,
+             D=128, msl=16384)
     a.update(kw)
-    return [a["q"], a["qs"], a["w"], a["kc"], a["ks"], a["bt"], a["bts"], a["P"], a["sl"], a["B"], a["H"],
-            a["D"], a["msl"]]
+    return [a["q"], a["qs"], a["w"], a["kc"], a["ks"], a["bt"], a["bts"], a["P"], a["r2b"], a["sl"], a["B"],
+            a["H"], a["D"], a["msl"]]
 
 
 def test_score_validation(lib):

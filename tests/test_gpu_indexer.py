@@ -24,11 +24,17 @@ def _inputs(case):
             dev(case.block_table), dev(case.seq_lens))
 
 
+def _r2b(case):
+    r2b = getattr(case, "row_to_batch", None)
+    return None if r2b is None else dev(r2b)
+
+
 def _fused(ops, case, k=None, ws=None):
     import torch
 
     slots, sc = ops.idx_score_topk_fused(*_inputs(case), case.page_size, case.max_seq_len,
-                                         case.k if k is None else k, return_scores=True, workspace=ws)
+                                         case.k if k is None else k, return_scores=True, workspace=ws,
+                                         row_to_batch=_r2b(case))
     torch.cuda.synchronize()
     return slots.cpu().numpy(), sc.cpu().numpy()
 
@@ -147,7 +153,7 @@ def _candidate_variant(case):
     big = copy.copy(case)
     big.max_seq_len = FUSED_SCORE_PATH_TOKENS // case.batch + 1
     cols = -(-big.max_seq_len // case.page_size)
-    bt = np.zeros((case.batch, cols), np.int32)
+    bt = np.zeros((case.block_table.shape[0], cols), np.int32)
     bt[:, :case.block_table.shape[1]] = case.block_table
     big.block_table = bt
     return big
@@ -327,3 +333,89 @@ def test_block_sparse_full_size(ops):
         for i, c in enumerate(sel):
             exp = int(case.block_table[b, c]) * bs + np.arange(bs)
             assert np.array_equal(slots[b, i * bs:(i + 1) * bs], exp)
+
+
+# ---------------------------------------------------------------------------
+# Multi-token decode rows: several query rows share a block-table row
+# ---------------------------------------------------------------------------
+
+
+def _expanded(case):
+    """The case with the indirection resolved: each query row gets its own
+    copy of its block-table row."""
+    import copy
+
+    flat = copy.copy(case)
+    flat.block_table = np.ascontiguousarray(case.block_table[case.row_to_batch])
+    flat.row_to_batch = None
+    return flat
+
+
+@pytest.mark.parametrize("page_size,k", [(64, 2048), (16, 300)])
+def test_multi_query_fused(ops, page_size, k):
+    """Each row's selection meets the oracle criterion, and equals the run
+    with the block-table rows copied out (same fp32 scores), for both fused
+    variants."""
+    case = workloads.multi_query_case(900 + page_size, requests=5, next_n=3, n_lo=1, n_hi=20000,
+                                      page_size=page_size, k=k)
+    log(f"multi-query fused: rows={case.batch} P={page_size} k={k}")
+    rows = [case_scores(case, b) for b in range(case.batch)]
+    bsig = rms(np.concatenate(rows))
+    flat = _expanded(case)
+    ref, _ = _fused(ops, flat)
+    for c in (case, _candidate_variant(case)):
+        slots, sc = _fused(ops, c)
+        assert np.array_equal(np.sort(slots, axis=1), np.sort(ref, axis=1)), c.max_seq_len
+    for b in range(case.batch):
+        n = int(case.seq_lens[b])
+        ts = oracle.token_slots(case.block_table[case.row_to_batch[b]], case.page_size, n)
+        check_fused_row(slots[b], sc[b], rows[b], ts, k, batch_sigma=bsig)
+
+
+def test_multi_query_scores(ops):
+    case = workloads.multi_query_case(911, requests=4, next_n=4, n_lo=1, n_hi=5000, page_size=32, k=0, heads=32)
+    out = ops.idx_score_fp8(*_inputs(case), case.page_size, case.max_seq_len, row_to_batch=_r2b(case))
+    flat = _expanded(case)
+    out2 = ops.idx_score_fp8(*_inputs(flat), flat.page_size, flat.max_seq_len)
+    import torch
+
+    torch.cuda.synchronize()
+    out, out2 = out.cpu().numpy(), out2.cpu().numpy()
+    for b in range(case.batch):
+        n = int(case.seq_lens[b])
+        assert np.array_equal(out[b, :n], out2[b, :n]), b
+        check_scores(out[b, :n], case_scores(case, b))
+
+
+def test_multi_query_block(ops):
+    bs = 64
+    case = workloads.multi_query_case(912, requests=4, next_n=3, n_lo=bs, n_hi=30000, page_size=bs, k=0)
+    flat = _expanded(case)
+    got = ops.block_topk(*_inputs(case), bs, case.max_seq_len, bs, 20, row_to_batch=_r2b(case))
+    exp = ops.block_topk(*_inputs(flat), bs, flat.max_seq_len, bs, 20)
+    import torch
+
+    torch.cuda.synchronize()
+    # output order within a row is unspecified: compare the block sets, and
+    # each block's slot list by block id
+    gb, gs = got[0].cpu().numpy(), got[1].cpu().numpy()
+    eb, es = exp[0].cpu().numpy(), exp[1].cpu().numpy()
+    assert np.array_equal(np.sort(gb, axis=1), np.sort(eb, axis=1))
+    for b in range(case.batch):
+        gmap = {int(x): tuple(gs[b, i * bs:(i + 1) * bs]) for i, x in enumerate(gb[b]) if x >= 0}
+        emap = {int(x): tuple(es[b, i * bs:(i + 1) * bs]) for i, x in enumerate(eb[b]) if x >= 0}
+        assert gmap == emap, b
+    blocks = gb
+    top = 20
+    for b in range(case.batch):
+        S = case_scores(case, b)
+        bsv = oracle.block_scores(S, bs)
+        nb = bsv.shape[0]
+        m = min(nb, top)
+        bt_row = case.block_table[case.row_to_batch[b]]
+        page_to_blk = {int(bt_row[c]): c for c in range(nb)}
+        sel = [page_to_blk[int(p)] for p in blocks[b, :m]]
+        assert len(set(sel)) == m and (blocks[b, m:] == -1).all()
+        sigma = float(np.sqrt(np.mean(S * S)))
+        kth = np.sort(bsv)[::-1][m - 1]
+        assert (bsv[sel] >= kth - 1e-3 * max(abs(kth), sigma)).all()

@@ -200,3 +200,52 @@ def test_block_short_row_padding():
     i1 = logical[1].tolist().index(1)
     sl = slot_lists[1][i1 * 128:(i1 + 1) * 128]
     assert (sl[:72] >= 0).all() and (sl[72:] == -1).all()
+
+
+def _expanded(case):
+    """The same case with the block-table indirection resolved: query row b
+    gets its own copy of block-table row row_to_batch[b]."""
+    import copy
+
+    flat = copy.copy(case)
+    flat.block_table = np.ascontiguousarray(case.block_table[case.row_to_batch])
+    flat.row_to_batch = None
+    return flat
+
+
+def test_multi_query_rows_share_the_request_cache():
+    """Multi-token decode rows: row r * next_n + t of request r sees the
+    request's first L_r - (next_n - 1 - t) tokens through the request's
+    block-table row. Resolving the indirection by copying block-table rows
+    gives identical scores and selections (the copy-versus-indirection check
+    of [SGL-37889], Modifications)."""
+    case = workloads.multi_query_case(31, requests=3, next_n=4, n_lo=1, n_hi=400, page_size=16, k=40, heads=16)
+    R, T = 3, 4
+    assert case.batch == R * T
+    assert np.array_equal(case.row_to_batch, np.repeat(np.arange(R), T))
+    base_lens = workloads.indexer_case(31, batch=R, n_lo=1, n_hi=400, page_size=16, k=40, heads=16).seq_lens
+    for r in range(R):
+        for t in range(T):
+            assert case.seq_lens[r * T + t] == max(int(base_lens[r]) - (T - 1 - t), 0)
+    flat = _expanded(case)
+    for b in range(case.batch):
+        assert np.array_equal(case_scores(case, b), case_scores(flat, b))
+    s1, p1, _ = fused_topk(case)
+    s2, p2, _ = fused_topk(flat)
+    assert np.array_equal(s1, s2) and np.array_equal(p1, p2)
+    # the last query token of a request sees the request's whole context, so
+    # its scores are index_scores over the request's own block-table row
+    for r in range(R):
+        b = r * T + T - 1
+        S = index_scores(case.q[b], case.q_scale[b], case.w[b], case.kcache, case.k_scale,
+                         case.block_table[r], case.page_size, int(base_lens[r]))
+        assert np.array_equal(case_scores(case, b), S)
+
+
+def test_multi_query_block_variant_matches_expanded():
+    case = workloads.multi_query_case(32, requests=2, next_n=3, n_lo=100, n_hi=700, page_size=16, k=0, heads=16)
+    flat = _expanded(case)
+    a = block_topk(case, block_size=16, top_blocks=5)
+    b = block_topk(flat, block_size=16, top_blocks=5)
+    for x, y in zip(a[:3], b[:3]):
+        assert np.array_equal(x, y)

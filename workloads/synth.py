@@ -38,6 +38,8 @@ STREAM_Q = 5
 STREAM_W = 6
 STREAM_KEY = 7
 STREAM_PAGE = 8
+STREAM_MQ = 9
+STREAM_MW = 10
 
 E4M3_MAX = 448.0
 # Values written into every cache slot and score cell that no row may read:
@@ -186,6 +188,7 @@ class IndexerCase:
     top_blocks: int = 0  # block-sparse variant: blocks kept per row
     max_seq_len: int = 0  # upper bound on seq_lens the caller promises
     meta: dict = field(default_factory=dict)
+    row_to_batch: Optional[np.ndarray] = None  # int32 [B]: block-table row of each query row
 
     @property
     def batch(self) -> int:
@@ -267,11 +270,39 @@ def indexer_case(seed: int, batch: int, n_lo: int, n_hi: int, page_size: int, k:
                        meta={"total_pages": total_pages, "sentinel_page": sentinel_page})
 
 
+def multi_query_case(seed: int, requests: int, next_n: int, n_lo: int, n_hi: int, page_size: int,
+                     k: int = 2048, heads: int = 64, dim: int = 128, name: str = "multi-query") -> IndexerCase:
+    """Multi-token decode rows: each of `requests` requests decodes `next_n`
+    query tokens at once. The cache and block table are those of an
+    indexer_case with one row per request (context length L_r); query row
+    r * next_n + t belongs to request r (row_to_batch), sees the causal
+    length L_r - (next_n - 1 - t), and draws its own query and head weights
+    from the same distributions as indexer_case."""
+    base = indexer_case(seed, batch=requests, n_lo=n_lo, n_hi=n_hi, page_size=page_size, k=k, heads=heads,
+                        dim=dim, name=name)
+    rows = requests * next_n
+    q = np.empty((rows, heads, dim), np.uint8)
+    q_scale = np.empty(rows, np.float32)
+    w = np.empty((rows, heads), np.float32)
+    for r in range(rows):
+        qf = rng(seed, STREAM_MQ, r).standard_normal((heads, dim), dtype=np.float32) * np.float32(0.5)
+        s = np.float32(np.abs(qf).max() / np.float32(E4M3_MAX))
+        q_scale[r] = s
+        q[r] = _to_e4m3_bytes(qf / s)
+        w[r] = rng(seed, STREAM_MW, r).standard_normal(heads, dtype=np.float32) / np.float32(8.0)
+    r2b = np.repeat(np.arange(requests, dtype=np.int32), next_n)
+    t = np.tile(np.arange(next_n, dtype=np.int32), requests)
+    lens = np.maximum(base.seq_lens[r2b] - (next_n - 1 - t), 0).astype(np.int32)
+    return IndexerCase(name, q, q_scale, w, base.kcache, base.k_scale, base.block_table, page_size, lens, k=k,
+                       max_seq_len=base.max_seq_len, meta=dict(base.meta, requests=requests, next_n=next_n),
+                       row_to_batch=r2b)
+
+
 # --------------------------------------------------------------------------
 # The five named workloads (full size) and reduced versions for quick tests
 # --------------------------------------------------------------------------
 
-SEEDS = {"c1": 101, "c2": 102, "c3": 103, "c4": 104, "c5": 105}
+SEEDS = {"c1": 101, "c2": 102, "c3": 103, "c4": 104, "c5": 105, "mtp": 106}
 
 
 def c1_decode_topk() -> RowsCase:
@@ -298,6 +329,13 @@ def c5_long_decode() -> IndexerCase:
                         name="long-decode-B64-n128k-320k-k2048")
 
 
+def mtp_decode() -> IndexerCase:
+    """Multi-token decode: 16 requests x 4 query tokens (64 rows sharing 16
+    block-table rows), contexts ~ U{16384..65536}, page_size 64, k 2048."""
+    return multi_query_case(SEEDS["mtp"], requests=16, next_n=4, n_lo=16384, n_hi=65536, page_size=64, k=2048,
+                            name="mtp-decode-16x4-n16k-64k-k2048")
+
+
 def expected_tokens(case: IndexerCase) -> int:
     return int(np.asarray(case.seq_lens, dtype=np.int64).sum())
 
@@ -307,7 +345,7 @@ def ceil_div(a: int, b: int) -> int:
 
 
 __all__ = [
-    "RowsCase", "IndexerCase", "decode_rows_case", "packed_prefill_case", "indexer_case",
-    "c1_decode_topk", "c2_fused_decode", "c3_packed_prefill", "c4_block_sparse", "c5_long_decode",
+    "RowsCase", "IndexerCase", "decode_rows_case", "packed_prefill_case", "indexer_case", "multi_query_case",
+    "c1_decode_topk", "c2_fused_decode", "c3_packed_prefill", "c4_block_sparse", "c5_long_decode", "mtp_decode",
     "SEEDS", "SENTINEL_KEY_BYTE", "SENTINEL_KEY_SCALE", "rng", "expected_tokens", "ceil_div",
 ]
