@@ -10,8 +10,9 @@ method's arithmetic.
 The oracle is plain, slow and meant to be checked by eye:
 
 * e4m3 decoding from the OCP 8-bit floating-point definition (``fp8.py``);
+* e4m3 encoding by nearest-value search over the same table (``fp8.py``);
 * float64 scoring, page gathering, top-k by a full stable sort, the page
-  transform and the block variant (``indexer.py``).
+  transform, the block variant and the key-cache writer (``indexer.py``).
 
 Each function names the passage of the pages it follows. Pages:
 
@@ -28,10 +29,12 @@ independent integer recomputation, brute force on tiny inputs, invariants and
 hand-built cases. None is "parity unpinned".
 """
 from . import fp8, indexer  # noqa: F401
-from .fp8 import E4M3FN_TABLE, decode_e4m3fn  # noqa: F401
+from .fp8 import E4M3FN_TABLE, decode_e4m3fn, encode_e4m3fn  # noqa: F401
 from .indexer import (  # noqa: F401
     block_scores,
     block_topk,
+    cache_write,
+    quantize_key,
     fused_topk,
     index_scores,
     page_transform,

@@ -49,3 +49,31 @@ def decode_e4m3fn(codes: np.ndarray) -> np.ndarray:
     if np.isnan(v).any():
         raise ValueError("e4m3fn NaN code in indexer input")
     return v
+
+
+# Non-negative finite codes 0x00..0x7E in ascending value order (0x7F is NaN).
+_NONNEG = E4M3FN_TABLE[:0x7F]
+
+
+def encode_e4m3fn(x) -> np.ndarray:
+    """Nearest e4m3fn code of each value, ties to the even code, magnitudes
+    above 448 saturating to 448, the sign kept (so -0.0 gives 0x80).
+
+    READING: the pages store index keys in an fp8 e4m3 cache ([ATOM-1473],
+    Pull request overview) without saying how keys are rounded into it. This
+    uses round-to-nearest-even, the IEEE default, and saturation, since the
+    format has no infinity. It is written as a search over the value table:
+    among adjacent codes exactly one is even, and an even code has a zero
+    mantissa LSB, which is what ties-to-even means.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if np.isnan(x).any():
+        raise ValueError("cannot encode NaN")
+    a = np.minimum(np.abs(x), 448.0)
+    lo = np.clip(np.searchsorted(_NONNEG, a, side="right") - 1, 0, 0x7E)  # _NONNEG[lo] <= a
+    hi = np.minimum(lo + 1, 0x7E)
+    dlo = a - _NONNEG[lo]
+    dhi = _NONNEG[hi] - a
+    up = (dhi < dlo) | ((dhi == dlo) & (lo % 2 == 1))
+    code = np.where(up, hi, lo).astype(np.uint8)
+    return (code | (np.signbit(x).astype(np.uint8) << 7)).astype(np.uint8)

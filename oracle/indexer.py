@@ -247,3 +247,42 @@ def block_topk(case, rows=None, block_size=None, top_blocks=None):
         logical.append(sel)
         bscores.append(bsv)
     return np.stack(blocks), np.stack(slot_lists), np.stack(logical), bscores
+
+
+# ---------------------------------------------------------------------------
+# Index-key cache writer
+# ---------------------------------------------------------------------------
+
+
+def quantize_key(k_row):
+    """One token's cache entry: scale = fp32(max|k| / 448), or 1 if that is
+    0; codes = e4m3fn(fp32(k / scale)).
+
+    [ATOM-1473], Pull request overview and the attention-layer diffs: the
+    index-key cache is allocated in fp8 and written with a key scale.
+    READING: one fp32 scale per cached token, chosen so the largest
+    magnitude maps to 448 (the e4m3 maximum); both divisions are fp32
+    divisions rounded to nearest, then ``encode_e4m3fn``. This is the format
+    every scoring function here reads (``index_scores``).
+    """
+    from .fp8 import encode_e4m3fn
+
+    k = np.asarray(k_row, dtype=np.float32)
+    m = np.float32(np.abs(k).max()) if k.size else np.float32(0.0)
+    scale = np.float32(m / np.float32(448.0))
+    if not scale > 0:
+        scale = np.float32(1.0)
+    return encode_e4m3fn((k / scale).astype(np.float32)), scale
+
+
+def cache_write(keys, slot_mapping, kcache, k_scale) -> None:
+    """Quantize each new key (``quantize_key``) and store it at its slot:
+    kcache[slot] = codes, k_scale[slot] = scale. Tokens with a negative slot
+    are skipped. Writes into ``kcache`` and ``k_scale`` in place."""
+    keys = np.asarray(keys, dtype=np.float32)
+    for t, s in enumerate(np.asarray(slot_mapping).astype(np.int64)):
+        if s < 0:
+            continue
+        codes, scale = quantize_key(keys[t])
+        kcache[s] = codes
+        k_scale[s] = scale
