@@ -14,7 +14,8 @@ roofline figure:
   * fused decode:    B 32, n ~ U[8192, 16384], k 2048;
   * block-sparse:    B 64, n 32768, top 32 blocks of 128;
   * long decode:     B 64, n ~ U[131072, 327680], k 2048;
-  * multi-token decode: 16 requests x 4 query rows, n ~ U[16384, 65536], k 2048.
+  * multi-token decode: 16 requests x 4 query rows, n ~ U[16384, 65536], k 2048;
+  * index-key cache write: 16384 bf16 keys into a 1M-slot cache.
 It also carries the CPU oracle's throughput on a bounded sample of the
 headline workload, run on the host's cores.
 
@@ -331,6 +332,28 @@ def bench_fused_mq(torch, ops, timer, case, warmup, steps, flush):
     return res
 
 
+def bench_cache_write(torch, ops, timer, warmup, steps, flush, tokens=16384, num_slots=1 << 20):
+    """Index-key cache writer: `tokens` new bf16 keys (one prefill chunk)
+    quantized into a cache of num_slots slots at distinct random slots.
+    Algorithmic bytes: keys read (2 B x 128) + slot ids read (4 B) + codes
+    (128 B) and scales (4 B) written, per token."""
+    g = np.random.default_rng(workloads.SEEDS["c3"])
+    keys = torch.from_numpy(g.standard_normal((tokens, 128)).astype(np.float32)).to(torch.bfloat16).cuda()
+    slots = torch.from_numpy(g.permutation(num_slots)[:tokens].astype(np.int32)).cuda()
+    kc = torch.zeros((num_slots, 128), dtype=torch.uint8, device="cuda")
+    ks = torch.zeros((num_slots,), dtype=torch.float32, device="cuda")
+
+    def step():
+        ops.idx_cache_write(keys, slots, kc, ks)
+
+    wall, us, region = timer.run(step, warmup, steps, flush)
+    res = summary(us, tokens * (2 * 128 + 4 + 128 + 4), tokens, region, timer.settled)
+    res["tokens"] = tokens
+    del keys, slots, kc, ks
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_unfused(torch, ops, timer, case, warmup, steps, flush):
     """The unfused path on the same inputs: idx_score_fp8 writes the score
     rows, then topk_rows selects and maps through the block table (the pages'
@@ -376,7 +399,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="all", help="comma list of c1..c5, mtp, or all")
+    ap.add_argument("--only", default="all", help="comma list of c1..c5, mtp, cw, or all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for PMC byte-counter calibration)")
@@ -392,7 +415,7 @@ def main(argv=None):
         print("bench.py measures one GPU only: the indexer top-k path here runs on a single MI355X "
               "(no sharding, no collectives); run with --gpus 1", file=sys.stderr)
         return 2
-    only = {"c1", "c2", "c3", "c4", "c5", "mtp"} if a.only == "all" else set(a.only.split(","))
+    only = {"c1", "c2", "c3", "c4", "c5", "mtp", "cw"} if a.only == "all" else set(a.only.split(","))
 
     case3 = None
     cpu = None
@@ -469,6 +492,9 @@ def main(argv=None):
         also["fused_decode_B32_k2048_unfused"] = bench_unfused(torch, ops, timer, c2, a.warmup, max(a.steps, 50),
                                                                True)
         del c2
+    if "cw" in only:
+        log("timing index-key cache write ...")
+        also["cache_write_16384_bf16"] = bench_cache_write(torch, ops, timer, a.warmup, max(a.steps, 50), True)
     if "mtp" in only:
         log("timing multi-token decode 16x4 ...")
         mq = workloads.mtp_decode()

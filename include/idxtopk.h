@@ -69,6 +69,11 @@ extern "C" {
 #define IDXTOPK_OP_PAGE_TRANSFORM 3
 #define IDXTOPK_OP_SCORE_TOPK_FUSED 4
 #define IDXTOPK_OP_BLOCK_TOPK 5
+#define IDXTOPK_OP_CACHE_WRITE 6
+
+/* Key element types for idx_cache_write. */
+#define IDXTOPK_KEY_F32 0  /* float */
+#define IDXTOPK_KEY_BF16 1 /* bfloat16, as its 16-bit pattern */
 
 /*
  * Indexer inputs shared by idx_score_fp8, idx_score_topk_fused and block_topk.
@@ -214,6 +219,36 @@ int block_topk(const uint8_t* q, const float* q_scale, const float* w,
                int32_t top_blocks,
                int32_t* out_blocks, int32_t* out_slots,
                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * idx_cache_write -- quantize new index keys into the paged fp8 cache.
+ *
+ * For every token t with s = slot_mapping[t] >= 0:
+ *   scale          = max_d |keys[t, d]| / 448   (fp32 division, rounded to
+ *                    nearest; 1 when that is 0),
+ *   kcache[s, d]   = e4m3fn(keys[t, d] / scale) (fp32 division rounded to
+ *                    nearest, then the nearest e4m3fn value, ties to the
+ *                    even mantissa, magnitudes above 448 saturating),
+ *   k_scale[s]     = scale.
+ * Tokens with a negative slot are skipped. This is the cache layout every
+ * indexer entry point above reads ([ATOM-1473] Pull request overview and the
+ * attention-layer diffs: the index-key cache is allocated in fp8 and written
+ * with a key scale; one scale per token and the rounding are this library's
+ * reading).
+ *
+ * keys          [tokens, key_stride] row-major, elements of key_dtype
+ *               (IDXTOPK_KEY_F32 or IDXTOPK_KEY_BF16); the first dim of
+ *               each row are the key. keys and key_stride must keep every
+ *               row 8-byte aligned (fp32) or 4-byte aligned (bf16).
+ * slot_mapping  int32 [tokens]: destination slot, or negative to skip.
+ *               Non-negative slots must be distinct (two tokens writing one
+ *               slot race) and below the cache's slot count.
+ * kcache        uint8 e4m3fn [num_slots, dim]; k_scale float [num_slots].
+ * dim == IDXTOPK_DIM. Keys must be finite. No workspace.
+ */
+int idx_cache_write(const void* keys, int32_t key_dtype, int64_t key_stride, int32_t tokens,
+                    int32_t dim, const int32_t* slot_mapping, uint8_t* kcache, float* k_scale,
+                    void* stream);
 
 /*
  * Workspace bytes an operation needs (0 when it needs none).

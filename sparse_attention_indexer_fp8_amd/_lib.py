@@ -23,6 +23,9 @@ OP_SCORE = 2
 OP_PAGE_TRANSFORM = 3
 OP_SCORE_TOPK_FUSED = 4
 OP_BLOCK_TOPK = 5
+OP_CACHE_WRITE = 6
+KEY_F32 = 0
+KEY_BF16 = 1
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -39,6 +42,7 @@ SIGNATURES = {
                                     _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "block_topk": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                           _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "idx_cache_write": (_i32, [_vp, _i32, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
     "idxtopk_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "idxtopk_status_str": (ctypes.c_char_p, [_i32]),
     "idxtopk_version": (_i32, []),

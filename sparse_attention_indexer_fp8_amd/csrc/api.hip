@@ -137,6 +137,21 @@ int block_topk(const uint8_t* q, const float* q_scale, const float* w, const uin
                                     static_cast<hipStream_t>(stream));
 }
 
+int idx_cache_write(const void* keys, int32_t key_dtype, int64_t key_stride, int32_t tokens,
+                    int32_t dim, const int32_t* slot_mapping, uint8_t* kcache, float* k_scale,
+                    void* stream) {
+  if (tokens < 0 || dim <= 0) return IDXTOPK_EINVAL;
+  if (dim != IDXTOPK_DIM) return IDXTOPK_EUNSUPPORTED;
+  if (key_dtype != IDXTOPK_KEY_F32 && key_dtype != IDXTOPK_KEY_BF16) return IDXTOPK_EUNSUPPORTED;
+  if (tokens == 0) return IDXTOPK_OK;
+  if (!keys || !slot_mapping || !kcache || !k_scale || key_stride < dim) return IDXTOPK_EINVAL;
+  // every row must start on a whole pair of elements (8 bytes fp32, 4 bf16)
+  const uintptr_t align = key_dtype == IDXTOPK_KEY_F32 ? 8u : 4u;
+  if (reinterpret_cast<uintptr_t>(keys) % align != 0 || key_stride % 2 != 0) return IDXTOPK_EINVAL;
+  return idxtopk::launch_cache_write(keys, key_dtype == IDXTOPK_KEY_BF16, key_stride, tokens, slot_mapping,
+                                     kcache, k_scale, static_cast<hipStream_t>(stream));
+}
+
 size_t idxtopk_workspace_bytes(int32_t op, int32_t rows, int32_t k, int32_t max_seq_len) {
   if (rows < 0 || max_seq_len < 0) return 0;
   switch (op) {

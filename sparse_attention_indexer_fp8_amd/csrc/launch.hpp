@@ -55,6 +55,9 @@ int launch_fused(const IndexerInputs& in, int k, int32_t* out_slots, float* out_
                  hipStream_t stream);
 
 size_t block_workspace_bytes(int rows, int block_size, int max_seq_len);
+
+int launch_cache_write(const void* keys, bool bf16, int64_t stride, int tokens, const int32_t* slots,
+                       uint8_t* kcache, float* kscale, hipStream_t stream);
 int launch_block_topk(const IndexerInputs& in, int block_size, int top_blocks, int32_t* out_blocks,
                       int32_t* out_slots, void* ws, hipStream_t stream);
 

@@ -197,3 +197,23 @@ def block_topk(q, q_scale, w, kcache, k_scale, block_table, seq_lens, page_size:
                                 _ptr(ws), ws.numel(), _stream())
     _lib.check("block_topk", st)
     return (out_blocks, out_slots) if return_slots else out_blocks
+
+
+def idx_cache_write(keys: torch.Tensor, slot_mapping: torch.Tensor, kcache: torch.Tensor,
+                    k_scale: torch.Tensor) -> None:
+    """Quantize new index keys (fp32 or bf16, [tokens, 128] with contiguous
+    rows) into the paged e4m3fn cache: kcache[slot] and k_scale[slot] for
+    every token whose slot is non-negative. In place."""
+    if keys.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"keys: expected float32 or bfloat16, got {keys.dtype}")
+    _need(keys, "keys", (keys.dtype,), 2, contiguous=False)
+    if keys.stride(1) != 1:
+        raise ValueError("keys rows must be contiguous")
+    _need(slot_mapping, "slot_mapping", (torch.int32,), 1)
+    _need(kcache, "kcache", _F8, 2)
+    _need(k_scale, "k_scale", (torch.float32,), 1)
+    T, D = keys.shape
+    dt = _lib.KEY_BF16 if keys.dtype == torch.bfloat16 else _lib.KEY_F32
+    st = _lib.load().idx_cache_write(_ptr(keys), dt, keys.stride(0), T, D, _ptr(slot_mapping),
+                                     _ptr(_as_u8(kcache)), _ptr(k_scale), _stream())
+    _lib.check("idx_cache_write", st)

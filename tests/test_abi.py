@@ -34,9 +34,10 @@ def lib():
     return _lib.load()
 
 
-def test_header_declares_the_five_ops():
+def test_header_declares_the_ops():
     names = _declared_functions()
-    for op in ("idx_score_fp8", "topk_rows", "idx_score_topk_fused", "topk_page_transform", "block_topk"):
+    for op in ("idx_score_fp8", "topk_rows", "idx_score_topk_fused", "topk_page_transform", "block_topk",
+               "idx_cache_write"):
         assert op in names
     assert {"idxtopk_workspace_bytes", "idxtopk_status_str", "idxtopk_version"} <= set(names)
 
@@ -142,6 +143,24 @@ def test_block_validation(lib):
     assert f(out=NULL) == -1
     assert f(nb=need - 1) == -3
     assert f(B=0) == 0
+
+
+def test_cache_write_validation(lib):
+    f = lambda keys=FAKE, dt=0, ks=128, T=16, D=128, sm=FAKE, kc=FAKE, sc=FAKE: lib.idx_cache_write(
+        keys, dt, ks, T, D, sm, kc, sc, NULL)
+    assert f(D=64) == -2
+    assert f(dt=2) == -2
+    assert f(T=-1) == -1
+    assert f(keys=NULL) == -1
+    assert f(sm=NULL) == -1
+    assert f(kc=NULL) == -1
+    assert f(sc=NULL) == -1
+    assert f(ks=100) == -1            # stride shorter than a key
+    assert f(ks=129) == -1            # odd stride breaks row alignment
+    assert f(keys=ctypes.c_void_p(0x1004)) == -1     # fp32 rows need 8-byte alignment
+    assert f(keys=ctypes.c_void_p(0x1002), dt=1) == -1  # bf16 rows need 4-byte alignment
+    assert f(T=0) == 0
+    assert lib.idxtopk_workspace_bytes(6, 16, 0, 128) == 0
 
 
 def test_workspace_bytes_rules(lib):
