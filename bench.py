@@ -177,7 +177,7 @@ def _oracle_rows(rows):
                             c.page_size, rows=rows).shape[0]
 
 
-def cpu_baseline(case, every: int = 4):
+def cpu_baseline(case, every: int = 2):
     import multiprocessing as mp
 
     global _CPU_CASE
@@ -191,9 +191,9 @@ def cpu_baseline(case, every: int = 4):
     wall = time.perf_counter() - t0
     assert done == len(rows)
     return {"value": round(len(rows) / wall, 1), "unit": "rows/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(rows)} of {case.rows} rows (every {every}th) of the packed-prefill buffer, "
+            "sample": f"{len(rows)} of {case.rows} rows (one row in {every}) of the packed-prefill buffer, "
                       f"oracle.topk_rows (float64 full stable sort per row + page transform), "
-                      f"{cores} forked worker processes, wall {wall:.2f} s"}
+                      f"{cores} forked worker processes, wall {wall:.2f} s (~{wall * cores:.0f} core-seconds)"}
 
 
 # ---------------------------------------------------------------------------
