@@ -15,7 +15,9 @@ roofline figure:
   * block-sparse:    B 64, n 32768, top 32 blocks of 128;
   * long decode:     B 64, n ~ U[131072, 327680], k 2048;
   * multi-token decode: 16 requests x 4 query rows, n ~ U[16384, 65536], k 2048;
-  * index-key cache write: 16384 bf16 keys into a 1M-slot cache.
+  * index-key cache write: 16384 bf16 keys into a 1M-slot cache;
+  * prefill indexer from the fp8 cache: the packed-prefill geometry (16384
+    rows, causal lengths 61809..70000 and 1..8192), scores then top-512.
 It also carries the CPU oracle's throughput on a bounded sample of the
 headline workload, run on the host's cores.
 
@@ -354,6 +356,51 @@ def bench_cache_write(torch, ops, timer, warmup, steps, flush, tokens=16384, num
     return res
 
 
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 matrix peak
+
+
+def bench_prefill(torch, ops, timer, case, warmup, steps):
+    """Prefill indexer from the fp8 cache: idx_score_fp8 with row_to_batch
+    (two rows per wave against one key load) writes the score rows, then
+    topk_rows selects k per row and maps through the block table. The score
+    step is a dense contraction, measured against the fp8 matrix peak
+    (2 * heads * 128 flops per (row, key)); the top-k step against HBM."""
+    args = [dev(torch, x) for x in (case.q, case.q_scale, case.w, case.kcache, case.k_scale,
+                                    case.block_table, case.seq_lens)]
+    r2b = dev(torch, case.row_to_batch)
+    bt, sl = args[5], args[6]
+    scores = torch.empty((case.batch, case.max_seq_len), dtype=torch.float32, device="cuda")
+    out = torch.empty((case.batch, case.k), dtype=torch.int32, device="cuda")
+
+    def score():
+        ops.idx_score_fp8(*args, case.page_size, case.max_seq_len, out=scores, row_to_batch=r2b)
+
+    def topk():
+        ops.topk_rows(scores, sl, case.k, row_to_batch=r2b, page_table=bt, page_size=case.page_size, out=out)
+
+    n = case.seq_lens.astype(np.int64)
+    flops = 2 * case.heads * case.dim * int(n.sum())
+    _, us_s, reg_s = timer.run(score, warmup, steps, False)
+    settled_s = timer.settled
+    _, us_t, reg_t = timer.run(topk, warmup, steps, False)
+    s_us = float(reg_s)
+    tflops = flops / (s_us * 1e-6) / 1e12
+    topk_bytes = int((4 * n[n > case.k]).sum()) + case.batch * case.k * 4 + int((4 * np.minimum(n, case.k)).sum()) \
+        + 8 * case.batch
+    res_t = summary(us_t, topk_bytes, case.batch, reg_t, timer.settled)
+    res = {"rows": case.batch, "row_tokens": int(n.sum()), "k": case.k,
+           "score": {"us_per_launch_mean": round(s_us, 2), "us_per_launch_median": round(float(np.median(us_s)), 2),
+                     "flops": flops, "achieved_TFLOPs": round(tflops, 1),
+                     "mfma_frac": round(tflops / FP8_PEAK_TFLOPS, 4), "bound": "mfma (fp8)",
+                     "settle_launches": settled_s},
+           "topk": res_t,
+           "us_per_call_total": round(s_us + res_t["us_per_launch_mean"], 2),
+           "score_buffer_bytes": int(scores.numel() * 4)}
+    del args, scores
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_unfused(torch, ops, timer, case, warmup, steps, flush):
     """The unfused path on the same inputs: idx_score_fp8 writes the score
     rows, then topk_rows selects and maps through the block table (the pages'
@@ -399,7 +446,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="all", help="comma list of c1..c5, mtp, cw, or all")
+    ap.add_argument("--only", default="all", help="comma list of c1..c5, mtp, cw, pf, or all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for PMC byte-counter calibration)")
@@ -415,7 +462,7 @@ def main(argv=None):
         print("bench.py measures one GPU only: the indexer top-k path here runs on a single MI355X "
               "(no sharding, no collectives); run with --gpus 1", file=sys.stderr)
         return 2
-    only = {"c1", "c2", "c3", "c4", "c5", "mtp", "cw"} if a.only == "all" else set(a.only.split(","))
+    only = {"c1", "c2", "c3", "c4", "c5", "mtp", "cw", "pf"} if a.only == "all" else set(a.only.split(","))
 
     case3 = None
     cpu = None
@@ -492,6 +539,12 @@ def main(argv=None):
         also["fused_decode_B32_k2048_unfused"] = bench_unfused(torch, ops, timer, c2, a.warmup, max(a.steps, 50),
                                                                True)
         del c2
+    if "pf" in only:
+        log("generating prefill indexer inputs ...")
+        pf = workloads.prefill_indexer()
+        log("timing prefill indexer (row-pair scores + top-k) ...")
+        also["prefill_indexer_16384_k512"] = bench_prefill(torch, ops, timer, pf, a.warmup, a.steps)
+        del pf
     if "cw" in only:
         log("timing index-key cache write ...")
         also["cache_write_16384_bf16"] = bench_cache_write(torch, ops, timer, a.warmup, max(a.steps, 50), True)

@@ -153,6 +153,159 @@ __global__ __launch_bounds__(IX_WG) void score_kernel(IndexerArgs a, float* scor
 }
 
 // ---------------------------------------------------------------------------
+// Unfused scores, rows in pairs (prefill and multi-token rows)
+// ---------------------------------------------------------------------------
+//
+// Query rows that map to one block-table row (a request's prefill rows or its
+// multi-token decode rows) read the same keys. Each wave here takes two
+// consecutive rows: every 16-token key group is loaded and rearranged once
+// and scored against both rows' queries (twice the MFMA and head-sum work per
+// key byte). The grid is chunk-major, so all workgroups stream the same
+// 64-page key chunk at about the same time and share it through the caches.
+// A chunk's page ids sit one per lane in a VGPR, so a group's page is one
+// readlane: no LDS and no barrier. Used when pages hold whole 16-token groups
+// (page_size % 16 == 0); a pair whose rows map to different block-table rows
+// is scored one row at a time.
+
+constexpr int PR_WG = 256;  // 4 waves, one pair of rows each
+constexpr int PR_RING = 4;  // key groups in flight per wave
+constexpr int PR_CHUNK_PAGES = kWave;
+
+template <int NT, bool TWO>
+__device__ __forceinline__ void pair_rows_range(const IndexerArgs& a, const QOperand<NT>& qa,
+                                                const QOperand<NT>& qb, float* ra, float* rb, int na, int nb,
+                                                const int32_t* bt_row, int kb, int ke) {
+  const uint32_t P = static_cast<uint32_t>(a.page_size);
+  const int l = lane_id();
+  const int c = l & 15, g = l >> 4;
+  const uint32_t pg0 = fdiv(static_cast<uint32_t>(kb), a.pdiv);
+  const uint32_t npg = fdiv(static_cast<uint32_t>(ke - 1), a.pdiv) - pg0 + 1;  // <= PR_CHUNK_PAGES
+  const int32_t pv = static_cast<uint32_t>(l) < npg ? bt_row[pg0 + l] : 0;
+  const int ngroups = (ke - kb + kGroup - 1) / kGroup;
+
+  // group gi -> this lane's 32 key bytes in the operand layout (bytes
+  // [32g, 32g + 32) of token c) and the token's scale. The group lies in one
+  // page, and tokens past ke read that page's bytes. Keys come mostly from
+  // the caches here (many rows read them), so the operand layout is loaded
+  // directly rather than as whole lines plus a permute: fewer instructions
+  // in a loop that instruction issue bounds (5.75 vs 6.01 ms on the prefill
+  // workload).
+  auto fetch = [&](int gi, KeyPieces& kp, float& ks) {
+    const int j0 = kb + gi * kGroup;
+    const uint32_t pg = fdiv(static_cast<uint32_t>(j0), a.pdiv);
+    uint32_t m = (static_cast<uint32_t>(__builtin_amdgcn_readlane(pv, pg - pg0)) - pg) * P;
+    asm volatile("" : "+s"(m));
+    const uint32_t s0 = m + static_cast<uint32_t>(j0);
+    const uint8_t* kp0 = a.kcache + (static_cast<uint64_t>(s0 + c) << 7) + 32 * g;
+    kp.x0 = load_v4i_stream(kp0);
+    kp.x1 = load_v4i_stream(kp0 + 16);
+    ks = a.k_scale[s0 + c];
+  };
+  auto consume = [&](int gi, float sa, float sb) {
+    const int j = kb + gi * kGroup + c;
+    if (g == 0 && j < na) ra[j] = sa;
+    if (TWO && g == 1 && j < nb) rb[j] = sb;
+  };
+  auto score2 = [&](const KeyPieces& kp, float ks, float& sa, float& sb) {
+    v8i kbv;
+    kbv[0] = kp.x0[0]; kbv[1] = kp.x0[1]; kbv[2] = kp.x0[2]; kbv[3] = kp.x0[3];
+    kbv[4] = kp.x1[0]; kbv[5] = kp.x1[1]; kbv[6] = kp.x1[2]; kbv[7] = kp.x1[3];
+    sa = score16<NT>(qa, kbv, ks);
+    sb = TWO ? score16<NT>(qb, kbv, ks) : 0.0f;
+  };
+
+  typedef float vks __attribute__((ext_vector_type(PR_RING)));
+  KeyPieces ring[PR_RING];
+  vks ksr;
+  const int gmax = ngroups - 1;
+#pragma unroll
+  for (int u = 0; u < PR_RING; ++u) {
+    float t;
+    fetch(min(u, gmax), ring[u], t);
+    ksr[u] = t;
+  }
+  int gi0 = 0;
+  for (; gi0 + 2 * PR_RING <= ngroups; gi0 += PR_RING) {
+#pragma unroll
+    for (int u = 0; u < PR_RING; ++u) {
+      float sa, sb;
+      score2(ring[u], ksr[u], sa, sb);
+      // the scores are final before the slot is refilled (see score_chunk)
+      asm volatile("" : "+v"(sa), "+v"(sb));
+      __builtin_amdgcn_sched_barrier(0);
+      float t;
+      fetch(gi0 + u + PR_RING, ring[u], t);
+      ksr[u] = t;
+      consume(gi0 + u, sa, sb);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < PR_RING; ++u) {
+    const int gi = gi0 + u;
+    if (gi < ngroups) {
+      float sa, sb;
+      score2(ring[u], ksr[u], sa, sb);
+      if (gi + PR_RING < ngroups) {
+        float t;
+        fetch(gi + PR_RING, ring[u], t);
+        ksr[u] = t;
+      }
+      consume(gi, sa, sb);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < PR_RING; ++u) {
+    const int gi = gi0 + PR_RING + u;
+    if (gi < ngroups) {
+      float sa, sb;
+      score2(ring[u], ksr[u], sa, sb);
+      consume(gi, sa, sb);
+    }
+  }
+}
+
+template <int NT>
+__global__ __launch_bounds__(PR_WG) void pair_score_kernel(IndexerArgs a, float* scores, int64_t sstride,
+                                                           int ntiles, int chunk) {
+  const int tile = blockIdx.x % ntiles;
+  const int kc = blockIdx.x / ntiles;
+  const int pair = tile * (PR_WG / kWave) + uniform(static_cast<int>(threadIdx.x) / kWave);
+  const int ba = 2 * pair, bb = ba + 1;
+  if (ba >= a.batch) return;
+  const bool has_b = bb < a.batch;
+  const int na = load_uniform(a.seq_lens + ba);
+  const int nb = has_b ? load_uniform(a.seq_lens + bb) : 0;
+  const int pa = a.row_to_batch ? load_uniform(a.row_to_batch + ba) : ba;
+  const int pb = has_b ? (a.row_to_batch ? load_uniform(a.row_to_batch + bb) : bb) : pa;
+  const int kb = kc * chunk;
+  float* ra = scores + static_cast<int64_t>(ba) * sstride;
+  float* rb = scores + static_cast<int64_t>(bb) * sstride;
+  const int32_t* bta = a.block_table + static_cast<int64_t>(pa) * a.bt_stride;
+  if (has_b && pa == pb) {
+    const int ke = min(kb + chunk, max(na, nb));
+    if (kb >= ke) return;
+    QOperand<NT> qa, qb;
+    load_query<NT>(qa, a.q + static_cast<int64_t>(ba) * a.heads * kDim, a.w + static_cast<int64_t>(ba) * a.heads,
+                   a.q_scale[ba]);
+    load_query<NT>(qb, a.q + static_cast<int64_t>(bb) * a.heads * kDim, a.w + static_cast<int64_t>(bb) * a.heads,
+                   a.q_scale[bb]);
+    pair_rows_range<NT, true>(a, qa, qb, ra, rb, na, nb, bta, kb, ke);
+  } else {
+    for (int r = 0; r < (has_b ? 2 : 1); ++r) {
+      const int b = r ? bb : ba;
+      const int n = r ? nb : na;
+      const int ke = min(kb + chunk, n);
+      if (kb >= ke) continue;
+      QOperand<NT> q1;
+      load_query<NT>(q1, a.q + static_cast<int64_t>(b) * a.heads * kDim, a.w + static_cast<int64_t>(b) * a.heads,
+                     a.q_scale[b]);
+      pair_rows_range<NT, false>(a, q1, q1, r ? rb : ra, r ? rb : ra, n, 0,
+                                 a.block_table + static_cast<int64_t>(r ? pb : pa) * a.bt_stride, kb, ke);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Fused decode score + top-k: chunk kernel, then per-row merge kernel
 // ---------------------------------------------------------------------------
 
@@ -998,6 +1151,23 @@ static int choose_chunk(int batch, int max_seq_len, int page_size, int align, in
 
 int launch_idx_score(const IndexerInputs& in, float* scores, int64_t score_stride, hipStream_t stream) {
   if (in.batch == 0) return 0;
+  if (in.row_to_batch && in.page_size % kGroup == 0 && in.heads <= 64) {
+    // rows sharing block-table rows: two rows per wave against one key load
+    int64_t chunk = static_cast<int64_t>(PR_CHUNK_PAGES) * in.page_size;
+    if (chunk > 8192) chunk = 8192 / in.page_size * in.page_size;
+    const IndexerArgs a = make_args(in, static_cast<int>(chunk), false);
+    const int pairs = (in.batch + 1) / 2;
+    const int ntiles = (pairs + PR_WG / kWave - 1) / (PR_WG / kWave);
+    const int nkc = static_cast<int>((static_cast<int64_t>(in.max_seq_len > 0 ? in.max_seq_len : 1) + chunk - 1) / chunk);
+    const dim3 grid(static_cast<unsigned>(ntiles * nkc));
+    (void)hipGetLastError();
+    switch (in.heads) {
+      case 16: hipLaunchKernelGGL(pair_score_kernel<1>, grid, dim3(PR_WG), 0, stream, a, scores, score_stride, ntiles, static_cast<int>(chunk)); break;
+      case 32: hipLaunchKernelGGL(pair_score_kernel<2>, grid, dim3(PR_WG), 0, stream, a, scores, score_stride, ntiles, static_cast<int>(chunk)); break;
+      default: hipLaunchKernelGGL(pair_score_kernel<4>, grid, dim3(PR_WG), 0, stream, a, scores, score_stride, ntiles, static_cast<int>(chunk)); break;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+  }
   const int chunk = choose_chunk(in.batch, in.max_seq_len, in.page_size, kGroup, 512, 8192);
   const IndexerArgs a = make_args(in, chunk, true);
   const dim3 grid(static_cast<unsigned>(a.nchunk_max * in.batch));

@@ -419,3 +419,55 @@ def test_multi_query_block(ops):
         sigma = float(np.sqrt(np.mean(S * S)))
         kth = np.sort(bsv)[::-1][m - 1]
         assert (bsv[sel] >= kth - 1e-3 * max(abs(kth), sigma)).all()
+
+
+@pytest.mark.parametrize("heads,page_size,next_n,requests", [(64, 64, 3, 5), (16, 16, 4, 3), (32, 128, 1, 7),
+                                                            (64, 32, 300, 2)])
+def test_row_pair_scores_match_per_row(ops, heads, page_size, next_n, requests):
+    """With row_to_batch, idx_score_fp8 scores two rows per wave against one
+    key load. Its scores are bit-identical to the one-row-per-workgroup path
+    on the same case with block-table rows copied out (pairs that straddle
+    two requests, odd row counts and single-row requests included)."""
+    import torch
+
+    case = workloads.multi_query_case(930 + next_n, requests=requests, next_n=next_n, n_lo=1, n_hi=6000,
+                                      page_size=page_size, k=0, heads=heads)
+    log(f"row pairs: rows={case.batch} heads={heads} P={page_size}")
+    out = ops.idx_score_fp8(*_inputs(case), case.page_size, case.max_seq_len, row_to_batch=_r2b(case))
+    flat = _expanded(case)
+    out2 = ops.idx_score_fp8(*_inputs(flat), flat.page_size, flat.max_seq_len)
+    torch.cuda.synchronize()
+    out, out2 = out.cpu().numpy(), out2.cpu().numpy()
+    for b in range(case.batch):
+        n = int(case.seq_lens[b])
+        assert np.array_equal(out[b, :n], out2[b, :n]), b
+    for b in (0, case.batch // 2, case.batch - 1):
+        n = int(case.seq_lens[b])
+        check_scores(out[b, :n], case_scores(case, b))
+
+
+def test_prefill_indexer_full_size_sampled(ops):
+    """The prefill workload at full size, in the launch configuration the
+    benchmark times (idx_score_fp8 with row_to_batch, then topk_rows through
+    the block table): sampled rows of both requests, including the longest
+    (70000 keys) and the shortest, against the oracle's scores and top-k."""
+    import torch
+
+    case = workloads.prefill_indexer()
+    log(f"prefill full size: rows={case.batch} max n={case.max_seq_len}")
+    r2b = _r2b(case)
+    scores = ops.idx_score_fp8(*_inputs(case), case.page_size, case.max_seq_len, row_to_batch=r2b)
+    slots = ops.topk_rows(scores, dev(case.seq_lens), case.k, row_to_batch=r2b, page_table=dev(case.block_table),
+                          page_size=case.page_size)
+    torch.cuda.synchronize()
+    rows = [0, 4095, 8191, 8192, 8192 + 511, 8192 + 4000, case.batch - 1]
+    sc = {b: scores[b].cpu().numpy() for b in rows}
+    slots = slots.cpu().numpy()
+    del scores
+    torch.cuda.empty_cache()
+    for b in rows:
+        n = int(case.seq_lens[b])
+        S = case_scores(case, b)
+        check_scores(sc[b][:n], S)
+        ts = oracle.token_slots(case.block_table[case.row_to_batch[b]], case.page_size, n)
+        check_fused_row(slots[b], None, S, ts, case.k)

@@ -271,7 +271,8 @@ def indexer_case(seed: int, batch: int, n_lo: int, n_hi: int, page_size: int, k:
 
 
 def multi_query_case(seed: int, requests: int, next_n: int, n_lo: int, n_hi: int, page_size: int,
-                     k: int = 2048, heads: int = 64, dim: int = 128, name: str = "multi-query") -> IndexerCase:
+                     k: int = 2048, heads: int = 64, dim: int = 128, name: str = "multi-query",
+                     fixed_lens: Optional[np.ndarray] = None) -> IndexerCase:
     """Multi-token decode rows: each of `requests` requests decodes `next_n`
     query tokens at once. The cache and block table are those of an
     indexer_case with one row per request (context length L_r); query row
@@ -279,7 +280,7 @@ def multi_query_case(seed: int, requests: int, next_n: int, n_lo: int, n_hi: int
     length L_r - (next_n - 1 - t), and draws its own query and head weights
     from the same distributions as indexer_case."""
     base = indexer_case(seed, batch=requests, n_lo=n_lo, n_hi=n_hi, page_size=page_size, k=k, heads=heads,
-                        dim=dim, name=name)
+                        dim=dim, name=name, fixed_lens=fixed_lens)
     rows = requests * next_n
     q = np.empty((rows, heads, dim), np.uint8)
     q_scale = np.empty(rows, np.float32)
@@ -336,6 +337,16 @@ def mtp_decode() -> IndexerCase:
                             name="mtp-decode-16x4-n16k-64k-k2048")
 
 
+def prefill_indexer() -> IndexerCase:
+    """Packed prefill from the fp8 cache, in the packed-prefill top-k
+    geometry: request 0 has 61808 cached tokens and request 1 none, each
+    extends by 8192 tokens (contexts 70000 and 8192), so the 16384 query rows
+    see causal lengths 61809..70000 and 1..8192. page_size 64, k = 512."""
+    return multi_query_case(SEEDS["c3"], requests=2, next_n=8192, n_lo=0, n_hi=0, page_size=64, k=512,
+                            name="prefill-indexer-2x8192-ctx70000-8192-k512",
+                            fixed_lens=np.array([70000, 8192], np.int32))
+
+
 def expected_tokens(case: IndexerCase) -> int:
     return int(np.asarray(case.seq_lens, dtype=np.int64).sum())
 
@@ -347,5 +358,6 @@ def ceil_div(a: int, b: int) -> int:
 __all__ = [
     "RowsCase", "IndexerCase", "decode_rows_case", "packed_prefill_case", "indexer_case", "multi_query_case",
     "c1_decode_topk", "c2_fused_decode", "c3_packed_prefill", "c4_block_sparse", "c5_long_decode", "mtp_decode",
+    "prefill_indexer",
     "SEEDS", "SENTINEL_KEY_BYTE", "SENTINEL_KEY_SCALE", "rng", "expected_tokens", "ceil_div",
 ]
