@@ -153,28 +153,38 @@ __global__ __launch_bounds__(IX_WG) void score_kernel(IndexerArgs a, float* scor
 }
 
 // ---------------------------------------------------------------------------
-// Unfused scores, rows in pairs (prefill and multi-token rows)
+// Unfused scores, rows in groups (prefill and multi-token rows)
 // ---------------------------------------------------------------------------
 //
 // Query rows that map to one block-table row (a request's prefill rows or its
-// multi-token decode rows) read the same keys. Each wave here takes two
-// consecutive rows: every 16-token key group is loaded and rearranged once
-// and scored against both rows' queries (twice the MFMA and head-sum work per
-// key byte). The grid is chunk-major, so all workgroups stream the same
-// 64-page key chunk at about the same time and share it through the caches.
-// A chunk's page ids sit one per lane in a VGPR, so a group's page is one
-// readlane: no LDS and no barrier. Used when pages hold whole 16-token groups
-// (page_size % 16 == 0); a pair whose rows map to different block-table rows
-// is scored one row at a time.
+// multi-token decode rows) read the same keys. Each wave here takes four
+// consecutive rows: every 16-token key group is loaded once and scored
+// against all four rows' queries, and the head sums of the four rows reduce
+// together (score16x4), so lane group g ends up holding row g's scores and
+// every lane stores. If the four rows do not share a block-table row, the
+// wave scores pairs (score16x2) or single rows instead. The grid is
+// chunk-major, so all workgroups stream the same 64-page key chunk at about
+// the same time and share it through the caches. A chunk's page ids sit one
+// per lane in a VGPR, so a group's page is one readlane: no LDS and no
+// barrier. Used when pages hold whole 16-token groups (page_size % 16 == 0).
+//
+// On the packed-prefill geometry (16384 rows, 573M row-keys) the four-row
+// path runs at ~1.67 PFLOP/s of fp8 products, a third of the matrix peak;
+// the per-head weighted ReLU costs two vector instructions per product
+// element, about as much issue time as the products themselves. Two rows
+// per wave (2 waves per SIMD) ran 5.75 ms, four rows (1 wave per SIMD,
+// 52 AGPRs) 5.61 ms, one row 10.6 ms; issuing the next group's products
+// before the current group's head sums did not help.
 
-constexpr int PR_WG = 256;  // 4 waves, one pair of rows each
+constexpr int PR_WG = 256;  // 4 waves, each up to 4 rows
 constexpr int PR_RING = 4;  // key groups in flight per wave
 constexpr int PR_CHUNK_PAGES = kWave;
 
-template <int NT, bool TWO>
-__device__ __forceinline__ void pair_rows_range(const IndexerArgs& a, const QOperand<NT>& qa,
-                                                const QOperand<NT>& qb, float* ra, float* rb, int na, int nb,
-                                                const int32_t* bt_row, int kb, int ke) {
+// Score R rows (R = 1, 2 or 4, all reading block-table row bt_row) over the
+// keys [kb, ke) of one chunk; row r's scores go to rows[r][j] for j < n[r].
+template <int NT, int R>
+__device__ __forceinline__ void rows_range(const IndexerArgs& a, const QOperand<NT> (&q)[R], float* const (&rows)[R],
+                                           const int (&n)[R], const int32_t* bt_row, int kb, int ke) {
   const uint32_t P = static_cast<uint32_t>(a.page_size);
   const int l = lane_id();
   const int c = l & 15, g = l >> 4;
@@ -187,9 +197,7 @@ __device__ __forceinline__ void pair_rows_range(const IndexerArgs& a, const QOpe
   // [32g, 32g + 32) of token c) and the token's scale. The group lies in one
   // page, and tokens past ke read that page's bytes. Keys come mostly from
   // the caches here (many rows read them), so the operand layout is loaded
-  // directly rather than as whole lines plus a permute: fewer instructions
-  // in a loop that instruction issue bounds (5.75 vs 6.01 ms on the prefill
-  // workload).
+  // directly rather than as whole lines plus a permute: fewer instructions.
   auto fetch = [&](int gi, KeyPieces& kp, float& ks) {
     const int j0 = kb + gi * kGroup;
     const uint32_t pg = fdiv(static_cast<uint32_t>(j0), a.pdiv);
@@ -201,17 +209,21 @@ __device__ __forceinline__ void pair_rows_range(const IndexerArgs& a, const QOpe
     kp.x1 = load_v4i_stream(kp0 + 16);
     ks = a.k_scale[s0 + c];
   };
-  auto consume = [&](int gi, float sa, float sb) {
+  // lane group g holds row (g % R)'s scores; groups g >= R repeat rows
+  float* const dst = rows[g % R];
+  const int nd = n[g % R];
+  const bool writer = g < R;
+  auto consume = [&](int gi, float sc) {
     const int j = kb + gi * kGroup + c;
-    if (g == 0 && j < na) ra[j] = sa;
-    if (TWO && g == 1 && j < nb) rb[j] = sb;
+    if (writer && j < nd) dst[j] = sc;
   };
-  auto score2 = [&](const KeyPieces& kp, float ks, float& sa, float& sb) {
+  auto score = [&](const KeyPieces& kp, float ks) {
     v8i kbv;
     kbv[0] = kp.x0[0]; kbv[1] = kp.x0[1]; kbv[2] = kp.x0[2]; kbv[3] = kp.x0[3];
     kbv[4] = kp.x1[0]; kbv[5] = kp.x1[1]; kbv[6] = kp.x1[2]; kbv[7] = kp.x1[3];
-    sa = score16<NT>(qa, kbv, ks);
-    sb = TWO ? score16<NT>(qb, kbv, ks) : 0.0f;
+    if constexpr (R == 4) return score16x4<NT>(q, kbv, ks);
+    else if constexpr (R == 2) return score16x2<NT>(q[0], q[1], kbv, ks);
+    else return score16<NT>(q[0], kbv, ks);
   };
 
   typedef float vks __attribute__((ext_vector_type(PR_RING)));
@@ -228,40 +240,54 @@ __device__ __forceinline__ void pair_rows_range(const IndexerArgs& a, const QOpe
   for (; gi0 + 2 * PR_RING <= ngroups; gi0 += PR_RING) {
 #pragma unroll
     for (int u = 0; u < PR_RING; ++u) {
-      float sa, sb;
-      score2(ring[u], ksr[u], sa, sb);
-      // the scores are final before the slot is refilled (see score_chunk)
-      asm volatile("" : "+v"(sa), "+v"(sb));
+      float sc = score(ring[u], ksr[u]);
+      // the score is final before the slot is refilled (see score_chunk)
+      asm volatile("" : "+v"(sc));
       __builtin_amdgcn_sched_barrier(0);
       float t;
       fetch(gi0 + u + PR_RING, ring[u], t);
       ksr[u] = t;
-      consume(gi0 + u, sa, sb);
+      consume(gi0 + u, sc);
     }
   }
 #pragma unroll
   for (int u = 0; u < PR_RING; ++u) {
     const int gi = gi0 + u;
     if (gi < ngroups) {
-      float sa, sb;
-      score2(ring[u], ksr[u], sa, sb);
+      const float sc = score(ring[u], ksr[u]);
       if (gi + PR_RING < ngroups) {
         float t;
         fetch(gi + PR_RING, ring[u], t);
         ksr[u] = t;
       }
-      consume(gi, sa, sb);
+      consume(gi, sc);
     }
   }
 #pragma unroll
   for (int u = 0; u < PR_RING; ++u) {
     const int gi = gi0 + PR_RING + u;
-    if (gi < ngroups) {
-      float sa, sb;
-      score2(ring[u], ksr[u], sa, sb);
-      consume(gi, sa, sb);
-    }
+    if (gi < ngroups) consume(gi, score(ring[u], ksr[u]));
   }
+}
+
+template <int NT, int R>
+__device__ __forceinline__ void score_rows(const IndexerArgs& a, float* scores, int64_t sstride, int b0,
+                                           const int (&nn)[4], const int (&pr)[4], int i0, int kb, int chunk) {
+  QOperand<NT> q[R];
+  float* rows[R];
+  int n[R];
+  int nmax = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int b = b0 + i0 + r;
+    load_query<NT>(q[r], a.q + static_cast<int64_t>(b) * a.heads * kDim, a.w + static_cast<int64_t>(b) * a.heads,
+                   a.q_scale[b]);
+    rows[r] = scores + static_cast<int64_t>(b) * sstride;
+    n[r] = nn[i0 + r];
+    nmax = max(nmax, n[r]);
+  }
+  const int ke = min(kb + chunk, nmax);
+  if (kb < ke) rows_range<NT, R>(a, q, rows, n, a.block_table + static_cast<int64_t>(pr[i0]) * a.bt_stride, kb, ke);
 }
 
 template <int NT>
@@ -269,38 +295,28 @@ __global__ __launch_bounds__(PR_WG) void pair_score_kernel(IndexerArgs a, float*
                                                            int ntiles, int chunk) {
   const int tile = blockIdx.x % ntiles;
   const int kc = blockIdx.x / ntiles;
-  const int pair = tile * (PR_WG / kWave) + uniform(static_cast<int>(threadIdx.x) / kWave);
-  const int ba = 2 * pair, bb = ba + 1;
-  if (ba >= a.batch) return;
-  const bool has_b = bb < a.batch;
-  const int na = load_uniform(a.seq_lens + ba);
-  const int nb = has_b ? load_uniform(a.seq_lens + bb) : 0;
-  const int pa = a.row_to_batch ? load_uniform(a.row_to_batch + ba) : ba;
-  const int pb = has_b ? (a.row_to_batch ? load_uniform(a.row_to_batch + bb) : bb) : pa;
+  const int quad = tile * (PR_WG / kWave) + uniform(static_cast<int>(threadIdx.x) / kWave);
+  const int b0 = 4 * quad;
+  if (b0 >= a.batch) return;
+  const int nr = min(4, a.batch - b0);
+  int nn[4], pr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = b0 + (i < nr ? i : 0);
+    nn[i] = i < nr ? load_uniform(a.seq_lens + b) : 0;
+    pr[i] = a.row_to_batch ? load_uniform(a.row_to_batch + b) : b;
+  }
   const int kb = kc * chunk;
-  float* ra = scores + static_cast<int64_t>(ba) * sstride;
-  float* rb = scores + static_cast<int64_t>(bb) * sstride;
-  const int32_t* bta = a.block_table + static_cast<int64_t>(pa) * a.bt_stride;
-  if (has_b && pa == pb) {
-    const int ke = min(kb + chunk, max(na, nb));
-    if (kb >= ke) return;
-    QOperand<NT> qa, qb;
-    load_query<NT>(qa, a.q + static_cast<int64_t>(ba) * a.heads * kDim, a.w + static_cast<int64_t>(ba) * a.heads,
-                   a.q_scale[ba]);
-    load_query<NT>(qb, a.q + static_cast<int64_t>(bb) * a.heads * kDim, a.w + static_cast<int64_t>(bb) * a.heads,
-                   a.q_scale[bb]);
-    pair_rows_range<NT, true>(a, qa, qb, ra, rb, na, nb, bta, kb, ke);
-  } else {
-    for (int r = 0; r < (has_b ? 2 : 1); ++r) {
-      const int b = r ? bb : ba;
-      const int n = r ? nb : na;
-      const int ke = min(kb + chunk, n);
-      if (kb >= ke) continue;
-      QOperand<NT> q1;
-      load_query<NT>(q1, a.q + static_cast<int64_t>(b) * a.heads * kDim, a.w + static_cast<int64_t>(b) * a.heads,
-                     a.q_scale[b]);
-      pair_rows_range<NT, false>(a, q1, q1, r ? rb : ra, r ? rb : ra, n, 0,
-                                 a.block_table + static_cast<int64_t>(r ? pb : pa) * a.bt_stride, kb, ke);
+  if (nr == 4 && pr[0] == pr[1] && pr[1] == pr[2] && pr[2] == pr[3]) {
+    score_rows<NT, 4>(a, scores, sstride, b0, nn, pr, 0, kb, chunk);
+    return;
+  }
+  for (int i0 = 0; i0 < nr; i0 += 2) {
+    if (i0 + 1 < nr && pr[i0] == pr[i0 + 1]) {
+      score_rows<NT, 2>(a, scores, sstride, b0, nn, pr, i0, kb, chunk);
+    } else {
+      score_rows<NT, 1>(a, scores, sstride, b0, nn, pr, i0, kb, chunk);
+      if (i0 + 1 < nr) score_rows<NT, 1>(a, scores, sstride, b0, nn, pr, i0 + 1, kb, chunk);
     }
   }
 }
@@ -1156,8 +1172,8 @@ int launch_idx_score(const IndexerInputs& in, float* scores, int64_t score_strid
     int64_t chunk = static_cast<int64_t>(PR_CHUNK_PAGES) * in.page_size;
     if (chunk > 8192) chunk = 8192 / in.page_size * in.page_size;
     const IndexerArgs a = make_args(in, static_cast<int>(chunk), false);
-    const int pairs = (in.batch + 1) / 2;
-    const int ntiles = (pairs + PR_WG / kWave - 1) / (PR_WG / kWave);
+    const int quads = (in.batch + 3) / 4;
+    const int ntiles = (quads + PR_WG / kWave - 1) / (PR_WG / kWave);
     const int nkc = static_cast<int>((static_cast<int64_t>(in.max_seq_len > 0 ? in.max_seq_len : 1) + chunk - 1) / chunk);
     const dim3 grid(static_cast<unsigned>(ntiles * nkc));
     (void)hipGetLastError();

@@ -165,6 +165,72 @@ __device__ __forceinline__ float score16(const QOperand<NT>& qo, const v8i kb, f
   return part * ks;
 }
 
+// Scores of token (tok0 + (lane & 15)) for two query rows against one key
+// operand: lanes 0-15 and 32-47 return row A's, lanes 16-31 and 48-63 row
+// B's. The permlane16 swap of A's partial sums against B's leaves A's and
+// B's pairwise sums in alternate 16-lane rows, so one permlane32 swap
+// finishes both; each row is summed in the same order as score16, so the
+// results are bit-identical to it.
+template <int NT>
+__device__ __forceinline__ float score16x2(const QOperand<NT>& qa, const QOperand<NT>& qb, const v8i kb,
+                                           float ks) {
+  v4f acc[2][NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    acc[0][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa.a[t], kb, zero, 0, 0, 0, 0, 0, 0);
+    acc[1][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qb.a[t], kb, zero, 0, 0, 0, 0, 0, 0);
+  }
+  float pa = 0.0f, pb = 0.0f;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pa = fmaf(qa.wt[t][r], relu_bits(acc[0][t][r]), pa);
+      pb = fmaf(qb.wt[t][r], relu_bits(acc[1][t][r]), pb);
+    }
+  }
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(pa), __float_as_uint(pb), false, false);
+  float part = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
+                                                    false, false);
+  part = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+  return part * ks;
+}
+
+// Scores of token (tok0 + (lane & 15)) for four query rows against one key
+// operand: lane group g (lanes 16g..16g+15) returns row g's. Two permlane16
+// swaps (rows 0 with 1, rows 2 with 3) and one permlane32 swap put every
+// row's four 16-lane partial sums together, in score16's order, so the
+// results are bit-identical to it.
+template <int NT>
+__device__ __forceinline__ float score16x4(const QOperand<NT> (&q)[4], const v8i kb, float ks) {
+  v4f acc[4][NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+      acc[r][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q[r].a[t], kb, zero, 0, 0, 0, 0, 0, 0);
+    }
+  }
+  float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = fmaf(q[r].wt[t][i], relu_bits(acc[r][t][i]), p[r]);
+    }
+  }
+  const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(p[0]), __float_as_uint(p[1]), false, false);
+  const auto s23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(p[2]), __float_as_uint(p[3]), false, false);
+  const float x = __uint_as_float(s01[0]) + __uint_as_float(s01[1]);
+  const float y = __uint_as_float(s23[0]) + __uint_as_float(s23[1]);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return (__uint_as_float(s32[0]) + __uint_as_float(s32[1])) * ks;
+}
+
 // Max number of page ids a chunk stages in LDS.
 constexpr int kMaxChunkPages = 1024;
 
