@@ -559,6 +559,7 @@ __device__ __forceinline__ void positions_to_slots(const IndexerArgs& a, int b, 
 }
 
 constexpr int MG_BATCH = 8;  // candidates per thread per pass of the merge
+constexpr int WS_PER = 16;   // threshold-bin keys per lane when one wave selects
 
 // One workgroup per row. The row's histogram is complete now (previous
 // kernel), so it names the exact threshold bin: candidates above it are
@@ -611,7 +612,23 @@ __global__ __launch_bounds__(MG_WG) void fused_merge_kernel(IndexerArgs a, Fused
   }
   __syncthreads();
   const uint32_t nb = s.bcnt;
-  if (!th.all && nb > 0) {
+  if (!th.all && nb > 0 && nb <= static_cast<uint32_t>(kWave * WS_PER)) {
+    // a small threshold bin: wave 0 alone selects and emits it
+    if (tid < kWave) {
+      uint64_t keys[WS_PER];
+      bool valid[WS_PER], keep[WS_PER];
+#pragma unroll
+      for (int e = 0; e < WS_PER; ++e) {
+        const uint32_t i = e * kWave + tid;
+        valid[e] = i < nb;
+        keys[e] = valid[e] ? s.buf[i] : 0ull;
+      }
+      const uint64_t T = nb > need ? wave_select<WS_PER>(keys, valid, need, s.sel.hist) : 0ull;
+#pragma unroll
+      for (int e = 0; e < WS_PER; ++e) keep[e] = valid[e] && keys[e] >= T;
+      emit_batch<WS_PER>(keys, keep, b, o, &s.ocnt);
+    }
+  } else if (!th.all && nb > 0) {
     if (nb <= static_cast<uint32_t>(MG_BUF)) {
       uint64_t keys[MG_MAXE];
       int nvk = 0;
@@ -897,7 +914,24 @@ __device__ __forceinline__ void fused_scores_merge_row(const IndexerArgs& a, con
   }
   __syncthreads();
   const uint32_t nb = s.bcnt;
-  if (!th.all && nb > 0) {
+  if (!th.all && nb > 0 && nb <= static_cast<uint32_t>(kWave * WS_PER)) {
+    // a small threshold bin: wave 0 alone selects and emits it (no
+    // workgroup barrier inside the select)
+    if (tid < kWave) {
+      uint64_t keys[WS_PER];
+      bool valid[WS_PER], keep[WS_PER];
+#pragma unroll
+      for (int e = 0; e < WS_PER; ++e) {
+        const uint32_t i = e * kWave + tid;
+        valid[e] = i < nb;
+        keys[e] = valid[e] ? s.buf[i] : 0ull;
+      }
+      const uint64_t T = nb > need ? wave_select<WS_PER>(keys, valid, need, s.sel.hist) : 0ull;
+#pragma unroll
+      for (int e = 0; e < WS_PER; ++e) keep[e] = valid[e] && keys[e] >= T;
+      emit(keys, keep, WS_PER);
+    }
+  } else if (!th.all && nb > 0) {
     if (nb <= static_cast<uint32_t>(FS_BUF)) {
       uint64_t keys[FS_MAXE];
       bool keep[FS_MAXE];

@@ -186,6 +186,70 @@ __device__ __forceinline__ uint64_t wg_select(ForEach&& for_each, uint32_t k, ui
   return lo;
 }
 
+// k-th largest of at most PER * 64 DISTINCT 64-bit keys held by one wave
+// (key[e] counts where valid[e]), with 1 <= k < the number of keys: returns
+// T such that exactly k keys are >= T. Wave-synchronous, no workgroup
+// barrier: `hist` is 256 words of LDS that only this wave uses.
+//
+// Method as wg_select's, with 256 bins per round: histogram the keys in
+// [lo, hi] into 256 equal bins, find the bin where the count from the top
+// reaches the remaining rank, narrow [lo, hi] to it. Each round shrinks the
+// range by 2^8, so at most 8 rounds run on 64-bit keys. The wave's LDS
+// operations complete in order, so no barrier separates the rounds.
+template <int PER>
+__device__ __forceinline__ uint64_t wave_select(const uint64_t (&key)[PER], const bool (&valid)[PER], uint32_t k,
+                                                uint32_t* hist) {
+  const int lane = lane_id();
+  uint64_t lo = ~0ull, hi = 0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e)
+    if (valid[e]) {
+      lo = key[e] < lo ? key[e] : lo;
+      hi = key[e] > hi ? key[e] : hi;
+    }
+  lo = wave_min_u64(lo);
+  hi = wave_max_u64(hi);
+  uint32_t kk = k;
+  for (int it = 0; it < 8; ++it) {
+    const uint64_t span = hi - lo;
+    if (span == 0) break;  // one key left, and it is the k-th
+    const int bits = 64 - __clzll(span);
+    const int shift = bits > 8 ? bits - 8 : 0;
+    reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+      if (valid[e] && key[e] >= lo && key[e] <= hi) atomicAdd(&hist[static_cast<uint32_t>((key[e] - lo) >> shift)], 1u);
+    const uint4 c4 = reinterpret_cast<const uint4*>(hist)[lane];  // bins 4 lane .. 4 lane + 3
+    const uint32_t c[4] = {c4.x, c4.y, c4.z, c4.w};
+    const uint32_t local = c[0] + c[1] + c[2] + c[3];
+    const uint32_t incl = wave_prefix_incl(local);
+    const uint32_t tot = __builtin_amdgcn_readlane(incl, kWave - 1);
+    const uint32_t above_l = tot - incl;  // keys in the bins of higher lanes
+    // the lane whose bins hold the kk-th key from the top
+    const bool mine = above_l < kk && above_l + local >= kk;
+    uint32_t bin = 0, above = above_l, cnt = 0;
+    if (mine) {
+      int i = 3;
+      for (; i > 0; --i) {
+        if (above + c[i] >= kk) break;
+        above += c[i];
+      }
+      bin = 4 * lane + i;
+      cnt = c[i];
+    }
+    const int src = __builtin_ctzll(ballot(mine));
+    bin = __builtin_amdgcn_readlane(bin, src);
+    above = __builtin_amdgcn_readlane(above, src);
+    cnt = __builtin_amdgcn_readlane(cnt, src);
+    kk -= above;
+    lo += static_cast<uint64_t>(bin) << shift;
+    const uint64_t top = lo + ((1ull << shift) - 1ull);
+    hi = top < hi ? top : hi;
+    if (cnt == kk) break;  // every key of the bin is taken: keys >= lo are exactly k
+  }
+  return lo;
+}
+
 // Threshold bin of a histogram for rank k: the highest bin b with
 // sum(bins >= b) >= k. Returns above = sum(bins > b) and the total count.
 // When total < k, returns bin 0 with all=true (everything is selected).
