@@ -111,7 +111,24 @@ size_t block_workspace_bytes(int rows, int block_size, int max_seq_len) {
 // the XCD count) and the XCDs holding the longest rows would finish last. The
 // row index is therefore rotated by the chunk index: a row's chunks land on
 // every XCD in turn.
+//
+// With quad_map, rows 4q..4q+3 (query rows of one request sit next to each
+// other and read the same keys) take the same chunk on one XCD back to back:
+// quad-slot Q = (quad, chunk) maps to workgroups 32 (Q / 8) + Q % 8 + 8 r,
+// r = 0..3, which the dispatcher sends to XCD Q % 8 one after another, so the
+// XCD's L2 fetches the chunk's keys once for all four. Quad-slots past the
+// grid's chunks get a chunk index >= nchunk_max, whose span starts past
+// every row's end.
 __device__ __forceinline__ void chunk_of(const IndexerArgs& a, int& b, int& c) {
+  if (a.quad_map) {
+    const int i = blockIdx.x;
+    const int r = (i >> 3) & 3;
+    const int Q = ((i >> 5) << 3) | (i & 7);
+    const int nq = a.batch >> 2;
+    c = Q / nq;
+    b = 4 * ((Q + c) % nq) + r;
+    return;
+  }
   c = blockIdx.x / a.batch;
   b = (blockIdx.x + c) % a.batch;
 }
@@ -1152,6 +1169,7 @@ static IndexerArgs make_args(const IndexerInputs& in, int chunk, bool guided = f
   a.batch = in.batch;
   a.heads = in.heads;
   a.chunk = chunk;
+  a.quad_map = in.row_to_batch != nullptr && in.batch % 4 == 0 && in.batch >= 8;
   const int msl = in.max_seq_len > 0 ? in.max_seq_len : 1;
   // Guided schedule when quarter chunks stay large (and aligned): full-size
   // chunks up to half the longest row, halves up to three quarters, then
@@ -1170,6 +1188,13 @@ static IndexerArgs make_args(const IndexerInputs& in, int chunk, bool guided = f
     a.nchunk_max = a.n_full;
   }
   return a;
+}
+
+// Workgroups of a chunk-major grid (chunk_of): every (row, chunk) pair, in
+// whole groups of 32 under quad_map.
+static unsigned chunk_grid(const IndexerArgs& a) {
+  const int64_t n = static_cast<int64_t>(a.nchunk_max) * a.batch;
+  return static_cast<unsigned>(a.quad_map ? (n + 31) / 32 * 32 : n);
 }
 
 // Tokens per workgroup: aim for ~2048 workgroups over the whole batch, keep
@@ -1220,7 +1245,7 @@ int launch_idx_score(const IndexerInputs& in, float* scores, int64_t score_strid
   }
   const int chunk = choose_chunk(in.batch, in.max_seq_len, in.page_size, kGroup, 512, 8192);
   const IndexerArgs a = make_args(in, chunk, true);
-  const dim3 grid(static_cast<unsigned>(a.nchunk_max * in.batch));
+  const dim3 grid(chunk_grid(a));
   (void)hipGetLastError();
   IDXTOPK_DISPATCH_NT(score_kernel, in.heads, grid, stream, a, scores, score_stride);
   return hipGetLastError() == hipSuccess ? 0 : -4;
@@ -1262,7 +1287,7 @@ static int launch_fused_scores(const IndexerInputs& in, const FusedWs& w, const 
   const int64_t page_cap = (static_cast<int64_t>(IX_PAGES - 2) * in.page_size) / kGroup * kGroup;
   if (ch > page_cap) ch = page_cap > kGroup ? page_cap : kGroup;
   const IndexerArgs a = make_args(in, static_cast<int>(ch), false);
-  const dim3 grid(static_cast<unsigned>(a.nchunk_max * in.batch));
+  const dim3 grid(chunk_grid(a));
   const size_t lds = static_cast<size_t>(ch) * sizeof(float);
   (void)hipGetLastError();
   IDXTOPK_DISPATCH_NT_LDS(fused_scores_chunk_kernel, in.heads, grid, lds, stream, a, w);
@@ -1287,7 +1312,7 @@ int launch_fused(const IndexerInputs& in, int k, int32_t* out_slots, float* out_
   o.slots = out_slots;
   o.scores = out_scores;
   o.k = k;
-  const dim3 grid(static_cast<unsigned>(a.nchunk_max * in.batch));
+  const dim3 grid(chunk_grid(a));
   (void)hipGetLastError();
   // the scores' dynamic LDS plus the static part stay within 64 KB
   static_assert(FU_CH_MAX * 4 + sizeof(ChunkLds) <= 64 * 1024, "fused chunk LDS");
@@ -1343,7 +1368,7 @@ int launch_block_topk(const IndexerInputs& in, int block_size, int top_blocks, i
   o.slots = out_slots;
   o.top = top_blocks;
   o.bs = block_size;
-  const dim3 grid(static_cast<unsigned>(a.nchunk_max * in.batch));
+  const dim3 grid(chunk_grid(a));
   (void)hipGetLastError();
   IDXTOPK_DISPATCH_NT(block_chunk_kernel, in.heads, grid, stream, a, w, block_size);
   hipLaunchKernelGGL(block_merge_kernel, dim3(in.batch), dim3(MG_WG), 0, stream, a, w, o);

@@ -55,6 +55,10 @@ struct IndexerArgs {
   int32_t n_half;
   int32_t tok_half;
   int32_t tok_quarter;
+  // Nonzero: consecutive query rows may share block-table rows, and the grid
+  // deals (row, chunk) pairs to workgroups in quads of rows (batch % 4 == 0,
+  // grid rounded up to a multiple of 32).
+  int32_t quad_map;
 };
 
 struct KeyPieces {
