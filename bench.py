@@ -55,7 +55,7 @@ COPY_CALIBRATION_BYTES = 1 << 30
 SETTLE_SECONDS = 0.25
 COUNTERS_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
-    "topk_rows": ["topk_rows.hip", "select.hpp", "common.hpp"],
+    "topk_rows": ["topk_rows.hip", "select.hpp", "sort.hpp", "common.hpp"],
     "fused": ["indexer.hip", "score_mfma.hpp", "select.hpp", "common.hpp"],
 }
 
@@ -74,7 +74,7 @@ def source_hash(kind: str) -> str:
 
 PMC_KERNELS = {
     # counters file name -> (source kind, kernel name prefix, grid size of the workload's launch)
-    "topk_rows_packed_prefill_16384x70001": ("topk_rows", "idxtopk::topk_rows_kernel", 16384 * 256),
+    "topk_rows_packed_prefill_16384x70001": ("topk_rows", "void idxtopk::topk_rows_kernel<false>", 16384 * 256),
     "fused_long_decode_B64_k2048": ("fused", "void idxtopk::fused_chunk_kernel", None),
 }
 
@@ -277,7 +277,7 @@ def dev(torch, a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def bench_rows(torch, ops, timer, case, warmup, steps, flush):
+def bench_rows(torch, ops, timer, case, warmup, steps, flush, sorted=False):
     sc = dev(torch, case.scores)
     sl = dev(torch, case.seq_lens)
     rs = None if case.row_starts is None else dev(torch, case.row_starts)
@@ -286,7 +286,7 @@ def bench_rows(torch, ops, timer, case, warmup, steps, flush):
     out = torch.empty((case.rows, case.k), dtype=torch.int32, device="cuda")
 
     def step():
-        ops.topk_rows(sc, sl, case.k, rs, rb, pt, case.page_size, out=out)
+        ops.topk_rows(sc, sl, case.k, rs, rb, pt, case.page_size, out=out, sorted=sorted)
 
     wall, us, region = timer.run(step, warmup, steps, flush)
     res = summary(us, rows_algorithmic_bytes(case), case.rows, region, timer.settled)
@@ -295,14 +295,15 @@ def bench_rows(torch, ops, timer, case, warmup, steps, flush):
     return wall, us, res
 
 
-def bench_fused(torch, ops, timer, case, warmup, steps, flush):
+def bench_fused(torch, ops, timer, case, warmup, steps, flush, sorted=False):
     args = [dev(torch, x) for x in (case.q, case.q_scale, case.w, case.kcache, case.k_scale,
                                     case.block_table, case.seq_lens)]
     out = torch.empty((case.batch, case.k), dtype=torch.int32, device="cuda")
     ws = ops.Workspace()
 
     def step():
-        ops.idx_score_topk_fused(*args, case.page_size, case.max_seq_len, case.k, workspace=ws, out=out)
+        ops.idx_score_topk_fused(*args, case.page_size, case.max_seq_len, case.k, workspace=ws, out=out,
+                                 sorted=sorted)
 
     wall, us, region = timer.run(step, warmup, steps, flush)
     res = summary(us, indexer_algorithmic_bytes(case, case.batch * case.k), case.batch, region, timer.settled)
@@ -525,6 +526,9 @@ def main(argv=None):
             "us_per_launch_median": res["us_per_launch_median"],
             "achieved_GBps": res["achieved_GBps"],
         }
+        log("timing packed-prefill top-k, sorted output ...")
+        _, _, also["packed_prefill_topk_sorted"] = bench_rows(torch, ops, timer, case3, a.warmup, a.steps,
+                                                              flush=False, sorted=True)
         del case3
     if "c1" in only:
         log("timing decode top-k ...")
@@ -535,6 +539,9 @@ def main(argv=None):
         log("timing fused decode B32 ...")
         c2 = workloads.c2_fused_decode()
         also["fused_decode_B32_k2048"] = bench_fused(torch, ops, timer, c2, a.warmup, max(a.steps, 50), True)
+        log("timing fused decode B32, sorted output ...")
+        also["fused_decode_B32_k2048_sorted"] = bench_fused(torch, ops, timer, c2, a.warmup, max(a.steps, 50), True,
+                                                            sorted=True)
         log("timing fused decode B32, unfused path ...")
         also["fused_decode_B32_k2048_unfused"] = bench_unfused(torch, ops, timer, c2, a.warmup, max(a.steps, 50),
                                                                True)

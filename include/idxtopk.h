@@ -61,6 +61,13 @@ extern "C" {
 #define IDXTOPK_DIM 128           /* index-key / query head dimension */
 #define IDXTOPK_MAX_K_ROWS 8192   /* topk_rows */
 #define IDXTOPK_MAX_K_FUSED 8192  /* idx_score_topk_fused */
+
+/* flags of topk_rows and idx_score_topk_fused */
+#define IDXTOPK_SORTED 1  /* each output row in descending score order, equal
+                             scores by ascending row-local position, -1
+                             padding last (the sorted-output variant of the
+                             selection; [SGL-37889] Modifications keeps the
+                             selected index row-local until the transform) */
 #define IDXTOPK_MAX_TOP_BLOCKS 4096 /* block_topk */
 
 /* Operation ids for idxtopk_workspace_bytes(). */
@@ -142,12 +149,15 @@ int idx_score_fp8(const uint8_t* q, const float* q_scale, const float* w,
  * p % page_size, or the positions themselves when page_table is NULL; -1 pads
  * rows with seq_lens[i] < k.
  *
+ * flags: 0, or IDXTOPK_SORTED for rows in sorted order (otherwise the order
+ * within a row is unspecified); any other bit gives IDXTOPK_EINVAL.
+ *
  * 1 <= k <= IDXTOPK_MAX_K_ROWS. No workspace.
  */
 int topk_rows(const float* scores, int64_t score_stride, int32_t rows,
               const int32_t* seq_lens, const int32_t* row_starts, const int32_t* row_to_batch,
               const int32_t* page_table, int64_t pt_stride, int32_t page_size,
-              int32_t k, int32_t* out, void* stream);
+              int32_t k, int32_t* out, int32_t flags, void* stream);
 
 /*
  * topk_page_transform -- map row-local positions to physical slots.
@@ -180,6 +190,9 @@ int topk_page_transform(const int32_t* idx, int32_t rows, int32_t k,
  *            bytes. It MUST be zero-filled before its first use, and every
  *            call leaves it zero-filled again. Concurrent calls must not
  *            share one workspace.
+ * flags      0, or IDXTOPK_SORTED (out_slots and out_scores in sorted order;
+ *            otherwise the order within a row is unspecified); any other
+ *            bit gives IDXTOPK_EINVAL.
  * 1 <= k <= IDXTOPK_MAX_K_FUSED.
  */
 int idx_score_topk_fused(const uint8_t* q, const float* q_scale, const float* w,
@@ -188,7 +201,7 @@ int idx_score_topk_fused(const uint8_t* q, const float* q_scale, const float* w,
                          const int32_t* row_to_batch, const int32_t* seq_lens, int32_t batch,
                          int32_t heads, int32_t dim, int32_t max_seq_len, int32_t k,
                          int32_t* out_slots, float* out_scores, void* workspace,
-                         size_t workspace_bytes, void* stream);
+                         size_t workspace_bytes, int32_t flags, void* stream);
 
 /*
  * block_topk -- block-sparse variant: block scores, top blocks, sparse list.

@@ -86,6 +86,10 @@ def topk_order(values: np.ndarray, k: int) -> np.ndarray:
     READING: the pages give no tie rule. Ties go to the lower position, and
     rows shorter than k are padded with -1. [SGL-37889], Modifications: the
     selected index stays row-local until the transform.
+
+    The outputs come in that sort's order (value descending, equal values by
+    ascending position, padding last), which is also the order of the
+    library's sorted-output variant.
     """
     v = _f64(values).reshape(-1)
     if np.isnan(v).any():

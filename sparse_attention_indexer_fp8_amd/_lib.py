@@ -26,6 +26,7 @@ OP_BLOCK_TOPK = 5
 OP_CACHE_WRITE = 6
 KEY_F32 = 0
 KEY_BF16 = 1
+SORTED = 1
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -36,10 +37,10 @@ _sz = ctypes.c_size_t
 SIGNATURES = {
     "idx_score_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32, _i32,
                              _i32, _vp, _i64, _vp]),
-    "topk_rows": (_i32, [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp]),
+    "topk_rows": (_i32, [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _i32, _vp]),
     "topk_page_transform": (_i32, [_vp, _i32, _i32, _vp, _i64, _i32, _vp, _vp, _vp]),
     "idx_score_topk_fused": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32,
-                                    _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
+                                    _i32, _i32, _i32, _vp, _vp, _vp, _sz, _i32, _vp]),
     "block_topk": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                           _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "idx_cache_write": (_i32, [_vp, _i32, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),

@@ -71,15 +71,15 @@ int idx_score_fp8(const uint8_t* q, const float* q_scale, const float* w, const 
 
 int topk_rows(const float* scores, int64_t score_stride, int32_t rows, const int32_t* seq_lens,
               const int32_t* row_starts, const int32_t* row_to_batch, const int32_t* page_table,
-              int64_t pt_stride, int32_t page_size, int32_t k, int32_t* out, void* stream) {
-  if (rows < 0 || k <= 0 || score_stride < 0) return IDXTOPK_EINVAL;
+              int64_t pt_stride, int32_t page_size, int32_t k, int32_t* out, int32_t flags, void* stream) {
+  if (rows < 0 || k <= 0 || score_stride < 0 || (flags & ~IDXTOPK_SORTED)) return IDXTOPK_EINVAL;
   if (rows > 0 && (!scores || !seq_lens || !out)) return IDXTOPK_EINVAL;
   if (page_table && (pt_stride < 0 || page_size <= 0)) return IDXTOPK_EINVAL;
   if (k > IDXTOPK_MAX_K_ROWS) return IDXTOPK_EUNSUPPORTED;
   if (rows == 0) return IDXTOPK_OK;
   return idxtopk::launch_topk_rows(scores, score_stride, rows, seq_lens, row_starts, row_to_batch,
                                    page_table, pt_stride, page_table ? page_size : 1, k, out,
-                                   static_cast<hipStream_t>(stream));
+                                   (flags & IDXTOPK_SORTED) != 0, static_cast<hipStream_t>(stream));
 }
 
 int topk_page_transform(const int32_t* idx, int32_t rows, int32_t k, const int32_t* page_table,
@@ -97,7 +97,8 @@ int idx_score_topk_fused(const uint8_t* q, const float* q_scale, const float* w,
                          int64_t bt_stride, int32_t page_size, const int32_t* row_to_batch,
                          const int32_t* seq_lens, int32_t batch, int32_t heads, int32_t dim, int32_t max_seq_len, int32_t k,
                          int32_t* out_slots, float* out_scores, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+                         size_t workspace_bytes, int32_t flags, void* stream) {
+  if (flags & ~IDXTOPK_SORTED) return IDXTOPK_EINVAL;
   const int st = check_indexer(q, q_scale, w, kcache, k_scale, block_table, bt_stride, page_size,
                                seq_lens, batch, heads, dim, max_seq_len);
   if (st != IDXTOPK_OK) return st;
@@ -108,7 +109,7 @@ int idx_score_topk_fused(const uint8_t* q, const float* q_scale, const float* w,
     return IDXTOPK_EWORKSPACE;
   return idxtopk::launch_fused(pack(q, q_scale, w, kcache, k_scale, block_table, bt_stride,
                                     page_size, row_to_batch, seq_lens, batch, heads, max_seq_len),
-                               k, out_slots, out_scores, workspace,
+                               k, out_slots, out_scores, workspace, (flags & IDXTOPK_SORTED) != 0,
                                static_cast<hipStream_t>(stream));
 }
 

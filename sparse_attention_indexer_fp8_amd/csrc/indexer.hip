@@ -63,6 +63,7 @@ struct FusedWs {
   uint32_t* ctr;   // [rows][4]: candidate count, done chunks
   uint64_t* cand;  // [rows][cap]
   int64_t cap;
+  float* sval;     // [rows][k]: scores of the selection for the sort pass
 };
 
 static inline FusedWs fused_ws(void* base, int rows, int max_seq_len) {
@@ -74,14 +75,15 @@ static inline FusedWs fused_ws(void* base, int rows, int max_seq_len) {
   p += align256(static_cast<size_t>(rows) * 16);
   w.cand = reinterpret_cast<uint64_t*>(p);
   w.cap = max_seq_len > 0 ? max_seq_len : 1;
+  p += align256(static_cast<size_t>(rows) * w.cap * 8);
+  w.sval = reinterpret_cast<float*>(p);
   return w;
 }
 
 size_t fused_workspace_bytes(int rows, int k, int max_seq_len) {
-  (void)k;
   const int64_t cap = max_seq_len > 0 ? max_seq_len : 1;
   return align256(static_cast<size_t>(rows) * HIST_BINS * 4) + align256(static_cast<size_t>(rows) * 16) +
-         align256(static_cast<size_t>(rows) * cap * 8);
+         align256(static_cast<size_t>(rows) * cap * 8) + align256(static_cast<size_t>(rows) * k * 4);
 }
 
 struct BlockWs {
@@ -380,6 +382,7 @@ struct FusedOut {
   int32_t* slots;
   float* scores;
   int k;
+  int keep_positions;  // leave row-local positions in `slots` (the sort pass maps them)
 };
 
 // Dynamic LDS: the chunk's scores (a.chunk floats).
@@ -710,7 +713,7 @@ __global__ __launch_bounds__(MG_WG) void fused_merge_kernel(IndexerArgs a, Fused
     }
   }
   __syncthreads();
-  {
+  if (!o.keep_positions) {
     const int32_t* bt_row = bt_row_of(a, b);
     positions_to_slots<MG_WG, 8>(a, b, o, min(s.ocnt, k), [&](uint32_t pg) { return bt_row[pg]; });
   }
@@ -1008,9 +1011,10 @@ __device__ __forceinline__ void fused_scores_merge_row(const IndexerArgs& a, con
   __syncthreads();
   const uint32_t nout = min(s.ocnt, k);
   // positions -> slots (this workgroup wrote them; the barrier orders it)
-  positions_to_slots<FS_WG, FS_PER>(a, b, o, nout, [&](uint32_t pg) {
-    return STAGED ? s.pages[pg] : bt_row[pg];
-  });
+  if (!o.keep_positions)
+    positions_to_slots<FS_WG, FS_PER>(a, b, o, nout, [&](uint32_t pg) {
+      return STAGED ? s.pages[pg] : bt_row[pg];
+    });
   // padding for rows shorter than k
   for (uint32_t i = nout + tid; i < k; i += FS_WG) {
     o.slots[orow + i] = -1;
@@ -1295,23 +1299,32 @@ static int launch_fused_scores(const IndexerInputs& in, const FusedWs& w, const 
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
+static int launch_fused_select(const IndexerInputs& in, const FusedWs& w, const FusedOut& o, hipStream_t stream);
+
+// Sorted output: the merges leave positions and scores (in the workspace's
+// score area when the caller wants none), then the sort pass orders and maps
+// them and clears that area again.
 int launch_fused(const IndexerInputs& in, int k, int32_t* out_slots, float* out_scores, void* ws,
-                 hipStream_t stream) {
+                 bool sorted, hipStream_t stream) {
   if (in.batch == 0) return 0;
-  if (static_cast<int64_t>(in.batch) * in.max_seq_len <= FS_MAX_TOKENS) {
-    FusedOut o;
-    o.slots = out_slots;
-    o.scores = out_scores;
-    o.k = k;
-    return launch_fused_scores(in, fused_ws(ws, in.batch, in.max_seq_len), o, stream);
-  }
-  const int chunk = choose_chunk(in.batch, in.max_seq_len, in.page_size, kGroup, 512, FU_CH_MAX);
-  const IndexerArgs a = make_args(in, chunk, true);
   const FusedWs w = fused_ws(ws, in.batch, in.max_seq_len);
   FusedOut o;
   o.slots = out_slots;
-  o.scores = out_scores;
+  o.scores = sorted && !out_scores ? w.sval : out_scores;
   o.k = k;
+  o.keep_positions = sorted;
+  const int e = launch_fused_select(in, w, o, stream);
+  if (e || !sorted) return e;
+  return launch_sort_rows(in.batch, k, out_slots, o.scores, nullptr, 0, nullptr, nullptr, in.block_table,
+                          in.bt_stride, in.page_size, in.row_to_batch, out_scores,
+                          out_scores ? nullptr : w.sval, stream);
+}
+
+static int launch_fused_select(const IndexerInputs& in, const FusedWs& w, const FusedOut& o, hipStream_t stream) {
+  if (static_cast<int64_t>(in.batch) * in.max_seq_len <= FS_MAX_TOKENS) return launch_fused_scores(in, w, o, stream);
+  const int chunk = choose_chunk(in.batch, in.max_seq_len, in.page_size, kGroup, 512, FU_CH_MAX);
+  const IndexerArgs a = make_args(in, chunk, true);
+  const int k = o.k;
   const dim3 grid(chunk_grid(a));
   (void)hipGetLastError();
   // the scores' dynamic LDS plus the static part stay within 64 KB

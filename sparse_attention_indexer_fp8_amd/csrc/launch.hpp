@@ -26,7 +26,16 @@ inline hipError_t allow_dynamic_lds(const void* kernel, size_t bytes, std::atomi
 int launch_topk_rows(const float* scores, int64_t stride, int rows, const int32_t* seq_lens,
                      const int32_t* row_starts, const int32_t* row_to_batch,
                      const int32_t* page_table, int64_t pt_stride, int page_size, int k,
-                     int32_t* out, hipStream_t stream);
+                     int32_t* out, bool sorted, hipStream_t stream);
+
+// Sorted output pass: orders each row's k entries (score descending, equal
+// scores by ascending position; -1 entries last) and maps them to slots.
+// Scores come from `vals` ([rows][k]) or, when it is null, from the score
+// buffer `scores` at the entry's position.
+int launch_sort_rows(int rows, int k, int32_t* pos, const float* vals, const float* scores, int64_t stride,
+                     const int32_t* row_starts, const int32_t* seq_lens, const int32_t* page_table,
+                     int64_t pt_stride, int page_size, const int32_t* row_to_batch, float* out_vals,
+                     float* clear_vals, hipStream_t stream);
 
 int launch_page_transform(const int32_t* idx, int rows, int k, const int32_t* page_table,
                           int64_t pt_stride, int page_size, const int32_t* row_to_batch,
@@ -52,7 +61,7 @@ int launch_idx_score(const IndexerInputs& in, float* scores, int64_t score_strid
 
 size_t fused_workspace_bytes(int rows, int k, int max_seq_len);
 int launch_fused(const IndexerInputs& in, int k, int32_t* out_slots, float* out_scores, void* ws,
-                 hipStream_t stream);
+                 bool sorted, hipStream_t stream);
 
 size_t block_workspace_bytes(int rows, int block_size, int max_seq_len);
 

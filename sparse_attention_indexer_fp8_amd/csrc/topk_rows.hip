@@ -36,6 +36,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "select.hpp"
+#include "sort.hpp"
 
 
 namespace idxtopk {
@@ -59,7 +60,8 @@ struct RowsArgs {
   FastDiv pdiv;
   int32_t k;
   int32_t* out;
-  int32_t cap;  // candidate buffer entries
+  int32_t cap;   // candidate buffer entries
+  int32_t npow;  // sorted output: power of two >= k (<= cap)
 };
 
 __device__ __forceinline__ int32_t map_slot(const int32_t* pt_row, uint32_t pos, uint32_t P,
@@ -390,6 +392,103 @@ __device__ __forceinline__ void emit_all(const RowCtx& r, const RowsArgs& a) {
     r.out[i] = (i < r.n) ? map_slot(r.pt_row, static_cast<uint32_t>(i), P, a.pdiv) : -1;
 }
 
+// Sorted output: keys[0, npow) (real entries first, then zeros) are put in
+// descending order, and entry i of the row's output is the key of rank i
+// mapped to its slot (-1 for a zero key). A larger key is the better entry
+// (higher score, then lower position), so the order is score descending,
+// equal scores by ascending position.
+//
+// Up to 2048 keys: E per thread in registers (block_sort_desc; `keys` then
+// serves as its exchange scratch), ranks tid*E .. tid*E + E - 1 written by
+// thread tid with all page lookups issued first.
+template <int E>
+__device__ __forceinline__ void sort_emit_reg(const RowCtx& r, const RowsArgs& a, uint64_t* keys) {
+  const int tid = threadIdx.x;
+  uint64_t x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = keys[e * TR_WG + tid];
+  __syncthreads();
+  block_sort_desc<TR_WG, E>(x, keys);
+  const uint32_t P = static_cast<uint32_t>(a.page_size);
+  uint32_t pg[E];
+  int32_t page[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) pg[e] = x[e] ? fdiv(rank_pos(x[e]), a.pdiv) : 0u;
+  if (r.pt_row && x[0]) {
+    // zero keys read page 0, which exists when this thread holds any entry
+#pragma unroll
+    for (int e = 0; e < E; ++e) page[e] = r.pt_row[pg[e]];
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = tid * E + e;
+    if (i < a.k) {
+      const uint32_t pos = rank_pos(x[e]);
+      r.out[i] = !x[e] ? -1
+               : r.pt_row ? static_cast<int32_t>(static_cast<int64_t>(page[e]) * P + (pos - pg[e] * P))
+                          : static_cast<int32_t>(pos);
+    }
+  }
+}
+
+// Larger sizes: a bitonic network in LDS, one barrier per step.
+__device__ __forceinline__ void sort_emit_lds(const RowCtx& r, const RowsArgs& a, uint64_t* keys) {
+  const int tid = threadIdx.x;
+  const int npow = a.npow;
+  for (int size = 2; size <= npow; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = tid; t < (npow >> 1); t += TR_WG) {
+        const int lo = 2 * t - (t & (stride - 1));
+        const int hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const uint64_t x = keys[lo], y = keys[hi];
+        if ((x < y) == desc) {
+          keys[lo] = y;
+          keys[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const uint32_t P = static_cast<uint32_t>(a.page_size);
+  for (int i0 = 0; i0 < a.k; i0 += TR_EMIT * TR_WG) {
+    uint64_t kk[TR_EMIT];
+    int32_t base[TR_EMIT];
+    uint32_t pg[TR_EMIT];
+#pragma unroll
+    for (int j = 0; j < TR_EMIT; ++j) {
+      const int i = i0 + j * TR_WG + tid;
+      kk[j] = i < a.k ? keys[i] : 0ull;
+      pg[j] = kk[j] ? fdiv(rank_pos(kk[j]), a.pdiv) : 0u;
+    }
+    if (r.pt_row) {
+      // all lookups issued before any is used; zero keys read page 0
+#pragma unroll
+      for (int j = 0; j < TR_EMIT; ++j) base[j] = kk[j] || r.n > 0 ? r.pt_row[pg[j]] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < TR_EMIT; ++j) {
+      const int i = i0 + j * TR_WG + tid;
+      if (i < a.k) {
+        const uint32_t pos = rank_pos(kk[j]);
+        r.out[i] = !kk[j] ? -1
+                 : r.pt_row ? static_cast<int32_t>(static_cast<int64_t>(base[j]) * P + (pos - pg[j] * P))
+                            : static_cast<int32_t>(pos);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void sort_emit(const RowCtx& r, const RowsArgs& a, uint64_t* keys) {
+  switch (a.npow) {
+    case 512: sort_emit_reg<2>(r, a, keys); break;
+    case 1024: sort_emit_reg<4>(r, a, keys); break;
+    case 2048: sort_emit_reg<8>(r, a, keys); break;
+    default: sort_emit_lds(r, a, keys); break;
+  }
+}
+
+template <bool SORTED>
 __global__ __launch_bounds__(TR_WG, 4) void topk_rows_kernel(RowsArgs a) {
   extern __shared__ uint64_t cand[];
   __shared__ TopkRowsLds s;
@@ -398,7 +497,15 @@ __global__ __launch_bounds__(TR_WG, 4) void topk_rows_kernel(RowsArgs a) {
   const uint32_t P = static_cast<uint32_t>(a.page_size);
   const RowCtx cur = row_setup(a, blockIdx.x);
   if (cur.trivial) {
-    emit_all(cur, a);
+    if (SORTED) {
+      // every position is selected: its keys, then the sort
+      for (int i = tid; i < a.npow; i += TR_WG)
+        cand[i] = i < cur.n ? rank_key(float_key(cur.base[i]), static_cast<uint32_t>(i)) : 0ull;
+      __syncthreads();
+      sort_emit(cur, a, cand);
+    } else {
+      emit_all(cur, a);
+    }
     return;
   }
   f4 ring[TR_RING][TR_VEC];
@@ -428,6 +535,39 @@ __global__ __launch_bounds__(TR_WG, 4) void topk_rows_kernel(RowsArgs a) {
   // row is padded with -1). Each round reserves output slots per wave, then
   // issues all its page-table gathers before using any.
   const uint64_t T = c > k ? select_buffer(cand, c, k, 0, s) : 0ull;
+  if (SORTED) {
+    // the kept keys move to the front of the buffer, in place: a round
+    // writes only below what all rounds so far have read (the barrier
+    // separates this round's reads from its writes), so nothing unread is
+    // overwritten
+    for (uint32_t b0 = 0; b0 < c; b0 += TR_EMIT * TR_WG) {
+      uint64_t key[TR_EMIT];
+      bool keep[TR_EMIT];
+      uint32_t mine = 0;
+#pragma unroll
+      for (int j = 0; j < TR_EMIT; ++j) {
+        const uint32_t i = b0 + j * TR_WG + tid;
+        key[j] = cand[i < c ? i : 0];
+        keep[j] = i < c && key[j] >= T;
+        mine += keep[j];
+      }
+      uint32_t at = wave_reserve(mine, &s.ocnt);
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < TR_EMIT; ++j) {
+        if (keep[j]) {
+          if (at < k) cand[at] = key[j];
+          ++at;
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t kept = s.ocnt < k ? s.ocnt : k;
+    for (uint32_t i = kept + tid; i < static_cast<uint32_t>(a.npow); i += TR_WG) cand[i] = 0ull;
+    __syncthreads();
+    sort_emit(cur, a, cand);
+    return;
+  }
   for (uint32_t b0 = 0; b0 < c; b0 += TR_EMIT * TR_WG) {
     bool keep[TR_EMIT];
     uint32_t pos[TR_EMIT];
@@ -476,7 +616,7 @@ static inline int rows_cap(int k) {
 int launch_topk_rows(const float* scores, int64_t stride, int rows, const int32_t* seq_lens,
                      const int32_t* row_starts, const int32_t* row_to_batch,
                      const int32_t* page_table, int64_t pt_stride, int page_size, int k,
-                     int32_t* out, hipStream_t stream) {
+                     int32_t* out, bool sorted, hipStream_t stream) {
   RowsArgs a;
   a.scores = scores;
   a.stride = stride;
@@ -490,12 +630,20 @@ int launch_topk_rows(const float* scores, int64_t stride, int rows, const int32_
   a.k = k;
   a.out = out;
   a.cap = rows_cap(k);
+  int npow = 512;  // at least two keys per thread
+  while (npow < k) npow <<= 1;
+  a.npow = npow;
+  if (sorted && a.cap < npow) a.cap = npow;
   const size_t lds = static_cast<size_t>(a.cap) * sizeof(uint64_t);
-  const void* kern = reinterpret_cast<const void*>(&topk_rows_kernel);
-  static std::atomic<size_t> granted{0};
-  if (allow_dynamic_lds(kern, lds, granted) != hipSuccess) return -4;
+  const void* kern = sorted ? reinterpret_cast<const void*>(&topk_rows_kernel<true>)
+                            : reinterpret_cast<const void*>(&topk_rows_kernel<false>);
+  static std::atomic<size_t> granted[2] = {{0}, {0}};
+  if (allow_dynamic_lds(kern, lds, granted[sorted]) != hipSuccess) return -4;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(topk_rows_kernel, dim3(rows), dim3(TR_WG), lds, stream, a);
+  if (sorted)
+    hipLaunchKernelGGL(topk_rows_kernel<true>, dim3(rows), dim3(TR_WG), lds, stream, a);
+  else
+    hipLaunchKernelGGL(topk_rows_kernel<false>, dim3(rows), dim3(TR_WG), lds, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -82,8 +82,10 @@ def _workspace(ws: Optional[Workspace]) -> Workspace:
 def topk_rows(scores: torch.Tensor, seq_lens: torch.Tensor, k: int,
               row_starts: Optional[torch.Tensor] = None, row_to_batch: Optional[torch.Tensor] = None,
               page_table: Optional[torch.Tensor] = None, page_size: int = 1,
-              out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Top-k of each row's fp32 window, mapped through the page table."""
+              out: Optional[torch.Tensor] = None, sorted: bool = False) -> torch.Tensor:
+    """Top-k of each row's fp32 window, mapped through the page table.
+    sorted: each row in descending score order, equal scores by ascending
+    position, -1 padding last (else the order within a row is unspecified)."""
     _need(scores, "scores", (torch.float32,), 2, contiguous=False)
     if scores.stride(1) != 1:
         raise ValueError("scores rows must be contiguous")
@@ -103,7 +105,7 @@ def topk_rows(scores: torch.Tensor, seq_lens: torch.Tensor, k: int,
     _need(out, "out", (torch.int32,), 2)
     st = _lib.load().topk_rows(_ptr(scores), scores.stride(0), rows, _ptr(seq_lens), _ptr(row_starts),
                                _ptr(row_to_batch), _ptr(page_table), pt_stride, int(page_size), int(k),
-                               _ptr(out), _stream())
+                               _ptr(out), _lib.SORTED if sorted else 0, _stream())
     _lib.check("topk_rows", st)
     return out
 
@@ -163,9 +165,12 @@ def idx_score_fp8(q, q_scale, w, kcache, k_scale, block_table, seq_lens, page_si
 def idx_score_topk_fused(q, q_scale, w, kcache, k_scale, block_table, seq_lens, page_size: int,
                          max_seq_len: int, k: int, return_scores: bool = False,
                          workspace: Optional[Workspace] = None, out: Optional[torch.Tensor] = None,
-                         out_scores: Optional[torch.Tensor] = None, row_to_batch: Optional[torch.Tensor] = None):
+                         out_scores: Optional[torch.Tensor] = None, row_to_batch: Optional[torch.Tensor] = None,
+                         sorted: bool = False):
     """Fused decode indexer: top-k slots per row (and their scores if asked).
-    row_to_batch: block-table row of each query row (default: row b -> b)."""
+    row_to_batch: block-table row of each query row (default: row b -> b).
+    sorted: rows in descending score order, equal scores by ascending
+    position, -1 padding last."""
     args, B, H, D = _indexer_args(q, q_scale, w, kcache, k_scale, block_table, seq_lens, row_to_batch)
     if out is None:
         out = torch.empty((B, k), dtype=torch.int32, device=q.device)
@@ -175,7 +180,7 @@ def idx_score_topk_fused(q, q_scale, w, kcache, k_scale, block_table, seq_lens, 
     ws = _workspace(workspace).get(nbytes)
     st = _lib.load().idx_score_topk_fused(*args, int(page_size), _ptr(row_to_batch), _ptr(seq_lens), B, H, D,
                                           int(max_seq_len), int(k), _ptr(out), _ptr(out_scores),
-                                          _ptr(ws), ws.numel(), _stream())
+                                          _ptr(ws), ws.numel(), _lib.SORTED if sorted else 0, _stream())
     _lib.check("idx_score_topk_fused", st)
     return (out, out_scores) if return_scores else out
 

@@ -67,10 +67,10 @@ NULL = None
 
 def _topk_rows(lib, **kw):
     a = dict(scores=FAKE, stride=4096, rows=8, seq_lens=FAKE, rs=NULL, r2b=NULL, pt=NULL, pts=0, P=1,
-             k=512, out=FAKE)
+             k=512, out=FAKE, flags=0)
     a.update(kw)
     return lib.topk_rows(a["scores"], a["stride"], a["rows"], a["seq_lens"], a["rs"], a["r2b"], a["pt"],
-                         a["pts"], a["P"], a["k"], a["out"], NULL)
+                         a["pts"], a["P"], a["k"], a["out"], a["flags"], NULL)
 
 
 def test_topk_rows_validation(lib):
@@ -83,7 +83,10 @@ def test_topk_rows_validation(lib):
     assert _topk_rows(lib, pt=FAKE, P=0) == -1
     assert _topk_rows(lib, pt=FAKE, pts=-1) == -1
     assert _topk_rows(lib, k=8193) == -2
+    assert _topk_rows(lib, flags=2) == -1          # unknown flag bit
+    assert _topk_rows(lib, flags=1, rows=-1) == -1
     assert _topk_rows(lib, rows=0) == 0  # nothing to do, nothing enqueued
+    assert _topk_rows(lib, rows=0, flags=1) == 0
 
 
 def test_page_transform_validation(lib):
@@ -121,15 +124,20 @@ def test_score_validation(lib):
 def test_fused_validation_and_workspace(lib):
     need = lib.idxtopk_workspace_bytes(4, 32, 2048, 16384)
     assert need > 32 * 16384 * 8
-    f = lambda k=2048, out=FAKE, ws=FAKE, nb=need, **kw: lib.idx_score_topk_fused(
-        *_indexer(**kw), k, out, NULL, ws, nb, NULL)
+    f = lambda k=2048, out=FAKE, ws=FAKE, nb=need, flags=0, **kw: lib.idx_score_topk_fused(
+        *_indexer(**kw), k, out, NULL, ws, nb, flags, NULL)
     assert f(k=0) == -1
     assert f(k=8193) == -2
     assert f(out=NULL) == -1
     assert f(ws=NULL) == -3
     assert f(nb=need - 1) == -3
     assert f(D=256) == -2
+    assert f(flags=4) == -1         # unknown flag bit
     assert f(B=0) == 0
+    assert f(B=0, flags=1) == 0
+    # the sorted output's score area: rows x k floats on top of the rest
+    assert lib.idxtopk_workspace_bytes(4, 32, 2048, 16384) - lib.idxtopk_workspace_bytes(4, 32, 1024, 16384) \
+        == 32 * 1024 * 4
 
 
 def test_block_validation(lib):

@@ -471,3 +471,52 @@ def test_prefill_indexer_full_size_sampled(ops):
         check_scores(sc[b][:n], S)
         ts = oracle.token_slots(case.block_table[case.row_to_batch[b]], case.page_size, n)
         check_fused_row(slots[b], None, S, ts, case.k)
+
+
+# Sorted output: rows in descending score order, equal scores by ascending
+# position, -1 padding last. The oracle's selection is a stable descending
+# sort, so its order is that order: with exact arithmetic the whole output
+# sequence must match, ties included.
+@pytest.mark.parametrize("variant", ["score-buffer", "candidates"])
+@pytest.mark.parametrize("with_scores", [True, False])
+@pytest.mark.parametrize("k", [100, 700, 3000, 8192])
+def test_fused_sorted_exact_order(ops, variant, with_scores, k):
+    import torch
+    from sparse_attention_indexer_fp8_amd import ops as o
+
+    case = _exact_case(640 + k, batch=5, n_lo=1, n_hi=12000, page_size=64, heads=64, k=k, first=(0, k - 1, k))
+    if variant == "candidates":
+        case = _candidate_variant(case)
+    ws = o.Workspace()
+    res = ops.idx_score_topk_fused(*_inputs(case), case.page_size, case.max_seq_len, case.k,
+                                   return_scores=with_scores, workspace=ws, row_to_batch=_r2b(case), sorted=True)
+    torch.cuda.synchronize()
+    slots, sc = (res[0].cpu().numpy(), res[1].cpu().numpy()) if with_scores else (res.cpu().numpy(), None)
+    ref_slots, ref_pos, scores = oracle.fused_topk(case)
+    for b in range(case.batch):
+        assert np.array_equal(slots[b], ref_slots[b]), b
+        if sc is not None:
+            m = min(int(case.seq_lens[b]), case.k)
+            assert np.array_equal(sc[b][:m].astype(np.float64), scores[b][ref_pos[b][:m]]), b
+            assert np.all(np.isneginf(sc[b][m:])), b
+    assert int(ws.buf.count_nonzero()) == 0, "the workspace must be left zero-filled"
+
+
+def test_fused_sorted_random_order(ops):
+    """Random inputs: the sorted call returns the unsorted call's selection,
+    ordered by its own scores (descending), and the same slots as a set."""
+    import torch
+
+    case = workloads.indexer_case(650, batch=6, n_lo=1, n_hi=30000, page_size=64, k=2048)
+    for big in (False, True):
+        c = _candidate_variant(case) if big else case
+        s0, v0 = _fused(ops, c)
+        s1, v1 = ops.idx_score_topk_fused(*_inputs(c), c.page_size, c.max_seq_len, c.k, return_scores=True,
+                                          row_to_batch=_r2b(c), sorted=True)
+        torch.cuda.synchronize()
+        s1, v1 = s1.cpu().numpy(), v1.cpu().numpy()
+        for b in range(c.batch):
+            assert np.array_equal(np.sort(s1[b]), np.sort(s0[b])), b
+            assert np.all(v1[b][:-1] >= v1[b][1:]), b  # (-inf padding compares equal)
+            # the score that goes with each slot is unchanged by the sort
+            assert dict(zip(s0[b].tolist(), v0[b].tolist())) == dict(zip(s1[b].tolist(), v1[b].tolist())), b

@@ -239,3 +239,36 @@ def test_packed_prefill_full_size(ops):
     ref = oracle.topk_rows(case.scores, case.seq_lens, case.k, case.row_starts, case.row_to_batch,
                            case.page_table, 1, rows=sample)
     assert np.array_equal(sorted_rows(got[sample]), sorted_rows(ref))
+
+
+# Sorted output: the oracle selects by a stable descending sort, so its order
+# is the sorted order (score descending, equal scores by ascending position,
+# -1 padding last) and the whole output must match element by element.
+@pytest.mark.parametrize("k", [1, 300, 512, 1000, 2048, 4000, 8192])
+def test_topk_rows_sorted_order(ops, k):
+    import torch
+
+    case = workloads.c1_decode_topk()
+    lens = case.seq_lens.copy()
+    lens[0] = min(k - 1, lens[0])  # a padded row (empty for k = 1)
+    out = ops.topk_rows(dev(case.scores), dev(lens), k, page_table=dev(case.page_table),
+                        page_size=case.page_size, sorted=True)
+    torch.cuda.synchronize()
+    ref = oracle.topk_rows(case.scores, lens, k, page_table=case.page_table, page_size=case.page_size)
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
+def test_topk_rows_sorted_ties_and_packed(ops):
+    """Scores on a quarter grid (many ties) in the packed layout with
+    row_starts and row_to_batch: ties come out by ascending position."""
+    import torch
+
+    case = workloads.packed_prefill_case(seed=661, prefix0=3000, new_tokens=128, k=256)
+    buf = (np.round(case.scores * 4) / 4).astype(np.float32)
+    out = ops.topk_rows(dev(buf), dev(case.seq_lens), case.k, row_starts=dev(case.row_starts),
+                        row_to_batch=dev(case.row_to_batch), page_table=dev(case.page_table),
+                        page_size=case.page_size, sorted=True)
+    torch.cuda.synchronize()
+    ref = oracle.topk_rows(buf, case.seq_lens, case.k, case.row_starts, case.row_to_batch, case.page_table,
+                           case.page_size)
+    assert np.array_equal(out.cpu().numpy(), ref)

@@ -51,6 +51,8 @@ def test_brute_force_unique_dominant_subset(seed):
         if all(_dominates(v, a, b) for a in s for b in range(n) if b not in s):
             winners.append(s)
     assert winners == [sel]
+    # and in order: each output beats the next one
+    assert all(_dominates(v, int(got[i]), int(got[i + 1])) for i in range(m - 1))
 
 
 @pytest.mark.parametrize("seed", range(20))
