@@ -11,8 +11,10 @@ The oracle is plain, slow and meant to be checked by eye:
 
 * e4m3 decoding from the OCP 8-bit floating-point definition (``fp8.py``);
 * e4m3 encoding by nearest-value search over the same table (``fp8.py``);
-* float64 scoring, page gathering, top-k by a full stable sort, the page
-  transform, the block variant and the key-cache writer (``indexer.py``).
+* bf16 decoding and encoding from the format's definition (``bf16.py``);
+* float64 scoring (fp8 and bf16 index caches), page gathering, top-k by a
+  full stable sort, the page transform, the block variant and the key-cache
+  writers (``indexer.py``).
 
 Each function names the passage of the pages it follows. Pages:
 
@@ -28,12 +30,15 @@ Parity status: every function here is pinned by the ``-m "not gpu"`` tests in
 independent integer recomputation, brute force on tiny inputs, invariants and
 hand-built cases. None is "parity unpinned".
 """
-from . import fp8, indexer  # noqa: F401
+from . import bf16, fp8, indexer  # noqa: F401
+from .bf16 import BF16_TABLE, decode_bf16, encode_bf16  # noqa: F401
 from .fp8 import E4M3FN_TABLE, decode_e4m3fn, encode_e4m3fn  # noqa: F401
 from .indexer import (  # noqa: F401
     block_scores,
     block_topk,
     cache_write,
+    cache_write_bf16,
+    index_scores_bf16,
     quantize_key,
     fused_topk,
     index_scores,

@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import numpy as np
 
+from .bf16 import decode_bf16, encode_bf16
 from .fp8 import decode_e4m3fn
 
 
@@ -157,6 +158,29 @@ def index_scores(q_b, q_scale_b, w_b, kcache, k_scale, bt_row, page_size: int, n
     return (np.maximum(logits, 0.0) * _f64(w_b)[None, :]).sum(axis=1)
 
 
+def index_scores_bf16(q_b, w_b, kcache, bt_row, page_size: int, n: int) -> np.ndarray:
+    """Indexer score of every visible key of one row from a bf16 index cache,
+    in float64: S[j] = sum_h w[h] * max(0, sum_d q[h, d] * k[slot_j, d]).
+
+    [ATOM-1473], Pull request overview: the index cache takes the model's
+    dtype when the KV cache is not fp8. READING: that dtype is bf16, the
+    queries are bf16 too, and there are no scales; the score is the same
+    weighted-ReLU head sum as the fp8 one with unit scales. ``q_b`` [H, D]
+    and ``kcache`` [slots, D] hold bf16 bit patterns.
+
+    A product of two bf16 values has at most 16 significant bits and is
+    exact in float64; the sum of 128 of them is exact whenever their
+    exponents span fewer than 30 binades (always for the small-integer
+    inputs of the exact tests), and otherwise within float64 rounding, far
+    below any fp32 tolerance.
+    """
+    qd = decode_bf16(q_b)  # [H, D]
+    slots = token_slots(bt_row, page_size, n)
+    kd = decode_bf16(np.asarray(kcache)[slots])  # [n, D]
+    dot = kd @ qd.T  # [n, H]
+    return (np.maximum(dot, 0.0) * _f64(w_b)[None, :]).sum(axis=1)
+
+
 def case_bt_row(case, b: int) -> np.ndarray:
     """Block-table row of query row b: ``row_to_batch[b]`` if the case has one,
     else b. Several query rows may share a block-table row (multi-token
@@ -167,7 +191,11 @@ def case_bt_row(case, b: int) -> np.ndarray:
 
 
 def case_scores(case, b: int) -> np.ndarray:
-    """``index_scores`` of row b of a workloads.IndexerCase."""
+    """``index_scores`` (or ``index_scores_bf16`` for a bf16 index cache) of
+    row b of a workloads.IndexerCase."""
+    if getattr(case, "cache_dtype", "fp8") == "bf16":
+        return index_scores_bf16(case.q[b], case.w[b], case.kcache, case_bt_row(case, b), case.page_size,
+                                 int(case.seq_lens[b]))
     return index_scores(case.q[b], case.q_scale[b], case.w[b], case.kcache, case.k_scale,
                         case_bt_row(case, b), case.page_size, int(case.seq_lens[b]))
 
@@ -290,3 +318,16 @@ def cache_write(keys, slot_mapping, kcache, k_scale) -> None:
         codes, scale = quantize_key(keys[t])
         kcache[s] = codes
         k_scale[s] = scale
+
+
+def cache_write_bf16(keys, slot_mapping, kcache) -> None:
+    """bf16 index cache writer: kcache[slot] = the nearest bf16 of each key
+    value (``encode_bf16``: round to nearest, ties to even), no scale. Tokens
+    with a negative slot are skipped. Writes into ``kcache`` (uint16) in
+    place. [ATOM-1473], Pull request overview: the non-fp8 index cache holds
+    keys in the model's dtype. A bf16 key is stored as it is."""
+    keys = np.asarray(keys, dtype=np.float64)
+    for t, s in enumerate(np.asarray(slot_mapping).astype(np.int64)):
+        if s < 0:
+            continue
+        kcache[s] = encode_bf16(keys[t])

@@ -48,12 +48,21 @@ E4M3_MAX = 448.0
 SENTINEL_KEY_BYTE = 0x7E
 SENTINEL_KEY_SCALE = 1.0e3
 SENTINEL_SCORE = np.float32(np.inf)
+# bf16 index cache: unused slots hold this key (2^23 in every dimension), far
+# above any real key, so reading one would show up in the scores
+SENTINEL_KEY_BF16 = 0x4B00
 
 _POOL_THREADS = 8
 
 
 def rng(seed: int, stream: int, row: int = 0) -> np.random.Generator:
     return np.random.default_rng([int(seed), int(stream), int(row)])
+
+
+def _to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """bf16 values drawn from float32 ones by keeping the upper 16 bits (a
+    bf16 value is the upper half of a float32 bit pattern)."""
+    return (np.ascontiguousarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
 def _to_e4m3_bytes(x: np.ndarray) -> np.ndarray:
@@ -189,6 +198,10 @@ class IndexerCase:
     max_seq_len: int = 0  # upper bound on seq_lens the caller promises
     meta: dict = field(default_factory=dict)
     row_to_batch: Optional[np.ndarray] = None  # int32 [B]: block-table row of each query row
+    # "fp8": q and kcache hold e4m3fn bytes with fp32 scales. "bf16": q
+    # [B, H, D] and kcache [num_slots, D] hold bf16 bit patterns (uint16);
+    # q_scale and k_scale are all ones and unused.
+    cache_dtype: str = "fp8"
 
     @property
     def batch(self) -> int:
@@ -205,16 +218,20 @@ class IndexerCase:
 
 def indexer_case(seed: int, batch: int, n_lo: int, n_hi: int, page_size: int, k: int = 2048,
                  heads: int = 64, dim: int = 128, block_size: int = 0, top_blocks: int = 0,
-                 fixed_lens: Optional[np.ndarray] = None, name: str = "indexer") -> IndexerCase:
-    """Paged fp8 indexer inputs.
+                 fixed_lens: Optional[np.ndarray] = None, name: str = "indexer",
+                 cache_dtype: str = "fp8") -> IndexerCase:
+    """Paged indexer inputs.
 
-    q ~ 0.5 N(0,1) per element with one fp32 scale per row (max|q| / 448); head
-    weights ~ N(0,1) / 8; keys ~ N(0,1) per element with one fp32 scale per
-    token (max|k_t| / 448). Every row gets ceil(n_b / page_size) pages drawn
-    from one permutation of all pages; one extra page filled with sentinels
-    backs every unused block-table entry, and unused slots of partly filled
-    pages hold sentinels too.
+    fp8 (default): q ~ 0.5 N(0,1) per element with one fp32 scale per row
+    (max|q| / 448); head weights ~ N(0,1) / 8; keys ~ N(0,1) per element with
+    one fp32 scale per token (max|k_t| / 448). bf16: the same q and key draws
+    kept as bf16 values (``_to_bf16_bits``), no scales. Every row gets
+    ceil(n_b / page_size) pages drawn from one permutation of all pages; one
+    extra page filled with sentinels backs every unused block-table entry,
+    and unused slots of partly filled pages hold sentinels too.
     """
+    assert cache_dtype in ("fp8", "bf16")
+    bf16 = cache_dtype == "bf16"
     if fixed_lens is not None:
         lens = np.asarray(fixed_lens, dtype=np.int32)
         assert lens.shape == (batch,)
@@ -229,18 +246,25 @@ def indexer_case(seed: int, batch: int, n_lo: int, n_hi: int, page_size: int, k:
     num_slots = (total_pages + 1) * P
     max_pages = max(1, (max_seq_len + P - 1) // P)
 
-    q = np.empty((batch, heads, dim), np.uint8)
-    q_scale = np.empty(batch, np.float32)
+    q = np.empty((batch, heads, dim), np.uint16 if bf16 else np.uint8)
+    q_scale = np.ones(batch, np.float32)
     w = np.empty((batch, heads), np.float32)
     for b in range(batch):
         qf = rng(seed, STREAM_Q, b).standard_normal((heads, dim), dtype=np.float32) * np.float32(0.5)
-        s = np.float32(np.abs(qf).max() / np.float32(E4M3_MAX))
-        q_scale[b] = s
-        q[b] = _to_e4m3_bytes(qf / s)
+        if bf16:
+            q[b] = _to_bf16_bits(qf)
+        else:
+            s = np.float32(np.abs(qf).max() / np.float32(E4M3_MAX))
+            q_scale[b] = s
+            q[b] = _to_e4m3_bytes(qf / s)
         w[b] = rng(seed, STREAM_W, b).standard_normal(heads, dtype=np.float32) / np.float32(8.0)
 
-    kcache = np.full((num_slots, dim), SENTINEL_KEY_BYTE, np.uint8)
-    k_scale = np.full(num_slots, SENTINEL_KEY_SCALE, np.float32)
+    if bf16:
+        kcache = np.full((num_slots, dim), SENTINEL_KEY_BF16, np.uint16)
+        k_scale = np.ones(num_slots, np.float32)
+    else:
+        kcache = np.full((num_slots, dim), SENTINEL_KEY_BYTE, np.uint8)
+        k_scale = np.full(num_slots, SENTINEL_KEY_SCALE, np.float32)
     bt = np.full((batch, max_pages), sentinel_page, np.int32)
     offs = np.concatenate([[0], np.cumsum(npages)]).astype(np.int64)
 
@@ -251,10 +275,13 @@ def indexer_case(seed: int, batch: int, n_lo: int, n_hi: int, page_size: int, k:
         if n == 0:
             return
         kf = rng(seed, STREAM_KEY, b).standard_normal((n, dim), dtype=np.float32)
+        slots = (pages[:, None] * P + np.arange(P, dtype=np.int64)[None, :]).reshape(-1)[:n]
+        if bf16:
+            kcache[slots] = _to_bf16_bits(kf)
+            return
         s = (np.abs(kf).max(axis=1) / np.float32(E4M3_MAX)).astype(np.float32)
         s = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
         kb = _to_e4m3_bytes(kf / s[:, None])
-        slots = (pages[:, None] * P + np.arange(P, dtype=np.int64)[None, :]).reshape(-1)[:n]
         kcache[slots] = kb
         k_scale[slots] = s
 
@@ -267,12 +294,13 @@ def indexer_case(seed: int, batch: int, n_lo: int, n_hi: int, page_size: int, k:
 
     return IndexerCase(name, q, q_scale, w, kcache, k_scale, bt, P, lens, k=k,
                        block_size=block_size, top_blocks=top_blocks, max_seq_len=max_seq_len,
-                       meta={"total_pages": total_pages, "sentinel_page": sentinel_page})
+                       meta={"total_pages": total_pages, "sentinel_page": sentinel_page},
+                       cache_dtype=cache_dtype)
 
 
 def multi_query_case(seed: int, requests: int, next_n: int, n_lo: int, n_hi: int, page_size: int,
                      k: int = 2048, heads: int = 64, dim: int = 128, name: str = "multi-query",
-                     fixed_lens: Optional[np.ndarray] = None) -> IndexerCase:
+                     fixed_lens: Optional[np.ndarray] = None, cache_dtype: str = "fp8") -> IndexerCase:
     """Multi-token decode rows: each of `requests` requests decodes `next_n`
     query tokens at once. The cache and block table are those of an
     indexer_case with one row per request (context length L_r); query row
@@ -280,30 +308,34 @@ def multi_query_case(seed: int, requests: int, next_n: int, n_lo: int, n_hi: int
     length L_r - (next_n - 1 - t), and draws its own query and head weights
     from the same distributions as indexer_case."""
     base = indexer_case(seed, batch=requests, n_lo=n_lo, n_hi=n_hi, page_size=page_size, k=k, heads=heads,
-                        dim=dim, name=name, fixed_lens=fixed_lens)
+                        dim=dim, name=name, fixed_lens=fixed_lens, cache_dtype=cache_dtype)
+    bf16 = cache_dtype == "bf16"
     rows = requests * next_n
-    q = np.empty((rows, heads, dim), np.uint8)
-    q_scale = np.empty(rows, np.float32)
+    q = np.empty((rows, heads, dim), np.uint16 if bf16 else np.uint8)
+    q_scale = np.ones(rows, np.float32)
     w = np.empty((rows, heads), np.float32)
     for r in range(rows):
         qf = rng(seed, STREAM_MQ, r).standard_normal((heads, dim), dtype=np.float32) * np.float32(0.5)
-        s = np.float32(np.abs(qf).max() / np.float32(E4M3_MAX))
-        q_scale[r] = s
-        q[r] = _to_e4m3_bytes(qf / s)
+        if bf16:
+            q[r] = _to_bf16_bits(qf)
+        else:
+            s = np.float32(np.abs(qf).max() / np.float32(E4M3_MAX))
+            q_scale[r] = s
+            q[r] = _to_e4m3_bytes(qf / s)
         w[r] = rng(seed, STREAM_MW, r).standard_normal(heads, dtype=np.float32) / np.float32(8.0)
     r2b = np.repeat(np.arange(requests, dtype=np.int32), next_n)
     t = np.tile(np.arange(next_n, dtype=np.int32), requests)
     lens = np.maximum(base.seq_lens[r2b] - (next_n - 1 - t), 0).astype(np.int32)
     return IndexerCase(name, q, q_scale, w, base.kcache, base.k_scale, base.block_table, page_size, lens, k=k,
                        max_seq_len=base.max_seq_len, meta=dict(base.meta, requests=requests, next_n=next_n),
-                       row_to_batch=r2b)
+                       row_to_batch=r2b, cache_dtype=cache_dtype)
 
 
 # --------------------------------------------------------------------------
 # The five named workloads (full size) and reduced versions for quick tests
 # --------------------------------------------------------------------------
 
-SEEDS = {"c1": 101, "c2": 102, "c3": 103, "c4": 104, "c5": 105, "mtp": 106}
+SEEDS = {"c1": 101, "c2": 102, "c3": 103, "c4": 104, "c5": 105, "mtp": 106, "bf16": 107}
 
 
 def c1_decode_topk() -> RowsCase:
@@ -337,6 +369,13 @@ def mtp_decode() -> IndexerCase:
                             name="mtp-decode-16x4-n16k-64k-k2048")
 
 
+def bf16_decode() -> IndexerCase:
+    """Fused decode from a bf16 index cache: the fused-decode geometry (32
+    rows, n ~ U{8192..16384}, page 64, k 2048) with bf16 queries and keys."""
+    return indexer_case(SEEDS["bf16"], batch=32, n_lo=8192, n_hi=16384, page_size=64, k=2048,
+                        name="fused-decode-bf16-B32-n8k-16k-k2048", cache_dtype="bf16")
+
+
 def prefill_indexer() -> IndexerCase:
     """Packed prefill from the fp8 cache, in the packed-prefill top-k
     geometry: request 0 has 61808 cached tokens and request 1 none, each
@@ -358,6 +397,6 @@ def ceil_div(a: int, b: int) -> int:
 __all__ = [
     "RowsCase", "IndexerCase", "decode_rows_case", "packed_prefill_case", "indexer_case", "multi_query_case",
     "c1_decode_topk", "c2_fused_decode", "c3_packed_prefill", "c4_block_sparse", "c5_long_decode", "mtp_decode",
-    "prefill_indexer",
+    "prefill_indexer", "bf16_decode", "SENTINEL_KEY_BF16",
     "SEEDS", "SENTINEL_KEY_BYTE", "SENTINEL_KEY_SCALE", "rng", "expected_tokens", "ceil_div",
 ]
