@@ -147,10 +147,11 @@ def rows_algorithmic_bytes(case) -> int:
 
 
 def indexer_algorithmic_bytes(case, out_entries: int) -> int:
-    """Keys (128 B + 4 B scale per token), block-table entries, queries, head
-    weights and scales, outputs. Query rows that share a block-table row
-    (row_to_batch) read nested windows of the same keys: those count once per
-    block-table row, at the longest window."""
+    """Keys (128 B + 4 B scale per token from an fp8 cache, 256 B from a bf16
+    one), block-table entries, queries, head weights and scales, outputs.
+    Query rows that share a block-table row (row_to_batch) read nested
+    windows of the same keys: those count once per block-table row, at the
+    longest window."""
     n = case.seq_lens.astype(np.int64)
     r2b = getattr(case, "row_to_batch", None)
     if r2b is not None:
@@ -158,9 +159,12 @@ def indexer_algorithmic_bytes(case, out_entries: int) -> int:
         np.maximum.at(longest, np.asarray(r2b, np.int64), n)
         n = longest
     P = case.page_size
-    keys = int((n * (case.dim + 4)).sum())
+    bf16 = getattr(case, "cache_dtype", "fp8") == "bf16"
+    per_token = 2 * case.dim if bf16 else case.dim + 4
+    keys = int((n * per_token).sum())
     table = int((4 * ((n + P - 1) // P)).sum())
-    query = case.batch * case.heads * (case.dim + 4) + 8 * case.batch
+    query = (case.batch * case.heads * (2 * case.dim + 4) + 4 * case.batch if bf16
+             else case.batch * case.heads * (case.dim + 4) + 8 * case.batch)
     return keys + table + query + 4 * out_entries
 
 
@@ -296,14 +300,16 @@ def bench_rows(torch, ops, timer, case, warmup, steps, flush, sorted=False):
 
 
 def bench_fused(torch, ops, timer, case, warmup, steps, flush, sorted=False):
-    args = [dev(torch, x) for x in (case.q, case.q_scale, case.w, case.kcache, case.k_scale,
-                                    case.block_table, case.seq_lens)]
+    bf16 = getattr(case, "cache_dtype", "fp8") == "bf16"
+    fields = ((case.q, case.w, case.kcache, case.block_table, case.seq_lens) if bf16 else
+              (case.q, case.q_scale, case.w, case.kcache, case.k_scale, case.block_table, case.seq_lens))
+    args = [dev(torch, x) for x in fields]
     out = torch.empty((case.batch, case.k), dtype=torch.int32, device="cuda")
     ws = ops.Workspace()
+    fused = ops.idx_score_topk_fused_bf16 if bf16 else ops.idx_score_topk_fused
 
     def step():
-        ops.idx_score_topk_fused(*args, case.page_size, case.max_seq_len, case.k, workspace=ws, out=out,
-                                 sorted=sorted)
+        fused(*args, case.page_size, case.max_seq_len, case.k, workspace=ws, out=out, sorted=sorted)
 
     wall, us, region = timer.run(step, warmup, steps, flush)
     res = summary(us, indexer_algorithmic_bytes(case, case.batch * case.k), case.batch, region, timer.settled)
@@ -447,7 +453,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="all", help="comma list of c1..c5, mtp, cw, pf, or all")
+    ap.add_argument("--only", default="all", help="comma list of c1..c5, mtp, cw, pf, bf16, bf16l, or all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for PMC byte-counter calibration)")
@@ -463,7 +469,8 @@ def main(argv=None):
         print("bench.py measures one GPU only: the indexer top-k path here runs on a single MI355X "
               "(no sharding, no collectives); run with --gpus 1", file=sys.stderr)
         return 2
-    only = {"c1", "c2", "c3", "c4", "c5", "mtp", "cw", "pf"} if a.only == "all" else set(a.only.split(","))
+    only = ({"c1", "c2", "c3", "c4", "c5", "mtp", "cw", "pf", "bf16", "bf16l"} if a.only == "all"
+            else set(a.only.split(",")))
 
     case3 = None
     cpu = None
@@ -566,6 +573,17 @@ def main(argv=None):
         also["block_sparse_B64_n32768_top32"] = bench_block(torch, ops, timer, c4, a.warmup, max(a.steps, 50),
                                                             True)
         del c4
+    if "bf16" in only:
+        log("timing fused decode B32 from a bf16 cache ...")
+        bc = workloads.bf16_decode()
+        also["fused_decode_bf16_B32_k2048"] = bench_fused(torch, ops, timer, bc, a.warmup, max(a.steps, 50), True)
+        del bc
+    if "bf16l" in only:
+        log("generating long decode B64 from a bf16 cache ...")
+        bl = workloads.bf16_long_decode()
+        log("timing long decode B64 from a bf16 cache ...")
+        also["long_decode_bf16_B64_k2048"] = bench_fused(torch, ops, timer, bl, a.warmup, a.steps, False)
+        del bl
     if "c5" in only:
         log("generating long decode B64 ...")
         c5 = workloads.c5_long_decode()

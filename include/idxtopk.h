@@ -264,6 +264,60 @@ int idx_cache_write(const void* keys, int32_t key_dtype, int64_t key_stride, int
                     void* stream);
 
 /*
+ * bf16 index cache ([ATOM-1473] Pull request overview: the index cache is
+ * fp8 when the KV cache is fp8 and takes the model's dtype otherwise;
+ * commit "convert auto for bf16 type"). The library reads that case as bf16
+ * queries and keys with no scales:
+ *   S[b, j] = sum_h w[b, h] * max(0, sum_d q[b, h, d] * kcache[slot_j, d]),
+ * products and sums in fp32 (v_mfma_f32_16x16x32_bf16).
+ *
+ * q       bf16 [batch, heads, dim], 16-byte aligned (bit patterns; any
+ *         16-bit element type);
+ * kcache  bf16 [num_slots, dim] (256 bytes per slot), 16-byte aligned;
+ * every other argument, the outputs, workspace, flags and status codes are
+ * those of the fp8 entry point of the same name without the suffix. A
+ * misaligned q or kcache gives IDXTOPK_EINVAL.
+ */
+int idx_score_bf16(const uint16_t* q, const float* w, const uint16_t* kcache,
+                   const int32_t* block_table, int64_t bt_stride, int32_t page_size,
+                   const int32_t* row_to_batch, const int32_t* seq_lens, int32_t batch,
+                   int32_t heads, int32_t dim, int32_t max_seq_len, float* scores,
+                   int64_t score_stride, void* stream);
+
+int idx_score_topk_fused_bf16(const uint16_t* q, const float* w, const uint16_t* kcache,
+                              const int32_t* block_table, int64_t bt_stride, int32_t page_size,
+                              const int32_t* row_to_batch, const int32_t* seq_lens, int32_t batch,
+                              int32_t heads, int32_t dim, int32_t max_seq_len, int32_t k,
+                              int32_t* out_slots, float* out_scores, void* workspace,
+                              size_t workspace_bytes, int32_t flags, void* stream);
+
+int block_topk_bf16(const uint16_t* q, const float* w, const uint16_t* kcache,
+                    const int32_t* block_table, int64_t bt_stride, int32_t page_size,
+                    const int32_t* row_to_batch, const int32_t* seq_lens, int32_t batch,
+                    int32_t heads, int32_t dim, int32_t max_seq_len, int32_t block_size,
+                    int32_t top_blocks, int32_t* out_blocks, int32_t* out_slots,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * idx_cache_write_bf16 -- store new index keys into the bf16 cache.
+ *
+ * For every token t with s = slot_mapping[t] >= 0: kcache[s, d] =
+ * bf16(keys[t, d]), rounded to nearest with ties to the even pattern for
+ * fp32 keys, copied as they are for bf16 keys; no scale. Tokens with a
+ * negative slot are skipped.
+ *
+ * keys          [tokens, key_stride] row-major, elements of key_dtype
+ *               (IDXTOPK_KEY_F32 or IDXTOPK_KEY_BF16); keys and every row
+ *               start 16-byte aligned, else IDXTOPK_EINVAL.
+ * slot_mapping  int32 [tokens], distinct non-negative slots below the
+ *               cache's slot count.
+ * kcache        bf16 [num_slots, dim], 16-byte aligned.
+ * dim == IDXTOPK_DIM. Keys must be finite. No workspace.
+ */
+int idx_cache_write_bf16(const void* keys, int32_t key_dtype, int64_t key_stride, int32_t tokens,
+                         int32_t dim, const int32_t* slot_mapping, uint16_t* kcache, void* stream);
+
+/*
  * Workspace bytes an operation needs (0 when it needs none).
  * For IDXTOPK_OP_BLOCK_TOPK, pass block_size as `k`. Returns 0 for invalid
  * arguments as well.

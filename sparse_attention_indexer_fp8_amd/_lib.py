@@ -44,6 +44,12 @@ SIGNATURES = {
     "block_topk": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                           _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "idx_cache_write": (_i32, [_vp, _i32, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "idx_score_bf16": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i64, _vp]),
+    "idx_score_topk_fused_bf16": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                         _vp, _vp, _vp, _sz, _i32, _vp]),
+    "block_topk_bf16": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                               _vp, _vp, _vp, _sz, _vp]),
+    "idx_cache_write_bf16": (_i32, [_vp, _i32, _i64, _i32, _i32, _vp, _vp, _vp]),
     "idxtopk_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "idxtopk_status_str": (ctypes.c_char_p, [_i32]),
     "idxtopk_version": (_i32, []),

@@ -9,14 +9,18 @@ using idxtopk::IndexerInputs;
 
 bool heads_ok(int32_t h) { return h == 16 || h == 32 || h == 64 || h == 128; }
 
-// Shared checks of the paged indexer inputs (no device access).
-int check_indexer(const uint8_t* q, const float* q_scale, const float* w, const uint8_t* kcache,
+// Shared checks of the paged indexer inputs (no device access). A bf16 cache
+// has no scales, and its query and key rows are read 16 bytes at a time.
+int check_indexer(const void* q, const float* q_scale, const float* w, const void* kcache,
                   const float* k_scale, const int32_t* block_table, int64_t bt_stride,
                   int32_t page_size, const int32_t* seq_lens, int32_t batch, int32_t heads,
-                  int32_t dim, int32_t max_seq_len) {
+                  int32_t dim, int32_t max_seq_len, bool bf16 = false) {
   if (batch < 0 || heads <= 0 || dim <= 0 || page_size <= 0 || bt_stride < 0 || max_seq_len < 0)
     return IDXTOPK_EINVAL;
-  if (batch > 0 && (!q || !q_scale || !w || !kcache || !k_scale || !block_table || !seq_lens))
+  if (batch > 0 && (!q || !w || !kcache || !block_table || !seq_lens)) return IDXTOPK_EINVAL;
+  if (batch > 0 && !bf16 && (!q_scale || !k_scale)) return IDXTOPK_EINVAL;
+  if (batch > 0 && bf16 &&
+      (reinterpret_cast<uintptr_t>(q) % 16 != 0 || reinterpret_cast<uintptr_t>(kcache) % 16 != 0))
     return IDXTOPK_EINVAL;
   if (dim != IDXTOPK_DIM || !heads_ok(heads)) return IDXTOPK_EUNSUPPORTED;
   // every visible token's logical page must exist in the block-table row
@@ -25,15 +29,16 @@ int check_indexer(const uint8_t* q, const float* q_scale, const float* w, const 
   return IDXTOPK_OK;
 }
 
-IndexerInputs pack(const uint8_t* q, const float* q_scale, const float* w, const uint8_t* kcache,
+IndexerInputs pack(const void* q, const float* q_scale, const float* w, const void* kcache,
                    const float* k_scale, const int32_t* block_table, int64_t bt_stride,
                    int32_t page_size, const int32_t* row_to_batch, const int32_t* seq_lens,
-                   int32_t batch, int32_t heads, int32_t max_seq_len) {
+                   int32_t batch, int32_t heads, int32_t max_seq_len, bool bf16 = false) {
   IndexerInputs in;
-  in.q = q;
+  in.bf16 = bf16;
+  in.q = static_cast<const uint8_t*>(q);
   in.q_scale = q_scale;
   in.w = w;
-  in.kcache = kcache;
+  in.kcache = static_cast<const uint8_t*>(kcache);
   in.k_scale = k_scale;
   in.block_table = block_table;
   in.bt_stride = bt_stride;
@@ -151,6 +156,79 @@ int idx_cache_write(const void* keys, int32_t key_dtype, int64_t key_stride, int
   if (reinterpret_cast<uintptr_t>(keys) % align != 0 || key_stride % 2 != 0) return IDXTOPK_EINVAL;
   return idxtopk::launch_cache_write(keys, key_dtype == IDXTOPK_KEY_BF16, key_stride, tokens, slot_mapping,
                                      kcache, k_scale, static_cast<hipStream_t>(stream));
+}
+
+int idx_score_bf16(const uint16_t* q, const float* w, const uint16_t* kcache, const int32_t* block_table,
+                   int64_t bt_stride, int32_t page_size, const int32_t* row_to_batch, const int32_t* seq_lens,
+                   int32_t batch, int32_t heads, int32_t dim, int32_t max_seq_len, float* scores,
+                   int64_t score_stride, void* stream) {
+  const int st = check_indexer(q, nullptr, w, kcache, nullptr, block_table, bt_stride, page_size, seq_lens, batch,
+                               heads, dim, max_seq_len, true);
+  if (st != IDXTOPK_OK) return st;
+  if (score_stride < 0 || (batch > 0 && !scores)) return IDXTOPK_EINVAL;
+  if (static_cast<int64_t>(max_seq_len) > score_stride) return IDXTOPK_EINVAL;
+  if (batch == 0 || max_seq_len == 0) return IDXTOPK_OK;
+  return idxtopk::launch_idx_score(pack(q, nullptr, w, kcache, nullptr, block_table, bt_stride, page_size,
+                                        row_to_batch, seq_lens, batch, heads, max_seq_len, true),
+                                   scores, score_stride, static_cast<hipStream_t>(stream));
+}
+
+int idx_score_topk_fused_bf16(const uint16_t* q, const float* w, const uint16_t* kcache,
+                              const int32_t* block_table, int64_t bt_stride, int32_t page_size,
+                              const int32_t* row_to_batch, const int32_t* seq_lens, int32_t batch, int32_t heads,
+                              int32_t dim, int32_t max_seq_len, int32_t k, int32_t* out_slots, float* out_scores,
+                              void* workspace, size_t workspace_bytes, int32_t flags, void* stream) {
+  if (flags & ~IDXTOPK_SORTED) return IDXTOPK_EINVAL;
+  const int st = check_indexer(q, nullptr, w, kcache, nullptr, block_table, bt_stride, page_size, seq_lens, batch,
+                               heads, dim, max_seq_len, true);
+  if (st != IDXTOPK_OK) return st;
+  if (k <= 0 || (batch > 0 && !out_slots)) return IDXTOPK_EINVAL;
+  if (k > IDXTOPK_MAX_K_FUSED) return IDXTOPK_EUNSUPPORTED;
+  if (batch == 0) return IDXTOPK_OK;
+  if (!workspace || workspace_bytes < idxtopk::fused_workspace_bytes(batch, k, max_seq_len))
+    return IDXTOPK_EWORKSPACE;
+  return idxtopk::launch_fused(pack(q, nullptr, w, kcache, nullptr, block_table, bt_stride, page_size, row_to_batch,
+                                    seq_lens, batch, heads, max_seq_len, true),
+                               k, out_slots, out_scores, workspace, (flags & IDXTOPK_SORTED) != 0,
+                               static_cast<hipStream_t>(stream));
+}
+
+int block_topk_bf16(const uint16_t* q, const float* w, const uint16_t* kcache, const int32_t* block_table,
+                    int64_t bt_stride, int32_t page_size, const int32_t* row_to_batch, const int32_t* seq_lens,
+                    int32_t batch, int32_t heads, int32_t dim, int32_t max_seq_len, int32_t block_size,
+                    int32_t top_blocks, int32_t* out_blocks, int32_t* out_slots, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  const int st = check_indexer(q, nullptr, w, kcache, nullptr, block_table, bt_stride, page_size, seq_lens, batch,
+                               heads, dim, max_seq_len, true);
+  if (st != IDXTOPK_OK) return st;
+  if (block_size <= 0 || top_blocks <= 0 || (batch > 0 && !out_blocks)) return IDXTOPK_EINVAL;
+  if (block_size != page_size || top_blocks > IDXTOPK_MAX_TOP_BLOCKS || block_size % 16 != 0 ||
+      block_size > 8192)
+    return IDXTOPK_EUNSUPPORTED;
+  if (batch == 0) return IDXTOPK_OK;
+  if (!workspace ||
+      workspace_bytes < idxtopk::block_workspace_bytes(batch, block_size, max_seq_len))
+    return IDXTOPK_EWORKSPACE;
+  return idxtopk::launch_block_topk(pack(q, nullptr, w, kcache, nullptr, block_table, bt_stride, page_size,
+                                         row_to_batch, seq_lens, batch, heads, max_seq_len, true),
+                                    block_size, top_blocks, out_blocks, out_slots, workspace,
+                                    static_cast<hipStream_t>(stream));
+}
+
+int idx_cache_write_bf16(const void* keys, int32_t key_dtype, int64_t key_stride, int32_t tokens, int32_t dim,
+                         const int32_t* slot_mapping, uint16_t* kcache, void* stream) {
+  if (tokens < 0 || dim <= 0) return IDXTOPK_EINVAL;
+  if (dim != IDXTOPK_DIM) return IDXTOPK_EUNSUPPORTED;
+  if (key_dtype != IDXTOPK_KEY_F32 && key_dtype != IDXTOPK_KEY_BF16) return IDXTOPK_EUNSUPPORTED;
+  if (tokens == 0) return IDXTOPK_OK;
+  if (!keys || !slot_mapping || !kcache || key_stride < dim) return IDXTOPK_EINVAL;
+  // every row starts on 16 bytes of the input and of the cache
+  const int64_t esize = key_dtype == IDXTOPK_KEY_F32 ? 4 : 2;
+  if (reinterpret_cast<uintptr_t>(keys) % 16 != 0 || (key_stride * esize) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(kcache) % 16 != 0)
+    return IDXTOPK_EINVAL;
+  return idxtopk::launch_cache_write_bf16(keys, key_dtype == IDXTOPK_KEY_BF16, key_stride, tokens, slot_mapping,
+                                          kcache, static_cast<hipStream_t>(stream));
 }
 
 size_t idxtopk_workspace_bytes(int32_t op, int32_t rows, int32_t k, int32_t max_seq_len) {

@@ -89,4 +89,57 @@ int launch_cache_write(const void* keys, bool bf16, int64_t stride, int tokens, 
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
+// ---------------------------------------------------------------------------
+// bf16 index cache ([ATOM-1473] Pull request overview: with a KV cache that
+// is not fp8 the index cache takes the model's dtype): keys stored as bf16,
+// 256 bytes per token, no scale.
+// ---------------------------------------------------------------------------
+
+// bf16 pattern of a finite fp32 value, rounded to nearest with ties to the
+// even pattern: adding 0x7FFF plus the bit that becomes the last kept one
+// carries into bit 16 exactly when the dropped half is above one half, or
+// one half with an odd kept part.
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Sixteen threads per token, eight dimensions each: one 16-byte store.
+// bf16 input is copied as it is.
+template <bool BF16_IN>
+__global__ __launch_bounds__(CW_WG) void cache_write_bf16_kernel(const void* keys, int64_t stride, int tokens,
+                                                                 const int32_t* slots, uint16_t* kcache) {
+  const int i = blockIdx.x * CW_WG + threadIdx.x;
+  const int t = i >> 4, part = i & 15;
+  if (t >= tokens) return;
+  const int32_t slot = slots[t];
+  if (slot < 0) return;
+  uint4 out;
+  if (BF16_IN) {
+    out = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(keys) + t * stride + 8 * part);
+  } else {
+    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(keys) + t * stride + 8 * part);
+    const float4 x = src[0], y = src[1];
+    out.x = bf16_bits(x.x) | (bf16_bits(x.y) << 16);
+    out.y = bf16_bits(x.z) | (bf16_bits(x.w) << 16);
+    out.z = bf16_bits(y.x) | (bf16_bits(y.y) << 16);
+    out.w = bf16_bits(y.z) | (bf16_bits(y.w) << 16);
+  }
+  *reinterpret_cast<uint4*>(kcache + static_cast<int64_t>(slot) * CW_DIM + 8 * part) = out;
+}
+
+int launch_cache_write_bf16(const void* keys, bool bf16_in, int64_t stride, int tokens, const int32_t* slots,
+                            uint16_t* kcache, hipStream_t stream) {
+  if (tokens == 0) return 0;
+  const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(tokens) * 16 + CW_WG - 1) / CW_WG));
+  (void)hipGetLastError();
+  if (bf16_in)
+    hipLaunchKernelGGL(cache_write_bf16_kernel<true>, grid, dim3(CW_WG), 0, stream, keys, stride, tokens, slots,
+                       kcache);
+  else
+    hipLaunchKernelGGL(cache_write_bf16_kernel<false>, grid, dim3(CW_WG), 0, stream, keys, stride, tokens, slots,
+                       kcache);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
 }  // namespace idxtopk

@@ -155,7 +155,7 @@ __device__ __forceinline__ void chunk_span(const IndexerArgs& a, int c, int& tb,
 // Unfused scores
 // ---------------------------------------------------------------------------
 
-template <int NT>
+template <int NT, bool BF = false>
 __global__ __launch_bounds__(IX_WG) void score_kernel(IndexerArgs a, float* scores, int64_t sstride) {
   __shared__ int32_t pages[IX_PAGES];
   int b, c;
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(IX_WG) void score_kernel(IndexerArgs a, float* scor
   if (tb >= n) return;
   const int te = min(n, tb + clen);
   float* srow = scores + static_cast<int64_t>(b) * sstride;
-  score_chunk<NT, IX_WG, IX_RING>(a, b, tb, te, pages, [&](int j, float s, bool valid) {
+  score_chunk_any<BF, NT, IX_WG, IX_RING>(a, b, tb, te, pages, [&](int j, float s, bool valid) {
     if (valid) srow[j] = s;
   });
 }
@@ -386,7 +386,7 @@ struct FusedOut {
 };
 
 // Dynamic LDS: the chunk's scores (a.chunk floats).
-template <int NT>
+template <int NT, bool BF = false>
 __global__ __launch_bounds__(IX_WG) void fused_chunk_kernel(IndexerArgs a, FusedWs ws, int k) {
   extern __shared__ float sc[];
   __shared__ ChunkLds s;
@@ -409,7 +409,7 @@ __global__ __launch_bounds__(IX_WG) void fused_chunk_kernel(IndexerArgs a, Fused
     s.lcnt2 = 0;
   }
   // (score_chunk synchronises before its first emit)
-  score_chunk<NT, IX_WG, IX_RING>(a, b, tb, te, s.pages, [&](int j, float v, bool valid) {
+  score_chunk_any<BF, NT, IX_WG, IX_RING>(a, b, tb, te, s.pages, [&](int j, float v, bool valid) {
     if (valid) {
       sc[j - tb] = v;
       atomicAdd(&s.hist[float_key(v) >> HIST_SHIFT], 1u);
@@ -768,7 +768,7 @@ struct ScoresChunkLds {
   int32_t pages[IX_PAGES];
 };
 
-template <int NT>
+template <int NT, bool BF = false>
 __global__ __launch_bounds__(IX_WG) void fused_scores_chunk_kernel(IndexerArgs a, FusedWs ws) {
   extern __shared__ float4 sc4[];
   float* sc = reinterpret_cast<float*>(sc4);
@@ -785,7 +785,7 @@ __global__ __launch_bounds__(IX_WG) void fused_scores_chunk_kernel(IndexerArgs a
 
   for (int i = tid; i < HIST_BINS; i += IX_WG) s.hist[i] = 0;
   // (score_chunk synchronises before its first emit)
-  score_chunk<NT, IX_WG, FS_RING>(a, b, tb, te, s.pages, [&](int j, float v, bool valid) {
+  score_chunk_any<BF, NT, IX_WG, FS_RING>(a, b, tb, te, s.pages, [&](int j, float v, bool valid) {
     if (valid) {
       sc[j - tb] = v;
       atomicAdd(&s.hist[float_key(v) >> HIST_SHIFT], 1u);
@@ -1062,7 +1062,7 @@ struct BlockOut {
   int bs;
 };
 
-template <int NT>
+template <int NT, bool BF = false>
 __global__ __launch_bounds__(IX_WG) void block_chunk_kernel(IndexerArgs a, BlockWs ws, int bs) {
   __shared__ BlockChunkLds s;
   const int tid = threadIdx.x;
@@ -1081,7 +1081,7 @@ __global__ __launch_bounds__(IX_WG) void block_chunk_kernel(IndexerArgs a, Block
   // A 16-token group lies inside one block (block size and chunk starts are
   // multiples of 16), so the group's maximum is taken in registers (DPP over
   // the 16 lanes of each row) and one lane updates the block.
-  score_chunk<NT, IX_WG, IX_RING>(a, b, tb, te, s.pages, [&](int j, float v, bool valid) {
+  score_chunk_any<BF, NT, IX_WG, IX_RING>(a, b, tb, te, s.pages, [&](int j, float v, bool valid) {
     uint32_t key = valid ? float_key(v) : 0u;
     key = row16_max(key);
     if (lane_id() == 0 && key) atomicMax(&s.bmax[fdiv(static_cast<uint32_t>(j - tb), a.pdiv)], key);
@@ -1215,22 +1215,29 @@ static int choose_chunk(int batch, int max_seq_len, int page_size, int align, in
   return static_cast<int>(ch);
 }
 
-#define IDXTOPK_DISPATCH_NT_LDS(KERNEL, heads, grid, lds, stream, ...)                               \
-  do {                                                                                            \
-    switch (heads) {                                                                              \
-      case 16: hipLaunchKernelGGL(KERNEL<1>, grid, dim3(IX_WG), lds, stream, __VA_ARGS__); break;   \
-      case 32: hipLaunchKernelGGL(KERNEL<2>, grid, dim3(IX_WG), lds, stream, __VA_ARGS__); break;   \
-      case 64: hipLaunchKernelGGL(KERNEL<4>, grid, dim3(IX_WG), lds, stream, __VA_ARGS__); break;   \
-      case 128: hipLaunchKernelGGL(KERNEL<8>, grid, dim3(IX_WG), lds, stream, __VA_ARGS__); break;  \
-      default: return -2;                                                                         \
-    }                                                                                             \
+#define IDXTOPK_SWITCH_NT(KERNEL, BFV, heads, grid, lds, stream, ...)                                  \
+  switch (heads) {                                                                                  \
+    case 16: hipLaunchKernelGGL((KERNEL<1, BFV>), grid, dim3(IX_WG), lds, stream, __VA_ARGS__); break; \
+    case 32: hipLaunchKernelGGL((KERNEL<2, BFV>), grid, dim3(IX_WG), lds, stream, __VA_ARGS__); break; \
+    case 64: hipLaunchKernelGGL((KERNEL<4, BFV>), grid, dim3(IX_WG), lds, stream, __VA_ARGS__); break; \
+    case 128: hipLaunchKernelGGL((KERNEL<8, BFV>), grid, dim3(IX_WG), lds, stream, __VA_ARGS__); break; \
+    default: return -2;                                                                             \
+  }
+// KERNEL<NT, bf16 cache> for the head count
+#define IDXTOPK_DISPATCH_NT_LDS(KERNEL, bf, heads, grid, lds, stream, ...)    \
+  do {                                                                        \
+    if (bf) {                                                                 \
+      IDXTOPK_SWITCH_NT(KERNEL, true, heads, grid, lds, stream, __VA_ARGS__)  \
+    } else {                                                                  \
+      IDXTOPK_SWITCH_NT(KERNEL, false, heads, grid, lds, stream, __VA_ARGS__) \
+    }                                                                         \
   } while (0)
-#define IDXTOPK_DISPATCH_NT(KERNEL, heads, grid, stream, ...) \
-  IDXTOPK_DISPATCH_NT_LDS(KERNEL, heads, grid, 0, stream, __VA_ARGS__)
+#define IDXTOPK_DISPATCH_NT(KERNEL, bf, heads, grid, stream, ...) \
+  IDXTOPK_DISPATCH_NT_LDS(KERNEL, bf, heads, grid, 0, stream, __VA_ARGS__)
 
 int launch_idx_score(const IndexerInputs& in, float* scores, int64_t score_stride, hipStream_t stream) {
   if (in.batch == 0) return 0;
-  if (in.row_to_batch && in.page_size % kGroup == 0 && in.heads <= 64) {
+  if (in.row_to_batch && !in.bf16 && in.page_size % kGroup == 0 && in.heads <= 64) {
     // rows sharing block-table rows: two rows per wave against one key load
     int64_t chunk = static_cast<int64_t>(PR_CHUNK_PAGES) * in.page_size;
     if (chunk > 8192) chunk = 8192 / in.page_size * in.page_size;
@@ -1251,39 +1258,46 @@ int launch_idx_score(const IndexerInputs& in, float* scores, int64_t score_strid
   const IndexerArgs a = make_args(in, chunk, true);
   const dim3 grid(chunk_grid(a));
   (void)hipGetLastError();
-  IDXTOPK_DISPATCH_NT(score_kernel, in.heads, grid, stream, a, scores, score_stride);
+  IDXTOPK_DISPATCH_NT(score_kernel, in.bf16, in.heads, grid, stream, a, scores, score_stride);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 // Workgroups of fused_scores_chunk_kernel that the current device holds at
 // once (all compute units, launched with the largest score LDS). Cached per
 // device and head count.
-static int fs_resident_wgs(int heads) {
-  static int cache[4][64] = {};
+static int fs_resident_wgs(int heads, bool bf) {
+  static int cache[2][4][64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   const int ti = heads == 16 ? 0 : heads == 32 ? 1 : heads == 64 ? 2 : 3;
-  if (cache[ti][dev] > 0) return cache[ti][dev];
+  if (cache[bf][ti][dev] > 0) return cache[bf][ti][dev];
   int cus = 0, per = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   const size_t lds = static_cast<size_t>(FS_CH_MAX) * sizeof(float);
   hipError_t e = hipErrorInvalidValue;
-  switch (heads) {
-    case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_scores_chunk_kernel<1>, IX_WG, lds); break;
-    case 32: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_scores_chunk_kernel<2>, IX_WG, lds); break;
-    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_scores_chunk_kernel<4>, IX_WG, lds); break;
-    case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_scores_chunk_kernel<8>, IX_WG, lds); break;
-    default: break;
+#define IDXTOPK_OCC(B)                                                                                          \
+  switch (heads) {                                                                                            \
+    case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_scores_chunk_kernel<1, B>, IX_WG, lds); break;   \
+    case 32: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_scores_chunk_kernel<2, B>, IX_WG, lds); break;   \
+    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_scores_chunk_kernel<4, B>, IX_WG, lds); break;   \
+    case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_scores_chunk_kernel<8, B>, IX_WG, lds); break;  \
+    default: break;                                                                                           \
   }
+  if (bf) {
+    IDXTOPK_OCC(true)
+  } else {
+    IDXTOPK_OCC(false)
+  }
+#undef IDXTOPK_OCC
   if (e != hipSuccess || per < 1) per = 1;
-  cache[ti][dev] = cus * per;
-  return cache[ti][dev];
+  cache[bf][ti][dev] = cus * per;
+  return cache[bf][ti][dev];
 }
 
 // Score-buffer path: chunks sized so the whole grid is resident at once.
 static int launch_fused_scores(const IndexerInputs& in, const FusedWs& w, const FusedOut& o, hipStream_t stream) {
   const int64_t tokens = static_cast<int64_t>(in.batch) * (in.max_seq_len > 0 ? in.max_seq_len : 1);
-  const int64_t nwg = fs_resident_wgs(in.heads);
+  const int64_t nwg = fs_resident_wgs(in.heads, in.bf16);
   int64_t ch = nwg > 0 ? (tokens + nwg - 1) / nwg : FS_CH_MAX;
   ch = (ch + kGroup - 1) / kGroup * kGroup;
   if (ch < FS_CH_MIN) ch = FS_CH_MIN;
@@ -1294,7 +1308,7 @@ static int launch_fused_scores(const IndexerInputs& in, const FusedWs& w, const 
   const dim3 grid(chunk_grid(a));
   const size_t lds = static_cast<size_t>(ch) * sizeof(float);
   (void)hipGetLastError();
-  IDXTOPK_DISPATCH_NT_LDS(fused_scores_chunk_kernel, in.heads, grid, lds, stream, a, w);
+  IDXTOPK_DISPATCH_NT_LDS(fused_scores_chunk_kernel, in.bf16, in.heads, grid, lds, stream, a, w);
   hipLaunchKernelGGL(fused_scores_merge_kernel, dim3(in.batch), dim3(FS_WG), 0, stream, a, w, o);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
@@ -1330,31 +1344,38 @@ static int launch_fused_select(const IndexerInputs& in, const FusedWs& w, const 
   // the scores' dynamic LDS plus the static part stay within 64 KB
   static_assert(FU_CH_MAX * 4 + sizeof(ChunkLds) <= 64 * 1024, "fused chunk LDS");
   const size_t lds = static_cast<size_t>(chunk) * sizeof(float);
-  IDXTOPK_DISPATCH_NT_LDS(fused_chunk_kernel, in.heads, grid, lds, stream, a, w, k);
+  IDXTOPK_DISPATCH_NT_LDS(fused_chunk_kernel, in.bf16, in.heads, grid, lds, stream, a, w, k);
   hipLaunchKernelGGL(fused_merge_kernel, dim3(in.batch), dim3(MG_WG), 0, stream, a, w, o);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 // Workgroups of block_chunk_kernel that the current device holds at once.
-static int bk_resident_wgs(int heads) {
-  static int cache[4][64] = {};
+static int bk_resident_wgs(int heads, bool bf) {
+  static int cache[2][4][64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   const int ti = heads == 16 ? 0 : heads == 32 ? 1 : heads == 64 ? 2 : 3;
-  if (cache[ti][dev] > 0) return cache[ti][dev];
+  if (cache[bf][ti][dev] > 0) return cache[bf][ti][dev];
   int cus = 0, per = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   hipError_t e = hipErrorInvalidValue;
-  switch (heads) {
-    case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, block_chunk_kernel<1>, IX_WG, 0); break;
-    case 32: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, block_chunk_kernel<2>, IX_WG, 0); break;
-    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, block_chunk_kernel<4>, IX_WG, 0); break;
-    case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, block_chunk_kernel<8>, IX_WG, 0); break;
-    default: break;
+#define IDXTOPK_OCC(B)                                                                                          \
+  switch (heads) {                                                                                            \
+    case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, block_chunk_kernel<1, B>, IX_WG, 0); break;   \
+    case 32: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, block_chunk_kernel<2, B>, IX_WG, 0); break;   \
+    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, block_chunk_kernel<4, B>, IX_WG, 0); break;   \
+    case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, block_chunk_kernel<8, B>, IX_WG, 0); break;  \
+    default: break;                                                                                           \
   }
+  if (bf) {
+    IDXTOPK_OCC(true)
+  } else {
+    IDXTOPK_OCC(false)
+  }
+#undef IDXTOPK_OCC
   if (e != hipSuccess || per < 1) per = 1;
-  cache[ti][dev] = cus * per;
-  return cache[ti][dev];
+  cache[bf][ti][dev] = cus * per;
+  return cache[bf][ti][dev];
 }
 
 int launch_block_topk(const IndexerInputs& in, int block_size, int top_blocks, int32_t* out_blocks,
@@ -1365,7 +1386,7 @@ int launch_block_topk(const IndexerInputs& in, int block_size, int top_blocks, i
   // of at most 8192 tokens, size the chunks for exactly that: every chunk
   // then runs at once, and each amortises its setup over more tokens.
   const int64_t tokens = static_cast<int64_t>(in.batch) * (in.max_seq_len > 0 ? in.max_seq_len : 1);
-  const int64_t nwg = bk_resident_wgs(in.heads);
+  const int64_t nwg = bk_resident_wgs(in.heads, in.bf16);
   if (nwg > 0 && tokens <= nwg * 8192) {
     int64_t ch = (tokens + nwg - 1) / nwg;
     ch = (ch + block_size - 1) / block_size * block_size;
@@ -1383,7 +1404,7 @@ int launch_block_topk(const IndexerInputs& in, int block_size, int top_blocks, i
   o.bs = block_size;
   const dim3 grid(chunk_grid(a));
   (void)hipGetLastError();
-  IDXTOPK_DISPATCH_NT(block_chunk_kernel, in.heads, grid, stream, a, w, block_size);
+  IDXTOPK_DISPATCH_NT(block_chunk_kernel, in.bf16, in.heads, grid, stream, a, w, block_size);
   hipLaunchKernelGGL(block_merge_kernel, dim3(in.batch), dim3(MG_WG), 0, stream, a, w, o);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

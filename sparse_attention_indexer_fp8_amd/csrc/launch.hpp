@@ -55,6 +55,7 @@ struct IndexerInputs {
   int32_t batch;
   int32_t heads;
   int32_t max_seq_len;
+  bool bf16 = false;  // bf16 index cache: q and kcache hold bf16, no scales
 };
 
 int launch_idx_score(const IndexerInputs& in, float* scores, int64_t score_stride, hipStream_t stream);
@@ -67,6 +68,8 @@ size_t block_workspace_bytes(int rows, int block_size, int max_seq_len);
 
 int launch_cache_write(const void* keys, bool bf16, int64_t stride, int tokens, const int32_t* slots,
                        uint8_t* kcache, float* kscale, hipStream_t stream);
+int launch_cache_write_bf16(const void* keys, bool bf16_in, int64_t stride, int tokens, const int32_t* slots,
+                            uint16_t* kcache, hipStream_t stream);
 int launch_block_topk(const IndexerInputs& in, int block_size, int top_blocks, int32_t* out_blocks,
                       int32_t* out_slots, void* ws, hipStream_t stream);
 

@@ -27,6 +27,7 @@ namespace idxtopk {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kDim = 128;
 constexpr int kGroup = 16;  // tokens per MFMA column block
@@ -380,6 +381,182 @@ __device__ void score_chunk(const IndexerArgs& a, int b, int tok_begin, int tok_
     score_chunk_impl<NT, WG, RING, true>(a, b, tok_begin, tok_end, lds_pages, emit);
   else
     score_chunk_impl<NT, WG, RING, false>(a, b, tok_begin, tok_end, lds_pages, emit);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 index cache: bf16 queries [B][H][128] and keys [slot][128] (256 bytes
+// per token), no scales. v_mfma_f32_16x16x32_bf16 contracts 32 dimensions:
+// lane (c, g) of the B operand holds 8 dimensions of token c, and the four
+// instructions of a 16-token group take dimensions [32s, 32s + 32), lane
+// group g the eight at 32s + 8g. One load instruction per s then covers 64
+// contiguous bytes of each of the group's 16 tokens. The accumulator layout
+// is the fp8 instruction's (lane (c, g) holds heads 4g .. 4g + 3 of token
+// c), so the weighted-ReLU head sum is score16's.
+// ---------------------------------------------------------------------------
+
+template <int NT>
+struct QOperandBF {
+  v4i a[NT][4];
+  float wt[NT][4];
+};
+
+struct KeyPiecesBF {
+  v4i x[4];
+};
+
+template <int NT>
+__device__ __forceinline__ void load_query_bf16(QOperandBF<NT>& qo, const uint8_t* q_row, const float* w_row) {
+  const int l = lane_id();
+  const int c = l & 15, g = l >> 4;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl)
+      qo.a[t][sl] = *reinterpret_cast<const v4i*>(q_row + ((16 * t + c) * kDim + 32 * sl + 8 * g) * 2);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) qo.wt[t][r] = w_row[16 * t + 4 * g + r];
+  }
+}
+
+// Score of token (tok0 + (lane & 15)) from a bf16 key group, in every lane.
+template <int NT>
+__device__ __forceinline__ float score16_bf16(const QOperandBF<NT>& qo, const KeyPiecesBF& kp) {
+  v4f acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, qo.a[t][sl]),
+                                                       __builtin_bit_cast(v8bf, kp.x[sl]), acc[t], 0, 0, 0);
+  }
+  float part = 0.0f;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part = fmaf(qo.wt[t][r], relu_bits(acc[t][r]), part);
+  }
+  const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part),
+                                                    false, false);
+  part = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
+                                                    false, false);
+  return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+}
+
+// score_chunk_impl for a bf16 cache: the same chunk staging, wave split,
+// ring discipline and emit contract; a group's keys are four 16-byte loads
+// per lane (token c, dimensions 32s + 8g .. + 8) and need no rearranging.
+template <int NT, int WG, int RING, bool WHOLE, class Emit>
+__device__ __forceinline__ void score_chunk_bf16_impl(const IndexerArgs& a, int b, int tok_begin, int tok_end,
+                                                      int32_t* lds_pages, Emit&& emit) {
+  constexpr int NW = WG / kWave;
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid / kWave);
+  const int l = lane_id();
+  const int c = l & 15, g = l >> 4;
+  const uint32_t P = static_cast<uint32_t>(a.page_size);
+
+  const uint32_t p0 = fdiv(static_cast<uint32_t>(tok_begin), a.pdiv);
+  const uint32_t p1 = fdiv(static_cast<uint32_t>(tok_end - 1), a.pdiv);
+  const int32_t* bt_row = bt_row_of(a, b);
+  for (int i = tid; i <= static_cast<int>(p1 - p0); i += WG) lds_pages[i] = bt_row[p0 + i];
+
+  QOperandBF<NT> qo;
+  load_query_bf16<NT>(qo, a.q + static_cast<int64_t>(b) * a.heads * kDim * 2, a.w + static_cast<int64_t>(b) * a.heads);
+  __syncthreads();
+
+  const int ngroups = (tok_end - tok_begin + kGroup - 1) / kGroup;
+  const int per = (ngroups + NW - 1) / NW;
+  const int g_lo = wave * per;
+  const int g_hi = min(ngroups, g_lo + per);
+  const int last = tok_end - 1;
+
+  // token j (clamped into the chunk) -> its cache slot (multiply and add kept
+  // apart, as in score_chunk_impl)
+  auto slot_of = [&](int j) {
+    j = j < last ? j : last;
+    const uint32_t pg = fdiv(static_cast<uint32_t>(j), a.pdiv);
+    uint32_t m = (static_cast<uint32_t>(lds_pages[pg - p0]) - pg) * P;
+    asm volatile("" : "+v"(m));
+    return m + static_cast<uint32_t>(j);
+  };
+  const int lp = 16 * g;
+  auto fetch = [&](int gi, KeyPiecesBF& kp) {
+    const int j0 = tok_begin + gi * kGroup;
+    uint32_t slot;
+    if (WHOLE) {
+      const uint32_t pg = fdiv(static_cast<uint32_t>(j0), a.pdiv);
+      uint32_t m = (static_cast<uint32_t>(uniform(lds_pages[pg - p0])) - pg) * P;
+      asm volatile("" : "+s"(m));
+      slot = m + static_cast<uint32_t>(j0) + c;
+    } else {
+      slot = slot_of(j0 + c);
+    }
+    const uint8_t* row = a.kcache + (static_cast<uint64_t>(slot) << 8) + lp;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) kp.x[sl] = load_v4i_stream(row + 64 * sl);
+  };
+
+  if (g_lo >= g_hi) return;
+  const int gmax = g_hi - 1;
+  auto consume = [&](int gi, float s) {
+    const int j = tok_begin + gi * kGroup + c;
+    emit(j, s, g == 0 && j < tok_end);
+  };
+
+  KeyPiecesBF ring[RING];
+#pragma unroll
+  for (int u = 0; u < RING; ++u) fetch(min(g_lo + u, gmax), ring[u]);
+
+  int gi0 = g_lo;
+  for (; gi0 + 2 * RING <= g_hi; gi0 += RING) {
+#pragma unroll
+    for (int u = 0; u < RING; ++u) {
+      float s = score16_bf16<NT>(qo, ring[u]);
+      asm volatile("" : "+v"(s));
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(gi0 + u + RING, ring[u]);
+      consume(gi0 + u, s);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < RING; ++u) {
+    const int gi = gi0 + u;
+    if (gi < g_hi) {
+      const float s = score16_bf16<NT>(qo, ring[u]);
+      if (gi + RING < g_hi) fetch(gi + RING, ring[u]);
+      consume(gi, s);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < RING; ++u) {
+    const int gi = gi0 + RING + u;
+    if (gi < g_hi) consume(gi, score16_bf16<NT>(qo, ring[u]));
+  }
+}
+
+// Score a chunk from a bf16 cache. A bf16 group is twice an fp8 group's
+// bytes, so half the ring depth keeps the same bytes in flight.
+template <int NT, int WG, int RING, class Emit>
+__device__ void score_chunk_bf16(const IndexerArgs& a, int b, int tok_begin, int tok_end, int32_t* lds_pages,
+                                 Emit&& emit) {
+  constexpr int R = RING > 2 ? RING / 2 : RING;
+  if (a.page_size % kGroup == 0 && tok_begin % kGroup == 0)
+    score_chunk_bf16_impl<NT, WG, R, true>(a, b, tok_begin, tok_end, lds_pages, emit);
+  else
+    score_chunk_bf16_impl<NT, WG, R, false>(a, b, tok_begin, tok_end, lds_pages, emit);
+}
+
+// Either cache format.
+template <bool BF, int NT, int WG, int RING, class Emit>
+__device__ __forceinline__ void score_chunk_any(const IndexerArgs& a, int b, int tok_begin, int tok_end,
+                                                int32_t* lds_pages, Emit&& emit) {
+  if constexpr (BF)
+    score_chunk_bf16<NT, WG, RING>(a, b, tok_begin, tok_end, lds_pages, emit);
+  else
+    score_chunk<NT, WG, RING>(a, b, tok_begin, tok_end, lds_pages, emit);
 }
 
 }  // namespace idxtopk

@@ -222,3 +222,93 @@ def idx_cache_write(keys: torch.Tensor, slot_mapping: torch.Tensor, kcache: torc
     st = _lib.load().idx_cache_write(_ptr(keys), dt, keys.stride(0), T, D, _ptr(slot_mapping),
                                      _ptr(_as_u8(kcache)), _ptr(k_scale), _stream())
     _lib.check("idx_cache_write", st)
+
+
+# ---------------------------------------------------------------------------
+# bf16 index cache: q [B, H, 128] and kcache [slots, 128] as bf16 (or their
+# 16-bit patterns as int16 / uint16), no scales.
+# ---------------------------------------------------------------------------
+
+_BF = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _indexer_args_bf16(q, w, kcache, block_table, seq_lens, row_to_batch=None):
+    _need(q, "q", _BF, 3)
+    _need(w, "w", (torch.float32,), 2)
+    _need(kcache, "kcache", _BF, 2)
+    _need(block_table, "block_table", (torch.int32,), 2, contiguous=False)
+    if block_table.stride(1) != 1:
+        raise ValueError("block_table rows must be contiguous")
+    _need(seq_lens, "seq_lens", (torch.int32,), 1)
+    if row_to_batch is not None:
+        _need(row_to_batch, "row_to_batch", (torch.int32,), 1)
+    B, H, D = q.shape
+    return [_ptr(q), _ptr(w), _ptr(kcache), _ptr(block_table), block_table.stride(0)], B, H, D
+
+
+def idx_score_bf16(q, w, kcache, block_table, seq_lens, page_size: int, max_seq_len: int,
+                   out: Optional[torch.Tensor] = None, row_to_batch: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Index scores from a bf16 index cache (other cells of `out` untouched)."""
+    args, B, H, D = _indexer_args_bf16(q, w, kcache, block_table, seq_lens, row_to_batch)
+    if out is None:
+        out = torch.full((B, max(1, max_seq_len)), float("nan"), dtype=torch.float32, device=q.device)
+    _need(out, "out", (torch.float32,), 2, contiguous=False)
+    st = _lib.load().idx_score_bf16(*args, int(page_size), _ptr(row_to_batch), _ptr(seq_lens), B, H, D,
+                                    int(max_seq_len), _ptr(out), out.stride(0), _stream())
+    _lib.check("idx_score_bf16", st)
+    return out
+
+
+def idx_score_topk_fused_bf16(q, w, kcache, block_table, seq_lens, page_size: int, max_seq_len: int, k: int,
+                              return_scores: bool = False, workspace: Optional[Workspace] = None,
+                              out: Optional[torch.Tensor] = None, out_scores: Optional[torch.Tensor] = None,
+                              row_to_batch: Optional[torch.Tensor] = None, sorted: bool = False):
+    """Fused decode indexer from a bf16 index cache: top-k slots per row (and
+    their scores if asked); `sorted` as in idx_score_topk_fused."""
+    args, B, H, D = _indexer_args_bf16(q, w, kcache, block_table, seq_lens, row_to_batch)
+    if out is None:
+        out = torch.empty((B, k), dtype=torch.int32, device=q.device)
+    if return_scores and out_scores is None:
+        out_scores = torch.empty((B, k), dtype=torch.float32, device=q.device)
+    nbytes = workspace_bytes(_lib.OP_SCORE_TOPK_FUSED, B, k, max_seq_len)
+    ws = _workspace(workspace).get(nbytes)
+    st = _lib.load().idx_score_topk_fused_bf16(*args, int(page_size), _ptr(row_to_batch), _ptr(seq_lens), B, H, D,
+                                               int(max_seq_len), int(k), _ptr(out), _ptr(out_scores),
+                                               _ptr(ws), ws.numel(), _lib.SORTED if sorted else 0, _stream())
+    _lib.check("idx_score_topk_fused_bf16", st)
+    return (out, out_scores) if return_scores else out
+
+
+def block_topk_bf16(q, w, kcache, block_table, seq_lens, page_size: int, max_seq_len: int, block_size: int,
+                    top_blocks: int, return_slots: bool = True, workspace: Optional[Workspace] = None,
+                    row_to_batch: Optional[torch.Tensor] = None):
+    """Top blocks per row from a bf16 index cache (and expanded slot lists)."""
+    args, B, H, D = _indexer_args_bf16(q, w, kcache, block_table, seq_lens, row_to_batch)
+    out_blocks = torch.empty((B, top_blocks), dtype=torch.int32, device=q.device)
+    out_slots = (torch.empty((B, top_blocks * block_size), dtype=torch.int32, device=q.device)
+                 if return_slots else None)
+    nbytes = workspace_bytes(_lib.OP_BLOCK_TOPK, B, block_size, max_seq_len)
+    ws = _workspace(workspace).get(nbytes)
+    st = _lib.load().block_topk_bf16(*args, int(page_size), _ptr(row_to_batch), _ptr(seq_lens), B, H, D,
+                                     int(max_seq_len), int(block_size), int(top_blocks), _ptr(out_blocks),
+                                     _ptr(out_slots), _ptr(ws), ws.numel(), _stream())
+    _lib.check("block_topk_bf16", st)
+    return (out_blocks, out_slots) if return_slots else out_blocks
+
+
+def idx_cache_write_bf16(keys: torch.Tensor, slot_mapping: torch.Tensor, kcache: torch.Tensor) -> None:
+    """Store new index keys (fp32 rounded to nearest even, or bf16 as they
+    are; [tokens, 128], rows contiguous and 16-byte aligned) into the bf16
+    cache at kcache[slot] for every non-negative slot. In place."""
+    if keys.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"keys: expected float32 or bfloat16, got {keys.dtype}")
+    _need(keys, "keys", (keys.dtype,), 2, contiguous=False)
+    if keys.stride(1) != 1:
+        raise ValueError("keys rows must be contiguous")
+    _need(slot_mapping, "slot_mapping", (torch.int32,), 1)
+    _need(kcache, "kcache", _BF, 2)
+    T, D = keys.shape
+    dt = _lib.KEY_BF16 if keys.dtype == torch.bfloat16 else _lib.KEY_F32
+    st = _lib.load().idx_cache_write_bf16(_ptr(keys), dt, keys.stride(0), T, D, _ptr(slot_mapping), _ptr(kcache),
+                                          _stream())
+    _lib.check("idx_cache_write_bf16", st)

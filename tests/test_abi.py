@@ -186,3 +186,54 @@ def test_binding_imports_without_gpu():
     from sparse_attention_indexer_fp8_amd import ops
 
     assert pkg.topk_rows is ops.topk_rows and pkg.ops is ops
+
+
+def _indexer_bf16(**kw):
+    a = dict(q=FAKE, w=FAKE, kc=FAKE, bt=FAKE, bts=256, P=64, r2b=NULL, sl=FAKE, B=32, H=64, D=128, msl=16384)
+    a.update(kw)
+    return [a["q"], a["w"], a["kc"], a["bt"], a["bts"], a["P"], a["r2b"], a["sl"], a["B"], a["H"], a["D"], a["msl"]]
+
+
+MISALIGNED = ctypes.c_void_p(0x1008)
+
+
+def test_bf16_validation(lib):
+    f = lambda out=FAKE, ss=16384, **kw: lib.idx_score_bf16(*_indexer_bf16(**kw), out, ss, NULL)
+    assert f(q=MISALIGNED) == -1     # 16-byte rows
+    assert f(kc=MISALIGNED) == -1
+    assert f(w=NULL) == -1
+    assert f(H=48) == -2
+    assert f(D=64) == -2
+    assert f(ss=100) == -1
+    assert f(B=0) == 0
+    need = lib.idxtopk_workspace_bytes(4, 32, 2048, 16384)
+    g = lambda k=2048, ws=FAKE, nb=need, flags=0, **kw: lib.idx_score_topk_fused_bf16(
+        *_indexer_bf16(**kw), k, FAKE, NULL, ws, nb, flags, NULL)
+    assert g(k=0) == -1
+    assert g(k=8193) == -2
+    assert g(flags=2) == -1
+    assert g(ws=NULL) == -3
+    assert g(kc=MISALIGNED) == -1
+    assert g(B=0) == 0
+    nb = lib.idxtopk_workspace_bytes(5, 32, 128, 32768)
+    h = lambda bs=128, top=32, **kw: lib.block_topk_bf16(*_indexer_bf16(**{"P": 128, "msl": 32768, **kw}), bs, top,
+                                                         FAKE, NULL, FAKE, nb, NULL)
+    assert h(bs=64) == -2
+    assert h(top=0) == -1
+    assert h(q=MISALIGNED) == -1
+    assert h(B=0) == 0
+
+
+def test_cache_write_bf16_validation(lib):
+    f = lambda keys=FAKE, dt=0, ks=128, T=16, D=128, sm=FAKE, kc=FAKE: lib.idx_cache_write_bf16(
+        keys, dt, ks, T, D, sm, kc, NULL)
+    assert f(dt=5) == -2
+    assert f(D=64) == -2
+    assert f(T=-1) == -1
+    assert f(keys=NULL) == -1
+    assert f(ks=100) == -1                # stride below dim
+    assert f(ks=130) == -1                # fp32 rows 520 bytes apart: not 16-byte aligned
+    assert f(dt=1, ks=132) == -1          # bf16 rows 264 bytes apart
+    assert f(keys=MISALIGNED) == -1
+    assert f(kc=MISALIGNED) == -1
+    assert f(T=0) == 0

@@ -335,7 +335,7 @@ def multi_query_case(seed: int, requests: int, next_n: int, n_lo: int, n_hi: int
 # The five named workloads (full size) and reduced versions for quick tests
 # --------------------------------------------------------------------------
 
-SEEDS = {"c1": 101, "c2": 102, "c3": 103, "c4": 104, "c5": 105, "mtp": 106, "bf16": 107}
+SEEDS = {"c1": 101, "c2": 102, "c3": 103, "c4": 104, "c5": 105, "mtp": 106, "bf16": 107, "bf16l": 108}
 
 
 def c1_decode_topk() -> RowsCase:
@@ -376,6 +376,13 @@ def bf16_decode() -> IndexerCase:
                         name="fused-decode-bf16-B32-n8k-16k-k2048", cache_dtype="bf16")
 
 
+def bf16_long_decode() -> IndexerCase:
+    """The long-decode geometry (64 rows, n ~ U{131072..327680}, page 64, k
+    2048) from a bf16 index cache."""
+    return indexer_case(SEEDS["bf16l"], batch=64, n_lo=131072, n_hi=327680, page_size=64, k=2048,
+                        name="long-decode-bf16-B64-n128k-320k-k2048", cache_dtype="bf16")
+
+
 def prefill_indexer() -> IndexerCase:
     """Packed prefill from the fp8 cache, in the packed-prefill top-k
     geometry: request 0 has 61808 cached tokens and request 1 none, each
@@ -397,6 +404,6 @@ def ceil_div(a: int, b: int) -> int:
 __all__ = [
     "RowsCase", "IndexerCase", "decode_rows_case", "packed_prefill_case", "indexer_case", "multi_query_case",
     "c1_decode_topk", "c2_fused_decode", "c3_packed_prefill", "c4_block_sparse", "c5_long_decode", "mtp_decode",
-    "prefill_indexer", "bf16_decode", "SENTINEL_KEY_BF16",
+    "prefill_indexer", "bf16_decode", "bf16_long_decode", "SENTINEL_KEY_BF16",
     "SEEDS", "SENTINEL_KEY_BYTE", "SENTINEL_KEY_SCALE", "rng", "expected_tokens", "ceil_div",
 ]
