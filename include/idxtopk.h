@@ -144,10 +144,18 @@ int idx_score_fp8(const uint8_t* q, const float* q_scale, const float* w,
  * row_to_batch the caller owns the page-table bound. The window may start at
  * any column, and score_stride need not be a multiple of 4.
  *
- * out int32 [rows, k]: for each row, the k best row-local positions, mapped to
+ * kv_offset (optional, int32 [rows]): for a call that sees one chunk of each
+ * request's KV (chunked-prefix-cache extend, the shape [SGL-37889]
+ * Modifications leaves to its legacy path: the addressing plan covers the
+ * whole forward, the call one chunk), the KV position of row i's window
+ * column 0. A selected window position t becomes p = t + kv_offset[i]
+ * (default 0) before the transform; the caller owns the page-table bound
+ * of p.
+ *
+ * out int32 [rows, k]: for each row, the k best positions p, mapped to
  * physical slots page_table[prow * pt_stride + p / page_size] * page_size +
  * p % page_size, or the positions themselves when page_table is NULL; -1 pads
- * rows with seq_lens[i] < k.
+ * rows with seq_lens[i] < k. Equal scores go to the lower position.
  *
  * flags: 0, or IDXTOPK_SORTED for rows in sorted order (otherwise the order
  * within a row is unspecified); any other bit gives IDXTOPK_EINVAL.
@@ -156,7 +164,7 @@ int idx_score_fp8(const uint8_t* q, const float* q_scale, const float* w,
  */
 int topk_rows(const float* scores, int64_t score_stride, int32_t rows,
               const int32_t* seq_lens, const int32_t* row_starts, const int32_t* row_to_batch,
-              const int32_t* page_table, int64_t pt_stride, int32_t page_size,
+              const int32_t* kv_offset, const int32_t* page_table, int64_t pt_stride, int32_t page_size,
               int32_t k, int32_t* out, int32_t flags, void* stream);
 
 /*

@@ -105,7 +105,7 @@ def topk_order(values: np.ndarray, k: int) -> np.ndarray:
 
 
 def topk_rows(scores: np.ndarray, seq_lens, k: int, row_starts=None, row_to_batch=None,
-              page_table=None, page_size: int = 1, rows=None) -> np.ndarray:
+              page_table=None, page_size: int = 1, rows=None, kv_offset=None) -> np.ndarray:
     """Top-k with page transform over an fp32 score buffer, row by row.
 
     [SGL-37889], Modifications: each row's window comes from the addressing
@@ -113,11 +113,20 @@ def topk_rows(scores: np.ndarray, seq_lens, k: int, row_starts=None, row_to_batc
     (``topk_order``), and the page-table row ``page_row`` maps them to slots
     (``page_transform``). With ``page_table=None`` the row-local positions
     are returned. ``rows`` picks a subset of rows (default: all).
+
+    ``kv_offset`` (per row, default 0): [SGL-37889] sends chunked-prefix-cache
+    extend, where the plan covers the whole forward but a call sees one
+    chunk, to its legacy path. READING: the window of row i then holds KV
+    positions kv_offset[i] .. kv_offset[i] + seq_lens[i] - 1, so each kept
+    window position gets kv_offset[i] added before the transform; -1
+    padding stays -1.
     """
     rows = range(int(np.asarray(seq_lens).shape[0])) if rows is None else list(rows)
     out = []
     for i in rows:
         pos = topk_order(row_window(scores, i, seq_lens, row_starts), k)
+        if kv_offset is not None:
+            pos = np.where(pos >= 0, pos + int(kv_offset[i]), -1)
         if page_table is not None:
             pos = page_transform(pos, page_table[page_row(i, row_to_batch)], page_size)
         out.append(pos)

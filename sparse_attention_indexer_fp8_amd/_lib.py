@@ -37,7 +37,7 @@ _sz = ctypes.c_size_t
 SIGNATURES = {
     "idx_score_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32, _i32,
                              _i32, _vp, _i64, _vp]),
-    "topk_rows": (_i32, [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _i32, _vp]),
+    "topk_rows": (_i32, [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _i32, _vp]),
     "topk_page_transform": (_i32, [_vp, _i32, _i32, _vp, _i64, _i32, _vp, _vp, _vp]),
     "idx_score_topk_fused": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32,
                                     _i32, _i32, _i32, _vp, _vp, _vp, _sz, _i32, _vp]),

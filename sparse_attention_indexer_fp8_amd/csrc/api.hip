@@ -75,14 +75,15 @@ int idx_score_fp8(const uint8_t* q, const float* q_scale, const float* w, const 
 }
 
 int topk_rows(const float* scores, int64_t score_stride, int32_t rows, const int32_t* seq_lens,
-              const int32_t* row_starts, const int32_t* row_to_batch, const int32_t* page_table,
+              const int32_t* row_starts, const int32_t* row_to_batch, const int32_t* kv_offset,
+              const int32_t* page_table,
               int64_t pt_stride, int32_t page_size, int32_t k, int32_t* out, int32_t flags, void* stream) {
   if (rows < 0 || k <= 0 || score_stride < 0 || (flags & ~IDXTOPK_SORTED)) return IDXTOPK_EINVAL;
   if (rows > 0 && (!scores || !seq_lens || !out)) return IDXTOPK_EINVAL;
   if (page_table && (pt_stride < 0 || page_size <= 0)) return IDXTOPK_EINVAL;
   if (k > IDXTOPK_MAX_K_ROWS) return IDXTOPK_EUNSUPPORTED;
   if (rows == 0) return IDXTOPK_OK;
-  return idxtopk::launch_topk_rows(scores, score_stride, rows, seq_lens, row_starts, row_to_batch,
+  return idxtopk::launch_topk_rows(scores, score_stride, rows, seq_lens, row_starts, row_to_batch, kv_offset,
                                    page_table, pt_stride, page_table ? page_size : 1, k, out,
                                    (flags & IDXTOPK_SORTED) != 0, static_cast<hipStream_t>(stream));
 }

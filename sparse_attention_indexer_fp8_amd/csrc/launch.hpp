@@ -24,7 +24,7 @@ inline hipError_t allow_dynamic_lds(const void* kernel, size_t bytes, std::atomi
 
 // All return 0 or -4 (launch failure); arguments are already validated.
 int launch_topk_rows(const float* scores, int64_t stride, int rows, const int32_t* seq_lens,
-                     const int32_t* row_starts, const int32_t* row_to_batch,
+                     const int32_t* row_starts, const int32_t* row_to_batch, const int32_t* kv_offset,
                      const int32_t* page_table, int64_t pt_stride, int page_size, int k,
                      int32_t* out, bool sorted, hipStream_t stream);
 

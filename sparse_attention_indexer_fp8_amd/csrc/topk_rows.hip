@@ -54,6 +54,7 @@ struct RowsArgs {
   const int32_t* seq_lens;
   const int32_t* row_starts;
   const int32_t* row_to_batch;
+  const int32_t* kv_offset;  // per row: KV position of the window's column 0, or null (0)
   const int32_t* page_table;
   int64_t pt_stride;
   int32_t page_size;
@@ -94,6 +95,7 @@ struct RowCtx {
   const f4* vbase;
   const int32_t* pt_row;
   int32_t* out;
+  uint32_t off;  // added to every selected row-local position before the transform
   bool trivial;  // n <= k: every position is selected
 };
 
@@ -105,6 +107,7 @@ __device__ __forceinline__ RowCtx row_setup(const RowsArgs& a, int row) {
   const int prow = a.row_to_batch ? load_uniform(a.row_to_batch + row) : row;
   r.pt_row = a.page_table ? a.page_table + static_cast<int64_t>(prow) * a.pt_stride : nullptr;
   r.out = a.out + static_cast<int64_t>(row) * a.k;
+  r.off = a.kv_offset ? static_cast<uint32_t>(load_uniform(a.kv_offset + row)) : 0u;
   r.trivial = r.n <= a.k;
   r.base = a.scores + static_cast<int64_t>(row) * a.stride + rs;
   const uintptr_t addr = reinterpret_cast<uintptr_t>(r.base);
@@ -389,7 +392,7 @@ __device__ __forceinline__ bool stream_row(const RowCtx& r, f4 (&ring)[TR_RING][
 __device__ __forceinline__ void emit_all(const RowCtx& r, const RowsArgs& a) {
   const uint32_t P = static_cast<uint32_t>(a.page_size);
   for (int i = threadIdx.x; i < a.k; i += TR_WG)
-    r.out[i] = (i < r.n) ? map_slot(r.pt_row, static_cast<uint32_t>(i), P, a.pdiv) : -1;
+    r.out[i] = (i < r.n) ? map_slot(r.pt_row, static_cast<uint32_t>(i) + r.off, P, a.pdiv) : -1;
 }
 
 // Sorted output: keys[0, npow) (real entries first, then zeros) are put in
@@ -413,7 +416,7 @@ __device__ __forceinline__ void sort_emit_reg(const RowCtx& r, const RowsArgs& a
   uint32_t pg[E];
   int32_t page[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) pg[e] = x[e] ? fdiv(rank_pos(x[e]), a.pdiv) : 0u;
+  for (int e = 0; e < E; ++e) pg[e] = x[e] ? fdiv(rank_pos(x[e]) + r.off, a.pdiv) : 0u;
   if (r.pt_row && x[0]) {
     // zero keys read page 0, which exists when this thread holds any entry
 #pragma unroll
@@ -423,7 +426,7 @@ __device__ __forceinline__ void sort_emit_reg(const RowCtx& r, const RowsArgs& a
   for (int e = 0; e < E; ++e) {
     const int i = tid * E + e;
     if (i < a.k) {
-      const uint32_t pos = rank_pos(x[e]);
+      const uint32_t pos = rank_pos(x[e]) + r.off;
       r.out[i] = !x[e] ? -1
                : r.pt_row ? static_cast<int32_t>(static_cast<int64_t>(page[e]) * P + (pos - pg[e] * P))
                           : static_cast<int32_t>(pos);
@@ -459,7 +462,7 @@ __device__ __forceinline__ void sort_emit_lds(const RowCtx& r, const RowsArgs& a
     for (int j = 0; j < TR_EMIT; ++j) {
       const int i = i0 + j * TR_WG + tid;
       kk[j] = i < a.k ? keys[i] : 0ull;
-      pg[j] = kk[j] ? fdiv(rank_pos(kk[j]), a.pdiv) : 0u;
+      pg[j] = kk[j] ? fdiv(rank_pos(kk[j]) + r.off, a.pdiv) : 0u;
     }
     if (r.pt_row) {
       // all lookups issued before any is used; zero keys read page 0
@@ -470,7 +473,7 @@ __device__ __forceinline__ void sort_emit_lds(const RowCtx& r, const RowsArgs& a
     for (int j = 0; j < TR_EMIT; ++j) {
       const int i = i0 + j * TR_WG + tid;
       if (i < a.k) {
-        const uint32_t pos = rank_pos(kk[j]);
+        const uint32_t pos = rank_pos(kk[j]) + r.off;
         r.out[i] = !kk[j] ? -1
                  : r.pt_row ? static_cast<int32_t>(static_cast<int64_t>(base[j]) * P + (pos - pg[j] * P))
                             : static_cast<int32_t>(pos);
@@ -577,7 +580,7 @@ __global__ __launch_bounds__(TR_WG, 4) void topk_rows_kernel(RowsArgs a) {
       const uint32_t i = b0 + j * TR_WG + tid;
       const uint64_t key = cand[i < c ? i : 0];
       keep[j] = i < c && key >= T;
-      pos[j] = rank_pos(key);
+      pos[j] = rank_pos(key) + cur.off;
       mine += keep[j];
     }
     uint32_t at = wave_reserve(mine, &s.ocnt);
@@ -614,7 +617,7 @@ static inline int rows_cap(int k) {
 }
 
 int launch_topk_rows(const float* scores, int64_t stride, int rows, const int32_t* seq_lens,
-                     const int32_t* row_starts, const int32_t* row_to_batch,
+                     const int32_t* row_starts, const int32_t* row_to_batch, const int32_t* kv_offset,
                      const int32_t* page_table, int64_t pt_stride, int page_size, int k,
                      int32_t* out, bool sorted, hipStream_t stream) {
   RowsArgs a;
@@ -623,6 +626,7 @@ int launch_topk_rows(const float* scores, int64_t stride, int rows, const int32_
   a.seq_lens = seq_lens;
   a.row_starts = row_starts;
   a.row_to_batch = row_to_batch;
+  a.kv_offset = kv_offset;
   a.page_table = page_table;
   a.pt_stride = pt_stride;
   a.page_size = page_size > 0 ? page_size : 1;

@@ -82,16 +82,19 @@ def _workspace(ws: Optional[Workspace]) -> Workspace:
 def topk_rows(scores: torch.Tensor, seq_lens: torch.Tensor, k: int,
               row_starts: Optional[torch.Tensor] = None, row_to_batch: Optional[torch.Tensor] = None,
               page_table: Optional[torch.Tensor] = None, page_size: int = 1,
-              out: Optional[torch.Tensor] = None, sorted: bool = False) -> torch.Tensor:
+              out: Optional[torch.Tensor] = None, sorted: bool = False,
+              kv_offset: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Top-k of each row's fp32 window, mapped through the page table.
     sorted: each row in descending score order, equal scores by ascending
-    position, -1 padding last (else the order within a row is unspecified)."""
+    position, -1 padding last (else the order within a row is unspecified).
+    kv_offset: int32 per row, the KV position of the window's first column
+    when the call sees one chunk of each request's KV (default 0)."""
     _need(scores, "scores", (torch.float32,), 2, contiguous=False)
     if scores.stride(1) != 1:
         raise ValueError("scores rows must be contiguous")
     rows = scores.shape[0]
     _need(seq_lens, "seq_lens", (torch.int32,), 1)
-    for name, t in (("row_starts", row_starts), ("row_to_batch", row_to_batch)):
+    for name, t in (("row_starts", row_starts), ("row_to_batch", row_to_batch), ("kv_offset", kv_offset)):
         if t is not None:
             _need(t, name, (torch.int32,), 1)
     pt_stride = 0
@@ -104,7 +107,8 @@ def topk_rows(scores: torch.Tensor, seq_lens: torch.Tensor, k: int,
         out = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
     _need(out, "out", (torch.int32,), 2)
     st = _lib.load().topk_rows(_ptr(scores), scores.stride(0), rows, _ptr(seq_lens), _ptr(row_starts),
-                               _ptr(row_to_batch), _ptr(page_table), pt_stride, int(page_size), int(k),
+                               _ptr(row_to_batch), _ptr(kv_offset), _ptr(page_table), pt_stride, int(page_size),
+                               int(k),
                                _ptr(out), _lib.SORTED if sorted else 0, _stream())
     _lib.check("topk_rows", st)
     return out

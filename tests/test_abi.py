@@ -69,7 +69,7 @@ def _topk_rows(lib, **kw):
     a = dict(scores=FAKE, stride=4096, rows=8, seq_lens=FAKE, rs=NULL, r2b=NULL, pt=NULL, pts=0, P=1,
              k=512, out=FAKE, flags=0)
     a.update(kw)
-    return lib.topk_rows(a["scores"], a["stride"], a["rows"], a["seq_lens"], a["rs"], a["r2b"], a["pt"],
+    return lib.topk_rows(a["scores"], a["stride"], a["rows"], a["seq_lens"], a["rs"], a["r2b"], NULL, a["pt"],
                          a["pts"], a["P"], a["k"], a["out"], a["flags"], NULL)
 
 

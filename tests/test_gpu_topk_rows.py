@@ -272,3 +272,60 @@ def test_topk_rows_sorted_ties_and_packed(ops):
     ref = oracle.topk_rows(buf, case.seq_lens, case.k, case.row_starts, case.row_to_batch, case.page_table,
                            case.page_size)
     assert np.array_equal(out.cpu().numpy(), ref)
+
+
+# Chunked-prefix-cache extend: the call sees one chunk [c0, c1) of each
+# request's KV, so row i's window is the slice of its full window that falls
+# in the chunk, starting c0 columns later, and kv_offset = c0 puts the kept
+# positions back in the request's KV before the page transform.
+def _chunk_call(case, c0, c1):
+    n = case.seq_lens.astype(np.int64)
+    lens = np.clip(np.minimum(n, c1) - c0, 0, None).astype(np.int32)
+    starts = (case.row_starts.astype(np.int64) + c0).astype(np.int32)
+    off = np.full(case.rows, c0, np.int32)
+    return lens, starts, off
+
+
+@pytest.mark.parametrize("c0,c1,sorted_", [(0, 1 << 30, False), (1000, 5000, False), (4096, 9000, True),
+                                           (8000, 1 << 30, True)])
+def test_topk_rows_kv_offset_chunk(ops, c0, c1, sorted_):
+    import torch
+
+    case = workloads.packed_prefill_case(seed=43, prefix0=7000, new_tokens=256, k=512)
+    lens, starts, off = _chunk_call(case, c0, c1)
+    out = ops.topk_rows(dev(case.scores), dev(lens), case.k, row_starts=dev(starts),
+                        row_to_batch=dev(case.row_to_batch), page_table=dev(case.page_table), page_size=1,
+                        sorted=sorted_, kv_offset=dev(off))
+    torch.cuda.synchronize()
+    ref = oracle.topk_rows(case.scores, lens, case.k, starts, case.row_to_batch, case.page_table, 1,
+                           kv_offset=off)
+    got = out.cpu().numpy()
+    if sorted_:
+        assert np.array_equal(got, ref)
+    else:
+        assert np.array_equal(sorted_rows(got), sorted_rows(ref))
+    if c0 == 0:
+        full = _run_rows(ops, case.scores, case.seq_lens, case.k, case.row_starts, case.row_to_batch,
+                         case.page_table, 1)
+        assert np.array_equal(sorted_rows(got), sorted_rows(full))
+
+
+def test_topk_rows_kv_offset_paged_unaligned(ops):
+    """Per-row offsets that do not fall on page boundaries (page size 16),
+    and the unpaged output (positions in the request's KV)."""
+    import torch
+
+    case = workloads.c1_decode_topk()
+    g = np.random.default_rng(44)
+    rows = case.scores.shape[0]
+    off = g.integers(0, 3000, size=rows).astype(np.int32)
+    P = 16
+    width = (4096 + 3000) // P + 2
+    pt = np.stack([g.permutation(rows * width)[:width] for _ in range(rows)]).astype(np.int32)
+    for page_table in (pt, None):
+        out = ops.topk_rows(dev(case.scores), dev(case.seq_lens), case.k,
+                            page_table=None if page_table is None else dev(page_table), page_size=P,
+                            kv_offset=dev(off))
+        torch.cuda.synchronize()
+        ref = oracle.topk_rows(case.scores, case.seq_lens, case.k, page_table=page_table, page_size=P, kv_offset=off)
+        assert np.array_equal(sorted_rows(out.cpu().numpy()), sorted_rows(ref))

@@ -151,3 +151,24 @@ def test_negative_zero_generated_cases_live():
     case = workloads.decode_rows_case(seed=101)
     fin = case.scores[np.isfinite(case.scores)]
     assert ((fin == 0) & np.signbit(fin)).any()
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_kv_offset_against_brute_force(seed):
+    """A call over one chunk of each row's KV: the kept positions are the
+    window's best (heapq.nlargest keyed on (value, -position)) shifted by the
+    row's offset, then mapped; -1 padding stays -1."""
+    g = np.random.default_rng(300 + seed)
+    rows, stride, k = 4, 64, int(g.integers(1, 20))
+    buf = np.round(g.standard_normal((rows, stride)) * 2) / 2  # ties
+    lens = g.integers(0, 40, size=rows).astype(np.int32)
+    starts = g.integers(0, stride - 40, size=rows).astype(np.int32)
+    off = g.integers(0, 500, size=rows).astype(np.int32)
+    pt = g.permutation(4096).reshape(4, 1024).astype(np.int32)
+    r2b = g.integers(0, 4, size=rows).astype(np.int32)
+    got = topk_rows(buf, lens, k, starts, r2b, pt, 1, kv_offset=off)
+    for i in range(rows):
+        n, s0 = int(lens[i]), int(starts[i])
+        best = heapq.nlargest(k, range(n), key=lambda t: (buf[i, s0 + t], -t))
+        exp = [int(pt[r2b[i], t + off[i]]) for t in best] + [-1] * (k - len(best))
+        assert got[i].tolist() == exp
