@@ -36,11 +36,13 @@ from .fp8 import E4M3FN_TABLE, decode_e4m3fn, encode_e4m3fn  # noqa: F401
 from .indexer import (  # noqa: F401
     block_scores,
     block_topk,
+    block_topk_heads,
     cache_write,
     cache_write_bf16,
     index_scores_bf16,
     quantize_key,
     fused_topk,
+    index_head_scores,
     index_scores,
     page_transform,
     token_slots,

@@ -190,6 +190,22 @@ def index_scores_bf16(q_b, w_b, kcache, bt_row, page_size: int, n: int) -> np.nd
     return (np.maximum(dot, 0.0) * _f64(w_b)[None, :]).sum(axis=1)
 
 
+def index_head_scores(q_b, q_scale_b, w_b, kcache, k_scale, bt_row, page_size: int, n: int) -> np.ndarray:
+    """Each head's term of the fp8 index score, [n, H] in float64:
+    T[j, h] = w[h] * max(0, s_q * s_k[slot_j] * dot(qhat_h, khat[slot_j])).
+
+    The index score is the sum of these terms over the heads
+    (``index_scores``). [ATOM-1473], Pull request overview: the partial top-k
+    kernel's grid has an index-head axis. READING for the per-head variant:
+    each head ranks keys by its own term.
+    """
+    qd = decode_e4m3fn(q_b)  # [H, D]
+    slots = token_slots(bt_row, page_size, n)
+    kd = decode_e4m3fn(np.asarray(kcache)[slots])  # [n, D]
+    logits = (kd @ qd.T) * float(q_scale_b) * _f64(np.asarray(k_scale)[slots])[:, None]
+    return np.maximum(logits, 0.0) * _f64(w_b)[None, :]
+
+
 def case_bt_row(case, b: int) -> np.ndarray:
     """Block-table row of query row b: ``row_to_batch[b]`` if the case has one,
     else b. Several query rows may share a block-table row (multi-token
@@ -288,6 +304,40 @@ def block_topk(case, rows=None, block_size=None, top_blocks=None):
         logical.append(sel)
         bscores.append(bsv)
     return np.stack(blocks), np.stack(slot_lists), np.stack(logical), bscores
+
+
+def block_topk_heads(case, rows=None, block_size=None, top_blocks=None):
+    """Per-head block selection: for every row b and head h, the top_blocks
+    best blocks by the head's own block score (the max of its term
+    ``index_head_scores`` over the block's visible tokens; ties to the lower
+    block id), as physical block ids and expanded slot lists, laid out
+    [R, H, top] and [R, H, top*bs] (fp8 index cache).
+
+    READING: [ATOM-1473]'s partial top-k grid runs over (query row, index
+    head, chunk); selecting per head is read as every head keeping its own
+    blocks, with the block rule of ``block_scores``.
+    """
+    bs = int(case.block_size if block_size is None else block_size)
+    top = int(case.top_blocks if top_blocks is None else top_blocks)
+    rows = range(case.batch) if rows is None else list(rows)
+    H = case.heads
+    blocks = np.full((len(rows), H, top), -1, np.int64)
+    slot_lists = np.full((len(rows), H, top * bs), -1, np.int64)
+    for ri, b in enumerate(rows):
+        n = int(case.seq_lens[b])
+        bt_row = case_bt_row(case, b)
+        tok_slots = token_slots(bt_row, case.page_size, n)
+        T = index_head_scores(case.q[b], case.q_scale[b], case.w[b], case.kcache, case.k_scale, bt_row,
+                              case.page_size, n)
+        for h in range(H):
+            bsv = block_scores(T[:, h], bs) if n > 0 else np.zeros(0)
+            for i, c in enumerate(topk_order(bsv, top)):
+                if c < 0:
+                    continue
+                blocks[ri, h, i] = int(bt_row[c * bs // case.page_size])
+                lo, hi = c * bs, min((c + 1) * bs, n)
+                slot_lists[ri, h, i * bs:i * bs + (hi - lo)] = tok_slots[lo:hi]
+    return blocks, slot_lists
 
 
 # ---------------------------------------------------------------------------

@@ -249,3 +249,33 @@ def test_multi_query_block_variant_matches_expanded():
     b = block_topk(flat, block_size=16, top_blocks=5)
     for x, y in zip(a[:3], b[:3]):
         assert np.array_equal(x, y)
+
+
+def test_head_terms_sum_to_index_score():
+    """The per-head terms add up to the (separately pinned) index score, and
+    each is the weight times a non-negative number."""
+    from oracle.indexer import case_bt_row, index_head_scores, index_scores
+
+    case = workloads.indexer_case(321, batch=2, n_lo=50, n_hi=400, page_size=16, k=8, heads=32)
+    for b in range(case.batch):
+        n = int(case.seq_lens[b])
+        args = (case.q[b], case.q_scale[b], case.w[b], case.kcache, case.k_scale, case_bt_row(case, b),
+                case.page_size, n)
+        T = index_head_scores(*args)
+        assert T.shape == (n, case.heads)
+        np.testing.assert_allclose(T.sum(axis=1), index_scores(*args), rtol=1e-12, atol=1e-12)
+        assert np.all(T * np.sign(case.w[b])[None, :] >= 0)
+
+
+def test_per_head_blocks_single_head_equal_block_topk():
+    """With one head of the 16 carrying weight and the rest weight 0, that
+    head's selection is the head-summed block selection."""
+    from oracle.indexer import block_topk, block_topk_heads
+
+    case = workloads.indexer_case(322, batch=2, n_lo=300, n_hi=2000, page_size=64, k=0, heads=16,
+                                  block_size=64, top_blocks=5)
+    case.w[:] = 0.0
+    case.w[:, 3] = 1.5
+    hb, hs = block_topk_heads(case)
+    rb, rs, _, _ = block_topk(case)
+    assert np.array_equal(hb[:, 3], rb) and np.array_equal(hs[:, 3], rs)
