@@ -431,16 +431,19 @@ def bench_unfused(torch, ops, timer, case, warmup, steps, flush):
     return res
 
 
-def bench_block(torch, ops, timer, case, warmup, steps, flush):
+def bench_block(torch, ops, timer, case, warmup, steps, flush, per_head=False):
+    """Block selection (per_head: one selection per (row, head), outputs
+    H times larger)."""
     args = [dev(torch, x) for x in (case.q, case.q_scale, case.w, case.kcache, case.k_scale,
                                     case.block_table, case.seq_lens)]
     ws = ops.Workspace()
+    op = ops.block_topk_heads if per_head else ops.block_topk
 
     def step():
-        ops.block_topk(*args, case.page_size, case.max_seq_len, case.block_size, case.top_blocks, workspace=ws)
+        op(*args, case.page_size, case.max_seq_len, case.block_size, case.top_blocks, workspace=ws)
 
     wall, us, region = timer.run(step, warmup, steps, flush)
-    out_entries = case.batch * case.top_blocks * (1 + case.block_size)
+    out_entries = case.batch * (case.heads if per_head else 1) * case.top_blocks * (1 + case.block_size)
     res = summary(us, indexer_algorithmic_bytes(case, out_entries), case.batch, region, timer.settled)
     res["tokens"] = int(case.seq_lens.astype(np.int64).sum())
     del args
@@ -572,6 +575,9 @@ def main(argv=None):
         c4 = workloads.c4_block_sparse()
         also["block_sparse_B64_n32768_top32"] = bench_block(torch, ops, timer, c4, a.warmup, max(a.steps, 50),
                                                             True)
+        log("timing block-sparse B64, per-head selection ...")
+        also["block_sparse_per_head_B64_H64_top32"] = bench_block(torch, ops, timer, c4, a.warmup,
+                                                                  max(a.steps, 50), True, per_head=True)
         del c4
     if "bf16" in only:
         log("timing fused decode B32 from a bf16 cache ...")

@@ -77,6 +77,7 @@ extern "C" {
 #define IDXTOPK_OP_SCORE_TOPK_FUSED 4
 #define IDXTOPK_OP_BLOCK_TOPK 5
 #define IDXTOPK_OP_CACHE_WRITE 6
+#define IDXTOPK_OP_BLOCK_TOPK_HEADS 7 /* workspace query with rows = batch * heads */
 
 /* Key element types for idx_cache_write. */
 #define IDXTOPK_KEY_F32 0  /* float */
@@ -240,6 +241,35 @@ int block_topk(const uint8_t* q, const float* q_scale, const float* w,
                int32_t top_blocks,
                int32_t* out_blocks, int32_t* out_slots,
                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * block_topk_heads -- per-head variant of block_topk: every index head keeps
+ * its own blocks.
+ *
+ * Head h's term of the index score, T_h[b, j] = w[b, h] * max(0, q_scale[b]
+ * * k_scale[slot_j] * sum_d q[b, h, d] * kcache[slot_j, d]) (the score is
+ * the sum of these over h), gives head h's block scores (the max over the
+ * block's visible tokens), and the top_blocks best blocks of every (row,
+ * head) are kept, ties to the lower block id ([ATOM-1473] Pull request
+ * overview: the partial top-k kernel's grid runs over query rows, index
+ * heads and chunks; per-head selection is this library's reading of that
+ * head axis).
+ *
+ * out_blocks  int32 [batch, heads, top_blocks] physical block ids, -1 pads;
+ * out_slots   optional int32 [batch, heads, top_blocks * block_size], laid
+ *             out as block_topk's per (row, head);
+ * workspace   at least idxtopk_workspace_bytes(IDXTOPK_OP_BLOCK_TOPK_HEADS,
+ *             batch * heads, block_size, max_seq_len) bytes, zero-filled
+ *             before first use and left zero-filled (as for block_topk).
+ * Other arguments, limits and status codes: block_topk's (fp8 cache).
+ */
+int block_topk_heads(const uint8_t* q, const float* q_scale, const float* w,
+                     const uint8_t* kcache, const float* k_scale,
+                     const int32_t* block_table, int64_t bt_stride, int32_t page_size,
+                     const int32_t* row_to_batch, const int32_t* seq_lens, int32_t batch,
+                     int32_t heads, int32_t dim, int32_t max_seq_len, int32_t block_size,
+                     int32_t top_blocks, int32_t* out_blocks, int32_t* out_slots,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * idx_cache_write -- quantize new index keys into the paged fp8 cache.

@@ -24,6 +24,7 @@ OP_PAGE_TRANSFORM = 3
 OP_SCORE_TOPK_FUSED = 4
 OP_BLOCK_TOPK = 5
 OP_CACHE_WRITE = 6
+OP_BLOCK_TOPK_HEADS = 7
 KEY_F32 = 0
 KEY_BF16 = 1
 SORTED = 1
@@ -43,6 +44,8 @@ SIGNATURES = {
                                     _i32, _i32, _i32, _vp, _vp, _vp, _sz, _i32, _vp]),
     "block_topk": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                           _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "block_topk_heads": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
+                                _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "idx_cache_write": (_i32, [_vp, _i32, _i64, _i32, _i32, _vp, _vp, _vp, _vp]),
     "idx_score_bf16": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i64, _vp]),
     "idx_score_topk_fused_bf16": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32,

@@ -159,6 +159,29 @@ int idx_cache_write(const void* keys, int32_t key_dtype, int64_t key_stride, int
                                      kcache, k_scale, static_cast<hipStream_t>(stream));
 }
 
+int block_topk_heads(const uint8_t* q, const float* q_scale, const float* w, const uint8_t* kcache,
+                     const float* k_scale, const int32_t* block_table, int64_t bt_stride, int32_t page_size,
+                     const int32_t* row_to_batch, const int32_t* seq_lens, int32_t batch, int32_t heads,
+                     int32_t dim, int32_t max_seq_len, int32_t block_size, int32_t top_blocks,
+                     int32_t* out_blocks, int32_t* out_slots, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  const int st = check_indexer(q, q_scale, w, kcache, k_scale, block_table, bt_stride, page_size,
+                               seq_lens, batch, heads, dim, max_seq_len);
+  if (st != IDXTOPK_OK) return st;
+  if (block_size <= 0 || top_blocks <= 0 || (batch > 0 && !out_blocks)) return IDXTOPK_EINVAL;
+  if (block_size != page_size || top_blocks > IDXTOPK_MAX_TOP_BLOCKS || block_size % 16 != 0 ||
+      block_size > 8192)
+    return IDXTOPK_EUNSUPPORTED;
+  if (batch == 0) return IDXTOPK_OK;
+  if (!workspace ||
+      workspace_bytes < idxtopk::block_workspace_bytes(batch * heads, block_size, max_seq_len))
+    return IDXTOPK_EWORKSPACE;
+  return idxtopk::launch_block_topk_heads(pack(q, q_scale, w, kcache, k_scale, block_table, bt_stride,
+                                               page_size, row_to_batch, seq_lens, batch, heads, max_seq_len),
+                                          block_size, top_blocks, out_blocks, out_slots, workspace,
+                                          static_cast<hipStream_t>(stream));
+}
+
 int idx_score_bf16(const uint16_t* q, const float* w, const uint16_t* kcache, const int32_t* block_table,
                    int64_t bt_stride, int32_t page_size, const int32_t* row_to_batch, const int32_t* seq_lens,
                    int32_t batch, int32_t heads, int32_t dim, int32_t max_seq_len, float* scores,
@@ -238,6 +261,7 @@ size_t idxtopk_workspace_bytes(int32_t op, int32_t rows, int32_t k, int32_t max_
     case IDXTOPK_OP_SCORE_TOPK_FUSED:
       return rows > 0 ? idxtopk::fused_workspace_bytes(rows, k, max_seq_len) : 0;
     case IDXTOPK_OP_BLOCK_TOPK:
+    case IDXTOPK_OP_BLOCK_TOPK_HEADS:  // rows = batch * heads
       if (k <= 0) return 0;
       return rows > 0 ? idxtopk::block_workspace_bytes(rows, k, max_seq_len) : 0;
     default:

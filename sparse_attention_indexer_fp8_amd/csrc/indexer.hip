@@ -1060,6 +1060,7 @@ struct BlockOut {
   int32_t* slots;
   int top;
   int bs;
+  int hp;  // selections per query row: 1, or the head count (per-head variant)
 };
 
 template <int NT, bool BF = false>
@@ -1091,15 +1092,18 @@ __global__ __launch_bounds__(IX_WG) void block_chunk_kernel(IndexerArgs a, Block
   for (int i = tid; i < nbc; i += IX_WG) bsc[blk0 + i] = s.bmax[i];
 }
 
+// One workgroup per selection: query row b, or (row b, head) in the per-head
+// variant, whose block maxima and outputs are laid out [rows * hp].
 __global__ __launch_bounds__(MG_WG) void block_merge_kernel(IndexerArgs a, BlockWs ws, BlockOut o) {
   __shared__ BlockMergeLds s;
   const int tid = threadIdx.x;
-  const int b = blockIdx.x;
+  const int sel_row = blockIdx.x;
+  const int b = sel_row / o.hp;
   const int n = a.seq_lens[b];
   const int bs = o.bs;
   const int top = o.top;
   const int nblk = (n + bs - 1) / bs;
-  uint32_t* bsc = ws.bscore + static_cast<int64_t>(b) * ws.nblk_max;
+  uint32_t* bsc = ws.bscore + static_cast<int64_t>(sel_row) * ws.nblk_max;
 
   wg_select_init<MG_WG>(s.sel);
   if (tid == 0) s.ocnt = 0;
@@ -1134,9 +1138,9 @@ __global__ __launch_bounds__(MG_WG) void block_merge_kernel(IndexerArgs a, Block
   const int nsel = min(static_cast<int>(s.ocnt), top);
   const int32_t* bt_row = bt_row_of(a, b);
   for (int i = tid; i < top; i += MG_WG)
-    o.blocks[static_cast<int64_t>(b) * top + i] = i < nsel ? bt_row[s.sel_blocks[i]] : -1;
+    o.blocks[static_cast<int64_t>(sel_row) * top + i] = i < nsel ? bt_row[s.sel_blocks[i]] : -1;
   if (o.slots) {
-    const int64_t slot_row = static_cast<int64_t>(b) * top * bs;
+    const int64_t slot_row = static_cast<int64_t>(sel_row) * top * bs;
     for (int e = tid; e < top * bs; e += MG_WG) {
       const int i = e / bs;
       const int t = e - i * bs;
@@ -1151,6 +1155,57 @@ __global__ __launch_bounds__(MG_WG) void block_merge_kernel(IndexerArgs a, Block
   // leave every workspace byte of this row zero again
   __syncthreads();
   for (int cb = tid; cb < nblk; cb += MG_WG) bsc[cb] = 0;
+}
+
+// Per-head block maxima (fp8 cache): each head's term of the score, maxed
+// over the block's visible tokens, for every (head, block) of the chunk:
+// the 16 tokens of a group are reduced in registers per head (DPP over each
+// 16-lane row, which holds four heads of the tile), and lane 0 of the row
+// raises the (head, block) entry in LDS.
+constexpr int BKH_MAX_BLOCKS = 64;  // blocks per chunk
+
+struct BlockHeadsLds {
+  int32_t pages[IX_PAGES];
+  uint32_t hmax[128 * BKH_MAX_BLOCKS];
+};
+
+template <int NT>
+__global__ __launch_bounds__(IX_WG) void block_heads_chunk_kernel(IndexerArgs a, BlockWs ws, int bs) {
+  __shared__ BlockHeadsLds s;
+  constexpr int H = 16 * NT;
+  const int tid = threadIdx.x;
+  int b, c;
+  chunk_of(a, b, c);
+  const int n = a.seq_lens[b];
+  int tb, clen;
+  chunk_span(a, c, tb, clen);
+  if (tb >= n) return;
+  const int te = min(n, tb + clen);
+  const int nbc = (te - tb + bs - 1) / bs;
+  for (int i = tid; i < H * BKH_MAX_BLOCKS; i += IX_WG) s.hmax[i] = 0;
+  // (score_chunk_heads synchronises before its first emit)
+  const int l = lane_id();
+  const int lc = l & 15, lg = l >> 4;
+  score_chunk_heads<NT, IX_WG, IX_RING>(a, b, tb, te, s.pages, [&](int j0, const float (&v)[NT][4]) {
+    const bool valid = j0 + lc < te;
+    // a group lies inside one block (block size and chunk start are
+    // multiples of 16)
+    const uint32_t blk = fdiv(static_cast<uint32_t>(j0 - tb), a.pdiv);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t key = row16_max(valid ? float_key(v[t][r]) : 0u);
+        if (lc == 0 && key) atomicMax(&s.hmax[(16 * t + 4 * lg + r) * BKH_MAX_BLOCKS + blk], key);
+      }
+    }
+  });
+  __syncthreads();
+  const int blk0 = tb / bs;
+  for (int i = tid; i < H * nbc; i += IX_WG) {
+    const int h = i / nbc, cb = i - h * nbc;
+    ws.bscore[(static_cast<int64_t>(b) * H + h) * ws.nblk_max + blk0 + cb] = s.hmax[h * BKH_MAX_BLOCKS + cb];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1402,10 +1457,41 @@ int launch_block_topk(const IndexerInputs& in, int block_size, int top_blocks, i
   o.slots = out_slots;
   o.top = top_blocks;
   o.bs = block_size;
+  o.hp = 1;
   const dim3 grid(chunk_grid(a));
   (void)hipGetLastError();
   IDXTOPK_DISPATCH_NT(block_chunk_kernel, in.bf16, in.heads, grid, stream, a, w, block_size);
   hipLaunchKernelGGL(block_merge_kernel, dim3(in.batch), dim3(MG_WG), 0, stream, a, w, o);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// Per-head block selection: chunks of at most BKH_MAX_BLOCKS blocks, one
+// selection per (row, head) in the merge.
+int launch_block_topk_heads(const IndexerInputs& in, int block_size, int top_blocks, int32_t* out_blocks,
+                            int32_t* out_slots, void* ws, hipStream_t stream) {
+  if (in.batch == 0) return 0;
+  int chunk = choose_chunk(in.batch, in.max_seq_len, in.page_size, block_size, 512, 8192);
+  if (chunk / block_size > BKH_MAX_BLOCKS) chunk = BKH_MAX_BLOCKS * block_size;
+  if (chunk < block_size) chunk = block_size;
+  const IndexerArgs a = make_args(in, chunk, true, block_size);
+  const BlockWs w = block_ws(ws, in.batch * in.heads, block_size, in.max_seq_len);
+  BlockOut o;
+  o.blocks = out_blocks;
+  o.slots = out_slots;
+  o.top = top_blocks;
+  o.bs = block_size;
+  o.hp = in.heads;
+  const dim3 grid(chunk_grid(a));
+  (void)hipGetLastError();
+  switch (in.heads) {
+    case 16: hipLaunchKernelGGL(block_heads_chunk_kernel<1>, grid, dim3(IX_WG), 0, stream, a, w, block_size); break;
+    case 32: hipLaunchKernelGGL(block_heads_chunk_kernel<2>, grid, dim3(IX_WG), 0, stream, a, w, block_size); break;
+    case 64: hipLaunchKernelGGL(block_heads_chunk_kernel<4>, grid, dim3(IX_WG), 0, stream, a, w, block_size); break;
+    case 128: hipLaunchKernelGGL(block_heads_chunk_kernel<8>, grid, dim3(IX_WG), 0, stream, a, w, block_size); break;
+    default: return -2;
+  }
+  hipLaunchKernelGGL(block_merge_kernel, dim3(static_cast<unsigned>(in.batch) * in.heads), dim3(MG_WG), 0, stream,
+                     a, w, o);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -72,5 +72,7 @@ int launch_cache_write_bf16(const void* keys, bool bf16_in, int64_t stride, int 
                             uint16_t* kcache, hipStream_t stream);
 int launch_block_topk(const IndexerInputs& in, int block_size, int top_blocks, int32_t* out_blocks,
                       int32_t* out_slots, void* ws, hipStream_t stream);
+int launch_block_topk_heads(const IndexerInputs& in, int block_size, int top_blocks, int32_t* out_blocks,
+                            int32_t* out_slots, void* ws, hipStream_t stream);
 
 }  // namespace idxtopk

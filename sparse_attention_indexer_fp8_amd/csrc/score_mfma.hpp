@@ -549,6 +549,115 @@ __device__ void score_chunk_bf16(const IndexerArgs& a, int b, int tok_begin, int
     score_chunk_bf16_impl<NT, WG, R, false>(a, b, tok_begin, tok_end, lds_pages, emit);
 }
 
+// ---------------------------------------------------------------------------
+// Per-head terms (fp8 cache): the block variant that selects per index head
+// needs every head's term of the score, not their sum.
+// ---------------------------------------------------------------------------
+
+// Lane (c, g) gets, for tile t and r = 0..3, the term of head 16t + 4g + r
+// for token c of the group: w * s_q (folded into wt) * relu(logit) * s_k.
+template <int NT>
+__device__ __forceinline__ void heads16(const QOperand<NT>& qo, const v8i kb, float ks, float (&v)[NT][4]) {
+  v4f acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.a[t], kb, zero, 0, 0, 0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[t][r] = qo.wt[t][r] * relu_bits(acc[t][r]) * ks;
+  }
+}
+
+// The chunk loop of score_chunk_impl (staged pages, waves on contiguous
+// group ranges, a ring of RING groups refilled right after use) with the
+// per-head terms: emit_heads(j0, v) is called by every lane for each group,
+// j0 the group's first token; lane (c, g) holds token j0 + c's terms of
+// heads 16t + 4g + r. Tokens at or past tok_end carry terms of unrelated
+// keys and must be ignored.
+template <int NT, int WG, int RING, bool WHOLE, class Emit>
+__device__ __forceinline__ void score_chunk_heads_impl(const IndexerArgs& a, int b, int tok_begin, int tok_end,
+                                                       int32_t* lds_pages, Emit&& emit_heads) {
+  constexpr int NW = WG / kWave;
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid / kWave);
+  const int l = lane_id();
+  const int c = l & 15;
+  const uint32_t P = static_cast<uint32_t>(a.page_size);
+
+  const uint32_t p0 = fdiv(static_cast<uint32_t>(tok_begin), a.pdiv);
+  const uint32_t p1 = fdiv(static_cast<uint32_t>(tok_end - 1), a.pdiv);
+  const int32_t* bt_row = bt_row_of(a, b);
+  for (int i = tid; i <= static_cast<int>(p1 - p0); i += WG) lds_pages[i] = bt_row[p0 + i];
+
+  QOperand<NT> qo;
+  load_query<NT>(qo, a.q + static_cast<int64_t>(b) * a.heads * kDim,
+                 a.w + static_cast<int64_t>(b) * a.heads, a.q_scale[b]);
+  __syncthreads();
+
+  const int ngroups = (tok_end - tok_begin + kGroup - 1) / kGroup;
+  const int per = (ngroups + NW - 1) / NW;
+  const int g_lo = wave * per;
+  const int g_hi = min(ngroups, g_lo + per);
+  const int last = tok_end - 1;
+  auto slot_of = [&](int j) {
+    j = j < last ? j : last;
+    const uint32_t pg = fdiv(static_cast<uint32_t>(j), a.pdiv);
+    uint32_t m = (static_cast<uint32_t>(lds_pages[pg - p0]) - pg) * P;
+    asm volatile("" : "+v"(m));
+    return m + static_cast<uint32_t>(j);
+  };
+  auto key_piece = [&](uint32_t slot, int lp) {
+    return load_v4i_stream(a.kcache + (static_cast<uint64_t>(slot) << 7) + lp);
+  };
+  const int lt = l >> 3, lp = 16 * (l & 7);
+  auto fetch = [&](int gi, KeyPieces& kp, float& ks) {
+    const int j0 = tok_begin + gi * kGroup;
+    if (WHOLE) {
+      const uint32_t pg = fdiv(static_cast<uint32_t>(j0), a.pdiv);
+      uint32_t m = (static_cast<uint32_t>(uniform(lds_pages[pg - p0])) - pg) * P;
+      asm volatile("" : "+s"(m));
+      const uint32_t s0 = m + static_cast<uint32_t>(j0);
+      kp.x0 = key_piece(s0 + lt, lp);
+      kp.x1 = key_piece(s0 + 8 + lt, lp);
+      ks = a.k_scale[s0 + c];
+    } else {
+      kp.x0 = key_piece(slot_of(j0 + lt), lp);
+      kp.x1 = key_piece(slot_of(j0 + 8 + lt), lp);
+      ks = a.k_scale[slot_of(j0 + c)];
+    }
+  };
+  if (g_lo >= g_hi) return;
+  const int gmax = g_hi - 1;
+  KeyPieces ring[RING];
+  float ksr[RING];
+#pragma unroll
+  for (int u = 0; u < RING; ++u) fetch(min(g_lo + u, gmax), ring[u], ksr[u]);
+  for (int gi0 = g_lo; gi0 < g_hi; gi0 += RING) {
+#pragma unroll
+    for (int u = 0; u < RING; ++u) {
+      const int gi = gi0 + u;
+      if (gi < g_hi) {
+        float v[NT][4];
+        heads16<NT>(qo, keys_to_operand(ring[u].x0, ring[u].x1), ksr[u], v);
+        if (gi + RING < g_hi) fetch(gi + RING, ring[u], ksr[u]);
+        emit_heads(tok_begin + gi * kGroup, v);
+      }
+    }
+  }
+}
+
+template <int NT, int WG, int RING, class Emit>
+__device__ void score_chunk_heads(const IndexerArgs& a, int b, int tok_begin, int tok_end, int32_t* lds_pages,
+                                  Emit&& emit_heads) {
+  if (a.page_size % kGroup == 0 && tok_begin % kGroup == 0)
+    score_chunk_heads_impl<NT, WG, RING, true>(a, b, tok_begin, tok_end, lds_pages, emit_heads);
+  else
+    score_chunk_heads_impl<NT, WG, RING, false>(a, b, tok_begin, tok_end, lds_pages, emit_heads);
+}
+
 // Either cache format.
 template <bool BF, int NT, int WG, int RING, class Emit>
 __device__ __forceinline__ void score_chunk_any(const IndexerArgs& a, int b, int tok_begin, int tok_end,

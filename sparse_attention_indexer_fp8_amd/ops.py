@@ -208,6 +208,25 @@ def block_topk(q, q_scale, w, kcache, k_scale, block_table, seq_lens, page_size:
     return (out_blocks, out_slots) if return_slots else out_blocks
 
 
+def block_topk_heads(q, q_scale, w, kcache, k_scale, block_table, seq_lens, page_size: int,
+                     max_seq_len: int, block_size: int, top_blocks: int, return_slots: bool = True,
+                     workspace: Optional[Workspace] = None, row_to_batch: Optional[torch.Tensor] = None):
+    """Per-head block selection: [B, H, top] physical block ids (and
+    [B, H, top * block_size] slot lists), each head ranking blocks by its own
+    term of the index score."""
+    args, B, H, D = _indexer_args(q, q_scale, w, kcache, k_scale, block_table, seq_lens, row_to_batch)
+    out_blocks = torch.empty((B, H, top_blocks), dtype=torch.int32, device=q.device)
+    out_slots = (torch.empty((B, H, top_blocks * block_size), dtype=torch.int32, device=q.device)
+                 if return_slots else None)
+    nbytes = workspace_bytes(_lib.OP_BLOCK_TOPK_HEADS, B * H, block_size, max_seq_len)
+    ws = _workspace(workspace).get(nbytes)
+    st = _lib.load().block_topk_heads(*args, int(page_size), _ptr(row_to_batch), _ptr(seq_lens), B, H, D,
+                                      int(max_seq_len), int(block_size), int(top_blocks), _ptr(out_blocks),
+                                      _ptr(out_slots), _ptr(ws), ws.numel(), _stream())
+    _lib.check("block_topk_heads", st)
+    return (out_blocks, out_slots) if return_slots else out_blocks
+
+
 def idx_cache_write(keys: torch.Tensor, slot_mapping: torch.Tensor, kcache: torch.Tensor,
                     k_scale: torch.Tensor) -> None:
     """Quantize new index keys (fp32 or bf16, [tokens, 128] with contiguous

@@ -237,3 +237,15 @@ def test_cache_write_bf16_validation(lib):
     assert f(keys=MISALIGNED) == -1
     assert f(kc=MISALIGNED) == -1
     assert f(T=0) == 0
+
+
+def test_block_heads_validation(lib):
+    need = lib.idxtopk_workspace_bytes(7, 32 * 64, 128, 32768)
+    assert need == lib.idxtopk_workspace_bytes(5, 32 * 64, 128, 32768)
+    f = lambda bs=128, top=32, nb=need, **kw: lib.block_topk_heads(
+        *_indexer(**{"P": 128, "msl": 32768, "bts": 256, **kw}), bs, top, FAKE, NULL, FAKE, nb, NULL)
+    assert f(bs=64) == -2
+    assert f(top=0) == -1
+    assert f(nb=need - 1) == -3        # sized for batch * heads selections
+    assert f(H=48) == -2
+    assert f(B=0) == 0

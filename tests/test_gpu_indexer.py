@@ -520,3 +520,53 @@ def test_fused_sorted_random_order(ops):
             assert np.all(v1[b][:-1] >= v1[b][1:]), b  # (-inf padding compares equal)
             # the score that goes with each slot is unchanged by the sort
             assert dict(zip(s0[b].tolist(), v0[b].tolist())) == dict(zip(s1[b].tolist(), v1[b].tolist())), b
+
+
+# Per-head block selection: every (row, head) keeps its own blocks by the
+# head's term of the score.
+@pytest.mark.parametrize("bs,top,heads", [(128, 32, 64), (64, 7, 16), (16, 5, 128)])
+def test_block_heads_exact(ops, bs, top, heads):
+    import torch
+
+    case = _exact_case(1000 + bs + heads, batch=4, n_lo=1, n_hi=9000, page_size=bs, heads=heads, k=0,
+                       block_size=bs, top_blocks=top, first=(0, bs * top - 5, bs * top + 1))
+    blocks, slots = ops.block_topk_heads(*_inputs(case), case.page_size, case.max_seq_len, bs, top)
+    torch.cuda.synchronize()
+    blocks, slots = blocks.cpu().numpy(), slots.cpu().numpy()
+    rb, rs = oracle.block_topk_heads(case)
+    for b in range(case.batch):
+        for h in range(heads):
+            assert np.array_equal(np.sort(blocks[b, h]), np.sort(rb[b, h])), (b, h)
+            got = {int(blocks[b, h, i]): slots[b, h, i * bs:(i + 1) * bs].tolist() for i in range(top)
+                   if blocks[b, h, i] >= 0}
+            exp = {int(rb[b, h, i]): rs[b, h, i * bs:(i + 1) * bs].tolist() for i in range(top) if rb[b, h, i] >= 0}
+            assert got == exp, (b, h)
+
+
+def test_block_heads_random_tolerance(ops):
+    """Random fp8 inputs: each (row, head)'s chosen blocks are within the
+    score tolerance of that head's top-th block score."""
+    import torch
+    from oracle.indexer import case_bt_row, index_head_scores
+
+    bs, top = 128, 16
+    case = workloads.indexer_case(1010, batch=3, n_lo=bs, n_hi=20000, page_size=bs, k=0, block_size=bs,
+                                  top_blocks=top, heads=32)
+    blocks = ops.block_topk_heads(*_inputs(case), case.page_size, case.max_seq_len, bs, top, return_slots=False)
+    torch.cuda.synchronize()
+    blocks = blocks.cpu().numpy()
+    for b in range(case.batch):
+        n = int(case.seq_lens[b])
+        bt = case_bt_row(case, b)
+        T = index_head_scores(case.q[b], case.q_scale[b], case.w[b], case.kcache, case.k_scale, bt,
+                              case.page_size, n)
+        nb = -(-n // bs)
+        page_to_blk = {int(bt[c]): c for c in range(nb)}
+        for h in range(case.heads):
+            bsv = oracle.block_scores(T[:, h], bs)
+            m = min(nb, top)
+            sel = [page_to_blk[int(p)] for p in blocks[b, h, :m]]
+            assert len(set(sel)) == m and (blocks[b, h, m:] == -1).all()
+            sigma = max(float(np.sqrt(np.mean(T[:, h] ** 2))), 1e-30)
+            kth = np.sort(bsv)[::-1][m - 1]
+            assert (bsv[sel] >= kth - 1e-3 * max(abs(kth), sigma)).all(), (b, h)
