@@ -570,3 +570,66 @@ def test_block_heads_random_tolerance(ops):
             sigma = max(float(np.sqrt(np.mean(T[:, h] ** 2))), 1e-30)
             kth = np.sort(bsv)[::-1][m - 1]
             assert (bsv[sel] >= kth - 1e-3 * max(abs(kth), sigma)).all(), (b, h)
+
+
+# ---------------------------------------------------------------------------
+# Full-size checks of the remaining benchmarked configurations, in the launch
+# configuration bench.py times.
+# ---------------------------------------------------------------------------
+
+def test_mtp_decode_full_size(ops):
+    """Multi-token decode 16 x 4 (n 16K-64K, k 2048): every row meets the
+    tolerance criterion."""
+    case = workloads.mtp_decode()
+    log(f"case {case.name}")
+    slots, sc = _fused(ops, case)
+    for b in range(case.batch):
+        n = int(case.seq_lens[b])
+        ts = oracle.token_slots(case.block_table[case.row_to_batch[b]], case.page_size, n)
+        check_fused_row(slots[b], sc[b], case_scores(case, b), ts, case.k)
+
+
+def test_fused_decode_full_size_sorted(ops):
+    """Fused decode B32 with sorted output: the same selection as the
+    unsorted call, each row in descending score order with its scores."""
+    import torch
+
+    case = workloads.c2_fused_decode()
+    s0, v0 = _fused(ops, case)
+    s1, v1 = ops.idx_score_topk_fused(*_inputs(case), case.page_size, case.max_seq_len, case.k, return_scores=True,
+                                      sorted=True)
+    torch.cuda.synchronize()
+    s1, v1 = s1.cpu().numpy(), v1.cpu().numpy()
+    for b in range(case.batch):
+        assert np.array_equal(np.sort(s1[b]), np.sort(s0[b])), b
+        assert np.all(v1[b][:-1] >= v1[b][1:]), b
+        assert dict(zip(s0[b].tolist(), v0[b].tolist())) == dict(zip(s1[b].tolist(), v1[b].tolist())), b
+
+
+def test_block_heads_full_size_sampled(ops):
+    """Per-head selection on the block-sparse geometry (B64, n 32768, top 32,
+    64 heads): sampled rows, every head, tolerance criterion."""
+    import torch
+    from oracle.indexer import case_bt_row, index_head_scores
+
+    case = workloads.c4_block_sparse()
+    bs, top = case.block_size, case.top_blocks
+    blocks, slots = ops.block_topk_heads(*_inputs(case), case.page_size, case.max_seq_len, bs, top)
+    torch.cuda.synchronize()
+    blocks, slots = blocks.cpu().numpy(), slots.cpu().numpy()
+    for b in (0, 33, 63):
+        n = int(case.seq_lens[b])
+        bt = case_bt_row(case, b)
+        T = index_head_scores(case.q[b], case.q_scale[b], case.w[b], case.kcache, case.k_scale, bt,
+                              case.page_size, n)
+        nb = -(-n // bs)
+        page_to_blk = {int(bt[c]): c for c in range(nb)}
+        for h in range(case.heads):
+            bsv = oracle.block_scores(T[:, h], bs)
+            sel = [page_to_blk[int(p)] for p in blocks[b, h]]
+            assert len(set(sel)) == top, (b, h)
+            sigma = max(float(np.sqrt(np.mean(T[:, h] ** 2))), 1e-30)
+            kth = np.sort(bsv)[::-1][top - 1]
+            assert (bsv[sel] >= kth - 1e-3 * max(abs(kth), sigma)).all(), (b, h)
+            for i, c in enumerate(sel):
+                assert np.array_equal(slots[b, h, i * bs:(i + 1) * bs], int(bt[c]) * bs + np.arange(bs)), (b, h)

@@ -239,6 +239,24 @@ def test_packed_prefill_full_size(ops):
     ref = oracle.topk_rows(case.scores, case.seq_lens, case.k, case.row_starts, case.row_to_batch,
                            case.page_table, 1, rows=sample)
     assert np.array_equal(sorted_rows(got[sample]), sorted_rows(ref))
+    # the same launch with sorted output: the same sets, every row in order
+    # (scores non-increasing, equal scores by ascending position), and the
+    # sampled rows exactly the oracle's sequence
+    log("sorted output")
+    sc = dev(case.scores)
+    out = ops.topk_rows(sc, dev(case.seq_lens), case.k, dev(case.row_starts), dev(case.row_to_batch),
+                        dev(case.page_table), 1, sorted=True)
+    torch.cuda.synchronize()
+    srt = out.cpu().numpy().astype(np.int64)
+    del sc
+    assert np.array_equal(sorted_rows(srt), sorted_rows(got))
+    for i in range(case.rows):
+        rs, p = int(case.row_starts[i]), int(case.row_to_batch[i])
+        row = srt[i][srt[i] >= 0]
+        pos = inv[p][row]
+        v = case.scores[i, rs + pos].astype(np.float64)
+        assert np.all((v[:-1] > v[1:]) | ((v[:-1] == v[1:]) & (pos[:-1] < pos[1:]))), i
+    assert np.array_equal(srt[sample], ref)
 
 
 # Sorted output: the oracle selects by a stable descending sort, so its order
