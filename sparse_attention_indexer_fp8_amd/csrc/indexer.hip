@@ -409,7 +409,7 @@ __global__ __launch_bounds__(IX_WG) void fused_chunk_kernel(IndexerArgs a, Fused
     s.lcnt2 = 0;
   }
   // (score_chunk synchronises before its first emit)
-  score_chunk_any<BF, NT, IX_WG, IX_RING>(a, b, tb, te, s.pages, [&](int j, float v, bool valid) {
+  score_chunk_any<BF, NT, IX_WG, IX_RING, true>(a, b, tb, te, s.pages, [&](int j, float v, bool valid) {
     if (valid) {
       sc[j - tb] = v;
       atomicAdd(&s.hist[float_key(v) >> HIST_SHIFT], 1u);

@@ -448,7 +448,12 @@ __device__ __forceinline__ float score16_bf16(const QOperandBF<NT>& qo, const Ke
 // score_chunk_impl for a bf16 cache: the same chunk staging, wave split,
 // ring discipline and emit contract; a group's keys are four 16-byte loads
 // per lane (token c, dimensions 32s + 8g .. + 8) and need no rearranging.
-template <int NT, int WG, int RING, bool WHOLE, class Emit>
+// One load instruction covers half of each token's two 128-byte lines, so
+// each line is fetched by two instructions. CACHED: ordinary loads, which
+// keep the line for its second half (faster for long rows); otherwise
+// nontemporal loads, which leave the caches to the data that follows (the
+// score-buffer variant's score rows).
+template <int NT, int WG, int RING, bool WHOLE, bool CACHED, class Emit>
 __device__ __forceinline__ void score_chunk_bf16_impl(const IndexerArgs& a, int b, int tok_begin, int tok_end,
                                                       int32_t* lds_pages, Emit&& emit) {
   constexpr int NW = WG / kWave;
@@ -496,7 +501,8 @@ __device__ __forceinline__ void score_chunk_bf16_impl(const IndexerArgs& a, int 
     }
     const uint8_t* row = a.kcache + (static_cast<uint64_t>(slot) << 8) + lp;
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl) kp.x[sl] = load_v4i_stream(row + 64 * sl);
+    for (int sl = 0; sl < 4; ++sl)
+      kp.x[sl] = CACHED ? *reinterpret_cast<const v4i*>(row + 64 * sl) : load_v4i_stream(row + 64 * sl);
   };
 
   if (g_lo >= g_hi) return;
@@ -539,14 +545,14 @@ __device__ __forceinline__ void score_chunk_bf16_impl(const IndexerArgs& a, int 
 
 // Score a chunk from a bf16 cache. A bf16 group is twice an fp8 group's
 // bytes, so half the ring depth keeps the same bytes in flight.
-template <int NT, int WG, int RING, class Emit>
+template <int NT, int WG, int RING, bool CACHED, class Emit>
 __device__ void score_chunk_bf16(const IndexerArgs& a, int b, int tok_begin, int tok_end, int32_t* lds_pages,
                                  Emit&& emit) {
   constexpr int R = RING > 2 ? RING / 2 : RING;
   if (a.page_size % kGroup == 0 && tok_begin % kGroup == 0)
-    score_chunk_bf16_impl<NT, WG, R, true>(a, b, tok_begin, tok_end, lds_pages, emit);
+    score_chunk_bf16_impl<NT, WG, R, true, CACHED>(a, b, tok_begin, tok_end, lds_pages, emit);
   else
-    score_chunk_bf16_impl<NT, WG, R, false>(a, b, tok_begin, tok_end, lds_pages, emit);
+    score_chunk_bf16_impl<NT, WG, R, false, CACHED>(a, b, tok_begin, tok_end, lds_pages, emit);
 }
 
 // ---------------------------------------------------------------------------
@@ -658,12 +664,13 @@ __device__ void score_chunk_heads(const IndexerArgs& a, int b, int tok_begin, in
     score_chunk_heads_impl<NT, WG, RING, false>(a, b, tok_begin, tok_end, lds_pages, emit_heads);
 }
 
-// Either cache format.
-template <bool BF, int NT, int WG, int RING, class Emit>
+// Either cache format (CACHED: see score_chunk_bf16_impl; fp8 keys are
+// always read nontemporally).
+template <bool BF, int NT, int WG, int RING, bool CACHED = false, class Emit>
 __device__ __forceinline__ void score_chunk_any(const IndexerArgs& a, int b, int tok_begin, int tok_end,
                                                 int32_t* lds_pages, Emit&& emit) {
   if constexpr (BF)
-    score_chunk_bf16<NT, WG, RING>(a, b, tok_begin, tok_end, lds_pages, emit);
+    score_chunk_bf16<NT, WG, RING, CACHED>(a, b, tok_begin, tok_end, lds_pages, emit);
   else
     score_chunk<NT, WG, RING>(a, b, tok_begin, tok_end, lds_pages, emit);
 }
