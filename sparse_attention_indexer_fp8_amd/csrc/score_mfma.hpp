@@ -96,11 +96,11 @@ __device__ __forceinline__ v4i load_v4i_stream(const uint8_t* p) {
 // Keys are fetched in whole lines: for a group of 16 tokens, lane l loads the
 // 16-byte piece (l & 7) of token (l >> 3) (x0) and of token 8 + (l >> 3) (x1),
 // so each load instruction covers eight complete 128-byte keys. The B operand
-// wants lane (c, g) to hold pieces 2g and 2g + 1 of token c; two rounds of
-// ds_bpermute move them. In round 0 a lane with c < 8 pulls piece 2g from x0
+// wants lane (c, g) to hold pieces 2g and 2g + 1 of token c; two steps of
+// ds_bpermute move them. In step 0 a lane with c < 8 pulls piece 2g from x0
 // of lane 8c + 2g, and a lane with c >= 8 pulls piece 2g + 1 from x1 of lane
-// 8(c - 8) + 2g + 1; round 1 pulls the other piece from the other parity.
-// Even lanes offer x0 in round 0 and x1 in round 1, odd lanes the reverse, so
+// 8(c - 8) + 2g + 1; step 1 pulls the other piece from the other parity.
+// Even lanes offer x0 in step 0 and x1 in step 1, odd lanes the reverse, so
 // every piece is sent once. Lanes with c >= 8 receive their pieces in swapped
 // order and put them back.
 __device__ __forceinline__ v8i keys_to_operand(const v4i x0, const v4i x1) {
