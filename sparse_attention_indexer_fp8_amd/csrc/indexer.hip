@@ -1208,6 +1208,79 @@ __global__ __launch_bounds__(IX_WG) void block_heads_chunk_kernel(IndexerArgs a,
   }
 }
 
+// Per-head merge with one wave per (row, head) selection, for rows of at most
+// BH_MAX_BLOCKS blocks and at most BH_MAX_TOP kept blocks: the selection's
+// block keys sit 16 per lane, wave_select finds the top-th, a ballot compacts
+// the kept block ids into this wave's LDS list, and the wave writes the
+// block ids, the slot lists and the zeros. No workgroup barrier: a wave whose
+// selection is past the end leaves at once.
+constexpr int BH_WAVES = 4;
+constexpr int BH_PER = 16;
+constexpr int BH_MAX_BLOCKS = BH_PER * kWave;
+constexpr int BH_MAX_TOP = 256;
+
+struct BlockHeadsMergeLds {
+  uint32_t hist[BH_WAVES][256];
+  int32_t sel[BH_WAVES][BH_MAX_TOP];
+};
+
+__global__ __launch_bounds__(BH_WAVES * kWave) void block_heads_merge_kernel(IndexerArgs a, BlockWs ws,
+                                                                              BlockOut o) {
+  __shared__ BlockHeadsMergeLds s;
+  const int wave = static_cast<int>(threadIdx.x) / kWave;
+  const int lane = lane_id();
+  const int sel_row = static_cast<int>(blockIdx.x) * BH_WAVES + wave;
+  if (sel_row >= a.batch * o.hp) return;
+  const int b = sel_row / o.hp;
+  const int n = a.seq_lens[b];
+  const int bs = o.bs;
+  const int top = o.top;
+  const int nblk = (n + bs - 1) / bs;
+  uint32_t* bsc = ws.bscore + static_cast<int64_t>(sel_row) * ws.nblk_max;
+  uint64_t keys[BH_PER];
+  bool valid[BH_PER];
+#pragma unroll
+  for (int e = 0; e < BH_PER; ++e) {
+    const int cb = e * kWave + lane;
+    valid[e] = cb < nblk;
+    keys[e] = valid[e] ? rank_key(bsc[cb], static_cast<uint32_t>(cb)) : 0ull;
+  }
+  const uint64_t T = nblk > top ? wave_select<BH_PER>(keys, valid, static_cast<uint32_t>(top), s.hist[wave]) : 0ull;
+  const int nsel = min(nblk, top);
+  uint32_t at = 0;
+#pragma unroll
+  for (int e = 0; e < BH_PER; ++e) {
+    const bool keep = valid[e] && keys[e] >= T;
+    const uint64_t mk = ballot(keep);
+    if (keep) s.sel[wave][at + lanes_below(mk)] = e * kWave + lane;
+    at += static_cast<uint32_t>(__popcll(mk));
+  }
+  // the wave's LDS writes complete before its reads (in-order LDS queue);
+  // keep the compiler from moving the reads up
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  const int32_t* bt_row = bt_row_of(a, b);
+  for (int i = lane; i < top; i += kWave)
+    o.blocks[static_cast<int64_t>(sel_row) * top + i] = i < nsel ? bt_row[s.sel[wave][i]] : -1;
+  if (o.slots) {
+    const int64_t slot_row = static_cast<int64_t>(sel_row) * top * bs;
+    for (int e = lane; e < top * bs; e += kWave) {
+      const int i = static_cast<int>(fdiv(static_cast<uint32_t>(e), a.pdiv));
+      const int t = e - i * bs;
+      int32_t v = -1;
+      if (i < nsel) {
+        const int cb = s.sel[wave][i];
+        if (cb * bs + t < n) v = static_cast<int32_t>(static_cast<int64_t>(bt_row[cb]) * bs + t);
+      }
+      o.slots[slot_row + e] = v;
+    }
+  }
+  // leave this selection's workspace entries zero again
+#pragma unroll
+  for (int e = 0; e < BH_PER; ++e)
+    if (valid[e]) bsc[e * kWave + lane] = 0;
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
@@ -1490,8 +1563,12 @@ int launch_block_topk_heads(const IndexerInputs& in, int block_size, int top_blo
     case 128: hipLaunchKernelGGL(block_heads_chunk_kernel<8>, grid, dim3(IX_WG), 0, stream, a, w, block_size); break;
     default: return -2;
   }
-  hipLaunchKernelGGL(block_merge_kernel, dim3(static_cast<unsigned>(in.batch) * in.heads), dim3(MG_WG), 0, stream,
-                     a, w, o);
+  const int64_t sels = static_cast<int64_t>(in.batch) * in.heads;
+  if (w.nblk_max <= BH_MAX_BLOCKS && top_blocks <= BH_MAX_TOP)
+    hipLaunchKernelGGL(block_heads_merge_kernel, dim3(static_cast<unsigned>((sels + BH_WAVES - 1) / BH_WAVES)),
+                       dim3(BH_WAVES * kWave), 0, stream, a, w, o);
+  else
+    hipLaunchKernelGGL(block_merge_kernel, dim3(static_cast<unsigned>(sels)), dim3(MG_WG), 0, stream, a, w, o);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

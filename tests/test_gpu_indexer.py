@@ -524,11 +524,14 @@ def test_fused_sorted_random_order(ops):
 
 # Per-head block selection: every (row, head) keeps its own blocks by the
 # head's term of the score.
-@pytest.mark.parametrize("bs,top,heads", [(128, 32, 64), (64, 7, 16), (16, 5, 128)])
-def test_block_heads_exact(ops, bs, top, heads):
+# (the last two cases take the workgroup merge: more than 256 kept blocks,
+# more than 1024 blocks per row)
+@pytest.mark.parametrize("bs,top,heads,n_hi", [(128, 32, 64, 9000), (64, 7, 16, 9000), (16, 5, 128, 9000),
+                                               (16, 300, 16, 9000), (16, 40, 16, 20000)])
+def test_block_heads_exact(ops, bs, top, heads, n_hi):
     import torch
 
-    case = _exact_case(1000 + bs + heads, batch=4, n_lo=1, n_hi=9000, page_size=bs, heads=heads, k=0,
+    case = _exact_case(1000 + bs + heads + top, batch=4, n_lo=1, n_hi=n_hi, page_size=bs, heads=heads, k=0,
                        block_size=bs, top_blocks=top, first=(0, bs * top - 5, bs * top + 1))
     blocks, slots = ops.block_topk_heads(*_inputs(case), case.page_size, case.max_seq_len, bs, top)
     torch.cuda.synchronize()
