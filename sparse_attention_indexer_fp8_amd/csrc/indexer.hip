@@ -1208,7 +1208,8 @@ __global__ __launch_bounds__(IX_WG) void block_heads_chunk_kernel(IndexerArgs a,
   }
 }
 
-// Per-head merge with one wave per (row, head) selection, for rows of at most
+// Per-head merge with one wave per (row, head) selection (there are batch x
+// heads of them, enough waves to fill the chip), for rows of at most
 // BH_MAX_BLOCKS blocks and at most BH_MAX_TOP kept blocks: the selection's
 // block keys sit 16 per lane, wave_select finds the top-th, a ballot compacts
 // the kept block ids into this wave's LDS list, and the wave writes the
@@ -1534,6 +1535,8 @@ int launch_block_topk(const IndexerInputs& in, int block_size, int top_blocks, i
   const dim3 grid(chunk_grid(a));
   (void)hipGetLastError();
   IDXTOPK_DISPATCH_NT(block_chunk_kernel, in.bf16, in.heads, grid, stream, a, w, block_size);
+  // one workgroup per row: with one selection per row there are too few
+  // selections for the one-wave merge (block-sparse B64: 72 vs 81 us)
   hipLaunchKernelGGL(block_merge_kernel, dim3(in.batch), dim3(MG_WG), 0, stream, a, w, o);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

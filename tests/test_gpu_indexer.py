@@ -236,12 +236,15 @@ def test_fused_never_reads_outside_windows(ops):
         check_fused_row(slots[b], sc[b], rows[b], ts, case.k, batch_sigma=bsig)
 
 
-@pytest.mark.parametrize("bs,top", [(128, 32), (64, 5), (16, 40)])
-def test_block_exact(ops, bs, top):
+# (the wave merge for most; the last two cases take the workgroup merge: more
+# than 256 kept blocks, more than 1024 blocks per row)
+@pytest.mark.parametrize("bs,top,n_hi", [(128, 32, 9000), (64, 5, 9000), (16, 40, 9000), (16, 300, 9000),
+                                         (16, 40, 20000)])
+def test_block_exact(ops, bs, top, n_hi):
     import torch
 
-    case = _exact_case(800 + bs, batch=5, n_lo=1, n_hi=9000, page_size=bs, k=0, block_size=bs, top_blocks=top,
-                       first=(0, bs * top - 5, bs * top + 1))
+    case = _exact_case(800 + bs + top, batch=5, n_lo=1, n_hi=n_hi, page_size=bs, k=0, block_size=bs,
+                       top_blocks=top, first=(0, bs * top - 5, bs * top + 1))
     blocks, slots = ops.block_topk(*_inputs(case), case.page_size, case.max_seq_len, bs, top)
     torch.cuda.synchronize()
     blocks, slots = blocks.cpu().numpy(), slots.cpu().numpy()
