@@ -1221,7 +1221,7 @@ constexpr int BH_MAX_BLOCKS = BH_PER * kWave;
 constexpr int BH_MAX_TOP = 256;
 
 struct BlockHeadsMergeLds {
-  uint32_t hist[BH_WAVES][256];
+  alignas(16) uint32_t hist[BH_WAVES][256];  // wave_select clears it 16 bytes per lane
   int32_t sel[BH_WAVES][BH_MAX_TOP];
 };
 
