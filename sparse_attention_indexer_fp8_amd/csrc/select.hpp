@@ -18,7 +18,7 @@ constexpr int kSelMembers = 64;   // threshold-bin size a single wave resolves
 // (16 l .. 16 l + 15) then sit in 16 rows of 64 consecutive words, one per
 // lane, so the scan reads and clears without bank conflicts.
 struct SelectLds {
-  uint32_t hist[kSelBins];
+  alignas(16) uint32_t hist[kSelBins];  // wave_select clears it 16 bytes per lane
   uint64_t red[2][16];
   uint64_t members[kSelMembers];
   uint64_t result;
