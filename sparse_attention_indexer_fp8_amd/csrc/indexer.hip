@@ -1051,6 +1051,7 @@ struct BlockChunkLds {
 
 struct BlockMergeLds {
   int32_t sel_blocks[BK_MAX_TOP];
+  int32_t phys[BK_MAX_TOP];  // physical block id of each selected block
   SelectLds sel;
   uint32_t ocnt;
 };
@@ -1090,6 +1091,43 @@ __global__ __launch_bounds__(IX_WG) void block_chunk_kernel(IndexerArgs a, Block
   __syncthreads();
   const int blk0 = tb / bs;
   for (int i = tid; i < nbc; i += IX_WG) bsc[blk0 + i] = s.bmax[i];
+}
+
+// Slot list of one selection: entry e of its top * bs entries is token
+// t = e % bs of selected block i = e / bs, i.e. slot phys[i] * bs + t when
+// block i exists (i < nsel) and its token is visible (cbs[i] * bs + t < n),
+// else -1. Thread `me` of NTH writes four consecutive entries per 16-byte
+// nontemporal store (the lists are written once) when the output is 16-byte
+// aligned (bs is a multiple of 16, so every selection's list then is too).
+// Slot ids are int32 outputs: the arithmetic wraps as their int32
+// conversion would.
+template <int NTH>
+__device__ __forceinline__ void write_slot_list(int32_t* srow, int top, int bs, int nsel, int n,
+                                                const int32_t* cbs, const int32_t* phys, const FastDiv& bdiv,
+                                                int me, bool vec) {
+  const int total = top * bs;
+  auto slot = [&](int i, int t) -> int32_t {
+    if (i >= nsel || cbs[i] * bs + t >= n) return -1;
+    return static_cast<int32_t>(static_cast<uint32_t>(phys[i]) * static_cast<uint32_t>(bs) +
+                                static_cast<uint32_t>(t));
+  };
+  if (vec) {
+    for (int e = 4 * me; e < total; e += 4 * NTH) {
+      const int i = static_cast<int>(fdiv(static_cast<uint32_t>(e), bdiv));
+      const int t = e - i * bs;
+      v4i v;
+      v.x = slot(i, t);
+      v.y = slot(i, t + 1);
+      v.z = slot(i, t + 2);
+      v.w = slot(i, t + 3);
+      __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(srow + e));
+    }
+  } else {
+    for (int e = me; e < total; e += NTH) {
+      const int i = static_cast<int>(fdiv(static_cast<uint32_t>(e), bdiv));
+      srow[e] = slot(i, e - i * bs);
+    }
+  }
 }
 
 // One workgroup per selection: query row b, or (row b, head) in the per-head
@@ -1137,20 +1175,15 @@ __global__ __launch_bounds__(MG_WG) void block_merge_kernel(IndexerArgs a, Block
   __syncthreads();
   const int nsel = min(static_cast<int>(s.ocnt), top);
   const int32_t* bt_row = bt_row_of(a, b);
-  for (int i = tid; i < top; i += MG_WG)
-    o.blocks[static_cast<int64_t>(sel_row) * top + i] = i < nsel ? bt_row[s.sel_blocks[i]] : -1;
+  for (int i = tid; i < top; i += MG_WG) {
+    const int32_t pb = i < nsel ? bt_row[s.sel_blocks[i]] : -1;
+    o.blocks[static_cast<int64_t>(sel_row) * top + i] = pb;
+    s.phys[i] = pb;
+  }
   if (o.slots) {
-    const int64_t slot_row = static_cast<int64_t>(sel_row) * top * bs;
-    for (int e = tid; e < top * bs; e += MG_WG) {
-      const int i = e / bs;
-      const int t = e - i * bs;
-      int32_t v = -1;
-      if (i < nsel) {
-        const int cb = s.sel_blocks[i];
-        if (cb * bs + t < n) v = static_cast<int32_t>(static_cast<int64_t>(bt_row[cb]) * bs + t);
-      }
-      o.slots[slot_row + e] = v;
-    }
+    __syncthreads();
+    write_slot_list<MG_WG>(o.slots + static_cast<int64_t>(sel_row) * top * bs, top, bs, nsel, n, s.sel_blocks,
+                           s.phys, a.pdiv, tid, (reinterpret_cast<uintptr_t>(o.slots) & 15u) == 0);
   }
   // leave every workspace byte of this row zero again
   __syncthreads();
@@ -1223,6 +1256,7 @@ constexpr int BH_MAX_TOP = 256;
 struct BlockHeadsMergeLds {
   alignas(16) uint32_t hist[BH_WAVES][256];  // wave_select clears it 16 bytes per lane
   int32_t sel[BH_WAVES][BH_MAX_TOP];
+  int32_t phys[BH_WAVES][BH_MAX_TOP];
 };
 
 __global__ __launch_bounds__(BH_WAVES * kWave) void block_heads_merge_kernel(IndexerArgs a, BlockWs ws,
@@ -1261,20 +1295,16 @@ __global__ __launch_bounds__(BH_WAVES * kWave) void block_heads_merge_kernel(Ind
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   const int32_t* bt_row = bt_row_of(a, b);
-  for (int i = lane; i < top; i += kWave)
-    o.blocks[static_cast<int64_t>(sel_row) * top + i] = i < nsel ? bt_row[s.sel[wave][i]] : -1;
+  for (int i = lane; i < top; i += kWave) {
+    const int32_t pb = i < nsel ? bt_row[s.sel[wave][i]] : -1;
+    o.blocks[static_cast<int64_t>(sel_row) * top + i] = pb;
+    s.phys[wave][i] = pb;
+  }
   if (o.slots) {
-    const int64_t slot_row = static_cast<int64_t>(sel_row) * top * bs;
-    for (int e = lane; e < top * bs; e += kWave) {
-      const int i = static_cast<int>(fdiv(static_cast<uint32_t>(e), a.pdiv));
-      const int t = e - i * bs;
-      int32_t v = -1;
-      if (i < nsel) {
-        const int cb = s.sel[wave][i];
-        if (cb * bs + t < n) v = static_cast<int32_t>(static_cast<int64_t>(bt_row[cb]) * bs + t);
-      }
-      o.slots[slot_row + e] = v;
-    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    write_slot_list<kWave>(o.slots + static_cast<int64_t>(sel_row) * top * bs, top, bs, nsel, n, s.sel[wave],
+                           s.phys[wave], a.pdiv, lane, (reinterpret_cast<uintptr_t>(o.slots) & 15u) == 0);
   }
   // leave this selection's workspace entries zero again
 #pragma unroll

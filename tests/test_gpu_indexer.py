@@ -639,3 +639,53 @@ def test_block_heads_full_size_sampled(ops):
             assert (bsv[sel] >= kth - 1e-3 * max(abs(kth), sigma)).all(), (b, h)
             for i, c in enumerate(sel):
                 assert np.array_equal(slots[b, h, i * bs:(i + 1) * bs], int(bt[c]) * bs + np.arange(bs)), (b, h)
+
+
+@pytest.mark.parametrize("entry", ["block_topk", "block_topk_heads"])
+def test_block_slots_unaligned_output(ops, entry):
+    """Slot lists written through an output pointer that is not 16-byte
+    aligned (entries stored one by one) equal the aligned call's (four
+    entries per 16-byte store), and both equal the oracle's."""
+    import torch
+    from sparse_attention_indexer_fp8_amd import _lib
+
+    bs, top = 64, 9
+    case = _exact_case(870 + len(entry), batch=3, n_lo=1, n_hi=9000, page_size=bs, heads=16, k=0,
+                       block_size=bs, top_blocks=top, first=(0, bs * top - 5))
+    ins = _inputs(case)
+    fn = getattr(ops, entry)
+    blocks, slots = fn(*ins, bs, case.max_seq_len, bs, top)
+    args, B, H, D = ops._indexer_args(*ins)
+    lead = (B, H) if entry == "block_topk_heads" else (B,)
+    op = _lib.OP_BLOCK_TOPK_HEADS if entry == "block_topk_heads" else _lib.OP_BLOCK_TOPK
+    rows = B * H if entry == "block_topk_heads" else B
+    ws = torch.zeros(ops.workspace_bytes(op, rows, bs, case.max_seq_len), dtype=torch.uint8, device="cuda")
+    out_blocks = torch.empty(lead + (top,), dtype=torch.int32, device="cuda")
+    buf = torch.full((int(np.prod(lead)) * top * bs + 1,), 7, dtype=torch.int32, device="cuda")
+    shifted = buf[1:]
+    assert shifted.data_ptr() % 16 != 0
+    st = getattr(_lib.load(), entry)(*args, bs, None, ops._ptr(ins[6]), B, H, D, case.max_seq_len, bs, top,
+                                     ops._ptr(out_blocks), ops._ptr(shifted), ops._ptr(ws), ws.numel(),
+                                     ops._stream())
+    _lib.check(entry, st)
+    torch.cuda.synchronize()
+    assert int(buf[0]) == 7
+
+    # the order of a selection's blocks is unspecified: compare each
+    # selection's blocks as a set, and each block's slot list
+    def lists(blk, sl):
+        blk = blk.reshape(-1, top).cpu().numpy()
+        sl = sl.reshape(-1, top * bs).cpu().numpy()
+        return [{int(blk[r, i]): sl[r, i * bs:(i + 1) * bs].tolist() for i in range(top) if blk[r, i] >= 0}
+                for r in range(blk.shape[0])], [int((blk[r] < 0).sum()) for r in range(blk.shape[0])]
+
+    got, got_pad = lists(out_blocks, shifted)
+    ref, ref_pad = lists(blocks, slots)
+    assert got == ref and got_pad == ref_pad
+    for r in range(len(got)):  # padding entries of the slot lists
+        n_sel = top - got_pad[r]
+        assert (shifted.reshape(-1, top * bs)[r, n_sel * bs:] == -1).all()
+    if entry == "block_topk":
+        rb, rs, _, _ = oracle.block_topk(case)
+        exp, _ = lists(torch.from_numpy(np.ascontiguousarray(rb)), torch.from_numpy(np.ascontiguousarray(rs)))
+        assert got == exp
