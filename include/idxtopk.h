@@ -198,7 +198,9 @@ int topk_page_transform(const int32_t* idx, int32_t rows, int32_t k,
  *            idxtopk_workspace_bytes(IDXTOPK_OP_SCORE_TOPK_FUSED, batch, k, max_seq_len)
  *            bytes. It MUST be zero-filled before its first use, and every
  *            call leaves it zero-filled again. Concurrent calls must not
- *            share one workspace.
+ *            share one workspace. A call that returns IDXTOPK_ELAUNCH may
+ *            have run its first kernel only and left nonzero bytes behind:
+ *            zero the workspace again before its next use.
  * flags      0, or IDXTOPK_SORTED (out_slots and out_scores in sorted order;
  *            otherwise the order within a row is unspecified); any other
  *            bit gives IDXTOPK_EINVAL.
@@ -230,7 +232,8 @@ int idx_score_topk_fused(const uint8_t* q, const float* q_scale, const float* w,
  *            block, or -1 past n_b or for padded blocks.
  * workspace  at least idxtopk_workspace_bytes(IDXTOPK_OP_BLOCK_TOPK, batch,
  *            block_size, max_seq_len) bytes, zero-filled before first use; left
- *            zero-filled by every call.
+ *            zero-filled by every call that returns IDXTOPK_OK (after
+ *            IDXTOPK_ELAUNCH, zero it again, as for idx_score_topk_fused).
  * 1 <= top_blocks <= IDXTOPK_MAX_TOP_BLOCKS.
  */
 int block_topk(const uint8_t* q, const float* q_scale, const float* w,

@@ -43,27 +43,6 @@ def sorted_rows(a: np.ndarray) -> np.ndarray:
     return np.sort(np.asarray(a, dtype=np.int64), axis=1)
 
 
-def expected_set_fast(vals: np.ndarray, k: int) -> np.ndarray:
-    """Exact top-k position set of one row in O(n), for full-size checks.
-
-    The set is every position with a value above the k-th largest value, plus
-    the lowest positions among those equal to it. This is the same set as the
-    oracle's stable sort, which takes too long for 16384 rows of 70000. Sorted
-    ascending, -1 padded.
-    """
-    v = np.asarray(vals, dtype=np.float64)
-    n = v.shape[0]
-    out = np.full(k, -1, np.int64)
-    if n <= k:
-        out[:n] = np.arange(n)
-        return np.sort(out)
-    kth = np.partition(v, n - k)[n - k]
-    gt = np.flatnonzero(v > kth)
-    eq = np.flatnonzero(v == kth)[:k - gt.shape[0]]
-    out[:] = np.sort(np.concatenate([gt, eq]))
-    return np.sort(out)
-
-
 def positions_from_slots(slots_row: np.ndarray, tok_slots: np.ndarray) -> np.ndarray:
     """Invert the token -> slot map of one row (slots are distinct)."""
     order = np.argsort(tok_slots)

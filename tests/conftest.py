@@ -13,6 +13,26 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long-running CPU test")
 
 
+def _may_run_gpu_tests(config) -> bool:
+    return (config.getoption("-m") or "").strip() != "not gpu"
+
+
+def pytest_sessionstart(session):
+    # The full-size parity checks run the oracle in forked workers. Fork them
+    # now, before collection asks whether a GPU is there (which initialises
+    # it), so no worker inherits an initialised device.
+    if _may_run_gpu_tests(session.config):
+        from tests import _oracle_pool
+
+        _oracle_pool.start()
+
+
+def pytest_sessionfinish(session, exitstatus):
+    from tests import _oracle_pool
+
+    _oracle_pool.stop()
+
+
 def _gpu_available():
     try:
         import torch

@@ -138,6 +138,41 @@ def test_fused_workspace_reuse_smaller_second_call(ops):
         assert np.array_equal(np.sort(slots, axis=1), np.sort(ref, axis=1))
 
 
+def test_default_workspace_per_stream(ops):
+    """Fused and block calls made on two streams at once with default
+    workspaces get one workspace per stream: both results stay exact."""
+    import torch
+
+    fa = _exact_case(611, batch=6, n_lo=3000, n_hi=20000, page_size=64, k=700)
+    fb = _exact_case(612, batch=5, n_lo=2000, n_hi=18000, page_size=64, k=300)
+    ba = _exact_case(613, batch=6, n_lo=3000, n_hi=9000, page_size=128, k=0, block_size=128, top_blocks=9)
+    ref_a, _, _ = oracle.fused_topk(fa)
+    ref_b, _, _ = oracle.fused_topk(fb)
+    ref_blk = oracle.block_topk(ba)
+    ins = {id(c): _inputs(c) for c in (fa, fb, ba)}
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(3):
+        with torch.cuda.stream(s1):
+            oa = ops.idx_score_topk_fused(*ins[id(fa)], fa.page_size, fa.max_seq_len, fa.k)
+            ob = ops.block_topk(*ins[id(ba)], ba.page_size, ba.max_seq_len, ba.block_size, ba.top_blocks,
+                                return_slots=False)
+        with torch.cuda.stream(s2):
+            oc = ops.idx_score_topk_fused(*ins[id(fb)], fb.page_size, fb.max_seq_len, fb.k)
+            od = ops.block_topk(*ins[id(ba)], ba.page_size, ba.max_seq_len, ba.block_size, ba.top_blocks,
+                                return_slots=False)
+        outs.append((oa, ob, oc, od))
+    torch.cuda.synchronize()
+    keys = {k for k in ops._default_ws if k[1] in (s1.cuda_stream, s2.cuda_stream)}
+    assert len(keys) == 2, "one default workspace per stream"
+    for oa, ob, oc, od in outs:
+        assert np.array_equal(np.sort(oa.cpu().numpy(), axis=1), np.sort(ref_a, axis=1))
+        assert np.array_equal(np.sort(oc.cpu().numpy(), axis=1), np.sort(ref_b, axis=1))
+        for o in (ob, od):
+            assert np.array_equal(np.sort(o.cpu().numpy(), axis=1), np.sort(ref_blk[0], axis=1))
+
+
 # Batches of at most this many tokens (batch * max_seq_len) take the
 # score-buffer variant of the fused path; larger ones the candidate variant.
 FUSED_SCORE_PATH_TOKENS = 1 << 21
@@ -282,40 +317,35 @@ def test_block_random_tolerance(ops):
         assert (bsv[sel] >= kth - 1e-3 * max(abs(kth), sigma)).all()
 
 
-def _sampled_full(case, rows):
-    return {b: case_scores(case, b) for b in rows}
-
-
 def test_fused_decode_full_size(ops):
-    """Full-size fused decode (B=32, n in [8192, 16384], k=2048): every row."""
+    """Full-size fused decode (B=32, n in [8192, 16384], k=2048): every row
+    against the oracle criterion, returned scores within the tolerance."""
+    from tests import _fullsize
+
     case = workloads.c2_fused_decode()
     log(f"case {case.name}")
     slots, sc = _fused(ops, case)
-    for b in range(case.batch):
-        n = int(case.seq_lens[b])
-        ts = oracle.token_slots(case.block_table[b], case.page_size, n)
-        check_fused_row(slots[b], sc[b], case_scores(case, b), ts, case.k)
+    _fullsize.run(_fullsize.fused_rows_task, _fullsize.fused_tasks(case, slots, sc), case.name)
 
 
-def test_long_decode_full_size_sampled(ops):
-    """Full-size long-context decode (B=64, n up to 327680): sampled rows."""
+def test_long_decode_full_size(ops):
+    """Full-size long-context decode (B=64, n up to 327680, k=2048): every
+    row against the oracle criterion, returned scores within the tolerance."""
+    from tests import _fullsize
+
     case = workloads.c5_long_decode()
     log(f"case {case.name} tokens={workloads.expected_tokens(case)}")
     slots, sc = _fused(ops, case)
-    longest = int(np.argmax(case.seq_lens))
-    shortest = int(np.argmin(case.seq_lens))
-    for b in sorted({0, 31, 63, longest, shortest}):
-        n = int(case.seq_lens[b])
-        ts = oracle.token_slots(case.block_table[b], case.page_size, n)
-        ov = check_fused_row(slots[b], sc[b], case_scores(case, b), ts, case.k)
-        log(f"row {b} n={n} overlap={ov:.4f}")
-    # every row: count / distinct / padding properties
-    for b in range(case.batch):
-        assert (slots[b] >= 0).all() and np.unique(slots[b]).shape[0] == case.k
+    case.kcache = case.k_scale = None  # the workers draw each row's keys again
+    _fullsize.run(_fullsize.fused_rows_task, _fullsize.fused_tasks(case, slots, sc), case.name)
 
 
 def test_block_sparse_full_size(ops):
+    """Full-size block-sparse decode (B=64, n=32768, top 32 of 256 blocks):
+    every row against the block-score criterion, slot lists exact."""
     import torch
+
+    from tests import _fullsize
 
     case = workloads.c4_block_sparse()
     log(f"case {case.name}")
@@ -323,24 +353,7 @@ def test_block_sparse_full_size(ops):
                                    case.top_blocks)
     torch.cuda.synchronize()
     blocks, slots = blocks.cpu().numpy(), slots.cpu().numpy()
-    bs, top = case.block_size, case.top_blocks
-    for b in (0, 17, 63):
-        S = case_scores(case, b)
-        bsv = oracle.block_scores(S, bs)
-        page_to_blk = {int(case.block_table[b, c]): c for c in range(bsv.shape[0])}
-        sel = [page_to_blk[int(p)] for p in blocks[b]]
-        sigma = float(np.sqrt(np.mean(S * S)))
-        kth = np.sort(bsv)[::-1][top - 1]
-        assert len(set(sel)) == top
-        assert (bsv[sel] >= kth - 1e-3 * max(abs(kth), sigma)).all()
-        for i, c in enumerate(sel):
-            exp = int(case.block_table[b, c]) * bs + np.arange(bs)
-            assert np.array_equal(slots[b, i * bs:(i + 1) * bs], exp)
-
-
-# ---------------------------------------------------------------------------
-# Multi-token decode rows: several query rows share a block-table row
-# ---------------------------------------------------------------------------
+    _fullsize.run(_fullsize.block_rows_task, _fullsize.block_tasks(case, blocks, slots), case.name)
 
 
 def _expanded(case):
@@ -449,12 +462,16 @@ def test_row_pair_scores_match_per_row(ops, heads, page_size, next_n, requests):
         check_scores(out[b, :n], case_scores(case, b))
 
 
-def test_prefill_indexer_full_size_sampled(ops):
+@pytest.mark.timeout(900)
+def test_prefill_indexer_full_size(ops):
     """The prefill workload at full size, in the launch configuration the
     benchmark times (idx_score_fp8 with row_to_batch, then topk_rows through
-    the block table): sampled rows of both requests, including the longest
-    (70000 keys) and the shortest, against the oracle's scores and top-k."""
+    the block table): every row's scores against the oracle's within the
+    tolerance and its selection against the oracle criterion, in the oracle
+    pool."""
     import torch
+
+    from tests import _fullsize
 
     case = workloads.prefill_indexer()
     log(f"prefill full size: rows={case.batch} max n={case.max_seq_len}")
@@ -463,23 +480,26 @@ def test_prefill_indexer_full_size_sampled(ops):
     slots = ops.topk_rows(scores, dev(case.seq_lens), case.k, row_to_batch=r2b, page_table=dev(case.block_table),
                           page_size=case.page_size)
     torch.cuda.synchronize()
-    rows = [0, 4095, 8191, 8192, 8192 + 511, 8192 + 4000, case.batch - 1]
-    sc = {b: scores[b].cpu().numpy() for b in rows}
+    host = scores.cpu().numpy()
     slots = slots.cpu().numpy()
     del scores
     torch.cuda.empty_cache()
-    for b in rows:
-        n = int(case.seq_lens[b])
-        S = case_scores(case, b)
-        check_scores(sc[b][:n], S)
-        ts = oracle.token_slots(case.block_table[case.row_to_batch[b]], case.page_size, n)
-        check_fused_row(slots[b], None, S, ts, case.k)
+    lens = case.seq_lens
+
+    def gpu_rows(rr):
+        return [host[b, :int(lens[b])] for b in rr]
+
+    # request 0's rows see ~62K-70K keys, request 1's 1..8192: smaller tasks
+    # for the long rows keep the pool busy to the end
+    def tasks():
+        yield from _fullsize.fused_tasks(case, slots, rows=np.arange(0, 8192), per_task=32, gpu_scores=gpu_rows)
+        yield from _fullsize.fused_tasks(case, slots, rows=np.arange(8192, case.batch), per_task=512,
+                                         gpu_scores=gpu_rows)
+
+    n = _fullsize.run(_fullsize.fused_rows_task, tasks(), case.name)
+    assert n == case.batch
 
 
-# Sorted output: rows in descending score order, equal scores by ascending
-# position, -1 padding last. The oracle's selection is a stable descending
-# sort, so its order is that order: with exact arithmetic the whole output
-# sequence must match, ties included.
 @pytest.mark.parametrize("variant", ["score-buffer", "candidates"])
 @pytest.mark.parametrize("with_scores", [True, False])
 @pytest.mark.parametrize("k", [100, 700, 3000, 8192])
@@ -586,13 +606,12 @@ def test_block_heads_random_tolerance(ops):
 def test_mtp_decode_full_size(ops):
     """Multi-token decode 16 x 4 (n 16K-64K, k 2048): every row meets the
     tolerance criterion."""
+    from tests import _fullsize
+
     case = workloads.mtp_decode()
     log(f"case {case.name}")
     slots, sc = _fused(ops, case)
-    for b in range(case.batch):
-        n = int(case.seq_lens[b])
-        ts = oracle.token_slots(case.block_table[case.row_to_batch[b]], case.page_size, n)
-        check_fused_row(slots[b], sc[b], case_scores(case, b), ts, case.k)
+    _fullsize.run(_fullsize.fused_rows_task, _fullsize.fused_tasks(case, slots, sc, per_task=4), case.name)
 
 
 def test_fused_decode_full_size_sorted(ops):
@@ -612,33 +631,21 @@ def test_fused_decode_full_size_sorted(ops):
         assert dict(zip(s0[b].tolist(), v0[b].tolist())) == dict(zip(s1[b].tolist(), v1[b].tolist())), b
 
 
-def test_block_heads_full_size_sampled(ops):
+def test_block_heads_full_size(ops):
     """Per-head selection on the block-sparse geometry (B64, n 32768, top 32,
-    64 heads): sampled rows, every head, tolerance criterion."""
+    64 heads): every row and head against the block-score criterion, slot
+    lists exact."""
     import torch
-    from oracle.indexer import case_bt_row, index_head_scores
+
+    from tests import _fullsize
 
     case = workloads.c4_block_sparse()
     bs, top = case.block_size, case.top_blocks
     blocks, slots = ops.block_topk_heads(*_inputs(case), case.page_size, case.max_seq_len, bs, top)
     torch.cuda.synchronize()
     blocks, slots = blocks.cpu().numpy(), slots.cpu().numpy()
-    for b in (0, 33, 63):
-        n = int(case.seq_lens[b])
-        bt = case_bt_row(case, b)
-        T = index_head_scores(case.q[b], case.q_scale[b], case.w[b], case.kcache, case.k_scale, bt,
-                              case.page_size, n)
-        nb = -(-n // bs)
-        page_to_blk = {int(bt[c]): c for c in range(nb)}
-        for h in range(case.heads):
-            bsv = oracle.block_scores(T[:, h], bs)
-            sel = [page_to_blk[int(p)] for p in blocks[b, h]]
-            assert len(set(sel)) == top, (b, h)
-            sigma = max(float(np.sqrt(np.mean(T[:, h] ** 2))), 1e-30)
-            kth = np.sort(bsv)[::-1][top - 1]
-            assert (bsv[sel] >= kth - 1e-3 * max(abs(kth), sigma)).all(), (b, h)
-            for i, c in enumerate(sel):
-                assert np.array_equal(slots[b, h, i * bs:(i + 1) * bs], int(bt[c]) * bs + np.arange(bs)), (b, h)
+    _fullsize.run(_fullsize.block_rows_task, _fullsize.block_tasks(case, blocks, slots, per_head=True, per_task=2),
+                  case.name + " per head")
 
 
 @pytest.mark.parametrize("entry", ["block_topk", "block_topk_heads"])

@@ -109,11 +109,17 @@ class RowsCase:
         return int(self.scores.shape[1])
 
 
-def _fill_row(buf_row: np.ndarray, start: int, n: int, seed: int, row: int, tie_frac: float) -> None:
+def window_values(seed: int, row: int, n: int, tie_frac: float) -> np.ndarray:
+    """The n fp32 values of row ``row``'s window (its own random streams), so
+    any row of a score buffer can be drawn again on its own."""
     v = rng(seed, STREAM_VAL, row).standard_normal(n, dtype=np.float32)
     _snap(v, tie_frac, rng(seed, STREAM_SNAP, row))
+    return v
+
+
+def _fill_row(buf_row: np.ndarray, start: int, n: int, seed: int, row: int, tie_frac: float) -> None:
     buf_row[:] = SENTINEL_SCORE
-    buf_row[start:start + n] = v
+    buf_row[start:start + n] = window_values(seed, row, n, tie_frac)
 
 
 def _fill_rows(scores, starts, lens, seed, tie_frac):
@@ -216,6 +222,30 @@ class IndexerCase:
         return int(self.q.shape[2])
 
 
+def query_row(seed: int, row: int, heads: int, dim: int, bf16: bool, q_stream: int = STREAM_Q,
+              w_stream: int = STREAM_W):
+    """Query row ``row``: (q [heads, dim] e4m3fn bytes or bf16 patterns, its
+    fp32 scale (1 for bf16), head weights [heads] fp32)."""
+    qf = rng(seed, q_stream, row).standard_normal((heads, dim), dtype=np.float32) * np.float32(0.5)
+    w = rng(seed, w_stream, row).standard_normal(heads, dtype=np.float32) / np.float32(8.0)
+    if bf16:
+        return _to_bf16_bits(qf), np.float32(1.0), w
+    s = np.float32(np.abs(qf).max() / np.float32(E4M3_MAX))
+    return _to_e4m3_bytes(qf / s), s, w
+
+
+def key_rows(seed: int, request: int, n: int, dim: int, bf16: bool):
+    """The n index keys of request ``request`` in token order: (keys [n, dim]
+    e4m3fn bytes or bf16 patterns, per-token fp32 scales [n] (ones for
+    bf16))."""
+    kf = rng(seed, STREAM_KEY, request).standard_normal((n, dim), dtype=np.float32)
+    if bf16:
+        return _to_bf16_bits(kf), np.ones(n, np.float32)
+    s = (np.abs(kf).max(axis=1) / np.float32(E4M3_MAX)).astype(np.float32)
+    s = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    return _to_e4m3_bytes(kf / s[:, None]), s
+
+
 def indexer_case(seed: int, batch: int, n_lo: int, n_hi: int, page_size: int, k: int = 2048,
                  heads: int = 64, dim: int = 128, block_size: int = 0, top_blocks: int = 0,
                  fixed_lens: Optional[np.ndarray] = None, name: str = "indexer",
@@ -250,14 +280,7 @@ def indexer_case(seed: int, batch: int, n_lo: int, n_hi: int, page_size: int, k:
     q_scale = np.ones(batch, np.float32)
     w = np.empty((batch, heads), np.float32)
     for b in range(batch):
-        qf = rng(seed, STREAM_Q, b).standard_normal((heads, dim), dtype=np.float32) * np.float32(0.5)
-        if bf16:
-            q[b] = _to_bf16_bits(qf)
-        else:
-            s = np.float32(np.abs(qf).max() / np.float32(E4M3_MAX))
-            q_scale[b] = s
-            q[b] = _to_e4m3_bytes(qf / s)
-        w[b] = rng(seed, STREAM_W, b).standard_normal(heads, dtype=np.float32) / np.float32(8.0)
+        q[b], q_scale[b], w[b] = query_row(seed, b, heads, dim, bf16)
 
     if bf16:
         kcache = np.full((num_slots, dim), SENTINEL_KEY_BF16, np.uint16)
@@ -274,16 +297,11 @@ def indexer_case(seed: int, batch: int, n_lo: int, n_hi: int, page_size: int, k:
         bt[b, :pages.shape[0]] = pages.astype(np.int32)
         if n == 0:
             return
-        kf = rng(seed, STREAM_KEY, b).standard_normal((n, dim), dtype=np.float32)
         slots = (pages[:, None] * P + np.arange(P, dtype=np.int64)[None, :]).reshape(-1)[:n]
-        if bf16:
-            kcache[slots] = _to_bf16_bits(kf)
-            return
-        s = (np.abs(kf).max(axis=1) / np.float32(E4M3_MAX)).astype(np.float32)
-        s = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
-        kb = _to_e4m3_bytes(kf / s[:, None])
+        kb, s = key_rows(seed, b, n, dim, bf16)
         kcache[slots] = kb
-        k_scale[slots] = s
+        if not bf16:
+            k_scale[slots] = s
 
     if batch * max_seq_len * dim < (1 << 24):
         for b in range(batch):
@@ -294,7 +312,8 @@ def indexer_case(seed: int, batch: int, n_lo: int, n_hi: int, page_size: int, k:
 
     return IndexerCase(name, q, q_scale, w, kcache, k_scale, bt, P, lens, k=k,
                        block_size=block_size, top_blocks=top_blocks, max_seq_len=max_seq_len,
-                       meta={"total_pages": total_pages, "sentinel_page": sentinel_page},
+                       meta={"total_pages": total_pages, "sentinel_page": sentinel_page, "seed": int(seed),
+                             "request_lens": lens.copy(), "q_streams": (STREAM_Q, STREAM_W)},
                        cache_dtype=cache_dtype)
 
 
@@ -315,20 +334,52 @@ def multi_query_case(seed: int, requests: int, next_n: int, n_lo: int, n_hi: int
     q_scale = np.ones(rows, np.float32)
     w = np.empty((rows, heads), np.float32)
     for r in range(rows):
-        qf = rng(seed, STREAM_MQ, r).standard_normal((heads, dim), dtype=np.float32) * np.float32(0.5)
-        if bf16:
-            q[r] = _to_bf16_bits(qf)
-        else:
-            s = np.float32(np.abs(qf).max() / np.float32(E4M3_MAX))
-            q_scale[r] = s
-            q[r] = _to_e4m3_bytes(qf / s)
-        w[r] = rng(seed, STREAM_MW, r).standard_normal(heads, dtype=np.float32) / np.float32(8.0)
+        q[r], q_scale[r], w[r] = query_row(seed, r, heads, dim, bf16, STREAM_MQ, STREAM_MW)
     r2b = np.repeat(np.arange(requests, dtype=np.int32), next_n)
     t = np.tile(np.arange(next_n, dtype=np.int32), requests)
     lens = np.maximum(base.seq_lens[r2b] - (next_n - 1 - t), 0).astype(np.int32)
     return IndexerCase(name, q, q_scale, w, base.kcache, base.k_scale, base.block_table, page_size, lens, k=k,
-                       max_seq_len=base.max_seq_len, meta=dict(base.meta, requests=requests, next_n=next_n),
+                       max_seq_len=base.max_seq_len,
+                       meta=dict(base.meta, requests=requests, next_n=next_n, q_streams=(STREAM_MQ, STREAM_MW)),
                        row_to_batch=r2b, cache_dtype=cache_dtype)
+
+
+@dataclass
+class RowInputs:
+    """One query row of an IndexerCase drawn again on its own: its query, its
+    scale and head weights, and the keys of its block-table row's request in
+    token order (keys[j] is the key of the row's token j)."""
+
+    q: np.ndarray
+    q_scale: np.float32
+    w: np.ndarray
+    keys: np.ndarray
+    k_scale: np.ndarray
+    n: int
+
+
+def row_spec(case: IndexerCase) -> dict:
+    """What ``row_inputs`` needs to draw any row of ``case`` again (small)."""
+    return {"seed": case.meta["seed"], "heads": case.heads, "dim": case.dim, "bf16": case.cache_dtype == "bf16",
+            "q_streams": tuple(case.meta["q_streams"]), "request_lens": np.asarray(case.meta["request_lens"]),
+            "row_to_batch": None if case.row_to_batch is None else np.asarray(case.row_to_batch),
+            "seq_lens": np.asarray(case.seq_lens)}
+
+
+def row_inputs(spec: dict, row: int, keys_cache: Optional[dict] = None) -> RowInputs:
+    """Row ``row`` of the case ``spec`` describes, from the same draws as the
+    whole case (``query_row``, ``key_rows``). ``keys_cache`` (a dict) keeps
+    each request's keys for later rows of the same request."""
+    request = row if spec["row_to_batch"] is None else int(spec["row_to_batch"][row])
+    q, s, w = query_row(spec["seed"], row, spec["heads"], spec["dim"], spec["bf16"], *spec["q_streams"])
+    key = (spec["seed"], request, spec["bf16"])
+    kv = None if keys_cache is None else keys_cache.get(key)
+    if kv is None:
+        kv = key_rows(spec["seed"], request, int(spec["request_lens"][request]), spec["dim"], spec["bf16"])
+        if keys_cache is not None:
+            keys_cache.clear()
+            keys_cache[key] = kv
+    return RowInputs(q, s, w, kv[0], kv[1], int(spec["seq_lens"][row]))
 
 
 # --------------------------------------------------------------------------
@@ -406,4 +457,5 @@ __all__ = [
     "c1_decode_topk", "c2_fused_decode", "c3_packed_prefill", "c4_block_sparse", "c5_long_decode", "mtp_decode",
     "prefill_indexer", "bf16_decode", "bf16_long_decode", "SENTINEL_KEY_BF16",
     "SEEDS", "SENTINEL_KEY_BYTE", "SENTINEL_KEY_SCALE", "rng", "expected_tokens", "ceil_div",
+    "window_values", "query_row", "key_rows", "RowInputs", "row_spec", "row_inputs",
 ]
