@@ -616,6 +616,20 @@ static inline int rows_cap(int k) {
   return (a > b ? a : b) + 8;
 }
 
+// What the streaming loop relies on (checked before every launch):
+//  * the first tile plus the scalar head and tail (at most 3 each) fits
+//    before any compaction: cap >= TR_TILE + 6;
+//  * after_tile's slack (cap - TR_TILE - k) / 2, computed in uint32, is at
+//    least 1: a smaller buffer would wrap it to ~2^31, the compaction select
+//    would stop after one histogram and keep nearly every key, and the next
+//    tile would be appended past the end of the buffer;
+//  * after a compaction the buffer holds at most k + slack keys, so the next
+//    tile fits: k + slack + TR_TILE <= cap, which the slack's definition
+//    gives for any cap above.
+static inline bool rows_cap_ok(int cap, int k) {
+  return cap >= TR_TILE + 6 && static_cast<int64_t>(cap) - TR_TILE - k >= 2;
+}
+
 int launch_topk_rows(const float* scores, int64_t stride, int rows, const int32_t* seq_lens,
                      const int32_t* row_starts, const int32_t* row_to_batch, const int32_t* kv_offset,
                      const int32_t* page_table, int64_t pt_stride, int page_size, int k,
@@ -638,6 +652,7 @@ int launch_topk_rows(const float* scores, int64_t stride, int rows, const int32_
   while (npow < k) npow <<= 1;
   a.npow = npow;
   if (sorted && a.cap < npow) a.cap = npow;
+  if (!rows_cap_ok(a.cap, k)) return -4;
   const size_t lds = static_cast<size_t>(a.cap) * sizeof(uint64_t);
   const void* kern = sorted ? reinterpret_cast<const void*>(&topk_rows_kernel<true>)
                             : reinterpret_cast<const void*>(&topk_rows_kernel<false>);

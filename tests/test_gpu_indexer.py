@@ -356,6 +356,11 @@ def test_block_sparse_full_size(ops):
     _fullsize.run(_fullsize.block_rows_task, _fullsize.block_tasks(case, blocks, slots), case.name)
 
 
+# ---------------------------------------------------------------------------
+# Multi-token decode rows: several query rows share a block-table row
+# ---------------------------------------------------------------------------
+
+
 def _expanded(case):
     """The case with the indirection resolved: each query row gets its own
     copy of its block-table row."""
@@ -500,6 +505,10 @@ def test_prefill_indexer_full_size(ops):
     assert n == case.batch
 
 
+# Sorted output: rows in descending score order, equal scores by ascending
+# position, -1 padding last. The oracle's selection is a stable descending
+# sort, so its order is that order: with exact arithmetic the whole output
+# sequence must match, ties included.
 @pytest.mark.parametrize("variant", ["score-buffer", "candidates"])
 @pytest.mark.parametrize("with_scores", [True, False])
 @pytest.mark.parametrize("k", [100, 700, 3000, 8192])

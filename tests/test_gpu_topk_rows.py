@@ -234,6 +234,8 @@ def test_packed_prefill_full_size(ops):
     n = _fullsize.run(_fullsize.packed_rows_task, _fullsize.packed_tasks(case, got, srt), "packed prefill")
     assert n == case.seq_lens.shape[0]
 
+
+@pytest.mark.parametrize("k", [1, 300, 512, 1000, 2048, 4000, 8192])
 def test_topk_rows_sorted_order(ops, k):
     import torch
 
