@@ -215,6 +215,33 @@ int idx_score_topk_fused(const uint8_t* q, const float* q_scale, const float* w,
                          size_t workspace_bytes, int32_t flags, void* stream);
 
 /*
+ * idx_score_topk_fused_noalloc -- idx_score_topk_fused with a built-in
+ * workspace, for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * Arguments, outputs, flags and status codes are idx_score_topk_fused's,
+ * without the workspace: the call uses a workspace of
+ * IDXTOPK_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
+ * on, from the first call on that GPU until the process ends. The call
+ * allocates and frees nothing. The first call on a device looks up that
+ * device's array (no allocation, no stream work).
+ * Returns IDXTOPK_EWORKSPACE when the call would need more than that:
+ * idxtopk_workspace_bytes(IDXTOPK_OP_SCORE_TOPK_FUSED, batch, k, max_seq_len)
+ * > IDXTOPK_NOALLOC_SCRATCH_BYTES.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (two streams, two threads) race and give wrong results. After a
+ * call that returned IDXTOPK_ELAUNCH, the next call first clears the array
+ * with a fill kernel on its stream.
+ */
+#define IDXTOPK_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20) /* 64 MiB per GPU */
+int idx_score_topk_fused_noalloc(const uint8_t* q, const float* q_scale, const float* w,
+                                 const uint8_t* kcache, const float* k_scale,
+                                 const int32_t* block_table, int64_t bt_stride, int32_t page_size,
+                                 const int32_t* row_to_batch, const int32_t* seq_lens, int32_t batch,
+                                 int32_t heads, int32_t dim, int32_t max_seq_len, int32_t k,
+                                 int32_t* out_slots, float* out_scores, int32_t flags, void* stream);
+
+/*
  * block_topk -- block-sparse variant: block scores, top blocks, sparse list.
  *
  * Block c of row b covers tokens [c * block_size, min((c + 1) * block_size,

@@ -28,6 +28,7 @@ OP_BLOCK_TOPK_HEADS = 7
 KEY_F32 = 0
 KEY_BF16 = 1
 SORTED = 1
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -42,6 +43,8 @@ SIGNATURES = {
     "topk_page_transform": (_i32, [_vp, _i32, _i32, _vp, _i64, _i32, _vp, _vp, _vp]),
     "idx_score_topk_fused": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32,
                                     _i32, _i32, _i32, _vp, _vp, _vp, _sz, _i32, _vp]),
+    "idx_score_topk_fused_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32,
+                                            _i32, _i32, _i32, _vp, _vp, _i32, _vp]),
     "block_topk": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32, _i32, _i32,
                           _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "block_topk_heads": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32, _i32, _i32,

@@ -3,7 +3,56 @@
 #include "../../include/idxtopk.h"
 #include "launch.hpp"
 
+#include <mutex>
+
 namespace {
+
+// ---------------------------------------------------------------------------
+// Built-in workspace of idx_score_topk_fused_noalloc
+// ---------------------------------------------------------------------------
+//
+// One array per GPU the library runs on, zero when the code object is loaded
+// and held until the process ends. Host code never passes `scratch` itself
+// to a kernel (on the host that name is only a stand-in, not a device
+// address): the first call on a device resolves the device's own address
+// with hipGetSymbolAddress, and every later use goes through that pointer.
+constexpr size_t kScratchBytes = IDXTOPK_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+struct ScratchState {
+  void* ptr = nullptr;  // the device address of `scratch` on this device
+  bool dirty = false;   // a failed launch may have left nonzero bytes
+};
+
+std::mutex g_scratch_mu;
+ScratchState g_scratch[kMaxDevices];
+
+// Zero fill with a kernel rather than a memset node, so that a caller may
+// capture the call in a graph.
+__global__ void zero_fill_kernel(uint4* p, size_t n16) {
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n16;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The current device's scratch address (resolved once per device), or null.
+void* scratch_ptr(int* dev_out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  *dev_out = dev;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev].ptr == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch[dev].ptr = p;
+  }
+  return g_scratch[dev].ptr;
+}
 
 using idxtopk::IndexerInputs;
 
@@ -117,6 +166,44 @@ int idx_score_topk_fused(const uint8_t* q, const float* q_scale, const float* w,
                                     page_size, row_to_batch, seq_lens, batch, heads, max_seq_len),
                                k, out_slots, out_scores, workspace, (flags & IDXTOPK_SORTED) != 0,
                                static_cast<hipStream_t>(stream));
+}
+
+int idx_score_topk_fused_noalloc(const uint8_t* q, const float* q_scale, const float* w,
+                                 const uint8_t* kcache, const float* k_scale, const int32_t* block_table,
+                                 int64_t bt_stride, int32_t page_size, const int32_t* row_to_batch,
+                                 const int32_t* seq_lens, int32_t batch, int32_t heads, int32_t dim,
+                                 int32_t max_seq_len, int32_t k, int32_t* out_slots, float* out_scores,
+                                 int32_t flags, void* stream) {
+  if (flags & ~IDXTOPK_SORTED) return IDXTOPK_EINVAL;
+  const int st = check_indexer(q, q_scale, w, kcache, k_scale, block_table, bt_stride, page_size,
+                               seq_lens, batch, heads, dim, max_seq_len);
+  if (st != IDXTOPK_OK) return st;
+  if (k <= 0 || (batch > 0 && !out_slots)) return IDXTOPK_EINVAL;
+  if (k > IDXTOPK_MAX_K_FUSED) return IDXTOPK_EUNSUPPORTED;
+  if (batch == 0) return IDXTOPK_OK;
+  const size_t need = idxtopk::fused_workspace_bytes(batch, k, max_seq_len);
+  if (need > kScratchBytes) return IDXTOPK_EWORKSPACE;
+  int dev = -1;
+  void* ws = scratch_ptr(&dev);
+  if (ws == nullptr) return IDXTOPK_ELAUNCH;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev].dirty) {
+      (void)hipGetLastError();
+      hipLaunchKernelGGL(zero_fill_kernel, dim3(1024), dim3(256), 0, s, static_cast<uint4*>(ws), kScratchBytes / 16);
+      if (hipGetLastError() != hipSuccess) return IDXTOPK_ELAUNCH;
+      g_scratch[dev].dirty = false;
+    }
+  }
+  const int e = idxtopk::launch_fused(pack(q, q_scale, w, kcache, k_scale, block_table, bt_stride, page_size,
+                                           row_to_batch, seq_lens, batch, heads, max_seq_len),
+                                      k, out_slots, out_scores, ws, (flags & IDXTOPK_SORTED) != 0, s);
+  if (e != 0) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    g_scratch[dev].dirty = true;
+  }
+  return e;
 }
 
 int block_topk(const uint8_t* q, const float* q_scale, const float* w, const uint8_t* kcache,

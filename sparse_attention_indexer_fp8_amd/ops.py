@@ -220,6 +220,23 @@ def idx_score_topk_fused(q, q_scale, w, kcache, k_scale, block_table, seq_lens, 
     return (out, out_scores) if return_scores else out
 
 
+def idx_score_topk_fused_noalloc(q, q_scale, w, kcache, k_scale, block_table, seq_lens, page_size: int,
+                                 max_seq_len: int, k: int, out: torch.Tensor, out_scores: Optional[torch.Tensor] = None,
+                                 row_to_batch: Optional[torch.Tensor] = None, sorted: bool = False):
+    """idx_score_topk_fused with the library's built-in workspace: the caller
+    passes the outputs (out [B, k] int32, optional out_scores [B, k] fp32)
+    and nothing is allocated. Calls that overlap on one GPU race."""
+    args, B, H, D = _indexer_args(q, q_scale, w, kcache, k_scale, block_table, seq_lens, row_to_batch)
+    _need(out, "out", (torch.int32,), 2)
+    if out_scores is not None:
+        _need(out_scores, "out_scores", (torch.float32,), 2)
+    st = _lib.load().idx_score_topk_fused_noalloc(*args, int(page_size), _ptr(row_to_batch), _ptr(seq_lens), B, H,
+                                                  D, int(max_seq_len), int(k), _ptr(out), _ptr(out_scores),
+                                                  _lib.SORTED if sorted else 0, _stream())
+    _lib.check("idx_score_topk_fused_noalloc", st)
+    return out
+
+
 def block_topk(q, q_scale, w, kcache, k_scale, block_table, seq_lens, page_size: int,
                max_seq_len: int, block_size: int, top_blocks: int, return_slots: bool = True,
                workspace: Optional[Workspace] = None, row_to_batch: Optional[torch.Tensor] = None):

@@ -249,3 +249,29 @@ def test_block_heads_validation(lib):
     assert f(nb=need - 1) == -3        # sized for batch * heads selections
     assert f(H=48) == -2
     assert f(B=0) == 0
+
+
+def test_fused_noalloc_validation(lib):
+    """Host-side checks of the built-in-workspace entry point (each returns
+    before any HIP call): bad arguments, and a call larger than the built-in
+    workspace."""
+    from sparse_attention_indexer_fp8_amd import _lib
+
+    d = _defines()
+
+    def call(batch=4, heads=64, dim=128, msl=4096, k=256, out=FAKE, flags=0, P=64, bts=64):
+        return lib.idx_score_topk_fused_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, bts, P, NULL, FAKE, batch, heads,
+                                                dim, msl, k, out, NULL, flags, NULL)
+
+    assert call(batch=-1) == -1
+    assert call(k=0) == -1
+    assert call(out=NULL) == -1
+    assert call(flags=2) == -1
+    assert call(dim=64) == -2
+    assert call(k=d["IDXTOPK_MAX_K_FUSED"] + 1) == -2
+    assert call(batch=0) == 0
+    # more than the built-in workspace holds
+    big = 1 << 20
+    need = lib.idxtopk_workspace_bytes(_lib.OP_SCORE_TOPK_FUSED, 64, 2048, big)
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    assert call(batch=64, msl=big, k=2048, bts=big // 64) == -3
