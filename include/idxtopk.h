@@ -196,11 +196,9 @@ int topk_page_transform(const int32_t* idx, int32_t rows, int32_t k,
  *            (-inf for padding).
  * workspace  device memory of at least
  *            idxtopk_workspace_bytes(IDXTOPK_OP_SCORE_TOPK_FUSED, batch, k, max_seq_len)
- *            bytes. It MUST be zero-filled before its first use, and every
- *            call leaves it zero-filled again. Concurrent calls must not
- *            share one workspace. A call that returns IDXTOPK_ELAUNCH may
- *            have run its first kernel only and left nonzero bytes behind:
- *            zero the workspace again before its next use.
+ *            bytes, with any contents: the call reads only what it wrote
+ *            itself, and no later call depends on what it leaves. Concurrent
+ *            calls must not share one workspace.
  * flags      0, or IDXTOPK_SORTED (out_slots and out_scores in sorted order;
  *            otherwise the order within a row is unspecified); any other
  *            bit gives IDXTOPK_EINVAL.
@@ -229,9 +227,8 @@ int idx_score_topk_fused(const uint8_t* q, const float* q_scale, const float* w,
  * idxtopk_workspace_bytes(IDXTOPK_OP_SCORE_TOPK_FUSED, batch, k, max_seq_len)
  * > IDXTOPK_NOALLOC_SCRATCH_BYTES.
  * Every call on one GPU shares that GPU's array: calls that may overlap on
- * one GPU (two streams, two threads) race and give wrong results. After a
- * call that returned IDXTOPK_ELAUNCH, the next call first clears the array
- * with a fill kernel on its stream.
+ * one GPU (two streams, two threads) race and give wrong results. (The
+ * array's contents never matter: each call reads only what it wrote.)
  */
 #define IDXTOPK_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20) /* 64 MiB per GPU */
 int idx_score_topk_fused_noalloc(const uint8_t* q, const float* q_scale, const float* w,
@@ -258,9 +255,8 @@ int idx_score_topk_fused_noalloc(const uint8_t* q, const float* q_scale, const f
  *            i * block_size + t is the slot of token t of the i-th emitted
  *            block, or -1 past n_b or for padded blocks.
  * workspace  at least idxtopk_workspace_bytes(IDXTOPK_OP_BLOCK_TOPK, batch,
- *            block_size, max_seq_len) bytes, zero-filled before first use; left
- *            zero-filled by every call that returns IDXTOPK_OK (after
- *            IDXTOPK_ELAUNCH, zero it again, as for idx_score_topk_fused).
+ *            block_size, max_seq_len) bytes, with any contents (as for
+ *            idx_score_topk_fused); concurrent calls must not share one.
  * 1 <= top_blocks <= IDXTOPK_MAX_TOP_BLOCKS.
  */
 int block_topk(const uint8_t* q, const float* q_scale, const float* w,
@@ -289,8 +285,8 @@ int block_topk(const uint8_t* q, const float* q_scale, const float* w,
  * out_slots   optional int32 [batch, heads, top_blocks * block_size], laid
  *             out as block_topk's per (row, head);
  * workspace   at least idxtopk_workspace_bytes(IDXTOPK_OP_BLOCK_TOPK_HEADS,
- *             batch * heads, block_size, max_seq_len) bytes, zero-filled
- *             before first use and left zero-filled (as for block_topk).
+ *             batch * heads, block_size, max_seq_len) bytes, with any
+ *             contents (as for block_topk).
  * Other arguments, limits and status codes: block_topk's (fp8 cache).
  */
 int block_topk_heads(const uint8_t* q, const float* q_scale, const float* w,

@@ -11,47 +11,34 @@ namespace {
 // Built-in workspace of idx_score_topk_fused_noalloc
 // ---------------------------------------------------------------------------
 //
-// One array per GPU the library runs on, zero when the code object is loaded
-// and held until the process ends. Host code never passes `scratch` itself
-// to a kernel (on the host that name is only a stand-in, not a device
-// address): the first call on a device resolves the device's own address
-// with hipGetSymbolAddress, and every later use goes through that pointer.
+// One array per GPU the library runs on, held until the process ends. Host
+// code never passes `scratch` itself to a kernel (on the host that name is
+// only a stand-in, not a device address): the first call on a device
+// resolves the device's own address with hipGetSymbolAddress, and every
+// later use goes through that pointer. The fused path needs no particular
+// workspace contents, so the array is never cleared.
 constexpr size_t kScratchBytes = IDXTOPK_NOALLOC_SCRATCH_BYTES;
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 constexpr int kMaxDevices = 64;
 
-struct ScratchState {
-  void* ptr = nullptr;  // the device address of `scratch` on this device
-  bool dirty = false;   // a failed launch may have left nonzero bytes
-};
-
 std::mutex g_scratch_mu;
-ScratchState g_scratch[kMaxDevices];
-
-// Zero fill with a kernel rather than a memset node, so that a caller may
-// capture the call in a graph.
-__global__ void zero_fill_kernel(uint4* p, size_t n16) {
-  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n16;
-       i += static_cast<size_t>(gridDim.x) * blockDim.x)
-    p[i] = make_uint4(0u, 0u, 0u, 0u);
-}
+void* g_scratch[kMaxDevices];  // the device address of `scratch` on each device
 
 // The current device's scratch address (resolved once per device), or null.
-void* scratch_ptr(int* dev_out) {
+void* scratch_ptr() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  *dev_out = dev;
   std::lock_guard<std::mutex> lock(g_scratch_mu);
-  if (g_scratch[dev].ptr == nullptr) {
+  if (g_scratch[dev] == nullptr) {
     void* p = nullptr;
     if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
       (void)hipGetLastError();
       return nullptr;
     }
-    g_scratch[dev].ptr = p;
+    g_scratch[dev] = p;
   }
-  return g_scratch[dev].ptr;
+  return g_scratch[dev];
 }
 
 using idxtopk::IndexerInputs;
@@ -183,27 +170,12 @@ int idx_score_topk_fused_noalloc(const uint8_t* q, const float* q_scale, const f
   if (batch == 0) return IDXTOPK_OK;
   const size_t need = idxtopk::fused_workspace_bytes(batch, k, max_seq_len);
   if (need > kScratchBytes) return IDXTOPK_EWORKSPACE;
-  int dev = -1;
-  void* ws = scratch_ptr(&dev);
+  void* ws = scratch_ptr();
   if (ws == nullptr) return IDXTOPK_ELAUNCH;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  {
-    std::lock_guard<std::mutex> lock(g_scratch_mu);
-    if (g_scratch[dev].dirty) {
-      (void)hipGetLastError();
-      hipLaunchKernelGGL(zero_fill_kernel, dim3(1024), dim3(256), 0, s, static_cast<uint4*>(ws), kScratchBytes / 16);
-      if (hipGetLastError() != hipSuccess) return IDXTOPK_ELAUNCH;
-      g_scratch[dev].dirty = false;
-    }
-  }
-  const int e = idxtopk::launch_fused(pack(q, q_scale, w, kcache, k_scale, block_table, bt_stride, page_size,
-                                           row_to_batch, seq_lens, batch, heads, max_seq_len),
-                                      k, out_slots, out_scores, ws, (flags & IDXTOPK_SORTED) != 0, s);
-  if (e != 0) {
-    std::lock_guard<std::mutex> lock(g_scratch_mu);
-    g_scratch[dev].dirty = true;
-  }
-  return e;
+  return idxtopk::launch_fused(pack(q, q_scale, w, kcache, k_scale, block_table, bt_stride, page_size,
+                                    row_to_batch, seq_lens, batch, heads, max_seq_len),
+                               k, out_slots, out_scores, ws, (flags & IDXTOPK_SORTED) != 0,
+                               static_cast<hipStream_t>(stream));
 }
 
 int block_topk(const uint8_t* q, const float* q_scale, const float* w, const uint8_t* kcache,

@@ -14,26 +14,25 @@
 // all XCDs. Chunks past a row's length exit at once. Every workgroup scores
 // its chunk with the fp8 MFMA core (score_mfma.hpp).
 //
-// Fused decode (idx_score_topk_fused), per chunk:
-//  1. Scores stay in LDS. A 4096-bin LDS histogram of the value keys' top 12
-//     bits is built on the fly.
-//  2. The chunk adds its histogram into the row's global histogram, then reads
-//     the global histogram back. The highest bin whose count from the top
-//     reaches k is a valid lower bound on the row's k-th score: every count
-//     seen belongs to a real token, whichever chunks have added so far.
-//  3. The chunk emits only tokens in bins >= that bound, as unique 64-bit
-//     keys (score key, inverted position), to the row's candidate list in
-//     the workspace.
-//  4. A second kernel merges, one workgroup per row, once every chunk is
-//     done. The complete histogram names the exact threshold bin.
-//     Candidates above it are emitted directly. Candidates in it go to LDS,
-//     and an exact select takes the remaining count. Output goes through the
-//     block table to slots. The merging workgroup then zeroes the row's
-//     histogram, counters and candidates, so the workspace is clean for the
-//     next call.
-// The score row never exists in HBM on this path. Batches of at most
-// FS_MAX_TOKENS tokens take a variant whose chunks write their scores to the
-// workspace instead (see "Fused decode, small batches" below).
+// Fused decode (idx_score_topk_fused):
+//  1. Per chunk: scores stay in LDS, with a 4096-bin LDS histogram of the
+//     value keys' top 12 bits. The chunk's bound is the bin where its own
+//     count from the top reaches a rank with a wide statistical margin over
+//     its expected share of the row's k best. Its tokens in bins at or above
+//     that bin go, as unique 64-bit keys (score key, inverted position), to
+//     the chunk's own range of the row's candidate area, and (count, bound)
+//     to the chunk's header. No chunk waits on another.
+//  2. Per row, once every chunk is done: the merge gathers the candidates,
+//     histograms them and takes the threshold bin for rank k. When that bin
+//     is at or above every chunk's bound, every token of the row in it and
+//     above is a candidate, so the selection is exact: candidates above the
+//     bin are emitted, those in it go through an exact select. Otherwise
+//     (best tokens crowded into a few chunks far beyond the margin) the
+//     merge scores the row again itself, keeping every token at or above
+//     the candidates' threshold bin, a proven lower bound, and selects from
+//     those. Output goes through the block table to slots.
+// The score row never exists in HBM, and the workspace needs no initial
+// contents: each entry the merge reads was written earlier in the call.
 #include "../../include/idxtopk.h"
 #include "common.hpp"
 #include "launch.hpp"
@@ -58,53 +57,66 @@ static_assert(IX_PAGES <= kMaxChunkPages, "page staging");
 
 static inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Fused decode: the candidates of chunk c of row b sit at its own tokens'
+// positions of the row's area, cand[b][tb_c, tb_c + count); hdr[b][c] holds
+// (count, bound bin). Every entry the merge reads was written earlier in the
+// same call, so the area needs no initial contents.
+constexpr int FE_CH_MIN = 256;         // shortest chunk: bounds the chunks of a row
+constexpr int FE_RESIDENT_MAX = 2048;  // longest chunk of the one-resident-wave sizing
+
 struct FusedWs {
-  uint32_t* hist;  // [rows][HIST_BINS]
-  uint32_t* ctr;   // [rows][4]: candidate count, done chunks
   uint64_t* cand;  // [rows][cap]
   int64_t cap;
+  uint2* hdr;      // [rows][hcap]
+  int32_t hcap;
   float* sval;     // [rows][k]: scores of the selection for the sort pass
 };
+
+// Chunk headers per row: enough for chunks of FE_CH_MIN tokens or more,
+// whichever schedule (chunks of a guided schedule are at least a quarter of
+// a chunk of 4096 tokens or more).
+static inline int32_t fused_hcap(int max_seq_len) {
+  return (max_seq_len > 0 ? max_seq_len : 1) / FE_CH_MIN + 8;
+}
 
 static inline FusedWs fused_ws(void* base, int rows, int max_seq_len) {
   char* p = static_cast<char*>(base);
   FusedWs w;
-  w.hist = reinterpret_cast<uint32_t*>(p);
-  p += align256(static_cast<size_t>(rows) * HIST_BINS * 4);
-  w.ctr = reinterpret_cast<uint32_t*>(p);
-  p += align256(static_cast<size_t>(rows) * 16);
-  w.cand = reinterpret_cast<uint64_t*>(p);
   w.cap = max_seq_len > 0 ? max_seq_len : 1;
+  w.hcap = fused_hcap(max_seq_len);
+  w.cand = reinterpret_cast<uint64_t*>(p);
   p += align256(static_cast<size_t>(rows) * w.cap * 8);
+  w.hdr = reinterpret_cast<uint2*>(p);
+  p += align256(static_cast<size_t>(rows) * w.hcap * 8);
   w.sval = reinterpret_cast<float*>(p);
   return w;
 }
 
 size_t fused_workspace_bytes(int rows, int k, int max_seq_len) {
   const int64_t cap = max_seq_len > 0 ? max_seq_len : 1;
-  return align256(static_cast<size_t>(rows) * HIST_BINS * 4) + align256(static_cast<size_t>(rows) * 16) +
-         align256(static_cast<size_t>(rows) * cap * 8) + align256(static_cast<size_t>(rows) * k * 4);
+  return align256(static_cast<size_t>(rows) * cap * 8) +
+         align256(static_cast<size_t>(rows) * fused_hcap(max_seq_len) * 8) +
+         align256(static_cast<size_t>(rows) * k * 4);
 }
 
+// Block top-k: bscore[r][c] is the value key of block c's maximum for
+// selection r. The chunks covering a row write every block entry the merge
+// reads, so the area needs no initial contents.
 struct BlockWs {
-  uint32_t* bscore;  // [rows][nblk_max] value keys of the block maxima
-  uint32_t* ctr;     // [rows][4]: done chunks
+  uint32_t* bscore;  // [rows][nblk_max]
   int64_t nblk_max;
 };
 
-static inline BlockWs block_ws(void* base, int rows, int block_size, int max_seq_len) {
-  char* p = static_cast<char*>(base);
+static inline BlockWs block_ws(void* base, int block_size, int max_seq_len) {
   BlockWs w;
   w.nblk_max = max_seq_len > 0 ? (max_seq_len + block_size - 1) / block_size : 1;
-  w.bscore = reinterpret_cast<uint32_t*>(p);
-  p += align256(static_cast<size_t>(rows) * w.nblk_max * 4);
-  w.ctr = reinterpret_cast<uint32_t*>(p);
+  w.bscore = static_cast<uint32_t*>(base);
   return w;
 }
 
 size_t block_workspace_bytes(int rows, int block_size, int max_seq_len) {
   const int64_t nblk = max_seq_len > 0 ? (max_seq_len + block_size - 1) / block_size : 1;
-  return align256(static_cast<size_t>(rows) * nblk * 4) + align256(static_cast<size_t>(rows) * 16);
+  return align256(static_cast<size_t>(rows) * nblk * 4);
 }
 
 // Workgroup -> (row b, chunk c), chunk-major. Workgroups are dealt to the
@@ -344,18 +356,27 @@ __global__ __launch_bounds__(PR_WG) void pair_score_kernel(IndexerArgs a, float*
 // Fused decode score + top-k: chunk kernel, then per-row merge kernel
 // ---------------------------------------------------------------------------
 
-constexpr int MG_WG = 512;                      // merge workgroup
-constexpr int MG_BUF = 6144;                    // threshold-bin entries held in LDS (48 KB)
-constexpr int MG_MAXE = MG_BUF / MG_WG;
+constexpr int MG_WG = 512;        // block merge workgroup
+constexpr int FM_WG = 1024;       // fused merge workgroup
+constexpr int MG_BUF = 8192;      // candidates of a row gathered in LDS (64 KB)
+constexpr int MG_MID = HIST_BINS / 2;  // threshold-bin keys held in LDS (over the histogram)
+constexpr int MG_MAXE = MG_MID / FM_WG;
+constexpr int MG_CHUNKS = 1024;   // chunk headers of a row held in LDS
+constexpr int MG_BATCH = 8;       // candidates per thread per pass of the merge
+constexpr int WS_PER = 16;        // threshold-bin keys per lane when one wave selects
 
 static_assert(HIST_BINS == 16 * IX_WG, "16 histogram bins per thread");
+constexpr int MG_HPER = HIST_BINS / FM_WG;  // histogram bins per merge thread
+static_assert(MG_HPER % 4 == 0, "whole 16-byte histogram reads");
 
-// The 16 counts of bins [16 t, 16 t + 16) of an LDS histogram, for thread t
-// (four 16-byte reads).
-__device__ __forceinline__ void own_bins16(const uint32_t* hist, uint32_t (&c)[16]) {
-  const uint4* p = reinterpret_cast<const uint4*>(hist) + threadIdx.x * 4;
+// The PER counts of bins [PER t, PER t + PER) of an LDS histogram, for
+// thread t (16-byte reads).
+template <int PER>
+__device__ __forceinline__ void own_bins(const uint32_t* hist, uint32_t (&c)[PER]) {
+  static_assert(PER % 4 == 0, "whole 16-byte reads");
+  const uint4* p = reinterpret_cast<const uint4*>(hist) + threadIdx.x * (PER / 4);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < PER / 4; ++j) {
     const uint4 v = p[j];
     c[4 * j + 0] = v.x;
     c[4 * j + 1] = v.y;
@@ -375,7 +396,6 @@ struct ChunkLds {
   uint32_t scratch[16];
   uint32_t lcnt;
   uint32_t lcnt2;
-  uint32_t gbase;
 };
 
 struct FusedOut {
@@ -385,7 +405,24 @@ struct FusedOut {
   int keep_positions;  // leave row-local positions in `slots` (the sort pass maps them)
 };
 
-// Dynamic LDS: the chunk's scores (a.chunk floats).
+// How many of its own best tokens a chunk sends to the merge: of the row's n
+// tokens, the chunk holds cnt, so on average mu = k * cnt / n of the row's k
+// best (fewer than that when the chunk is a random part of the row: the
+// count is binomial, its standard deviation below sqrt(mu)). Sending mu +
+// 6 sqrt(mu) + 16 leaves a margin of more than six standard deviations; a
+// row whose best tokens crowd into some chunks beyond that is caught by the
+// merge's check and scored again there. When the rank reaches cnt (always
+// when n <= k) the chunk sends every token.
+__device__ __forceinline__ uint32_t chunk_rank(int k, int cnt, int n) {
+  const float mu = static_cast<float>(k) * static_cast<float>(cnt) / static_cast<float>(n);
+  const float r = mu + 6.0f * sqrtf(mu) + 16.0f;
+  return r >= static_cast<float>(cnt) ? static_cast<uint32_t>(cnt) + 1u : static_cast<uint32_t>(r);
+}
+
+// One workgroup per (row, chunk). Dynamic LDS: the chunk's scores (a.chunk
+// floats). Nothing here waits on another workgroup: the chunk's bound comes
+// from its own histogram, its candidates go to its own tokens' range of the
+// row's candidate area, its count and bound to its own header.
 template <int NT, bool BF = false>
 __global__ __launch_bounds__(IX_WG) void fused_chunk_kernel(IndexerArgs a, FusedWs ws, int k) {
   extern __shared__ float sc[];
@@ -399,67 +436,39 @@ __global__ __launch_bounds__(IX_WG) void fused_chunk_kernel(IndexerArgs a, Fused
   if (tb >= n) return;
   const int te = min(n, tb + clen);
   const int cnt = te - tb;
-  uint32_t* Hg = ws.hist + static_cast<int64_t>(b) * HIST_BINS;
-  uint32_t* ctr = ws.ctr + static_cast<int64_t>(b) * 4;
-  uint64_t* cand = ws.cand + static_cast<int64_t>(b) * ws.cap;
+  uint64_t* cand = ws.cand + static_cast<int64_t>(b) * ws.cap + tb;
 
   for (int i = tid; i < HIST_BINS; i += IX_WG) s.hist[i] = 0;
   if (tid == 0) {
     s.lcnt = 0;
     s.lcnt2 = 0;
   }
-  // (score_chunk synchronises before its first emit)
-  score_chunk_any<BF, NT, IX_WG, IX_RING, true>(a, b, tb, te, s.pages, [&](int j, float v, bool valid) {
+  // (score_chunk synchronises before its first emit). A bf16 cache is read
+  // with ordinary loads for large batches (the second half of each line then
+  // comes from the cache) and nontemporal ones for decode batches.
+  auto emit = [&](int j, float v, bool valid) {
     if (valid) {
       sc[j - tb] = v;
       atomicAdd(&s.hist[float_key(v) >> HIST_SHIFT], 1u);
     }
-  });
+  };
+  if (a.cached_keys)
+    score_chunk_any<BF, NT, IX_WG, IX_RING, true>(a, b, tb, te, s.pages, emit);
+  else
+    score_chunk_any<BF, NT, IX_WG, IX_RING, false>(a, b, tb, te, s.pages, emit);
   __syncthreads();
 
-  // 1. The chunk's own threshold bin: the row holds these tokens, so the
-  //    row's threshold bin is at least this one, and counts of lower bins
-  //    can never decide it.
+  // The chunk's bound: the highest bin whose count from the top reaches
+  // chunk_rank (bin 0, every token, when the chunk holds fewer).
   uint32_t c16[16];
-  own_bins16(s.hist, c16);
-  const BinThreshold own = wg_threshold_counts<IX_WG, 16>(c16, static_cast<uint32_t>(k), s.scratch);
-  const uint32_t lo_bin = own.all ? 0u : own.bin;
-  // 2. Publish the counts of bins >= lo_bin to the row's histogram, then read
-  //    the row's counts back (coalesced: bin i * IX_WG + tid; all loads issued
-  //    before any is used; bins below lo_bin re-read lo_bin's counter).
-  uint32_t g16[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t bin = i * IX_WG + tid;
-    const uint32_t h = s.hist[bin];
-    if (h && bin >= lo_bin) add_dev(&Hg[bin], h);
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t bin = i * IX_WG + tid;
-    g16[i] = ld_acquire_dev(&Hg[bin >= lo_bin ? bin : lo_bin]);
-  }
-  // 3. Bound the row's k-th score with what the row's histogram holds so far.
-  //    Per bin, max(row count seen, own count) never exceeds the number of
-  //    real tokens in that bin, so the threshold bin of these counts is a
-  //    valid lower bound whatever has become visible; bins below lo_bin
-  //    cannot hold it. (Each thread rewrites only the bins it read.)
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t bin = i * IX_WG + tid;
-    const uint32_t l = s.hist[bin];
-    s.hist[bin] = bin >= lo_bin ? (g16[i] > l ? g16[i] : l) : 0u;
-  }
-  __syncthreads();
-  own_bins16(s.hist, c16);
-  const BinThreshold bound = wg_threshold_counts<IX_WG, 16>(c16, static_cast<uint32_t>(k), s.scratch);
-  const uint32_t bin_g = bound.all ? 0u : bound.bin;
+  own_bins<16>(s.hist, c16);
+  const BinThreshold own = wg_threshold_counts<IX_WG, 16>(c16, chunk_rank(k, cnt, n), s.scratch);
+  const uint32_t bin_c = own.all ? 0u : own.bin;
 
-  // 4. Emit this chunk's candidates (bin >= bound) to the row's list: staged
-  //    in LDS (over the histogram, which is no longer read) with one slot
-  //    reservation per wave per batch, then one global reservation and a
-  //    coalesced copy. If more than FU_STAGE pass, a second pass writes them
-  //    straight to the list instead.
+  // Every token in bins >= bin_c, as unique keys: staged in LDS (over the
+  // histogram, no longer read) with one slot reservation per wave per batch,
+  // then copied out coalesced. If more than FU_STAGE pass, a second pass
+  // writes them straight out instead.
   constexpr int EB = 8;
   for (int i0 = 0; i0 < cnt; i0 += EB * IX_WG) {
     uint32_t key[EB];
@@ -469,7 +478,7 @@ __global__ __launch_bounds__(IX_WG) void fused_chunk_kernel(IndexerArgs a, Fused
     for (int j = 0; j < EB; ++j) {
       const int i = i0 + j * IX_WG + tid;
       key[j] = float_key(sc[i < cnt ? i : 0]);
-      keep[j] = i < cnt && (key[j] >> HIST_SHIFT) >= bin_g;
+      keep[j] = i < cnt && (key[j] >> HIST_SHIFT) >= bin_c;
       mine += keep[j];
     }
     uint32_t at = wave_reserve(mine, &s.lcnt);
@@ -483,11 +492,8 @@ __global__ __launch_bounds__(IX_WG) void fused_chunk_kernel(IndexerArgs a, Fused
   }
   __syncthreads();
   const uint32_t m = s.lcnt;
-  if (tid == 0) s.gbase = m ? add_dev(&ctr[0], m) : 0u;
-  __syncthreads();
-  const uint32_t gbase = s.gbase;
   if (m <= FU_STAGE) {
-    for (uint32_t i = tid; i < m; i += IX_WG) cand[gbase + i] = s.stage[i];
+    for (uint32_t i = tid; i < m; i += IX_WG) cand[i] = s.stage[i];
   } else {
     for (int i0 = 0; i0 < cnt; i0 += EB * IX_WG) {
       uint32_t key[EB];
@@ -497,32 +503,46 @@ __global__ __launch_bounds__(IX_WG) void fused_chunk_kernel(IndexerArgs a, Fused
       for (int j = 0; j < EB; ++j) {
         const int i = i0 + j * IX_WG + tid;
         key[j] = float_key(sc[i < cnt ? i : 0]);
-        keep[j] = i < cnt && (key[j] >> HIST_SHIFT) >= bin_g;
+        keep[j] = i < cnt && (key[j] >> HIST_SHIFT) >= bin_c;
         mine += keep[j];
       }
-      uint32_t at = gbase + wave_reserve(mine, &s.lcnt2);
+      uint32_t at = wave_reserve(mine, &s.lcnt2);
 #pragma unroll
       for (int j = 0; j < EB; ++j)
         if (keep[j]) cand[at++] = rank_key(key[j], static_cast<uint32_t>(tb + i0 + j * IX_WG + tid));
     }
   }
+  if (tid == 0) ws.hdr[static_cast<int64_t>(b) * ws.hcap + c] = make_uint2(m, bin_c);
 }
 
+constexpr int MG_SPEC = MG_BUF / FM_WG;  // candidate loads per thread issued with the headers
+constexpr int MG_PAGES = 8192;           // block-table entries of a row staged in LDS
+constexpr int MG_PG_PER = MG_PAGES / FM_WG;
+
 struct MergeLds {
-  uint64_t buf[MG_BUF];
+  uint64_t buf[MG_BUF];  // the row's candidates (or, rescoring, the staged pages)
+  union {
+    alignas(16) uint32_t hist[HIST_BINS];  // histogram of the candidates' bins
+    uint64_t mid[MG_MID];                  // then the threshold bin's keys
+  };
+  int32_t pages[MG_PAGES];       // the row's block-table entries (rows of at most MG_PAGES pages)
+  uint32_t coff[MG_CHUNKS + 1];  // first candidate of each chunk in the gathered order
+  uint32_t ctb[MG_CHUNKS];       // first token of each chunk
+  uint32_t ccnt[MG_CHUNKS];      // candidates of each chunk
   SelectLds sel;
   uint32_t scratch[24];
   uint32_t ocnt;
-  uint32_t bcnt;
+  uint32_t mcnt;
+  uint32_t fcnt;
+  uint32_t maxbin;
 };
 
 // Emit this thread's keys with keep[e] set: one output reservation per
-// wave, then each key's row-local position (and score) is stored. The merge
-// turns positions into slots in one pass at the end (positions_to_slots).
-// All lanes of the wave must call.
-template <int N>
+// wave, then out_of(position) (its slot, or the position itself) and the
+// score are stored. All lanes of the wave must call.
+template <int N, class OutOf>
 __device__ __forceinline__ void emit_batch(const uint64_t (&keys)[N], const bool (&keep)[N], int b,
-                                           const FusedOut& o, uint32_t* ocnt) {
+                                           const FusedOut& o, uint32_t* ocnt, OutOf&& out_of) {
   uint32_t mine = 0;
 #pragma unroll
   for (int e = 0; e < N; ++e) mine += keep[e];
@@ -532,7 +552,7 @@ __device__ __forceinline__ void emit_batch(const uint64_t (&keys)[N], const bool
   for (int e = 0; e < N; ++e) {
     if (keep[e]) {
       if (at < static_cast<uint32_t>(o.k)) {
-        o.slots[row + at] = static_cast<int32_t>(rank_pos(keys[e]));
+        o.slots[row + at] = out_of(rank_pos(keys[e]));
         if (o.scores) o.scores[row + at] = key_float(rank_vkey(keys[e]));
       }
       ++at;
@@ -578,60 +598,332 @@ __device__ __forceinline__ void positions_to_slots(const IndexerArgs& a, int b, 
   }
 }
 
-constexpr int MG_BATCH = 8;  // candidates per thread per pass of the merge
-constexpr int WS_PER = 16;   // threshold-bin keys per lane when one wave selects
+// Workgroup-wide exclusive prefix sum of one value per thread (every thread
+// must call); `scratch` holds at least WG/64 words. Returns the thread's
+// offset, and the total in `total`.
+template <int WG>
+__device__ __forceinline__ uint32_t wg_exclusive_sum(uint32_t x, uint32_t* scratch, uint32_t& total) {
+  constexpr int NW = WG / kWave;
+  const int wave = threadIdx.x / kWave;
+  const uint32_t incl = wave_prefix_incl(x);
+  if (lane_id() == kWave - 1) scratch[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t t = scratch[w];
+    before += w < wave ? t : 0u;
+    total += t;
+  }
+  __syncthreads();
+  return before + incl - x;
+}
 
-// One workgroup per row. The row's histogram is complete now (previous
-// kernel), so it names the exact threshold bin: candidates above it are
-// selected outright, candidates inside it go through an exact radix select
-// for the remaining count. Then every workspace byte the row used is zeroed.
-__global__ __launch_bounds__(MG_WG) void fused_merge_kernel(IndexerArgs a, FusedWs ws, FusedOut o) {
+// Where the merge reads the row's candidates: gathered in LDS, in the
+// chunks' ranges of the row's candidate area (too many to gather), or,
+// after rescoring, packed at the start of that area.
+struct CandSource {
+  const uint64_t* lds;      // gathered (or null)
+  const uint64_t* list;     // packed list in the workspace (or null)
+  const uint64_t* regions;  // the row's candidate area, chunk ranges
+  const uint32_t* coff;     // chunk offsets in the gathered order (LDS)
+  const uint32_t* ctb;      // chunk first tokens (LDS)
+  int nch;
+  __device__ __forceinline__ uint64_t at(uint32_t i) const {
+    if (lds) return lds[i];
+    if (list) return list[i];
+    // the chunk holding flat index i: the last c with coff[c] <= i
+    int lo = 0, hi = nch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (coff[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    return regions[ctb[lo] + (i - coff[lo])];
+  }
+};
+
+// Number of chunks of the schedule whose first token lies below n
+// (chunk_span grows with the chunk index).
+__device__ __forceinline__ int chunks_below(const IndexerArgs& a, int n) {
+  if (n <= 0) return 0;
+  int c;
+  if (n <= a.tok_half) {
+    c = (n + a.chunk - 1) / a.chunk;
+  } else if (n <= a.tok_quarter) {
+    const int h = a.chunk / 2;
+    c = a.n_full + (n - a.tok_half + h - 1) / h;
+  } else {
+    const int q = a.chunk / 4;
+    c = a.n_full + a.n_half + (n - a.tok_quarter + q - 1) / q;
+  }
+  return c < a.nchunk_max ? c : a.nchunk_max;
+}
+
+// One workgroup per row (see the section comment above). Leaves nothing in
+// the workspace that a later call depends on.
+template <int NT, bool BF = false>
+__global__ __launch_bounds__(FM_WG) void fused_merge_kernel(IndexerArgs a, FusedWs ws, FusedOut o) {
   __shared__ MergeLds s;
   const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = lane_id();
   const int b = blockIdx.x;
   const int n = a.seq_lens[b];
   const uint32_t k = static_cast<uint32_t>(o.k);
-  uint32_t* Hg = ws.hist + static_cast<int64_t>(b) * HIST_BINS;
-  uint32_t* ctr = ws.ctr + static_cast<int64_t>(b) * 4;
+  const uint32_t P = static_cast<uint32_t>(a.page_size);
   uint64_t* cand = ws.cand + static_cast<int64_t>(b) * ws.cap;
-  const uint32_t ncand = n > 0 ? ctr[0] : 0u;
+  const uint2* hdr = ws.hdr + static_cast<int64_t>(b) * ws.hcap;
+  const int32_t* bt_row = bt_row_of(a, b);
+  const int nch = chunks_below(a, n);
+  const bool staged = n > 0 && nch <= MG_CHUNKS;
+  const int npages = n > 0 ? static_cast<int>(fdiv(static_cast<uint32_t>(n - 1), a.pdiv)) + 1 : 0;
+  const bool pages_staged = !o.keep_positions && npages <= MG_PAGES;
 
-  wg_select_init<MG_WG>(s.sel);
+  wg_select_init<FM_WG>(s.sel);
+  for (int i = tid; i < HIST_BINS; i += FM_WG) s.hist[i] = 0;
   if (tid == 0) {
     s.ocnt = 0;
-    s.bcnt = 0;
+    s.mcnt = 0;
+    s.fcnt = 0;
+    s.maxbin = 0;
   }
-  const BinThreshold th = wg_threshold_bin<MG_WG, HIST_BINS>([&](int i) { return Hg[i]; }, k, s.scratch);
+
+  // In flight together: the chunk headers, the first `spec` candidates of
+  // every chunk (MG_BUF spread evenly over the row's chunks; most chunks send
+  // fewer), and the row's block table.
+  constexpr int PC = MG_CHUNKS / FM_WG;
+  uint2 h[PC];
+  const int spec = staged ? MG_BUF / nch : 1;
+  const float rspec = 1.0f / static_cast<float>(spec);
+  // flat index f -> (chunk c, entry j): a float estimate of f / spec (f <
+  // 2^13), corrected by one step
+  auto split = [&](int f, int& c, int& j) {
+    c = static_cast<int>(static_cast<float>(f) * rspec);
+    c -= c * spec > f;
+    c += (c + 1) * spec <= f;
+    j = f - c * spec;
+  };
+  uint64_t sk[MG_SPEC];
+  int32_t pg[MG_PG_PER];
+  if (staged) {
+#pragma unroll
+    for (int e = 0; e < PC; ++e) {
+      const int c = tid * PC + e;
+      h[e] = c < nch ? hdr[c] : make_uint2(0u, 0u);
+    }
+#pragma unroll
+    for (int e = 0; e < MG_SPEC; ++e) {
+      int c, j;
+      split(e * FM_WG + tid, c, j);
+      int tb, clen;
+      chunk_span(a, c < nch ? c : 0, tb, clen);
+      // within the chunk's own tokens, so inside the row's area
+      sk[e] = c < nch && j < clen && tb + j < n ? cand[tb + j] : 0ull;
+    }
+  }
+  if (pages_staged) {
+#pragma unroll
+    for (int r = 0; r < MG_PG_PER; ++r) {
+      const int i = r * FM_WG + tid;
+      pg[r] = i < npages ? bt_row[i] : 0;
+    }
+  }
+
+  // Chunk counts prefix-summed into coff; the highest chunk bound.
+  uint32_t total = 0;
+  if (staged) {
+    uint32_t sum = 0, mx = 0;
+#pragma unroll
+    for (int e = 0; e < PC; ++e) {
+      sum += h[e].x;
+      mx = h[e].y > mx ? h[e].y : mx;
+    }
+    uint32_t off = wg_exclusive_sum<FM_WG>(sum, s.scratch, total);
+#pragma unroll
+    for (int e = 0; e < PC; ++e) {
+      const int c = tid * PC + e;
+      if (c < nch) {
+        int tb, clen;
+        chunk_span(a, c, tb, clen);
+        s.coff[c] = off;
+        s.ctb[c] = static_cast<uint32_t>(tb);
+        s.ccnt[c] = h[e].x;
+      }
+      off += h[e].x;
+    }
+    if (tid == 0) s.coff[nch] = total;
+    mx = wave_max_u32(mx);
+    if (lane == 0) atomicMax(&s.maxbin, mx);
+  }
+  __syncthreads();
+  const bool gathered = staged && total <= static_cast<uint32_t>(MG_BUF);
+  // Place the loaded candidates: into LDS when they all fit, else into the
+  // histogram (of the candidates' bins); then load what the first loads did
+  // not cover (chunks that sent more than `spec`), one wave per chunk.
+  if (staged) {
+#pragma unroll
+    for (int e = 0; e < MG_SPEC; ++e) {
+      int c, j;
+      split(e * FM_WG + tid, c, j);
+      if (c < nch && static_cast<uint32_t>(j) < s.ccnt[c]) {
+        if (gathered) s.buf[s.coff[c] + j] = sk[e];
+        else atomicAdd(&s.hist[rank_vkey(sk[e]) >> HIST_SHIFT], 1u);
+      }
+    }
+    for (int c = wave; c < nch; c += FM_WG / kWave) {
+      const uint32_t cnt = s.ccnt[c];
+      if (cnt <= static_cast<uint32_t>(spec)) continue;
+      const uint32_t tb = s.ctb[c], off = s.coff[c];
+      for (uint32_t j = spec + lane; j < cnt; j += kWave) {
+        const uint64_t key = cand[tb + j];
+        if (gathered) s.buf[off + j] = key;
+        else atomicAdd(&s.hist[rank_vkey(key) >> HIST_SHIFT], 1u);
+      }
+    }
+  }
+  if (pages_staged) {
+#pragma unroll
+    for (int r = 0; r < MG_PG_PER; ++r) {
+      const int i = r * FM_WG + tid;
+      if (i < npages) s.pages[i] = pg[r];
+    }
+  }
+  __syncthreads();
+
+  // Output of a selected position: its slot when the row's block table is
+  // staged in LDS; otherwise the position itself (for the sort pass, or for
+  // positions_to_slots below, which batches the block-table lookups).
+  auto out_of = [&](uint32_t pos) -> int32_t {
+    if (!pages_staged) return static_cast<int32_t>(pos);
+    const uint32_t lp = fdiv(pos, a.pdiv);
+    uint32_t x = (static_cast<uint32_t>(s.pages[lp]) - lp) * P;
+    asm volatile("" : "+v"(x));  // a 64-bit mad here would wait on loads in flight
+    return static_cast<int32_t>(x + pos);
+  };
+
+  // Candidates in LDS: the exact k-th key T among them by an adaptive
+  // radix select (bins spread over the candidates' own range). The selection
+  // is the row's when T's bin is at or above every chunk's bound (each chunk
+  // sent all of its tokens in bins >= its bound, so every token >= T is a
+  // candidate), or, with at most k candidates, when every token was sent.
+  bool done = false;      // selected and emitted from LDS
+  uint32_t lo_bin = 0u;   // rescoring keeps the tokens in bins >= lo_bin
+  if (gathered) {
+    uint64_t T = 0;
+    bool ok;
+    if (total > k) {
+      uint64_t mn = ~0ull, mx = 0;
+      lds_for_each<FM_WG, 4>(s.buf, total, [&](uint64_t x) {
+        mn = x < mn ? x : mn;
+        mx = x > mx ? x : mx;
+      });
+      wg_range<FM_WG>(mn, mx, s.sel);
+      T = wg_select<FM_WG>([&](auto&& f) { lds_for_each<FM_WG, 4>(s.buf, total, f); }, k, mn, mx, s.sel);
+      ok = (rank_vkey(T) >> HIST_SHIFT) >= s.maxbin;
+      lo_bin = rank_vkey(T) >> HIST_SHIFT;  // T is at or below the row's k-th best key
+    } else {
+      ok = total == static_cast<uint32_t>(n);
+    }
+    if (ok) {
+      for (uint32_t i0 = 0; i0 < total; i0 += FM_WG * MG_BATCH) {
+        uint64_t key[MG_BATCH];
+        bool keep[MG_BATCH];
+#pragma unroll
+        for (int j = 0; j < MG_BATCH; ++j) {
+          const uint32_t i = i0 + j * FM_WG + tid;
+          key[j] = i < total ? s.buf[i] : 0ull;
+          keep[j] = i < total && key[j] >= T;
+        }
+        emit_batch<MG_BATCH>(key, keep, b, o, &s.ocnt, out_of);
+      }
+      done = true;
+    }
+  }
+  CandSource src{nullptr, nullptr, cand, s.coff, s.ctb, nch};
+  uint32_t ncand = total;
+  BinThreshold th{0u, 0u, 0u, true};
+  if (!done) {
+    bool ok = false;
+    if (staged && !gathered) {
+      // too many candidates for LDS: threshold bin from their histogram
+      uint32_t h8[MG_HPER];
+      own_bins<MG_HPER>(s.hist, h8);
+      th = wg_threshold_counts<FM_WG, MG_HPER>(h8, k, s.scratch);
+      ok = th.all ? total == static_cast<uint32_t>(n) : th.bin >= s.maxbin;
+      lo_bin = th.all ? 0u : th.bin;
+    }
+    if (!ok && n > 0) {
+      // Score the row again and keep every token in bins >= lo_bin: the
+      // candidates' k-th best key is at or below the row's k-th best, so no
+      // token of the row's top k is dropped.
+      __syncthreads();
+      for (int i = tid; i < HIST_BINS; i += FM_WG) s.hist[i] = 0;
+      if (tid == 0) s.fcnt = 0;
+      int32_t* spages = reinterpret_cast<int32_t*>(s.buf);
+      const int64_t span64 = (static_cast<int64_t>(IX_PAGES - 2) * a.page_size) / kGroup * kGroup;
+      const int span = static_cast<int>(span64 > kGroup ? span64 : kGroup);
+      for (int t0 = 0; t0 < n; t0 += span) {
+        const int t1 = min(n, t0 + span);
+        score_chunk_any<BF, NT, FM_WG, 1, true>(a, b, t0, t1, spages, [&](int j, float v, bool valid) {
+          const uint32_t key = float_key(v);
+          const bool keep = valid && (key >> HIST_SHIFT) >= lo_bin;
+          const uint64_t mk = ballot(keep);
+          if (mk) {
+            uint32_t base = 0;
+            if (lane_id() == 0) base = atomicAdd(&s.fcnt, static_cast<uint32_t>(__popcll(mk)));
+            base = uniform(base);
+            if (keep) {
+              cand[base + lanes_below(mk)] = rank_key(key, static_cast<uint32_t>(j));
+              atomicAdd(&s.hist[key >> HIST_SHIFT], 1u);
+            }
+          }
+        });
+        __syncthreads();  // the staged pages are replaced by the next span's
+      }
+      ncand = s.fcnt;
+      src = CandSource{nullptr, cand, cand, s.coff, s.ctb, 0};
+      uint32_t h8[MG_HPER];
+      own_bins<MG_HPER>(s.hist, h8);
+      th = wg_threshold_counts<FM_WG, MG_HPER>(h8, k, s.scratch);
+    }
+  }
   const uint32_t bstar = th.all ? 0u : th.bin;
   const uint32_t need = th.all ? 0u : k - th.above;
-  // Pass over the candidates: keys above the threshold bin (or all keys when
-  // the row holds fewer than k) are emitted, keys inside it go to LDS.
-  for (uint32_t i0 = 0; i0 < ncand; i0 += MG_WG * MG_BATCH) {
+  if (done) ncand = 0;  // nothing left to classify
+
+  // Classify: keys above the threshold bin (all keys when the row holds at
+  // most k) are emitted, keys inside it go to LDS (over the histogram).
+  for (uint32_t i0 = 0; i0 < ncand; i0 += FM_WG * MG_BATCH) {
     uint64_t key[MG_BATCH];
     bool keep[MG_BATCH], mid[MG_BATCH];
     uint32_t nmid = 0;
 #pragma unroll
     for (int j = 0; j < MG_BATCH; ++j) {
-      const uint32_t i = i0 + j * MG_WG + tid;
-      const bool valid = i < ncand;
-      key[j] = valid ? cand[i] : 0ull;
+      const uint32_t i = i0 + j * FM_WG + tid;
+      key[j] = i < ncand ? src.at(i) : 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < MG_BATCH; ++j) {
+      const bool valid = i0 + j * FM_WG + tid < ncand;
       const uint32_t bin = rank_vkey(key[j]) >> HIST_SHIFT;
       keep[j] = valid && (th.all || bin > bstar);
       mid[j] = valid && !th.all && bin == bstar;
       nmid += mid[j];
     }
-    emit_batch<MG_BATCH>(key, keep, b, o, &s.ocnt);
-    uint32_t at = wave_reserve(nmid, &s.bcnt);
+    emit_batch<MG_BATCH>(key, keep, b, o, &s.ocnt, out_of);
+    uint32_t at = wave_reserve(nmid, &s.mcnt);
 #pragma unroll
     for (int j = 0; j < MG_BATCH; ++j) {
       if (mid[j]) {
-        if (at < static_cast<uint32_t>(MG_BUF)) s.buf[at] = key[j];
+        if (at < static_cast<uint32_t>(MG_MID)) s.mid[at] = key[j];
         ++at;
       }
     }
   }
   __syncthreads();
-  const uint32_t nb = s.bcnt;
+  const uint32_t nb = s.mcnt;
   if (!th.all && nb > 0 && nb <= static_cast<uint32_t>(kWave * WS_PER)) {
     // a small threshold bin: wave 0 alone selects and emits it
     if (tid < kWave) {
@@ -641,23 +933,23 @@ __global__ __launch_bounds__(MG_WG) void fused_merge_kernel(IndexerArgs a, Fused
       for (int e = 0; e < WS_PER; ++e) {
         const uint32_t i = e * kWave + tid;
         valid[e] = i < nb;
-        keys[e] = valid[e] ? s.buf[i] : 0ull;
+        keys[e] = valid[e] ? s.mid[i] : 0ull;
       }
       const uint64_t T = nb > need ? wave_select<WS_PER>(keys, valid, need, s.sel.hist) : 0ull;
 #pragma unroll
       for (int e = 0; e < WS_PER; ++e) keep[e] = valid[e] && keys[e] >= T;
-      emit_batch<WS_PER>(keys, keep, b, o, &s.ocnt);
+      emit_batch<WS_PER>(keys, keep, b, o, &s.ocnt, out_of);
     }
   } else if (!th.all && nb > 0) {
-    if (nb <= static_cast<uint32_t>(MG_BUF)) {
+    if (nb <= static_cast<uint32_t>(MG_MID)) {
       uint64_t keys[MG_MAXE];
       int nvk = 0;
 #pragma unroll
       for (int e = 0; e < MG_MAXE; ++e) {
-        const uint32_t i = tid + e * MG_WG;
+        const uint32_t i = tid + e * FM_WG;
         keys[e] = 0;
         if (i < nb) {
-          keys[e] = s.buf[i];
+          keys[e] = s.mid[i];
           nvk = e + 1;
         }
       }
@@ -670,8 +962,8 @@ __global__ __launch_bounds__(MG_WG) void fused_merge_kernel(IndexerArgs a, Fused
             mn = keys[e] < mn ? keys[e] : mn;
             mx = keys[e] > mx ? keys[e] : mx;
           }
-        wg_range<MG_WG>(mn, mx, s.sel);
-        T = wg_select<MG_WG>(
+        wg_range<FM_WG>(mn, mx, s.sel);
+        T = wg_select<FM_WG>(
             [&](auto&& f) {
 #pragma unroll
               for (int e = 0; e < MG_MAXE; ++e)
@@ -682,13 +974,13 @@ __global__ __launch_bounds__(MG_WG) void fused_merge_kernel(IndexerArgs a, Fused
       bool keep[MG_MAXE];
 #pragma unroll
       for (int e = 0; e < MG_MAXE; ++e) keep[e] = e < nvk && keys[e] >= T;
-      emit_batch<MG_MAXE>(keys, keep, b, o, &s.ocnt);
+      emit_batch<MG_MAXE>(keys, keep, b, o, &s.ocnt, out_of);
     } else {
-      // threshold bin larger than the LDS buffer: select straight from the
-      // candidate list (several passes over it)
+      // threshold bin larger than its LDS area: select straight from the
+      // candidates (several passes over them)
       auto each_mid = [&](auto&& f) {
-        for (uint32_t i = tid; i < ncand; i += MG_WG) {
-          const uint64_t key = cand[i];
+        for (uint32_t i = tid; i < ncand; i += FM_WG) {
+          const uint64_t key = src.at(i);
           if ((rank_vkey(key) >> HIST_SHIFT) == bstar) f(key);
         }
       };
@@ -697,344 +989,29 @@ __global__ __launch_bounds__(MG_WG) void fused_merge_kernel(IndexerArgs a, Fused
         mn = key < mn ? key : mn;
         mx = key > mx ? key : mx;
       });
-      wg_range<MG_WG>(mn, mx, s.sel);
-      const uint64_t T = wg_select<MG_WG>(each_mid, need, mn, mx, s.sel);
-      for (uint32_t i0 = 0; i0 < ncand; i0 += MG_WG * MG_BATCH) {
+      wg_range<FM_WG>(mn, mx, s.sel);
+      const uint64_t T = wg_select<FM_WG>(each_mid, need, mn, mx, s.sel);
+      for (uint32_t i0 = 0; i0 < ncand; i0 += FM_WG * MG_BATCH) {
         uint64_t key[MG_BATCH];
         bool keep[MG_BATCH];
 #pragma unroll
         for (int j = 0; j < MG_BATCH; ++j) {
-          const uint32_t i = i0 + j * MG_WG + tid;
-          key[j] = i < ncand ? cand[i] : 0ull;
+          const uint32_t i = i0 + j * FM_WG + tid;
+          key[j] = i < ncand ? src.at(i) : 0ull;
           keep[j] = i < ncand && (rank_vkey(key[j]) >> HIST_SHIFT) == bstar && key[j] >= T;
         }
-        emit_batch<MG_BATCH>(key, keep, b, o, &s.ocnt);
+        emit_batch<MG_BATCH>(key, keep, b, o, &s.ocnt, out_of);
       }
     }
   }
   __syncthreads();
-  if (!o.keep_positions) {
-    const int32_t* bt_row = bt_row_of(a, b);
-    positions_to_slots<MG_WG, 8>(a, b, o, min(s.ocnt, k), [&](uint32_t pg) { return bt_row[pg]; });
-  }
+  if (!pages_staged && !o.keep_positions)
+    positions_to_slots<FM_WG, 8>(a, b, o, min(s.ocnt, k), [&](uint32_t lp) { return bt_row[lp]; });
   // padding for rows shorter than k
-  for (uint32_t i = min(s.ocnt, k) + tid; i < k; i += MG_WG) {
+  for (uint32_t i = min(s.ocnt, k) + tid; i < k; i += FM_WG) {
     o.slots[static_cast<int64_t>(b) * o.k + i] = -1;
     if (o.scores) o.scores[static_cast<int64_t>(b) * o.k + i] = -__builtin_inff();
   }
-  // leave every workspace byte of this row zero again (any later call, of any
-  // shape or op, may lay its counters over these bytes)
-  for (uint32_t i = tid; i < ncand; i += MG_WG) cand[i] = 0;
-  if (n > 0)
-    for (int i = tid; i < HIST_BINS; i += MG_WG) Hg[i] = 0;
-  if (tid == 0) ctr[0] = 0;
-}
-
-// ---------------------------------------------------------------------------
-// Fused decode, small batches: score buffer instead of candidates
-// ---------------------------------------------------------------------------
-//
-// When the batch holds few tokens (batch * max_seq_len <= FS_MAX_TOKENS) the
-// chunks are sized so that every chunk workgroup is resident at once, and a
-// chunk ends without waiting on anything: it writes its scores to the
-// workspace (the candidate area, as fp32 [rows][cap]) and adds its histogram
-// to the row's with fire-and-forget atomics. The per-chunk bound, the
-// read-back and the candidate reservation of the path above each cost a
-// dependent round trip that a short chunk cannot hide. One workgroup per row
-// then issues the histogram, the block table and its first scores together,
-// takes the exact threshold bin, emits the scores above it and selects
-// inside it. The extra bytes (scores written, read back and zeroed: 12 B per
-// token against 132 B of key and scale) stay in the last-level cache at
-// these sizes.
-
-constexpr int64_t FS_MAX_TOKENS = int64_t{1} << 21;
-constexpr int FS_CH_MAX = 4096;  // chunk tokens (dynamic LDS for the scores)
-constexpr int FS_CH_MIN = 256;
-constexpr int FS_RING = 4;       // key groups in flight per wave
-constexpr int FS_WG = 1024;      // merge workgroup
-constexpr int FS_PER = 8;        // scores per thread per pass of the merge
-constexpr int FS_BUF = 4096;     // threshold-bin keys held in LDS (32 KB)
-constexpr int FS_MAXE = FS_BUF / FS_WG;
-static_assert(FS_MAXE <= FS_PER, "slot lookups of one emission");
-constexpr int FS_PAGES = 4096;   // block-table entries staged in LDS
-constexpr int FS_PG_PER = FS_PAGES / FS_WG;
-
-__device__ __forceinline__ float* fused_scores_row(const FusedWs& w, int b) {
-  return reinterpret_cast<float*>(w.cand) + static_cast<int64_t>(b) * w.cap;
-}
-
-struct ScoresChunkLds {
-  alignas(16) uint32_t hist[HIST_BINS];
-  int32_t pages[IX_PAGES];
-};
-
-template <int NT, bool BF = false>
-__global__ __launch_bounds__(IX_WG) void fused_scores_chunk_kernel(IndexerArgs a, FusedWs ws) {
-  extern __shared__ float4 sc4[];
-  float* sc = reinterpret_cast<float*>(sc4);
-  __shared__ ScoresChunkLds s;
-  const int tid = threadIdx.x;
-  int b, c;
-  chunk_of(a, b, c);
-  const int n = a.seq_lens[b];
-  int tb, clen;
-  chunk_span(a, c, tb, clen);
-  if (tb >= n) return;
-  const int te = min(n, tb + clen);
-  const int cnt = te - tb;
-
-  for (int i = tid; i < HIST_BINS; i += IX_WG) s.hist[i] = 0;
-  // (score_chunk synchronises before its first emit)
-  score_chunk_any<BF, NT, IX_WG, FS_RING>(a, b, tb, te, s.pages, [&](int j, float v, bool valid) {
-    if (valid) {
-      sc[j - tb] = v;
-      atomicAdd(&s.hist[float_key(v) >> HIST_SHIFT], 1u);
-    }
-  });
-  __syncthreads();
-  // scores out, 16 bytes per lane where the row's base allows it
-  float* srow = fused_scores_row(ws, b) + tb;
-  if ((reinterpret_cast<uintptr_t>(srow) & 15u) == 0) {
-    for (int i = 4 * tid; i < cnt; i += 4 * IX_WG) {
-      if (i + 4 <= cnt) {
-        *reinterpret_cast<float4*>(srow + i) = sc4[i / 4];
-      } else {
-        for (int e = i; e < cnt; ++e) srow[e] = sc[e];
-      }
-    }
-  } else {
-    for (int i = tid; i < cnt; i += IX_WG) srow[i] = sc[i];
-  }
-  uint32_t* Hg = ws.hist + static_cast<int64_t>(b) * HIST_BINS;
-#pragma unroll
-  for (int i = 0; i < HIST_BINS / IX_WG; ++i) {
-    const int bin = i * IX_WG + tid;
-    const uint32_t h = s.hist[bin];
-    if (h) add_dev(&Hg[bin], h);
-  }
-}
-
-struct ScoresMergeLds {
-  uint64_t buf[FS_BUF];
-  int32_t pages[FS_PAGES];
-  SelectLds sel;
-  uint32_t scratch[24];
-  uint32_t ocnt;
-  uint32_t bcnt;
-};
-
-// One workgroup per row: exact top-k of the row's scores from its complete
-// histogram, then the row's scores and histogram are zeroed again. STAGED:
-// the row's block table fits in LDS (else slots are looked up in HBM).
-template <bool STAGED>
-__device__ __forceinline__ void fused_scores_merge_row(const IndexerArgs& a, const FusedWs& ws, const FusedOut& o,
-                                                       ScoresMergeLds& s, int b, int n, int npages) {
-  const int tid = threadIdx.x;
-  const uint32_t k = static_cast<uint32_t>(o.k);
-  const uint32_t P = static_cast<uint32_t>(a.page_size);
-  uint32_t* Hg = ws.hist + static_cast<int64_t>(b) * HIST_BINS;
-  float* srow = fused_scores_row(ws, b);
-  const int32_t* bt_row = bt_row_of(a, b);
-  const int64_t orow = static_cast<int64_t>(b) * o.k;
-
-  wg_select_init<FS_WG>(s.sel);
-  if (tid == 0) {
-    s.ocnt = 0;
-    s.bcnt = 0;
-  }
-  // In flight together: the first pass of scores, the block table, the
-  // histogram (indices past the row re-read entry 0, which exists).
-  float v0[FS_PER];
-#pragma unroll
-  for (int e = 0; e < FS_PER; ++e) {
-    const int i = e * FS_WG + tid;
-    v0[e] = srow[i < n ? i : 0];
-  }
-  if (STAGED && npages > 0) {
-    int32_t pg[FS_PG_PER];
-#pragma unroll
-    for (int r = 0; r < FS_PG_PER; ++r) {
-      const int i = r * FS_WG + tid;
-      pg[r] = bt_row[i < npages ? i : 0];
-    }
-#pragma unroll
-    for (int r = 0; r < FS_PG_PER; ++r)
-      if (r * FS_WG + tid < npages) s.pages[r * FS_WG + tid] = pg[r];
-  }
-  const BinThreshold th = wg_threshold_bin<FS_WG, HIST_BINS>([&](int i) { return Hg[i]; }, k, s.scratch);
-  const uint32_t bstar = th.all ? 0u : th.bin;
-  const uint32_t need = th.all ? 0u : k - th.above;
-
-  // Selected tokens are first written to the output row as positions (and
-  // scores); one coalesced pass at the end turns positions into slots, so
-  // no block-table lookup sits on the selection passes.
-  auto emit = [&](const uint64_t* key, const bool* keep, int m) {
-    uint32_t mine = 0;
-    for (int e = 0; e < m; ++e) mine += keep[e];
-    uint32_t at = wave_reserve(mine, &s.ocnt);
-    for (int e = 0; e < m; ++e) {
-      if (keep[e]) {
-        if (at < k) {
-          o.slots[orow + at] = static_cast<int32_t>(rank_pos(key[e]));
-          if (o.scores) o.scores[orow + at] = key_float(rank_vkey(key[e]));
-        }
-        ++at;
-      }
-    }
-  };
-  // One pass: scores above the threshold bin (all of them when the row holds
-  // at most k) are emitted, scores inside it go to LDS as unique keys.
-  auto pass = [&](const float (&v)[FS_PER], int base) {
-    static_assert(FS_PER <= 32, "bit masks");
-    uint32_t keepm = 0, midm = 0;
-#pragma unroll
-    for (int e = 0; e < FS_PER; ++e) {
-      const bool valid = base + e * FS_WG + tid < n;
-      const uint32_t bin = float_key(v[e]) >> HIST_SHIFT;
-      keepm |= static_cast<uint32_t>(valid && (th.all || bin > bstar)) << e;
-      midm |= static_cast<uint32_t>(valid && !th.all && bin == bstar) << e;
-    }
-    uint32_t at = wave_reserve(__builtin_popcount(keepm), &s.ocnt);
-#pragma unroll
-    for (int e = 0; e < FS_PER; ++e) {
-      if ((keepm >> e) & 1u) {
-        if (at < k) {
-          o.slots[orow + at] = base + e * FS_WG + tid;
-          if (o.scores) o.scores[orow + at] = v[e];
-        }
-        ++at;
-      }
-    }
-    uint32_t bt = wave_reserve(__builtin_popcount(midm), &s.bcnt);
-#pragma unroll
-    for (int e = 0; e < FS_PER; ++e) {
-      if ((midm >> e) & 1u) {
-        if (bt < static_cast<uint32_t>(FS_BUF))
-          s.buf[bt] = rank_key(float_key(v[e]), static_cast<uint32_t>(base + e * FS_WG + tid));
-        ++bt;
-      }
-    }
-  };
-  // the next pass's scores are in flight while this pass is processed
-  for (int base = 0; base == 0 || base < n; base += FS_PER * FS_WG) {
-    float nx[FS_PER];
-    const int nb0 = base + FS_PER * FS_WG;
-    if (nb0 < n) {
-#pragma unroll
-      for (int e = 0; e < FS_PER; ++e) {
-        const int i = nb0 + e * FS_WG + tid;
-        nx[e] = srow[i < n ? i : 0];
-      }
-    }
-    pass(v0, base);
-    if (nb0 < n) {
-#pragma unroll
-      for (int e = 0; e < FS_PER; ++e) v0[e] = nx[e];
-    }
-  }
-  __syncthreads();
-  const uint32_t nb = s.bcnt;
-  if (!th.all && nb > 0 && nb <= static_cast<uint32_t>(kWave * WS_PER)) {
-    // a small threshold bin: wave 0 alone selects and emits it (no
-    // workgroup barrier inside the select)
-    if (tid < kWave) {
-      uint64_t keys[WS_PER];
-      bool valid[WS_PER], keep[WS_PER];
-#pragma unroll
-      for (int e = 0; e < WS_PER; ++e) {
-        const uint32_t i = e * kWave + tid;
-        valid[e] = i < nb;
-        keys[e] = valid[e] ? s.buf[i] : 0ull;
-      }
-      const uint64_t T = nb > need ? wave_select<WS_PER>(keys, valid, need, s.sel.hist) : 0ull;
-#pragma unroll
-      for (int e = 0; e < WS_PER; ++e) keep[e] = valid[e] && keys[e] >= T;
-      emit(keys, keep, WS_PER);
-    }
-  } else if (!th.all && nb > 0) {
-    if (nb <= static_cast<uint32_t>(FS_BUF)) {
-      uint64_t keys[FS_MAXE];
-      bool keep[FS_MAXE];
-      uint64_t mn = ~0ull, mx = 0;
-#pragma unroll
-      for (int e = 0; e < FS_MAXE; ++e) {
-        const uint32_t i = tid + e * FS_WG;
-        keys[e] = i < nb ? s.buf[i] : 0ull;
-        if (i < nb) {
-          mn = keys[e] < mn ? keys[e] : mn;
-          mx = keys[e] > mx ? keys[e] : mx;
-        }
-      }
-      uint64_t T = 0;  // keys >= T are selected
-      if (nb > need) {
-        wg_range<FS_WG>(mn, mx, s.sel);
-        T = wg_select<FS_WG>(
-            [&](auto&& f) {
-#pragma unroll
-              for (int e = 0; e < FS_MAXE; ++e)
-                if (tid + e * FS_WG < nb) f(keys[e]);
-            },
-            need, mn, mx, s.sel);
-      }
-#pragma unroll
-      for (int e = 0; e < FS_MAXE; ++e) keep[e] = tid + e * FS_WG < nb && keys[e] >= T;
-      emit(keys, keep, FS_MAXE);
-    } else {
-      // threshold bin larger than the LDS buffer: select straight from the
-      // row's scores (several passes over them)
-      auto each_mid = [&](auto&& f) {
-        for (int i = tid; i < n; i += FS_WG) {
-          const uint32_t vk = float_key(srow[i]);
-          if ((vk >> HIST_SHIFT) == bstar) f(rank_key(vk, static_cast<uint32_t>(i)));
-        }
-      };
-      uint64_t mn = ~0ull, mx = 0;
-      each_mid([&](uint64_t key) {
-        mn = key < mn ? key : mn;
-        mx = key > mx ? key : mx;
-      });
-      wg_range<FS_WG>(mn, mx, s.sel);
-      const uint64_t T = wg_select<FS_WG>(each_mid, need, mn, mx, s.sel);
-      for (int i0 = 0; i0 < n; i0 += FS_WG) {
-        const int i = i0 + tid;
-        uint64_t key = 0;
-        bool keep = false;
-        if (i < n) {
-          const uint32_t vk = float_key(srow[i]);
-          key = rank_key(vk, static_cast<uint32_t>(i));
-          keep = (vk >> HIST_SHIFT) == bstar && key >= T;
-        }
-        emit(&key, &keep, 1);
-      }
-    }
-  }
-  __syncthreads();
-  const uint32_t nout = min(s.ocnt, k);
-  // positions -> slots (this workgroup wrote them; the barrier orders it)
-  if (!o.keep_positions)
-    positions_to_slots<FS_WG, FS_PER>(a, b, o, nout, [&](uint32_t pg) {
-      return STAGED ? s.pages[pg] : bt_row[pg];
-    });
-  // padding for rows shorter than k
-  for (uint32_t i = nout + tid; i < k; i += FS_WG) {
-    o.slots[orow + i] = -1;
-    if (o.scores) o.scores[orow + i] = -__builtin_inff();
-  }
-  // leave the row's workspace bytes zero again
-  for (int i = tid; i < n; i += FS_WG) srow[i] = 0.0f;
-  if (n > 0)
-    for (int i = tid; i < HIST_BINS; i += FS_WG) Hg[i] = 0;
-}
-
-__global__ __launch_bounds__(FS_WG) void fused_scores_merge_kernel(IndexerArgs a, FusedWs ws, FusedOut o) {
-  __shared__ ScoresMergeLds s;
-  const int b = blockIdx.x;
-  const int n = a.seq_lens[b];
-  const int npages = n > 0 ? static_cast<int>(fdiv(static_cast<uint32_t>(n - 1), a.pdiv)) + 1 : 0;
-  if (npages <= FS_PAGES)
-    fused_scores_merge_row<true>(a, ws, o, s, b, n, npages);
-  else
-    fused_scores_merge_row<false>(a, ws, o, s, b, n, npages);
 }
 
 // ---------------------------------------------------------------------------
@@ -1185,9 +1162,6 @@ __global__ __launch_bounds__(MG_WG) void block_merge_kernel(IndexerArgs a, Block
     write_slot_list<MG_WG>(o.slots + static_cast<int64_t>(sel_row) * top * bs, top, bs, nsel, n, s.sel_blocks,
                            s.phys, a.pdiv, tid, (reinterpret_cast<uintptr_t>(o.slots) & 15u) == 0);
   }
-  // leave every workspace byte of this row zero again
-  __syncthreads();
-  for (int cb = tid; cb < nblk; cb += MG_WG) bsc[cb] = 0;
 }
 
 // Per-head block maxima (fp8 cache): each head's term of the score, maxed
@@ -1246,7 +1220,7 @@ __global__ __launch_bounds__(IX_WG) void block_heads_chunk_kernel(IndexerArgs a,
 // BH_MAX_BLOCKS blocks and at most BH_MAX_TOP kept blocks: the selection's
 // block keys sit 16 per lane, wave_select finds the top-th, a ballot compacts
 // the kept block ids into this wave's LDS list, and the wave writes the
-// block ids, the slot lists and the zeros. No workgroup barrier: a wave whose
+// block ids and the slot lists. No workgroup barrier: a wave whose
 // selection is past the end leaves at once.
 constexpr int BH_WAVES = 4;
 constexpr int BH_PER = 16;
@@ -1306,10 +1280,6 @@ __global__ __launch_bounds__(BH_WAVES * kWave) void block_heads_merge_kernel(Ind
     write_slot_list<kWave>(o.slots + static_cast<int64_t>(sel_row) * top * bs, top, bs, nsel, n, s.sel[wave],
                            s.phys[wave], a.pdiv, lane, (reinterpret_cast<uintptr_t>(o.slots) & 15u) == 0);
   }
-  // leave this selection's workspace entries zero again
-#pragma unroll
-  for (int e = 0; e < BH_PER; ++e)
-    if (valid[e]) bsc[e * kWave + lane] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -1333,6 +1303,7 @@ static IndexerArgs make_args(const IndexerInputs& in, int chunk, bool guided = f
   a.heads = in.heads;
   a.chunk = chunk;
   a.quad_map = in.row_to_batch != nullptr && in.batch % 4 == 0 && in.batch >= 8;
+  a.cached_keys = 0;
   const int msl = in.max_seq_len > 0 ? in.max_seq_len : 1;
   // Guided schedule when quarter chunks stay large (and aligned): full-size
   // chunks up to half the longest row, halves up to three quarters, then
@@ -1421,10 +1392,10 @@ int launch_idx_score(const IndexerInputs& in, float* scores, int64_t score_strid
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-// Workgroups of fused_scores_chunk_kernel that the current device holds at
-// once (all compute units, launched with the largest score LDS). Cached per
-// device and head count.
-static int fs_resident_wgs(int heads, bool bf) {
+// Workgroups of fused_chunk_kernel that the current device holds at once
+// (all compute units, with the score LDS of a FE_RESIDENT_MAX-token chunk).
+// Cached per device, head count and cache format.
+static int fused_resident_wgs(int heads, bool bf) {
   static int cache[2][4][64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
@@ -1432,15 +1403,15 @@ static int fs_resident_wgs(int heads, bool bf) {
   if (cache[bf][ti][dev] > 0) return cache[bf][ti][dev];
   int cus = 0, per = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  const size_t lds = static_cast<size_t>(FS_CH_MAX) * sizeof(float);
+  const size_t lds = static_cast<size_t>(FE_RESIDENT_MAX) * sizeof(float);
   hipError_t e = hipErrorInvalidValue;
-#define IDXTOPK_OCC(B)                                                                                          \
-  switch (heads) {                                                                                            \
-    case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_scores_chunk_kernel<1, B>, IX_WG, lds); break;   \
-    case 32: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_scores_chunk_kernel<2, B>, IX_WG, lds); break;   \
-    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_scores_chunk_kernel<4, B>, IX_WG, lds); break;   \
-    case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_scores_chunk_kernel<8, B>, IX_WG, lds); break;  \
-    default: break;                                                                                           \
+#define IDXTOPK_OCC(B)                                                                                         \
+  switch (heads) {                                                                                           \
+    case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_chunk_kernel<1, B>, IX_WG, lds); break;   \
+    case 32: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_chunk_kernel<2, B>, IX_WG, lds); break;   \
+    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_chunk_kernel<4, B>, IX_WG, lds); break;   \
+    case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_chunk_kernel<8, B>, IX_WG, lds); break;  \
+    default: break;                                                                                          \
   }
   if (bf) {
     IDXTOPK_OCC(true)
@@ -1453,30 +1424,39 @@ static int fs_resident_wgs(int heads, bool bf) {
   return cache[bf][ti][dev];
 }
 
-// Score-buffer path: chunks sized so the whole grid is resident at once.
-static int launch_fused_scores(const IndexerInputs& in, const FusedWs& w, const FusedOut& o, hipStream_t stream) {
+#define IDXTOPK_MERGE_NT(BFV, heads, grid, stream, ...)                                                        \
+  switch (heads) {                                                                                            \
+    case 16: hipLaunchKernelGGL((fused_merge_kernel<1, BFV>), grid, dim3(FM_WG), 0, stream, __VA_ARGS__); break; \
+    case 32: hipLaunchKernelGGL((fused_merge_kernel<2, BFV>), grid, dim3(FM_WG), 0, stream, __VA_ARGS__); break; \
+    case 64: hipLaunchKernelGGL((fused_merge_kernel<4, BFV>), grid, dim3(FM_WG), 0, stream, __VA_ARGS__); break; \
+    case 128: hipLaunchKernelGGL((fused_merge_kernel<8, BFV>), grid, dim3(FM_WG), 0, stream, __VA_ARGS__); break; \
+    default: return -2;                                                                                       \
+  }
+
+// Chunk size: when the batch fits one resident wave of chunk workgroups at
+// up to FE_RESIDENT_MAX tokens each (decode batches), chunks are sized so
+// that the whole grid runs at once; larger batches take chunks of up to
+// FU_CH_MAX tokens on the guided schedule (about 2048 workgroups).
+static IndexerArgs fused_args(const IndexerInputs& in) {
   const int64_t tokens = static_cast<int64_t>(in.batch) * (in.max_seq_len > 0 ? in.max_seq_len : 1);
-  const int64_t nwg = fs_resident_wgs(in.heads, in.bf16);
-  int64_t ch = nwg > 0 ? (tokens + nwg - 1) / nwg : FS_CH_MAX;
-  ch = (ch + kGroup - 1) / kGroup * kGroup;
-  if (ch < FS_CH_MIN) ch = FS_CH_MIN;
-  if (ch > FS_CH_MAX) ch = FS_CH_MAX;
+  const int64_t nwg = fused_resident_wgs(in.heads, in.bf16);
   const int64_t page_cap = (static_cast<int64_t>(IX_PAGES - 2) * in.page_size) / kGroup * kGroup;
-  if (ch > page_cap) ch = page_cap > kGroup ? page_cap : kGroup;
-  const IndexerArgs a = make_args(in, static_cast<int>(ch), false);
-  const dim3 grid(chunk_grid(a));
-  const size_t lds = static_cast<size_t>(ch) * sizeof(float);
-  (void)hipGetLastError();
-  IDXTOPK_DISPATCH_NT_LDS(fused_scores_chunk_kernel, in.bf16, in.heads, grid, lds, stream, a, w);
-  hipLaunchKernelGGL(fused_scores_merge_kernel, dim3(in.batch), dim3(FS_WG), 0, stream, a, w, o);
-  return hipGetLastError() == hipSuccess ? 0 : -4;
+  if (nwg > 0 && tokens <= nwg * FE_RESIDENT_MAX) {
+    int64_t ch = (tokens + nwg - 1) / nwg;
+    ch = (ch + kGroup - 1) / kGroup * kGroup;
+    if (ch < FE_CH_MIN) ch = FE_CH_MIN;
+    if (ch > page_cap) ch = page_cap;
+    if (ch < kGroup) ch = kGroup;
+    return make_args(in, static_cast<int>(ch), false);
+  }
+  IndexerArgs a = make_args(in, choose_chunk(in.batch, in.max_seq_len, in.page_size, kGroup, 512, FU_CH_MAX), true);
+  a.cached_keys = 1;
+  return a;
 }
 
-static int launch_fused_select(const IndexerInputs& in, const FusedWs& w, const FusedOut& o, hipStream_t stream);
-
-// Sorted output: the merges leave positions and scores (in the workspace's
+// Sorted output: the merge leaves positions and scores (in the workspace's
 // score area when the caller wants none), then the sort pass orders and maps
-// them and clears that area again.
+// them.
 int launch_fused(const IndexerInputs& in, int k, int32_t* out_slots, float* out_scores, void* ws,
                  bool sorted, hipStream_t stream) {
   if (in.batch == 0) return 0;
@@ -1486,26 +1466,25 @@ int launch_fused(const IndexerInputs& in, int k, int32_t* out_slots, float* out_
   o.scores = sorted && !out_scores ? w.sval : out_scores;
   o.k = k;
   o.keep_positions = sorted;
-  const int e = launch_fused_select(in, w, o, stream);
-  if (e || !sorted) return e;
-  return launch_sort_rows(in.batch, k, out_slots, o.scores, nullptr, 0, nullptr, nullptr, in.block_table,
-                          in.bt_stride, in.page_size, in.row_to_batch, out_scores,
-                          out_scores ? nullptr : w.sval, stream);
-}
-
-static int launch_fused_select(const IndexerInputs& in, const FusedWs& w, const FusedOut& o, hipStream_t stream) {
-  if (static_cast<int64_t>(in.batch) * in.max_seq_len <= FS_MAX_TOKENS) return launch_fused_scores(in, w, o, stream);
-  const int chunk = choose_chunk(in.batch, in.max_seq_len, in.page_size, kGroup, 512, FU_CH_MAX);
-  const IndexerArgs a = make_args(in, chunk, true);
-  const int k = o.k;
+  const IndexerArgs a = fused_args(in);
+  // every chunk of a row has a header (chunks are at least FE_CH_MIN tokens:
+  // the page-staging cap is 496 tokens or more)
+  if (a.nchunk_max > w.hcap) return -4;
   const dim3 grid(chunk_grid(a));
   (void)hipGetLastError();
   // the scores' dynamic LDS plus the static part stay within 64 KB
   static_assert(FU_CH_MAX * 4 + sizeof(ChunkLds) <= 64 * 1024, "fused chunk LDS");
-  const size_t lds = static_cast<size_t>(chunk) * sizeof(float);
+  const size_t lds = static_cast<size_t>(a.chunk) * sizeof(float);
   IDXTOPK_DISPATCH_NT_LDS(fused_chunk_kernel, in.bf16, in.heads, grid, lds, stream, a, w, k);
-  hipLaunchKernelGGL(fused_merge_kernel, dim3(in.batch), dim3(MG_WG), 0, stream, a, w, o);
-  return hipGetLastError() == hipSuccess ? 0 : -4;
+  if (in.bf16) {
+    IDXTOPK_MERGE_NT(true, in.heads, dim3(in.batch), stream, a, w, o)
+  } else {
+    IDXTOPK_MERGE_NT(false, in.heads, dim3(in.batch), stream, a, w, o)
+  }
+  if (hipGetLastError() != hipSuccess) return -4;
+  if (!sorted) return 0;
+  return launch_sort_rows(in.batch, k, out_slots, o.scores, nullptr, 0, nullptr, nullptr, in.block_table,
+                          in.bt_stride, in.page_size, in.row_to_batch, out_scores, stream);
 }
 
 // Workgroups of block_chunk_kernel that the current device holds at once.
@@ -1555,7 +1534,7 @@ int launch_block_topk(const IndexerInputs& in, int block_size, int top_blocks, i
   }
   if (chunk / block_size > BK_MAX_BLOCKS_PER_CHUNK) chunk = BK_MAX_BLOCKS_PER_CHUNK * block_size;
   const IndexerArgs a = make_args(in, chunk, true, block_size);
-  const BlockWs w = block_ws(ws, in.batch, block_size, in.max_seq_len);
+  const BlockWs w = block_ws(ws, block_size, in.max_seq_len);
   BlockOut o;
   o.blocks = out_blocks;
   o.slots = out_slots;
@@ -1580,7 +1559,7 @@ int launch_block_topk_heads(const IndexerInputs& in, int block_size, int top_blo
   if (chunk / block_size > BKH_MAX_BLOCKS) chunk = BKH_MAX_BLOCKS * block_size;
   if (chunk < block_size) chunk = block_size;
   const IndexerArgs a = make_args(in, chunk, true, block_size);
-  const BlockWs w = block_ws(ws, in.batch * in.heads, block_size, in.max_seq_len);
+  const BlockWs w = block_ws(ws, block_size, in.max_seq_len);
   BlockOut o;
   o.blocks = out_blocks;
   o.slots = out_slots;

@@ -35,7 +35,7 @@ int launch_topk_rows(const float* scores, int64_t stride, int rows, const int32_
 int launch_sort_rows(int rows, int k, int32_t* pos, const float* vals, const float* scores, int64_t stride,
                      const int32_t* row_starts, const int32_t* seq_lens, const int32_t* page_table,
                      int64_t pt_stride, int page_size, const int32_t* row_to_batch, float* out_vals,
-                     float* clear_vals, hipStream_t stream);
+                     hipStream_t stream);
 
 int launch_page_transform(const int32_t* idx, int rows, int k, const int32_t* page_table,
                           int64_t pt_stride, int page_size, const int32_t* row_to_batch,

@@ -60,6 +60,9 @@ struct IndexerArgs {
   // deals (row, chunk) pairs to workgroups in quads of rows (batch % 4 == 0,
   // grid rounded up to a multiple of 32).
   int32_t quad_map;
+  // Nonzero: a bf16 cache is read with ordinary (cached) loads in the fused
+  // chunk kernel, else with nontemporal ones.
+  int32_t cached_keys;
 };
 
 struct KeyPieces {

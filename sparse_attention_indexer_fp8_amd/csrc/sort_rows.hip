@@ -22,7 +22,6 @@ struct SortArgs {
   FastDiv pdiv;
   const int32_t* row_to_batch;  // page-table row of each row, or null (row i -> i)
   float* out_vals;             // sorted scores out (may alias vals; -inf pads), or null
-  float* clear_vals;           // if not null: [rows][k] cells set to 0 once read (workspace)
   int32_t k;
   int32_t npow;                // power of two >= k, at least 256
 };
@@ -75,13 +74,6 @@ __global__ __launch_bounds__(WG) void sort_rows_kernel(SortArgs a) {
     const bool real = j < a.k && p[e] >= 0 && (a.vals || p[e] < n);
     r[e] = real ? rank_key(float_key(v[e]), static_cast<uint32_t>(p[e])) : 0ull;
   }
-  if (a.clear_vals) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int j = e * WG + tid;
-      if (j < a.k) a.clear_vals[row + j] = 0.0f;
-    }
-  }
   block_sort_desc<WG, E>(r, xs);
   const int base = tid * E;  // rank of r[0]
   const int32_t* pt_row = nullptr;
@@ -119,7 +111,7 @@ __global__ __launch_bounds__(WG) void sort_rows_kernel(SortArgs a) {
 int launch_sort_rows(int rows, int k, int32_t* pos, const float* vals, const float* scores, int64_t stride,
                      const int32_t* row_starts, const int32_t* seq_lens, const int32_t* page_table,
                      int64_t pt_stride, int page_size, const int32_t* row_to_batch, float* out_vals,
-                     float* clear_vals, hipStream_t stream) {
+                     hipStream_t stream) {
   if (rows == 0) return 0;
   SortArgs a;
   a.pos = pos;
@@ -134,7 +126,6 @@ int launch_sort_rows(int rows, int k, int32_t* pos, const float* vals, const flo
   a.pdiv = make_fastdiv(static_cast<uint32_t>(a.page_size));
   a.row_to_batch = row_to_batch;
   a.out_vals = out_vals;
-  a.clear_vals = clear_vals;
   a.k = k;
   int npow = SR_MIN_NPOW;
   while (npow < k) npow <<= 1;

@@ -51,38 +51,30 @@ def workspace_bytes(op: int, rows: int, k: int, max_seq_len: int) -> int:
 
 
 class Workspace:
-    """A zero-filled device buffer that the library keeps zero-filled between calls.
+    """A device buffer for the fused and block ops; its contents never matter.
 
     Calls that share one Workspace must not run concurrently. A call enqueues
     its kernels on torch's current stream; the buffer is recorded on every
     stream it is used on, so the caching allocator never hands its memory to
     another tensor while a kernel on any of those streams may still use it.
-    After a failed launch the buffer may hold nonzero bytes, so the next call
-    gets a freshly zeroed one.
     """
 
     def __init__(self, device=None):
         self.device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
         self.buf: Optional[torch.Tensor] = None
-        self.poisoned = False
         self._streams = set()
 
     def get(self, nbytes: int) -> torch.Tensor:
         stream = torch.cuda.current_stream(self.device)
-        if self.poisoned or self.buf is None or self.buf.numel() < nbytes:
+        if self.buf is None or self.buf.numel() < nbytes:
             # the old buffer's memory returns to the pool only after the work
             # queued on every stream it was recorded on
-            self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
-            self.poisoned = False
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
             self._streams = {stream.cuda_stream}
         elif stream.cuda_stream not in self._streams:
             self.buf.record_stream(stream)
             self._streams.add(stream.cuda_stream)
         return self.buf
-
-    def poison(self) -> None:
-        """Mark the buffer as possibly dirty (a launch failed midway)."""
-        self.poisoned = True
 
 
 # One default Workspace per (device, stream): calls on one stream run in
@@ -99,14 +91,6 @@ def _workspace(ws: Optional[Workspace]) -> Workspace:
     if key not in _default_ws:
         _default_ws[key] = Workspace(torch.device("cuda", dev))
     return _default_ws[key]
-
-
-def _check_ws(fn: str, st: int, ws: Workspace) -> None:
-    """Status check of a call that used a workspace: a launch failure may
-    leave the workspace dirty, so it is replaced before its next use."""
-    if st == _lib.IDXTOPK_ELAUNCH:
-        ws.poison()
-    _lib.check(fn, st)
 
 
 def topk_rows(scores: torch.Tensor, seq_lens: torch.Tensor, k: int,
@@ -211,12 +195,11 @@ def idx_score_topk_fused(q, q_scale, w, kcache, k_scale, block_table, seq_lens, 
     if return_scores and out_scores is None:
         out_scores = torch.empty((B, k), dtype=torch.float32, device=q.device)
     nbytes = workspace_bytes(_lib.OP_SCORE_TOPK_FUSED, B, k, max_seq_len)
-    wso = _workspace(workspace)
-    ws = wso.get(nbytes)
+    ws = _workspace(workspace).get(nbytes)
     st = _lib.load().idx_score_topk_fused(*args, int(page_size), _ptr(row_to_batch), _ptr(seq_lens), B, H, D,
                                           int(max_seq_len), int(k), _ptr(out), _ptr(out_scores),
                                           _ptr(ws), ws.numel(), _lib.SORTED if sorted else 0, _stream())
-    _check_ws("idx_score_topk_fused", st, wso)
+    _lib.check("idx_score_topk_fused", st)
     return (out, out_scores) if return_scores else out
 
 
@@ -247,13 +230,12 @@ def block_topk(q, q_scale, w, kcache, k_scale, block_table, seq_lens, page_size:
     out_slots = (torch.empty((B, top_blocks * block_size), dtype=torch.int32, device=q.device)
                  if return_slots else None)
     nbytes = workspace_bytes(_lib.OP_BLOCK_TOPK, B, block_size, max_seq_len)
-    wso = _workspace(workspace)
-    ws = wso.get(nbytes)
+    ws = _workspace(workspace).get(nbytes)
     st = _lib.load().block_topk(*args, int(page_size), _ptr(row_to_batch), _ptr(seq_lens), B, H, D,
                                 int(max_seq_len),
                                 int(block_size), int(top_blocks), _ptr(out_blocks), _ptr(out_slots),
                                 _ptr(ws), ws.numel(), _stream())
-    _check_ws("block_topk", st, wso)
+    _lib.check("block_topk", st)
     return (out_blocks, out_slots) if return_slots else out_blocks
 
 
@@ -268,12 +250,11 @@ def block_topk_heads(q, q_scale, w, kcache, k_scale, block_table, seq_lens, page
     out_slots = (torch.empty((B, H, top_blocks * block_size), dtype=torch.int32, device=q.device)
                  if return_slots else None)
     nbytes = workspace_bytes(_lib.OP_BLOCK_TOPK_HEADS, B * H, block_size, max_seq_len)
-    wso = _workspace(workspace)
-    ws = wso.get(nbytes)
+    ws = _workspace(workspace).get(nbytes)
     st = _lib.load().block_topk_heads(*args, int(page_size), _ptr(row_to_batch), _ptr(seq_lens), B, H, D,
                                       int(max_seq_len), int(block_size), int(top_blocks), _ptr(out_blocks),
                                       _ptr(out_slots), _ptr(ws), ws.numel(), _stream())
-    _check_ws("block_topk_heads", st, wso)
+    _lib.check("block_topk_heads", st)
     return (out_blocks, out_slots) if return_slots else out_blocks
 
 
@@ -344,12 +325,11 @@ def idx_score_topk_fused_bf16(q, w, kcache, block_table, seq_lens, page_size: in
     if return_scores and out_scores is None:
         out_scores = torch.empty((B, k), dtype=torch.float32, device=q.device)
     nbytes = workspace_bytes(_lib.OP_SCORE_TOPK_FUSED, B, k, max_seq_len)
-    wso = _workspace(workspace)
-    ws = wso.get(nbytes)
+    ws = _workspace(workspace).get(nbytes)
     st = _lib.load().idx_score_topk_fused_bf16(*args, int(page_size), _ptr(row_to_batch), _ptr(seq_lens), B, H, D,
                                                int(max_seq_len), int(k), _ptr(out), _ptr(out_scores),
                                                _ptr(ws), ws.numel(), _lib.SORTED if sorted else 0, _stream())
-    _check_ws("idx_score_topk_fused_bf16", st, wso)
+    _lib.check("idx_score_topk_fused_bf16", st)
     return (out, out_scores) if return_scores else out
 
 
@@ -362,12 +342,11 @@ def block_topk_bf16(q, w, kcache, block_table, seq_lens, page_size: int, max_seq
     out_slots = (torch.empty((B, top_blocks * block_size), dtype=torch.int32, device=q.device)
                  if return_slots else None)
     nbytes = workspace_bytes(_lib.OP_BLOCK_TOPK, B, block_size, max_seq_len)
-    wso = _workspace(workspace)
-    ws = wso.get(nbytes)
+    ws = _workspace(workspace).get(nbytes)
     st = _lib.load().block_topk_bf16(*args, int(page_size), _ptr(row_to_batch), _ptr(seq_lens), B, H, D,
                                      int(max_seq_len), int(block_size), int(top_blocks), _ptr(out_blocks),
                                      _ptr(out_slots), _ptr(ws), ws.numel(), _stream())
-    _check_ws("block_topk_bf16", st, wso)
+    _lib.check("block_topk_bf16", st)
     return (out_blocks, out_slots) if return_slots else out_blocks
 
 

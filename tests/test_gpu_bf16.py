@@ -16,9 +16,10 @@ from tests._helpers import check_fused_row, check_scores, dev, log, rms
 
 pytestmark = pytest.mark.gpu
 
-# batches of at most this many tokens take the score-buffer variant of the
-# fused path, larger ones the candidate variant
-FUSED_SCORE_PATH_TOKENS = 1 << 21
+# batches of more than this many tokens never fit one resident wave of the
+# fused path's chunk workgroups (at most 8192 tokens each, at most 8 per
+# compute unit on 256 units): they take the guided chunk schedule
+FUSED_GUIDED_TOKENS = 1 << 24
 
 
 @pytest.fixture(scope="module")
@@ -62,9 +63,9 @@ def _exact_case(seed, batch, n_lo, n_hi, page_size, heads=64, k=64, first=(), **
     return case
 
 
-def _candidate_variant(case):
+def _guided_variant(case):
     big = copy.copy(case)
-    big.max_seq_len = FUSED_SCORE_PATH_TOKENS // case.batch + 1
+    big.max_seq_len = FUSED_GUIDED_TOKENS // case.batch + 1
     cols = -(-big.max_seq_len // case.page_size)
     bt = np.zeros((case.block_table.shape[0], cols), np.int32)
     bt[:, :case.block_table.shape[1]] = case.block_table
@@ -112,13 +113,13 @@ def test_bf16_score_exact_values(ops):
         assert np.array_equal(out[b, :n].astype(np.float64), case_scores(case, b))
 
 
-@pytest.mark.parametrize("variant", ["score-buffer", "candidates"])
+@pytest.mark.parametrize("variant", ["resident", "guided"])
 @pytest.mark.parametrize("page_size,heads,k", [(64, 64, 64), (16, 16, 300), (1, 32, 200), (48, 128, 700)])
 def test_bf16_fused_exact_sets(ops, variant, page_size, heads, k):
     case = _exact_case(1400 + page_size + heads, batch=5, n_lo=1, n_hi=12000, page_size=page_size, heads=heads,
                        k=k, first=(0, k - 1, k))
-    if variant == "candidates":
-        case = _candidate_variant(case)
+    if variant == "guided":
+        case = _guided_variant(case)
     slots, sc = _fused(ops, case)
     ref_slots, ref_pos, scores = oracle.fused_topk(case)
     for b in range(case.batch):
@@ -128,11 +129,11 @@ def test_bf16_fused_exact_sets(ops, variant, page_size, heads, k):
         assert np.array_equal(np.sort(sc[b][:m].astype(np.float64)), exp_s), b
 
 
-@pytest.mark.parametrize("variant", ["score-buffer", "candidates"])
+@pytest.mark.parametrize("variant", ["resident", "guided"])
 def test_bf16_fused_tolerance_random(ops, variant):
     case = workloads.indexer_case(1500, batch=6, n_lo=1, n_hi=20000, page_size=64, k=2048, cache_dtype="bf16")
-    if variant == "candidates":
-        case = _candidate_variant(case)
+    if variant == "guided":
+        case = _guided_variant(case)
     slots, sc = _fused(ops, case)
     rows = [case_scores(case, b) for b in range(case.batch)]
     bsig = rms(np.concatenate(rows))

@@ -126,7 +126,8 @@ def test_fused_tolerance_random(ops, page_size, k, n_lo, n_hi):
 
 
 def test_fused_workspace_reuse_smaller_second_call(ops):
-    """The workspace is left zeroed: a second call with a smaller input is exact."""
+    """Calls sharing one workspace do not depend on what an earlier call left
+    in it: a second call with a smaller input is exact."""
     from sparse_attention_indexer_fp8_amd import ops as o
 
     ws = o.Workspace()
@@ -173,20 +174,21 @@ def test_default_workspace_per_stream(ops):
             assert np.array_equal(np.sort(o.cpu().numpy(), axis=1), np.sort(ref_blk[0], axis=1))
 
 
-# Batches of at most this many tokens (batch * max_seq_len) take the
-# score-buffer variant of the fused path; larger ones the candidate variant.
-FUSED_SCORE_PATH_TOKENS = 1 << 21
+# Batches of more than this many tokens never fit one resident wave of the
+# fused path's chunk workgroups (at most 8192 tokens each, at most 8 per
+# compute unit on 256 units): they take the guided chunk schedule
+FUSED_GUIDED_TOKENS = 1 << 24
 
 
-def _candidate_variant(case):
+def _guided_variant(case):
     """The same case with a max_seq_len (an upper bound on every row length)
-    large enough to send it down the candidate variant. The block table gets
+    large enough to send it down the guided chunk schedule. The block table gets
     zero columns so it covers that bound, as the API requires; no row reads
     them."""
     import copy
 
     big = copy.copy(case)
-    big.max_seq_len = FUSED_SCORE_PATH_TOKENS // case.batch + 1
+    big.max_seq_len = FUSED_GUIDED_TOKENS // case.batch + 1
     cols = -(-big.max_seq_len // case.page_size)
     bt = np.zeros((case.block_table.shape[0], cols), np.int32)
     bt[:, :case.block_table.shape[1]] = case.block_table
@@ -196,13 +198,13 @@ def _candidate_variant(case):
 
 @pytest.mark.parametrize("page_size,heads,k", [(64, 64, 2048), (16, 32, 300), (1, 16, 100)])
 def test_fused_both_variants_exact(ops, page_size, heads, k):
-    """The score-buffer and candidate variants of the fused path select the
-    oracle's exact set on the same inputs."""
+    """Both chunk schedules of the fused path (resident chunks and the guided
+    schedule) select the oracle's exact set on the same inputs."""
     case = _exact_case(450 + page_size, batch=6, n_lo=1, n_hi=16000, page_size=page_size, heads=heads, k=k,
                        first=(0, k - 1, k, 16000))
-    assert case.batch * case.max_seq_len <= FUSED_SCORE_PATH_TOKENS
+    assert case.batch * case.max_seq_len <= FUSED_GUIDED_TOKENS
     ref_slots, _, _ = oracle.fused_topk(case)
-    big = _candidate_variant(case)
+    big = _guided_variant(case)
     for c in (case, big):
         log(f"fused variant check: batch={c.batch} max_seq_len={c.max_seq_len} k={k} page_size={page_size}")
         slots, _ = _fused(ops, c)
@@ -211,13 +213,13 @@ def test_fused_both_variants_exact(ops, page_size, heads, k):
 
 
 def test_fused_workspace_reuse_across_variants(ops):
-    """Each variant leaves the workspace zeroed for the other."""
+    """Calls of both chunk schedules share one workspace in any order."""
     from sparse_attention_indexer_fp8_amd import ops as o
 
     ws = o.Workspace()
     a = _exact_case(611, batch=4, n_lo=3000, n_hi=20000, page_size=64, k=700)
     b = _exact_case(612, batch=3, n_lo=100, n_hi=5000, page_size=16, k=300)
-    a_big = _candidate_variant(a)
+    a_big = _guided_variant(a)
     for case in (a, a_big, b, a_big, a):
         slots, _ = _fused(ops, case, ws=ws)
         ref, _, _ = oracle.fused_topk(case)
@@ -234,10 +236,88 @@ def test_fused_all_scores_tied(ops):
     ref_slots, ref_pos, _ = oracle.fused_topk(case)
     for b in range(case.batch):
         assert np.array_equal(np.sort(ref_pos[b]), np.arange(case.k)), b
-    for c in (case, _candidate_variant(case)):
+    for c in (case, _guided_variant(case)):
         slots, _ = _fused(ops, c)
         for b in range(case.batch):
             assert np.array_equal(np.sort(slots[b]), np.sort(ref_slots[b])), (c.max_seq_len, b)
+
+
+def _crowded_case(seed, batch, n_lo, n_hi, page_size, k, heads=16):
+    """Exact-arithmetic rows whose best tokens all sit at the end of the row:
+    query 1.0 in every dimension, only head 0 weighted (1.0), unit scales,
+    and token j's key holds 1.0 in its first m_j = 1 + 127 j // n dimensions
+    and 0 elsewhere, so S[j] = m_j grows with the position (ties in runs).
+    The chunks at the end of a row hold its whole top k, far more than their
+    share, so the merge's check fails and it scores the row again."""
+    case = workloads.indexer_case(seed, batch=batch, n_lo=n_lo, n_hi=n_hi, page_size=page_size, k=k, heads=heads,
+                                  fixed_lens=_lens(seed, batch, n_lo, n_hi))
+    case.q[:] = 0x38
+    case.q_scale[:] = 1.0
+    case.w[:] = 0.0
+    case.w[:, 0] = 1.0
+    for b in range(batch):
+        n = int(case.seq_lens[b])
+        ts = oracle.token_slots(case.block_table[b], case.page_size, n)
+        m = 1 + (127 * np.arange(n)) // max(n, 1)
+        keys = np.where(np.arange(case.dim)[None, :] < m[:, None], 0x38, 0x00).astype(np.uint8)
+        case.kcache[ts] = keys
+        case.k_scale[ts] = 1.0
+    return case
+
+
+@pytest.mark.parametrize("sorted_out", [False, True])
+@pytest.mark.parametrize("page_size,k,n_lo,n_hi", [(64, 2048, 6000, 30000), (16, 300, 400, 9000),
+                                                   (1, 100, 150, 4000)])
+def test_fused_crowded_rows_rescored(ops, page_size, k, n_lo, n_hi, sorted_out):
+    """Rows whose top k crowd into their last chunks (far beyond the chunks'
+    margin): the merge scores them again and the result is still the
+    oracle's exact selection, on both chunk schedules."""
+    import torch
+
+    case = _crowded_case(660 + page_size, batch=5, n_lo=n_lo, n_hi=n_hi, page_size=page_size, k=k)
+    ref_slots, ref_pos, scores = oracle.fused_topk(case)
+    for c in (case, _guided_variant(case)):
+        log(f"crowded rows: max_seq_len={c.max_seq_len} k={k} page_size={page_size} sorted={sorted_out}")
+        slots, sc = ops.idx_score_topk_fused(*_inputs(c), c.page_size, c.max_seq_len, k, return_scores=True,
+                                             sorted=sorted_out)
+        torch.cuda.synchronize()
+        slots, sc = slots.cpu().numpy(), sc.cpu().numpy()
+        for b in range(case.batch):
+            if sorted_out:
+                assert np.array_equal(slots[b], ref_slots[b]), b
+            else:
+                assert np.array_equal(np.sort(slots[b]), np.sort(ref_slots[b])), b
+            m = min(int(case.seq_lens[b]), k)
+            assert np.array_equal(np.sort(sc[b][:m].astype(np.float64)), np.sort(scores[b][ref_pos[b][:m]])), b
+
+
+def test_fused_dirty_workspace(ops):
+    """The fused and block ops need no particular workspace contents: a
+    workspace filled with 0xFF bytes gives the oracle's exact results."""
+    import torch
+
+    from sparse_attention_indexer_fp8_amd import ops as o
+
+    fc = _exact_case(670, batch=5, n_lo=1, n_hi=20000, page_size=64, k=700, first=(0, 699, 700))
+    bc = _exact_case(671, batch=4, n_lo=1, n_hi=9000, page_size=128, k=0, block_size=128, top_blocks=7,
+                     first=(0, 128 * 7))
+    for c, op in ((fc, "fused"), (_guided_variant(fc), "fused"), (bc, "block")):
+        ws = o.Workspace()
+        if op == "fused":
+            buf = ws.get(ops.workspace_bytes(o._lib.OP_SCORE_TOPK_FUSED, c.batch, c.k, c.max_seq_len))
+        else:
+            buf = ws.get(ops.workspace_bytes(o._lib.OP_BLOCK_TOPK, c.batch, c.block_size, c.max_seq_len))
+        buf.fill_(0xFF)
+        if op == "fused":
+            slots, _ = _fused(ops, c, ws=ws)
+            ref, _, _ = oracle.fused_topk(c)
+            assert np.array_equal(np.sort(slots, axis=1), np.sort(ref, axis=1))
+        else:
+            blocks, sl = ops.block_topk(*_inputs(c), c.page_size, c.max_seq_len, c.block_size, c.top_blocks,
+                                        workspace=ws)
+            torch.cuda.synchronize()
+            rb, rs, _, _ = oracle.block_topk(c)
+            assert np.array_equal(np.sort(blocks.cpu().numpy(), axis=1), np.sort(rb, axis=1))
 
 
 @pytest.mark.parametrize("page_size,k,n_lo,n_hi,batch", [(64, 2048, 1, 20000, 6), (16, 300, 100, 9000, 5),
@@ -253,7 +333,7 @@ def test_fused_equals_unfused(ops, page_size, k, n_lo, n_hi, batch):
     ref = ops.topk_rows(scores, dev(case.seq_lens), k, page_table=dev(case.block_table), page_size=page_size)
     torch.cuda.synchronize()
     ref = np.sort(ref.cpu().numpy(), axis=1)
-    for c in (case, _candidate_variant(case)):
+    for c in (case, _guided_variant(case)):
         slots, _ = _fused(ops, c)
         assert np.array_equal(np.sort(slots, axis=1), ref), c.max_seq_len
 
@@ -384,7 +464,7 @@ def test_multi_query_fused(ops, page_size, k):
     bsig = rms(np.concatenate(rows))
     flat = _expanded(case)
     ref, _ = _fused(ops, flat)
-    for c in (case, _candidate_variant(case)):
+    for c in (case, _guided_variant(case)):
         slots, sc = _fused(ops, c)
         assert np.array_equal(np.sort(slots, axis=1), np.sort(ref, axis=1)), c.max_seq_len
     for b in range(case.batch):
@@ -509,7 +589,7 @@ def test_prefill_indexer_full_size(ops):
 # position, -1 padding last. The oracle's selection is a stable descending
 # sort, so its order is that order: with exact arithmetic the whole output
 # sequence must match, ties included.
-@pytest.mark.parametrize("variant", ["score-buffer", "candidates"])
+@pytest.mark.parametrize("variant", ["resident", "guided"])
 @pytest.mark.parametrize("with_scores", [True, False])
 @pytest.mark.parametrize("k", [100, 700, 3000, 8192])
 def test_fused_sorted_exact_order(ops, variant, with_scores, k):
@@ -517,8 +597,8 @@ def test_fused_sorted_exact_order(ops, variant, with_scores, k):
     from sparse_attention_indexer_fp8_amd import ops as o
 
     case = _exact_case(640 + k, batch=5, n_lo=1, n_hi=12000, page_size=64, heads=64, k=k, first=(0, k - 1, k))
-    if variant == "candidates":
-        case = _candidate_variant(case)
+    if variant == "guided":
+        case = _guided_variant(case)
     ws = o.Workspace()
     res = ops.idx_score_topk_fused(*_inputs(case), case.page_size, case.max_seq_len, case.k,
                                    return_scores=with_scores, workspace=ws, row_to_batch=_r2b(case), sorted=True)
@@ -531,7 +611,6 @@ def test_fused_sorted_exact_order(ops, variant, with_scores, k):
             m = min(int(case.seq_lens[b]), case.k)
             assert np.array_equal(sc[b][:m].astype(np.float64), scores[b][ref_pos[b][:m]]), b
             assert np.all(np.isneginf(sc[b][m:])), b
-    assert int(ws.buf.count_nonzero()) == 0, "the workspace must be left zero-filled"
 
 
 def test_fused_sorted_random_order(ops):
@@ -541,7 +620,7 @@ def test_fused_sorted_random_order(ops):
 
     case = workloads.indexer_case(650, batch=6, n_lo=1, n_hi=30000, page_size=64, k=2048)
     for big in (False, True):
-        c = _candidate_variant(case) if big else case
+        c = _guided_variant(case) if big else case
         s0, v0 = _fused(ops, c)
         s1, v1 = ops.idx_score_topk_fused(*_inputs(c), c.page_size, c.max_seq_len, c.k, return_scores=True,
                                           row_to_batch=_r2b(c), sorted=True)

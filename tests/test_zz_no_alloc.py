@@ -1,9 +1,9 @@
 """idx_score_topk_fused_noalloc (built-in workspace) against idx_score_topk_fused
 (caller workspace): the same outputs, call after call, on the same GPU.
 
-Two calls in a row, the second with a smaller input, for the score-buffer
-variant (small batches) and the candidate variant (larger ones), plain and
-sorted output; each result also meets the oracle criterion.
+Two calls in a row, the second with a smaller input, for decode-size
+batches and for batches of a few million tokens, plain and sorted output;
+each result also meets the oracle criterion.
 """
 import numpy as np
 import pytest
@@ -44,12 +44,12 @@ def _both(ops, case, sorted_out):
 
 
 @pytest.mark.parametrize("sorted_out", [False, True])
-@pytest.mark.parametrize("variant", ["score-buffer", "candidates"])
+@pytest.mark.parametrize("variant", ["decode", "large"])
 def test_noalloc_equals_workspace_call(ops, variant, sorted_out):
-    if variant == "score-buffer":
+    if variant == "decode":
         cases = [workloads.indexer_case(951, batch=16, n_lo=4000, n_hi=20000, page_size=64, k=1024),
                  workloads.indexer_case(952, batch=5, n_lo=100, n_hi=3000, page_size=64, k=300)]
-    else:  # more than 2^21 tokens per call
+    else:  # about two million tokens per call
         cases = [workloads.indexer_case(953, batch=9, n_lo=200000, n_hi=260000, page_size=64, k=2048),
                  workloads.indexer_case(954, batch=8, n_lo=150000, n_hi=270000, page_size=64, k=512)]
     for i, case in enumerate(cases):
