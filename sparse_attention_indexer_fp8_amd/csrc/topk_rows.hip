@@ -63,6 +63,8 @@ struct RowsArgs {
   int32_t* out;
   int32_t cap;   // candidate buffer entries
   int32_t npow;  // sorted output: power of two >= k (<= cap)
+  int32_t rows;
+  int32_t short_rows;  // rows of at most SR_MAX_N keys take one wave each
 };
 
 __device__ __forceinline__ int32_t map_slot(const int32_t* pt_row, uint32_t pos, uint32_t P,
@@ -491,14 +493,13 @@ __device__ __forceinline__ void sort_emit(const RowCtx& r, const RowsArgs& a, ui
   }
 }
 
+// The whole workgroup selects the k best keys of row `cur` (any length) and
+// writes its output row.
 template <bool SORTED>
-__global__ __launch_bounds__(TR_WG, 4) void topk_rows_kernel(RowsArgs a) {
-  extern __shared__ uint64_t cand[];
-  __shared__ TopkRowsLds s;
+__device__ __forceinline__ void wg_row(const RowsArgs& a, const RowCtx& cur, uint64_t* cand, TopkRowsLds& s) {
   const uint32_t tid = threadIdx.x;
   const uint32_t k = static_cast<uint32_t>(a.k);
   const uint32_t P = static_cast<uint32_t>(a.page_size);
-  const RowCtx cur = row_setup(a, blockIdx.x);
   if (cur.trivial) {
     if (SORTED) {
       // every position is selected: its keys, then the sort
@@ -608,6 +609,249 @@ __global__ __launch_bounds__(TR_WG, 4) void topk_rows_kernel(RowsArgs a) {
   for (uint32_t i = c + tid; i < k; i += TR_WG) cur.out[i] = -1;
 }
 
+// ---------------------------------------------------------------------------
+// Short rows: one wave per row, no workgroup barrier
+// ---------------------------------------------------------------------------
+//
+// A row of at most SR_MAX_N keys (with k <= SR_MAX_K) is read by one wave in
+// quarters of SR_QV float4 vectors, two quarters in flight. The first
+// quarter (plus the scalar head and tail) sets an estimated bound L, as the
+// workgroup path's first tile does: 256 equal-width value bins over the
+// quarter's range, L the lower edge of the bin where the count from the top
+// reaches ~1.5 k n0 / n + 8. Every element >= L goes, as a unique 64-bit
+// key, to the wave's own SR_CAP-entry LDS area by ballot compaction. If
+// between k and SR_CAP keys were kept, L lies at or below the row's k-th
+// value, so every element of the top k is among them: wave_select finds the
+// k-th key T exactly and the keys >= T are emitted. Otherwise the row goes
+// to the workgroup path afterwards.
+
+constexpr int SR_MAX_N = 8192;
+constexpr int SR_MAX_K = 512;
+constexpr int SR_V = 8;                 // float4 per lane per quarter
+constexpr int SR_QV = SR_V * kWave;     // vectors per quarter (2048 floats)
+constexpr int SR_CAP = 1024;            // candidates per wave
+constexpr int SR_PER = SR_CAP / kWave;  // candidates per lane in the select
+constexpr int SR_EMIT = 8;              // outputs per lane per emission round
+constexpr int SR_MIN_ROWS = 2048;       // launches with fewer rows keep a workgroup per row
+static_assert(SR_MAX_N <= 4 * SR_QV * 4, "four quarters cover a short row");
+static_assert(SR_PER % SR_EMIT == 0, "whole emission rounds");
+
+// Returns false when the row needs the workgroup path.
+__device__ __forceinline__ bool short_row(const RowsArgs& a, const RowCtx& r, uint64_t* wc, uint32_t* hist) {
+  const int lane = lane_id();
+  const uint32_t k = static_cast<uint32_t>(a.k);
+  const uint32_t P = static_cast<uint32_t>(a.page_size);
+  const int n = r.n;
+  if (n <= static_cast<int>(k)) {
+    for (int i = lane; i < static_cast<int>(k); i += kWave)
+      r.out[i] = i < n ? map_slot(r.pt_row, static_cast<uint32_t>(i) + r.off, P, a.pdiv) : -1;
+    return true;
+  }
+  // the head / tail element of this lane, if any
+  const bool has_x = lane < r.head + r.ntail;
+  const uint32_t xpos = static_cast<uint32_t>(lane < r.head ? lane : r.tail0 + (lane - r.head));
+  const float xv = has_x ? r.base[xpos] : 0.0f;
+  const int nq = (r.nv + SR_QV - 1) / SR_QV;  // quarters holding vectors (0 .. 4)
+  f4 A[SR_V], B[SR_V];
+  auto load_q = [&](int q, f4 (&X)[SR_V]) {
+#pragma unroll
+    for (int v = 0; v < SR_V; ++v) {
+      int vi = q * SR_QV + v * kWave + lane;
+      vi = vi < r.nv ? vi : r.nv - 1;
+      X[v] = __builtin_nontemporal_load(r.vbase + vi);
+    }
+  };
+  if (nq > 0) load_q(0, A);
+  if (nq > 1) load_q(1, B);
+
+  // Estimated bound from the first quarter and the head / tail elements.
+  const int n0 = 4 * min(r.nv, SR_QV) + r.head + r.ntail;
+  const uint64_t want = (3ull * k * static_cast<uint64_t>(n0) + 2ull * n - 1) / (2ull * n) + 8u;
+  float lf = -__builtin_inff();
+  if (want < static_cast<uint64_t>(n0)) {
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+    auto see = [&](bool ok, float x) {
+      const uint32_t key = ok ? float_key(x) : 0u;
+      kmax = key > kmax ? key : kmax;
+      kmin = ok && key < kmin ? key : kmin;
+    };
+    see(has_x, xv);
+#pragma unroll
+    for (int v = 0; v < SR_V; ++v) {
+      const bool ok = v * kWave + lane < r.nv;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) see(ok, A[v][c]);
+    }
+    const float vmin = key_float(wave_min_u32(kmin)), vmax = key_float(wave_max_u32(kmax));
+    const float width = vmax - vmin;
+    if (width > 0.0f && width < __builtin_inff()) {
+      const float scale = 256.0f / width;
+      reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      auto add = [&](bool ok, float x) {
+        if (ok) {
+          float f = (x - vmin) * scale;
+          f = f < 255.0f ? f : 255.0f;
+          f = f > 0.0f ? f : 0.0f;
+          atomicAdd(&hist[static_cast<uint32_t>(f)], 1u);
+        }
+      };
+      add(has_x, xv);
+#pragma unroll
+      for (int v = 0; v < SR_V; ++v) {
+        const bool ok = v * kWave + lane < r.nv;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) add(ok, A[v][c]);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      const uint4 c4 = reinterpret_cast<const uint4*>(hist)[lane];  // bins 4 lane .. 4 lane + 3
+      const uint32_t cb[4] = {c4.x, c4.y, c4.z, c4.w};
+      const uint32_t local = cb[0] + cb[1] + cb[2] + cb[3];
+      const uint32_t incl = wave_prefix_incl(local);
+      const uint32_t tot = __builtin_amdgcn_readlane(incl, kWave - 1);
+      const uint32_t above = tot - incl;  // counts of higher lanes' bins
+      const uint32_t rank = static_cast<uint32_t>(want);
+      const bool mine = above < rank && above + local >= rank;
+      uint32_t bin = 0;
+      if (mine) {
+        uint32_t acc = above;
+        int i = 3;
+        for (; i > 0; --i) {
+          if (acc + cb[i] >= rank) break;
+          acc += cb[i];
+        }
+        bin = 4 * lane + i;
+      }
+      bin = __builtin_amdgcn_readlane(bin, __builtin_ctzll(ballot(mine)));
+      lf = vmin + static_cast<float>(bin) / scale;
+    }
+  }
+
+  // Keep every element >= lf (ballot compaction; the count is uniform).
+  uint32_t cnt = 0;
+  auto take = [&](bool keep, float x, uint32_t pos) {
+    const uint64_t m = ballot(keep);
+    const uint32_t at = cnt + lanes_below(m);
+    if (keep && at < static_cast<uint32_t>(SR_CAP)) wc[at] = rank_key(float_key(x), pos);
+    cnt += static_cast<uint32_t>(__popcll(m));
+  };
+  auto filter_q = [&](int q, const f4 (&X)[SR_V]) {
+#pragma unroll
+    for (int v = 0; v < SR_V; ++v) {
+      const int vi = q * SR_QV + v * kWave + lane;
+      const bool ok = vi < r.nv;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        take(ok && X[v][c] >= lf, X[v][c], static_cast<uint32_t>(r.head + 4 * vi + c));
+    }
+  };
+  take(has_x && xv >= lf, xv, xpos);
+  if (nq > 0) filter_q(0, A);
+  if (nq > 2) load_q(2, A);
+  if (nq > 1) filter_q(1, B);
+  if (nq > 3) load_q(3, B);
+  if (nq > 2) filter_q(2, A);
+  if (nq > 3) filter_q(3, B);
+  if (cnt < k || cnt > static_cast<uint32_t>(SR_CAP)) return false;
+
+  // The k-th key T of the kept ones, then the keys >= T (exactly k) out.
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  uint64_t keys[SR_PER];
+  bool valid[SR_PER];
+#pragma unroll
+  for (int e = 0; e < SR_PER; ++e) {
+    const uint32_t i = e * kWave + lane;
+    valid[e] = i < cnt;
+    keys[e] = valid[e] ? wc[i] : 0ull;
+  }
+  const uint64_t T = cnt > k ? wave_select<SR_PER>(keys, valid, k, hist) : 0ull;
+  uint32_t at = 0;
+#pragma unroll
+  for (int e0 = 0; e0 < SR_PER; e0 += SR_EMIT) {
+    bool keep[SR_EMIT];
+    uint32_t pos[SR_EMIT], idx[SR_EMIT], pg[SR_EMIT];
+    int32_t page[SR_EMIT];
+#pragma unroll
+    for (int e = 0; e < SR_EMIT; ++e) {
+      keep[e] = valid[e0 + e] && keys[e0 + e] >= T;
+      const uint64_t m = ballot(keep[e]);
+      idx[e] = at + lanes_below(m);
+      at += static_cast<uint32_t>(__popcll(m));
+      pos[e] = rank_pos(keys[e0 + e]) + r.off;
+      pg[e] = keep[e] ? fdiv(pos[e], a.pdiv) : 0u;
+    }
+    if (r.pt_row) {
+      // all lookups issued before any is used; entries not kept read page 0
+#pragma unroll
+      for (int e = 0; e < SR_EMIT; ++e) page[e] = r.pt_row[pg[e]];
+    }
+#pragma unroll
+    for (int e = 0; e < SR_EMIT; ++e)
+      if (keep[e])
+        r.out[idx[e]] = r.pt_row ? static_cast<int32_t>(static_cast<int64_t>(page[e]) * P + (pos[e] - pg[e] * P))
+                                 : static_cast<int32_t>(pos[e]);
+  }
+  return true;
+}
+
+// Short rows are taken four to a workgroup, one wave per row. A group is
+// the rows 32 m + x + 8 j (j = 0..3) for x = row % 8: workgroups are dealt
+// to the 8 XCDs round-robin by index, so a group's rows, and the workgroup
+// that takes them, sit on one XCD, and the groups spread over all eight.
+// Inside an XCD, consecutive workgroups go to its shader engines in turn,
+// so the workgroup that takes a group's short rows is its first short row
+// counting from member m % 4: the taking workgroups then spread over the
+// engines. The group's other short-row workgroups leave at once (a long row
+// keeps its own workgroup). Rows whose estimate failed are then selected by
+// the whole workgroup, one after another.
+__device__ __forceinline__ int group_row(int base, int j) { return base + 8 * j; }
+
+__device__ __forceinline__ void short_group(const RowsArgs& a, uint64_t* cand, TopkRowsLds& s) {
+  const int base = (static_cast<int>(blockIdx.x) / 32) * 32 + static_cast<int>(blockIdx.x) % 8;
+  const int wave = uniform(static_cast<int>(threadIdx.x) / kWave);
+  const int m = static_cast<int>(blockIdx.x) / 32;
+  int leader = -1;
+  bool my_short = false;  // this wave's row is short
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int w = (m + t) & 3;
+    const int row = group_row(base, w);
+    const bool sh = row < a.rows && load_uniform(a.seq_lens + row) <= SR_MAX_N;
+    if (leader < 0 && sh) leader = row;
+    my_short = w == wave ? sh : my_short;
+  }
+  if (leader != static_cast<int>(blockIdx.x)) return;
+  bool ok = true;
+  if (my_short) {
+    const RowCtx r = row_setup(a, group_row(base, wave));
+    ok = short_row(a, r, cand + wave * SR_CAP, s.sel.hist + wave * (kSelBins / 4));
+  }
+  if (lane_id() == 0) s.sel.bcast[wave] = ok ? 0u : 1u;
+  __syncthreads();
+  uint32_t failed = 0;  // bit w: row g0 + w needs the workgroup path
+#pragma unroll
+  for (int w = 0; w < 4; ++w) failed |= s.sel.bcast[w] << w;
+  failed = static_cast<uint32_t>(uniform(static_cast<int>(failed)));
+  __syncthreads();
+  while (failed) {
+    const int w = __builtin_ctz(failed);
+    failed &= failed - 1;
+    wg_row<false>(a, row_setup(a, group_row(base, w)), cand, s);
+    __syncthreads();
+  }
+}
+
+template <bool SORTED>
+__global__ __launch_bounds__(TR_WG, 4) void topk_rows_kernel(RowsArgs a) {
+  extern __shared__ uint64_t cand[];
+  __shared__ TopkRowsLds s;
+  if (!SORTED && a.short_rows && load_uniform(a.seq_lens + blockIdx.x) <= SR_MAX_N) {
+    short_group(a, cand, s);
+    return;
+  }
+  wg_row<SORTED>(a, row_setup(a, blockIdx.x), cand, s);
+}
+
 // Candidate buffer entries: at least two tiles (the first tile is appended
 // whole in the worst case), and k plus one and a half tiles so that a
 // compaction frees at least a quarter tile beyond the next tile.
@@ -653,6 +897,11 @@ int launch_topk_rows(const float* scores, int64_t stride, int rows, const int32_
   a.npow = npow;
   if (sorted && a.cap < npow) a.cap = npow;
   if (!rows_cap_ok(a.cap, k)) return -4;
+  a.rows = rows;
+  // One wave per short row: it takes longer per row than a workgroup does,
+  // so it pays only when there are rows enough to fill the chip (and it
+  // needs four wave areas in the candidate buffer).
+  a.short_rows = !sorted && k <= SR_MAX_K && a.cap >= 4 * SR_CAP && rows >= SR_MIN_ROWS;
   const size_t lds = static_cast<size_t>(a.cap) * sizeof(uint64_t);
   const void* kern = sorted ? reinterpret_cast<const void*>(&topk_rows_kernel<true>)
                             : reinterpret_cast<const void*>(&topk_rows_kernel<false>);

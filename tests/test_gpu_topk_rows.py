@@ -135,6 +135,56 @@ def test_adversarial_rows(ops, k):
         assert np.array_equal(np.sort(got[i]), np.sort(ref[i])), nm
 
 
+@pytest.mark.parametrize("k,page_size,with_offset", [(512, 1, False), (64, 16, True), (300, 1, True)])
+def test_short_rows_one_wave(ops, k, page_size, with_offset):
+    """Launches of 2048 rows or more take rows of at most 8192 keys one wave
+    per row. Every row against the oracle: lengths 1..8192 at odd window
+    starts (so heads and tails are scalar, and some rows have no whole
+    vector), 5% ties, and rows that defeat the wave's estimated bound and go
+    to the workgroup path (ascending, descending, all equal, +-inf, a run of
+    -0.0 / +0.0), with page tables and per-row KV offsets."""
+    import torch
+
+    rows, stride = 2304, 8200
+    g = np.random.default_rng(500 + k)
+    lens = g.integers(1, 8193, size=rows).astype(np.int32)
+    lens[:8] = [1, 2, 3, 5, 6, 7, k, k + 1]
+    starts = g.integers(0, stride - lens + 1).astype(np.int32)
+    buf = np.full((rows, stride), np.inf, np.float32)
+    for i in range(rows):
+        n = int(lens[i])
+        kind = i % 16
+        if kind == 1:
+            v = np.arange(n, dtype=np.float32)
+        elif kind == 2:
+            v = np.arange(n, 0, -1, dtype=np.float32)
+        elif kind == 3:
+            v = np.full(n, 0.25, np.float32)
+        elif kind == 4:
+            v = g.standard_normal(n).astype(np.float32)
+            v[g.random(n) < 0.01] = np.inf
+            v[g.random(n) < 0.01] = -np.inf
+        elif kind == 5:
+            v = np.where(g.random(n) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+        else:
+            v = g.standard_normal(n).astype(np.float32)
+            m = g.random(n) < 0.05
+            v[m] = np.round(v[m] * 16) / 16
+        buf[i, starts[i]:starts[i] + n] = v
+    off = g.integers(0, 1000, size=rows).astype(np.int32) if with_offset else None
+    width = -(-(stride + 1000) // page_size)
+    pt = np.stack([g.permutation(width * 2)[:width] for _ in range(4)]).astype(np.int32)
+    r2b = g.integers(0, 4, size=rows).astype(np.int32)
+    log(f"short rows: rows={rows} k={k} page_size={page_size} offset={with_offset}")
+    out = ops.topk_rows(dev(buf), dev(lens), k, dev(starts), dev(r2b), dev(pt), page_size,
+                        kv_offset=None if off is None else dev(off))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = oracle.topk_rows(buf, lens, k, starts, r2b, pt, page_size, kv_offset=off)
+    bad = [i for i in range(rows) if not np.array_equal(np.sort(got[i]), np.sort(ref[i]))]
+    assert not bad, f"rows differ from the oracle: {bad[:10]}"
+
+
 def test_restream_inside_persistent_loop(ops):
     """More rows than resident workgroups, so each workgroup takes several rows
     in turn: descending rows defeat the estimated first-tile bound and are
