@@ -394,6 +394,30 @@ const char* idxtopk_status_str(int32_t status);
 /* IDXTOPK_VERSION of the loaded library. */
 int32_t idxtopk_version(void);
 
+/*
+ * Checked builds. libidxtopk_checked.so is the same library built with
+ * device-side checks of the caller-owned preconditions listed at the top of
+ * this file and of the library's internal bounds; the kernels otherwise run
+ * as in a release build and their results are the same. A failed check sets
+ * its bit in a device error word:
+ */
+#define IDXTOPK_CHK_WINDOW 0x1         /* topk_rows: a window outside its buffer row */
+#define IDXTOPK_CHK_CAND_OVERFLOW 0x2  /* topk_rows: candidate buffer overrun (internal) */
+#define IDXTOPK_CHK_POSITION 0x4       /* a selected position outside its row (internal) */
+#define IDXTOPK_CHK_SEQ_LEN 0x8        /* seq_lens[b] < 0 or above max_seq_len */
+#define IDXTOPK_CHK_ROW_TO_BATCH 0x10  /* row_to_batch[b] < 0 */
+#define IDXTOPK_CHK_PAGE_ID 0x20       /* a block-table or page-table entry < 0 */
+#define IDXTOPK_CHK_CHUNK_COUNT 0x40   /* fused: chunk candidates above its tokens (internal) */
+#define IDXTOPK_CHK_BLOCK 0x80         /* block top-k: a block outside the row (internal) */
+#define IDXTOPK_CHECKS_OFF 0x80000000u /* a release build: no checks compiled in */
+/*
+ * idxtopk_check_status -- the bits of every check that failed since the
+ * last clear (0: none), after waiting for the current device's queued work.
+ * clear != 0 zeroes the words. A release build returns IDXTOPK_CHECKS_OFF
+ * without touching the device.
+ */
+uint32_t idxtopk_check_status(int32_t clear);
+
 #ifdef __cplusplus
 }
 #endif

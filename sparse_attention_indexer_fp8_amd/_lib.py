@@ -6,11 +6,14 @@ required: if libidxtopk.so has not been built, importing the ops raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libidxtopk.so")
+# the same library built with device-side checks (idxtopk_check_status)
+CHECKED_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libidxtopk_checked.so")
 
 IDXTOPK_OK = 0
 IDXTOPK_EINVAL = -1
@@ -29,6 +32,7 @@ KEY_F32 = 0
 KEY_BF16 = 1
 SORTED = 1
 NOALLOC_SCRATCH_BYTES = 64 << 20
+CHECKS_OFF = 0x80000000
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -59,22 +63,26 @@ SIGNATURES = {
     "idxtopk_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "idxtopk_status_str": (ctypes.c_char_p, [_i32]),
     "idxtopk_version": (_i32, []),
+    "idxtopk_check_status": (ctypes.c_uint32, [_i32]),
 }
 
 _lock = threading.Lock()
-_LIB = None
+_LIBS = {}
+_active = [LIB_PATH]  # the library the ops call (a test may switch it, see using())
 
 
 class LibraryMissing(ImportError):
     pass
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libidxtopk.so and declare its C signatures (raises if not built)."""
-    global _LIB
+def load(path: str = None) -> ctypes.CDLL:
+    """Load a libidxtopk build (default: the one the ops call, normally
+    libidxtopk.so) and declare its C signatures (raises if not built)."""
+    path = _active[0] if path is None else path
     with _lock:
-        if _LIB is not None:
-            return _LIB
+        lib = _LIBS.get(path)
+        if lib is not None:
+            return lib
         if not os.path.exists(path):
             raise LibraryMissing(
                 f"{path} is not built; run `python -m sparse_attention_indexer_fp8_amd.build` "
@@ -84,8 +92,21 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.restype = res
             fn.argtypes = args
-        _LIB = lib
+        _LIBS[path] = lib
         return lib
+
+
+@contextlib.contextmanager
+def using(path: str):
+    """Make the ops call the library at `path` (e.g. CHECKED_LIB_PATH) inside
+    the block."""
+    load(path)
+    prev = _active[0]
+    _active[0] = path
+    try:
+        yield load(path)
+    finally:
+        _active[0] = prev
 
 
 class IdxTopkError(RuntimeError):

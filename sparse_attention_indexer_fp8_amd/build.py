@@ -1,6 +1,6 @@
 """Build libidxtopk.so (HIP, gfx950) in-tree with hipcc.
 
-Usage: python -m sparse_attention_indexer_fp8_amd.build [--debug] [-j N]
+Usage: python -m sparse_attention_indexer_fp8_amd.build [--debug] [--checked] [-j N]
 """
 from __future__ import annotations
 
@@ -17,6 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 SOURCES = ["api.hip", "topk_rows.hip", "page_transform.hip", "indexer.hip", "cache_write.hip", "sort_rows.hip"]
 LIB_NAME = "libidxtopk.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# the same library with device-side checks (IDXTOPK_CHECKS=1)
+CHECKED_LIB_PATH = os.path.join(PKG, "libidxtopk_checked.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
@@ -49,33 +51,40 @@ def _run(cmd):
     return out
 
 
-def build(debug: bool = False, jobs: int = 4, verbose: bool = False) -> str:
+def build(debug: bool = False, jobs: int = 4, verbose: bool = False, checked: bool = False) -> str:
+    """Build libidxtopk.so (or, with checked=True, libidxtopk_checked.so:
+    -O3 plus the device-side checks)."""
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    bdir = os.path.join(BUILD_DIR, "checked") if checked else BUILD_DIR
+    out_path = CHECKED_LIB_PATH if checked else LIB_PATH
+    os.makedirs(bdir, exist_ok=True)
     opt = ["-O1", "-g"] if debug else ["-O3"]
+    if checked:
+        opt = opt + ["-DIDXTOPK_CHECKS=1"]
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         cmds.append([hipcc, *COMMON_FLAGS, *opt, "-c", os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(max(1, jobs)) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
                 print(out)
-    tmp = LIB_PATH + ".tmp"
+    tmp = out_path + ".tmp"
     _run([hipcc, *COMMON_FLAGS, "-shared", *objs, "-o", tmp])
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out_path)
+    return out_path
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--debug", action="store_true")
+    ap.add_argument("--checked", action="store_true", help="build libidxtopk_checked.so (device-side checks)")
     ap.add_argument("-j", "--jobs", type=int, default=4)
     ap.add_argument("-v", "--verbose", action="store_true")
     a = ap.parse_args(argv)
-    path = build(debug=a.debug, jobs=a.jobs, verbose=a.verbose)
+    path = build(debug=a.debug, jobs=a.jobs, verbose=a.verbose, checked=a.checked)
     print(path)
 
 

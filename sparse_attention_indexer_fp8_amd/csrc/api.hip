@@ -341,5 +341,16 @@ const char* idxtopk_status_str(int32_t status) {
 
 int32_t idxtopk_version(void) { return IDXTOPK_VERSION; }
 
+uint32_t idxtopk_check_status(int32_t clear) {
+#if IDXTOPK_CHECKS
+  // synchronous: waits for the device's queued work, then reads the words
+  (void)hipDeviceSynchronize();
+  return idxtopk::check_word_topk_rows(clear != 0) | idxtopk::check_word_indexer(clear != 0);
+#else
+  (void)clear;
+  return IDXTOPK_CHECKS_OFF;
+#endif
+}
+
 }  // extern "C"
 #pragma GCC visibility pop

@@ -9,6 +9,48 @@ namespace idxtopk {
 constexpr int kWave = 64;
 
 // ---------------------------------------------------------------------------
+// Checked builds (IDXTOPK_CHECKS=1, libidxtopk_checked.so): device-side
+// checks of the callers' preconditions and of internal bounds. A failed
+// check sets its bit in this source file's error word (one word per source
+// file: each is its own code object), which idxtopk_check_status reads;
+// the kernels then carry on exactly as a release build does. In a release
+// build a check compiles to nothing and its arguments are not evaluated.
+// ---------------------------------------------------------------------------
+#ifndef IDXTOPK_CHECKS
+#define IDXTOPK_CHECKS 0
+#endif
+
+constexpr uint32_t kChkWindow = 1u << 0;        // topk_rows: a window outside its buffer row
+constexpr uint32_t kChkCandOverflow = 1u << 1;  // topk_rows: candidate buffer overrun
+constexpr uint32_t kChkPosition = 1u << 2;      // a selected position outside its row, before the lookup
+constexpr uint32_t kChkSeqLen = 1u << 3;        // seq_lens[b] < 0 or above max_seq_len
+constexpr uint32_t kChkRowToBatch = 1u << 4;    // row_to_batch[b] < 0
+constexpr uint32_t kChkPageId = 1u << 5;        // a block-table or page-table entry < 0
+constexpr uint32_t kChkChunkCount = 1u << 6;    // fused: a chunk header's count above the chunk's tokens
+constexpr uint32_t kChkBlock = 1u << 7;         // block top-k: a selected block outside the row
+
+#if IDXTOPK_CHECKS
+static __device__ uint32_t g_check_word;
+__device__ __forceinline__ void check_failed(uint32_t bit) { atomicOr(&g_check_word, bit); }
+#define IDXTOPK_CHECK(ok, bit)                  \
+  do {                                          \
+    if (!(ok)) ::idxtopk::check_failed((bit));  \
+  } while (0)
+// This source file's error word (host side; synchronous), cleared if asked.
+static inline uint32_t read_check_word(bool clear) {
+  uint32_t v = 0;
+  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_check_word), sizeof(v)) != hipSuccess) return 0xffffffffu;
+  if (clear) {
+    const uint32_t z = 0;
+    (void)hipMemcpyToSymbol(HIP_SYMBOL(g_check_word), &z, sizeof(z));
+  }
+  return v;
+}
+#else
+#define IDXTOPK_CHECK(ok, bit) ((void)0)
+#endif
+
+// ---------------------------------------------------------------------------
 // Ordered keys
 // ---------------------------------------------------------------------------
 

@@ -172,7 +172,7 @@ __global__ __launch_bounds__(IX_WG) void score_kernel(IndexerArgs a, float* scor
   __shared__ int32_t pages[IX_PAGES];
   int b, c;
   chunk_of(a, b, c);
-  const int n = a.seq_lens[b];
+  const int n = row_len(a, b);
   int tb, clen;
   chunk_span(a, c, tb, clen);
   if (tb >= n) return;
@@ -335,6 +335,7 @@ __global__ __launch_bounds__(PR_WG) void pair_score_kernel(IndexerArgs a, float*
   for (int i = 0; i < 4; ++i) {
     const int b = b0 + (i < nr ? i : 0);
     nn[i] = i < nr ? load_uniform(a.seq_lens + b) : 0;
+    IDXTOPK_CHECK(nn[i] >= 0 && nn[i] <= a.max_seq_len, kChkSeqLen);
     pr[i] = a.row_to_batch ? load_uniform(a.row_to_batch + b) : b;
   }
   const int kb = kc * chunk;
@@ -430,7 +431,7 @@ __global__ __launch_bounds__(IX_WG) void fused_chunk_kernel(IndexerArgs a, Fused
   const int tid = threadIdx.x;
   int b, c;
   chunk_of(a, b, c);
-  const int n = a.seq_lens[b];
+  const int n = row_len(a, b);
   int tb, clen;
   chunk_span(a, c, tb, clen);
   if (tb >= n) return;
@@ -670,7 +671,7 @@ __global__ __launch_bounds__(FM_WG) void fused_merge_kernel(IndexerArgs a, Fused
   const int wave = tid / kWave;
   const int lane = lane_id();
   const int b = blockIdx.x;
-  const int n = a.seq_lens[b];
+  const int n = row_len(a, b);
   const uint32_t k = static_cast<uint32_t>(o.k);
   const uint32_t P = static_cast<uint32_t>(a.page_size);
   uint64_t* cand = ws.cand + static_cast<int64_t>(b) * ws.cap;
@@ -747,6 +748,7 @@ __global__ __launch_bounds__(FM_WG) void fused_merge_kernel(IndexerArgs a, Fused
       if (c < nch) {
         int tb, clen;
         chunk_span(a, c, tb, clen);
+        IDXTOPK_CHECK(h[e].x <= static_cast<uint32_t>(min(clen, n - tb)), kChkChunkCount);
         s.coff[c] = off;
         s.ctb[c] = static_cast<uint32_t>(tb);
         s.ccnt[c] = h[e].x;
@@ -796,6 +798,7 @@ __global__ __launch_bounds__(FM_WG) void fused_merge_kernel(IndexerArgs a, Fused
   // staged in LDS; otherwise the position itself (for the sort pass, or for
   // positions_to_slots below, which batches the block-table lookups).
   auto out_of = [&](uint32_t pos) -> int32_t {
+    IDXTOPK_CHECK(pos < static_cast<uint32_t>(n), kChkPosition);
     if (!pages_staged) return static_cast<int32_t>(pos);
     const uint32_t lp = fdiv(pos, a.pdiv);
     uint32_t x = (static_cast<uint32_t>(s.pages[lp]) - lp) * P;
@@ -1047,7 +1050,7 @@ __global__ __launch_bounds__(IX_WG) void block_chunk_kernel(IndexerArgs a, Block
   const int tid = threadIdx.x;
   int b, c;
   chunk_of(a, b, c);
-  const int n = a.seq_lens[b];
+  const int n = row_len(a, b);
   int tb, clen;
   chunk_span(a, c, tb, clen);
   if (tb >= n) return;
@@ -1114,7 +1117,7 @@ __global__ __launch_bounds__(MG_WG) void block_merge_kernel(IndexerArgs a, Block
   const int tid = threadIdx.x;
   const int sel_row = blockIdx.x;
   const int b = sel_row / o.hp;
-  const int n = a.seq_lens[b];
+  const int n = row_len(a, b);
   const int bs = o.bs;
   const int top = o.top;
   const int nblk = (n + bs - 1) / bs;
@@ -1153,7 +1156,9 @@ __global__ __launch_bounds__(MG_WG) void block_merge_kernel(IndexerArgs a, Block
   const int nsel = min(static_cast<int>(s.ocnt), top);
   const int32_t* bt_row = bt_row_of(a, b);
   for (int i = tid; i < top; i += MG_WG) {
+    IDXTOPK_CHECK(i >= nsel || s.sel_blocks[i] < nblk, kChkBlock);
     const int32_t pb = i < nsel ? bt_row[s.sel_blocks[i]] : -1;
+    IDXTOPK_CHECK(i >= nsel || pb >= 0, kChkPageId);
     o.blocks[static_cast<int64_t>(sel_row) * top + i] = pb;
     s.phys[i] = pb;
   }
@@ -1183,7 +1188,7 @@ __global__ __launch_bounds__(IX_WG) void block_heads_chunk_kernel(IndexerArgs a,
   const int tid = threadIdx.x;
   int b, c;
   chunk_of(a, b, c);
-  const int n = a.seq_lens[b];
+  const int n = row_len(a, b);
   int tb, clen;
   chunk_span(a, c, tb, clen);
   if (tb >= n) return;
@@ -1241,7 +1246,7 @@ __global__ __launch_bounds__(BH_WAVES * kWave) void block_heads_merge_kernel(Ind
   const int sel_row = static_cast<int>(blockIdx.x) * BH_WAVES + wave;
   if (sel_row >= a.batch * o.hp) return;
   const int b = sel_row / o.hp;
-  const int n = a.seq_lens[b];
+  const int n = row_len(a, b);
   const int bs = o.bs;
   const int top = o.top;
   const int nblk = (n + bs - 1) / bs;
@@ -1270,7 +1275,9 @@ __global__ __launch_bounds__(BH_WAVES * kWave) void block_heads_merge_kernel(Ind
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   const int32_t* bt_row = bt_row_of(a, b);
   for (int i = lane; i < top; i += kWave) {
+    IDXTOPK_CHECK(i >= nsel || s.sel[wave][i] < nblk, kChkBlock);
     const int32_t pb = i < nsel ? bt_row[s.sel[wave][i]] : -1;
+    IDXTOPK_CHECK(i >= nsel || pb >= 0, kChkPageId);
     o.blocks[static_cast<int64_t>(sel_row) * top + i] = pb;
     s.phys[wave][i] = pb;
   }
@@ -1301,6 +1308,7 @@ static IndexerArgs make_args(const IndexerInputs& in, int chunk, bool guided = f
   a.seq_lens = in.seq_lens;
   a.batch = in.batch;
   a.heads = in.heads;
+  a.max_seq_len = in.max_seq_len;
   a.chunk = chunk;
   a.quad_map = in.row_to_batch != nullptr && in.batch % 4 == 0 && in.batch >= 8;
   a.cached_keys = 0;
@@ -1364,6 +1372,15 @@ static int choose_chunk(int batch, int max_seq_len, int page_size, int align, in
   } while (0)
 #define IDXTOPK_DISPATCH_NT(KERNEL, bf, heads, grid, stream, ...) \
   IDXTOPK_DISPATCH_NT_LDS(KERNEL, bf, heads, grid, 0, stream, __VA_ARGS__)
+
+uint32_t check_word_indexer(bool clear) {
+#if IDXTOPK_CHECKS
+  return read_check_word(clear);
+#else
+  (void)clear;
+  return 0;
+#endif
+}
 
 int launch_idx_score(const IndexerInputs& in, float* scores, int64_t score_stride, hipStream_t stream) {
   if (in.batch == 0) return 0;

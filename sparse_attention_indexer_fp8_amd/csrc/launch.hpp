@@ -22,6 +22,11 @@ inline hipError_t allow_dynamic_lds(const void* kernel, size_t bytes, std::atomi
   return e;
 }
 
+// Error words of the checked build, one per source file with checks
+// (read, and cleared if asked; 0 in a release build, which has none).
+uint32_t check_word_topk_rows(bool clear);
+uint32_t check_word_indexer(bool clear);
+
 // All return 0 or -4 (launch failure); arguments are already validated.
 int launch_topk_rows(const float* scores, int64_t stride, int rows, const int32_t* seq_lens,
                      const int32_t* row_starts, const int32_t* row_to_batch, const int32_t* kv_offset,

@@ -46,6 +46,7 @@ struct IndexerArgs {
   const int32_t* seq_lens;
   int32_t batch;
   int32_t heads;
+  int32_t max_seq_len;  // the caller's bound on every seq_lens[b]
   int32_t chunk;       // tokens per full-size chunk
   int32_t nchunk_max;  // chunks per row in the grid
   // Guided chunk schedule: chunks [0, n_full) have `chunk` tokens, the next
@@ -72,7 +73,16 @@ struct KeyPieces {
 // Block-table row of query row b (several query rows may share one).
 __device__ __forceinline__ const int32_t* bt_row_of(const IndexerArgs& a, int b) {
   const int prow = a.row_to_batch ? load_uniform(a.row_to_batch + b) : b;
+  IDXTOPK_CHECK(prow >= 0, kChkRowToBatch);
   return a.block_table + static_cast<int64_t>(prow) * a.bt_stride;
+}
+
+// seq_lens[b], the number of visible keys of row b (checked builds check it
+// against the caller's bound).
+__device__ __forceinline__ int row_len(const IndexerArgs& a, int b) {
+  const int n = a.seq_lens[b];
+  IDXTOPK_CHECK(n >= 0 && n <= a.max_seq_len, kChkSeqLen);
+  return n;
 }
 
 template <int NT>
@@ -265,7 +275,10 @@ __device__ __forceinline__ void score_chunk_impl(const IndexerArgs& a, int b, in
   const uint32_t p0 = fdiv(static_cast<uint32_t>(tok_begin), a.pdiv);
   const uint32_t p1 = fdiv(static_cast<uint32_t>(tok_end - 1), a.pdiv);
   const int32_t* bt_row = bt_row_of(a, b);
-  for (int i = tid; i <= static_cast<int>(p1 - p0); i += WG) lds_pages[i] = bt_row[p0 + i];
+  for (int i = tid; i <= static_cast<int>(p1 - p0); i += WG) {
+    lds_pages[i] = bt_row[p0 + i];
+    IDXTOPK_CHECK(lds_pages[i] >= 0, kChkPageId);
+  }
 
   QOperand<NT> qo;
   load_query<NT>(qo, a.q + static_cast<int64_t>(b) * a.heads * kDim,
@@ -469,7 +482,10 @@ __device__ __forceinline__ void score_chunk_bf16_impl(const IndexerArgs& a, int 
   const uint32_t p0 = fdiv(static_cast<uint32_t>(tok_begin), a.pdiv);
   const uint32_t p1 = fdiv(static_cast<uint32_t>(tok_end - 1), a.pdiv);
   const int32_t* bt_row = bt_row_of(a, b);
-  for (int i = tid; i <= static_cast<int>(p1 - p0); i += WG) lds_pages[i] = bt_row[p0 + i];
+  for (int i = tid; i <= static_cast<int>(p1 - p0); i += WG) {
+    lds_pages[i] = bt_row[p0 + i];
+    IDXTOPK_CHECK(lds_pages[i] >= 0, kChkPageId);
+  }
 
   QOperandBF<NT> qo;
   load_query_bf16<NT>(qo, a.q + static_cast<int64_t>(b) * a.heads * kDim * 2, a.w + static_cast<int64_t>(b) * a.heads);
@@ -599,7 +615,10 @@ __device__ __forceinline__ void score_chunk_heads_impl(const IndexerArgs& a, int
   const uint32_t p0 = fdiv(static_cast<uint32_t>(tok_begin), a.pdiv);
   const uint32_t p1 = fdiv(static_cast<uint32_t>(tok_end - 1), a.pdiv);
   const int32_t* bt_row = bt_row_of(a, b);
-  for (int i = tid; i <= static_cast<int>(p1 - p0); i += WG) lds_pages[i] = bt_row[p0 + i];
+  for (int i = tid; i <= static_cast<int>(p1 - p0); i += WG) {
+    lds_pages[i] = bt_row[p0 + i];
+    IDXTOPK_CHECK(lds_pages[i] >= 0, kChkPageId);
+  }
 
   QOperand<NT> qo;
   load_query<NT>(qo, a.q + static_cast<int64_t>(b) * a.heads * kDim,

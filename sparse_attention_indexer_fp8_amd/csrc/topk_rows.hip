@@ -111,6 +111,8 @@ __device__ __forceinline__ RowCtx row_setup(const RowsArgs& a, int row) {
   r.out = a.out + static_cast<int64_t>(row) * a.k;
   r.off = a.kv_offset ? static_cast<uint32_t>(load_uniform(a.kv_offset + row)) : 0u;
   r.trivial = r.n <= a.k;
+  IDXTOPK_CHECK(r.n >= 0 && rs >= 0 && rs + r.n <= a.stride, kChkWindow);
+  IDXTOPK_CHECK(prow >= 0, kChkRowToBatch);
   r.base = a.scores + static_cast<int64_t>(row) * a.stride + rs;
   const uintptr_t addr = reinterpret_cast<uintptr_t>(r.base);
   int head = static_cast<int>(((16u - (addr & 15u)) & 15u) >> 2);
@@ -276,6 +278,7 @@ __device__ __forceinline__ void after_tile(const RowCtx& r, int t, uint32_t k, i
   __syncthreads();
   const uint32_t c = s.cnt;
   __syncthreads();
+  IDXTOPK_CHECK(c <= static_cast<uint32_t>(cap), kChkCandOverflow);
   if (t + 1 == r.ntiles || c <= k || c + TR_TILE <= static_cast<uint32_t>(cap)) return;
   const uint32_t slack = (static_cast<uint32_t>(cap) - TR_TILE - k) / 2;
   const uint64_t T = select_buffer(cand, c, k, slack, s);
@@ -581,6 +584,7 @@ __device__ __forceinline__ void wg_row(const RowsArgs& a, const RowCtx& cur, uin
       const uint32_t i = b0 + j * TR_WG + tid;
       const uint64_t key = cand[i < c ? i : 0];
       keep[j] = i < c && key >= T;
+      IDXTOPK_CHECK(!keep[j] || rank_pos(key) < static_cast<uint32_t>(cur.n), kChkPosition);
       pos[j] = rank_pos(key) + cur.off;
       mine += keep[j];
     }
@@ -595,6 +599,8 @@ __device__ __forceinline__ void wg_row(const RowsArgs& a, const RowCtx& cur, uin
         pg[j] = keep[j] ? fdiv(pos[j], a.pdiv) : 0u;
         base[j] = cur.pt_row[pg[j]];
       }
+#pragma unroll
+      for (int j = 0; j < TR_EMIT; ++j) IDXTOPK_CHECK(!keep[j] || base[j] >= 0, kChkPageId);
     }
 #pragma unroll
     for (int j = 0; j < TR_EMIT; ++j) {
@@ -777,6 +783,7 @@ __device__ __forceinline__ bool short_row(const RowsArgs& a, const RowCtx& r, ui
       const uint64_t m = ballot(keep[e]);
       idx[e] = at + lanes_below(m);
       at += static_cast<uint32_t>(__popcll(m));
+      IDXTOPK_CHECK(!keep[e] || rank_pos(keys[e0 + e]) < static_cast<uint32_t>(n), kChkPosition);
       pos[e] = rank_pos(keys[e0 + e]) + r.off;
       pg[e] = keep[e] ? fdiv(pos[e], a.pdiv) : 0u;
     }
@@ -784,6 +791,8 @@ __device__ __forceinline__ bool short_row(const RowsArgs& a, const RowCtx& r, ui
       // all lookups issued before any is used; entries not kept read page 0
 #pragma unroll
       for (int e = 0; e < SR_EMIT; ++e) page[e] = r.pt_row[pg[e]];
+#pragma unroll
+      for (int e = 0; e < SR_EMIT; ++e) IDXTOPK_CHECK(!keep[e] || page[e] >= 0, kChkPageId);
     }
 #pragma unroll
     for (int e = 0; e < SR_EMIT; ++e)
@@ -872,6 +881,15 @@ static inline int rows_cap(int k) {
 //    gives for any cap above.
 static inline bool rows_cap_ok(int cap, int k) {
   return cap >= TR_TILE + 6 && static_cast<int64_t>(cap) - TR_TILE - k >= 2;
+}
+
+uint32_t check_word_topk_rows(bool clear) {
+#if IDXTOPK_CHECKS
+  return read_check_word(clear);
+#else
+  (void)clear;
+  return 0;
+#endif
 }
 
 int launch_topk_rows(const float* scores, int64_t stride, int rows, const int32_t* seq_lens,

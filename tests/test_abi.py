@@ -20,8 +20,8 @@ def _declared_functions():
 
 def _defines():
     out = {}
-    for m in re.finditer(r"#define\s+(IDXTOPK_[A-Z0-9_]+)\s+\(?(-?\d+)\)?", open(HEADER).read()):
-        out[m.group(1)] = int(m.group(2))
+    for m in re.finditer(r"#define\s+(IDXTOPK_[A-Z0-9_]+)\s+\(?(-?(?:0x[0-9a-fA-F]+|\d+))u?\)?", open(HEADER).read()):
+        out[m.group(1)] = int(m.group(2), 0)
     return out
 
 
@@ -275,3 +275,14 @@ def test_fused_noalloc_validation(lib):
     need = lib.idxtopk_workspace_bytes(_lib.OP_SCORE_TOPK_FUSED, 64, 2048, big)
     assert need > _lib.NOALLOC_SCRATCH_BYTES
     assert call(batch=64, msl=big, k=2048, bts=big // 64) == -3
+
+
+def test_release_build_has_no_checks(lib):
+    """The release library reports that no device-side checks are compiled in
+    (without touching the device); the checked build is a separate file."""
+    from sparse_attention_indexer_fp8_amd import _lib
+
+    d = _defines()
+    assert lib.idxtopk_check_status(0) == _lib.CHECKS_OFF == 0x80000000
+    assert (d["IDXTOPK_CHK_WINDOW"], d["IDXTOPK_CHK_SEQ_LEN"]) == (0x1, 0x8)
+    assert _lib.CHECKED_LIB_PATH != _lib.LIB_PATH
