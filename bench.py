@@ -415,7 +415,26 @@ def bench_prefill(torch, ops, timer, case, warmup, steps):
            "topk": res_t,
            "us_per_call_total": round(s_us + res_t["us_per_launch_mean"], 2),
            "score_buffer_bytes": int(scores.numel() * 4)}
-    del args, scores
+    del scores
+    torch.cuda.empty_cache()
+
+    # The fused call: no score buffer (its workspace holds candidate lists).
+    ws = ops.Workspace()
+    ws_bytes = ops.workspace_bytes(ops._lib.OP_SCORE_TOPK_PREFILL, case.batch, case.k, case.max_seq_len)
+    ws.get(ws_bytes)
+
+    def fused():
+        ops.idx_score_topk_prefill(*args, case.page_size, case.max_seq_len, case.k, workspace=ws, out=out,
+                                   row_to_batch=r2b)
+
+    _, us_f, reg_f = timer.run(fused, warmup, steps, False)
+    f_us = float(reg_f)
+    res["fused"] = {"us_per_call_mean": round(f_us, 2), "us_per_call_median": round(float(np.median(us_f)), 2),
+                    "row_tokens_per_s": round(float(n.sum()) / (f_us * 1e-6), 1),
+                    "score_flops_TFLOPs": round(flops / (f_us * 1e-6) / 1e12, 1),
+                    "workspace_bytes": int(ws_bytes), "score_buffer_bytes": 0,
+                    "settle_launches": timer.settled}
+    del args, ws
     torch.cuda.empty_cache()
     return res
 

@@ -61,6 +61,7 @@ extern "C" {
 #define IDXTOPK_DIM 128           /* index-key / query head dimension */
 #define IDXTOPK_MAX_K_ROWS 8192   /* topk_rows */
 #define IDXTOPK_MAX_K_FUSED 8192  /* idx_score_topk_fused */
+#define IDXTOPK_MAX_K_PREFILL 2048 /* idx_score_topk_prefill */
 
 /* flags of topk_rows and idx_score_topk_fused */
 #define IDXTOPK_SORTED 1  /* each output row in descending score order, equal
@@ -78,6 +79,7 @@ extern "C" {
 #define IDXTOPK_OP_BLOCK_TOPK 5
 #define IDXTOPK_OP_CACHE_WRITE 6
 #define IDXTOPK_OP_BLOCK_TOPK_HEADS 7 /* workspace query with rows = batch * heads */
+#define IDXTOPK_OP_SCORE_TOPK_PREFILL 8
 
 /* Key element types for idx_cache_write. */
 #define IDXTOPK_KEY_F32 0  /* float */
@@ -237,6 +239,43 @@ int idx_score_topk_fused_noalloc(const uint8_t* q, const float* q_scale, const f
                                  const int32_t* row_to_batch, const int32_t* seq_lens, int32_t batch,
                                  int32_t heads, int32_t dim, int32_t max_seq_len, int32_t k,
                                  int32_t* out_slots, float* out_scores, int32_t flags, void* stream);
+
+/*
+ * idx_score_topk_prefill -- fused prefill indexer: score + top-k + page
+ * transform for packed prefill rows, with no score row in HBM.
+ *
+ * The result is idx_score_topk_fused's (same arguments, outputs, flags and
+ * status codes): for every query row b, the top k tokens of
+ * S[b, 0:seq_lens[b]] (ties to the lower position) as physical slots of
+ * block-table row row_to_batch[b]. The query rows of a prefill batch are
+ * packed, request after request, and each keeps the top k of its causal
+ * window ([SGL-37889] Motivation and Modifications: packed prefill rows
+ * addressed through row_to_batch, k = 512, the selection mapped through the
+ * page table); the intermediate score tensor is removed as in
+ * [ATOM-1473]'s fused decode kernel (Pull request overview).
+ *
+ * This path is built for many rows per request: four consecutive rows that
+ * name the same block-table row share every key load. Chunks of each row
+ * keep the tokens above a bound taken from a sample of their own scores;
+ * rows whose bound was too high are scored again in full, so every row is
+ * exact.
+ *
+ * workspace  at least idxtopk_workspace_bytes(IDXTOPK_OP_SCORE_TOPK_PREFILL,
+ *            batch, k, max_seq_len) bytes (about 8 (k + 6 sqrt(k n / 1024)
+ *            + 6 n / 1024) bytes per row for n = max_seq_len, plus
+ *            16 max_seq_len * 8), with any contents: the call reads only
+ *            what it wrote itself. Concurrent calls must not share one
+ *            workspace.
+ * Supported: fp8 cache, heads 16, 32 or 64, page_size a multiple of 16,
+ * 1 <= k <= IDXTOPK_MAX_K_PREFILL; others give IDXTOPK_EUNSUPPORTED.
+ */
+int idx_score_topk_prefill(const uint8_t* q, const float* q_scale, const float* w,
+                           const uint8_t* kcache, const float* k_scale,
+                           const int32_t* block_table, int64_t bt_stride, int32_t page_size,
+                           const int32_t* row_to_batch, const int32_t* seq_lens, int32_t batch,
+                           int32_t heads, int32_t dim, int32_t max_seq_len, int32_t k,
+                           int32_t* out_slots, float* out_scores, void* workspace,
+                           size_t workspace_bytes, int32_t flags, void* stream);
 
 /*
  * block_topk -- block-sparse variant: block scores, top blocks, sparse list.

@@ -28,6 +28,7 @@ OP_SCORE_TOPK_FUSED = 4
 OP_BLOCK_TOPK = 5
 OP_CACHE_WRITE = 6
 OP_BLOCK_TOPK_HEADS = 7
+OP_SCORE_TOPK_PREFILL = 8
 KEY_F32 = 0
 KEY_BF16 = 1
 SORTED = 1
@@ -46,6 +47,8 @@ SIGNATURES = {
     "topk_rows": (_i32, [_vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _i32, _vp]),
     "topk_page_transform": (_i32, [_vp, _i32, _i32, _vp, _i64, _i32, _vp, _vp, _vp]),
     "idx_score_topk_fused": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32,
+                                    _i32, _i32, _i32, _vp, _vp, _vp, _sz, _i32, _vp]),
+    "idx_score_topk_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32,
                                     _i32, _i32, _i32, _vp, _vp, _vp, _sz, _i32, _vp]),
     "idx_score_topk_fused_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _i32, _i32,
                                             _i32, _i32, _i32, _vp, _vp, _i32, _vp]),

@@ -14,7 +14,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["api.hip", "topk_rows.hip", "page_transform.hip", "indexer.hip", "cache_write.hip", "sort_rows.hip"]
+SOURCES = ["api.hip", "topk_rows.hip", "page_transform.hip", "indexer.hip", "cache_write.hip", "sort_rows.hip", "prefill.hip"]
 LIB_NAME = "libidxtopk.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 # the same library with device-side checks (IDXTOPK_CHECKS=1)

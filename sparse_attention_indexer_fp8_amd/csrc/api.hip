@@ -178,6 +178,28 @@ int idx_score_topk_fused_noalloc(const uint8_t* q, const float* q_scale, const f
                                static_cast<hipStream_t>(stream));
 }
 
+int idx_score_topk_prefill(const uint8_t* q, const float* q_scale, const float* w,
+                           const uint8_t* kcache, const float* k_scale, const int32_t* block_table,
+                           int64_t bt_stride, int32_t page_size, const int32_t* row_to_batch,
+                           const int32_t* seq_lens, int32_t batch, int32_t heads, int32_t dim,
+                           int32_t max_seq_len, int32_t k, int32_t* out_slots, float* out_scores,
+                           void* workspace, size_t workspace_bytes, int32_t flags, void* stream) {
+  if (flags & ~IDXTOPK_SORTED) return IDXTOPK_EINVAL;
+  const int st = check_indexer(q, q_scale, w, kcache, k_scale, block_table, bt_stride, page_size,
+                               seq_lens, batch, heads, dim, max_seq_len);
+  if (st != IDXTOPK_OK) return st;
+  if (k <= 0 || (batch > 0 && !out_slots)) return IDXTOPK_EINVAL;
+  if (k > IDXTOPK_MAX_K_PREFILL || page_size % 16 != 0 || (heads != 16 && heads != 32 && heads != 64))
+    return IDXTOPK_EUNSUPPORTED;
+  if (batch == 0) return IDXTOPK_OK;
+  if (!workspace || workspace_bytes < idxtopk::prefill_workspace_bytes(batch, k, max_seq_len))
+    return IDXTOPK_EWORKSPACE;
+  return idxtopk::launch_prefill_fused(pack(q, q_scale, w, kcache, k_scale, block_table, bt_stride,
+                                            page_size, row_to_batch, seq_lens, batch, heads, max_seq_len),
+                                       k, out_slots, out_scores, workspace, (flags & IDXTOPK_SORTED) != 0,
+                                       static_cast<hipStream_t>(stream));
+}
+
 int block_topk(const uint8_t* q, const float* q_scale, const float* w, const uint8_t* kcache,
                const float* k_scale, const int32_t* block_table, int64_t bt_stride,
                int32_t page_size, const int32_t* row_to_batch, const int32_t* seq_lens,
@@ -319,6 +341,9 @@ size_t idxtopk_workspace_bytes(int32_t op, int32_t rows, int32_t k, int32_t max_
   switch (op) {
     case IDXTOPK_OP_SCORE_TOPK_FUSED:
       return rows > 0 ? idxtopk::fused_workspace_bytes(rows, k, max_seq_len) : 0;
+    case IDXTOPK_OP_SCORE_TOPK_PREFILL:
+      if (k <= 0) return 0;
+      return rows > 0 ? idxtopk::prefill_workspace_bytes(rows, k, max_seq_len) : 0;
     case IDXTOPK_OP_BLOCK_TOPK:
     case IDXTOPK_OP_BLOCK_TOPK_HEADS:  // rows = batch * heads
       if (k <= 0) return 0;
@@ -345,7 +370,8 @@ uint32_t idxtopk_check_status(int32_t clear) {
 #if IDXTOPK_CHECKS
   // synchronous: waits for the device's queued work, then reads the words
   (void)hipDeviceSynchronize();
-  return idxtopk::check_word_topk_rows(clear != 0) | idxtopk::check_word_indexer(clear != 0);
+  return idxtopk::check_word_topk_rows(clear != 0) | idxtopk::check_word_indexer(clear != 0) |
+         idxtopk::check_word_prefill(clear != 0);
 #else
   (void)clear;
   return IDXTOPK_CHECKS_OFF;

@@ -126,10 +126,27 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
+// s_waitcnt vmcnt(0): wait until every vector memory operation of the wave
+// has completed (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and
+// lgkmcnt 11:8 left at their maximum). A loop that streams loads ahead must
+// not carry a store into its next iteration: loads and stores share this
+// counter and complete out of order with respect to each other, so the
+// compiler would then wait for every load in flight before the next use.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Inclusive prefix sum across the wave with DPP row shifts and row
 // broadcasts (no LDS traffic).
+// Inclusive prefix sum within each 16-lane row of the wave (DPP row shifts).
+__device__ __forceinline__ uint32_t row16_prefix_incl(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  return x;
+}
+
 __device__ __forceinline__ uint32_t wave_prefix_incl(uint32_t x) {
   x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);  // row_shr:1
   x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false);  // row_shr:2

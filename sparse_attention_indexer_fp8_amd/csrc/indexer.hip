@@ -38,24 +38,15 @@
 #include "launch.hpp"
 #include "score_mfma.hpp"
 #include "select.hpp"
+#include "indexer_shared.hpp"
 
 namespace idxtopk {
 
-constexpr int IX_WG = 256;
-constexpr int IX_RING = 4;  // 16-token key groups in flight per wave
-constexpr int HIST_BITS = 12;
-constexpr int HIST_BINS = 1 << HIST_BITS;
-constexpr int HIST_SHIFT = 32 - HIST_BITS;
-constexpr int FU_CH_MAX = 8192;
-constexpr int IX_PAGES = 512;
-
-static_assert(IX_PAGES <= kMaxChunkPages, "page staging");
 
 // ---------------------------------------------------------------------------
 // Workspace layouts
 // ---------------------------------------------------------------------------
 
-static inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // Fused decode: the candidates of chunk c of row b sit at its own tokens'
 // positions of the row's area, cand[b][tb_c, tb_c + count); hdr[b][c] holds
@@ -205,105 +196,17 @@ __global__ __launch_bounds__(IX_WG) void score_kernel(IndexerArgs a, float* scor
 // element, about as much issue time as the products themselves. Two rows
 // per wave (2 waves per SIMD) ran 5.75 ms, four rows (1 wave per SIMD,
 // 52 AGPRs) 5.61 ms, one row 10.6 ms; issuing the next group's products
-// before the current group's head sums did not help.
+// before the current group's head sums did not help. The key stream itself
+// is RowGroupStream (indexer_shared.hpp).
 
-constexpr int PR_WG = 256;  // 4 waves, each up to 4 rows
-constexpr int PR_RING = 4;  // key groups in flight per wave
-constexpr int PR_CHUNK_PAGES = kWave;
-
-// Score R rows (R = 1, 2 or 4, all reading block-table row bt_row) over the
-// keys [kb, ke) of one chunk; row r's scores go to rows[r][j] for j < n[r].
-template <int NT, int R>
-__device__ __forceinline__ void rows_range(const IndexerArgs& a, const QOperand<NT> (&q)[R], float* const (&rows)[R],
-                                           const int (&n)[R], const int32_t* bt_row, int kb, int ke) {
-  const uint32_t P = static_cast<uint32_t>(a.page_size);
-  const int l = lane_id();
-  const int c = l & 15, g = l >> 4;
-  const uint32_t pg0 = fdiv(static_cast<uint32_t>(kb), a.pdiv);
-  const uint32_t npg = fdiv(static_cast<uint32_t>(ke - 1), a.pdiv) - pg0 + 1;  // <= PR_CHUNK_PAGES
-  const int32_t pv = static_cast<uint32_t>(l) < npg ? bt_row[pg0 + l] : 0;
-  const int ngroups = (ke - kb + kGroup - 1) / kGroup;
-
-  // group gi -> this lane's 32 key bytes in the operand layout (bytes
-  // [32g, 32g + 32) of token c) and the token's scale. The group lies in one
-  // page, and tokens past ke read that page's bytes. Keys come mostly from
-  // the caches here (many rows read them), so the operand layout is loaded
-  // directly rather than as whole lines plus a permute: fewer instructions.
-  auto fetch = [&](int gi, KeyPieces& kp, float& ks) {
-    const int j0 = kb + gi * kGroup;
-    const uint32_t pg = fdiv(static_cast<uint32_t>(j0), a.pdiv);
-    uint32_t m = (static_cast<uint32_t>(__builtin_amdgcn_readlane(pv, pg - pg0)) - pg) * P;
-    asm volatile("" : "+s"(m));
-    const uint32_t s0 = m + static_cast<uint32_t>(j0);
-    const uint8_t* kp0 = a.kcache + (static_cast<uint64_t>(s0 + c) << 7) + 32 * g;
-    kp.x0 = load_v4i_stream(kp0);
-    kp.x1 = load_v4i_stream(kp0 + 16);
-    ks = a.k_scale[s0 + c];
-  };
-  // lane group g holds row (g % R)'s scores; groups g >= R repeat rows
-  float* const dst = rows[g % R];
-  const int nd = n[g % R];
-  const bool writer = g < R;
-  auto consume = [&](int gi, float sc) {
-    const int j = kb + gi * kGroup + c;
-    if (writer && j < nd) dst[j] = sc;
-  };
-  auto score = [&](const KeyPieces& kp, float ks) {
-    v8i kbv;
-    kbv[0] = kp.x0[0]; kbv[1] = kp.x0[1]; kbv[2] = kp.x0[2]; kbv[3] = kp.x0[3];
-    kbv[4] = kp.x1[0]; kbv[5] = kp.x1[1]; kbv[6] = kp.x1[2]; kbv[7] = kp.x1[3];
-    if constexpr (R == 4) return score16x4<NT>(q, kbv, ks);
-    else if constexpr (R == 2) return score16x2<NT>(q[0], q[1], kbv, ks);
-    else return score16<NT>(q[0], kbv, ks);
-  };
-
-  typedef float vks __attribute__((ext_vector_type(PR_RING)));
-  KeyPieces ring[PR_RING];
-  vks ksr;
-  const int gmax = ngroups - 1;
-#pragma unroll
-  for (int u = 0; u < PR_RING; ++u) {
-    float t;
-    fetch(min(u, gmax), ring[u], t);
-    ksr[u] = t;
-  }
-  int gi0 = 0;
-  for (; gi0 + 2 * PR_RING <= ngroups; gi0 += PR_RING) {
-#pragma unroll
-    for (int u = 0; u < PR_RING; ++u) {
-      float sc = score(ring[u], ksr[u]);
-      // the score is final before the slot is refilled (see score_chunk)
-      asm volatile("" : "+v"(sc));
-      __builtin_amdgcn_sched_barrier(0);
-      float t;
-      fetch(gi0 + u + PR_RING, ring[u], t);
-      ksr[u] = t;
-      consume(gi0 + u, sc);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < PR_RING; ++u) {
-    const int gi = gi0 + u;
-    if (gi < ngroups) {
-      const float sc = score(ring[u], ksr[u]);
-      if (gi + PR_RING < ngroups) {
-        float t;
-        fetch(gi + PR_RING, ring[u], t);
-        ksr[u] = t;
-      }
-      consume(gi, sc);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < PR_RING; ++u) {
-    const int gi = gi0 + PR_RING + u;
-    if (gi < ngroups) consume(gi, score(ring[u], ksr[u]));
-  }
-}
+// Scores wait in LDS (PR_STAGE groups per row) and go out together, so
+// stores are in flight into the key stream only once per PR_STAGE groups.
+constexpr int PR_STAGE = 32;
 
 template <int NT, int R>
 __device__ __forceinline__ void score_rows(const IndexerArgs& a, float* scores, int64_t sstride, int b0,
-                                           const int (&nn)[4], const int (&pr)[4], int i0, int kb, int chunk) {
+                                           const int (&nn)[4], const int (&pr)[4], int i0, int kb, int chunk,
+                                           float (&stage)[4][PR_STAGE * kGroup]) {
   QOperand<NT> q[R];
   float* rows[R];
   int n[R];
@@ -318,7 +221,28 @@ __device__ __forceinline__ void score_rows(const IndexerArgs& a, float* scores, 
     nmax = max(nmax, n[r]);
   }
   const int ke = min(kb + chunk, nmax);
-  if (kb < ke) rows_range<NT, R>(a, q, rows, n, a.block_table + static_cast<int64_t>(pr[i0]) * a.bt_stride, kb, ke);
+  if (kb >= ke) return;
+  RowGroupStream<NT, R> st(a, q, a.block_table + static_cast<int64_t>(pr[i0]) * a.bt_stride, kb, ke);
+  // lane group g holds row (g % R)'s scores; groups g >= R repeat rows
+  const int l = lane_id();
+  const int c = l & 15, g = l >> 4;
+  auto in_order = [](int s) { return s; };
+  st.prime(in_order);
+  for (int s0 = 0; s0 < st.ngroups; s0 += PR_STAGE) {
+    const int s1 = min(st.ngroups, s0 + PR_STAGE);
+    st.run(s0, s1, in_order, [&](int s, int, float sc) {
+      if (g < R) stage[g][(s - s0) * kGroup + c] = sc;
+    });
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    const int t0 = kb + s0 * kGroup;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int lim = min(n[r] - t0, (s1 - s0) * kGroup);
+      for (int i = l; i < lim; i += kWave) rows[r][t0 + i] = stage[r][i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    wait_vmem_all();
+  }
 }
 
 template <int NT>
@@ -339,16 +263,18 @@ __global__ __launch_bounds__(PR_WG) void pair_score_kernel(IndexerArgs a, float*
     pr[i] = a.row_to_batch ? load_uniform(a.row_to_batch + b) : b;
   }
   const int kb = kc * chunk;
+  __shared__ float stage[PR_WG / kWave][4][PR_STAGE * kGroup];
+  auto& sw = stage[uniform(static_cast<int>(threadIdx.x) / kWave)];
   if (nr == 4 && pr[0] == pr[1] && pr[1] == pr[2] && pr[2] == pr[3]) {
-    score_rows<NT, 4>(a, scores, sstride, b0, nn, pr, 0, kb, chunk);
+    score_rows<NT, 4>(a, scores, sstride, b0, nn, pr, 0, kb, chunk, sw);
     return;
   }
   for (int i0 = 0; i0 < nr; i0 += 2) {
     if (i0 + 1 < nr && pr[i0] == pr[i0 + 1]) {
-      score_rows<NT, 2>(a, scores, sstride, b0, nn, pr, i0, kb, chunk);
+      score_rows<NT, 2>(a, scores, sstride, b0, nn, pr, i0, kb, chunk, sw);
     } else {
-      score_rows<NT, 1>(a, scores, sstride, b0, nn, pr, i0, kb, chunk);
-      if (i0 + 1 < nr) score_rows<NT, 1>(a, scores, sstride, b0, nn, pr, i0 + 1, kb, chunk);
+      score_rows<NT, 1>(a, scores, sstride, b0, nn, pr, i0, kb, chunk, sw);
+      if (i0 + 1 < nr) score_rows<NT, 1>(a, scores, sstride, b0, nn, pr, i0 + 1, kb, chunk, sw);
     }
   }
 }
@@ -399,12 +325,6 @@ struct ChunkLds {
   uint32_t lcnt2;
 };
 
-struct FusedOut {
-  int32_t* slots;
-  float* scores;
-  int k;
-  int keep_positions;  // leave row-local positions in `slots` (the sort pass maps them)
-};
 
 // How many of its own best tokens a chunk sends to the merge: of the row's n
 // tokens, the chunk holds cnt, so on average mu = k * cnt / n of the row's k
@@ -538,28 +458,6 @@ struct MergeLds {
   uint32_t maxbin;
 };
 
-// Emit this thread's keys with keep[e] set: one output reservation per
-// wave, then out_of(position) (its slot, or the position itself) and the
-// score are stored. All lanes of the wave must call.
-template <int N, class OutOf>
-__device__ __forceinline__ void emit_batch(const uint64_t (&keys)[N], const bool (&keep)[N], int b,
-                                           const FusedOut& o, uint32_t* ocnt, OutOf&& out_of) {
-  uint32_t mine = 0;
-#pragma unroll
-  for (int e = 0; e < N; ++e) mine += keep[e];
-  uint32_t at = wave_reserve(mine, ocnt);
-  const int64_t row = static_cast<int64_t>(b) * o.k;
-#pragma unroll
-  for (int e = 0; e < N; ++e) {
-    if (keep[e]) {
-      if (at < static_cast<uint32_t>(o.k)) {
-        o.slots[row + at] = out_of(rank_pos(keys[e]));
-        if (o.scores) o.scores[row + at] = key_float(rank_vkey(keys[e]));
-      }
-      ++at;
-    }
-  }
-}
 
 // Row b's first nout output entries hold row-local positions written by this
 // workgroup (a barrier must separate the writes from this call): map them to
@@ -1293,65 +1191,6 @@ __global__ __launch_bounds__(BH_WAVES * kWave) void block_heads_merge_kernel(Ind
 // Launchers
 // ---------------------------------------------------------------------------
 
-static IndexerArgs make_args(const IndexerInputs& in, int chunk, bool guided = false, int guide_align = 16) {
-  IndexerArgs a;
-  a.q = in.q;
-  a.q_scale = in.q_scale;
-  a.w = in.w;
-  a.kcache = in.kcache;
-  a.k_scale = in.k_scale;
-  a.block_table = in.block_table;
-  a.row_to_batch = in.row_to_batch;
-  a.bt_stride = in.bt_stride;
-  a.page_size = in.page_size;
-  a.pdiv = make_fastdiv(static_cast<uint32_t>(in.page_size));
-  a.seq_lens = in.seq_lens;
-  a.batch = in.batch;
-  a.heads = in.heads;
-  a.max_seq_len = in.max_seq_len;
-  a.chunk = chunk;
-  a.quad_map = in.row_to_batch != nullptr && in.batch % 4 == 0 && in.batch >= 8;
-  a.cached_keys = 0;
-  const int msl = in.max_seq_len > 0 ? in.max_seq_len : 1;
-  // Guided schedule when quarter chunks stay large (and aligned): full-size
-  // chunks up to half the longest row, halves up to three quarters, then
-  // quarters.
-  const int quarter = chunk / 4;
-  if (guided && chunk % 4 == 0 && quarter >= 1024 && quarter % guide_align == 0 && msl > 2 * chunk) {
-    a.n_full = (msl / 2) / chunk;
-    a.tok_half = a.n_full * chunk;
-    a.n_half = ((msl - a.tok_half) / 2) / (chunk / 2);
-    a.tok_quarter = a.tok_half + a.n_half * (chunk / 2);
-    a.nchunk_max = a.n_full + a.n_half + (msl - a.tok_quarter + quarter - 1) / quarter;
-  } else {
-    a.n_full = (msl + chunk - 1) / chunk;
-    a.n_half = 0;
-    a.tok_half = a.tok_quarter = a.n_full * chunk;
-    a.nchunk_max = a.n_full;
-  }
-  return a;
-}
-
-// Workgroups of a chunk-major grid (chunk_of): every (row, chunk) pair, in
-// whole groups of 32 under quad_map.
-static unsigned chunk_grid(const IndexerArgs& a) {
-  const int64_t n = static_cast<int64_t>(a.nchunk_max) * a.batch;
-  return static_cast<unsigned>(a.quad_map ? (n + 31) / 32 * 32 : n);
-}
-
-// Tokens per workgroup: aim for ~2048 workgroups over the whole batch, keep
-// the chunk's block-table entries within the LDS staging area, keep it a
-// multiple of `align`, and stay within [lo, hi].
-static int choose_chunk(int batch, int max_seq_len, int page_size, int align, int lo, int hi) {
-  const int64_t total = static_cast<int64_t>(batch) * (max_seq_len > 0 ? max_seq_len : 1);
-  int64_t ch = lo;
-  while (ch < hi && total / ch > 2048) ch *= 2;
-  const int64_t page_cap = static_cast<int64_t>(IX_PAGES - 2) * page_size;
-  if (ch > page_cap) ch = page_cap;
-  ch = (ch / align) * align;
-  if (ch < align) ch = align;
-  return static_cast<int>(ch);
-}
 
 #define IDXTOPK_SWITCH_NT(KERNEL, BFV, heads, grid, lds, stream, ...)                                  \
   switch (heads) {                                                                                  \

@@ -26,6 +26,7 @@ inline hipError_t allow_dynamic_lds(const void* kernel, size_t bytes, std::atomi
 // (read, and cleared if asked; 0 in a release build, which has none).
 uint32_t check_word_topk_rows(bool clear);
 uint32_t check_word_indexer(bool clear);
+uint32_t check_word_prefill(bool clear);
 
 // All return 0 or -4 (launch failure); arguments are already validated.
 int launch_topk_rows(const float* scores, int64_t stride, int rows, const int32_t* seq_lens,
@@ -68,6 +69,10 @@ int launch_idx_score(const IndexerInputs& in, float* scores, int64_t score_strid
 size_t fused_workspace_bytes(int rows, int k, int max_seq_len);
 int launch_fused(const IndexerInputs& in, int k, int32_t* out_slots, float* out_scores, void* ws,
                  bool sorted, hipStream_t stream);
+
+size_t prefill_workspace_bytes(int rows, int k, int max_seq_len);
+int launch_prefill_fused(const IndexerInputs& in, int k, int32_t* out_slots, float* out_scores, void* ws,
+                         bool sorted, hipStream_t stream);
 
 size_t block_workspace_bytes(int rows, int block_size, int max_seq_len);
 

@@ -223,23 +223,33 @@ __device__ __forceinline__ float score16x2(const QOperand<NT>& qa, const QOperan
 // results are bit-identical to it.
 template <int NT>
 __device__ __forceinline__ float score16x4(const QOperand<NT> (&q)[4], const v8i kb, float ks) {
-  v4f acc[4][NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-      acc[r][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q[r].a[t], kb, zero, 0, 0, 0, 0, 0, 0);
-    }
-  }
+  // Products i = 4 t + r (row r, head tile t). A wave issues one instruction
+  // at a time, so the vector work of product i - 2 (ReLU and weighted sum,
+  // 8 instructions) is placed after product i: it runs while the matrix
+  // core works on products i - 1 and i, whose results it does not need,
+  // and only about three products' results are live at once. Each row's sum
+  // still runs over t, then the tile's four heads, as in score16.
+  constexpr int N = 4 * NT;
+  v4f acc[N];
   float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto fold = [&](int i) __attribute__((always_inline)) {
+    const int t = i / 4, r = i % 4;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
+    for (int j = 0; j < 4; ++j) p[r] = fmaf(q[r].wt[t][j], relu_bits(acc[i][j]), p[r]);
+  };
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < N; ++i) {
+    const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q[i % 4].a[i / 4], kb, zero, 0, 0, 0, 0, 0, 0);
+    if (i >= 2) fold(i - 2);
+  }
+  fold(N - 2);
+  fold(N - 1);
+  // the order above, for the scheduler: product, then 8 vector instructions
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = fmaf(q[r].wt[t][i], relu_bits(acc[r][t][i]), p[r]);
-    }
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i >= 2) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
   }
   const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(p[0]), __float_as_uint(p[1]), false, false);
   const auto s23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(p[2]), __float_as_uint(p[3]), false, false);

@@ -203,6 +203,30 @@ def idx_score_topk_fused(q, q_scale, w, kcache, k_scale, block_table, seq_lens, 
     return (out, out_scores) if return_scores else out
 
 
+def idx_score_topk_prefill(q, q_scale, w, kcache, k_scale, block_table, seq_lens, page_size: int,
+                           max_seq_len: int, k: int, return_scores: bool = False,
+                           workspace: Optional[Workspace] = None, out: Optional[torch.Tensor] = None,
+                           out_scores: Optional[torch.Tensor] = None, row_to_batch: Optional[torch.Tensor] = None,
+                           sorted: bool = False):
+    """Fused prefill indexer: top-k slots of each packed prefill row (and
+    their scores if asked), with no score row in device memory. Rows are
+    grouped four at a time by their block-table row (row_to_batch) to share
+    key loads. sorted: rows in descending score order, equal scores by
+    ascending position, -1 padding last."""
+    args, B, H, D = _indexer_args(q, q_scale, w, kcache, k_scale, block_table, seq_lens, row_to_batch)
+    if out is None:
+        out = torch.empty((B, k), dtype=torch.int32, device=q.device)
+    if return_scores and out_scores is None:
+        out_scores = torch.empty((B, k), dtype=torch.float32, device=q.device)
+    nbytes = workspace_bytes(_lib.OP_SCORE_TOPK_PREFILL, B, k, max_seq_len)
+    ws = _workspace(workspace).get(nbytes)
+    st = _lib.load().idx_score_topk_prefill(*args, int(page_size), _ptr(row_to_batch), _ptr(seq_lens), B, H, D,
+                                            int(max_seq_len), int(k), _ptr(out), _ptr(out_scores),
+                                            _ptr(ws), ws.numel(), _lib.SORTED if sorted else 0, _stream())
+    _lib.check("idx_score_topk_prefill", st)
+    return (out, out_scores) if return_scores else out
+
+
 def idx_score_topk_fused_noalloc(q, q_scale, w, kcache, k_scale, block_table, seq_lens, page_size: int,
                                  max_seq_len: int, k: int, out: torch.Tensor, out_scores: Optional[torch.Tensor] = None,
                                  row_to_batch: Optional[torch.Tensor] = None, sorted: bool = False):

@@ -37,7 +37,7 @@ def lib():
 def test_header_declares_the_ops():
     names = _declared_functions()
     for op in ("idx_score_fp8", "topk_rows", "idx_score_topk_fused", "topk_page_transform", "block_topk",
-               "idx_cache_write"):
+               "idx_cache_write", "idx_score_topk_prefill"):
         assert op in names
     assert {"idxtopk_workspace_bytes", "idxtopk_status_str", "idxtopk_version"} <= set(names)
 
@@ -138,6 +138,28 @@ def test_fused_validation_and_workspace(lib):
     # the sorted output's score area: rows x k floats on top of the rest
     assert lib.idxtopk_workspace_bytes(4, 32, 2048, 16384) - lib.idxtopk_workspace_bytes(4, 32, 1024, 16384) \
         == 32 * 1024 * 4
+
+
+def test_prefill_validation_and_workspace(lib):
+    """The fused prefill indexer: argument checks and a workspace far below
+    the score buffer it replaces (16384 rows x 70001 fp32 = 4.59 GB)."""
+    rows, k, msl = 16384, 512, 70001
+    need = lib.idxtopk_workspace_bytes(8, rows, k, msl)
+    assert rows * k * 8 < need < rows * msl * 4 // 4
+    assert lib.idxtopk_workspace_bytes(8, rows, 0, msl) == 0
+    small = lib.idxtopk_workspace_bytes(8, 32, 512, 16384)
+    f = lambda k=512, out=FAKE, ws=FAKE, nb=small, flags=0, **kw: lib.idx_score_topk_prefill(
+        *_indexer(**kw), k, out, NULL, ws, nb, flags, NULL)
+    assert f(k=0) == -1
+    assert f(k=2049) == -2
+    assert f(out=NULL) == -1
+    assert f(ws=NULL) == -3
+    assert f(nb=small - 1) == -3
+    assert f(H=128) == -2           # 16, 32 or 64 heads
+    assert f(P=8, bts=2048) == -2   # pages of whole 16-token groups
+    assert f(D=256) == -2
+    assert f(flags=4) == -1
+    assert f(B=0) == 0
 
 
 def test_block_validation(lib):
