@@ -57,7 +57,8 @@ SETTLE_SECONDS = 0.25
 COUNTERS_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "topk_rows": ["topk_rows.hip", "select.hpp", "sort.hpp", "common.hpp"],
-    "fused": ["indexer.hip", "score_mfma.hpp", "select.hpp", "common.hpp"],
+    "fused": ["indexer.hip", "indexer_shared.hpp", "score_mfma.hpp", "select.hpp", "common.hpp"],
+    "prefill": ["prefill.hip", "indexer_shared.hpp", "score_mfma.hpp", "select.hpp", "common.hpp"],
 }
 
 
@@ -85,9 +86,30 @@ def source_hash(kind: str) -> str:
 
 
 PMC_KERNELS = {
-    # counters file name -> (source kind, kernel name prefix, grid size of the workload's launch)
-    "topk_rows_packed_prefill_16384x70001": ("topk_rows", "void idxtopk::topk_rows_kernel<false>", 16384 * 256),
-    "fused_long_decode_B64_k2048": ("fused", "void idxtopk::fused_chunk_kernel", None),
+    # counters file name -> (source kind, kernel name prefix, grid size (threads) of the workload's launch,
+    # the benchmark entry it belongs to)
+    "topk_rows_packed_prefill_16384x70001": ("topk_rows", "void idxtopk::topk_rows_kernel<false>", 16384 * 256,
+                                             None),
+    "fused_long_decode_B64_k2048": ("fused", "void idxtopk::fused_chunk_kernel<4, false>", 1310720,
+                                    "long_decode_B64_k2048"),
+    "fused_decode_B32_chunk": ("fused", "void idxtopk::fused_chunk_kernel<4, false>", 196608,
+                               "fused_decode_B32_k2048"),
+    "fused_decode_B32_merge": ("fused", "void idxtopk::fused_merge_kernel<4, false>", 32768,
+                               "fused_decode_B32_k2048"),
+    "mtp_decode_16x4_chunk": ("fused", "void idxtopk::fused_chunk_kernel<4, false>", 524288,
+                              "mtp_decode_16x4_k2048"),
+    "block_sparse_B64_chunk": ("fused", "void idxtopk::block_chunk_kernel<4, false>", 196608,
+                               "block_sparse_B64_n32768_top32"),
+    "block_sparse_B64_merge": ("fused", "idxtopk::block_merge_kernel", 32768, "block_sparse_B64_n32768_top32"),
+    "block_heads_B64_chunk": ("fused", "void idxtopk::block_heads_chunk_kernel<4>", 524288,
+                              "block_sparse_per_head_B64_H64_top32"),
+    "block_heads_B64_merge": ("fused", "idxtopk::block_heads_merge_kernel", 262144,
+                              "block_sparse_per_head_B64_H64_top32"),
+    "prefill_scores_16384": ("fused", "void idxtopk::pair_score_kernel<4>", 4718592, "prefill_indexer_16384_k512"),
+    "prefill_fused_chunk_16384": ("prefill", "void idxtopk::prefill_chunk_kernel<4>", 4718592,
+                                  "prefill_indexer_16384_k512"),
+    "prefill_fused_merge_16384": ("prefill", "void idxtopk::prefill_merge_kernel", 8388608,
+                                  "prefill_indexer_16384_k512"),
 }
 
 
@@ -111,7 +133,7 @@ def write_counters_from_pmc(fetch_csv: str, write_csv: str, command: str) -> Non
         if not copies:
             raise SystemExit(f"{path}: no 1 GiB copy dispatch to calibrate {counter}")
         factor = (COPY_CALIBRATION_BYTES / 1024) / (sum(copies) / len(copies))
-        for name, (kind, prefix, grid) in PMC_KERNELS.items():
+        for name, (kind, prefix, grid, _) in PMC_KERNELS.items():
             vals = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"].startswith(prefix)
                     and (grid is None or int(r["Grid_Size"]) == grid)]
             if vals:
@@ -344,10 +366,20 @@ def bench_fused_mq(torch, ops, timer, case, warmup, steps, flush):
         ops.idx_score_topk_fused(*args, case.page_size, case.max_seq_len, case.k, workspace=ws, out=out,
                                  row_to_batch=r2b)
 
+    def step_rows():
+        ops.idx_score_topk_prefill(*args, case.page_size, case.max_seq_len, case.k, workspace=ws, out=out,
+                                   row_to_batch=r2b)
+
+    nbytes = indexer_algorithmic_bytes(case, case.batch * case.k)
     wall, us, region = timer.run(step, warmup, steps, flush)
-    res = summary(us, indexer_algorithmic_bytes(case, case.batch * case.k), case.batch, region, timer.settled)
+    res = summary(us, nbytes, case.batch, region, timer.settled)
+    res["call"] = "idx_score_topk_fused (rows of a request dealt to one XCD, keys shared through its L2)"
     res["rows"] = case.batch
     res["row_tokens"] = int(case.seq_lens.astype(np.int64).sum())
+    # the row-group call on the same rows (each key group loaded once for a
+    # request's four rows), for comparison
+    wall, us, region = timer.run(step_rows, warmup, steps, flush)
+    res["row_group_call"] = summary(us, nbytes, case.batch, region, timer.settled)
     del args
     torch.cuda.empty_cache()
     return res
@@ -626,11 +658,14 @@ def main(argv=None):
         c5 = workloads.c5_long_decode()
         log("timing long decode B64 ...")
         also["long_decode_B64_k2048"] = bench_fused(torch, ops, timer, c5, a.warmup, a.steps, False)
-        also["long_decode_B64_k2048"]["chunk_kernel_traffic"] = counter_traffic("fused_long_decode_B64_k2048",
-                                                                                "fused")
         log("timing long decode B64, unfused path ...")
         also["long_decode_B64_k2048_unfused"] = bench_unfused(torch, ops, timer, c5, a.warmup, a.steps, False)
         del c5
+    # HBM bytes per launch of each kernel with committed counters (null when
+    # the kernel's code changed since they were taken)
+    for name, (kind, _, _, key) in PMC_KERNELS.items():
+        if key in also:
+            also[key].setdefault("counter_traffic_bytes", {})[name] = counter_traffic(name, kind)
     if line is None:
         line = {"metric": METRIC, "value": None, "unit": "rows/s", "n_gpus": 1, "steps": a.steps,
                 "warmup": a.warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

@@ -69,18 +69,18 @@ __device__ __forceinline__ void emit_batch(const uint64_t (&keys)[N], const bool
 // lines plus a permute: fewer instructions.
 //
 // Groups are visited in the order gi = order(s), s = 0 .. ngroups - 1 (a
-// permutation of the groups). A ring of PR_RING groups' key loads is kept
-// in flight: slot u holds the group of sequence index s with s % PR_RING ==
-// u, and is refilled with the group PR_RING ahead right after its scores
-// are taken. run() may be called several times over consecutive ranges of
-// s that start at multiples of PR_RING; loads for the next range are
-// already in flight while the caller works between two ranges.
+// permutation of the groups). A ring of RING groups' key loads is kept in
+// flight: slot u holds the group of sequence index s with s % RING == u, and
+// is refilled with the group RING ahead right after its scores are taken.
+// run() may be called several times over consecutive ranges of s that
+// start at multiples of RING; loads for the next range are already in
+// flight while the caller works between two ranges.
 
 constexpr int PR_WG = 256;  // 4 waves, each up to 4 rows
 constexpr int PR_RING = 4;  // key groups in flight per wave
 constexpr int PR_CHUNK_PAGES = kWave;
 
-template <int NT, int R>
+template <int NT, int R, int RING = PR_RING>
 struct RowGroupStream {
   const IndexerArgs& a;
   const QOperand<NT> (&q)[R];
@@ -88,8 +88,8 @@ struct RowGroupStream {
   int32_t pv;
   int kb;
   int ngroups;
-  KeyPieces ring[PR_RING];
-  float ks[PR_RING];
+  KeyPieces ring[RING];
+  float ks[RING];
 
   __device__ __forceinline__ RowGroupStream(const IndexerArgs& a_, const QOperand<NT> (&q_)[R],
                                             const int32_t* bt_row, int kb_, int ke)
@@ -128,15 +128,15 @@ struct RowGroupStream {
     else return score16<NT>(q[0], kbv, ks[u]);
   }
 
-  // Issue the loads of s = 0 .. PR_RING - 1 (repeating the last group when
+  // Issue the loads of s = 0 .. RING - 1 (repeating the last group when
   // there are fewer).
   template <class Order>
   __device__ __forceinline__ void prime(Order&& order) {
 #pragma unroll
-    for (int u = 0; u < PR_RING; ++u) fetch(order(min(u, ngroups - 1)), u);
+    for (int u = 0; u < RING; ++u) fetch(order(min(u, ngroups - 1)), u);
   }
 
-  // consume(s, gi, score) for s in [s0, s1), s0 % PR_RING == 0.
+  // consume(s, gi, score) for s in [s0, s1), s0 % RING == 0.
   template <class Order, class Consume>
   __device__ __forceinline__ void run(int s0, int s1, Order&& order, Consume&& consume) {
     auto step = [&](int s, int u, bool refill) __attribute__((always_inline)) {
@@ -144,19 +144,19 @@ struct RowGroupStream {
       // the score is final before the slot is refilled (see score_chunk)
       asm volatile("" : "+v"(sc));
       __builtin_amdgcn_sched_barrier(0);
-      if (refill) fetch(order(s + PR_RING), u);
+      if (refill) fetch(order(s + RING), u);
       consume(s, order(s), sc);
     };
     int s = s0;
     // refills below ngroups without a check
-    for (; s + PR_RING <= s1 && s + 2 * PR_RING <= ngroups; s += PR_RING) {
+    for (; s + RING <= s1 && s + 2 * RING <= ngroups; s += RING) {
 #pragma unroll
-      for (int u = 0; u < PR_RING; ++u) step(s + u, u, true);
+      for (int u = 0; u < RING; ++u) step(s + u, u, true);
     }
-    for (; s < s1; s += PR_RING) {
+    for (; s < s1; s += RING) {
 #pragma unroll
-      for (int u = 0; u < PR_RING; ++u)
-        if (s + u < s1) step(s + u, u, s + u + PR_RING < ngroups);
+      for (int u = 0; u < RING; ++u)
+        if (s + u < s1) step(s + u, u, s + u + RING < ngroups);
     }
   }
 };

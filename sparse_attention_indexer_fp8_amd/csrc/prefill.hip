@@ -21,8 +21,9 @@
 //     are visited strided first: every S-th group (about 1024 tokens) is the
 //     sample, whose value keys go to LDS. Per row, the sample holds on
 //     average mu = k m / n of the row's k best (m sampled of the row's n
-//     tokens); its r-th best key with r = mu + 6 sqrt(mu) + 6 becomes the
-//     chunk's bound for the row (no bound when r would not fit in the
+//     tokens); a lower bound of its r-th best key with r = mu + 6 sqrt(mu)
+//     + 6 (the edge of a histogram bin, two 256-bin rounds at most) becomes
+//     the chunk's bound for the row (no bound when r would not fit in the
 //     sample or the row has at most k tokens). The chunk then keeps every
 //     token at or above its bound, sampled ones included, as unique 64-bit
 //     keys (value key, inverted position): staged per row in LDS by ballot
@@ -51,10 +52,12 @@
 namespace idxtopk {
 
 constexpr int PF_SAMPLE = 64;       // sampled 16-token groups per (row, chunk), at most
+constexpr int PF_RING = PR_RING;    // key groups in flight per wave
 constexpr int PF_STAGE = 256;       // staged candidates per (wave, row)
 constexpr int PF_MERGE_WG = 512;
 constexpr int PF_MERGE_PER_MAX = 32;
 constexpr int PF_FB_WGS = 16;       // workgroups of the fallback kernel
+constexpr int64_t PF_MIN_WAVES = 2048;  // chunk waves a launch should hold (two per SIMD)
 constexpr int64_t PF_CAP_MAX = static_cast<int64_t>(PF_MERGE_WG) * PF_MERGE_PER_MAX;
 
 #if IDXTOPK_CHECKS
@@ -189,7 +192,7 @@ __device__ __forceinline__ void prefill_rows(const IndexerArgs& a, const Prefill
   }
   const int ke = min(kb + pp.chunk, nmax);
   if (kb >= ke) return;
-  RowGroupStream<NT, R> st(a, q, a.block_table + static_cast<int64_t>(prow) * a.bt_stride, kb, ke);
+  RowGroupStream<NT, R, PF_RING> st(a, q, a.block_table + static_cast<int64_t>(prow) * a.bt_stride, kb, ke);
   const int G = st.ngroups;
   const int S = pp.stride;
   // Visiting order: the sampled groups 0, S, 2S, ... first, then the others
@@ -197,7 +200,7 @@ __device__ __forceinline__ void prefill_rows(const IndexerArgs& a, const Prefill
   const bool whole = G <= PF_SAMPLE;
   const int Se = whole ? 1 : S;
   const int cnt0 = whole ? G : (G + S - 1) / S;
-  const int nA = whole ? G : min(PF_SAMPLE, (cnt0 + PR_RING - 1) / PR_RING * PR_RING);
+  const int nA = whole ? G : min(PF_SAMPLE, (cnt0 + PF_RING - 1) / PF_RING * PF_RING);
   // after the sample, the t-th other group is t + t / (S - 1) + 1 (no
   // branches: both forms are computed and one is selected)
   auto later = [&](int s) -> int {
@@ -231,15 +234,14 @@ __device__ __forceinline__ void prefill_rows(const IndexerArgs& a, const Prefill
   float per_lane = 0.0f;  // expected kept tokens per lane over the other groups (largest row)
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    uint64_t key[SP];
+    uint32_t key[SP];
     bool valid[SP];
     uint32_t mine = 0;
 #pragma unroll
     for (int e = 0; e < SP; ++e) {
       const int i = e * kWave + l;
-      const uint32_t v = i < m_all ? L.samp[r][i] : 0u;
-      valid[e] = v != 0u;
-      key[e] = (static_cast<uint64_t>(v) << 32) | static_cast<uint32_t>(i);
+      key[e] = i < m_all ? L.samp[r][i] : 0u;
+      valid[e] = key[e] != 0u;
       mine += valid[e];
     }
     const uint32_t m = wave_sum(mine);
@@ -249,7 +251,9 @@ __device__ __forceinline__ void prefill_rows(const IndexerArgs& a, const Prefill
       const float mu = static_cast<float>(k) * static_cast<float>(m) / static_cast<float>(n[r]);
       const uint32_t rank = static_cast<uint32_t>(ceilf(mu + 6.0f * sqrtf(mu) + 6.0f));
       if (rank < m) {
-        T[r] = static_cast<uint32_t>(wave_select<SP>(key, valid, rank, L.hist) >> 32);
+        // a lower bound is enough: a few more sampled tokens above it only
+        // lower the bound further
+        T[r] = wave_lower_bound<SP>(key, valid, rank, rank / 8u + 8u, L.hist);
         rank_f = static_cast<float>(rank);
       }
     }
@@ -257,7 +261,7 @@ __device__ __forceinline__ void prefill_rows(const IndexerArgs& a, const Prefill
     per_lane = fmaxf(per_lane, share * static_cast<float>(G - nA));
     kept[r] = 0u;
 #pragma unroll
-    for (int e = 0; e < SP; ++e) kept[r] += valid[e] && static_cast<uint32_t>(key[e] >> 32) >= T[r];
+    for (int e = 0; e < SP; ++e) kept[r] += valid[e] && key[e] >= T[r];
     pre[r] = wave_prefix_incl(kept[r]);
   }
   uint32_t tot = 0u, bnd = 0u;
@@ -547,8 +551,15 @@ int launch_prefill_fused(const IndexerInputs& in, int k, int32_t* out_slots, flo
   o.k = k;
   o.keep_positions = sorted;
 
+  // Chunks of up to PR_CHUNK_PAGES pages (8192 tokens at most), halved
+  // while the grid would hold fewer than PF_MIN_WAVES waves and a chunk
+  // keeps at least 1024 tokens (few rows, e.g. multi-token decode).
   int64_t chunk = static_cast<int64_t>(PR_CHUNK_PAGES) * in.page_size;
   if (chunk > 8192) chunk = 8192 / in.page_size * in.page_size;
+  const int64_t quads = (in.batch + 3) / 4;
+  const int64_t msl = in.max_seq_len > 0 ? in.max_seq_len : 1;
+  while (chunk / 2 >= 1024 && (chunk / 2) % in.page_size == 0 && quads * ((msl + chunk - 1) / chunk) < PF_MIN_WAVES)
+    chunk /= 2;
   const IndexerArgs a = make_args(in, static_cast<int>(chunk), false);
   PrefillParams pp;
   pp.k = k;
@@ -556,8 +567,7 @@ int launch_prefill_fused(const IndexerInputs& in, int k, int32_t* out_slots, flo
   const int gfull = static_cast<int>(chunk / kGroup);
   pp.stride = (gfull + PF_SAMPLE - 1) / PF_SAMPLE;
   pp.sdiv1 = make_fastdiv(static_cast<uint32_t>(pp.stride > 1 ? pp.stride - 1 : 1));  // S - 1 (1 when S = 1)
-  const int quads = (in.batch + 3) / 4;
-  pp.ntiles = (quads + PR_WG / kWave - 1) / (PR_WG / kWave);
+  pp.ntiles = static_cast<int>((quads + PR_WG / kWave - 1) / (PR_WG / kWave));
   const int nkc = static_cast<int>((static_cast<int64_t>(in.max_seq_len > 0 ? in.max_seq_len : 1) + chunk - 1) / chunk);
 
   (void)hipGetLastError();

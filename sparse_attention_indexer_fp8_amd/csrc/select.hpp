@@ -250,6 +250,69 @@ __device__ __forceinline__ uint64_t wave_select(const uint64_t (&key)[PER], cons
   return lo;
 }
 
+// A lower bound T for the rank-th largest of at most PER * 64 32-bit keys
+// held by one wave (key[e] counts where valid[e]; 1 <= rank <= their
+// number): at least `rank` keys are >= T, and at most rank + slack unless
+// two rounds were not enough to narrow it. Each round histograms the keys
+// of the current range [lo, hi] into 256 equal bins (the `hist` words of
+// LDS that only this wave uses) and keeps the bin where the count from the
+// top reaches the remaining rank; T is that bin's lower edge. Wave-
+// synchronous, no barrier (the wave's LDS operations complete in order).
+template <int PER>
+__device__ __forceinline__ uint32_t wave_lower_bound(const uint32_t (&key)[PER], const bool (&valid)[PER],
+                                                     uint32_t rank, uint32_t slack, uint32_t* hist) {
+  const int lane = lane_id();
+  uint32_t lo = ~0u, hi = 0u;
+#pragma unroll
+  for (int e = 0; e < PER; ++e)
+    if (valid[e]) {
+      lo = key[e] < lo ? key[e] : lo;
+      hi = key[e] > hi ? key[e] : hi;
+    }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  uint32_t kk = rank;
+  for (int it = 0; it < 2; ++it) {
+    const uint32_t span = hi - lo;
+    if (span == 0u) break;
+    const int bits = 32 - __clz(span);
+    const int shift = bits > 8 ? bits - 8 : 0;
+    reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+      if (valid[e] && key[e] >= lo && key[e] <= hi) atomicAdd(&hist[(key[e] - lo) >> shift], 1u);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    const uint4 c4 = reinterpret_cast<const uint4*>(hist)[lane];  // bins 4 lane .. 4 lane + 3
+    const uint32_t c[4] = {c4.x, c4.y, c4.z, c4.w};
+    const uint32_t local = c[0] + c[1] + c[2] + c[3];
+    const uint32_t incl = wave_prefix_incl(local);
+    const uint32_t tot = __builtin_amdgcn_readlane(incl, kWave - 1);
+    const uint32_t above_l = tot - incl;  // keys in the bins of higher lanes
+    const bool mine = above_l < kk && above_l + local >= kk;
+    uint32_t bin = 0, above = above_l, cnt = 0;
+    if (mine) {
+      int i = 3;
+      for (; i > 0; --i) {
+        if (above + c[i] >= kk) break;
+        above += c[i];
+      }
+      bin = 4 * lane + i;
+      cnt = c[i];
+    }
+    const int src = __builtin_ctzll(ballot(mine));
+    bin = __builtin_amdgcn_readlane(bin, src);
+    above = __builtin_amdgcn_readlane(above, src);
+    cnt = __builtin_amdgcn_readlane(cnt, src);
+    kk -= above;
+    lo += bin << shift;
+    const uint32_t top = lo + ((1u << shift) - 1u);
+    hi = top < hi ? top : hi;
+    if (cnt - kk <= slack) break;  // keys >= lo: (rank - kk) + cnt
+  }
+  return lo;
+}
+
 // Threshold bin of a histogram for rank k: the highest bin b with
 // sum(bins >= b) >= k. Returns above = sum(bins > b) and the total count.
 // When total < k, returns bin 0 with all=true (everything is selected).

@@ -231,3 +231,24 @@ def test_prefill_fused_full_size(ops):
 
     n = _fullsize.run(_fullsize.fused_rows_task, tasks(), case.name + " fused")
     assert n == case.batch
+
+
+@pytest.mark.timeout(600)
+def test_prefill_call_on_multi_token_decode_full_size(ops):
+    """The multi-token decode workload (16 requests x 4 query rows, contexts
+    16K..64K, k 2048) through the row-group call, as the benchmark times it
+    (small chunks: few row quads): every row against the oracle criterion,
+    and the same selection as the per-row fused call (same fp32 scores)."""
+    from tests import _fullsize
+
+    case = workloads.mtp_decode()
+    log(f"mtp through the row-group call: rows={case.batch} max n={case.max_seq_len}")
+    slots, sc = _prefill(ops, case)
+    import torch
+
+    ref, _ = ops.idx_score_topk_fused(*_inputs(case), case.page_size, case.max_seq_len, case.k, return_scores=True,
+                                      row_to_batch=dev(case.row_to_batch))
+    torch.cuda.synchronize()
+    assert np.array_equal(np.sort(slots, axis=1), np.sort(ref.cpu().numpy(), axis=1))
+    n = _fullsize.run(_fullsize.fused_rows_task, _fullsize.fused_tasks(case, slots, sc), case.name + " row-group")
+    assert n == case.batch
