@@ -165,7 +165,8 @@ constexpr int PF_LIST = 32;
 
 struct PrefillWaveLds {
   union {
-    uint32_t samp[4][PF_SAMPLE * kGroup];  // sampled value keys per row (0: no token)
+    uint32_t samp[4][PF_SAMPLE * kGroup + kGroup];  // sampled value keys per row (0: no token); rows
+                                                    // padded so the four rows' lanes write distinct banks
     struct {
       float sc[PF_LIST * kWave];           // then: lane l's kept scores at [i * 64 + l]
       uint32_t gi[PF_LIST * kWave];        // and their groups
