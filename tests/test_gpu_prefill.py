@@ -252,3 +252,45 @@ def test_prefill_call_on_multi_token_decode_full_size(ops):
     assert np.array_equal(np.sort(slots, axis=1), np.sort(ref.cpu().numpy(), axis=1))
     n = _fullsize.run(_fullsize.fused_rows_task, _fullsize.fused_tasks(case, slots, sc), case.name + " row-group")
     assert n == case.batch
+
+
+def test_prefill_edge_shapes(ops):
+    """Shapes at the edges of the row-group call, each against the oracle's
+    exact selection on exact inputs: every row empty; max_seq_len 0; no
+    row_to_batch (each row its own block-table row: rows scored one at a
+    time); a batch that is not a multiple of four; k above every row's
+    length; a single row."""
+    import torch
+
+    base = _exactify(_prefill_case(820, 3, 7, 1, 5000, 64, 300, heads=16), 820)
+
+    def run(case, k, r2b=True):
+        slots, sc = ops.idx_score_topk_prefill(*_inputs(case), case.page_size, case.max_seq_len, k,
+                                               return_scores=True,
+                                               row_to_batch=dev(case.row_to_batch) if r2b else None)
+        torch.cuda.synchronize()
+        return slots.cpu().numpy(), sc.cpu().numpy()
+
+    # every row empty (max_seq_len kept), then max_seq_len 0
+    import copy
+
+    empty = copy.copy(base)
+    empty.seq_lens = np.zeros_like(base.seq_lens)
+    for msl in (base.max_seq_len, 0):
+        empty.max_seq_len = msl
+        slots, sc = run(empty, 300)
+        assert (slots == -1).all() and (sc == -np.inf).all(), msl
+    # no row_to_batch: the block table expanded to one row per query row
+    flat = copy.copy(base)
+    flat.block_table = np.ascontiguousarray(base.block_table[base.row_to_batch])
+    flat.row_to_batch = np.arange(base.batch, dtype=np.int32)
+    slots, sc = run(flat, 300, r2b=False)
+    _check_exact(flat, slots, sc, 300)
+    # 21 rows (not a multiple of 4), one row, and k above every length
+    short = _exactify(_prefill_case(821, 3, 7, 1, 1500, 64, 2048, heads=16), 821)
+    for case, rows, k in ((base, base.batch, 300), (base, 1, 300), (short, short.batch, 2048)):
+        part = copy.copy(case)
+        part.q, part.q_scale, part.w = case.q[:rows], case.q_scale[:rows], case.w[:rows]
+        part.seq_lens, part.row_to_batch = case.seq_lens[:rows], case.row_to_batch[:rows]
+        slots, sc = run(part, k)
+        _check_exact(part, slots, sc, k)
