@@ -185,10 +185,11 @@ __global__ __launch_bounds__(IX_WG) void score_kernel(IndexerArgs a, float* scor
 // together (score16x4), so lane group g ends up holding row g's scores and
 // every lane stores. If the four rows do not share a block-table row, the
 // wave scores pairs (score16x2) or single rows instead. The grid is
-// chunk-major, so all workgroups stream the same 64-page key chunk at about
-// the same time and share it through the caches. A chunk's page ids sit one
-// per lane in a VGPR, so a group's page is one readlane: no LDS and no
-// barrier. Used when pages hold whole 16-token groups (page_size % 16 == 0).
+// chunk-major, so all workgroups stream the same key chunk (up to 128 pages,
+// 8192 tokens) at about the same time and share it through the caches. A
+// chunk's page ids sit in VGPRs, two per lane, so a group's page is a
+// readlane: no LDS and no barrier. Used when pages hold whole 16-token
+// groups (page_size % 16 == 0).
 //
 // On the packed-prefill geometry (16384 rows, 573M row-keys) the four-row
 // path runs at ~1.67 PFLOP/s of fp8 products, a third of the matrix peak;

@@ -62,8 +62,8 @@ __device__ __forceinline__ void emit_batch(const uint64_t (&keys)[N], const bool
 // loaded once and goes through the MFMA core against all R queries
 // (score16x4 / score16x2 / score16), so lane (g, c) = (lane / 16, lane % 16)
 // ends up holding row (g % R)'s score of the group's token c. The chunk's
-// page ids sit one per lane in a VGPR (at most 64 pages), so a group's page
-// is one readlane: no LDS and no barrier. Pages hold whole 16-token groups
+// page ids sit in two VGPRs, two per lane (at most 128 pages), so a group's
+// page is a readlane: no LDS and no barrier. Pages hold whole 16-token groups
 // (page_size % 16 == 0). Keys come mostly from the caches here (many rows
 // read them), so the operand layout is loaded directly rather than as whole
 // lines plus a permute: fewer instructions.
@@ -78,14 +78,14 @@ __device__ __forceinline__ void emit_batch(const uint64_t (&keys)[N], const bool
 
 constexpr int PR_WG = 256;  // 4 waves, each up to 4 rows
 constexpr int PR_RING = 4;  // key groups in flight per wave
-constexpr int PR_CHUNK_PAGES = kWave;
+constexpr int PR_CHUNK_PAGES = 2 * kWave;  // page ids of a chunk: two per lane
 
 template <int NT, int R, int RING = PR_RING>
 struct RowGroupStream {
   const IndexerArgs& a;
   const QOperand<NT> (&q)[R];
   uint32_t pg0;
-  int32_t pv;
+  int32_t pv0, pv1;  // the chunk's page ids: page i at lane i (pv0) or i - 64 (pv1)
   int kb;
   int ngroups;
   KeyPieces ring[RING];
@@ -97,7 +97,8 @@ struct RowGroupStream {
     const int l = lane_id();
     pg0 = fdiv(static_cast<uint32_t>(kb), a.pdiv);
     const uint32_t npg = fdiv(static_cast<uint32_t>(ke - 1), a.pdiv) - pg0 + 1;  // <= PR_CHUNK_PAGES
-    pv = static_cast<uint32_t>(l) < npg ? bt_row[pg0 + l] : 0;
+    pv0 = static_cast<uint32_t>(l) < npg ? bt_row[pg0 + l] : 0;
+    pv1 = static_cast<uint32_t>(l + kWave) < npg ? bt_row[pg0 + kWave + l] : 0;
     ngroups = (ke - kb + kGroup - 1) / kGroup;
   }
 
@@ -110,7 +111,10 @@ struct RowGroupStream {
     const uint32_t P = static_cast<uint32_t>(a.page_size);
     const int j0 = kb + gi * kGroup;
     const uint32_t pg = fdiv(static_cast<uint32_t>(j0), a.pdiv);
-    uint32_t m = (static_cast<uint32_t>(__builtin_amdgcn_readlane(pv, pg - pg0)) - pg) * P;
+    const uint32_t i = pg - pg0;
+    const uint32_t page = i < static_cast<uint32_t>(kWave) ? __builtin_amdgcn_readlane(pv0, i)
+                                                           : __builtin_amdgcn_readlane(pv1, i - kWave);
+    uint32_t m = (page - pg) * P;
     asm volatile("" : "+s"(m));
     const uint32_t s0 = m + static_cast<uint32_t>(j0);
     const uint8_t* kp0 = a.kcache + (static_cast<uint64_t>(s0 + c) << 7) + 32 * g;
