@@ -106,7 +106,7 @@ PMC_KERNELS = {
     "block_heads_B64_merge": ("fused", "idxtopk::block_heads_merge_kernel", 262144,
                               "block_sparse_per_head_B64_H64_top32"),
     "prefill_scores_16384": ("fused", "void idxtopk::pair_score_kernel<4>", 4718592, "prefill_indexer_16384_k512"),
-    "prefill_fused_chunk_16384": ("prefill", "void idxtopk::prefill_chunk_kernel<4>", 4718592,
+    "prefill_fused_chunk_16384": ("prefill", "void idxtopk::prefill_chunk_kernel<4, false>", 4718592,
                                   "prefill_indexer_16384_k512"),
     "prefill_fused_merge_16384": ("prefill", "void idxtopk::prefill_merge_kernel", 8388608,
                                   "prefill_indexer_16384_k512"),

@@ -153,7 +153,58 @@ struct PrefillParams {
   int stride;     // S: one sampled group in S (1 when a chunk has at most PF_SAMPLE groups)
   FastDiv sdiv1;  // division by S - 1 (by 1 when S = 1)
   int ntiles;     // workgroups per chunk
+  int balanced;   // nonzero: waves take (quad, chunk) pairs of the balanced schedule (prefill_chunk_kernel<NT, true>)
 };
+
+// Balanced schedule for calls of few rows (at most PF_BAL_QUADS quads, e.g.
+// multi-token decode). A chunk-major grid over max_seq_len leaves the waves
+// past each request's context idle and gives the others whole chunks of
+// PF_SAMPLE groups. Here every wave reads the quads' lengths (lane q: quad
+// q's longest row), sizes the chunks from the actual total of 16-token
+// groups so that the grid's waves share it evenly (at most PF_SAMPLE groups,
+// so a chunk is all sample), and takes the i-th (quad, chunk) pair in quad
+// order. Every wave computes the same schedule on its own: no LDS, no
+// barrier.
+constexpr int PF_BAL_QUADS = kWave;
+
+// ceil(x / d) for x < 2^24 and d >= 1, from a float estimate corrected by one
+// step each way (rd = 1 / d up to rounding).
+__device__ __forceinline__ uint32_t ceil_div_small(uint32_t x, uint32_t d, float rd) {
+  const uint32_t y = x + d - 1u;
+  uint32_t q = static_cast<uint32_t>(static_cast<float>(y) * rd);
+  q -= q * d > y;
+  q += (q + 1u) * d <= y;
+  return q;
+}
+
+// Pair of wave index i: quad `quad`, keys from kb, `chunk` tokens per chunk.
+// Returns false past the last pair. The pairs number at most the grid's
+// waves W: with g = ceil(G / (W - nq)) groups per chunk, the quads' chunks
+// number at most G / g + nq <= W; with g capped at PF_SAMPLE, at most nq
+// ceil(max_seq_len / (16 PF_SAMPLE)), which the host's grid holds.
+__device__ __forceinline__ bool balanced_pair(const IndexerArgs& a, uint32_t i, int& quad, int& kb, int& chunk) {
+  const int l = lane_id();
+  const int nq = (a.batch + 3) / 4;
+  uint32_t gq = 0u;  // 16-token groups of quad l's longest row
+  if (l < nq) {
+    int m = 0;
+    for (int r = 0; r < 4 && 4 * l + r < a.batch; ++r) m = max(m, row_len(a, 4 * l + r));
+    gq = static_cast<uint32_t>((m + kGroup - 1) / kGroup);
+  }
+  const uint32_t G = wave_sum(gq);
+  const uint32_t W = gridDim.x * (PR_WG / kWave);
+  uint32_t g = (G + (W - nq) - 1u) / (W - nq);
+  g = g < 1u ? 1u : g > static_cast<uint32_t>(PF_SAMPLE) ? static_cast<uint32_t>(PF_SAMPLE) : g;
+  const uint32_t nc = gq > 0u ? ceil_div_small(gq, g, 1.0f / static_cast<float>(g)) : 0u;
+  const uint32_t incl = wave_prefix_incl(nc);
+  if (i >= __builtin_amdgcn_readlane(incl, kWave - 1)) return false;
+  const bool here = incl - nc <= i && i < incl;
+  const int src = static_cast<int>(__builtin_ctzll(ballot(here)));
+  quad = src;
+  kb = static_cast<int>((i - __builtin_amdgcn_readlane(incl - nc, src)) * g * kGroup);
+  chunk = static_cast<int>(g * kGroup);
+  return true;
+}
 
 // Per-lane lists of kept tokens: PF_LIST entries (score, group) per lane.
 // A wave whose rows keep more than PF_LIST / 4 tokens per lane on average
@@ -172,11 +223,11 @@ struct PrefillWaveLds {
       uint32_t gi[PF_LIST * kWave];        // and their groups
     } list;
   };
-  alignas(16) uint32_t hist[256];          // wave_select
+  alignas(16) uint32_t hist[256];          // wave_lower_bound
 };
 
 // Rows b0 + i0 .. + R - 1 (one block-table row, prow) over the chunk at kb.
-template <int NT, int R>
+template <int NT, int R, int RING>
 __device__ __forceinline__ void prefill_rows(const IndexerArgs& a, const PrefillWs& w, const PrefillParams& pp,
                                              PrefillWaveLds& L, int b0, const int (&nn)[4], int i0, int prow,
                                              int kb) {
@@ -193,7 +244,8 @@ __device__ __forceinline__ void prefill_rows(const IndexerArgs& a, const Prefill
   }
   const int ke = min(kb + pp.chunk, nmax);
   if (kb >= ke) return;
-  RowGroupStream<NT, R, PF_RING> st(a, q, a.block_table + static_cast<int64_t>(prow) * a.bt_stride, kb, ke);
+  static_assert(PF_LIST % RING == 0, "list segments start at multiples of the ring");
+  RowGroupStream<NT, R, RING> st(a, q, a.block_table + static_cast<int64_t>(prow) * a.bt_stride, kb, ke);
   const int G = st.ngroups;
   const int S = pp.stride;
   // Visiting order: the sampled groups 0, S, 2S, ... first, then the others
@@ -201,7 +253,7 @@ __device__ __forceinline__ void prefill_rows(const IndexerArgs& a, const Prefill
   const bool whole = G <= PF_SAMPLE;
   const int Se = whole ? 1 : S;
   const int cnt0 = whole ? G : (G + S - 1) / S;
-  const int nA = whole ? G : min(PF_SAMPLE, (cnt0 + PF_RING - 1) / PF_RING * PF_RING);
+  const int nA = whole ? G : min(PF_SAMPLE, (cnt0 + RING - 1) / RING * RING);
   // after the sample, the t-th other group is t + t / (S - 1) + 1 (no
   // branches: both forms are computed and one is selected)
   auto later = [&](int s) -> int {
@@ -231,7 +283,7 @@ __device__ __forceinline__ void prefill_rows(const IndexerArgs& a, const Prefill
   constexpr int SP = PF_SAMPLE * kGroup / kWave;  // sample entries per lane
   const uint32_t k = static_cast<uint32_t>(pp.k);
   const int m_all = nA * kGroup;
-  uint32_t T[R], pre[R], kept[R];
+  uint32_t T[R], pre[R], kept[R], kbits[R];
   float per_lane = 0.0f;  // expected kept tokens per lane over the other groups (largest row)
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -260,9 +312,11 @@ __device__ __forceinline__ void prefill_rows(const IndexerArgs& a, const Prefill
     }
     const float share = m > 0u ? rank_f / static_cast<float>(m) : 1.0f;
     per_lane = fmaxf(per_lane, share * static_cast<float>(G - nA));
-    kept[r] = 0u;
+    // this lane's sampled tokens at or above the bound, as a bit mask
+    kbits[r] = 0u;
 #pragma unroll
-    for (int e = 0; e < SP; ++e) kept[r] += valid[e] && key[e] >= T[r];
+    for (int e = 0; e < SP; ++e) kbits[r] |= (valid[e] && key[e] >= T[r] ? 1u : 0u) << e;
+    kept[r] = static_cast<uint32_t>(__builtin_popcount(kbits[r]));
     pre[r] = wave_prefix_incl(kept[r]);
   }
   uint32_t tot = 0u, bnd = 0u;
@@ -282,15 +336,13 @@ __device__ __forceinline__ void prefill_rows(const IndexerArgs& a, const Prefill
     if (__builtin_amdgcn_readlane(pre[r], kWave - 1) == 0u) continue;
     uint32_t at = __builtin_amdgcn_readlane(base, r) + pre[r] - kept[r];
     uint64_t* dst = w.cand + static_cast<int64_t>(b0 + i0 + r) * w.cap;
-#pragma unroll
-    for (int e = 0; e < SP; ++e) {
-      const int i = e * kWave + l;
-      const uint32_t v = i < m_all ? L.samp[r][i] : 0u;
-      if (v != 0u && v >= T[r]) {
-        const int j = kb + order(i >> 4) * kGroup + (i & 15);
-        if (at < static_cast<uint32_t>(w.cap)) dst[at] = rank_key(v, static_cast<uint32_t>(j));
-        ++at;
-      }
+    // only this lane's kept entries (a few), not all SP of them
+    for (uint32_t bits = kbits[r]; bits != 0u; bits &= bits - 1u) {
+      const int i = __builtin_ctz(bits) * kWave + l;
+      const uint32_t v = L.samp[r][i];
+      const int j = kb + order(i >> 4) * kGroup + (i & 15);
+      if (at < static_cast<uint32_t>(w.cap)) dst[at] = rank_key(v, static_cast<uint32_t>(j));
+      ++at;
     }
   }
   float my_thr = thr[0];
@@ -342,13 +394,18 @@ __device__ __forceinline__ void prefill_rows(const IndexerArgs& a, const Prefill
   }
 }
 
-template <int NT>
+template <int NT, bool BAL>
 __global__ __launch_bounds__(PR_WG) void prefill_chunk_kernel(IndexerArgs a, PrefillWs w, PrefillParams pp) {
   __shared__ PrefillWaveLds lds[PR_WG / kWave];
-  const int tile = blockIdx.x % pp.ntiles;
-  const int kc = blockIdx.x / pp.ntiles;
+  constexpr int RING = PF_RING;
   const int wave = uniform(static_cast<int>(threadIdx.x) / kWave);
-  const int quad = tile * (PR_WG / kWave) + wave;
+  int quad, kb;
+  if constexpr (BAL) {
+    if (!balanced_pair(a, blockIdx.x * (PR_WG / kWave) + wave, quad, kb, pp.chunk)) return;
+  } else {
+    quad = static_cast<int>(blockIdx.x % pp.ntiles) * (PR_WG / kWave) + wave;
+    kb = static_cast<int>(blockIdx.x / pp.ntiles) * pp.chunk;
+  }
   const int b0 = 4 * quad;
   if (b0 >= a.batch) return;
   const int nr = min(4, a.batch - b0);
@@ -361,18 +418,17 @@ __global__ __launch_bounds__(PR_WG) void prefill_chunk_kernel(IndexerArgs a, Pre
     pr[i] = a.row_to_batch ? load_uniform(a.row_to_batch + b) : b;
     IDXTOPK_CHECK(pr[i] >= 0, kChkRowToBatch);
   }
-  const int kb = kc * pp.chunk;
   PrefillWaveLds& L = lds[wave];
   if (nr == 4 && pr[0] == pr[1] && pr[1] == pr[2] && pr[2] == pr[3]) {
-    prefill_rows<NT, 4>(a, w, pp, L, b0, nn, 0, pr[0], kb);
+    prefill_rows<NT, 4, RING>(a, w, pp, L, b0, nn, 0, pr[0], kb);
     return;
   }
   for (int i0 = 0; i0 < nr; i0 += 2) {
     if (i0 + 1 < nr && pr[i0] == pr[i0 + 1]) {
-      prefill_rows<NT, 2>(a, w, pp, L, b0, nn, i0, pr[i0], kb);
+      prefill_rows<NT, 2, RING>(a, w, pp, L, b0, nn, i0, pr[i0], kb);
     } else {
-      prefill_rows<NT, 1>(a, w, pp, L, b0, nn, i0, pr[i0], kb);
-      if (i0 + 1 < nr) prefill_rows<NT, 1>(a, w, pp, L, b0, nn, i0 + 1, pr[i0 + 1], kb);
+      prefill_rows<NT, 1, RING>(a, w, pp, L, b0, nn, i0, pr[i0], kb);
+      if (i0 + 1 < nr) prefill_rows<NT, 1, RING>(a, w, pp, L, b0, nn, i0 + 1, pr[i0 + 1], kb);
     }
   }
 }
@@ -541,6 +597,19 @@ __global__ __launch_bounds__(IX_WG) void prefill_fallback_kernel(IndexerArgs a, 
 // Launcher
 // ---------------------------------------------------------------------------
 
+// SIMDs of the current device (four per compute unit), cached per device.
+static int64_t prefill_simds() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    cache[dev] = 4 * cus;
+  }
+  return cache[dev];
+}
+
 int launch_prefill_fused(const IndexerInputs& in, int k, int32_t* out_slots, float* out_scores, void* ws,
                          bool sorted, hipStream_t stream) {
   if (in.batch == 0) return 0;
@@ -570,15 +639,33 @@ int launch_prefill_fused(const IndexerInputs& in, int k, int32_t* out_slots, flo
   pp.sdiv1 = make_fastdiv(static_cast<uint32_t>(pp.stride > 1 ? pp.stride - 1 : 1));  // S - 1 (1 when S = 1)
   pp.ntiles = static_cast<int>((quads + PR_WG / kWave - 1) / (PR_WG / kWave));
   const int nkc = static_cast<int>((static_cast<int64_t>(in.max_seq_len > 0 ? in.max_seq_len : 1) + chunk - 1) / chunk);
+  // Few quads: the balanced schedule over a grid of at least one wave per
+  // SIMD, and at least nq chunks of PF_SAMPLE groups per quad's bound.
+  pp.balanced = quads <= PF_BAL_QUADS;
+  int64_t nwg = static_cast<int64_t>(pp.ntiles) * nkc;
+  if (pp.balanced) {
+    const int64_t full = quads * ((msl + PF_SAMPLE * kGroup - 1) / (PF_SAMPLE * kGroup));
+    int64_t waves = prefill_simds();
+    if (waves < full) waves = full;
+    if (waves < 2 * quads) waves = 2 * quads;
+    nwg = (waves + PR_WG / kWave - 1) / (PR_WG / kWave);
+  }
 
   (void)hipGetLastError();
   hipLaunchKernelGGL(prefill_zero_kernel, dim3((in.batch + 255) / 256), dim3(256), 0, stream, w, in.batch);
-  const dim3 grid(static_cast<unsigned>(pp.ntiles * nkc));
-  switch (in.heads) {
-    case 16: hipLaunchKernelGGL(prefill_chunk_kernel<1>, grid, dim3(PR_WG), 0, stream, a, w, pp); break;
-    case 32: hipLaunchKernelGGL(prefill_chunk_kernel<2>, grid, dim3(PR_WG), 0, stream, a, w, pp); break;
-    default: hipLaunchKernelGGL(prefill_chunk_kernel<4>, grid, dim3(PR_WG), 0, stream, a, w, pp); break;
+  const dim3 grid(static_cast<unsigned>(nwg));
+#define IDXTOPK_PF_CHUNK(BAL)                                                                                 \
+  switch (in.heads) {                                                                                         \
+    case 16: hipLaunchKernelGGL((prefill_chunk_kernel<1, BAL>), grid, dim3(PR_WG), 0, stream, a, w, pp); break; \
+    case 32: hipLaunchKernelGGL((prefill_chunk_kernel<2, BAL>), grid, dim3(PR_WG), 0, stream, a, w, pp); break; \
+    default: hipLaunchKernelGGL((prefill_chunk_kernel<4, BAL>), grid, dim3(PR_WG), 0, stream, a, w, pp); break; \
   }
+  if (pp.balanced) {
+    IDXTOPK_PF_CHUNK(true)
+  } else {
+    IDXTOPK_PF_CHUNK(false)
+  }
+#undef IDXTOPK_PF_CHUNK
   const int64_t per = (w.cap + PF_MERGE_WG - 1) / PF_MERGE_WG;
   const dim3 rows(static_cast<unsigned>(in.batch));
   if (per <= 2) hipLaunchKernelGGL(prefill_merge_kernel<2>, rows, dim3(PF_MERGE_WG), 0, stream, a, w, o);

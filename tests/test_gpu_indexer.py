@@ -321,11 +321,15 @@ def test_fused_dirty_workspace(ops):
 
 
 @pytest.mark.parametrize("page_size,k,n_lo,n_hi,batch", [(64, 2048, 1, 20000, 6), (16, 300, 100, 9000, 5),
-                                                         (1, 64, 1, 3000, 4)])
+                                                         (1, 64, 1, 3000, 4), (16, 64, 0, 700, 300),
+                                                         (64, 100, 0, 3000, 40)])
 def test_fused_equals_unfused(ops, page_size, k, n_lo, n_hi, batch):
     """idx_score_fp8 then topk_rows through the block table (the unfused
     path) computes the same fp32 score per token as the fused kernels, so
-    both fused variants select exactly its set, ties included."""
+    both chunk schedules of the fused path (chunks sized for one resident
+    wave of workgroups, and the guided schedule of the large max_seq_len
+    variant) select exactly its set, ties included, also for batches with
+    empty rows and a batch of 300 short rows."""
     import torch
 
     case = workloads.indexer_case(800 + k, batch=batch, n_lo=n_lo, n_hi=n_hi, page_size=page_size, k=k)
