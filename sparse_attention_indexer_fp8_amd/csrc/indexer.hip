@@ -660,9 +660,9 @@ __global__ __launch_bounds__(FM_WG) void fused_merge_kernel(IndexerArgs a, Fused
   }
   __syncthreads();
   const bool gathered = staged && total <= static_cast<uint32_t>(MG_BUF);
-  // Place the loaded candidates: into LDS when they all fit, else into the
-  // histogram (of the candidates' bins); then load what the first loads did
-  // not cover (chunks that sent more than `spec`), one wave per chunk.
+  // Place the loaded candidates: into the histogram of their bins, and into
+  // LDS when they all fit; then load what the first loads did not cover
+  // (chunks that sent more than `spec`), one wave per chunk.
   if (staged) {
 #pragma unroll
     for (int e = 0; e < MG_SPEC; ++e) {
@@ -670,7 +670,7 @@ __global__ __launch_bounds__(FM_WG) void fused_merge_kernel(IndexerArgs a, Fused
       split(e * FM_WG + tid, c, j);
       if (c < nch && static_cast<uint32_t>(j) < s.ccnt[c]) {
         if (gathered) s.buf[s.coff[c] + j] = sk[e];
-        else atomicAdd(&s.hist[rank_vkey(sk[e]) >> HIST_SHIFT], 1u);
+        atomicAdd(&s.hist[rank_vkey(sk[e]) >> HIST_SHIFT], 1u);
       }
     }
     for (int c = wave; c < nch; c += FM_WG / kWave) {
@@ -680,7 +680,7 @@ __global__ __launch_bounds__(FM_WG) void fused_merge_kernel(IndexerArgs a, Fused
       for (uint32_t j = spec + lane; j < cnt; j += kWave) {
         const uint64_t key = cand[tb + j];
         if (gathered) s.buf[off + j] = key;
-        else atomicAdd(&s.hist[rank_vkey(key) >> HIST_SHIFT], 1u);
+        atomicAdd(&s.hist[rank_vkey(key) >> HIST_SHIFT], 1u);
       }
     }
   }
@@ -705,95 +705,62 @@ __global__ __launch_bounds__(FM_WG) void fused_merge_kernel(IndexerArgs a, Fused
     return static_cast<int32_t>(x + pos);
   };
 
-  // Candidates in LDS: the exact k-th key T among them by an adaptive
-  // radix select (bins spread over the candidates' own range). The selection
-  // is the row's when T's bin is at or above every chunk's bound (each chunk
-  // sent all of its tokens in bins >= its bound, so every token >= T is a
-  // candidate), or, with at most k candidates, when every token was sent.
-  bool done = false;      // selected and emitted from LDS
-  uint32_t lo_bin = 0u;   // rescoring keeps the tokens in bins >= lo_bin
-  if (gathered) {
-    uint64_t T = 0;
-    bool ok;
-    if (total > k) {
-      uint64_t mn = ~0ull, mx = 0;
-      lds_for_each<FM_WG, 4>(s.buf, total, [&](uint64_t x) {
-        mn = x < mn ? x : mn;
-        mx = x > mx ? x : mx;
-      });
-      wg_range<FM_WG>(mn, mx, s.sel);
-      T = wg_select<FM_WG>([&](auto&& f) { lds_for_each<FM_WG, 4>(s.buf, total, f); }, k, mn, mx, s.sel);
-      ok = (rank_vkey(T) >> HIST_SHIFT) >= s.maxbin;
-      lo_bin = rank_vkey(T) >> HIST_SHIFT;  // T is at or below the row's k-th best key
-    } else {
-      ok = total == static_cast<uint32_t>(n);
-    }
-    if (ok) {
-      for (uint32_t i0 = 0; i0 < total; i0 += FM_WG * MG_BATCH) {
-        uint64_t key[MG_BATCH];
-        bool keep[MG_BATCH];
-#pragma unroll
-        for (int j = 0; j < MG_BATCH; ++j) {
-          const uint32_t i = i0 + j * FM_WG + tid;
-          key[j] = i < total ? s.buf[i] : 0ull;
-          keep[j] = i < total && key[j] >= T;
-        }
-        emit_batch<MG_BATCH>(key, keep, b, o, &s.ocnt, out_of);
-      }
-      done = true;
-    }
-  }
-  CandSource src{nullptr, nullptr, cand, s.coff, s.ctb, nch};
+  // The threshold bin: the bin of the candidates' k-th best key, from the
+  // histogram of their bins. The selection is the row's when that bin is at
+  // or above every chunk's bound (each chunk sent all of its tokens in bins
+  // >= its bound, so every token of the row in bins above it, and every
+  // token of the bin at or above the k-th key, is a candidate), or, with at
+  // most k candidates, when every token was sent. Then the keys above the
+  // bin are emitted and those in it selected exactly, from LDS when the
+  // candidates were gathered there, else from the chunks' ranges.
+  CandSource src{gathered ? s.buf : nullptr, nullptr, cand, s.coff, s.ctb, nch};
   uint32_t ncand = total;
   BinThreshold th{0u, 0u, 0u, true};
-  if (!done) {
-    bool ok = false;
-    if (staged && !gathered) {
-      // too many candidates for LDS: threshold bin from their histogram
-      uint32_t h8[MG_HPER];
-      own_bins<MG_HPER>(s.hist, h8);
-      th = wg_threshold_counts<FM_WG, MG_HPER>(h8, k, s.scratch);
-      ok = th.all ? total == static_cast<uint32_t>(n) : th.bin >= s.maxbin;
-      lo_bin = th.all ? 0u : th.bin;
-    }
-    if (!ok && n > 0) {
-      // Score the row again and keep every token in bins >= lo_bin: the
-      // candidates' k-th best key is at or below the row's k-th best, so no
-      // token of the row's top k is dropped.
-      __syncthreads();
-      for (int i = tid; i < HIST_BINS; i += FM_WG) s.hist[i] = 0;
-      if (tid == 0) s.fcnt = 0;
-      int32_t* spages = reinterpret_cast<int32_t*>(s.buf);
-      const int64_t span64 = (static_cast<int64_t>(IX_PAGES - 2) * a.page_size) / kGroup * kGroup;
-      const int span = static_cast<int>(span64 > kGroup ? span64 : kGroup);
-      for (int t0 = 0; t0 < n; t0 += span) {
-        const int t1 = min(n, t0 + span);
-        score_chunk_any<BF, NT, FM_WG, 1, true>(a, b, t0, t1, spages, [&](int j, float v, bool valid) {
-          const uint32_t key = float_key(v);
-          const bool keep = valid && (key >> HIST_SHIFT) >= lo_bin;
-          const uint64_t mk = ballot(keep);
-          if (mk) {
-            uint32_t base = 0;
-            if (lane_id() == 0) base = atomicAdd(&s.fcnt, static_cast<uint32_t>(__popcll(mk)));
-            base = uniform(base);
-            if (keep) {
-              cand[base + lanes_below(mk)] = rank_key(key, static_cast<uint32_t>(j));
-              atomicAdd(&s.hist[key >> HIST_SHIFT], 1u);
-            }
+  bool ok = false;
+  uint32_t lo_bin = 0u;  // rescoring keeps the tokens in bins >= lo_bin
+  if (staged) {
+    uint32_t h8[MG_HPER];
+    own_bins<MG_HPER>(s.hist, h8);
+    th = wg_threshold_counts<FM_WG, MG_HPER>(h8, k, s.scratch);
+    ok = th.all ? total == static_cast<uint32_t>(n) : th.bin >= s.maxbin;
+    lo_bin = th.all ? 0u : th.bin;  // the candidates' k-th best key is at or below the row's
+  }
+  if (!ok && n > 0) {
+    // Score the row again and keep every token in bins >= lo_bin: the
+    // candidates' k-th best key is at or below the row's k-th best, so no
+    // token of the row's top k is dropped.
+    __syncthreads();
+    for (int i = tid; i < HIST_BINS; i += FM_WG) s.hist[i] = 0;
+    if (tid == 0) s.fcnt = 0;
+    int32_t* spages = reinterpret_cast<int32_t*>(s.buf);
+    const int64_t span64 = (static_cast<int64_t>(IX_PAGES - 2) * a.page_size) / kGroup * kGroup;
+    const int span = static_cast<int>(span64 > kGroup ? span64 : kGroup);
+    for (int t0 = 0; t0 < n; t0 += span) {
+      const int t1 = min(n, t0 + span);
+      score_chunk_any<BF, NT, FM_WG, 1, true>(a, b, t0, t1, spages, [&](int j, float v, bool valid) {
+        const uint32_t key = float_key(v);
+        const bool keep = valid && (key >> HIST_SHIFT) >= lo_bin;
+        const uint64_t mk = ballot(keep);
+        if (mk) {
+          uint32_t base = 0;
+          if (lane_id() == 0) base = atomicAdd(&s.fcnt, static_cast<uint32_t>(__popcll(mk)));
+          base = uniform(base);
+          if (keep) {
+            cand[base + lanes_below(mk)] = rank_key(key, static_cast<uint32_t>(j));
+            atomicAdd(&s.hist[key >> HIST_SHIFT], 1u);
           }
-        });
-        __syncthreads();  // the staged pages are replaced by the next span's
-      }
-      ncand = s.fcnt;
-      src = CandSource{nullptr, cand, cand, s.coff, s.ctb, 0};
-      uint32_t h8[MG_HPER];
-      own_bins<MG_HPER>(s.hist, h8);
-      th = wg_threshold_counts<FM_WG, MG_HPER>(h8, k, s.scratch);
+        }
+      });
+      __syncthreads();  // the staged pages are replaced by the next span's
     }
+    ncand = s.fcnt;
+    src = CandSource{nullptr, cand, cand, s.coff, s.ctb, 0};
+    uint32_t h8[MG_HPER];
+    own_bins<MG_HPER>(s.hist, h8);
+    th = wg_threshold_counts<FM_WG, MG_HPER>(h8, k, s.scratch);
   }
   const uint32_t bstar = th.all ? 0u : th.bin;
   const uint32_t need = th.all ? 0u : k - th.above;
-  if (done) ncand = 0;  // nothing left to classify
 
   // Classify: keys above the threshold bin (all keys when the row holds at
   // most k) are emitted, keys inside it go to LDS (over the histogram).
