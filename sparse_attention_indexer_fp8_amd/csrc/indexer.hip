@@ -292,10 +292,20 @@ constexpr int MG_MAXE = MG_MID / FM_WG;
 constexpr int MG_CHUNKS = 1024;   // chunk headers of a row held in LDS
 constexpr int MG_BATCH = 8;       // candidates per thread per pass of the merge
 constexpr int WS_PER = 16;        // threshold-bin keys per lane when one wave selects
+constexpr int MG_SUB_BITS = 8;    // sub-bins of the threshold bin: the next 8 bits of the value key
+constexpr int MG_SUB = 1 << MG_SUB_BITS;
+static_assert(MG_SUB == 4 * kWave, "one wave scans the sub-histogram, four sub-bins per lane");
+static_assert(FM_WG <= kWave * WS_PER, "wave 0 holds a threshold bin of one key per thread");
+static_assert(MG_CHUNKS >= MG_SUB, "the sub-histogram reuses the chunk counts");
 
 static_assert(HIST_BINS == 16 * IX_WG, "16 histogram bins per thread");
 constexpr int MG_HPER = HIST_BINS / FM_WG;  // histogram bins per merge thread
 static_assert(MG_HPER % 4 == 0, "whole 16-byte histogram reads");
+
+// Sub-bin of a candidate key inside its histogram bin.
+__device__ __forceinline__ uint32_t sub_bin(uint64_t key) {
+  return (rank_vkey(key) >> (HIST_SHIFT - MG_SUB_BITS)) & static_cast<uint32_t>(MG_SUB - 1);
+}
 
 // The PER counts of bins [PER t, PER t + PER) of an LDS histogram, for
 // thread t (16-byte reads).
@@ -450,7 +460,7 @@ struct MergeLds {
   int32_t pages[MG_PAGES];       // the row's block-table entries (rows of at most MG_PAGES pages)
   uint32_t coff[MG_CHUNKS + 1];  // first candidate of each chunk in the gathered order
   uint32_t ctb[MG_CHUNKS];       // first token of each chunk
-  uint32_t ccnt[MG_CHUNKS];      // candidates of each chunk
+  alignas(16) uint32_t ccnt[MG_CHUNKS];  // candidates of each chunk (then the sub-histogram)
   SelectLds sel;
   uint32_t scratch[24];
   uint32_t ocnt;
@@ -713,6 +723,11 @@ __global__ __launch_bounds__(FM_WG) void fused_merge_kernel(IndexerArgs a, Fused
   // most k candidates, when every token was sent. Then the keys above the
   // bin are emitted and those in it selected exactly, from LDS when the
   // candidates were gathered there, else from the chunks' ranges.
+  // The chunk counts are not read again: their words hold the threshold
+  // bin's sub-histogram (the next MG_SUB_BITS bits of the value key), built
+  // while classifying (the barriers below order the clearing before it).
+  uint32_t* sub = s.ccnt;
+  for (int i = tid; i < MG_SUB; i += FM_WG) sub[i] = 0u;
   CandSource src{gathered ? s.buf : nullptr, nullptr, cand, s.coff, s.ctb, nch};
   uint32_t ncand = total;
   BinThreshold th{0u, 0u, 0u, true};
@@ -788,26 +803,70 @@ __global__ __launch_bounds__(FM_WG) void fused_merge_kernel(IndexerArgs a, Fused
       if (mid[j]) {
         if (at < static_cast<uint32_t>(MG_MID)) s.mid[at] = key[j];
         ++at;
+        atomicAdd(&sub[sub_bin(key[j])], 1u);
       }
     }
   }
   __syncthreads();
   const uint32_t nb = s.mcnt;
-  if (!th.all && nb > 0 && nb <= static_cast<uint32_t>(kWave * WS_PER)) {
-    // a small threshold bin: wave 0 alone selects and emits it
-    if (tid < kWave) {
+  if (!th.all && nb > 0 && nb <= static_cast<uint32_t>(FM_WG)) {
+    // A threshold bin of at most one key per thread. Its sub-histogram gives
+    // the sub-bin sb holding the need-th key from the top (every wave finds
+    // it on its own): keys in higher sub-bins are taken, and need2 of the
+    // cnt2 keys of sb: all of them, or the best need2 by their rank among
+    // them (gathered in LDS), or, when more than kSelMembers keys share sb
+    // (equal scores), by an exact select in wave 0.
+    const uint4 c4 = reinterpret_cast<const uint4*>(sub)[lane];  // sub-bins 4 lane .. 4 lane + 3
+    const uint32_t cb[4] = {c4.x, c4.y, c4.z, c4.w};
+    const uint32_t local = cb[0] + cb[1] + cb[2] + cb[3];
+    const uint32_t incl = wave_prefix_incl(local);
+    const uint32_t above_l = __builtin_amdgcn_readlane(incl, kWave - 1) - incl;
+    const bool mine = above_l < need && above_l + local >= need;
+    uint32_t sbl = 0u, above2 = above_l, cnt2 = 0u;
+    if (mine) {
+      int i = 3;
+      for (; i > 0; --i) {
+        if (above2 + cb[i] >= need) break;
+        above2 += cb[i];
+      }
+      sbl = 4u * static_cast<uint32_t>(lane) + static_cast<uint32_t>(i);
+      cnt2 = cb[i];
+    }
+    const int srcl = __builtin_ctzll(ballot(mine));
+    const uint32_t sb = __builtin_amdgcn_readlane(sbl, srcl);
+    const uint32_t need2 = need - __builtin_amdgcn_readlane(above2, srcl);
+    cnt2 = __builtin_amdgcn_readlane(cnt2, srcl);
+    const bool all2 = cnt2 == need2;
+    const bool few = cnt2 <= static_cast<uint32_t>(kSelMembers);
+    const bool valid = static_cast<uint32_t>(tid) < nb;
+    uint64_t key[1] = {valid ? s.mid[tid] : 0ull};
+    const uint32_t sbk = sub_bin(key[0]);
+    const bool tie = valid && sbk == sb && !all2;
+    bool keep[1] = {valid && (sbk > sb || (sbk == sb && all2))};
+    emit_batch<1>(key, keep, b, o, &s.ocnt, out_of);
+    if (!all2 && few) {
+      // s.sel.mcnt is zero here (wg_select_init) and is left zero again
+      if (tie) s.sel.members[atomicAdd(&s.sel.mcnt, 1u)] = key[0];
+      __syncthreads();
+      uint32_t rank = 0u;
+      if (tie)
+        for (uint32_t j = 0; j < cnt2; ++j) rank += s.sel.members[j] > key[0];
+      keep[0] = tie && rank < need2;
+      emit_batch<1>(key, keep, b, o, &s.ocnt, out_of);
+      if (tid == 0) s.sel.mcnt = 0u;
+    } else if (!all2 && tid < kWave) {
       uint64_t keys[WS_PER];
-      bool valid[WS_PER], keep[WS_PER];
+      bool tk[WS_PER];
 #pragma unroll
       for (int e = 0; e < WS_PER; ++e) {
         const uint32_t i = e * kWave + tid;
-        valid[e] = i < nb;
-        keys[e] = valid[e] ? s.mid[i] : 0ull;
+        keys[e] = i < nb ? s.mid[i] : 0ull;
+        tk[e] = i < nb && sub_bin(keys[e]) == sb;
       }
-      const uint64_t T = nb > need ? wave_select<WS_PER>(keys, valid, need, s.sel.hist) : 0ull;
+      const uint64_t T = wave_select<WS_PER>(keys, tk, need2, s.sel.hist);
 #pragma unroll
-      for (int e = 0; e < WS_PER; ++e) keep[e] = valid[e] && keys[e] >= T;
-      emit_batch<WS_PER>(keys, keep, b, o, &s.ocnt, out_of);
+      for (int e = 0; e < WS_PER; ++e) tk[e] = tk[e] && keys[e] >= T;
+      emit_batch<WS_PER>(keys, tk, b, o, &s.ocnt, out_of);
     }
   } else if (!th.all && nb > 0) {
     if (nb <= static_cast<uint32_t>(MG_MID)) {
