@@ -265,6 +265,50 @@ def _crowded_case(seed, batch, n_lo, n_hi, page_size, k, heads=16):
     return case
 
 
+def _tied_case(seed, batch, n, page_size, k, top, tied, heads=64):
+    """Exact-arithmetic rows of n tokens with integer scores S[j] = m_j (query
+    1.0 in every dimension, only head 0 weighted, unit scales, key j holding
+    1.0 in its first m_j dimensions): `top` tokens at random positions score
+    60..127, `tied` others score exactly 50, and the rest 0..45. The value 50
+    is alone in its histogram bin and in its sub-bin."""
+    case = workloads.indexer_case(seed, batch=batch, n_lo=n, n_hi=n, page_size=page_size, k=k, heads=heads,
+                                  fixed_lens=np.full(batch, n, np.int32))
+    case.q[:] = 0x38
+    case.q_scale[:] = 1.0
+    case.w[:] = 0.0
+    case.w[:, 0] = 1.0
+    g = np.random.default_rng(seed + 7)
+    for b in range(batch):
+        m = g.integers(0, 46, size=n)
+        perm = g.permutation(n)
+        m[perm[:top]] = g.integers(60, 128, size=top)
+        m[perm[top:top + tied]] = 50
+        ts = oracle.token_slots(case.block_table[b], case.page_size, n)
+        case.kcache[ts] = np.where(np.arange(case.dim)[None, :] < m[:, None], 0x38, 0x00).astype(np.uint8)
+        case.k_scale[ts] = 1.0
+    return case
+
+
+@pytest.mark.parametrize("top,tied,k", [(50, 50, 100), (50, 40, 70), (50, 300, 100), (50, 1500, 100),
+                                        (50, 3000, 100)])
+def test_fused_threshold_bin_ties(ops, top, tied, k):
+    """The row's k-th score is shared by `tied` tokens, so the merge's
+    threshold bin (and its sub-bin) holds exactly those: all of them are
+    taken (k = top + tied), a few are ranked against each other, one wave
+    selects among up to 1024, the workgroup among up to 2048, and beyond that
+    the merge selects from the candidates themselves. Ties go to the lower
+    positions, exactly as the oracle takes them, on both chunk schedules."""
+    case = _tied_case(640 + tied, batch=3, n=6000, page_size=64, k=k, top=top, tied=tied)
+    ref_slots, ref_pos, scores = oracle.fused_topk(case)
+    for b in range(case.batch):
+        assert np.sum(scores[b][ref_pos[b]] == 50.0) == k - top, b
+    for c in (case, _guided_variant(case)):
+        slots, sc = _fused(ops, c)
+        for b in range(case.batch):
+            assert np.array_equal(np.sort(slots[b]), np.sort(ref_slots[b])), (c.max_seq_len, b)
+            assert np.array_equal(np.sort(sc[b].astype(np.float64)), np.sort(scores[b][ref_pos[b]])), b
+
+
 @pytest.mark.parametrize("sorted_out", [False, True])
 @pytest.mark.parametrize("page_size,k,n_lo,n_hi", [(64, 2048, 6000, 30000), (16, 300, 400, 9000),
                                                    (1, 100, 150, 4000)])
