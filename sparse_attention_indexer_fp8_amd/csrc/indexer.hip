@@ -54,12 +54,18 @@ namespace idxtopk {
 // same call, so the area needs no initial contents.
 constexpr int FE_CH_MIN = 256;         // shortest chunk: bounds the chunks of a row
 constexpr int FE_RESIDENT_MAX = 2048;  // longest chunk of the one-resident-wave sizing
+constexpr int FE_WIN = 64;             // bins of a chunk's candidate-count window
 
+// win[b][c][i]: how many of chunk c's candidates lie in histogram bin
+// bound_c + i, i < FE_WIN (16-bit counts, two per word; entries of bins past
+// the last are not written). For rows of many candidates the merge adds
+// these instead of counting each candidate of those bins.
 struct FusedWs {
   uint64_t* cand;  // [rows][cap]
   int64_t cap;
   uint2* hdr;      // [rows][hcap]
   int32_t hcap;
+  uint32_t* win;   // [rows][hcap][FE_WIN / 2]
   float* sval;     // [rows][k]: scores of the selection for the sort pass
 };
 
@@ -79,6 +85,8 @@ static inline FusedWs fused_ws(void* base, int rows, int max_seq_len) {
   p += align256(static_cast<size_t>(rows) * w.cap * 8);
   w.hdr = reinterpret_cast<uint2*>(p);
   p += align256(static_cast<size_t>(rows) * w.hcap * 8);
+  w.win = reinterpret_cast<uint32_t*>(p);
+  p += align256(static_cast<size_t>(rows) * w.hcap * FE_WIN * 2);
   w.sval = reinterpret_cast<float*>(p);
   return w;
 }
@@ -87,6 +95,7 @@ size_t fused_workspace_bytes(int rows, int k, int max_seq_len) {
   const int64_t cap = max_seq_len > 0 ? max_seq_len : 1;
   return align256(static_cast<size_t>(rows) * cap * 8) +
          align256(static_cast<size_t>(rows) * fused_hcap(max_seq_len) * 8) +
+         align256(static_cast<size_t>(rows) * fused_hcap(max_seq_len) * FE_WIN * 2) +
          align256(static_cast<size_t>(rows) * k * 4);
 }
 
@@ -286,12 +295,15 @@ __global__ __launch_bounds__(PR_WG) void pair_score_kernel(IndexerArgs a, float*
 
 constexpr int MG_WG = 512;        // block merge workgroup
 constexpr int FM_WG = 1024;       // fused merge workgroup
-constexpr int MG_BUF = 8192;      // candidates of a row gathered in LDS (64 KB)
+constexpr int MG_BUF = 10240;     // candidates of a row gathered in LDS (80 KB)
 constexpr int MG_MID = HIST_BINS / 2;  // threshold-bin keys held in LDS (over the histogram)
 constexpr int MG_MAXE = MG_MID / FM_WG;
 constexpr int MG_CHUNKS = 1024;   // chunk headers of a row held in LDS
 constexpr int MG_BATCH = 8;       // candidates per thread per pass of the merge
 constexpr int WS_PER = 16;        // threshold-bin keys per lane when one wave selects
+constexpr int MG_HIST_MAX = 4096;  // candidates beyond which the merge counts them through the chunks' windows
+constexpr int MG_WPT = 2;          // window words per merge thread (rows of up to 64 chunks)
+constexpr int MG_WIN_CHUNKS = 32;  // rows of fewer chunks count every candidate on its own
 constexpr int MG_SUB_BITS = 8;    // sub-bins of the threshold bin: the next 8 bits of the value key
 constexpr int MG_SUB = 1 << MG_SUB_BITS;
 static_assert(MG_SUB == 4 * kWave, "one wave scans the sub-histogram, four sub-bins per lane");
@@ -396,6 +408,14 @@ __global__ __launch_bounds__(IX_WG) void fused_chunk_kernel(IndexerArgs a, Fused
   own_bins<16>(s.hist, c16);
   const BinThreshold own = wg_threshold_counts<IX_WG, 16>(c16, chunk_rank(k, cnt, n), s.scratch);
   const uint32_t bin_c = own.all ? 0u : own.bin;
+  // the candidates per bin for bins bin_c .. bin_c + FE_WIN - 1 (this
+  // thread holds the counts of bins 16 tid .. 16 tid + 15)
+  uint16_t* win = reinterpret_cast<uint16_t*>(ws.win + (static_cast<int64_t>(b) * ws.hcap + c) * (FE_WIN / 2));
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t bin = 16u * static_cast<uint32_t>(tid) + static_cast<uint32_t>(i);
+    if (bin >= bin_c && bin < bin_c + static_cast<uint32_t>(FE_WIN)) win[bin - bin_c] = static_cast<uint16_t>(c16[i]);
+  }
 
   // Every token in bins >= bin_c, as unique keys: staged in LDS (over the
   // histogram, no longer read) with one slot reservation per wave per batch,
@@ -447,7 +467,8 @@ __global__ __launch_bounds__(IX_WG) void fused_chunk_kernel(IndexerArgs a, Fused
   if (tid == 0) ws.hdr[static_cast<int64_t>(b) * ws.hcap + c] = make_uint2(m, bin_c);
 }
 
-constexpr int MG_SPEC = MG_BUF / FM_WG;  // candidate loads per thread issued with the headers
+constexpr int MG_SPEC = 8;  // candidate loads per thread issued with the headers
+static_assert(MG_SPEC * FM_WG <= MG_BUF, "the first loads fit the gather buffer");
 constexpr int MG_PAGES = 8192;           // block-table entries of a row staged in LDS
 constexpr int MG_PG_PER = MG_PAGES / FM_WG;
 
@@ -461,6 +482,7 @@ struct MergeLds {
   uint32_t coff[MG_CHUNKS + 1];  // first candidate of each chunk in the gathered order
   uint32_t ctb[MG_CHUNKS];       // first token of each chunk
   alignas(16) uint32_t ccnt[MG_CHUNKS];  // candidates of each chunk (then the sub-histogram)
+  uint32_t cbin[MG_CHUNKS];       // bound bin of each chunk
   SelectLds sel;
   uint32_t scratch[24];
   uint32_t ocnt;
@@ -601,14 +623,14 @@ __global__ __launch_bounds__(FM_WG) void fused_merge_kernel(IndexerArgs a, Fused
   }
 
   // In flight together: the chunk headers, the first `spec` candidates of
-  // every chunk (MG_BUF spread evenly over the row's chunks; most chunks send
-  // fewer), and the row's block table.
+  // every chunk (MG_SPEC * FM_WG entries spread evenly over the row's chunks;
+  // most chunks send fewer), and the row's block table.
   constexpr int PC = MG_CHUNKS / FM_WG;
   uint2 h[PC];
-  const int spec = staged ? MG_BUF / nch : 1;
+  const int spec = staged ? MG_SPEC * FM_WG / nch : 1;
   const float rspec = 1.0f / static_cast<float>(spec);
   // flat index f -> (chunk c, entry j): a float estimate of f / spec (f <
-  // 2^13), corrected by one step
+  // 2^14), corrected by one step
   auto split = [&](int f, int& c, int& j) {
     c = static_cast<int>(static_cast<float>(f) * rspec);
     c -= c * spec > f;
@@ -617,11 +639,22 @@ __global__ __launch_bounds__(FM_WG) void fused_merge_kernel(IndexerArgs a, Fused
   };
   uint64_t sk[MG_SPEC];
   int32_t pg[MG_PG_PER];
+  // the chunks' candidate-count windows, for rows of many chunks (long rows,
+  // whose candidates crowd into few bins) when they fit MG_WPT words per thread
+  constexpr int WW = FE_WIN / 2;  // window words per chunk
+  const bool windows = staged && nch >= MG_WIN_CHUNKS && nch * WW <= MG_WPT * FM_WG;
+  uint32_t wv[MG_WPT];
   if (staged) {
 #pragma unroll
     for (int e = 0; e < PC; ++e) {
       const int c = tid * PC + e;
       h[e] = c < nch ? hdr[c] : make_uint2(0u, 0u);
+    }
+    const uint32_t* wrow = ws.win + static_cast<int64_t>(b) * ws.hcap * WW;
+#pragma unroll
+    for (int r = 0; r < MG_WPT; ++r) {
+      const int f = r * FM_WG + tid;
+      wv[r] = windows && f < nch * WW ? wrow[f] : 0u;
     }
 #pragma unroll
     for (int e = 0; e < MG_SPEC; ++e) {
@@ -661,6 +694,7 @@ __global__ __launch_bounds__(FM_WG) void fused_merge_kernel(IndexerArgs a, Fused
         s.coff[c] = off;
         s.ctb[c] = static_cast<uint32_t>(tb);
         s.ccnt[c] = h[e].x;
+        s.cbin[c] = h[e].y;
       }
       off += h[e].x;
     }
@@ -670,6 +704,15 @@ __global__ __launch_bounds__(FM_WG) void fused_merge_kernel(IndexerArgs a, Fused
   }
   __syncthreads();
   const bool gathered = staged && total <= static_cast<uint32_t>(MG_BUF);
+  // Many candidates crowd into few histogram bins (long rows: the row's top
+  // sliver), where per-candidate atomics serialise on those bins; such rows
+  // add their chunks' windows instead (one add per chunk and bin) and count
+  // on their own only the candidates past their chunk's window.
+  const bool use_win = windows && total > static_cast<uint32_t>(MG_HIST_MAX);
+  auto count = [&](uint64_t key, int c) {
+    const uint32_t bin = rank_vkey(key) >> HIST_SHIFT;
+    if (!use_win || bin >= s.cbin[c] + static_cast<uint32_t>(FE_WIN)) atomicAdd(&s.hist[bin], 1u);
+  };
   // Place the loaded candidates: into the histogram of their bins, and into
   // LDS when they all fit; then load what the first loads did not cover
   // (chunks that sent more than `spec`), one wave per chunk.
@@ -680,7 +723,20 @@ __global__ __launch_bounds__(FM_WG) void fused_merge_kernel(IndexerArgs a, Fused
       split(e * FM_WG + tid, c, j);
       if (c < nch && static_cast<uint32_t>(j) < s.ccnt[c]) {
         if (gathered) s.buf[s.coff[c] + j] = sk[e];
-        atomicAdd(&s.hist[rank_vkey(sk[e]) >> HIST_SHIFT], 1u);
+        count(sk[e], c);
+      }
+    }
+    if (use_win) {
+#pragma unroll
+      for (int r = 0; r < MG_WPT; ++r) {
+        const int f = r * FM_WG + tid;
+        if (f < nch * WW) {
+          // window entries of bins past the last were never written
+          const uint32_t bin = s.cbin[f / WW] + 2u * static_cast<uint32_t>(f % WW);
+          const uint32_t lo = wv[r] & 0xFFFFu, hi = wv[r] >> 16;
+          if (lo != 0u && bin < static_cast<uint32_t>(HIST_BINS)) atomicAdd(&s.hist[bin], lo);
+          if (hi != 0u && bin + 1u < static_cast<uint32_t>(HIST_BINS)) atomicAdd(&s.hist[bin + 1u], hi);
+        }
       }
     }
     for (int c = wave; c < nch; c += FM_WG / kWave) {
@@ -690,7 +746,7 @@ __global__ __launch_bounds__(FM_WG) void fused_merge_kernel(IndexerArgs a, Fused
       for (uint32_t j = spec + lane; j < cnt; j += kWave) {
         const uint64_t key = cand[tb + j];
         if (gathered) s.buf[off + j] = key;
-        atomicAdd(&s.hist[rank_vkey(key) >> HIST_SHIFT], 1u);
+        count(key, c);
       }
     }
   }
