@@ -300,14 +300,12 @@ constexpr int MG_MID = HIST_BINS / 2;  // threshold-bin keys held in LDS (over t
 constexpr int MG_MAXE = MG_MID / FM_WG;
 constexpr int MG_CHUNKS = 1024;   // chunk headers of a row held in LDS
 constexpr int MG_BATCH = 8;       // candidates per thread per pass of the merge
-constexpr int WS_PER = 16;        // threshold-bin keys per lane when one wave selects
 constexpr int MG_HIST_MAX = 4096;  // candidates beyond which the merge counts them through the chunks' windows
 constexpr int MG_WPT = 2;          // window words per merge thread (rows of up to 64 chunks)
 constexpr int MG_WIN_CHUNKS = 32;  // rows of fewer chunks count every candidate on its own
 constexpr int MG_SUB_BITS = 8;    // sub-bins of the threshold bin: the next 8 bits of the value key
 constexpr int MG_SUB = 1 << MG_SUB_BITS;
 static_assert(MG_SUB == 4 * kWave, "one wave scans the sub-histogram, four sub-bins per lane");
-static_assert(FM_WG <= kWave * WS_PER, "wave 0 holds a threshold bin of one key per thread");
 static_assert(MG_CHUNKS >= MG_SUB, "the sub-histogram reuses the chunk counts");
 
 static_assert(HIST_BINS == 16 * IX_WG, "16 histogram bins per thread");
@@ -865,13 +863,14 @@ __global__ __launch_bounds__(FM_WG) void fused_merge_kernel(IndexerArgs a, Fused
   }
   __syncthreads();
   const uint32_t nb = s.mcnt;
-  if (!th.all && nb > 0 && nb <= static_cast<uint32_t>(FM_WG)) {
-    // A threshold bin of at most one key per thread. Its sub-histogram gives
-    // the sub-bin sb holding the need-th key from the top (every wave finds
-    // it on its own): keys in higher sub-bins are taken, and need2 of the
-    // cnt2 keys of sb: all of them, or the best need2 by their rank among
-    // them (gathered in LDS), or, when more than kSelMembers keys share sb
-    // (equal scores), by an exact select in wave 0.
+  if (!th.all && nb > 0 && nb <= static_cast<uint32_t>(MG_MID)) {
+    // A threshold bin held in LDS (MG_MAXE keys per thread at most). Its
+    // sub-histogram gives the sub-bin sb holding the need-th key from the
+    // top (every wave finds it on its own): keys in higher sub-bins are
+    // taken, and need2 of the cnt2 keys of sb: all of them, or the best
+    // need2 by their rank among them (gathered in LDS), or, when more than
+    // kSelMembers keys share sb (equal scores), by the workgroup select
+    // over those keys alone.
     const uint4 c4 = reinterpret_cast<const uint4*>(sub)[lane];  // sub-bins 4 lane .. 4 lane + 3
     const uint32_t cb[4] = {c4.x, c4.y, c4.z, c4.w};
     const uint32_t local = cb[0] + cb[1] + cb[2] + cb[3];
@@ -893,99 +892,79 @@ __global__ __launch_bounds__(FM_WG) void fused_merge_kernel(IndexerArgs a, Fused
     const uint32_t need2 = need - __builtin_amdgcn_readlane(above2, srcl);
     cnt2 = __builtin_amdgcn_readlane(cnt2, srcl);
     const bool all2 = cnt2 == need2;
-    const bool few = cnt2 <= static_cast<uint32_t>(kSelMembers);
-    const bool valid = static_cast<uint32_t>(tid) < nb;
-    uint64_t key[1] = {valid ? s.mid[tid] : 0ull};
-    const uint32_t sbk = sub_bin(key[0]);
-    const bool tie = valid && sbk == sb && !all2;
-    bool keep[1] = {valid && (sbk > sb || (sbk == sb && all2))};
-    emit_batch<1>(key, keep, b, o, &s.ocnt, out_of);
-    if (!all2 && few) {
-      // s.sel.mcnt is zero here (wg_select_init) and is left zero again
-      if (tie) s.sel.members[atomicAdd(&s.sel.mcnt, 1u)] = key[0];
-      __syncthreads();
-      uint32_t rank = 0u;
-      if (tie)
-        for (uint32_t j = 0; j < cnt2; ++j) rank += s.sel.members[j] > key[0];
-      keep[0] = tie && rank < need2;
-      emit_batch<1>(key, keep, b, o, &s.ocnt, out_of);
-      if (tid == 0) s.sel.mcnt = 0u;
-    } else if (!all2 && tid < kWave) {
-      uint64_t keys[WS_PER];
-      bool tk[WS_PER];
+    uint64_t keys[MG_MAXE];
+    bool keep[MG_MAXE], tie[MG_MAXE];
 #pragma unroll
-      for (int e = 0; e < WS_PER; ++e) {
-        const uint32_t i = e * kWave + tid;
-        keys[e] = i < nb ? s.mid[i] : 0ull;
-        tk[e] = i < nb && sub_bin(keys[e]) == sb;
-      }
-      const uint64_t T = wave_select<WS_PER>(keys, tk, need2, s.sel.hist);
-#pragma unroll
-      for (int e = 0; e < WS_PER; ++e) tk[e] = tk[e] && keys[e] >= T;
-      emit_batch<WS_PER>(keys, tk, b, o, &s.ocnt, out_of);
+    for (int e = 0; e < MG_MAXE; ++e) {
+      const uint32_t i = tid + e * FM_WG;
+      const bool valid = i < nb;
+      keys[e] = valid ? s.mid[i] : 0ull;
+      const uint32_t sbk = sub_bin(keys[e]);
+      keep[e] = valid && (sbk > sb || (sbk == sb && all2));
+      tie[e] = valid && sbk == sb && !all2;
     }
-  } else if (!th.all && nb > 0) {
-    if (nb <= static_cast<uint32_t>(MG_MID)) {
-      uint64_t keys[MG_MAXE];
-      int nvk = 0;
+    emit_batch<MG_MAXE>(keys, keep, b, o, &s.ocnt, out_of);
+    if (!all2 && cnt2 <= static_cast<uint32_t>(kSelMembers)) {
+      // s.sel.mcnt is zero here (wg_select_init) and is left zero again
+#pragma unroll
+      for (int e = 0; e < MG_MAXE; ++e)
+        if (tie[e]) s.sel.members[atomicAdd(&s.sel.mcnt, 1u)] = keys[e];
+      __syncthreads();
 #pragma unroll
       for (int e = 0; e < MG_MAXE; ++e) {
-        const uint32_t i = tid + e * FM_WG;
-        keys[e] = 0;
-        if (i < nb) {
-          keys[e] = s.mid[i];
-          nvk = e + 1;
-        }
+        uint32_t rank = 0u;
+        if (tie[e])
+          for (uint32_t j = 0; j < cnt2; ++j) rank += s.sel.members[j] > keys[e];
+        keep[e] = tie[e] && rank < need2;
       }
-      uint64_t T = 0;  // keys >= T are selected
-      if (nb > need) {
-        uint64_t mn = ~0ull, mx = 0;
-#pragma unroll
-        for (int e = 0; e < MG_MAXE; ++e)
-          if (e < nvk) {
-            mn = keys[e] < mn ? keys[e] : mn;
-            mx = keys[e] > mx ? keys[e] : mx;
-          }
-        wg_range<FM_WG>(mn, mx, s.sel);
-        T = wg_select<FM_WG>(
-            [&](auto&& f) {
-#pragma unroll
-              for (int e = 0; e < MG_MAXE; ++e)
-                if (e < nvk) f(keys[e]);
-            },
-            need, mn, mx, s.sel);
-      }
-      bool keep[MG_MAXE];
-#pragma unroll
-      for (int e = 0; e < MG_MAXE; ++e) keep[e] = e < nvk && keys[e] >= T;
       emit_batch<MG_MAXE>(keys, keep, b, o, &s.ocnt, out_of);
-    } else {
-      // threshold bin larger than its LDS area: select straight from the
-      // candidates (several passes over them)
-      auto each_mid = [&](auto&& f) {
-        for (uint32_t i = tid; i < ncand; i += FM_WG) {
-          const uint64_t key = src.at(i);
-          if ((rank_vkey(key) >> HIST_SHIFT) == bstar) f(key);
-        }
-      };
+      if (tid == 0) s.sel.mcnt = 0u;
+    } else if (!all2) {
       uint64_t mn = ~0ull, mx = 0;
-      each_mid([&](uint64_t key) {
-        mn = key < mn ? key : mn;
-        mx = key > mx ? key : mx;
-      });
-      wg_range<FM_WG>(mn, mx, s.sel);
-      const uint64_t T = wg_select<FM_WG>(each_mid, need, mn, mx, s.sel);
-      for (uint32_t i0 = 0; i0 < ncand; i0 += FM_WG * MG_BATCH) {
-        uint64_t key[MG_BATCH];
-        bool keep[MG_BATCH];
 #pragma unroll
-        for (int j = 0; j < MG_BATCH; ++j) {
-          const uint32_t i = i0 + j * FM_WG + tid;
-          key[j] = i < ncand ? src.at(i) : 0ull;
-          keep[j] = i < ncand && (rank_vkey(key[j]) >> HIST_SHIFT) == bstar && key[j] >= T;
+      for (int e = 0; e < MG_MAXE; ++e)
+        if (tie[e]) {
+          mn = keys[e] < mn ? keys[e] : mn;
+          mx = keys[e] > mx ? keys[e] : mx;
         }
-        emit_batch<MG_BATCH>(key, keep, b, o, &s.ocnt, out_of);
+      wg_range<FM_WG>(mn, mx, s.sel);
+      const uint64_t T = wg_select<FM_WG>(
+          [&](auto&& f) {
+#pragma unroll
+            for (int e = 0; e < MG_MAXE; ++e)
+              if (tie[e]) f(keys[e]);
+          },
+          need2, mn, mx, s.sel);
+#pragma unroll
+      for (int e = 0; e < MG_MAXE; ++e) keep[e] = tie[e] && keys[e] >= T;
+      emit_batch<MG_MAXE>(keys, keep, b, o, &s.ocnt, out_of);
+    }
+  } else if (!th.all && nb > 0) {
+    // threshold bin larger than its LDS area: select straight from the
+    // candidates (several passes over them)
+    auto each_mid = [&](auto&& f) {
+      for (uint32_t i = tid; i < ncand; i += FM_WG) {
+        const uint64_t key = src.at(i);
+        if ((rank_vkey(key) >> HIST_SHIFT) == bstar) f(key);
       }
+    };
+    uint64_t mn = ~0ull, mx = 0;
+    each_mid([&](uint64_t key) {
+      mn = key < mn ? key : mn;
+      mx = key > mx ? key : mx;
+    });
+    wg_range<FM_WG>(mn, mx, s.sel);
+    const uint64_t T = wg_select<FM_WG>(each_mid, need, mn, mx, s.sel);
+    for (uint32_t i0 = 0; i0 < ncand; i0 += FM_WG * MG_BATCH) {
+      uint64_t key[MG_BATCH];
+      bool keep[MG_BATCH];
+#pragma unroll
+      for (int j = 0; j < MG_BATCH; ++j) {
+        const uint32_t i = i0 + j * FM_WG + tid;
+        key[j] = i < ncand ? src.at(i) : 0ull;
+        keep[j] = i < ncand && (rank_vkey(key[j]) >> HIST_SHIFT) == bstar && key[j] >= T;
+      }
+      emit_batch<MG_BATCH>(key, keep, b, o, &s.ocnt, out_of);
     }
   }
   __syncthreads();

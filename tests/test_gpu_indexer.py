@@ -294,9 +294,10 @@ def _tied_case(seed, batch, n, page_size, k, top, tied, heads=64):
 def test_fused_threshold_bin_ties(ops, top, tied, k):
     """The row's k-th score is shared by `tied` tokens, so the merge's
     threshold bin (and its sub-bin) holds exactly those: all of them are
-    taken (k = top + tied), a few are ranked against each other, one wave
-    selects among up to 1024, the workgroup among up to 2048, and beyond that
-    the merge selects from the candidates themselves. Ties go to the lower
+    taken (k = top + tied), a few (at most 64) are ranked against each
+    other, more go through the workgroup select over the sub-bin's keys
+    (threshold bins of up to 2048 keys held in LDS), and beyond that the
+    merge selects from the candidates themselves. Ties go to the lower
     positions, exactly as the oracle takes them, on both chunk schedules."""
     case = _tied_case(640 + tied, batch=3, n=6000, page_size=64, k=k, top=top, tied=tied)
     ref_slots, ref_pos, scores = oracle.fused_topk(case)
