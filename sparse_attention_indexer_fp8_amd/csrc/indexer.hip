@@ -20,13 +20,17 @@
 //     count from the top reaches a rank with a wide statistical margin over
 //     its expected share of the row's k best. Its tokens in bins at or above
 //     that bin go, as unique 64-bit keys (score key, inverted position), to
-//     the chunk's own range of the row's candidate area, and (count, bound)
-//     to the chunk's header. No chunk waits on another.
+//     the chunk's own range of the row's candidate area, (count, bound) to
+//     the chunk's header, and its counts of the 64 bins from the bound up to
+//     a window beside it. No chunk waits on another.
 //  2. Per row, once every chunk is done: the merge gathers the candidates,
-//     histograms them and takes the threshold bin for rank k. When that bin
-//     is at or above every chunk's bound, every token of the row in it and
-//     above is a candidate, so the selection is exact: candidates above the
-//     bin are emitted, those in it go through an exact select. Otherwise
+//     histograms them (long rows add the chunks' windows instead of
+//     counting each candidate) and takes the threshold bin for rank k. When
+//     that bin is at or above every chunk's bound, every token of the row
+//     in it and above is a candidate, so the selection is exact: candidates
+//     above the bin are emitted, and those in it are split once more by the
+//     next 8 bits of their value key, the keys of the one sub-bin holding
+//     the k-th going through an exact select. Otherwise
 //     (best tokens crowded into a few chunks far beyond the margin) the
 //     merge scores the row again itself, keeping every token at or above
 //     the candidates' threshold bin, a proven lower bound, and selects from
