@@ -152,6 +152,29 @@ def _crowded(case):
     return case
 
 
+@pytest.mark.parametrize("requests,next_n", [(4, 64), (5, 52), (8, 33)])
+def test_prefill_schedule_boundary(ops, requests, next_n):
+    """Around the switch between the two chunk schedules: 64 row quads
+    (256 rows: the balanced schedule, chunk sizes taken on the device from
+    the rows' lengths), 65 quads (260 rows: the chunk-major grid), and 66
+    quads whose rows straddle requests. Each equals the unfused path's
+    selection exactly, with the returned scores equal to the score rows."""
+    import torch
+
+    case = _prefill_case(760 + requests, requests, next_n, 1, 6000, 64, 300)
+    log(f"prefill schedule boundary: rows={case.batch} quads={(case.batch + 3) // 4}")
+    slots, sc = _prefill(ops, case)
+    ref, scores = _unfused(ops, case)
+    assert np.array_equal(np.sort(slots, axis=1), np.sort(ref, axis=1))
+    host = scores.cpu().numpy()
+    del scores
+    torch.cuda.empty_cache()
+    for b in range(case.batch):
+        n = int(case.seq_lens[b])
+        m = min(n, case.k)
+        assert np.array_equal(np.sort(sc[b][:m]), np.sort(host[b, :n])[::-1][:m][::-1]), b
+
+
 @pytest.mark.parametrize("sorted_out", [False, True])
 @pytest.mark.parametrize("page_size,k,n_hi", [(64, 512, 30000), (16, 300, 9000), (128, 2048, 40000)])
 def test_prefill_rows_rescored(ops, page_size, k, n_hi, sorted_out):
