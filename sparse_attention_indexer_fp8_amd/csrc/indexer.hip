@@ -61,8 +61,9 @@ constexpr int FE_RESIDENT_MAX = 2048;  // longest chunk of the one-resident-wave
 constexpr int FE_WIN = 64;             // bins of a chunk's candidate-count window
 
 // win[b][c][i]: how many of chunk c's candidates lie in histogram bin
-// bound_c + i, i < FE_WIN (16-bit counts, two per word; entries of bins past
-// the last are not written). For rows of many candidates the merge adds
+// bound_c + i, i < FE_WIN (16-bit counts, two per word: a chunk holds at
+// most FU_CH_MAX = 8192 tokens; entries of bins past the last are not
+// written). For rows of many candidates the merge adds
 // these instead of counting each candidate of those bins.
 struct FusedWs {
   uint64_t* cand;  // [rows][cap]
