@@ -227,7 +227,7 @@ struct PrefillWaveLds {
 };
 
 // Rows b0 + i0 .. + R - 1 (one block-table row, prow) over the chunk at kb.
-template <int NT, int R, int RING>
+template <int NT, int R>
 __device__ __forceinline__ void prefill_rows(const IndexerArgs& a, const PrefillWs& w, const PrefillParams& pp,
                                              PrefillWaveLds& L, int b0, const int (&nn)[4], int i0, int prow,
                                              int kb) {
@@ -244,8 +244,8 @@ __device__ __forceinline__ void prefill_rows(const IndexerArgs& a, const Prefill
   }
   const int ke = min(kb + pp.chunk, nmax);
   if (kb >= ke) return;
-  static_assert(PF_LIST % RING == 0, "list segments start at multiples of the ring");
-  RowGroupStream<NT, R, RING> st(a, q, a.block_table + static_cast<int64_t>(prow) * a.bt_stride, kb, ke);
+  static_assert(PF_LIST % PF_RING == 0, "list segments start at multiples of the ring");
+  RowGroupStream<NT, R, PF_RING> st(a, q, a.block_table + static_cast<int64_t>(prow) * a.bt_stride, kb, ke);
   const int G = st.ngroups;
   const int S = pp.stride;
   // Visiting order: the sampled groups 0, S, 2S, ... first, then the others
@@ -253,7 +253,7 @@ __device__ __forceinline__ void prefill_rows(const IndexerArgs& a, const Prefill
   const bool whole = G <= PF_SAMPLE;
   const int Se = whole ? 1 : S;
   const int cnt0 = whole ? G : (G + S - 1) / S;
-  const int nA = whole ? G : min(PF_SAMPLE, (cnt0 + RING - 1) / RING * RING);
+  const int nA = whole ? G : min(PF_SAMPLE, (cnt0 + PF_RING - 1) / PF_RING * PF_RING);
   // after the sample, the t-th other group is t + t / (S - 1) + 1 (no
   // branches: both forms are computed and one is selected)
   auto later = [&](int s) -> int {
@@ -397,7 +397,6 @@ __device__ __forceinline__ void prefill_rows(const IndexerArgs& a, const Prefill
 template <int NT, bool BAL>
 __global__ __launch_bounds__(PR_WG) void prefill_chunk_kernel(IndexerArgs a, PrefillWs w, PrefillParams pp) {
   __shared__ PrefillWaveLds lds[PR_WG / kWave];
-  constexpr int RING = PF_RING;
   const int wave = uniform(static_cast<int>(threadIdx.x) / kWave);
   int quad, kb;
   if constexpr (BAL) {
@@ -420,15 +419,15 @@ __global__ __launch_bounds__(PR_WG) void prefill_chunk_kernel(IndexerArgs a, Pre
   }
   PrefillWaveLds& L = lds[wave];
   if (nr == 4 && pr[0] == pr[1] && pr[1] == pr[2] && pr[2] == pr[3]) {
-    prefill_rows<NT, 4, RING>(a, w, pp, L, b0, nn, 0, pr[0], kb);
+    prefill_rows<NT, 4>(a, w, pp, L, b0, nn, 0, pr[0], kb);
     return;
   }
   for (int i0 = 0; i0 < nr; i0 += 2) {
     if (i0 + 1 < nr && pr[i0] == pr[i0 + 1]) {
-      prefill_rows<NT, 2, RING>(a, w, pp, L, b0, nn, i0, pr[i0], kb);
+      prefill_rows<NT, 2>(a, w, pp, L, b0, nn, i0, pr[i0], kb);
     } else {
-      prefill_rows<NT, 1, RING>(a, w, pp, L, b0, nn, i0, pr[i0], kb);
-      if (i0 + 1 < nr) prefill_rows<NT, 1, RING>(a, w, pp, L, b0, nn, i0 + 1, pr[i0 + 1], kb);
+      prefill_rows<NT, 1>(a, w, pp, L, b0, nn, i0, pr[i0], kb);
+      if (i0 + 1 < nr) prefill_rows<NT, 1>(a, w, pp, L, b0, nn, i0 + 1, pr[i0 + 1], kb);
     }
   }
 }
