@@ -265,6 +265,20 @@ def _crowded_case(seed, batch, n_lo, n_hi, page_size, k, heads=16):
     return case
 
 
+@pytest.mark.parametrize("batch,n,k", [(16, 16384, 2048), (12, 30000, 2048)])
+def test_fused_exact_many_chunks(ops, batch, n, k):
+    """Exact arithmetic on rows of 32 to 64 chunks with more than 4096
+    candidates each: the merge adds the chunks' candidate-count windows to
+    its histogram instead of counting every candidate; the sets and scores
+    equal the oracle's exactly (ties by position included)."""
+    case = _exact_case(660 + batch, batch=batch, n_lo=n, n_hi=n, page_size=64, heads=64, k=k)
+    slots, sc = _fused(ops, case)
+    ref_slots, ref_pos, scores = oracle.fused_topk(case)
+    for b in range(case.batch):
+        assert np.array_equal(np.sort(slots[b]), np.sort(ref_slots[b])), b
+        assert np.array_equal(np.sort(sc[b].astype(np.float64)), np.sort(scores[b][ref_pos[b]])), b
+
+
 def _tied_case(seed, batch, n, page_size, k, top, tied, heads=64):
     """Exact-arithmetic rows of n tokens with integer scores S[j] = m_j (query
     1.0 in every dimension, only head 0 weighted, unit scales, key j holding
