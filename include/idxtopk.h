@@ -448,6 +448,7 @@ int32_t idxtopk_version(void);
 #define IDXTOPK_CHK_PAGE_ID 0x20       /* a block-table or page-table entry < 0 */
 #define IDXTOPK_CHK_CHUNK_COUNT 0x40   /* fused: chunk candidates above its tokens (internal) */
 #define IDXTOPK_CHK_BLOCK 0x80         /* block top-k: a block outside the row (internal) */
+#define IDXTOPK_CHK_MERGE_COUNT 0x100  /* fused merge: candidate counts inconsistent (internal) */
 #define IDXTOPK_CHECKS_OFF 0x80000000u /* a release build: no checks compiled in */
 /*
  * idxtopk_check_status -- the bits of every check that failed since the

@@ -28,6 +28,7 @@ constexpr uint32_t kChkRowToBatch = 1u << 4;    // row_to_batch[b] < 0
 constexpr uint32_t kChkPageId = 1u << 5;        // a block-table or page-table entry < 0
 constexpr uint32_t kChkChunkCount = 1u << 6;    // fused: a chunk header's count above the chunk's tokens
 constexpr uint32_t kChkBlock = 1u << 7;         // block top-k: a selected block outside the row
+constexpr uint32_t kChkMergeCount = 1u << 8;    // fused merge: histogram or threshold sub-bin counts inconsistent
 
 #if IDXTOPK_CHECKS
 static __device__ uint32_t g_check_word;

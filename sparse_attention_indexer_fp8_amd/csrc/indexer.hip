@@ -796,6 +796,8 @@ __global__ __launch_bounds__(FM_WG) void fused_merge_kernel(IndexerArgs a, Fused
     uint32_t h8[MG_HPER];
     own_bins<MG_HPER>(s.hist, h8);
     th = wg_threshold_counts<FM_WG, MG_HPER>(h8, k, s.scratch);
+    // the histogram (windows included) counts every candidate once
+    IDXTOPK_CHECK(th.total == total, kChkMergeCount);
     ok = th.all ? total == static_cast<uint32_t>(n) : th.bin >= s.maxbin;
     lo_bin = th.all ? 0u : th.bin;  // the candidates' k-th best key is at or below the row's
   }
@@ -897,6 +899,7 @@ __global__ __launch_bounds__(FM_WG) void fused_merge_kernel(IndexerArgs a, Fused
     const uint32_t need2 = need - __builtin_amdgcn_readlane(above2, srcl);
     cnt2 = __builtin_amdgcn_readlane(cnt2, srcl);
     const bool all2 = cnt2 == need2;
+    IDXTOPK_CHECK(need2 >= 1u && cnt2 >= need2, kChkMergeCount);
     uint64_t keys[MG_MAXE];
     bool keep[MG_MAXE], tie[MG_MAXE];
 #pragma unroll
