@@ -172,9 +172,16 @@ __device__ __forceinline__ void chunk_span(const IndexerArgs& a, int c, int& tb,
 // Unfused scores
 // ---------------------------------------------------------------------------
 
+// A wave's scores wait in LDS and go out SK_STAGE groups at a time (a wave
+// scores consecutive groups, so a run of staged groups is one contiguous
+// stretch of the row): full-line stores instead of one 64-byte store per
+// group.
+constexpr int SK_STAGE = 32;
+
 template <int NT, bool BF = false>
 __global__ __launch_bounds__(IX_WG) void score_kernel(IndexerArgs a, float* scores, int64_t sstride) {
   __shared__ int32_t pages[IX_PAGES];
+  __shared__ float stage[IX_WG / kWave][SK_STAGE * kGroup];
   int b, c;
   chunk_of(a, b, c);
   const int n = row_len(a, b);
@@ -183,9 +190,23 @@ __global__ __launch_bounds__(IX_WG) void score_kernel(IndexerArgs a, float* scor
   if (tb >= n) return;
   const int te = min(n, tb + clen);
   float* srow = scores + static_cast<int64_t>(b) * sstride;
-  score_chunk_any<BF, NT, IX_WG, IX_RING>(a, b, tb, te, pages, [&](int j, float s, bool valid) {
-    if (valid) srow[j] = s;
+  const int l = lane_id();
+  float* st = stage[uniform(static_cast<int>(threadIdx.x) / kWave)];
+  int ns = 0;     // groups staged (the same in every lane)
+  int first = 0;  // first token of the staged run
+  auto flush = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    const int lim = min(ns * kGroup, te - first);
+    for (int i = l; i < lim; i += kWave) srow[first + i] = st[i];
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    ns = 0;
+  };
+  score_chunk_any<BF, NT, IX_WG, IX_RING>(a, b, tb, te, pages, [&](int j, float s, bool) {
+    if (ns == 0) first = __builtin_amdgcn_readfirstlane(j - (l & 15));
+    if (l < kGroup) st[ns * kGroup + l] = s;
+    if (++ns == SK_STAGE) flush();
   });
+  if (ns > 0) flush();
 }
 
 // ---------------------------------------------------------------------------
