@@ -98,7 +98,7 @@ PMC_KERNELS = {
                                "fused_decode_B32_k2048"),
     "mtp_decode_16x4_chunk": ("fused", "void idxtopk::fused_chunk_kernel<4, false>", 524288,
                               "mtp_decode_16x4_k2048"),
-    "mtp_decode_16x4_rowgroup_chunk": ("prefill", "void idxtopk::prefill_chunk_kernel<4, true>", 65536,
+    "mtp_decode_16x4_rowgroup_chunk": ("prefill", "void idxtopk::prefill_chunk_kernel<4, true, 4>", 65536,
                                        "mtp_decode_16x4_k2048"),
     "block_sparse_B64_chunk": ("fused", "void idxtopk::block_chunk_kernel<4, false>", 196608,
                                "block_sparse_B64_n32768_top32"),
@@ -108,7 +108,7 @@ PMC_KERNELS = {
     "block_heads_B64_merge": ("fused", "idxtopk::block_heads_merge_kernel", 262144,
                               "block_sparse_per_head_B64_H64_top32"),
     "prefill_scores_16384": ("fused", "void idxtopk::pair_score_kernel<4>", 4718592, "prefill_indexer_16384_k512"),
-    "prefill_fused_chunk_16384": ("prefill", "void idxtopk::prefill_chunk_kernel<4, false>", 2359296,
+    "prefill_fused_chunk_16384": ("prefill", "void idxtopk::prefill_chunk_kernel<4, false, 2>", 4718592,
                                   "prefill_indexer_16384_k512"),
     "prefill_fused_merge_16384": ("prefill", "void idxtopk::prefill_merge_kernel", 8388608,
                                   "prefill_indexer_16384_k512"),

@@ -15,9 +15,11 @@
 // One call, four kernels on the caller's stream:
 //  0. prefill_zero_kernel clears each row's candidate count and bound and
 //     the fallback queue (the workspace needs no initial contents).
-//  1. prefill_chunk_kernel, one wave per (four query rows of one request,
-//     chunk of keys), chunk-major: each 16-token key group is loaded once
-//     and scored against the four rows (RowGroupStream). The chunk's groups
+//  1. prefill_chunk_kernel, one wave per (two query rows of one request,
+//     chunk of keys), chunk-major, three waves per SIMD (calls of few rows:
+//     four rows per wave under the balanced schedule): each 16-token key
+//     group is loaded once per wave and scored against its rows
+//     (RowGroupStream). The chunk's groups
 //     are visited strided first: every S-th group (about 1024 tokens) is the
 //     sample, whose value keys go to LDS. Per row, the sample holds on
 //     average mu = k m / n of the row's k best (m sampled of the row's n
@@ -206,31 +208,38 @@ __device__ __forceinline__ bool balanced_pair(const IndexerArgs& a, uint32_t i, 
   return true;
 }
 
-// Per-lane lists of kept tokens: PF_LIST entries (score, group) per lane.
-// A wave whose rows keep more than PF_LIST / 4 tokens per lane on average
-// (dense: short rows, or rows without a bound) flushes after every PF_LIST
-// groups, so no list can overflow; the others flush once, after the chunk,
-// and a lane that outgrows its list (far beyond its average) sends its row
-// to the fallback.
-constexpr int PF_LIST = 32;
+// Per-lane lists of kept tokens: pf_list<RM>() entries (score, group) per
+// lane, for waves of up to RM rows. A wave whose rows keep more than a
+// quarter of that per lane on average (dense: short rows, or rows without a
+// bound) flushes after every list length of groups, so no list can
+// overflow; the others flush once, after the chunk, and a lane that
+// outgrows its list (far beyond its average) sends its row to the fallback.
+// Pair waves keep shorter lists: their LDS then leaves room for four waves
+// per SIMD.
+template <int RM>
+constexpr int pf_list() { return RM == 4 ? 32 : 16; }
 
+template <int RM>
 struct PrefillWaveLds {
   union {
-    uint32_t samp[4][PF_SAMPLE * kGroup + kGroup];  // sampled value keys per row (0: no token); rows
-                                                    // padded so the four rows' lanes write distinct banks
+    uint32_t samp[RM][PF_SAMPLE * kGroup + kGroup];  // sampled value keys per row (0: no token); rows
+                                                     // padded so the rows' lanes write distinct banks
     struct {
-      float sc[PF_LIST * kWave];           // then: lane l's kept scores at [i * 64 + l]
-      uint32_t gi[PF_LIST * kWave];        // and their groups
+      float sc[pf_list<RM>() * kWave];     // then: lane l's kept scores at [i * 64 + l]
+      uint32_t gi[pf_list<RM>() * kWave];  // and their groups
     } list;
   };
   alignas(16) uint32_t hist[256];          // wave_lower_bound
 };
 
-// Rows b0 + i0 .. + R - 1 (one block-table row, prow) over the chunk at kb.
-template <int NT, int R>
+// Rows b0 + i0 .. + R - 1 (one block-table row, prow) over the chunk at kb,
+// in a wave of up to RM rows.
+template <int NT, int R, int RM>
 __device__ __forceinline__ void prefill_rows(const IndexerArgs& a, const PrefillWs& w, const PrefillParams& pp,
-                                             PrefillWaveLds& L, int b0, const int (&nn)[4], int i0, int prow,
+                                             PrefillWaveLds<RM>& L, int b0, const int (&nn)[4], int i0, int prow,
                                              int kb) {
+  static_assert(R <= RM, "rows of the wave");
+  constexpr int LIST = pf_list<RM>();
   QOperand<NT> q[R];
   int n[R];
   int nmax = 0;
@@ -244,7 +253,7 @@ __device__ __forceinline__ void prefill_rows(const IndexerArgs& a, const Prefill
   }
   const int ke = min(kb + pp.chunk, nmax);
   if (kb >= ke) return;
-  static_assert(PF_LIST % PF_RING == 0, "list segments start at multiples of the ring");
+  static_assert(LIST % PF_RING == 0, "list segments start at multiples of the ring");
   RowGroupStream<NT, R, PF_RING> st(a, q, a.block_table + static_cast<int64_t>(prow) * a.bt_stride, kb, ke);
   const int G = st.ngroups;
   const int S = pp.stride;
@@ -358,11 +367,11 @@ __device__ __forceinline__ void prefill_rows(const IndexerArgs& a, const Prefill
   uint32_t my_cnt = 0u;
   uint64_t* my_dst = w.cand + static_cast<int64_t>(b0 + i0 + (writer ? g : 0)) * w.cap;
   const int lim = writer ? my_n - kb - c : INT32_MIN;  // group gi holds this lane's token iff 16 gi < lim
-  const int seg = per_lane > static_cast<float>(PF_LIST / 4) ? PF_LIST : G;
+  const int seg = per_lane > static_cast<float>(LIST / 4) ? LIST : G;
   for (int s0 = nA; s0 < G; s0 += seg) {
     st.run(s0, min(G, s0 + seg), later, [&](int, int gi, float sc) {
       if (gi * kGroup < lim && sc >= my_thr) {
-        if (my_cnt < static_cast<uint32_t>(PF_LIST)) {
+        if (my_cnt < static_cast<uint32_t>(LIST)) {
           L.list.sc[my_cnt * kWave + l] = sc;
           L.list.gi[my_cnt * kWave + l] = static_cast<uint32_t>(gi);
         }
@@ -371,8 +380,8 @@ __device__ __forceinline__ void prefill_rows(const IndexerArgs& a, const Prefill
     });
     // lanes 16 g .. 16 g + 15 hold row g's lists; a list that overflowed
     // makes its row's count exceed the candidate capacity (fallback)
-    const uint32_t held = min(my_cnt, static_cast<uint32_t>(PF_LIST));
-    const uint32_t over = my_cnt > static_cast<uint32_t>(PF_LIST) ? static_cast<uint32_t>(w.cap) + 1u : 0u;
+    const uint32_t held = min(my_cnt, static_cast<uint32_t>(LIST));
+    const uint32_t over = my_cnt > static_cast<uint32_t>(LIST) ? static_cast<uint32_t>(w.cap) + 1u : 0u;
     const uint32_t p = row16_prefix_incl(held + over);
     uint32_t fbase = 0u;
     if (c == 15 && writer && p != 0u) fbase = atomicAdd(w.cnt + b0 + i0 + g, p);
@@ -394,40 +403,51 @@ __device__ __forceinline__ void prefill_rows(const IndexerArgs& a, const Prefill
   }
 }
 
-template <int NT, bool BAL>
-__global__ __launch_bounds__(PR_WG) void prefill_chunk_kernel(IndexerArgs a, PrefillWs w, PrefillParams pp) {
-  __shared__ PrefillWaveLds lds[PR_WG / kWave];
+// One wave per (RM rows, chunk): RM = 4 (quads, one wave per SIMD: the four
+// rows' query operands take most of the registers) or RM = 2 (pairs, three
+// waves per SIMD). Per group of 16 keys a quad issues 16 products and their
+// ReLU and weighted sums from one wave, which leaves the matrix core idle
+// while that wave waits on its own results; three pair waves per SIMD keep
+// it busy from the others. A quad's two pairs sit in one workgroup and read
+// the same keys on the same compute unit.
+template <int NT, bool BAL, int RM>
+__global__ __launch_bounds__(PR_WG, RM == 4 ? 1 : 3) void prefill_chunk_kernel(IndexerArgs a, PrefillWs w,
+                                                                                PrefillParams pp) {
+  static_assert(RM == 4 || (RM == 2 && !BAL), "rows per wave");
+  __shared__ PrefillWaveLds<RM> lds[PR_WG / kWave];
   const int wave = uniform(static_cast<int>(threadIdx.x) / kWave);
-  int quad, kb;
+  int unit, kb;
   if constexpr (BAL) {
-    if (!balanced_pair(a, blockIdx.x * (PR_WG / kWave) + wave, quad, kb, pp.chunk)) return;
+    if (!balanced_pair(a, blockIdx.x * (PR_WG / kWave) + wave, unit, kb, pp.chunk)) return;
   } else {
-    quad = static_cast<int>(blockIdx.x % pp.ntiles) * (PR_WG / kWave) + wave;
+    unit = static_cast<int>(blockIdx.x % pp.ntiles) * (PR_WG / kWave) + wave;
     kb = static_cast<int>(blockIdx.x / pp.ntiles) * pp.chunk;
   }
-  const int b0 = 4 * quad;
+  const int b0 = RM * unit;
   if (b0 >= a.batch) return;
-  const int nr = min(4, a.batch - b0);
-  int nn[4], pr[4];
+  const int nr = min(RM, a.batch - b0);
+  int nn[4] = {0, 0, 0, 0}, pr[4] = {0, 0, 0, 0};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < RM; ++i) {
     const int b = b0 + (i < nr ? i : 0);
     nn[i] = i < nr ? load_uniform(a.seq_lens + b) : 0;
     IDXTOPK_CHECK(nn[i] >= 0 && nn[i] <= a.max_seq_len, kChkSeqLen);
     pr[i] = a.row_to_batch ? load_uniform(a.row_to_batch + b) : b;
     IDXTOPK_CHECK(pr[i] >= 0, kChkRowToBatch);
   }
-  PrefillWaveLds& L = lds[wave];
-  if (nr == 4 && pr[0] == pr[1] && pr[1] == pr[2] && pr[2] == pr[3]) {
-    prefill_rows<NT, 4>(a, w, pp, L, b0, nn, 0, pr[0], kb);
-    return;
+  PrefillWaveLds<RM>& L = lds[wave];
+  if constexpr (RM == 4) {
+    if (nr == 4 && pr[0] == pr[1] && pr[1] == pr[2] && pr[2] == pr[3]) {
+      prefill_rows<NT, 4, RM>(a, w, pp, L, b0, nn, 0, pr[0], kb);
+      return;
+    }
   }
   for (int i0 = 0; i0 < nr; i0 += 2) {
     if (i0 + 1 < nr && pr[i0] == pr[i0 + 1]) {
-      prefill_rows<NT, 2>(a, w, pp, L, b0, nn, i0, pr[i0], kb);
+      prefill_rows<NT, 2, RM>(a, w, pp, L, b0, nn, i0, pr[i0], kb);
     } else {
-      prefill_rows<NT, 1>(a, w, pp, L, b0, nn, i0, pr[i0], kb);
-      if (i0 + 1 < nr) prefill_rows<NT, 1>(a, w, pp, L, b0, nn, i0 + 1, pr[i0 + 1], kb);
+      prefill_rows<NT, 1, RM>(a, w, pp, L, b0, nn, i0, pr[i0], kb);
+      if (i0 + 1 < nr) prefill_rows<NT, 1, RM>(a, w, pp, L, b0, nn, i0 + 1, pr[i0 + 1], kb);
     }
   }
 }
@@ -636,11 +656,13 @@ int launch_prefill_fused(const IndexerInputs& in, int k, int32_t* out_slots, flo
   const int gfull = static_cast<int>(chunk / kGroup);
   pp.stride = (gfull + PF_SAMPLE - 1) / PF_SAMPLE;
   pp.sdiv1 = make_fastdiv(static_cast<uint32_t>(pp.stride > 1 ? pp.stride - 1 : 1));  // S - 1 (1 when S = 1)
-  pp.ntiles = static_cast<int>((quads + PR_WG / kWave - 1) / (PR_WG / kWave));
-  const int nkc = static_cast<int>((static_cast<int64_t>(in.max_seq_len > 0 ? in.max_seq_len : 1) + chunk - 1) / chunk);
-  // Few quads: the balanced schedule over a grid of at least one wave per
-  // SIMD, and at least nq chunks of PF_SAMPLE groups per quad's bound.
+  // Few quads: the balanced schedule (quad waves); otherwise pair waves.
   pp.balanced = quads <= PF_BAL_QUADS;
+  const int64_t units = pp.balanced ? quads : (in.batch + 1) / 2;
+  pp.ntiles = static_cast<int>((units + PR_WG / kWave - 1) / (PR_WG / kWave));
+  const int nkc = static_cast<int>((static_cast<int64_t>(in.max_seq_len > 0 ? in.max_seq_len : 1) + chunk - 1) / chunk);
+  // The balanced schedule runs over a grid of at least one wave per SIMD,
+  // and at least nq chunks of PF_SAMPLE groups per quad's bound.
   int64_t nwg = static_cast<int64_t>(pp.ntiles) * nkc;
   if (pp.balanced) {
     const int64_t full = quads * ((msl + PF_SAMPLE * kGroup - 1) / (PF_SAMPLE * kGroup));
@@ -653,16 +675,16 @@ int launch_prefill_fused(const IndexerInputs& in, int k, int32_t* out_slots, flo
   (void)hipGetLastError();
   hipLaunchKernelGGL(prefill_zero_kernel, dim3((in.batch + 255) / 256), dim3(256), 0, stream, w, in.batch);
   const dim3 grid(static_cast<unsigned>(nwg));
-#define IDXTOPK_PF_CHUNK(BAL)                                                                                 \
-  switch (in.heads) {                                                                                         \
-    case 16: hipLaunchKernelGGL((prefill_chunk_kernel<1, BAL>), grid, dim3(PR_WG), 0, stream, a, w, pp); break; \
-    case 32: hipLaunchKernelGGL((prefill_chunk_kernel<2, BAL>), grid, dim3(PR_WG), 0, stream, a, w, pp); break; \
-    default: hipLaunchKernelGGL((prefill_chunk_kernel<4, BAL>), grid, dim3(PR_WG), 0, stream, a, w, pp); break; \
+#define IDXTOPK_PF_CHUNK(BAL, RM)                                                                          \
+  switch (in.heads) {                                                                                      \
+    case 16: hipLaunchKernelGGL((prefill_chunk_kernel<1, BAL, RM>), grid, dim3(PR_WG), 0, stream, a, w, pp); break; \
+    case 32: hipLaunchKernelGGL((prefill_chunk_kernel<2, BAL, RM>), grid, dim3(PR_WG), 0, stream, a, w, pp); break; \
+    default: hipLaunchKernelGGL((prefill_chunk_kernel<4, BAL, RM>), grid, dim3(PR_WG), 0, stream, a, w, pp); break; \
   }
   if (pp.balanced) {
-    IDXTOPK_PF_CHUNK(true)
+    IDXTOPK_PF_CHUNK(true, 4)
   } else {
-    IDXTOPK_PF_CHUNK(false)
+    IDXTOPK_PF_CHUNK(false, 2)
   }
 #undef IDXTOPK_PF_CHUNK
   const int64_t per = (w.cap + PF_MERGE_WG - 1) / PF_MERGE_WG;

@@ -209,9 +209,9 @@ def idx_score_topk_prefill(q, q_scale, w, kcache, k_scale, block_table, seq_lens
                            out_scores: Optional[torch.Tensor] = None, row_to_batch: Optional[torch.Tensor] = None,
                            sorted: bool = False):
     """Fused prefill indexer: top-k slots of each packed prefill row (and
-    their scores if asked), with no score row in device memory. Rows are
-    grouped four at a time by their block-table row (row_to_batch) to share
-    key loads. sorted: rows in descending score order, equal scores by
+    their scores if asked), with no score row in device memory. Rows that
+    share a block-table row (row_to_batch) are scored two at a time (four in
+    calls of few rows) against each key load. sorted: rows in descending score order, equal scores by
     ascending position, -1 padding last."""
     args, B, H, D = _indexer_args(q, q_scale, w, kcache, k_scale, block_table, seq_lens, row_to_batch)
     if out is None:
