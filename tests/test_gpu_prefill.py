@@ -152,13 +152,15 @@ def _crowded(case):
     return case
 
 
-@pytest.mark.parametrize("requests,next_n", [(4, 64), (5, 52), (8, 33)])
+@pytest.mark.parametrize("requests,next_n", [(4, 64), (5, 52), (8, 33), (7, 39)])
 def test_prefill_schedule_boundary(ops, requests, next_n):
     """Around the switch between the two chunk schedules: 64 row quads
     (256 rows: the balanced schedule, chunk sizes taken on the device from
-    the rows' lengths), 65 quads (260 rows: the chunk-major grid), and 66
-    quads whose rows straddle requests. Each equals the unfused path's
-    selection exactly, with the returned scores equal to the score rows."""
+    the rows' lengths), 65 quads (260 rows: the chunk-major grid, two rows
+    per wave), 66 quads whose row pairs straddle requests, and 273 rows (an
+    odd count: the last pair wave holds one row). Each equals the unfused
+    path's selection exactly, with the returned scores equal to the score
+    rows."""
     import torch
 
     case = _prefill_case(760 + requests, requests, next_n, 1, 6000, 64, 300)
