@@ -59,6 +59,7 @@ namespace idxtopk {
 constexpr int FE_CH_MIN = 256;         // shortest chunk: bounds the chunks of a row
 constexpr int FE_RESIDENT_MAX = 2048;  // longest chunk of the one-resident-wave sizing
 constexpr int FE_WIN = 64;             // bins of a chunk's candidate-count window
+constexpr size_t FE_PAIR_LDS = 53 * 1024;  // LDS of a two-row chunk workgroup: three per CU
 
 // win[b][c][i]: how many of chunk c's candidates lie in histogram bin
 // bound_c + i, i < FE_WIN (16-bit counts, two per word: a chunk holds at
@@ -361,15 +362,20 @@ __device__ __forceinline__ void own_bins(const uint32_t* hist, uint32_t (&c)[PER
 
 constexpr uint32_t FU_STAGE = HIST_BINS / 2;  // candidates staged in the histogram's LDS
 
-struct ChunkLds {
+// Selection state of one (row, chunk) in LDS.
+struct ChunkSel {
   union {
     alignas(16) uint32_t hist[HIST_BINS];  // the chunk's histogram, until its bound is known
     uint64_t stage[FU_STAGE];              // then the chunk's candidates
   };
-  int32_t pages[IX_PAGES];
   uint32_t scratch[16];
   uint32_t lcnt;
   uint32_t lcnt2;
+};
+
+struct ChunkLds {
+  ChunkSel sel;
+  int32_t pages[IX_PAGES];
 };
 
 
@@ -387,45 +393,14 @@ __device__ __forceinline__ uint32_t chunk_rank(int k, int cnt, int n) {
   return r >= static_cast<float>(cnt) ? static_cast<uint32_t>(cnt) + 1u : static_cast<uint32_t>(r);
 }
 
-// One workgroup per (row, chunk). Dynamic LDS: the chunk's scores (a.chunk
-// floats). Nothing here waits on another workgroup: the chunk's bound comes
-// from its own histogram, its candidates go to its own tokens' range of the
-// row's candidate area, its count and bound to its own header.
-template <int NT, bool BF = false>
-__global__ __launch_bounds__(IX_WG) void fused_chunk_kernel(IndexerArgs a, FusedWs ws, int k) {
-  extern __shared__ float sc[];
-  __shared__ ChunkLds s;
+// After a chunk's scores (scr[0 .. cnt), tokens tb .. tb + cnt - 1 of row
+// b, which has n tokens) and their histogram (s.hist) are in LDS, and s.lcnt
+// and s.lcnt2 are zero: the chunk's bound, its window of per-bin counts, its
+// candidates and its header. Every thread of the workgroup calls.
+__device__ __forceinline__ void chunk_emit(const FusedWs& ws, int k, int b, int c, int tb, int cnt, int n,
+                                           const float* scr, ChunkSel& s) {
   const int tid = threadIdx.x;
-  int b, c;
-  chunk_of(a, b, c);
-  const int n = row_len(a, b);
-  int tb, clen;
-  chunk_span(a, c, tb, clen);
-  if (tb >= n) return;
-  const int te = min(n, tb + clen);
-  const int cnt = te - tb;
   uint64_t* cand = ws.cand + static_cast<int64_t>(b) * ws.cap + tb;
-
-  for (int i = tid; i < HIST_BINS; i += IX_WG) s.hist[i] = 0;
-  if (tid == 0) {
-    s.lcnt = 0;
-    s.lcnt2 = 0;
-  }
-  // (score_chunk synchronises before its first emit). A bf16 cache is read
-  // with ordinary loads for large batches (the second half of each line then
-  // comes from the cache) and nontemporal ones for decode batches.
-  auto emit = [&](int j, float v, bool valid) {
-    if (valid) {
-      sc[j - tb] = v;
-      atomicAdd(&s.hist[float_key(v) >> HIST_SHIFT], 1u);
-    }
-  };
-  if (a.cached_keys)
-    score_chunk_any<BF, NT, IX_WG, IX_RING, true>(a, b, tb, te, s.pages, emit);
-  else
-    score_chunk_any<BF, NT, IX_WG, IX_RING, false>(a, b, tb, te, s.pages, emit);
-  __syncthreads();
-
   // The chunk's bound: the highest bin whose count from the top reaches
   // chunk_rank (bin 0, every token, when the chunk holds fewer).
   uint32_t c16[16];
@@ -453,7 +428,7 @@ __global__ __launch_bounds__(IX_WG) void fused_chunk_kernel(IndexerArgs a, Fused
 #pragma unroll
     for (int j = 0; j < EB; ++j) {
       const int i = i0 + j * IX_WG + tid;
-      key[j] = float_key(sc[i < cnt ? i : 0]);
+      key[j] = float_key(scr[i < cnt ? i : 0]);
       keep[j] = i < cnt && (key[j] >> HIST_SHIFT) >= bin_c;
       mine += keep[j];
     }
@@ -478,7 +453,7 @@ __global__ __launch_bounds__(IX_WG) void fused_chunk_kernel(IndexerArgs a, Fused
 #pragma unroll
       for (int j = 0; j < EB; ++j) {
         const int i = i0 + j * IX_WG + tid;
-        key[j] = float_key(sc[i < cnt ? i : 0]);
+        key[j] = float_key(scr[i < cnt ? i : 0]);
         keep[j] = i < cnt && (key[j] >> HIST_SHIFT) >= bin_c;
         mine += keep[j];
       }
@@ -489,6 +464,168 @@ __global__ __launch_bounds__(IX_WG) void fused_chunk_kernel(IndexerArgs a, Fused
     }
   }
   if (tid == 0) ws.hdr[static_cast<int64_t>(b) * ws.hcap + c] = make_uint2(m, bin_c);
+}
+
+// One workgroup per (row, chunk). Dynamic LDS: the chunk's scores (a.chunk
+// floats). Nothing here waits on another workgroup: the chunk's bound comes
+// from its own histogram, its candidates go to its own tokens' range of the
+// row's candidate area, its count and bound to its own header.
+template <int NT, bool BF = false>
+__global__ __launch_bounds__(IX_WG) void fused_chunk_kernel(IndexerArgs a, FusedWs ws, int k) {
+  extern __shared__ float sc[];
+  __shared__ ChunkLds s;
+  const int tid = threadIdx.x;
+  int b, c;
+  chunk_of(a, b, c);
+  const int n = row_len(a, b);
+  int tb, clen;
+  chunk_span(a, c, tb, clen);
+  if (tb >= n) return;
+  const int te = min(n, tb + clen);
+  const int cnt = te - tb;
+
+  for (int i = tid; i < HIST_BINS; i += IX_WG) s.sel.hist[i] = 0;
+  if (tid == 0) {
+    s.sel.lcnt = 0;
+    s.sel.lcnt2 = 0;
+  }
+  // (score_chunk synchronises before its first emit). A bf16 cache is read
+  // with ordinary loads for large batches (the second half of each line then
+  // comes from the cache) and nontemporal ones for decode batches.
+  auto emit = [&](int j, float v, bool valid) {
+    if (valid) {
+      sc[j - tb] = v;
+      atomicAdd(&s.sel.hist[float_key(v) >> HIST_SHIFT], 1u);
+    }
+  };
+  if (a.cached_keys)
+    score_chunk_any<BF, NT, IX_WG, IX_RING, true>(a, b, tb, te, s.pages, emit);
+  else
+    score_chunk_any<BF, NT, IX_WG, IX_RING, false>(a, b, tb, te, s.pages, emit);
+  __syncthreads();
+
+  chunk_emit(ws, k, b, c, tb, cnt, n, sc, s.sel);
+}
+
+// ---------------------------------------------------------------------------
+// Fused decode, two rows of one request per workgroup
+// ---------------------------------------------------------------------------
+//
+// Multi-token decode rows (row_to_batch; a request's rows next to each
+// other) read the same keys. Here a workgroup takes rows b0 and b0 + 1 over
+// one chunk: its four waves split the chunk's 16-token groups, and each
+// group is loaded once per wave and scored against both rows
+// (RowGroupStream with score16x2, whose sums run in the per-row scorer's
+// order, so the scores are bit-identical). Each row keeps its own scores and
+// histogram in LDS; its chunk bound, window, candidates and header then
+// follow as in fused_chunk_kernel, so the merge reads the same workspace.
+// Rows of a pair that do not share a block-table row are scored one after
+// the other.
+//
+// Pair slot P = (quad, chunk) is taken by workgroups 16 (P / 8) + P % 8 + 8 h
+// for the rows 4 quad + 2 h and 4 quad + 2 h + 1 (h = 0, 1): the dispatcher
+// sends both to XCD P % 8, so a quad's four rows read the chunk's keys
+// through one L2. The row index rotates with the chunk as in chunk_of.
+// Requires batch % 4 == 0 (quad_map).
+__device__ __forceinline__ void pair_chunk_of(const IndexerArgs& a, int& b0, int& c) {
+  const int i = blockIdx.x;
+  const int h = (i >> 3) & 1;
+  const int Q = ((i >> 4) << 3) | (i & 7);
+  const int nq = a.batch >> 2;
+  c = Q / nq;
+  b0 = 4 * ((Q + c) % nq) + 2 * h;
+}
+
+// Workgroups of the pair grid: every (pair, chunk), in whole groups of 16.
+static inline unsigned pair_chunk_grid(const IndexerArgs& a) {
+  const int64_t n = static_cast<int64_t>(a.nchunk_max) * (a.batch / 2);
+  return static_cast<unsigned>((n + 15) / 16 * 16);
+}
+
+// Rows b0 + r0 .. b0 + r0 + R - 1 (block-table row prow) over tokens
+// [kb, ke) of the chunk that starts at tb: score j of pair row r goes to
+// sc[r * chunk + j - tb] and into sel[r]'s histogram, for j < te[r].
+template <int NT, int R>
+__device__ __forceinline__ void pair_score_rows(const IndexerArgs& a, int b0, int r0, int prow, int kb, int ke,
+                                                int tb, const int (&te)[2], float* sc, ChunkSel (&sel)[2]) {
+  QOperand<NT> q[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int b = b0 + r0 + r;
+    load_query<NT>(q[r], a.q + static_cast<int64_t>(b) * a.heads * kDim, a.w + static_cast<int64_t>(b) * a.heads,
+                   a.q_scale[b]);
+  }
+  RowGroupStream<NT, R> st(a, q, a.block_table + static_cast<int64_t>(prow) * a.bt_stride, kb, ke);
+  // lane group g holds row (g % R)'s scores; groups g >= R repeat rows
+  const int l = lane_id();
+  const int c = l & 15, g = l >> 4;
+  const int r = r0 + (g < R ? g : 0);
+  const int lim = g < R ? te[r] : INT32_MIN;
+  float* srow = sc + r * a.chunk - tb;
+  uint32_t* hist = sel[r].hist;
+  auto in_order = [](int s) { return s; };
+  st.prime(in_order);
+  st.run(0, st.ngroups, in_order, [&](int, int gi, float v) {
+    const int j = kb + gi * kGroup + c;
+    if (j < lim) {
+      srow[j] = v;
+      atomicAdd(&hist[float_key(v) >> HIST_SHIFT], 1u);
+    }
+  });
+}
+
+// Dynamic LDS: the two rows' scores (2 a.chunk floats).
+template <int NT>
+__global__ __launch_bounds__(IX_WG, 3) void fused_pair_chunk_kernel(IndexerArgs a, FusedWs ws, int k) {
+  extern __shared__ float sc[];
+  __shared__ ChunkSel sel[2];
+  const int tid = threadIdx.x;
+  int b0, c;
+  pair_chunk_of(a, b0, c);
+  int tb, clen;
+  chunk_span(a, c, tb, clen);
+  const int n[2] = {row_len(a, b0), row_len(a, b0 + 1)};
+  const int nmax = max(n[0], n[1]);
+  if (tb >= nmax) return;
+  // a row with te[r] <= tb has no token in this chunk
+  const int te[2] = {min(n[0], tb + clen), min(n[1], tb + clen)};
+  for (int i = tid; i < HIST_BINS; i += IX_WG) {
+    sel[0].hist[i] = 0;
+    sel[1].hist[i] = 0;
+  }
+  if (tid == 0) {
+    sel[0].lcnt = 0;
+    sel[0].lcnt2 = 0;
+    sel[1].lcnt = 0;
+    sel[1].lcnt2 = 0;
+  }
+  __syncthreads();
+
+  const int ke = min(nmax, tb + clen);
+  const int G = (ke - tb + kGroup - 1) / kGroup;
+  const int wave = uniform(tid / kWave);
+  const int per = (G + IX_WG / kWave - 1) / (IX_WG / kWave);
+  const int g_lo = wave * per;
+  const int g_hi = min(G, g_lo + per);
+  if (g_lo < g_hi) {
+    const int kb = tb + g_lo * kGroup;
+    const int kw = min(ke, tb + g_hi * kGroup);
+    const int pr[2] = {load_uniform(a.row_to_batch + b0), load_uniform(a.row_to_batch + b0 + 1)};
+    IDXTOPK_CHECK(pr[0] >= 0 && pr[1] >= 0, kChkRowToBatch);
+    if (pr[0] == pr[1]) {
+      pair_score_rows<NT, 2>(a, b0, 0, pr[0], kb, kw, tb, te, sc, sel);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int kr = min(kw, te[r]);
+        if (kb < kr) pair_score_rows<NT, 1>(a, b0, r, pr[r], kb, kr, tb, te, sc, sel);
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    if (te[r] > tb) chunk_emit(ws, k, b0 + r, c, tb, te[r] - tb, n[r], sc + r * a.chunk, sel[r]);
 }
 
 constexpr int MG_SPEC = 8;  // candidate loads per thread issued with the headers
@@ -1406,6 +1543,17 @@ static IndexerArgs fused_args(const IndexerInputs& in) {
   return a;
 }
 
+// Two rows per chunk workgroup (fused_pair_chunk_kernel): rows in quads of
+// a request (quad_map), an fp8 cache whose pages hold whole 16-token groups,
+// at most 64 heads, two rows' scores within the LDS budget, and a wave's
+// quarter of a chunk within the key stream's 128 page ids.
+static bool fused_pairs(const IndexerInputs& in, const IndexerArgs& a) {
+  if (!a.quad_map || in.bf16 || in.page_size % kGroup != 0 || in.heads > 64) return false;
+  if (2 * static_cast<size_t>(a.chunk) * sizeof(float) + 2 * sizeof(ChunkSel) > FE_PAIR_LDS) return false;
+  const int64_t wave_tokens = (static_cast<int64_t>(a.chunk) / kGroup + 3) / 4 * kGroup;
+  return wave_tokens / in.page_size + 2 <= PR_CHUNK_PAGES;
+}
+
 // Sorted output: the merge leaves positions and scores (in the workspace's
 // score area when the caller wants none), then the sort pass orders and maps
 // them.
@@ -1422,12 +1570,22 @@ int launch_fused(const IndexerInputs& in, int k, int32_t* out_slots, float* out_
   // every chunk of a row has a header (chunks are at least FE_CH_MIN tokens:
   // the page-staging cap is 496 tokens or more)
   if (a.nchunk_max > w.hcap) return -4;
-  const dim3 grid(chunk_grid(a));
   (void)hipGetLastError();
   // the scores' dynamic LDS plus the static part stay within 64 KB
   static_assert(FU_CH_MAX * 4 + sizeof(ChunkLds) <= 64 * 1024, "fused chunk LDS");
-  const size_t lds = static_cast<size_t>(a.chunk) * sizeof(float);
-  IDXTOPK_DISPATCH_NT_LDS(fused_chunk_kernel, in.bf16, in.heads, grid, lds, stream, a, w, k);
+  if (fused_pairs(in, a)) {
+    const size_t lds = 2 * static_cast<size_t>(a.chunk) * sizeof(float);
+    const dim3 grid(pair_chunk_grid(a));
+    switch (in.heads) {
+      case 16: hipLaunchKernelGGL(fused_pair_chunk_kernel<1>, grid, dim3(IX_WG), lds, stream, a, w, k); break;
+      case 32: hipLaunchKernelGGL(fused_pair_chunk_kernel<2>, grid, dim3(IX_WG), lds, stream, a, w, k); break;
+      default: hipLaunchKernelGGL(fused_pair_chunk_kernel<4>, grid, dim3(IX_WG), lds, stream, a, w, k); break;
+    }
+  } else {
+    const dim3 grid(chunk_grid(a));
+    const size_t lds = static_cast<size_t>(a.chunk) * sizeof(float);
+    IDXTOPK_DISPATCH_NT_LDS(fused_chunk_kernel, in.bf16, in.heads, grid, lds, stream, a, w, k);
+  }
   if (in.bf16) {
     IDXTOPK_MERGE_NT(true, in.heads, dim3(in.batch), stream, a, w, o)
   } else {

@@ -536,6 +536,35 @@ def test_multi_query_fused(ops, page_size, k):
         check_fused_row(slots[b], sc[b], rows[b], ts, k, batch_sigma=bsig)
 
 
+@pytest.mark.parametrize("heads,page_size,k,requests,next_n", [
+    (64, 64, 2048, 8, 3),   # 24 rows: row pairs straddle requests
+    (32, 16, 300, 4, 4),    # 16 rows: each quad one request
+    (16, 128, 700, 6, 2),   # 12 rows: pairs within requests, quads across two
+    (64, 32, 64, 3, 4),     # 12 rows, k far below the row lengths
+])
+def test_multi_query_fused_row_pairs(ops, heads, page_size, k, requests, next_n):
+    """Rows in quads (a row count that is a multiple of 4): the fused call
+    scores two rows per chunk workgroup against one key load. Its selection
+    equals the per-row call's on the expanded block tables (the same fp32
+    scores), on the one-wave and the guided chunk schedules, and every row
+    meets the oracle criterion."""
+    case = workloads.multi_query_case(940 + page_size, requests=requests, next_n=next_n, n_lo=1, n_hi=20000,
+                                      page_size=page_size, k=k, heads=heads)
+    assert case.batch % 4 == 0
+    log(f"multi-query fused, row pairs: rows={case.batch} heads={heads} P={page_size} k={k}")
+    rows = [case_scores(case, b) for b in range(case.batch)]
+    bsig = rms(np.concatenate(rows))
+    ref, ref_sc = _fused(ops, _expanded(case))
+    for c in (case, _guided_variant(case)):
+        slots, sc = _fused(ops, c)
+        assert np.array_equal(np.sort(slots, axis=1), np.sort(ref, axis=1)), c.max_seq_len
+        assert np.array_equal(np.sort(sc, axis=1), np.sort(ref_sc, axis=1)), c.max_seq_len
+    for b in range(case.batch):
+        n = int(case.seq_lens[b])
+        ts = oracle.token_slots(case.block_table[case.row_to_batch[b]], case.page_size, n)
+        check_fused_row(slots[b], sc[b], rows[b], ts, k, batch_sigma=bsig)
+
+
 def test_multi_query_scores(ops):
     case = workloads.multi_query_case(911, requests=4, next_n=4, n_lo=1, n_hi=5000, page_size=32, k=0, heads=32)
     out = ops.idx_score_fp8(*_inputs(case), case.page_size, case.max_seq_len, row_to_batch=_r2b(case))
