@@ -96,7 +96,7 @@ PMC_KERNELS = {
                                "fused_decode_B32_k2048"),
     "fused_decode_B32_merge": ("fused", "void idxtopk::fused_merge_kernel<4, false>", 32768,
                                "fused_decode_B32_k2048"),
-    "mtp_decode_16x4_chunk": ("fused", "void idxtopk::fused_chunk_kernel<4, false>", 524288,
+    "mtp_decode_16x4_chunk": ("fused", "void idxtopk::fused_pair_chunk_kernel<4>", 262144,
                               "mtp_decode_16x4_k2048"),
     "mtp_decode_16x4_rowgroup_chunk": ("prefill", "void idxtopk::prefill_chunk_kernel<4, true, 4>", 65536,
                                        "mtp_decode_16x4_k2048"),
@@ -375,7 +375,8 @@ def bench_fused_mq(torch, ops, timer, case, warmup, steps, flush):
     nbytes = indexer_algorithmic_bytes(case, case.batch * case.k)
     wall, us, region = timer.run(step, warmup, steps, flush)
     res = summary(us, nbytes, case.batch, region, timer.settled)
-    res["call"] = "idx_score_topk_fused (rows of a request dealt to one XCD, keys shared through its L2)"
+    res["call"] = ("idx_score_topk_fused (two rows of a request per chunk workgroup against one key load; "
+                   "a request's rows on one XCD, keys shared through its L2)")
     res["rows"] = case.batch
     res["row_tokens"] = int(case.seq_lens.astype(np.int64).sum())
     # the row-group call on the same rows (each key group loaded once for a
