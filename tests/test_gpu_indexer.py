@@ -565,6 +565,29 @@ def test_multi_query_fused_row_pairs(ops, heads, page_size, k, requests, next_n)
         check_fused_row(slots[b], sc[b], rows[b], ts, k, batch_sigma=bsig)
 
 
+def test_multi_query_fused_row_pairs_short_rows(ops):
+    """Two rows per chunk workgroup at the edges: contexts 1, 2, 3 and 16
+    give rows of 0 to 3 keys (a pair with one empty row, pairs shorter than
+    k) beside longer requests, so chunks hold one row of a pair and not the
+    other. The selection equals the per-row call's on the expanded block
+    tables and meets the oracle criterion."""
+    lens = np.array([1, 2, 3, 16, 2047, 2049, 4100, 9000], np.int32)
+    case = workloads.multi_query_case(960, requests=8, next_n=2, n_lo=0, n_hi=0, page_size=64, k=2048, heads=64,
+                                      fixed_lens=lens)
+    assert case.batch % 4 == 0 and int(case.seq_lens.min()) == 0
+    log(f"multi-query fused, row pairs, short rows: rows={case.batch} lens={case.seq_lens.tolist()}")
+    rows = [case_scores(case, b) for b in range(case.batch)]
+    bsig = rms(np.concatenate([r for r in rows if r.size]))
+    ref, ref_sc = _fused(ops, _expanded(case))
+    slots, sc = _fused(ops, case)
+    assert np.array_equal(np.sort(slots, axis=1), np.sort(ref, axis=1))
+    assert np.array_equal(np.sort(sc, axis=1), np.sort(ref_sc, axis=1))
+    for b in range(case.batch):
+        n = int(case.seq_lens[b])
+        ts = oracle.token_slots(case.block_table[case.row_to_batch[b]], case.page_size, n)
+        check_fused_row(slots[b], sc[b], rows[b], ts, case.k, batch_sigma=bsig)
+
+
 def test_multi_query_scores(ops):
     case = workloads.multi_query_case(911, requests=4, next_n=4, n_lo=1, n_hi=5000, page_size=32, k=0, heads=32)
     out = ops.idx_score_fp8(*_inputs(case), case.page_size, case.max_seq_len, row_to_batch=_r2b(case))
