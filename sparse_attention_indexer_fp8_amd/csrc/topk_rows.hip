@@ -861,6 +861,147 @@ __global__ __launch_bounds__(TR_WG, 4) void topk_rows_kernel(RowsArgs a) {
   wg_row<SORTED>(a, row_setup(a, blockIdx.x), cand, s);
 }
 
+// ---------------------------------------------------------------------------
+// Launches of few short rows: one 1024-thread workgroup per row
+// ---------------------------------------------------------------------------
+//
+// Rows of at most SM_MAX_N keys (every window of a score buffer whose row
+// stride is at most SM_MAX_N), in launches too small to fill the chip. Each
+// thread holds SM_PER consecutive keys in registers after one load round
+// trip, and the k-th value key T is found exactly by a radix select over the
+// 32-bit value keys, 8 bits per round from the top: each round histograms
+// the digit of the keys that match the bits found so far, and one wave finds
+// the digit where the count from the top reaches the remaining rank. Every
+// key above T is kept, and of the keys equal to T the remaining rank's count
+// with the lowest positions; one workgroup scan of the packed (above, equal)
+// counts gives each thread both its output offset and its ties' ranks. The
+// kept positions then go through the page table, their lookups issued
+// together.
+constexpr int SM_WG = 1024;
+constexpr int SM_PER = 4;
+constexpr int SM_MAX_N = SM_WG * SM_PER;
+constexpr int SM_WAVES = SM_WG / kWave;
+
+struct SmallRowLds {
+  uint32_t hist[256];
+  uint32_t wsum[SM_WAVES];
+  uint32_t digit;
+  uint32_t above;
+};
+
+__global__ __launch_bounds__(SM_WG) void topk_small_rows_kernel(RowsArgs a) {
+  __shared__ SmallRowLds s;
+  const RowCtx r = row_setup(a, blockIdx.x);
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = uniform(tid / kWave);
+  const uint32_t k = static_cast<uint32_t>(a.k);
+  const uint32_t P = static_cast<uint32_t>(a.page_size);
+  IDXTOPK_CHECK(r.n <= SM_MAX_N, kChkWindow);
+  const int n = r.n < SM_MAX_N ? r.n : SM_MAX_N;
+  if (static_cast<uint32_t>(n) <= k) {
+    for (int i = tid; i < static_cast<int>(k); i += SM_WG)
+      r.out[i] = i < n ? map_slot(r.pt_row, static_cast<uint32_t>(i) + r.off, P, a.pdiv) : -1;
+    return;
+  }
+
+  // this thread's keys: positions SM_PER tid .. SM_PER tid + SM_PER - 1
+  uint32_t vk[SM_PER];
+  bool ok[SM_PER];
+#pragma unroll
+  for (int e = 0; e < SM_PER; ++e) {
+    const int p = SM_PER * tid + e;
+    ok[e] = p < n;
+    const float x = r.base[ok[e] ? p : 0];  // n > k >= 1 here, so position 0 exists
+    vk[e] = ok[e] ? float_key(x) : 0u;
+  }
+
+  // Radix select: T = the k-th largest value key; kk ends as the number of
+  // keys equal to T that are kept.
+  uint32_t prefix = 0u, pmask = 0u, kk = k;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int shift = 24 - 8 * d;
+    if (tid < 256) s.hist[tid] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < SM_PER; ++e)
+      if (ok[e] && (vk[e] & pmask) == prefix) atomicAdd(&s.hist[(vk[e] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (wave == 0) {
+      // lane l holds digits 4 l .. 4 l + 3; counts from the top
+      const uint4 c4 = reinterpret_cast<const uint4*>(s.hist)[lane];
+      const uint32_t c[4] = {c4.x, c4.y, c4.z, c4.w};
+      const uint32_t local = c[0] + c[1] + c[2] + c[3];
+      const uint32_t incl = wave_prefix_incl(local);
+      const uint32_t tot = __builtin_amdgcn_readlane(incl, kWave - 1);
+      uint32_t above = tot - incl;  // keys in the digits of higher lanes
+      if (above < kk && above + local >= kk) {
+        int i = 3;
+        for (; i > 0; --i) {
+          if (above + c[i] >= kk) break;
+          above += c[i];
+        }
+        s.digit = 4u * static_cast<uint32_t>(lane) + static_cast<uint32_t>(i);
+        s.above = above;
+      }
+    }
+    __syncthreads();
+    kk -= s.above;
+    prefix |= s.digit << shift;
+    pmask |= 255u << shift;
+  }
+  const uint32_t T = prefix;
+
+  // Offsets: one scan of (above T) << 16 | (equal to T) in position order.
+  uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+  for (int e = 0; e < SM_PER; ++e) {
+    gt += ok[e] && vk[e] > T;
+    eq += ok[e] && vk[e] == T;
+  }
+  const uint32_t mine = (gt << 16) | eq;
+  const uint32_t incl = wave_prefix_incl(mine);
+  if (lane == kWave - 1) s.wsum[wave] = incl;
+  __syncthreads();
+  uint32_t before = incl - mine;
+  for (int w = 0; w < wave; ++w) before += s.wsum[w];
+  const uint32_t eq_before = before & 0xffffu;
+  uint32_t at = (before >> 16) + (eq_before < kk ? eq_before : kk);
+  uint32_t tie = eq_before;
+
+  bool keep[SM_PER];
+  uint32_t idx[SM_PER], pos[SM_PER], pg[SM_PER];
+  int32_t page[SM_PER];
+#pragma unroll
+  for (int e = 0; e < SM_PER; ++e) {
+    keep[e] = false;
+    if (ok[e] && vk[e] > T) {
+      keep[e] = true;
+    } else if (ok[e] && vk[e] == T) {
+      keep[e] = tie < kk;
+      ++tie;
+    }
+    idx[e] = at;
+    at += keep[e];
+    pos[e] = static_cast<uint32_t>(SM_PER * tid + e) + r.off;
+    pg[e] = keep[e] && r.pt_row ? fdiv(pos[e], a.pdiv) : 0u;
+    IDXTOPK_CHECK(!keep[e] || idx[e] < k, kChkPosition);
+  }
+  if (r.pt_row) {
+    // all lookups issued before any is used; entries not kept read page 0
+#pragma unroll
+    for (int e = 0; e < SM_PER; ++e) page[e] = r.pt_row[pg[e]];
+#pragma unroll
+    for (int e = 0; e < SM_PER; ++e) IDXTOPK_CHECK(!keep[e] || page[e] >= 0, kChkPageId);
+  }
+#pragma unroll
+  for (int e = 0; e < SM_PER; ++e)
+    if (keep[e] && idx[e] < k)
+      r.out[idx[e]] = r.pt_row ? static_cast<int32_t>(static_cast<int64_t>(page[e]) * P + (pos[e] - pg[e] * P))
+                               : static_cast<int32_t>(pos[e]);
+}
+
 // Candidate buffer entries: at least two tiles (the first tile is appended
 // whole in the worst case), and k plus one and a half tiles so that a
 // compaction frees at least a quarter tile beyond the next tile.
@@ -916,6 +1057,13 @@ int launch_topk_rows(const float* scores, int64_t stride, int rows, const int32_
   if (sorted && a.cap < npow) a.cap = npow;
   if (!rows_cap_ok(a.cap, k)) return -4;
   a.rows = rows;
+  // Launches of few rows whose windows hold at most SM_MAX_N keys (the row
+  // stride bounds every window): one 1024-thread workgroup per row.
+  if (!sorted && rows < SR_MIN_ROWS && stride <= SM_MAX_N) {
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(topk_small_rows_kernel, dim3(rows), dim3(SM_WG), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+  }
   // One wave per short row: it takes longer per row than a workgroup does,
   // so it pays only when there are rows enough to fill the chip (and it
   // needs four wave areas in the candidate buffer).

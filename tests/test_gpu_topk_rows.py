@@ -135,6 +135,39 @@ def test_adversarial_rows(ops, k):
         assert np.array_equal(np.sort(got[i]), np.sort(ref[i])), nm
 
 
+@pytest.mark.parametrize("k", [1, 512, 2048, 4095])
+def test_small_rows_adversarial(ops, k):
+    """Launches of few rows whose windows hold at most 4096 keys take one
+    1024-thread workgroup per row (radix select on the value keys, ties to the
+    lowest positions). The adversarial rows at 4096 keys and at shorter and
+    odd lengths, exact sets against the oracle."""
+    rows = _adversarial_rows(n=4096)
+    names = list(rows)
+    buf = np.stack([rows[nm] for nm in names])
+    for lens in (np.full(len(names), 4096, np.int32),
+                 np.array([4095, 3001, 2049, 1025, min(k + 1, 4096), 7, 4096], np.int32)):
+        got = _run_rows(ops, buf, lens, k)
+        ref = oracle.topk_rows(buf, lens, k)
+        for i, nm in enumerate(names):
+            assert np.array_equal(np.sort(got[i]), np.sort(ref[i])), (nm, int(lens[i]))
+
+
+def test_small_rows_packed_paged(ops):
+    """The one-workgroup small-row path with packed windows at unaligned
+    starts, row_to_batch, a page size of 3 and heavily tied values."""
+    g = np.random.default_rng(12)
+    rows, stride, k, P, reqs = 40, 4093, 300, 3, 5
+    lens = g.integers(1, 2000, size=rows).astype(np.int32)
+    starts = g.integers(0, stride - lens + 1).astype(np.int32)
+    buf = np.round(g.standard_normal((rows, stride)) * 3).astype(np.float32)
+    r2b = g.integers(0, reqs, size=rows).astype(np.int32)
+    npg = -(-2000 // P) + 1
+    pt = np.stack([g.permutation(npg * 4)[:npg] for _ in range(reqs)]).astype(np.int32)
+    got = _run_rows(ops, buf, lens, k, starts, r2b, pt, P)
+    ref = oracle.topk_rows(buf, lens, k, starts, r2b, pt, P)
+    assert np.array_equal(sorted_rows(got), sorted_rows(ref))
+
+
 @pytest.mark.parametrize("k,page_size,with_offset", [(512, 1, False), (64, 16, True), (300, 1, True)])
 def test_short_rows_one_wave(ops, k, page_size, with_offset):
     """Launches of 2048 rows or more take rows of at most 8192 keys one wave
