@@ -868,15 +868,17 @@ __global__ __launch_bounds__(TR_WG, 4) void topk_rows_kernel(RowsArgs a) {
 // Rows of at most SM_MAX_N keys (every window of a score buffer whose row
 // stride is at most SM_MAX_N), in launches too small to fill the chip. Each
 // thread holds SM_PER consecutive keys in registers after one load round
-// trip, and the k-th value key T is found exactly by a radix select over the
-// 32-bit value keys, 8 bits per round from the top: each round histograms
-// the digit of the keys that match the bits found so far, and one wave finds
-// the digit where the count from the top reaches the remaining rank. Every
-// key above T is kept, and of the keys equal to T the remaining rank's count
-// with the lowest positions; one workgroup scan of the packed (above, equal)
-// counts gives each thread both its output offset and its ties' ranks. The
-// kept positions then go through the page table, their lookups issued
-// together.
+// trip, and the k-th value key is located by a radix select over the 32-bit
+// value keys, 8 bits per round from the top: each round histograms the digit
+// of the keys that match the bits found so far (the prefix), and one wave
+// finds the digit where the count from the top reaches the remaining rank.
+// The select stops early when the keys matching the prefix number exactly
+// the remaining rank. Every key above the prefix (in its bits) is kept, and
+// of the keys matching it the remaining rank's count with the lowest
+// positions (all of them after an early stop); one workgroup scan of the
+// packed (above, matching) counts gives each thread both its output offset
+// and its ties' ranks. The kept positions then go through the page table,
+// their lookups issued together.
 constexpr int SM_WG = 1024;
 constexpr int SM_PER = 4;
 constexpr int SM_MAX_N = SM_WG * SM_PER;
@@ -887,6 +889,7 @@ struct SmallRowLds {
   uint32_t wsum[SM_WAVES];
   uint32_t digit;
   uint32_t above;
+  uint32_t count;  // keys with the found digit
 };
 
 __global__ __launch_bounds__(SM_WG) void topk_small_rows_kernel(RowsArgs a) {
@@ -916,10 +919,10 @@ __global__ __launch_bounds__(SM_WG) void topk_small_rows_kernel(RowsArgs a) {
     vk[e] = ok[e] ? float_key(x) : 0u;
   }
 
-  // Radix select: T = the k-th largest value key; kk ends as the number of
-  // keys equal to T that are kept.
+  // Radix select: (prefix, pmask) ends as the bits of the k-th largest value
+  // key that the rounds resolved, kk as the number of keys matching them
+  // that are kept.
   uint32_t prefix = 0u, pmask = 0u, kk = k;
-#pragma unroll
   for (int d = 0; d < 4; ++d) {
     const int shift = 24 - 8 * d;
     if (tid < 256) s.hist[tid] = 0u;
@@ -944,21 +947,23 @@ __global__ __launch_bounds__(SM_WG) void topk_small_rows_kernel(RowsArgs a) {
         }
         s.digit = 4u * static_cast<uint32_t>(lane) + static_cast<uint32_t>(i);
         s.above = above;
+        s.count = c[i];
       }
     }
     __syncthreads();
     kk -= s.above;
     prefix |= s.digit << shift;
     pmask |= 255u << shift;
+    if (s.count == kk) break;  // every key matching the prefix is kept
   }
-  const uint32_t T = prefix;
 
-  // Offsets: one scan of (above T) << 16 | (equal to T) in position order.
+  // Offsets: one scan of (above the prefix) << 16 | (matching it) in
+  // position order.
   uint32_t gt = 0u, eq = 0u;
 #pragma unroll
   for (int e = 0; e < SM_PER; ++e) {
-    gt += ok[e] && vk[e] > T;
-    eq += ok[e] && vk[e] == T;
+    gt += ok[e] && (vk[e] & pmask) > prefix;
+    eq += ok[e] && (vk[e] & pmask) == prefix;
   }
   const uint32_t mine = (gt << 16) | eq;
   const uint32_t incl = wave_prefix_incl(mine);
@@ -976,9 +981,9 @@ __global__ __launch_bounds__(SM_WG) void topk_small_rows_kernel(RowsArgs a) {
 #pragma unroll
   for (int e = 0; e < SM_PER; ++e) {
     keep[e] = false;
-    if (ok[e] && vk[e] > T) {
+    if (ok[e] && (vk[e] & pmask) > prefix) {
       keep[e] = true;
-    } else if (ok[e] && vk[e] == T) {
+    } else if (ok[e] && (vk[e] & pmask) == prefix) {
       keep[e] = tie < kk;
       ++tie;
     }

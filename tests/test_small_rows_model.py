@@ -4,12 +4,15 @@ Not the oracle and not the kernel: a plain restatement of the kernel's
 steps for one row of at most 4096 keys, 1024 threads of 4 consecutive keys
 each:
 
-* four radix rounds over the 32-bit value keys, 8 bits per round from the
-  top; in each round one wave of 64 lanes (4 digits per lane) finds the
-  digit where the count from the top reaches the remaining rank;
-* one scan of the packed counts (keys above the threshold) << 16 | (keys
-  equal to it) in thread order, which gives each thread its output offset
-  and its ties' ranks; the ties with the lowest positions are kept.
+* up to four radix rounds over the 32-bit value keys, 8 bits per round
+  from the top; in each round one wave of 64 lanes (4 digits per lane)
+  finds the digit where the count from the top reaches the remaining rank,
+  and the rounds stop early when the keys matching the bits found so far
+  (the prefix) number exactly the remaining rank;
+* one scan of the packed counts (keys above the prefix) << 16 | (keys
+  matching it) in thread order, which gives each thread its output offset
+  and its ties' ranks; the matching keys with the lowest positions are
+  kept.
 
 Checked here: every round has exactly one lane that holds the digit, the
 packed counts never carry between their halves, exactly k distinct outputs
@@ -58,17 +61,18 @@ def small_row(vals: np.ndarray, k: int) -> list:
                 while i > 0 and above + int(c[i]) < kk:
                     above += int(c[i])
                     i -= 1
-                holders.append((4 * lane + i, above))
+                holders.append((4 * lane + i, above, int(c[i])))
         assert len(holders) == 1
-        digit, above = holders[0]
+        digit, above, count = holders[0]
         kk -= above
         prefix |= digit << shift
         pmask |= 255 << shift
-    T = prefix
-    t_keys = vk.reshape(SM_WG, SM_PER)
+        if count == kk:
+            break
+    t_keys = vk.reshape(SM_WG, SM_PER) & pmask
     t_ok = ok.reshape(SM_WG, SM_PER)
-    gt = (t_ok & (t_keys > T)).sum(axis=1)
-    eq = (t_ok & (t_keys == T)).sum(axis=1)
+    gt = (t_ok & (t_keys > prefix)).sum(axis=1)
+    eq = (t_ok & (t_keys == prefix)).sum(axis=1)
     assert gt.sum() < 1 << 16 and eq.sum() < 1 << 16
     packed = (gt << 16) | eq
     before = np.concatenate([[0], np.cumsum(packed)[:-1]])
@@ -82,9 +86,9 @@ def small_row(vals: np.ndarray, k: int) -> list:
             if not ok[p]:
                 continue
             keep = False
-            if vk[p] > T:
+            if vk[p] & pmask > prefix:
                 keep = True
-            elif vk[p] == T:
+            elif vk[p] & pmask == prefix:
                 keep = tie < kk
                 tie += 1
             if keep:
