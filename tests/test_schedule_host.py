@@ -1,6 +1,7 @@
-"""Host-side checks of the balanced (quad, chunk) schedule of the row-group
-call for few rows: the arithmetic its kernel relies on, restated and checked
-over many length mixes (no GPU)."""
+"""Host-side checks of the chunk schedules (no GPU): the balanced (quad,
+chunk) schedule of the row-group call for few rows, restated and checked
+over many length mixes, and the workgroup -> (rows, chunk) maps of the
+chunk-major indexer grids (one row, or two rows of a quad, per workgroup)."""
 import math
 
 import numpy as np
@@ -77,3 +78,70 @@ def test_balanced_pairs_fit_grid_and_cover_every_group(seed):
 def test_balanced_all_rows_empty():
     W, gsz, gq, pairs = schedule(np.zeros(8, np.int64), msl=4096)
     assert pairs == [] and gsz == 1
+
+
+# ---------------------------------------------------------------------------
+# Chunk-major grids of the indexer kernels (csrc/indexer.hip: chunk_of with
+# quad_map, pair_chunk_of), restated: workgroup index -> (rows, chunk).
+# ---------------------------------------------------------------------------
+
+
+def quad_slot(i: int, batch: int):
+    """chunk_of under quad_map: workgroup i -> (row, chunk)."""
+    r = (i >> 3) & 3
+    Q = ((i >> 5) << 3) | (i & 7)
+    nq = batch >> 2
+    c = Q // nq
+    return 4 * ((Q + c) % nq) + r, c
+
+
+def pair_slot(i: int, batch: int):
+    """pair_chunk_of: workgroup i -> (first row of the pair, chunk)."""
+    h = (i >> 3) & 1
+    Q = ((i >> 4) << 3) | (i & 7)
+    nq = batch >> 2
+    c = Q // nq
+    return 4 * ((Q + c) % nq) + 2 * h, c
+
+
+@pytest.mark.parametrize("batch,nchunk", [(8, 1), (12, 5), (64, 33), (16, 40), (256, 3)])
+def test_pair_grid_covers_every_pair_chunk_once(batch, nchunk):
+    """Every (pair, chunk) with chunk < nchunk is taken by exactly one
+    workgroup of the pair grid (whole groups of 16), padding workgroups get
+    chunks >= nchunk, and the two pairs of a quad on one chunk sit on the same
+    XCD (workgroups dealt to 8 XCDs round-robin by index)."""
+    grid = -(-(nchunk * (batch // 2)) // 16) * 16
+    seen = {}
+    for i in range(grid):
+        b0, c = pair_slot(i, batch)
+        assert b0 % 2 == 0 and 0 <= b0 <= batch - 2
+        if c >= nchunk:
+            continue
+        assert (b0, c) not in seen
+        seen[(b0, c)] = i % 8
+    assert len(seen) == nchunk * (batch // 2)
+    for (b0, c), xcd in seen.items():
+        if b0 % 4 == 0:
+            assert seen[(b0 + 2, c)] == xcd
+
+
+@pytest.mark.parametrize("batch,nchunk", [(8, 1), (12, 5), (64, 33)])
+def test_quad_grid_matches_pair_grid_rows(batch, nchunk):
+    """The per-row quad grid (chunk_of) and the pair grid cover the same
+    (row, chunk) set, and both keep a quad's rows of one chunk on one XCD."""
+    grid_q = -(-(nchunk * batch) // 32) * 32
+    rows_q = {}
+    for i in range(grid_q):
+        b, c = quad_slot(i, batch)
+        if c < nchunk:
+            assert (b, c) not in rows_q
+            rows_q[(b, c)] = i % 8
+    grid_p = -(-(nchunk * (batch // 2)) // 16) * 16
+    rows_p = set()
+    for i in range(grid_p):
+        b0, c = pair_slot(i, batch)
+        if c < nchunk:
+            rows_p.update({(b0, c), (b0 + 1, c)})
+    assert set(rows_q) == rows_p == {(b, c) for b in range(batch) for c in range(nchunk)}
+    for (b, c), xcd in rows_q.items():
+        assert rows_q[(b - b % 4, c)] == xcd
