@@ -607,7 +607,7 @@ __device__ __forceinline__ void wg_row(const RowsArgs& a, const RowCtx& cur, uin
       if (keep[j]) {
         const int32_t slot = paged ? static_cast<int32_t>(static_cast<int64_t>(base[j]) * P + (pos[j] - pg[j] * P))
                                    : static_cast<int32_t>(pos[j]);
-        if (at < k) cur.out[at] = slot;
+        if (at < k) __builtin_nontemporal_store(slot, cur.out + at);  // read by the next kernel, not by this one
         ++at;
       }
     }
@@ -797,8 +797,9 @@ __device__ __forceinline__ bool short_row(const RowsArgs& a, const RowCtx& r, ui
 #pragma unroll
     for (int e = 0; e < SR_EMIT; ++e)
       if (keep[e])
-        r.out[idx[e]] = r.pt_row ? static_cast<int32_t>(static_cast<int64_t>(page[e]) * P + (pos[e] - pg[e] * P))
-                                 : static_cast<int32_t>(pos[e]);
+        __builtin_nontemporal_store(r.pt_row ? static_cast<int32_t>(static_cast<int64_t>(page[e]) * P + (pos[e] - pg[e] * P))
+                                            : static_cast<int32_t>(pos[e]),
+                                    r.out + idx[e]);
   }
   return true;
 }
